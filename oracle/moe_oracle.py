@@ -1,0 +1,313 @@
+"""Plain, slow CPU oracle of the dropless MoE layer hot path.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path imports, calls or
+links this module; only the tests, the package smoke check and the benchmark's
+CPU-baseline leg do.  It shares no code with the HIP library: its only input
+dependency is the seeded input generator (``moe_inputs``), which holds none of
+the layer's arithmetic.
+
+Source.  The page "Accelerating dropless MoE training in JAX with NVIDIA
+Transformer Engine" (cited below as *TE-MoE*) describes the layer: a learned
+router picks the Top-K experts of each token (introduction); every token is
+processed by each expert it chose, with nothing dropped or padded (section
+"How is dropless MoE different from capacity-based MoE?"); tokens are
+dispatched into per-expert groups of variable length, the grouped MLP runs two
+grouped GEMMs over those groups, and combine restores the original token order
+(Figure 3 paragraph of "What specialised optimisations does dropless MoE
+need?"); one grouped GEMM handles every expert at its real token count
+("Optimisation 1: Grouped GEMM").  The page prints no formula.  Where it is
+silent this oracle takes the plainest reading the rest supports:
+
+* router logits are x . Wr^T (Wr stored [E, d]); keys are fp32(logit + bias),
+  or the logits themselves when there is no bias;
+* the K experts with the largest keys are chosen (ties: lower expert index;
+  keys compared in the total order of fp32 bit patterns, so -0.0 < +0.0),
+  listed by descending key;
+* scores are a softmax over all E keys (or a sigmoid per key) and the K chosen
+  scores are divided by their sum (renormalised gates);
+* rows of each expert group are in ascending token order (a stable counting
+  sort of the slots s = t*K + k);
+* an expert is SwiGLU: h = silu(x Wg^T) * (x Wu^T), y = h W2^T, no biases;
+  the first grouped GEMM is gate and up together (W13 = [Wg; Wu], [2F, d]),
+  the second is the down projection (W2 [d, F]);
+* the gates are applied in combine: y_t = sum_k g_tk * Y_perm[pos(t, k)];
+* backward holds the routing fixed and yields dX, dW13, dW2 and d_gates.
+
+Arithmetic is fp64 from the exact input values with no intermediate rounding;
+the only fp32 step is the key add, because it decides the integer routing and
+both sides must take that decision in the same precision.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+SCORE_SOFTMAX, SCORE_SIGMOID = 0, 1
+
+
+# ----------------------------------------------------------------------------
+# value decoding (bf16 inputs arrive as uint16 bit patterns)
+
+def to_f64(a: np.ndarray) -> np.ndarray:
+    """Exact fp64 value of an fp32 / fp64 array or of bf16 bit patterns (uint16)."""
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def _fp32_order(v: np.float32) -> int:
+    """Rank of an fp32 value in the total order of bit patterns (NaN excluded)."""
+    u = int(np.float32(v).view(np.uint32))
+    return (~u) & 0xFFFFFFFF if u & 0x80000000 else u | 0x80000000
+
+
+# ----------------------------------------------------------------------------
+# S0: router logits  (TE-MoE introduction: a learned router scores the experts)
+
+def router_logits(x: np.ndarray, w_router: np.ndarray) -> np.ndarray:
+    """logits[t, e] = sum_j x[t, j] * Wr[e, j], computed in fp64, rounded once to fp32."""
+    return (to_f64(x) @ to_f64(w_router).T).astype(np.float32)
+
+
+# ----------------------------------------------------------------------------
+# S1-S3: routing  (TE-MoE introduction: Top-K experts per token; "What are the
+# challenges in MoE training?": every expert gets a different, data-dependent
+# number of tokens, i.e. ragged groups)
+
+@dataclass
+class Routing:
+    keys: np.ndarray      # [T, E] fp32  logit + bias
+    idx: np.ndarray       # [T, K] int32 chosen experts, by descending key
+    gates: np.ndarray     # [T, K] fp64  renormalised gate values
+    counts: np.ndarray    # [E]    int64 slots per expert
+    offsets: np.ndarray   # [E+1]  int64 exclusive prefix sum of counts
+    slot_pos: np.ndarray  # [T*K]  int64 row of slot s in expert-contiguous order
+    row_src: np.ndarray   # [T*K]  int64 slot held by permuted row r (inverse of slot_pos)
+
+
+def route(logits: np.ndarray, bias: np.ndarray | None, K: int, score: int = SCORE_SOFTMAX,
+          renorm: bool = True) -> Routing:
+    logits = np.asarray(logits, dtype=np.float32)
+    T, E = logits.shape
+    if not 1 <= K <= E:
+        raise ValueError("need 1 <= K <= E")
+    if bias is None:
+        keys = logits.copy()              # no add: a -0.0 logit stays -0.0
+    else:
+        keys = logits + np.asarray(bias, np.float32)[None, :]   # fp32 add, nearest even
+
+    idx = np.zeros((T, K), np.int32)
+    gates = np.zeros((T, K), np.float64)
+    for t in range(T):
+        row = keys[t]
+        # S1a: order experts by (key descending, expert ascending); keep the first K
+        order = sorted(range(E), key=lambda e: (-_fp32_order(row[e]), e))
+        chosen = order[:K]
+        # S1b: scores in fp64 over all experts
+        k64 = row.astype(np.float64)
+        if score == SCORE_SOFTMAX:
+            z = np.exp(k64 - k64.max())
+            s = z / z.sum()
+        elif score == SCORE_SIGMOID:
+            s = 1.0 / (1.0 + np.exp(-k64))
+        else:
+            raise ValueError("score must be softmax (0) or sigmoid (1)")
+        # S1c: renormalise over the chosen experts
+        sel = s[chosen]
+        g = sel / sel.sum() if renorm else sel
+        idx[t] = chosen
+        gates[t] = g
+
+    # S2: per-expert histogram and its exclusive prefix sum
+    M = T * K
+    counts = np.zeros(E, np.int64)
+    for s_ in range(M):
+        counts[idx.flat[s_]] += 1
+    offsets = np.zeros(E + 1, np.int64)
+    for e in range(E):
+        offsets[e + 1] = offsets[e] + counts[e]
+
+    # S3: stable counting sort of the slots by expert
+    cursor = offsets[:E].copy()
+    slot_pos = np.zeros(M, np.int64)
+    row_src = np.zeros(M, np.int64)
+    for t in range(T):
+        for k in range(K):
+            e = idx[t, k]
+            s_ = t * K + k
+            slot_pos[s_] = cursor[e]
+            row_src[cursor[e]] = s_
+            cursor[e] += 1
+    return Routing(keys, idx, gates, counts, offsets, slot_pos, row_src)
+
+
+# ----------------------------------------------------------------------------
+# S4: permute / dispatch into expert-contiguous order (TE-MoE Figure 3 paragraph)
+
+def permute(x: np.ndarray, row_src: np.ndarray, K: int) -> np.ndarray:
+    """X_perm[r] = x[row_src[r] // K]: a copy of the token's row, bits unchanged."""
+    x = np.asarray(x)
+    out = np.empty((len(row_src),) + x.shape[1:], dtype=x.dtype)
+    for r, s_ in enumerate(row_src):
+        out[r] = x[s_ // K]
+    return out
+
+
+# ----------------------------------------------------------------------------
+# S5, S6: the two grouped GEMMs ("Optimisation 1: Grouped GEMM": every expert
+# matmul at its actual token count; here a plain loop over experts)
+
+def grouped_gemm(a: np.ndarray, b: np.ndarray, offsets: np.ndarray, b_layout: str = "nk") -> np.ndarray:
+    """C[rows of group g] = A[rows of g] . B_g^T  (b_layout "nk": B [G, N, Kd])
+    or A[rows of g] . B_g  (b_layout "kn": B [G, Kd, N]); fp64."""
+    A = to_f64(a)
+    B = to_f64(b)
+    G = B.shape[0]
+    N = B.shape[1] if b_layout == "nk" else B.shape[2]
+    C = np.zeros((A.shape[0], N), np.float64)
+    for g in range(G):
+        lo, hi = int(offsets[g]), int(offsets[g + 1])
+        if hi == lo:
+            continue
+        Bg = B[g].T if b_layout == "nk" else B[g]
+        C[lo:hi] = A[lo:hi] @ Bg
+    return C
+
+
+def silu(v: np.ndarray) -> np.ndarray:
+    return v / (1.0 + np.exp(-v))
+
+
+def swiglu(pre: np.ndarray) -> np.ndarray:
+    """h = silu(gate) * up, with pre = [gate | up] along the last axis."""
+    F = pre.shape[-1] // 2
+    return silu(pre[..., :F]) * pre[..., F:]
+
+
+def grouped_wgrad(x: np.ndarray, dy: np.ndarray, offsets: np.ndarray) -> np.ndarray:
+    """dW[g] = dY_g^T . X_g over the rows of group g, [G, N, Kd]; zeros for empty groups."""
+    X = to_f64(x)
+    D = to_f64(dy)
+    G = len(offsets) - 1
+    dW = np.zeros((G, D.shape[1], X.shape[1]), np.float64)
+    for g in range(G):
+        lo, hi = int(offsets[g]), int(offsets[g + 1])
+        if hi > lo:
+            dW[g] = D[lo:hi].T @ X[lo:hi]
+    return dW
+
+
+# ----------------------------------------------------------------------------
+# S7: unpermute + gate-weighted combine (TE-MoE Figure 3 paragraph: combine
+# restores the original token order)
+
+def combine(y_perm: np.ndarray, slot_pos: np.ndarray, gates: np.ndarray | None, T: int, K: int) -> np.ndarray:
+    """Y[t] = sum_{k<K} g_tk * Y_perm[slot_pos[t*K+k]]  (g = 1 when gates is None)."""
+    Yp = to_f64(y_perm)
+    Y = np.zeros((T, Yp.shape[1]), np.float64)
+    for t in range(T):
+        for k in range(K):
+            g = 1.0 if gates is None else float(gates[t, k])
+            Y[t] += g * Yp[slot_pos[t * K + k]]
+    return Y
+
+
+# ----------------------------------------------------------------------------
+# the whole forward layer
+
+def forward(x, w_router, bias, w13, w2, K, score=SCORE_SOFTMAX, renorm=True, logits=None) -> dict:
+    """Router -> dispatch -> two grouped GEMMs -> combine.  Returns every intermediate.
+
+    ``logits`` (fp32 [T, E]) replaces the router product when given."""
+    T = np.asarray(x).shape[0]
+    if logits is None:
+        logits = router_logits(x, w_router)
+    r = route(logits, bias, K, score, renorm)
+    x_perm = permute(x, r.row_src, K)
+    pre = grouped_gemm(x_perm, w13, r.offsets, "nk")          # [M, 2F]
+    h = swiglu(pre)                                           # [M, F]
+    y_perm = grouped_gemm(h, w2, r.offsets, "nk")             # [M, d]
+    y = combine(y_perm, r.slot_pos, r.gates, T, K)
+    return {"logits": logits, "routing": r, "x_perm": x_perm, "pre": pre, "h": h,
+            "y_perm": y_perm, "y": y}
+
+
+def backward(dy, fwd: dict, w13, w2, K) -> dict:
+    """Gradients of <dY, Y> with the routing held fixed.
+
+    B1 combine backward: dY_perm[pos(s)] = g_s dY[t], d_gate_s = <dY[t], Y_perm[pos(s)]>
+    B2 down dgrad + SwiGLU backward: dH = dY_perm_e W2_e, dA = [dG | dU]
+    B3 down wgrad:  dW2_e = dY_perm_e^T H_e
+    B4 gate/up dgrad: dX_perm_e = dA_e W13_e
+    B5 gate/up wgrad: dW13_e = dA_e^T X_perm_e
+    B6 permute backward: dX[t] = sum_k dX_perm[pos(t, k)]
+    """
+    r: Routing = fwd["routing"]
+    dY = to_f64(dy)
+    T = dY.shape[0]
+    M = T * K
+    gates = r.gates
+    y_perm = fwd["y_perm"]
+    dy_perm = np.zeros((M, dY.shape[1]), np.float64)
+    d_gates = np.zeros((T, K), np.float64)
+    for t in range(T):
+        for k in range(K):
+            p = r.slot_pos[t * K + k]
+            dy_perm[p] = gates[t, k] * dY[t]
+            d_gates[t, k] = float(dY[t] @ y_perm[p])
+    pre = fwd["pre"]
+    F = pre.shape[1] // 2
+    dh = grouped_gemm(dy_perm, w2, r.offsets, "kn")           # [M, F]
+    G, U = pre[:, :F], pre[:, F:]
+    sg = 1.0 / (1.0 + np.exp(-G))
+    d_pre = np.concatenate([dh * U * sg * (1.0 + G * (1.0 - sg)), dh * G * sg], axis=1)
+    dw2 = grouped_wgrad(fwd["h"], dy_perm, r.offsets)        # [E, d, F]
+    dx_perm = grouped_gemm(d_pre, w13, r.offsets, "kn")       # [M, d]
+    dw13 = grouped_wgrad(fwd["x_perm"], d_pre, r.offsets)    # [E, 2F, d]
+    dx = combine(dx_perm, r.slot_pos, None, T, K)
+    return {"dy_perm": dy_perm, "d_gates": d_gates, "dh": dh, "d_pre": d_pre, "dw2": dw2,
+            "dx_perm": dx_perm, "dw13": dw13, "dx": dx}
+
+
+# ----------------------------------------------------------------------------
+# independent evaluations used to pin the per-expert loop
+
+def dense_gate_matrix(routing: Routing, E: int) -> np.ndarray:
+    """G[t, e] = gate of expert e for token t, 0 where e was not chosen."""
+    T, K = routing.idx.shape
+    Gm = np.zeros((T, E), np.float64)
+    for t in range(T):
+        for k in range(K):
+            Gm[t, routing.idx[t, k]] = routing.gates[t, k]
+    return Gm
+
+
+def dense_layer(x, gate_matrix: np.ndarray, w13, w2) -> np.ndarray:
+    """Every expert on every token, masked by the dense gate matrix:
+    Y = sum_e G[:, e] * (silu(X Wg_e^T) * (X Wu_e^T)) W2_e^T."""
+    X = to_f64(x)
+    W13 = to_f64(w13)
+    W2 = to_f64(w2)
+    Y = np.zeros((X.shape[0], W2.shape[1]), np.float64)
+    for e in range(W13.shape[0]):
+        Y += gate_matrix[:, e:e + 1] * (swiglu(X @ W13[e].T) @ W2[e].T)
+    return Y
+
+
+def capacity_layer(x, routing: Routing, w13, w2, capacity: int) -> np.ndarray:
+    """Capacity-based contrast (TE-MoE "How is dropless MoE different from
+    capacity-based MoE?"): each expert takes at most ``capacity`` slots in
+    token order and the rest are dropped (contribute zero)."""
+    T, K = routing.idx.shape
+    E = to_f64(w13).shape[0]
+    taken = np.zeros(E, np.int64)
+    Gm = np.zeros((T, E), np.float64)
+    for t in range(T):
+        for k in range(K):
+            e = routing.idx[t, k]
+            if taken[e] < capacity:
+                Gm[t, e] += routing.gates[t, k]
+                taken[e] += 1
+    return dense_layer(x, Gm, w13, w2)

@@ -1,0 +1,388 @@
+"""Pins of the CPU oracle against facts fixed outside the oracle itself.
+
+Each test checks the oracle against a hand-derived value, a closed form, a
+library routine for a special case, brute force on tiny inputs, or an
+invariant of the method, so that a dropped term, a wrong sign or index or a
+transposed operand anywhere in it fails at least one test.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+from scipy.special import expit, softmax
+
+import moe_inputs as mi
+import oracle as orc
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_examples.json")
+
+
+def _tiny(T=48, d=16, E=6, K=2, F=8, seed=11, bias=False):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((T, d)).astype(np.float32)
+    wr = (rng.standard_normal((E, d)) / math.sqrt(d)).astype(np.float32)
+    w13 = (rng.standard_normal((E, 2 * F, d)) / math.sqrt(d)).astype(np.float32)
+    w2 = (rng.standard_normal((E, d, F)) / math.sqrt(F)).astype(np.float32)
+    b = rng.standard_normal(E).astype(np.float32) if bias else None
+    return x, wr, w13, w2, b
+
+
+# ---------------------------------------------------------------- worked examples
+
+def _golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+def test_worked_example_single_expert_swiglu():
+    c = _golden()["single_expert_swiglu"]
+    out = orc.forward(np.array(c["x"], np.float32), None, None, np.array(c["w13"], np.float32),
+                      np.array(c["w2"], np.float32), c["K"], logits=np.array(c["logits"], np.float32))
+    assert out["routing"].idx.tolist() == c["expect_idx"]
+    assert out["routing"].gates.tolist() == c["expect_gates"]
+    np.testing.assert_allclose(out["h"], c["expect_h"], rtol=1e-14)
+    np.testing.assert_allclose(out["y"], c["expect_y"], rtol=1e-14)
+
+
+def test_worked_example_two_tokens_two_experts():
+    c = _golden()["two_tokens_two_experts"]
+    out = orc.forward(np.array(c["x"], np.float32), None, None, np.array(c["w13"], np.float32),
+                      np.array(c["w2"], np.float32), c["K"], logits=np.array(c["logits"], np.float32))
+    r = out["routing"]
+    assert r.idx.tolist() == c["expect_idx"]
+    # ln 3 is rounded to fp32 in the logits, so the gates are 3/4, 1/4 within ~1e-7
+    np.testing.assert_allclose(r.gates, c["expect_gates"], atol=1e-7)
+    assert r.counts.tolist() == c["expect_counts"]
+    assert r.offsets.tolist() == c["expect_offsets"]
+    assert r.row_src.tolist() == c["expect_row_src"]
+    assert r.slot_pos.tolist() == c["expect_slot_pos"]
+    np.testing.assert_allclose(out["y"], c["expect_y"], rtol=1e-6)
+
+
+# ---------------------------------------------------------------- routing
+
+@pytest.mark.parametrize("K", [1, 2, 3, 6])
+@pytest.mark.parametrize("score", [orc.SCORE_SOFTMAX, orc.SCORE_SIGMOID])
+def test_topk_matches_brute_force_over_subsets(K, score):
+    rng = np.random.default_rng(100 + K)
+    T, E = 40, 6
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    r = orc.route(logits, None, K, score)
+    for t in range(T):
+        best = max(itertools.combinations(range(E), K),
+                   key=lambda S: sum(float(logits[t, e]) for e in S))
+        assert set(r.idx[t].tolist()) == set(best)
+        ks = logits[t, r.idx[t]]
+        assert np.all(ks[:-1] > ks[1:]), "chosen experts must be listed by descending key"
+        assert len(set(r.idx[t].tolist())) == K
+
+
+def test_tie_break_lower_expert_first_and_signed_zero():
+    keys = np.array([[1.0, 3.0, 3.0, 2.0]], np.float32)
+    assert orc.route(keys, None, 2).idx.tolist() == [[1, 2]]
+    assert orc.route(keys, None, 3).idx.tolist() == [[1, 2, 3]]
+    z = np.array([[-0.0, 0.0, -1.0]], np.float32)
+    assert orc.route(z, None, 1).idx.tolist() == [[1]]
+    allsame = np.zeros((1, 5), np.float32)
+    assert orc.route(allsame, None, 3).idx.tolist() == [[0, 1, 2]]
+
+
+def test_gates_closed_forms_softmax():
+    rng = np.random.default_rng(7)
+    T, E, K = 30, 8, 3
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    r = orc.route(logits, None, K, orc.SCORE_SOFTMAX, renorm=True)
+    for t in range(T):
+        # renormalised softmax over all E == softmax over the K chosen keys
+        ref = softmax(logits[t, r.idx[t]].astype(np.float64))
+        np.testing.assert_allclose(r.gates[t], ref, rtol=1e-12)
+    np.testing.assert_allclose(r.gates.sum(1), 1.0, rtol=1e-12)
+    # without renormalisation the gates are the full softmax at the chosen experts
+    r2 = orc.route(logits, None, K, orc.SCORE_SOFTMAX, renorm=False)
+    full = softmax(logits.astype(np.float64), axis=1)
+    np.testing.assert_allclose(r2.gates, np.take_along_axis(full, r2.idx.astype(np.int64), 1), rtol=1e-12)
+    # K = E: the renormalised gates are the full softmax in key order
+    r3 = orc.route(logits, None, E)
+    np.testing.assert_allclose(r3.gates, np.take_along_axis(full, r3.idx.astype(np.int64), 1), rtol=1e-12)
+    # K = 1: the gate is exactly 1
+    assert np.all(orc.route(logits, None, 1).gates == 1.0)
+
+
+def test_gates_closed_forms_sigmoid():
+    rng = np.random.default_rng(8)
+    T, E, K = 30, 8, 4
+    logits = (2 * rng.standard_normal((T, E))).astype(np.float32)
+    r = orc.route(logits, None, K, orc.SCORE_SIGMOID, renorm=True)
+    for t in range(T):
+        s = expit(logits[t, r.idx[t]].astype(np.float64))
+        np.testing.assert_allclose(r.gates[t], s / s.sum(), rtol=1e-12)
+    r2 = orc.route(logits, None, K, orc.SCORE_SIGMOID, renorm=False)
+    np.testing.assert_allclose(r2.gates, expit(np.take_along_axis(logits, r2.idx.astype(np.int64), 1)
+                                               .astype(np.float64)), rtol=1e-12)
+
+
+def test_bias_changes_routing_as_predicted():
+    """The bias is a non-weight input of its own: it shifts the keys before the
+    choice and before the scores."""
+    rng = np.random.default_rng(9)
+    T, E, K = 64, 8, 2
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    b = np.zeros(E, np.float32)
+    b[5] = 100.0
+    b[2] = -np.inf
+    r = orc.route(logits, b, K)
+    assert np.all(r.idx[:, 0] == 5)
+    assert not np.any(r.idx == 2)
+    keys = logits + b
+    for t in range(T):
+        np.testing.assert_allclose(r.gates[t], softmax(keys[t, r.idx[t]].astype(np.float64)), rtol=1e-12)
+    # the key add is an fp32 add: the routing sees fp32(logit + bias)
+    assert r.keys.dtype == np.float32 and np.array_equal(r.keys, logits + b)
+
+
+def test_counts_offsets_and_stable_permutation():
+    rng = np.random.default_rng(10)
+    T, E, K = 200, 7, 3
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    logits[:, 4] -= 3.0  # a rarely chosen expert
+    logits[:, 6] = -np.inf  # an expert that gets nothing
+    r = orc.route(logits, None, K)
+    M = T * K
+    assert r.counts.sum() == M
+    assert np.array_equal(r.counts, np.bincount(r.idx.ravel(), minlength=E))
+    assert r.counts[6] == 0
+    assert np.array_equal(r.offsets, np.concatenate([[0], np.cumsum(r.counts)]))
+    assert np.array_equal(r.row_src, np.argsort(r.idx.ravel(), kind="stable"))
+    assert np.array_equal(r.slot_pos[r.row_src], np.arange(M))
+    assert np.array_equal(np.sort(r.slot_pos), np.arange(M))
+    for e in range(E):
+        toks = r.row_src[r.offsets[e]:r.offsets[e + 1]] // K
+        assert np.all(np.diff(toks) > 0)
+
+
+# ---------------------------------------------------------------- permute / combine
+
+def test_permute_is_a_bit_copy():
+    rng = np.random.default_rng(12)
+    T, d, E, K = 50, 24, 5, 2
+    x = mi.f32_to_bf16_bits(rng.standard_normal((T, d)).astype(np.float32))
+    r = orc.route(rng.standard_normal((T, E)).astype(np.float32), None, K)
+    xp = orc.permute(x, r.row_src, K)
+    assert xp.dtype == np.uint16
+    assert np.array_equal(xp, x[r.row_src // K])
+
+
+def test_identity_experts_return_x_times_gate_sum():
+    rng = np.random.default_rng(13)
+    T, d, E, K = 64, 10, 6, 3
+    x = rng.standard_normal((T, d)).astype(np.float32)
+    r = orc.route(rng.standard_normal((T, E)).astype(np.float32), None, K)
+    xp = orc.permute(x, r.row_src, K)
+    y = orc.combine(xp, r.slot_pos, r.gates, T, K)
+    np.testing.assert_allclose(y, x.astype(np.float64) * r.gates.sum(1, keepdims=True), rtol=1e-14)
+    np.testing.assert_allclose(y, x.astype(np.float64), rtol=1e-14)
+    y1 = orc.combine(xp, r.slot_pos, None, T, K)
+    np.testing.assert_array_equal(y1, K * x.astype(np.float64))
+
+
+def test_permute_and_unit_combine_are_adjoint():
+    rng = np.random.default_rng(14)
+    T, d, E, K = 40, 6, 5, 2
+    x = rng.standard_normal((T, d))
+    r = orc.route(rng.standard_normal((T, E)).astype(np.float32), None, K)
+    v = rng.standard_normal((T * K, d))
+    lhs = float((orc.permute(x, r.row_src, K) * v).sum())
+    rhs = float((x * orc.combine(v, r.slot_pos, None, T, K)).sum())
+    assert abs(lhs - rhs) < 1e-12 * max(1.0, abs(lhs))
+
+
+# ---------------------------------------------------------------- grouped GEMM
+
+def test_grouped_gemm_single_group_is_plain_matmul():
+    rng = np.random.default_rng(15)
+    a = rng.standard_normal((37, 12))
+    b = rng.standard_normal((1, 9, 12))
+    np.testing.assert_allclose(orc.grouped_gemm(a, b, np.array([0, 37])), np.matmul(a, b[0].T), rtol=1e-13)
+
+
+def test_grouped_gemm_equal_counts_is_batched_gemm():
+    rng = np.random.default_rng(16)
+    G, m, n, k = 4, 5, 7, 6
+    a = rng.standard_normal((G * m, k))
+    b = rng.standard_normal((G, n, k))
+    ref = np.einsum("gmk,gnk->gmn", a.reshape(G, m, k), b).reshape(G * m, n)
+    np.testing.assert_allclose(orc.grouped_gemm(a, b, np.arange(G + 1) * m), ref, rtol=1e-13)
+    # the K-by-N layout of the same weights gives the same product
+    np.testing.assert_allclose(orc.grouped_gemm(a, np.ascontiguousarray(b.transpose(0, 2, 1)),
+                                                np.arange(G + 1) * m, "kn"), ref, rtol=1e-13)
+
+
+def test_grouped_gemm_scaled_identity_detects_wrong_expert():
+    rng = np.random.default_rng(17)
+    counts = np.array([3, 0, 5, 1, 4])
+    off = np.concatenate([[0], np.cumsum(counts)])
+    d = 8
+    a = rng.standard_normal((off[-1], d))
+    c = np.array([2.0, 4.0, 0.5, 8.0, 0.25])
+    b = np.stack([ci * np.eye(d) for ci in c])
+    out = orc.grouped_gemm(a, b, off)
+    for g in range(5):
+        np.testing.assert_array_equal(out[off[g]:off[g + 1]], c[g] * a[off[g]:off[g + 1]])
+
+
+def test_wgrad_sums_to_one_dense_gemm_and_zero_for_empty_groups():
+    rng = np.random.default_rng(18)
+    counts = np.array([4, 0, 7, 2])
+    off = np.concatenate([[0], np.cumsum(counts)])
+    x = rng.standard_normal((off[-1], 5))
+    dy = rng.standard_normal((off[-1], 3))
+    dW = orc.grouped_wgrad(x, dy, off)
+    assert dW.shape == (4, 3, 5)
+    np.testing.assert_array_equal(dW[1], 0.0)
+    np.testing.assert_allclose(dW.sum(0), dy.T @ x, rtol=1e-12)
+    np.testing.assert_allclose(dW[2], sum(np.outer(dy[i], x[i]) for i in range(off[2], off[3])), rtol=1e-12)
+
+
+def test_swiglu_closed_forms():
+    v = np.array([[0.0, 2.0, -2.0, 40.0, 1.0, 3.0, 5.0, 7.0]])   # gate | up
+    h = orc.swiglu(v)
+    t1 = math.tanh(1.0)
+    np.testing.assert_allclose(h, [[0.0, 2 * (1 + t1) / 2 * 3.0, -2 * (1 - t1) / 2 * 5.0, 40.0 * 7.0]], rtol=1e-14)
+
+
+# ---------------------------------------------------------------- whole layer
+
+@pytest.mark.parametrize("score", [orc.SCORE_SOFTMAX, orc.SCORE_SIGMOID])
+def test_layer_matches_dense_masked_evaluation(score):
+    x, wr, w13, w2, b = _tiny(bias=True)
+    out = orc.forward(x, wr, b, w13, w2, K=2, score=score)
+    ref = orc.dense_layer(x, orc.dense_gate_matrix(out["routing"], 6), w13, w2)
+    np.testing.assert_allclose(out["y"], ref, rtol=1e-11, atol=1e-12)
+
+
+def test_layer_matches_dense_on_tiny_fp32_workload():
+    cfg = mi.CONFIGS["tiny_fp32"]
+    inp = mi.make(cfg)
+    out = orc.forward(inp["x"], inp["w_router"], inp["bias"], inp["w13"], inp["w2"], cfg.K)
+    ref = orc.dense_layer(inp["x"], orc.dense_gate_matrix(out["routing"], cfg.E), inp["w13"], inp["w2"])
+    np.testing.assert_allclose(out["y"], ref, rtol=1e-10, atol=1e-12)
+    assert out["routing"].counts.sum() == cfg.T * cfg.K
+
+
+def test_capacity_contrast():
+    x, wr, w13, w2, _ = _tiny(T=60)
+    out = orc.forward(x, wr, None, w13, w2, K=2)
+    r = out["routing"]
+    big = int(r.counts.max())
+    np.testing.assert_allclose(orc.capacity_layer(x, r, w13, w2, big), out["y"], rtol=1e-11, atol=1e-12)
+    dropped = orc.capacity_layer(x, r, w13, w2, big - 2)
+    assert np.abs(dropped - out["y"]).max() > 1e-3
+
+
+def test_router_logits_on_basis_vectors():
+    rng = np.random.default_rng(19)
+    wr = rng.standard_normal((5, 7)).astype(np.float32)
+    x = np.eye(7, dtype=np.float32)
+    np.testing.assert_array_equal(orc.router_logits(x, wr), wr.T)
+    x2 = np.zeros((1, 7), np.float32)
+    x2[0, 2], x2[0, 4] = 2.0, -0.5
+    np.testing.assert_allclose(orc.router_logits(x2, wr)[0], 2 * wr[:, 2] - 0.5 * wr[:, 4], rtol=1e-6)
+
+
+# ---------------------------------------------------------------- backward
+
+def _fixed_route_loss(x, w13, w2, gm, dy):
+    return float((dy * orc.dense_layer(x, gm, w13, w2)).sum())
+
+
+def test_backward_matches_central_differences():
+    T, d, E, K, F = 6, 5, 3, 2, 4
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((T, d))
+    w13 = rng.standard_normal((E, 2 * F, d)) / math.sqrt(d)
+    w2 = rng.standard_normal((E, d, F)) / math.sqrt(F)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    dy = rng.standard_normal((T, d))
+    fwd = orc.forward(x, None, None, w13, w2, K, logits=logits)
+    bwd = orc.backward(dy, fwd, w13, w2, K)
+    r = fwd["routing"]
+    gm = orc.dense_gate_matrix(r, E)
+    eps = 1e-6
+
+    def fd(arr, fn):
+        g = np.zeros_like(arr)
+        for i in np.ndindex(arr.shape):
+            old = arr[i]
+            arr[i] = old + eps
+            lp = fn()
+            arr[i] = old - eps
+            lm = fn()
+            arr[i] = old
+            g[i] = (lp - lm) / (2 * eps)
+        return g
+
+    loss = lambda: _fixed_route_loss(x, w13, w2, gm, dy)  # noqa: E731
+    np.testing.assert_allclose(bwd["dx"], fd(x, loss), rtol=1e-6, atol=1e-8)
+    np.testing.assert_allclose(bwd["dw13"], fd(w13, loss), rtol=1e-6, atol=1e-8)
+    np.testing.assert_allclose(bwd["dw2"], fd(w2, loss), rtol=1e-6, atol=1e-8)
+    # d_gates: derivative of the loss with respect to each slot's gate value
+    dg = np.zeros((T, K))
+    for t in range(T):
+        for k in range(K):
+            e = r.idx[t, k]
+            old = gm[t, e]
+            gm[t, e] = old + eps
+            lp = loss()
+            gm[t, e] = old - eps
+            lm = loss()
+            gm[t, e] = old
+            dg[t, k] = (lp - lm) / (2 * eps)
+    np.testing.assert_allclose(bwd["d_gates"], dg, rtol=1e-6, atol=1e-8)
+
+
+def test_backward_empty_expert_gets_zero_weight_gradient():
+    T, d, E, K, F = 12, 4, 4, 2, 3
+    rng = np.random.default_rng(22)
+    x = rng.standard_normal((T, d))
+    w13 = rng.standard_normal((E, 2 * F, d))
+    w2 = rng.standard_normal((E, d, F))
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    logits[:, 3] = -np.inf
+    fwd = orc.forward(x, None, None, w13, w2, K, logits=logits)
+    bwd = orc.backward(rng.standard_normal((T, d)), fwd, w13, w2, K)
+    assert fwd["routing"].counts[3] == 0
+    np.testing.assert_array_equal(bwd["dw13"][3], 0.0)
+    np.testing.assert_array_equal(bwd["dw2"][3], 0.0)
+
+
+# ---------------------------------------------------------------- workloads
+
+def test_workload_loads_have_the_documented_shape():
+    """Realised loads on token prefixes: near-uniform (Mixtral-shaped), skewed
+    with empty experts (many small experts), 4 empty experts (DeepSeek-V3 share)."""
+    c2 = mi.CONFIGS["mixtral"]
+    i2 = mi.make(c2, rows=2048, weights=False)
+    r2 = orc.route(orc.router_logits(i2["x"], i2["w_router"]), i2["bias"], c2.K)
+    assert r2.counts.min() > 0.8 * 2048 * 2 / 8 and r2.counts.max() < 1.2 * 2048 * 2 / 8
+
+    c4 = mi.CONFIGS["dsv3_share"]
+    i4 = mi.make(c4, rows=1024, weights=False)
+    r4 = orc.route(orc.router_logits(i4["x"], i4["w_router"]), i4["bias"], c4.K, orc.SCORE_SIGMOID)
+    assert (r4.counts == 0).sum() == 4
+    assert r4.counts.max() > 5 * np.median(r4.counts[r4.counts > 0]) / 2
+
+    c5 = mi.CONFIGS["mixtral_bwd_skew"]
+    hot, dead = mi.skew_choice(c5)
+    lg = mi.skew_logits(orc.router_logits(i2["x"], i2["w_router"]), hot, dead)
+    r5 = orc.route(lg, None, c5.K)
+    assert r5.counts[hot] == 2048 and all(r5.counts[e] == 0 for e in dead)
+
+
+def test_input_prefix_rows_are_reproducible():
+    c = mi.CONFIGS["fine_grained"]
+    a = mi.normal(c.seed, mi.TAG_X, (c.T, c.d), 1.0, True, rows=3000)
+    b = mi.normal(c.seed, mi.TAG_X, (c.T, c.d), 1.0, True, rows=100)
+    assert np.array_equal(a[:100], b)
