@@ -1,0 +1,161 @@
+"""Dropless MoE layer hot path for AMD Instinct MI355X (gfx950).
+
+Thin ctypes binding of ``libmoe.so`` (declared in ``include/moe.h``).  Each
+function has the name of the C entry point it calls and only marshals
+arguments: torch tensors are passed as device pointers and the current HIP
+stream as ``moe_stream_t``.  Every step of the layer runs in the library's HIP
+kernels; there is no other code path.  Importing the package does not load the
+library; the first call does, and raises if ``libmoe.so`` is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe.so")
+
+MOE_OK, MOE_INVALID_ARG, MOE_UNSUPPORTED, MOE_HIP_ERROR = 0, 1, 2, 3
+MOE_F32, MOE_BF16 = 0, 1
+MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
+MOE_LAYOUT_NK, MOE_LAYOUT_KN = 0, 1
+MOE_EPI_NONE, MOE_EPI_SWIGLU, MOE_EPI_DSWIGLU = 0, 1, 2
+MOE_MAX_EXPERTS, MOE_MAX_TOPK, MOE_MAX_GROUPS = 256, 32, 1024
+
+# exported symbols and their C signatures (mirrors include/moe.h)
+_c = ctypes
+_P, _I32, _I64, _SZ = _c.c_void_p, _c.c_int32, _c.c_int64, _c.c_size_t
+SIGNATURES = {
+    "moe_abi_version": (_I32, []),
+    "moe_status_str": (_c.c_char_p, [_I32]),
+    "moe_route_workspace_size": (_I32, [_I64, _I32, _c.POINTER(_SZ)]),
+    "moe_router_logits": (_I32, [_P, _P, _I64, _I64, _I32, _I32, _P, _P]),
+    "moe_route": (_I32, [_P, _P, _I64, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_permute": (_I32, [_P, _I64, _I64, _I32, _I32, _P, _P, _P, _P, _P, _P]),
+    "moe_grouped_gemm": (_I32, [_P, _P, _I32, _P, _I64, _I64, _I64, _I32, _I32, _I32, _P, _P, _P, _P]),
+    "moe_unpermute_combine": (_I32, [_P, _P, _P, _I64, _I64, _I32, _I32, _P, _P]),
+    "moe_grouped_gemm_wgrad": (_I32, [_P, _P, _P, _I64, _I64, _I64, _I32, _I32, _I32, _P, _P]),
+}
+
+_lib = None
+
+
+class MoEError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {status_str(status)} ({status})")
+        self.status = status
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libmoe.so (raises if it was not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise ImportError(f"{path} not found: build it with `python -m dropless_mixture_experts_amd.build`")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(lib, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def _call(name: str, *args) -> None:
+    st = getattr(load_library(), name)(*args)
+    if st != MOE_OK:
+        raise MoEError(name, st)
+
+
+def _ptr(t) -> int | None:
+    """Device pointer of a tensor (None for None)."""
+    if t is None:
+        return None
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    if t.dtype == torch.float32:
+        return MOE_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def moe_abi_version() -> int:
+    return int(load_library().moe_abi_version())
+
+
+def status_str(status: int) -> str:
+    return load_library().moe_status_str(status).decode()
+
+
+moe_status_str = status_str
+
+
+def moe_route_workspace_size(T: int, E: int) -> int:
+    n = ctypes.c_size_t(0)
+    _call("moe_route_workspace_size", T, E, ctypes.byref(n))
+    return int(n.value)
+
+
+def moe_router_logits(x, w_router, logits, stream=None) -> None:
+    """logits[T, E] (fp32) = x[T, d] . w_router[E, d]^T."""
+    T, d = x.shape
+    E = w_router.shape[0]
+    _call("moe_router_logits", _ptr(x), _ptr(w_router), T, d, E, dtype_code(x), _ptr(logits), _stream(stream))
+
+
+def moe_route(logits, bias, K: int, score: int, renorm: bool, topk_idx, topk_gate, counts, offsets,
+              slot_pos, row_src, ws, stream=None) -> None:
+    """Top-K routing + histogram + offsets + stable slot positions (all on the device)."""
+    T, E = logits.shape
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _call("moe_route", _ptr(logits), _ptr(bias), T, E, K, score, int(bool(renorm)), _ptr(topk_idx),
+          _ptr(topk_gate), _ptr(counts), _ptr(offsets), _ptr(slot_pos), _ptr(row_src), _ptr(ws), ws_bytes,
+          _stream(stream))
+
+
+def moe_permute(x, K: int, row_src, x_perm, row_scale=None, y_perm_dot=None, dgate_out=None,
+                stream=None) -> None:
+    """x_perm[r] = (row_scale[s] *) x[s // K] for s = row_src[r]; optional dgate_out[s] = <x[t], y_perm_dot[r]>."""
+    T, d = x.shape
+    _call("moe_permute", _ptr(x), T, d, K, dtype_code(x), _ptr(row_src), _ptr(row_scale), _ptr(y_perm_dot),
+          _ptr(dgate_out), _ptr(x_perm), _stream(stream))
+
+
+def moe_grouped_gemm(A, B, b_layout: int, group_offsets, C, epilogue: int = MOE_EPI_NONE, epi_in=None,
+                     epi_save=None, stream=None) -> None:
+    """One launch over all groups: C_g = epilogue(A_g . B_g^T (NK) or A_g . B_g (KN))."""
+    M, Kd = A.shape
+    G = B.shape[0]
+    N = B.shape[1] if b_layout == MOE_LAYOUT_NK else B.shape[2]
+    _call("moe_grouped_gemm", _ptr(A), _ptr(B), b_layout, _ptr(group_offsets), M, N, Kd, G, dtype_code(A),
+          epilogue, _ptr(epi_in), _ptr(epi_save), _ptr(C), _stream(stream))
+
+
+def moe_unpermute_combine(y_perm, slot_pos, gates, T: int, K: int, y, stream=None) -> None:
+    """y[t] = sum_k gates[t, k] * y_perm[slot_pos[t*K + k]] (gates None: unit weights)."""
+    d = y_perm.shape[1]
+    _call("moe_unpermute_combine", _ptr(y_perm), _ptr(slot_pos), _ptr(gates), T, d, K, dtype_code(y_perm),
+          _ptr(y), _stream(stream))
+
+
+def moe_grouped_gemm_wgrad(X, dY, group_offsets, dW, accumulate: bool = False, stream=None) -> None:
+    """dW[g] (fp32) = dY_g^T . X_g over the rows of group g; zeros for empty groups."""
+    M, Kd = X.shape
+    N = dY.shape[1]
+    G = dW.shape[0]
+    _call("moe_grouped_gemm_wgrad", _ptr(X), _ptr(dY), _ptr(group_offsets), M, N, Kd, G, dtype_code(X),
+          int(bool(accumulate)), _ptr(dW), _stream(stream))
+
+
+from .layer import MoEBuffers, layer_backward, layer_forward  # noqa: E402,F401

@@ -1,0 +1,37 @@
+// Host-side launchers of the gfx950 kernels; called by the C ABI layer after
+// it has validated every argument.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kRouteChunk = 128;  // tokens per workgroup in the routing kernels
+
+size_t route_workspace_bytes(int64_t T, int E);
+
+hipError_t launch_router_logits(const void* x, const void* w, int64_t T, int64_t d, int E, int dtype,
+                                float* logits, hipStream_t s);
+
+hipError_t launch_route(const float* logits, const float* bias, int64_t T, int E, int K, int score,
+                        int renorm, int32_t* topk_idx, float* topk_gate, int32_t* counts,
+                        int32_t* offsets, int32_t* slot_pos, int32_t* row_src, void* ws,
+                        hipStream_t s);
+
+hipError_t launch_permute(const void* x, int64_t T, int64_t d, int K, int dtype, const int32_t* row_src,
+                          const float* row_scale, const void* y_perm_dot, float* dgate_out,
+                          void* x_perm, hipStream_t s);
+
+hipError_t launch_combine(const void* y_perm, const int32_t* slot_pos, const float* gates, int64_t T,
+                          int64_t d, int K, int dtype, void* y, hipStream_t s);
+
+hipError_t launch_grouped_gemm(const void* A, const void* B, int b_layout, const int32_t* offs,
+                               int64_t M, int64_t N, int64_t Kd, int G, int dtype, int epilogue,
+                               const void* epi_in, void* epi_save, void* C, hipStream_t s);
+
+hipError_t launch_grouped_wgrad(const void* X, const void* dY, const int32_t* offs, int64_t M,
+                                int64_t N, int64_t Kd, int G, int dtype, int accumulate, float* dW,
+                                hipStream_t s);
+
+}  // namespace moe

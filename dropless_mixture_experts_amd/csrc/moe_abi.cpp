@@ -1,0 +1,130 @@
+// C ABI of the MoE library: host-side argument checks, then kernel launches on
+// the caller's stream.  Nothing here allocates, synchronises or reads device
+// memory; every rejection happens before the first HIP call.
+#include <hip/hip_runtime.h>
+
+#include "../../include/moe.h"
+#include "internal.h"
+
+namespace {
+
+constexpr int64_t kMaxGroups = MOE_MAX_GROUPS;
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+inline bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+inline bool dtype_ok(int32_t dt) { return dt == MOE_F32 || dt == MOE_BF16; }
+
+inline int32_t from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_HIP_ERROR; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_str(int32_t status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_INVALID_ARG: return "invalid argument";
+    case MOE_UNSUPPORTED: return "unsupported dtype/layout/epilogue combination";
+    case MOE_HIP_ERROR: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+int32_t moe_route_workspace_size(int64_t T, int32_t E, size_t* bytes) {
+  if (!bytes || T < 0 || E < 1 || E > MOE_MAX_EXPERTS) return MOE_INVALID_ARG;
+  *bytes = moe::route_workspace_bytes(T, E);
+  return MOE_OK;
+}
+
+int32_t moe_router_logits(const void* x, const void* w_router, int64_t T, int64_t d, int32_t E,
+                          int32_t dtype, float* logits, moe_stream_t stream) {
+  if (T < 0 || d < 8 || d % 8 != 0 || E < 1 || E > MOE_MAX_EXPERTS) return MOE_INVALID_ARG;
+  if (!dtype_ok(dtype)) return MOE_UNSUPPORTED;
+  if (T >= ((int64_t)1 << 36)) return MOE_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!x || !w_router || !logits) return MOE_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned4(logits)) return MOE_INVALID_ARG;
+  return from_hip(moe::launch_router_logits(x, w_router, T, d, E, dtype, logits, (hipStream_t)stream));
+}
+
+int32_t moe_route(const float* logits, const float* bias, int64_t T, int32_t E, int32_t K,
+                  int32_t score, int32_t renorm, int32_t* topk_idx, float* topk_gate,
+                  int32_t* counts, int32_t* offsets, int32_t* slot_pos, int32_t* row_src,
+                  void* ws, size_t ws_bytes, moe_stream_t stream) {
+  if (T < 0 || E < 1 || E > MOE_MAX_EXPERTS || K < 1 || K > E || K > MOE_MAX_TOPK) return MOE_INVALID_ARG;
+  if (score != MOE_SCORE_SOFTMAX && score != MOE_SCORE_SIGMOID) return MOE_UNSUPPORTED;
+  if (T * (int64_t)K >= ((int64_t)1 << 31)) return MOE_INVALID_ARG;
+  if (!counts || !offsets) return MOE_INVALID_ARG;
+  if (T > 0 && (!logits || !topk_idx || !topk_gate || !slot_pos || !row_src)) return MOE_INVALID_ARG;
+  const size_t need = moe::route_workspace_bytes(T, E);
+  if (ws_bytes < need || (need > 0 && !ws)) return MOE_INVALID_ARG;
+  return from_hip(moe::launch_route(logits, bias, T, E, K, score, renorm != 0, topk_idx, topk_gate,
+                                    counts, offsets, slot_pos, row_src, ws, (hipStream_t)stream));
+}
+
+int32_t moe_permute(const void* x, int64_t T, int64_t d, int32_t K, int32_t dtype,
+                    const int32_t* row_src, const float* row_scale, const void* y_perm_dot,
+                    float* dgate_out, void* x_perm, moe_stream_t stream) {
+  if (T < 0 || d < 8 || d % 8 != 0 || K < 1 || K > MOE_MAX_TOPK) return MOE_INVALID_ARG;
+  if (!dtype_ok(dtype)) return MOE_UNSUPPORTED;
+  if ((y_perm_dot == nullptr) != (dgate_out == nullptr)) return MOE_INVALID_ARG;
+  if (T * (int64_t)K >= ((int64_t)1 << 31)) return MOE_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!x || !row_src || !x_perm) return MOE_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(x_perm) || (y_perm_dot && !aligned16(y_perm_dot))) return MOE_INVALID_ARG;
+  return from_hip(moe::launch_permute(x, T, d, K, dtype, row_src, row_scale, y_perm_dot, dgate_out,
+                                      x_perm, (hipStream_t)stream));
+}
+
+int32_t moe_grouped_gemm(const void* A, const void* B, int32_t b_layout,
+                         const int32_t* group_offsets, int64_t M, int64_t N, int64_t Kd, int32_t G,
+                         int32_t dtype, int32_t epilogue, const void* epi_in, void* epi_save,
+                         void* C, moe_stream_t stream) {
+  if (M < 0 || M >= ((int64_t)1 << 31) || N < 8 || N % 8 != 0 || Kd < 8 || Kd % 8 != 0) return MOE_INVALID_ARG;
+  if (G < 1 || G > kMaxGroups) return MOE_INVALID_ARG;
+  if (!dtype_ok(dtype)) return MOE_UNSUPPORTED;
+  if (b_layout != MOE_LAYOUT_NK && b_layout != MOE_LAYOUT_KN) return MOE_UNSUPPORTED;
+  if (epilogue != MOE_EPI_NONE && epilogue != MOE_EPI_SWIGLU && epilogue != MOE_EPI_DSWIGLU)
+    return MOE_UNSUPPORTED;
+  if (epilogue == MOE_EPI_SWIGLU && (b_layout != MOE_LAYOUT_NK || N % 16 != 0)) return MOE_UNSUPPORTED;
+  if (epilogue == MOE_EPI_DSWIGLU && !epi_in) return MOE_INVALID_ARG;
+  if (!B || !group_offsets) return MOE_INVALID_ARG;
+  if (M == 0) return MOE_OK;
+  if (!A || !C) return MOE_INVALID_ARG;
+  if (!aligned16(A) || !aligned16(B) || !aligned4(group_offsets)) return MOE_INVALID_ARG;
+  if ((epi_in && !aligned16(epi_in)) || (epi_save && !aligned16(epi_save)) || !aligned16(C))
+    return MOE_INVALID_ARG;
+  return from_hip(moe::launch_grouped_gemm(A, B, b_layout, group_offsets, M, N, Kd, G, dtype, epilogue,
+                                           epi_in, epilogue == MOE_EPI_SWIGLU ? epi_save : nullptr, C,
+                                           (hipStream_t)stream));
+}
+
+int32_t moe_unpermute_combine(const void* y_perm, const int32_t* slot_pos, const float* gates,
+                              int64_t T, int64_t d, int32_t K, int32_t dtype, void* y,
+                              moe_stream_t stream) {
+  if (T < 0 || d < 8 || d % 8 != 0 || K < 1 || K > MOE_MAX_TOPK) return MOE_INVALID_ARG;
+  if (!dtype_ok(dtype)) return MOE_UNSUPPORTED;
+  if (T * (int64_t)K >= ((int64_t)1 << 31)) return MOE_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!y_perm || !slot_pos || !y) return MOE_INVALID_ARG;
+  if (!aligned16(y_perm) || !aligned16(y)) return MOE_INVALID_ARG;
+  return from_hip(moe::launch_combine(y_perm, slot_pos, gates, T, d, K, dtype, y, (hipStream_t)stream));
+}
+
+int32_t moe_grouped_gemm_wgrad(const void* X, const void* dY, const int32_t* group_offsets,
+                               int64_t M, int64_t N, int64_t Kd, int32_t G, int32_t dtype,
+                               int32_t accumulate, float* dW, moe_stream_t stream) {
+  if (M < 0 || M >= ((int64_t)1 << 31) || N < 8 || N % 8 != 0 || Kd < 8 || Kd % 8 != 0) return MOE_INVALID_ARG;
+  if (G < 1 || G > kMaxGroups) return MOE_INVALID_ARG;
+  if (!dtype_ok(dtype)) return MOE_UNSUPPORTED;
+  if (!group_offsets || !dW) return MOE_INVALID_ARG;
+  if (M > 0 && (!X || !dY)) return MOE_INVALID_ARG;
+  if ((X && !aligned16(X)) || (dY && !aligned16(dY)) || !aligned4(dW) || !aligned4(group_offsets))
+    return MOE_INVALID_ARG;
+  return from_hip(moe::launch_grouped_wgrad(X, dY, group_offsets, M, N, Kd, G, dtype, accumulate != 0, dW,
+                                            (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,182 @@
+// Dispatch (permute) and combine (unpermute + gate-weighted sum) on one GPU.
+//
+// Tokens move into expert-contiguous order before the grouped MLP and come
+// back to their original order afterwards (page "Accelerating dropless MoE
+// training in JAX with NVIDIA Transformer Engine", Figure 3 paragraph of
+// "What specialised optimisations does dropless MoE need?").  Both are pure
+// HBM streams: one wave moves one row with 16-byte lanes, so every row read
+// and written is a run of full 64-byte segments.
+#include "common.h"
+#include "internal.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kRowsPerBlock = 4;  // one wave per row
+constexpr int kUnroll = 4;        // 16-byte vectors in flight per lane
+
+// x_perm[r] = (scale_s *) x[s / K] for s = row_src[r]; optional dgate_s = <x[s/K], ydot[r]>.
+template <typename T, bool SCALE, bool DOT>
+__global__ __launch_bounds__(256) void permute_kernel(const uint4* __restrict__ x, int64_t nvec, int K,
+                                                      const int32_t* __restrict__ row_src,
+                                                      const float* __restrict__ row_scale,
+                                                      const uint4* __restrict__ ydot,
+                                                      float* __restrict__ dgate,
+                                                      uint4* __restrict__ xp, int64_t M) {
+  using E = Elem<T>;
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (r >= M) return;
+  int64_t s = row_src[r];
+  s = s < 0 ? 0 : (s >= M ? M - 1 : s);  // never leave the buffers, whatever row_src holds
+  const uint4* src = x + (s / K) * nvec;
+  uint4* dst = xp + r * nvec;
+  const uint4* yd = DOT ? ydot + r * nvec : nullptr;
+  const float sc = SCALE ? row_scale[s] : 1.f;
+  float dot = 0.f;
+  for (int64_t i0 = 0; i0 < nvec; i0 += 64 * kUnroll) {
+    uint4 v[kUnroll], w[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t i = i0 + u * 64 + lane;
+      if (i < nvec) {
+        v[u] = src[i];  // a token row is read K times: keep it cacheable
+        if (DOT) w[u] = ld_nt(yd + i);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t i = i0 + u * 64 + lane;
+      if (i < nvec) {
+        uint4 o = v[u];
+        if (SCALE || DOT) {
+          float f[E::kVec];
+          E::to_f32(v[u], f);
+          if (DOT) {
+            float g[E::kVec];
+            E::to_f32(w[u], g);
+#pragma unroll
+            for (int q = 0; q < E::kVec; ++q) dot += f[q] * g[q];
+          }
+          if (SCALE) {
+#pragma unroll
+            for (int q = 0; q < E::kVec; ++q) f[q] *= sc;
+            o = E::from_f32(f);
+          }
+        }
+        st_nt(dst + i, o);
+      }
+    }
+  }
+  if (DOT) {
+    dot = wave_sum(dot);
+    if (lane == 0) dgate[s] = dot;
+  }
+}
+
+// y[t] = sum_k g_tk * y_perm[slot_pos[t*K + k]], fp32 in ascending k, rounded once.
+template <typename T, bool GATES>
+__global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ yp,
+                                                      const int32_t* __restrict__ slot_pos,
+                                                      const float* __restrict__ gates, int64_t ntok,
+                                                      int64_t nvec, int K, uint4* __restrict__ y) {
+  using E = Elem<T>;
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (t >= ntok) return;
+  // lane k holds slot k's row and gate (K <= 32)
+  int pos = 0;
+  float gk = 1.f;
+  const int64_t M = ntok * K;
+  if (lane < K) {
+    pos = slot_pos[t * K + lane];
+    pos = pos < 0 ? 0 : (pos >= M ? (int)(M - 1) : pos);
+    if (GATES) gk = gates[t * K + lane];
+  }
+  for (int64_t i0 = 0; i0 < nvec; i0 += 64 * 2) {
+    float acc[2][E::kVec];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int q = 0; q < E::kVec; ++q) acc[u][q] = 0.f;
+    for (int k = 0; k < K; ++k) {
+      const int64_t p = __shfl(pos, k, 64);
+      const float g = __shfl(gk, k, 64);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int64_t i = i0 + u * 64 + lane;
+        if (i < nvec) {
+          float f[E::kVec];
+          E::to_f32(ld_nt(yp + p * nvec + i), f);
+#pragma unroll
+          for (int q = 0; q < E::kVec; ++q) acc[u][q] = fmaf(g, f[q], acc[u][q]);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int64_t i = i0 + u * 64 + lane;
+      if (i < nvec) st_nt(y + t * nvec + i, E::from_f32(acc[u]));
+    }
+  }
+}
+
+template <typename T>
+hipError_t permute_t(const void* x, int64_t T_, int64_t d, int K, const int32_t* row_src,
+                     const float* row_scale, const void* ydot, float* dgate, void* xp, hipStream_t s) {
+  const int64_t M = T_ * K;
+  if (M == 0) return hipSuccess;
+  const int64_t nvec = d / Elem<T>::kVec;
+  const dim3 grid((unsigned)((M + kRowsPerBlock - 1) / kRowsPerBlock));
+  const uint4* xv = (const uint4*)x;
+  const uint4* yv = (const uint4*)ydot;
+  uint4* o = (uint4*)xp;
+  const bool dot = ydot != nullptr && dgate != nullptr;
+  if (row_scale && dot)
+    hipLaunchKernelGGL((permute_kernel<T, true, true>), grid, dim3(256), 0, s, xv, nvec, K, row_src,
+                       row_scale, yv, dgate, o, M);
+  else if (row_scale)
+    hipLaunchKernelGGL((permute_kernel<T, true, false>), grid, dim3(256), 0, s, xv, nvec, K, row_src,
+                       row_scale, yv, dgate, o, M);
+  else if (dot)
+    hipLaunchKernelGGL((permute_kernel<T, false, true>), grid, dim3(256), 0, s, xv, nvec, K, row_src,
+                       row_scale, yv, dgate, o, M);
+  else
+    hipLaunchKernelGGL((permute_kernel<T, false, false>), grid, dim3(256), 0, s, xv, nvec, K, row_src,
+                       row_scale, yv, dgate, o, M);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t combine_t(const void* yp, const int32_t* slot_pos, const float* gates, int64_t T_, int64_t d,
+                     int K, void* y, hipStream_t s) {
+  if (T_ == 0) return hipSuccess;
+  const int64_t nvec = d / Elem<T>::kVec;
+  const dim3 grid((unsigned)((T_ + kRowsPerBlock - 1) / kRowsPerBlock));
+  if (gates)
+    hipLaunchKernelGGL((combine_kernel<T, true>), grid, dim3(256), 0, s, (const uint4*)yp, slot_pos,
+                       gates, T_, nvec, K, (uint4*)y);
+  else
+    hipLaunchKernelGGL((combine_kernel<T, false>), grid, dim3(256), 0, s, (const uint4*)yp, slot_pos,
+                       gates, T_, nvec, K, (uint4*)y);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_permute(const void* x, int64_t T, int64_t d, int K, int dtype, const int32_t* row_src,
+                          const float* row_scale, const void* y_perm_dot, float* dgate_out,
+                          void* x_perm, hipStream_t s) {
+  if (dtype == 1)
+    return permute_t<bf16_t>(x, T, d, K, row_src, row_scale, y_perm_dot, dgate_out, x_perm, s);
+  return permute_t<float>(x, T, d, K, row_src, row_scale, y_perm_dot, dgate_out, x_perm, s);
+}
+
+hipError_t launch_combine(const void* y_perm, const int32_t* slot_pos, const float* gates, int64_t T,
+                          int64_t d, int K, int dtype, void* y, hipStream_t s) {
+  if (dtype == 1) return combine_t<bf16_t>(y_perm, slot_pos, gates, T, d, K, y, s);
+  return combine_t<float>(y_perm, slot_pos, gates, T, d, K, y, s);
+}
+
+}  // namespace moe

@@ -1,0 +1,290 @@
+// Top-K routing, expert histogram, prefix sum and stable slot positions.
+//
+// The learned router picks the Top-K experts of every token, and every expert
+// then owns a data-dependent, ragged number of slots (page "Accelerating
+// dropless MoE training in JAX with NVIDIA Transformer Engine": introduction
+// and "What are the challenges in MoE training?").  The counts never leave
+// the device ("What specialised optimisations does dropless MoE need?").
+//
+// Three launches, all with shapes fixed on the host:
+//   R1 route_topk_kernel     one workgroup per chunk of 128 tokens.  A group of
+//                            G lanes (G = next power of two >= E, at most 64)
+//                            selects the K largest keys of one token with
+//                            butterfly max-reductions; scores and gates follow.
+//                            The chunk's slots are then ranked stably per
+//                            expert with wave ballots, giving a per-chunk
+//                            histogram and each slot's rank inside its chunk.
+//   R2 route_scan_kernel     one workgroup: per expert, an exclusive scan of
+//                            the chunk histograms; counts and offsets.
+//   R3 route_finalize_kernel slot_pos = offsets[e] + chunk base + rank; row_src.
+#include "common.h"
+#include "internal.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kTopkThreads = 256;
+constexpr int kMaxTopK = 32;
+constexpr int kMaxExperts = 256;
+
+// rank in the total order of fp32 bit patterns: -inf < ... < -0 < +0 < ... < +inf
+__device__ __forceinline__ uint32_t f32_order(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float order_to_f32(uint32_t o) {
+  uint32_t u = (o & 0x80000000u) ? (o & 0x7fffffffu) : ~o;
+  return __uint_as_float(u);
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  lo = __shfl_xor(lo, m, 64);
+  hi = __shfl_xor(hi, m, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int o = 1; o < G; o <<= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// G lanes per token; each lane holds up to KPL keys (expert e = lane + j*G).
+template <int G>
+__global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
+    const float* __restrict__ logits, const float* __restrict__ bias, int T, int E, int K,
+    int score, int renorm, int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate,
+    int32_t* __restrict__ local_rank, int32_t* __restrict__ hist) {
+  constexpr int KPL = (G == 64) ? (kMaxExperts / 64) : 1;
+  constexpr int TPP = kTopkThreads / G;  // tokens per pass
+  __shared__ uint8_t s_sel[kRouteChunk * kMaxTopK];
+  __shared__ uint16_t s_rank[kRouteChunk * kMaxTopK];
+  __shared__ int s_cnt[4][kMaxExperts];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int lig = tid & (G - 1);
+  const int64_t t0 = (int64_t)blockIdx.x * kRouteChunk;
+  const int ntok = (int)min((int64_t)kRouteChunk, (int64_t)T - t0);
+
+  for (int tl = tid / G; tl < ntok; tl += TPP) {
+    const int64_t t = t0 + tl;
+    const float* row = logits + t * E;
+    float kf[KPL];
+    uint64_t comp[KPL];
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+      const int e = lig + j * G;
+      if (e < E) {
+        float v = row[e];
+        if (bias) v = v + bias[e];
+        kf[j] = v;
+        comp[j] = ((uint64_t)f32_order(v) << 32) | (uint32_t)(0xffffffffu - (uint32_t)e);
+      } else {
+        kf[j] = -INFINITY;
+        comp[j] = 0;
+      }
+    }
+    float top_key = 0.f, my_key = 0.f;
+    int my_e = 0;
+    for (int k = 0; k < K; ++k) {
+      uint64_t best = comp[0];
+#pragma unroll
+      for (int j = 1; j < KPL; ++j) best = comp[j] > best ? comp[j] : best;
+#pragma unroll
+      for (int o = 1; o < G; o <<= 1) {
+        const uint64_t other = shfl_xor_u64(best, o);
+        best = other > best ? other : best;
+      }
+      const int e = (int)(0xffffffffu - (uint32_t)best);
+#pragma unroll
+      for (int j = 0; j < KPL; ++j)
+        if (lig + j * G == e) comp[j] = 0;
+      const float key = order_to_f32((uint32_t)(best >> 32));
+      if (k == 0) top_key = key;
+      if (lig == k) {
+        my_e = e;
+        my_key = key;
+      }
+    }
+    float s = 0.f;
+    if (lig < K) s = (score == 1) ? 1.f / (1.f + expf(-my_key)) : expf(my_key - top_key);
+    float denom;
+    if (renorm) {
+      denom = group_sum<G>(s);
+    } else if (score == 0) {
+      float z = 0.f;
+#pragma unroll
+      for (int j = 0; j < KPL; ++j) z += expf(kf[j] - top_key);
+      denom = group_sum<G>(z);
+    } else {
+      denom = 1.f;
+    }
+    if (lig < K) {
+      topk_idx[t * K + lig] = my_e;
+      topk_gate[t * K + lig] = s / denom;
+      s_sel[tl * K + lig] = (uint8_t)my_e;
+    }
+  }
+
+  // ---- stable per-expert ranks of the chunk's slots (slot order = t*K + k)
+  for (int e = lane; e < E; e += 64) s_cnt[wave][e] = 0;
+  __syncthreads();
+  const int n = ntok * K;
+  const int seg = ((n + 255) / 256) * 64;  // slots per wave, a multiple of 64
+  const int beg = wave * seg;
+  const int end = min(n, beg + seg);
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int b = beg; b < end; b += 64) {
+    const int s = b + lane;
+    const bool valid = s < end;
+    const int e = valid ? (int)s_sel[s] : 0;
+    uint64_t eq = __ballot(valid);
+#pragma unroll
+    for (int bit = 0; bit < 8; ++bit) {
+      const uint64_t m = __ballot(valid && ((e >> bit) & 1));
+      eq &= ((e >> bit) & 1) ? m : ~m;
+    }
+    int c = 0;
+    if (valid) {
+      c = s_cnt[wave][e];
+      s_rank[s] = (uint16_t)(c + __popcll(eq & lt_mask));
+    }
+    // the highest lane of each equal-expert set advances that expert's counter
+    if (valid && (eq >> lane) == 1ull) s_cnt[wave][e] = c + __popcll(eq);
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += kTopkThreads) {
+    int run = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int v = s_cnt[w][e];
+      s_cnt[w][e] = run;
+      run += v;
+    }
+    hist[(int64_t)blockIdx.x * E + e] = run;
+  }
+  __syncthreads();
+  for (int s = tid; s < n; s += kTopkThreads) {
+    const int w = s / seg;
+    local_rank[t0 * K + s] = s_cnt[w][s_sel[s]] + s_rank[s];
+  }
+}
+
+// One workgroup of 16 waves.  hist[c][e] (chunk counts) becomes the exclusive
+// prefix of expert e's counts over chunks 0..c-1.
+__global__ __launch_bounds__(1024) void route_scan_kernel(int32_t* __restrict__ hist, int nch, int E,
+                                                          int32_t* __restrict__ counts,
+                                                          int32_t* __restrict__ offsets) {
+  __shared__ int s_tot[kMaxExperts];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  for (int e = wave; e < E; e += 16) {
+    int run = 0;
+    for (int c0 = 0; c0 < nch; c0 += 64) {
+      const int c = c0 + lane;
+      const int v = (c < nch) ? hist[(int64_t)c * E + e] : 0;
+      int inc = v;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int u = __shfl_up(inc, o, 64);
+        if (lane >= o) inc += u;
+      }
+      if (c < nch) hist[(int64_t)c * E + e] = run + inc - v;
+      run += __shfl(inc, 63, 64);
+    }
+    if (lane == 0) s_tot[e] = run;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    int v[4];
+    int loc = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = lane * 4 + j;
+      v[j] = (e < E) ? s_tot[e] : 0;
+      loc += v[j];
+    }
+    int inc = loc;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += u;
+    }
+    int run = inc - loc;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = lane * 4 + j;
+      if (e < E) {
+        counts[e] = v[j];
+        offsets[e] = run;
+      }
+      run += v[j];
+    }
+    if (lane == 63) offsets[E] = inc;
+  }
+}
+
+__global__ __launch_bounds__(256) void route_finalize_kernel(const int32_t* __restrict__ topk_idx,
+                                                             const int32_t* __restrict__ hist,
+                                                             const int32_t* __restrict__ offsets,
+                                                             int64_t M, int K, int E,
+                                                             int32_t* __restrict__ slot_pos,
+                                                             int32_t* __restrict__ row_src) {
+  const int64_t s = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (s >= M) return;
+  const int64_t c = (s / K) / kRouteChunk;
+  const int e = topk_idx[s];
+  const int pos = offsets[e] + hist[c * E + e] + slot_pos[s];
+  slot_pos[s] = pos;
+  if ((uint64_t)pos < (uint64_t)M) row_src[pos] = (int32_t)s;
+}
+
+}  // namespace
+
+size_t route_workspace_bytes(int64_t T, int E) {
+  const int64_t nch = (T + kRouteChunk - 1) / kRouteChunk;
+  return (size_t)(((nch * E * 4) + 255) / 256 * 256);
+}
+
+hipError_t launch_route(const float* logits, const float* bias, int64_t T, int E, int K, int score,
+                        int renorm, int32_t* topk_idx, float* topk_gate, int32_t* counts,
+                        int32_t* offsets, int32_t* slot_pos, int32_t* row_src, void* ws,
+                        hipStream_t s) {
+  const int nch = (int)((T + kRouteChunk - 1) / kRouteChunk);
+  int32_t* hist = (int32_t*)ws;
+  if (nch > 0) {
+    int G = 1;
+    while (G < E && G < 64) G <<= 1;
+#define MOE_TOPK_CASE(g)                                                                       \
+  case g:                                                                                      \
+    hipLaunchKernelGGL(route_topk_kernel<g>, dim3(nch), dim3(kTopkThreads), 0, s, logits, bias, \
+                       (int)T, E, K, score, renorm, topk_idx, topk_gate, slot_pos, hist);      \
+    break;
+    switch (G) {
+      MOE_TOPK_CASE(1)
+      MOE_TOPK_CASE(2)
+      MOE_TOPK_CASE(4)
+      MOE_TOPK_CASE(8)
+      MOE_TOPK_CASE(16)
+      MOE_TOPK_CASE(32)
+      MOE_TOPK_CASE(64)
+      default:
+        return hipErrorInvalidValue;
+    }
+#undef MOE_TOPK_CASE
+  }
+  hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, s, hist, nch, E, counts, offsets);
+  const int64_t M = T * K;
+  if (M > 0) {
+    hipLaunchKernelGGL(route_finalize_kernel, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, s,
+                       topk_idx, hist, offsets, M, K, E, slot_pos, row_src);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

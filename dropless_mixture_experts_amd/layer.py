@@ -1,0 +1,94 @@
+"""The dropless MoE layer as a sequence of C-ABI calls.
+
+Forward (page "Accelerating dropless MoE training in JAX with NVIDIA
+Transformer Engine", Figure 3 paragraph: router -> dispatch -> grouped MLP of
+two grouped GEMMs -> combine):
+    moe_router_logits -> moe_route -> moe_permute
+      -> moe_grouped_gemm (gate/up, SwiGLU epilogue) -> moe_grouped_gemm (down)
+      -> moe_unpermute_combine
+Backward (routing held fixed):
+    moe_permute (gate-scaled dY + d_gates) -> moe_grouped_gemm (KN, SwiGLU backward)
+      -> moe_grouped_gemm_wgrad (dW2) -> moe_grouped_gemm (KN, dX_perm)
+      -> moe_grouped_gemm_wgrad (dW13) -> moe_unpermute_combine (unit weights, dX)
+
+torch provides device memory and the stream; every arithmetic step runs in
+libmoe.so.  Buffers are allocated once per shape and reused, so a forward can
+be captured in a HIP graph and replayed.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import (MOE_EPI_DSWIGLU, MOE_EPI_NONE, MOE_EPI_SWIGLU, MOE_LAYOUT_KN, MOE_LAYOUT_NK,
+               moe_grouped_gemm, moe_grouped_gemm_wgrad, moe_permute, moe_route,
+               moe_route_workspace_size, moe_router_logits, moe_unpermute_combine)
+
+
+class MoEBuffers:
+    """Device buffers of one layer shape."""
+
+    def __init__(self, T: int, d: int, E: int, K: int, F: int, dtype: torch.dtype, device="cuda",
+                 save_pre: bool = False, backward: bool = False):
+        self.T, self.d, self.E, self.K, self.F = T, d, E, K, F
+        M = T * K
+        dev = torch.device(device)
+        i32 = dict(dtype=torch.int32, device=dev)
+        f32 = dict(dtype=torch.float32, device=dev)
+        act = dict(dtype=dtype, device=dev)
+        self.logits = torch.empty((T, E), **f32)
+        self.topk_idx = torch.empty((T, K), **i32)
+        self.gates = torch.empty((T, K), **f32)
+        self.counts = torch.empty((E,), **i32)
+        self.offsets = torch.empty((E + 1,), **i32)
+        self.slot_pos = torch.empty((M,), **i32)
+        self.row_src = torch.empty((M,), **i32)
+        ws = moe_route_workspace_size(T, E)
+        self.ws = torch.empty((max(ws, 256),), dtype=torch.uint8, device=dev)
+        self.x_perm = torch.empty((M, d), **act)
+        self.h = torch.empty((M, F), **act)
+        self.pre = torch.empty((M, 2 * F), **act) if (save_pre or backward) else None
+        self.y_perm = torch.empty((M, d), **act)
+        self.y = torch.empty((T, d), **act)
+        if backward:
+            self.dy_perm = torch.empty((M, d), **act)
+            self.d_gates = torch.empty((T, K), **f32)
+            self.d_pre = torch.empty((M, 2 * F), **act)
+            self.dx_perm = torch.empty((M, d), **act)
+            self.dx = torch.empty((T, d), **act)
+            self.dw13 = torch.empty((E, 2 * F, d), **f32)
+            self.dw2 = torch.empty((E, d, F), **f32)
+
+
+def layer_forward(x, w_router, bias, w13, w2, K: int, score: int, renorm: bool, bufs: MoEBuffers,
+                  logits=None, stream=None):
+    """y = combine(down(SwiGLU(gate_up(permute(x))))) with top-K routing; returns bufs.y.
+
+    ``logits`` (fp32 [T, E]) skips the router product and routes on the given values."""
+    b = bufs
+    if logits is None:
+        moe_router_logits(x, w_router, b.logits, stream=stream)
+        logits = b.logits
+    moe_route(logits, bias, K, score, renorm, b.topk_idx, b.gates, b.counts, b.offsets, b.slot_pos,
+              b.row_src, b.ws, stream=stream)
+    moe_permute(x, K, b.row_src, b.x_perm, stream=stream)
+    moe_grouped_gemm(b.x_perm, w13, MOE_LAYOUT_NK, b.offsets, b.h, MOE_EPI_SWIGLU, epi_save=b.pre,
+                     stream=stream)
+    moe_grouped_gemm(b.h, w2, MOE_LAYOUT_NK, b.offsets, b.y_perm, MOE_EPI_NONE, stream=stream)
+    moe_unpermute_combine(b.y_perm, b.slot_pos, b.gates, b.T, K, b.y, stream=stream)
+    return b.y
+
+
+def layer_backward(dy, w13, w2, K: int, bufs: MoEBuffers, stream=None):
+    """Gradients of <dY, Y> with the routing of the last forward held fixed.
+
+    Returns (dx, dw13, dw2, d_gates) in bufs."""
+    b = bufs
+    moe_permute(dy, K, b.row_src, b.dy_perm, row_scale=b.gates, y_perm_dot=b.y_perm, dgate_out=b.d_gates,
+                stream=stream)
+    moe_grouped_gemm(b.dy_perm, w2, MOE_LAYOUT_KN, b.offsets, b.d_pre, MOE_EPI_DSWIGLU, epi_in=b.pre,
+                     stream=stream)
+    moe_grouped_gemm_wgrad(b.h, b.dy_perm, b.offsets, b.dw2, stream=stream)
+    moe_grouped_gemm(b.d_pre, w13, MOE_LAYOUT_KN, b.offsets, b.dx_perm, MOE_EPI_NONE, stream=stream)
+    moe_grouped_gemm_wgrad(b.x_perm, b.d_pre, b.offsets, b.dw13, stream=stream)
+    moe_unpermute_combine(b.dx_perm, b.slot_pos, None, b.T, K, b.dx, stream=stream)
+    return b.dx, b.dw13, b.dw2, b.d_gates

@@ -1,0 +1,184 @@
+/*
+ * moe.h - C ABI of the dropless mixture-of-experts (MoE) layer hot path for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow the page "Accelerating dropless MoE training in JAX
+ * with NVIDIA Transformer Engine" (cited as TE-MoE):
+ *   - a learned router picks the Top-K experts of every token (introduction;
+ *     "Optimisation 2": fused router kernels assign tokens to experts);
+ *   - tokens are dispatched into expert-contiguous groups of variable length,
+ *     two grouped GEMMs run over those groups, and combine restores the
+ *     original token order (Figure 3 paragraph of "What specialised
+ *     optimisations does dropless MoE need?");
+ *   - no token is dropped and nothing is padded ("How is dropless MoE
+ *     different from capacity-based MoE?");
+ *   - group sizes stay on the device, so no device-to-host copy sits on the
+ *     critical path and the whole layer can be captured in a graph
+ *     ("What specialised optimisations..." and "Optimisation 1: Grouped GEMM").
+ *
+ * Notation: T tokens, d model width, E experts, K experts per token, F expert
+ * FFN width, M = T*K routed slots; slot s = t*K + k.
+ *
+ * Conventions shared by every entry point
+ *   - Pointers marked DEVICE are device memory (hipMalloc / torch CUDA
+ *     tensors) owned by the caller; all tensors are dense row-major
+ *     (C-contiguous) and 16-byte aligned.  The library never allocates,
+ *     frees, synchronises, copies to the host or prints.
+ *   - Every call only enqueues kernels on `stream` (a hipStream_t; NULL is
+ *     the default stream) and returns; calls are capturable in a hipGraph.
+ *   - Return value: MOE_OK, or MOE_INVALID_ARG / MOE_UNSUPPORTED for
+ *     arguments rejected on the host before anything is launched, or
+ *     MOE_HIP_ERROR when a launch fails.  Values that live on the device
+ *     (logits, offsets) are not checked: NaN logits and group offsets that are
+ *     not monotone with offsets[G] == M are the caller's error and give
+ *     undefined results (never an out-of-bounds access for offsets within
+ *     [0, M]).
+ *   - dtype: MOE_F32 or MOE_BF16.  bf16 tensors are stored as 16-bit bf16;
+ *     arithmetic accumulates in fp32 and rounds results to bf16 to nearest
+ *     even.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void* moe_stream_t; /* a hipStream_t */
+
+enum moe_status { MOE_OK = 0, MOE_INVALID_ARG = 1, MOE_UNSUPPORTED = 2, MOE_HIP_ERROR = 3 };
+enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 };
+enum moe_score { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 };
+enum moe_layout { MOE_LAYOUT_NK = 0, MOE_LAYOUT_KN = 1 };
+enum moe_epilogue { MOE_EPI_NONE = 0, MOE_EPI_SWIGLU = 1, MOE_EPI_DSWIGLU = 2 };
+
+#define MOE_ABI_VERSION 1
+#define MOE_MAX_EXPERTS 256
+#define MOE_MAX_TOPK 32
+#define MOE_MAX_GROUPS 1024
+
+/* Version of this ABI (MOE_ABI_VERSION). */
+int32_t moe_abi_version(void);
+
+/* Static string naming a status code; never NULL. */
+const char* moe_status_str(int32_t status);
+
+/*
+ * Bytes of device workspace moe_route needs for T tokens and E experts.
+ * Writes the size to *bytes.  MOE_INVALID_ARG if bytes is NULL, T < 0 or E is
+ * outside [1, MOE_MAX_EXPERTS].
+ */
+int32_t moe_route_workspace_size(int64_t T, int32_t E, size_t* bytes);
+
+/*
+ * Router logits (S0; TE-MoE introduction: the learned router scores experts).
+ *   logits[t, e] = sum_j x[t, j] * w_router[e, j], fp32 accumulation.
+ *   x         DEVICE [T, d]  dtype
+ *   w_router  DEVICE [E, d]  dtype (row e scores expert e)
+ *   logits    DEVICE [T, E]  fp32 (written)
+ * Requires T >= 0, d >= 8 and d % 8 == 0, 1 <= E <= MOE_MAX_EXPERTS.
+ */
+int32_t moe_router_logits(const void* x, const void* w_router, int64_t T, int64_t d, int32_t E,
+                          int32_t dtype, float* logits, moe_stream_t stream);
+
+/*
+ * Top-K routing, expert histogram, prefix sum and stable slot positions
+ * (S1-S3; TE-MoE introduction and "What are the challenges in MoE training?":
+ * every expert gets a data-dependent number of tokens).
+ *   key[t, e] = fp32(logits[t, e] + bias[e])   (key = logit when bias is NULL)
+ *   topk_idx[t, :]  the K experts with the largest keys, by descending key;
+ *                   ties go to the lower expert index; keys compare in the
+ *                   total order of fp32 bit patterns (-0.0 < +0.0)
+ *   score = SOFTMAX: s_e = softmax over all E keys;  SIGMOID: s_e = 1/(1+exp(-key))
+ *   topk_gate[t, k] = s_idx / sum_k' s_idx'  (renorm != 0)  or  s_idx  (renorm == 0)
+ *   counts[e]   = number of slots routed to e;  offsets = exclusive scan, offsets[E] = M
+ *   slot_pos[s] = row of slot s in expert-contiguous order, rows of an expert
+ *                 ordered by ascending slot; row_src[slot_pos[s]] = s
+ *   logits   DEVICE [T, E] fp32;   bias DEVICE [E] fp32 or NULL (-inf masks an expert)
+ *   topk_idx DEVICE [T, K] int32;  topk_gate DEVICE [T, K] fp32
+ *   counts   DEVICE [E] int32;     offsets DEVICE [E+1] int32
+ *   slot_pos, row_src DEVICE [T*K] int32
+ *   ws       DEVICE scratch of at least moe_route_workspace_size(T, E) bytes
+ * Requires 1 <= K <= E <= MOE_MAX_EXPERTS, K <= MOE_MAX_TOPK, T*K < 2^31.
+ * Keys must not be NaN and each token needs a finite key among its K chosen.
+ */
+int32_t moe_route(const float* logits, const float* bias, int64_t T, int32_t E, int32_t K,
+                  int32_t score, int32_t renorm, int32_t* topk_idx, float* topk_gate,
+                  int32_t* counts, int32_t* offsets, int32_t* slot_pos, int32_t* row_src,
+                  void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/*
+ * Permute / dispatch into expert-contiguous order (S4; TE-MoE Figure 3
+ * paragraph), and the combine backward (B1) when the optional arguments are
+ * given.  For every permuted row r with s = row_src[r], t = s / K:
+ *   x_perm[r] = x[t]                                (row_scale == NULL: a bit copy)
+ *   x_perm[r] = round(row_scale[s] * x[t])          (row_scale != NULL)
+ *   dgate_out[s] = sum_j x[t, j] * y_perm_dot[r, j]  (when y_perm_dot and dgate_out are given)
+ *   x          DEVICE [T, d] dtype;   row_src DEVICE [T*K] int32 (a permutation of [0, T*K))
+ *   row_scale  DEVICE [T*K] fp32 or NULL
+ *   y_perm_dot DEVICE [T*K, d] dtype or NULL;  dgate_out DEVICE [T*K] fp32 or NULL (both or neither)
+ *   x_perm     DEVICE [T*K, d] dtype (written)
+ * Requires d % 8 == 0, 1 <= K <= MOE_MAX_TOPK.
+ */
+int32_t moe_permute(const void* x, int64_t T, int64_t d, int32_t K, int32_t dtype,
+                    const int32_t* row_src, const float* row_scale, const void* y_perm_dot,
+                    float* dgate_out, void* x_perm, moe_stream_t stream);
+
+/*
+ * Grouped GEMM over variable-length row groups in one launch (S5/S6 and
+ * backward B2/B4; TE-MoE "Optimisation 1: Grouped GEMM": one kernel call for
+ * all experts, each at its actual token count, computing only valid rows).
+ * Group g owns rows [group_offsets[g], group_offsets[g+1]) of A and C.
+ *   layout NK: B [G, N, Kd],  P = A_g . B_g^T      layout KN: B [G, Kd, N],  P = A_g . B_g
+ *   epilogue NONE:    C [M, N]   = P
+ *   epilogue SWIGLU:  N = 2F is the width of P = [gate | up];
+ *                     C [M, F]   = silu(P[:, :F]) * P[:, F:]
+ *                     epi_save [M, 2F] = P (dtype) when not NULL (kept for backward)
+ *   epilogue DSWIGLU: P = dH [M, N] with N = F; epi_in = saved pre-activations
+ *                     [M, 2F] (G | U);  C [M, 2F] = [dH*U*silu'(G) | dH*silu(G)]
+ *   A DEVICE [M, Kd] dtype;  group_offsets DEVICE [G+1] int32 (read on the device only)
+ * Requires 0 <= M < 2^31, N >= 8, N % 8 == 0 (SWIGLU: N % 16 == 0 and layout NK),
+ * Kd >= 8, Kd % 8 == 0, 1 <= G <= MOE_MAX_GROUPS; epi_in is required for DSWIGLU.
+ * Rows of C outside every group are not written.
+ */
+int32_t moe_grouped_gemm(const void* A, const void* B, int32_t b_layout,
+                         const int32_t* group_offsets, int64_t M, int64_t N, int64_t Kd, int32_t G,
+                         int32_t dtype, int32_t epilogue, const void* epi_in, void* epi_save,
+                         void* C, moe_stream_t stream);
+
+/*
+ * Unpermute + gate-weighted combine back to token order (S7; TE-MoE Figure 3
+ * paragraph: combine restores the original token order), and the permute
+ * backward (B6) with gates == NULL.
+ *   y[t] = round( sum_{k=0..K-1} g[t, k] * y_perm[slot_pos[t*K + k]] )
+ *   accumulated in fp32 in ascending k; g = 1 when gates is NULL.
+ *   y_perm DEVICE [T*K, d] dtype;  slot_pos DEVICE [T*K] int32;  gates DEVICE [T, K] fp32 or NULL
+ *   y      DEVICE [T, d] dtype (written)
+ * Requires d % 8 == 0, 1 <= K <= MOE_MAX_TOPK.
+ */
+int32_t moe_unpermute_combine(const void* y_perm, const int32_t* slot_pos, const float* gates,
+                              int64_t T, int64_t d, int32_t K, int32_t dtype, void* y,
+                              moe_stream_t stream);
+
+/*
+ * Per-group weight gradient with a ragged reduction length (backward B3/B5 of
+ * the grouped GEMMs; the counterpart of "Optimisation 1" for training).
+ *   dW[g] = dY_g^T . X_g  over the rows of group g, dW [G, N, Kd] fp32
+ *   (the same [out, in] layout as the weights); groups without rows get 0
+ *   (accumulate == 0) or are left unchanged (accumulate != 0: dW += ...).
+ *   X DEVICE [M, Kd] dtype;  dY DEVICE [M, N] dtype;  group_offsets DEVICE [G+1] int32
+ * Deterministic: no atomics, fixed summation order.
+ * X and dY may be NULL when M == 0.
+ * Requires 0 <= M < 2^31, N >= 8, N % 8 == 0, Kd >= 8, Kd % 8 == 0, 1 <= G <= MOE_MAX_GROUPS.
+ */
+int32_t moe_grouped_gemm_wgrad(const void* X, const void* dY, const int32_t* group_offsets,
+                               int64_t M, int64_t N, int64_t Kd, int32_t G, int32_t dtype,
+                               int32_t accumulate, float* dW, moe_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H_ */

@@ -161,18 +161,18 @@ def permute(x: np.ndarray, row_src: np.ndarray, K: int) -> np.ndarray:
 
 def grouped_gemm(a: np.ndarray, b: np.ndarray, offsets: np.ndarray, b_layout: str = "nk") -> np.ndarray:
     """C[rows of group g] = A[rows of g] . B_g^T  (b_layout "nk": B [G, N, Kd])
-    or A[rows of g] . B_g  (b_layout "kn": B [G, Kd, N]); fp64."""
+    or A[rows of g] . B_g  (b_layout "kn": B [G, Kd, N]); fp64.  Weights are
+    widened to fp64 one group at a time, and only for groups that own rows."""
     A = to_f64(a)
-    B = to_f64(b)
-    G = B.shape[0]
-    N = B.shape[1] if b_layout == "nk" else B.shape[2]
+    G = b.shape[0]
+    N = b.shape[1] if b_layout == "nk" else b.shape[2]
     C = np.zeros((A.shape[0], N), np.float64)
     for g in range(G):
         lo, hi = int(offsets[g]), int(offsets[g + 1])
         if hi == lo:
             continue
-        Bg = B[g].T if b_layout == "nk" else B[g]
-        C[lo:hi] = A[lo:hi] @ Bg
+        Bg = to_f64(b[g])
+        C[lo:hi] = A[lo:hi] @ (Bg.T if b_layout == "nk" else Bg)
     return C
 
 
@@ -214,6 +214,32 @@ def combine(y_perm: np.ndarray, slot_pos: np.ndarray, gates: np.ndarray | None, 
     return Y
 
 
+def combine_backward(dy, y_perm, slot_pos, gates, T: int, K: int):
+    """Adjoint of the gate-weighted combine:
+    dY_perm[slot_pos[s]] = g_s dY[t] and d_gate_s = <dY[t], Y_perm[slot_pos[s]]>."""
+    dY = to_f64(dy)
+    Yp = to_f64(y_perm)
+    dy_perm = np.zeros((T * K, dY.shape[1]), np.float64)
+    d_gates = np.zeros((T, K), np.float64)
+    for t in range(T):
+        for k in range(K):
+            p = slot_pos[t * K + k]
+            dy_perm[p] = float(gates[t, k]) * dY[t]
+            d_gates[t, k] = float(dY[t] @ Yp[p])
+    return dy_perm, d_gates
+
+
+def swiglu_backward(dh, pre):
+    """d[gate | up] of h = silu(gate) * up:  dG = dH U silu'(G), dU = dH silu(G),
+    with silu'(G) = s (1 + G (1 - s)), s = sigmoid(G)."""
+    dH = to_f64(dh)
+    P = to_f64(pre)
+    F = P.shape[1] // 2
+    G, U = P[:, :F], P[:, F:]
+    sg = 1.0 / (1.0 + np.exp(-G))
+    return np.concatenate([dH * U * sg * (1.0 + G * (1.0 - sg)), dH * G * sg], axis=1)
+
+
 # ----------------------------------------------------------------------------
 # the whole forward layer
 
@@ -245,24 +271,11 @@ def backward(dy, fwd: dict, w13, w2, K) -> dict:
     B6 permute backward: dX[t] = sum_k dX_perm[pos(t, k)]
     """
     r: Routing = fwd["routing"]
-    dY = to_f64(dy)
-    T = dY.shape[0]
-    M = T * K
-    gates = r.gates
-    y_perm = fwd["y_perm"]
-    dy_perm = np.zeros((M, dY.shape[1]), np.float64)
-    d_gates = np.zeros((T, K), np.float64)
-    for t in range(T):
-        for k in range(K):
-            p = r.slot_pos[t * K + k]
-            dy_perm[p] = gates[t, k] * dY[t]
-            d_gates[t, k] = float(dY[t] @ y_perm[p])
+    T = np.asarray(dy).shape[0]
+    dy_perm, d_gates = combine_backward(dy, fwd["y_perm"], r.slot_pos, r.gates, T, K)
     pre = fwd["pre"]
-    F = pre.shape[1] // 2
     dh = grouped_gemm(dy_perm, w2, r.offsets, "kn")           # [M, F]
-    G, U = pre[:, :F], pre[:, F:]
-    sg = 1.0 / (1.0 + np.exp(-G))
-    d_pre = np.concatenate([dh * U * sg * (1.0 + G * (1.0 - sg)), dh * G * sg], axis=1)
+    d_pre = swiglu_backward(dh, pre)
     dw2 = grouped_wgrad(fwd["h"], dy_perm, r.offsets)        # [E, d, F]
     dx_perm = grouped_gemm(d_pre, w13, r.offsets, "kn")       # [M, d]
     dw13 = grouped_wgrad(fwd["x_perm"], d_pre, r.offsets)    # [E, 2F, d]
@@ -286,13 +299,15 @@ def dense_gate_matrix(routing: Routing, E: int) -> np.ndarray:
 
 def dense_layer(x, gate_matrix: np.ndarray, w13, w2) -> np.ndarray:
     """Every expert on every token, masked by the dense gate matrix:
-    Y = sum_e G[:, e] * (silu(X Wg_e^T) * (X Wu_e^T)) W2_e^T."""
+    Y = sum_e G[:, e] * (silu(X Wg_e^T) * (X Wu_e^T)) W2_e^T.
+    (Experts whose gate column is all zero add nothing and are skipped.)"""
     X = to_f64(x)
-    W13 = to_f64(w13)
-    W2 = to_f64(w2)
-    Y = np.zeros((X.shape[0], W2.shape[1]), np.float64)
-    for e in range(W13.shape[0]):
-        Y += gate_matrix[:, e:e + 1] * (swiglu(X @ W13[e].T) @ W2[e].T)
+    E = w13.shape[0]
+    Y = np.zeros((X.shape[0], w2.shape[1]), np.float64)
+    for e in range(E):
+        if not np.any(gate_matrix[:, e]):
+            continue
+        Y += gate_matrix[:, e:e + 1] * (swiglu(X @ to_f64(w13[e]).T) @ to_f64(w2[e]).T)
     return Y
 
 
@@ -301,7 +316,7 @@ def capacity_layer(x, routing: Routing, w13, w2, capacity: int) -> np.ndarray:
     capacity-based MoE?"): each expert takes at most ``capacity`` slots in
     token order and the rest are dropped (contribute zero)."""
     T, K = routing.idx.shape
-    E = to_f64(w13).shape[0]
+    E = w13.shape[0]
     taken = np.zeros(E, np.int64)
     Gm = np.zeros((T, E), np.float64)
     for t in range(T):

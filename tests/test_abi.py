@@ -1,0 +1,119 @@
+"""CPU checks of the C ABI: the library loads, exports every entry point that
+include/moe.h declares, and rejects bad arguments on the host before any
+launch.  No kernel runs here."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import dropless_mixture_experts_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int32_t|const char\*)\s+(moe_\w+)\s*\(", src, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return moe.load_library()
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for n in ["moe_route", "moe_permute", "moe_grouped_gemm", "moe_unpermute_combine",
+              "moe_grouped_gemm_wgrad", "moe_router_logits", "moe_route_workspace_size",
+              "moe_status_str", "moe_abi_version"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", moe.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\sT\s+(moe_\w+)$", out, re.M))
+    for n in _declared():
+        assert n in exported, n
+        assert hasattr(lib, n)
+    assert set(moe.SIGNATURES) == set(_declared())
+
+
+def test_version_and_status_strings(lib):
+    assert moe.moe_abi_version() == 1
+    assert moe.status_str(0) == "ok"
+    assert "invalid" in moe.status_str(1)
+    assert moe.status_str(99) == "unknown status"
+
+
+def test_route_workspace_size():
+    assert moe.moe_route_workspace_size(0, 8) == 0
+    assert moe.moe_route_workspace_size(8192, 8) == 64 * 8 * 4
+    assert moe.moe_route_workspace_size(129, 3) == 256
+    with pytest.raises(moe.MoEError):
+        moe.moe_route_workspace_size(10, 0)
+    with pytest.raises(moe.MoEError):
+        moe.moe_route_workspace_size(10, 257)
+
+
+P = 1 << 20  # a fake, 16-byte aligned "device" address: never dereferenced on these paths
+
+
+def test_route_rejects_bad_arguments(lib):
+    ok_ws = 1 << 20
+    args = lambda **kw: dict(dict(logits=P, bias=None, T=100, E=8, K=2, score=0, renorm=1, idx=P, gate=P,  # noqa
+                                  counts=P, offsets=P, pos=P, src=P, ws=P, wsb=ok_ws), **kw)
+
+    def call(a):
+        return lib.moe_route(a["logits"], a["bias"], a["T"], a["E"], a["K"], a["score"], a["renorm"],
+                             a["idx"], a["gate"], a["counts"], a["offsets"], a["pos"], a["src"], a["ws"],
+                             a["wsb"], None)
+    assert call(args(K=9)) == 1           # K > E
+    assert call(args(K=0)) == 1
+    assert call(args(E=257, K=2)) == 1    # too many experts
+    assert call(args(E=64, K=33)) == 1    # K above the top-K limit
+    assert call(args(T=-1)) == 1
+    assert call(args(score=2)) == 2       # unknown score function
+    assert call(args(logits=None)) == 1
+    assert call(args(counts=None)) == 1
+    assert call(args(wsb=16)) == 1        # workspace too small
+    assert call(args(ws=None)) == 1
+    assert call(args(T=1 << 28, K=8)) == 1  # T*K >= 2^31
+
+
+def test_gemm_rejects_bad_arguments(lib):
+    def call(A=P, B=P, lay=0, offs=P, M=512, N=256, Kd=128, G=4, dt=1, epi=0, ein=None, esave=None, C=P):
+        return lib.moe_grouped_gemm(A, B, lay, offs, M, N, Kd, G, dt, epi, ein, esave, C, None)
+    assert call(N=12) == 1
+    assert call(Kd=4) == 1
+    assert call(G=0) == 1
+    assert call(G=moe.MOE_MAX_GROUPS + 1) == 1
+    assert call(dt=7) == 2
+    assert call(lay=2) == 2
+    assert call(epi=3) == 2
+    assert call(epi=1, lay=1) == 2        # SwiGLU epilogue needs the N-by-K weight layout
+    assert call(epi=1, N=24) == 2         # gate|up halves must be 8-aligned
+    assert call(epi=2, ein=None) == 1     # SwiGLU backward needs the saved pre-activations
+    assert call(A=P + 4) == 1             # misaligned
+    assert call(C=None) == 1
+    assert call(M=-1) == 1
+    assert call(M=0) == 0                 # nothing to do: returns before any launch
+
+
+def test_wgrad_permute_combine_reject_bad_arguments(lib):
+    assert lib.moe_grouped_gemm_wgrad(P, P, P, 64, 12, 16, 2, 1, 0, P, None) == 1
+    assert lib.moe_grouped_gemm_wgrad(P, P, None, 64, 16, 16, 2, 1, 0, P, None) == 1
+    assert lib.moe_grouped_gemm_wgrad(P, P, P, 64, 16, 16, 2, 5, 0, P, None) == 2
+    assert lib.moe_permute(P, 10, 12, 2, 1, P, None, None, None, P, None) == 1     # d % 8
+    assert lib.moe_permute(P, 10, 16, 2, 1, P, None, P, None, P, None) == 1        # dot without output
+    assert lib.moe_permute(P, 10, 16, 33, 1, P, None, None, None, P, None) == 1    # K limit
+    assert lib.moe_permute(P, 0, 16, 2, 1, None, None, None, None, None, None) == 0  # empty: no launch
+    assert lib.moe_unpermute_combine(P, P, None, 10, 16, 0, 1, P, None) == 1
+    assert lib.moe_unpermute_combine(P, None, None, 10, 16, 2, 1, P, None) == 1
+    assert lib.moe_unpermute_combine(None, None, None, 0, 16, 2, 1, None, None) == 0
+    assert lib.moe_router_logits(P, P, 10, 16, 0, 1, P, None) == 1
+    assert lib.moe_router_logits(P, P, 10, 20, 8, 1, P, None) == 1
+    assert lib.moe_router_logits(P, P, 10, 16, 8, 3, P, None) == 2
+    assert lib.moe_router_logits(None, None, 0, 16, 8, 1, None, None) == 0
