@@ -66,7 +66,7 @@ template <> struct Mma<float> {
 // Loader of an operand whose rows are K-contiguous: LDS row r <- global row ptr_r.
 // Thread tid moves chunk (tid & 7) of rows (tid >> 3) + 32 i, i < 8.
 struct RowLoader {
-  const char* ptr[8];
+  const char* ptr[8];  // start of each row (K offset 0)
   int64_t kbytes;  // K extent in bytes
   int c;
   uint4 reg[8];
@@ -335,7 +335,7 @@ void grouped_gemm_kernel(GemmParams p) {
     for (int i = 0; i < 8; ++i) {
       int64_t row = m0 + (tid >> 3) + 32 * i;
       row = row < p.M ? row : p.M - 1;
-      la.ptr[i] = A + row * p.Kd * esz + la.c * 16;
+      la.ptr[i] = A + row * p.Kd * esz;
     }
   }
   f32x16 acc[4][4];
@@ -357,7 +357,7 @@ void grouped_gemm_kernel(GemmParams p) {
         n = (int64_t)nt * kTile + r;
         n = n < p.N ? n : p.N - 1;
       }
-      lb.ptr[i] = Bg + n * p.Kd * esz + lb.c * 16;
+      lb.ptr[i] = Bg + n * p.Kd * esz;
     }
     mainloop<T, EPI>(la, lb, nk, smem, acc);
   } else {
