@@ -1,0 +1,203 @@
+"""Benchmark of the dropless MoE layer forward on one MI355X.
+
+One step = the whole forward hot path over one batch of synthetic tokens:
+router logits -> top-K routing (histogram, offsets, stable positions) ->
+permute -> grouped GEMM gate/up + SwiGLU -> grouped GEMM down -> combine.
+Inputs and weights are resident in HBM before the timed region.
+
+Prints ONE JSON line.  value = tokens/s of the layer forward; the roofline
+object reports the dominant kernel (the gate/up grouped GEMM) against the
+bf16 dense MFMA peak, with its duration measured by HIP events on the stream
+the kernels run on; cpu_baseline times the CPU oracle on a bounded sample of
+the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3       # MI355X fp32 (matrix)
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixtral",
+                    choices=["mixtral", "fine_grained", "dsv3_share", "tiny_fp32"])
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target duration of the CPU-oracle sample (0 disables it)")
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="per-launch HBM bytes measured with rocprofv3 counters, if present")
+    return ap.parse_args()
+
+
+def to_dev(a, torch):
+    if a is None:
+        return None
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def cpu_baseline(cfg, inp, target_s: float) -> dict | None:
+    """The CPU oracle (never tuned) on the first S tokens of the same workload."""
+    if target_s <= 0:
+        return None
+    import oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+
+    def run(S):
+        t0 = time.perf_counter()
+        orc.forward(inp["x"][:S], inp["w_router"], inp["bias"], inp["w13"], inp["w2"], cfg.K, cfg.score,
+                    cfg.renorm)
+        return time.perf_counter() - t0
+
+    S = min(64, cfg.T)
+    dt = run(S)
+    # widening the weights to fp64 is a fixed cost per call; scale the token count for the rest
+    S2 = int(min(cfg.T, max(S, S * target_s / max(dt, 1e-3))))
+    if S2 > S:
+        S, dt = S2, run(S2)
+    return {"value": S / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"first {S} of {cfg.T} tokens of the {cfg.name} workload, full forward "
+                      f"(router, top-K, permute, per-expert fp64 GEMMs, combine) in {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import dropless_mixture_experts_amd as moe
+    import moe_inputs as mi
+
+    cfg = mi.CONFIGS[args.workload]
+    torch.cuda.set_device(0)
+    t_gen = time.perf_counter()
+    inp = mi.make(cfg)
+    gen_s = time.perf_counter() - t_gen
+    dt = torch.bfloat16 if cfg.bf16 else torch.float32
+    x, wr, b = to_dev(inp["x"], torch), to_dev(inp["w_router"], torch), to_dev(inp["bias"], torch)
+    w13, w2 = to_dev(inp["w13"], torch), to_dev(inp["w2"], torch)
+    bufs = moe.MoEBuffers(cfg.T, cfg.d, cfg.E, cfg.K, cfg.F, dt)
+    stream = torch.cuda.current_stream()
+
+    names = ["router", "route", "permute", "gemm_gate_up", "gemm_down", "combine"]
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record(stream)
+        mark(0)
+        moe.moe_router_logits(x, wr, bufs.logits)
+        mark(1)
+        moe.moe_route(bufs.logits, b, cfg.K, cfg.score, cfg.renorm, bufs.topk_idx, bufs.gates, bufs.counts,
+                      bufs.offsets, bufs.slot_pos, bufs.row_src, bufs.ws)
+        mark(2)
+        moe.moe_permute(x, cfg.K, bufs.row_src, bufs.x_perm)
+        mark(3)
+        moe.moe_grouped_gemm(bufs.x_perm, w13, moe.MOE_LAYOUT_NK, bufs.offsets, bufs.h, moe.MOE_EPI_SWIGLU)
+        mark(4)
+        moe.moe_grouped_gemm(bufs.h, w2, moe.MOE_LAYOUT_NK, bufs.offsets, bufs.y_perm, moe.MOE_EPI_NONE)
+        mark(5)
+        moe.moe_unpermute_combine(bufs.y_perm, bufs.slot_pos, bufs.gates, cfg.T, cfg.K, bufs.y)
+        mark(6)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K whole steps; HIP events on the launch stream bracket every kernel call
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / max(args.steps, 1)
+    per = np.zeros(len(names))
+    for ev in evs:
+        per += np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(6)])
+    per /= max(args.steps, 1)
+    kms = dict(zip(names, per.tolist()))
+
+    M = cfg.T * cfg.K
+    esz = 2 if cfg.bf16 else 4
+    flops_up = 2.0 * M * (2 * cfg.F) * cfg.d
+    flops_down = 2.0 * M * cfg.F * cfg.d
+    peak = PEAK_BF16_TFLOPS if cfg.bf16 else PEAK_F32_TFLOPS
+    tf_up = flops_up / (kms["gemm_gate_up"] * 1e-3) / 1e12
+    tf_down = flops_down / (kms["gemm_down"] * 1e-3) / 1e12
+    tf_gg = (flops_up + flops_down) / ((kms["gemm_gate_up"] + kms["gemm_down"]) * 1e-3) / 1e12
+    perm_bytes = (cfg.T + M) * cfg.d * esz + 4 * M
+    comb_bytes = (M + cfg.T) * cfg.d * esz + 8 * M
+    router_bytes = cfg.T * cfg.d * esz + cfg.E * cfg.d * esz + 4 * cfg.T * cfg.E
+
+    traffic = None
+    try:
+        with open(args.traffic) as f:
+            tr = json.load(f)
+        key = f"{cfg.name}/gemm_gate_up"
+        if key in tr:
+            traffic = tr[key]["bytes_per_launch"]
+    except (OSError, ValueError, KeyError):
+        traffic = None
+
+    tokens_per_s = cfg.T / (ms_per_step * 1e-3)
+    counts = bufs.counts.cpu().numpy()
+    cpu = cpu_baseline(cfg, inp, args.cpu_seconds)
+
+    out = {
+        "metric": "MoE layer forward tokens/s (grouped-GEMM TFLOP/s and % of bf16 MFMA peak alongside)",
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.bf16 else "f32",
+        "data": "synthetic (seeded N(0,1) tokens, random-init router and SwiGLU experts)",
+        "config": {"workload": cfg.name, "tokens": cfg.T, "d_model": cfg.d, "experts": cfg.E, "top_k": cfg.K,
+                   "ffn": cfg.F, "score": "sigmoid" if cfg.score else "softmax", "renorm": cfg.renorm,
+                   "parallelism": "single GPU"},
+        "grouped_gemm": {"tflops": tf_gg, "frac_of_peak": tf_gg / peak, "gate_up_tflops": tf_up,
+                         "down_tflops": tf_down, "flops_per_step": flops_up + flops_down},
+        "kernels_ms": kms,
+        "hbm_gbs": {"permute": perm_bytes / (kms["permute"] * 1e-3) / 1e9,
+                    "combine": comb_bytes / (kms["combine"] * 1e-3) / 1e9,
+                    "router": router_bytes / (kms["router"] * 1e-3) / 1e9},
+        "load": {"min": int(counts.min()), "max": int(counts.max()), "empty": int((counts == 0).sum())},
+        "roofline": {"kernel": "grouped GEMM gate/up + SwiGLU", "bound": "mfma", "achieved": tf_up,
+                     "peak": peak, "unit": "TFLOP/s", "frac": tf_up / peak, "traffic": traffic},
+        "cpu_baseline": cpu,
+        "input_generation_s": gen_s,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -12,8 +12,8 @@
 //     for fp32 inputs).
 //   * K is staged through LDS 128 bytes per row at a time, two stages
 //     (2 x 64 KB); rows are 8 chunks of 16 bytes with the chunk index XORed by
-//     (row & 7), so both the 16-byte LDS writes and the MFMA operand reads hit
-//     distinct banks.  The next stage's global loads are in flight while the
+//     a function of the row, so both the 16-byte LDS writes and the MFMA
+//     operand reads hit distinct banks.  The next stage's global loads are in flight while the
 //     current stage is multiplied.
 //   * Operands stored K-contiguous are copied chunk for chunk; operands stored
 //     with K as the row index (the K-by-N weight layout of the data-gradient
@@ -44,7 +44,12 @@ constexpr int kGroupM = 8;                 // row tiles that share a column tile
 enum { EPI_NONE = 0, EPI_SWIGLU = 1, EPI_DSWIGLU = 2 };
 enum { LAYOUT_NK = 0, LAYOUT_KN = 1 };
 
-__device__ __forceinline__ int swz(int row, int c) { return row * kCPR + (c ^ (row & 7)); }
+// LDS chunk index of (row, 16-byte chunk c).  The XOR pattern g(row) = (row & 7) ^ ((row >> 3) & 1)
+// makes the 16 lanes that one LDS cycle serves (16 consecutive rows, one logical chunk:
+// the MFMA operand reads) and the row-major writes (2 rows x 8 chunks) hit 16 distinct
+// 16-byte bank groups of a 256-byte-wide LDS, and any 8 consecutive rows distinct ones too.
+__device__ __forceinline__ int swz_x(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+__device__ __forceinline__ int swz(int row, int c) { return row * kCPR + (c ^ swz_x(row)); }
 
 template <typename T> struct Mma;
 template <> struct Mma<bf16_t> {
@@ -71,12 +76,16 @@ struct RowLoader {
   int c;
   uint4 reg[8];
 
+  // branch-free: a chunk past the K extent reads an in-row address and is replaced by zeros
   __device__ __forceinline__ void load(int stage) {
-    const int64_t off = (int64_t)stage * kRowBytes + c * 16;
+    int64_t off = (int64_t)stage * kRowBytes + c * 16;
     const bool ok = off < kbytes;
+    off = ok ? off : kbytes - 16;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      reg[i] = ok ? *(const uint4*)(ptr[i] + off) : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < 8; ++i) {
+      const uint4 v = *(const uint4*)(ptr[i] + off);
+      reg[i] = ok ? v : make_uint4(0, 0, 0, 0);
+    }
   }
   __device__ __forceinline__ void store(uint4* lds) const {
     const int r0 = threadIdx.x >> 3;
@@ -116,17 +125,19 @@ struct ColLoader {
     }
   }
 
+  // branch-free: rows past k_end and column blocks past ncols read an in-range
+  // address of the same operand and are replaced by zeros
   __device__ __forceinline__ void load(int stage) {
     constexpr int BK = kRowBytes / Elem<T>::kBytes;
 #pragma unroll
     for (int p = 0; p < PB; ++p) {
-      const int64_t n = n0 + (int64_t)nb[p] * VE;
+      const int64_t n = n_valid[p] ? n0 + (int64_t)nb[p] * VE : n0;
 #pragma unroll
       for (int v = 0; v < VE; ++v) {
         const int64_t k = k_begin + (int64_t)stage * BK + kb[p] * VE + v;
-        reg[p][v] = (n_valid[p] && k < k_end)
-                        ? *(const uint4*)(base + k * ld + n * Elem<T>::kBytes)
-                        : make_uint4(0, 0, 0, 0);
+        const bool ok = n_valid[p] && k < k_end;
+        const uint4 val = *(const uint4*)(base + (ok ? k : k_begin) * ld + n * Elem<T>::kBytes);
+        reg[p][v] = ok ? val : make_uint4(0, 0, 0, 0);
       }
     }
   }
@@ -167,9 +178,42 @@ __device__ __forceinline__ void ColLoader<float>::store(uint4* lds) const {
   }
 }
 
+// Instruction order of one main-loop stage (scheduler groups, in order):
+// operand reads of sub-step 0, the next stage's global loads, operand reads of
+// sub-step 1, then each sub-step's MFMAs with the following sub-step's operand
+// reads behind them; the next stage's LDS writes are spread through the MFMAs
+// of sub-steps 2 and 3.
+enum { SG_MFMA = 0x008, SG_VMEM_READ = 0x020, SG_DS_READ = 0x100, SG_DS_WRITE = 0x200 };
+template <typename T>
+__device__ __forceinline__ void schedule_stage() {
+  constexpr int kMfmaPerSub = 16 * (Elem<T>::kVec == 8 ? 1 : 4);
+  __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 8, 0);
+  __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, 16, 0);
+  __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 8, 0);
+  __builtin_amdgcn_sched_group_barrier(SG_MFMA, kMfmaPerSub, 0);
+  __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 8, 0);
+  __builtin_amdgcn_sched_group_barrier(SG_MFMA, kMfmaPerSub, 0);
+  __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 8, 0);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, kMfmaPerSub / 8, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_DS_WRITE, 1, 0);
+  }
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, kMfmaPerSub / 8, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_DS_WRITE, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(SG_MFMA, kMfmaPerSub, 0);
+}
+
 // ---------------------------------------------------------------------------
-// Double-buffered main loop: acc[i][j] += A-tile rows x B-tile rows over nk stages.
-// BROW(wn, j) gives the first LDS row of B fragment j of wave column wn.
+// Main loop: acc[i][j] += A-tile rows x B-tile rows over nk stages of 128 K-bytes.
+// LDS holds two stages.  Within a stage the four 16-byte K sub-steps use two
+// register sets of MFMA operands, so the LDS reads of sub-step kk+1 are in
+// flight while sub-step kk multiplies; the global loads of the next stage are
+// issued at the top of the stage and written to the other LDS buffer during
+// the last sub-step.  The loop body has no branches.
 template <typename T, int EPI, typename LA, typename LB>
 __device__ __forceinline__ void mainloop(LA& la, LB& lb, int nk, uint4* smem, f32x16 (&acc)[4][4]) {
   const int lane = threadIdx.x & 63;
@@ -184,45 +228,261 @@ __device__ __forceinline__ void mainloop(LA& la, LB& lb, int nk, uint4* smem, f3
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
   if (nk <= 0) return;
 
-  int arow[4], brow[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) arow[i] = wm * 128 + i * 32 + l32;
+  // every operand row a lane reads is l32 plus a multiple of 32: one XOR for all fragments
+  const int x = swz_x(l32);
+  const int a_row8 = (wm * 128 + l32) * kCPR;
+  int b_row8[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j)
-    brow[j] = (EPI == EPI_SWIGLU ? ((j >> 1) * 128 + wn * 64 + (j & 1) * 32) : (wn * 128 + j * 32)) + l32;
+    b_row8[j] = ((EPI == EPI_SWIGLU ? ((j >> 1) * 128 + wn * 64 + (j & 1) * 32) : (wn * 128 + j * 32)) + l32) * kCPR;
+
+  auto read = [&](const uint4* As, const uint4* Bs, int kk, uint4 (&a)[4], uint4 (&b)[4]) {
+    const int cc = (2 * kk + hi) ^ x;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = As[a_row8 + i * 32 * kCPR + cc];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = Bs[b_row8[j] + cc];
+  };
+  auto mma16 = [&](const uint4 (&a)[4], const uint4 (&b)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) Mma<T>::run(a[i], b[j], acc[i][j]);
+  };
 
   la.load(0);
   lb.load(0);
   la.store(smem);
   lb.store(smem + kTileChunks);
   __syncthreads();
+  uint4 fa0[4], fb0[4], fa1[4], fb1[4];
   for (int s = 0; s < nk; ++s) {
     const uint4* As = smem + (s & 1) * 2 * kTileChunks;
     const uint4* Bs = As + kTileChunks;
-    const bool more = s + 1 < nk;
-    if (more) {
-      la.load(s + 1);
-      lb.load(s + 1);
-    }
-#pragma unroll
-    for (int kk = 0; kk < kCPR / 2; ++kk) {
-      const int c = 2 * kk + hi;
-      uint4 a[4], b[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = As[swz(arow[i], c)];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = Bs[swz(brow[j], c)];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) Mma<T>::run(a[i], b[j], acc[i][j]);
-    }
-    if (more) {
-      uint4* An = smem + ((s + 1) & 1) * 2 * kTileChunks;
-      la.store(An);
-      lb.store(An + kTileChunks);
-    }
+    uint4* An = smem + ((s + 1) & 1) * 2 * kTileChunks;
+    const int sn = s + 1 < nk ? s + 1 : s;  // the last stage reloads itself into the idle buffer
+    read(As, Bs, 0, fa0, fb0);
+    la.load(sn);
+    lb.load(sn);
+    read(As, Bs, 1, fa1, fb1);
+    mma16(fa0, fb0);
+    read(As, Bs, 2, fa0, fb0);
+    mma16(fa1, fb1);
+    read(As, Bs, 3, fa1, fb1);
+    mma16(fa0, fb0);
+    la.store(An);
+    lb.store(An + kTileChunks);
+    mma16(fa1, fb1);
+    schedule_stage<T>();
     __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// LDS-DMA main loop for operands whose rows are K-contiguous (the forward
+// N-by-K weight layout).  global_load_lds_dwordx4 moves 16 bytes per lane from
+// global memory straight into LDS (lane L lands at M0 + 16 L), so no VGPRs or
+// LDS write instructions are spent on staging and several stages can be in
+// flight: 4 LDS stages of 64 K-bytes per row, each stage's loads issued three
+// stages before it is consumed.  Rows are 4 chunks of 16 bytes, the chunk
+// index XORed with (row >> 2) & 3, which keeps the 16 lanes of one LDS cycle
+// (16 consecutive rows, one chunk) on distinct bank groups.  The DMA is issued
+// through inline assembly so that the compiler does not serialise every LDS
+// read behind it; completion is tracked with explicit vmcnt waits and one
+// workgroup barrier per stage.
+constexpr int kDmaStages = 4;
+constexpr int kDmaRowBytes = 64;
+constexpr int kDmaCPR = kDmaRowBytes / 16;          // 4 chunks per row
+constexpr int kDmaOpUnits = kTile * kDmaCPR;        // 1024 chunks = 16 KB per operand per stage
+constexpr int kDmaStageUnits = 2 * kDmaOpUnits;     // A then B
+
+__device__ __forceinline__ int dswz_x(int row) { return (row >> 2) & 3; }
+
+__device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_byte) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(lds_byte), "v"(gptr) : "memory", "m0");
+}
+__device__ __forceinline__ void wait_vmcnt_8() { asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); }
+__device__ __forceinline__ void wait_vmcnt_16() { asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); }
+__device__ __forceinline__ void wait_vmcnt_0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// asrc[q] / bsrc[q]: global address, at K offset 0, of the 16 bytes this lane moves
+// with DMA instruction q of operand A / B (LDS rows (wave*4 + q)*16 + lane/4).
+template <typename T, int EPI>
+__device__ __forceinline__ void mainloop_dma(const char* const (&asrc)[4], const char* const (&bsrc)[4],
+                                             int nk, uint4* smem, f32x16 (&acc)[4][4]) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l32 = lane & 31, hi = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  if (nk <= 0) return;
+
+  const uint32_t wbase = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)smem + wave * 4 * 1024);
+  auto issue = [&](int st) {
+    const uint32_t lb = wbase + (uint32_t)(st & (kDmaStages - 1)) * (kDmaStageUnits * 16);
+    const int64_t koff = (int64_t)st * kDmaRowBytes;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) lds_dma16(asrc[q] + koff, lb + q * 1024);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) lds_dma16(bsrc[q] + koff, lb + kDmaOpUnits * 16 + q * 1024);
+  };
+
+  const int x = dswz_x(l32);
+  const int a_row4 = (wm * 128 + l32) * kDmaCPR;
+  int b_row4[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    b_row4[j] = kDmaOpUnits +
+                ((EPI == EPI_SWIGLU ? ((j >> 1) * 128 + wn * 64 + (j & 1) * 32) : (wn * 128 + j * 32)) + l32) * kDmaCPR;
+  auto read = [&](int st, int kk, uint4 (&a)[4], uint4 (&b)[4]) {
+    const uint4* S = smem + (st & (kDmaStages - 1)) * kDmaStageUnits;
+    const int cc = (2 * kk + hi) ^ x;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = S[a_row4 + i * 32 * kDmaCPR + cc];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = S[b_row4[j] + cc];
+  };
+  auto mma16 = [&](const uint4 (&a)[4], const uint4 (&b)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) Mma<T>::run(a[i], b[j], acc[i][j]);
+  };
+
+  issue(0);
+  if (nk > 1) issue(1);
+  if (nk > 2) issue(2);
+  if (nk > 2) wait_vmcnt_16();
+  else if (nk > 1) wait_vmcnt_8();
+  else wait_vmcnt_0();
+  __syncthreads();
+  uint4 fa0[4], fb0[4], fa1[4], fb1[4];
+  read(0, 0, fa0, fb0);
+  int s = 0;
+  // steady state, straight-line so that LDS read counts stay exact: stage s+1 has
+  // landed for this thread after vmcnt(8); after the barrier it has for every thread,
+  // and every wave has finished reading stage s-1, whose buffer stage s+3 reuses
+  for (; s + 3 < nk; ++s) {
+    read(s, 1, fa1, fb1);
+    mma16(fa0, fb0);
+    wait_vmcnt_8();
+    __syncthreads();
+    issue(s + 3);
+    read(s + 1, 0, fa0, fb0);
+    mma16(fa1, fb1);
+  }
+  // drain the last (up to three) stages
+  for (; s < nk; ++s) {
+    read(s, 1, fa1, fb1);
+    mma16(fa0, fb0);
+    if (s + 1 < nk) {
+      if (s + 2 < nk) wait_vmcnt_8();
+      else wait_vmcnt_0();
+      __syncthreads();
+      read(s + 1, 0, fa0, fb0);
+    }
+    mma16(fa1, fb1);
+  }
+}
+
+// Eight-wave variant of the LDS-DMA main loop: two waves per SIMD, each owning a
+// 128 x 64 block of the 256 x 256 tile (4 x 2 MFMA tiles, 128 accumulators).  A
+// single wave per SIMD cannot pull LDS operands fast enough to keep its MFMA
+// pipe busy; two waves per SIMD double the LDS read rate, and each wave's MFMAs
+// cover the other's LDS, barrier and memory waits.  Stage and DMA layout are
+// those of mainloop_dma; each thread issues 2 + 2 DMA per stage.
+constexpr int kThreads8 = 512;
+__device__ __forceinline__ void wait_vmcnt_4() { asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); }
+
+template <typename T, int EPI>
+__device__ __forceinline__ void mainloop8_dma(const char* const (&asrc)[2], const char* const (&bsrc)[2],
+                                              int nk, uint4* smem, f32x16 (&acc)[4][2]) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave >> 2, wn = wave & 3;
+  const int l32 = lane & 31, hi = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  if (nk <= 0) return;
+
+  const uint32_t wbase = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)smem + wave * 2 * 1024);
+  auto issue = [&](int st) {
+    const uint32_t lb = wbase + (uint32_t)(st & (kDmaStages - 1)) * (kDmaStageUnits * 16);
+    const int64_t koff = (int64_t)st * kDmaRowBytes;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) lds_dma16(asrc[q] + koff, lb + q * 1024);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) lds_dma16(bsrc[q] + koff, lb + kDmaOpUnits * 16 + q * 1024);
+  };
+
+  const int x = dswz_x(l32);
+  const int a_row4 = (wm * 128 + l32) * kDmaCPR;
+  int b_row4[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    b_row4[j] = kDmaOpUnits + ((EPI == EPI_SWIGLU ? (j * 128 + wn * 32) : (wn * 64 + j * 32)) + l32) * kDmaCPR;
+  auto read = [&](int st, int kk, uint4 (&a)[4], uint4 (&b)[2]) {
+    const uint4* S = smem + (st & (kDmaStages - 1)) * kDmaStageUnits;
+    const int cc = (2 * kk + hi) ^ x;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = S[a_row4 + i * 32 * kDmaCPR + cc];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) b[j] = S[b_row4[j] + cc];
+  };
+  auto mma8 = [&](const uint4 (&a)[4], const uint4 (&b)[2]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) Mma<T>::run(a[i], b[j], acc[i][j]);
+  };
+
+  issue(0);
+  if (nk > 1) issue(1);
+  if (nk > 2) issue(2);
+  if (nk > 2) wait_vmcnt_8();
+  else if (nk > 1) wait_vmcnt_4();
+  else wait_vmcnt_0();
+  __syncthreads();
+  uint4 fa0[4], fb0[2], fa1[4], fb1[2];
+  read(0, 0, fa0, fb0);
+  int s = 0;
+  constexpr int kMfmaPer8 = 8 * (Elem<T>::kVec == 8 ? 1 : 4);
+  for (; s + 3 < nk; ++s) {
+    // region 1: operand reads of sub-step 1, then the MFMAs of sub-step 0
+    read(s, 1, fa1, fb1);
+    mma8(fa0, fb0);
+    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 6, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, kMfmaPer8, 0);
+    __builtin_amdgcn_sched_barrier(0);  // keep those MFMAs ahead of the workgroup barrier
+    wait_vmcnt_4();
+    __syncthreads();
+    // region 2: next stage's DMA and its sub-step-0 reads, then the MFMAs of sub-step 1
+    issue(s + 3);
+    read(s + 1, 0, fa0, fb0);
+    mma8(fa1, fb1);
+    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 6, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, kMfmaPer8, 0);
+  }
+  for (; s < nk; ++s) {
+    read(s, 1, fa1, fb1);
+    mma8(fa0, fb0);
+    if (s + 1 < nk) {
+      if (s + 2 < nk) wait_vmcnt_4();
+      else wait_vmcnt_0();
+      __syncthreads();
+      read(s + 1, 0, fa0, fb0);
+    }
+    mma8(fa1, fb1);
   }
 }
 
@@ -253,19 +513,74 @@ struct GemmParams {
   int NT;  // column tiles
 };
 
-template <typename T, int BL, int EPI>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void grouped_gemm_kernel(GemmParams p) {
-  __shared__ uint4 smem[4 * kTileChunks];
-  __shared__ int s_wtot[4];
-  __shared__ int s_res[2];
+// Epilogue of one wave: acc[i][j] is the 32 x 32 tile at rows row0 + 32 i and
+// columns col[j]; a lane holds column (lane & 31) and rows 8 (r/4) + 4 (lane/32) + r%4.
+// SwiGLU: fragments j < NJ/2 are gate columns and j + NJ/2 the matching up columns.
+template <typename T, int EPI, int NI, int NJ>
+__device__ __forceinline__ void store_tile(const GemmParams& p, const f32x16 (&acc)[NI][NJ], int64_t row0,
+                                           int64_t re, const int64_t (&col)[NJ]) {
   using E = Elem<T>;
+  const int lane = threadIdx.x & 63;
+  const int l32 = lane & 31, hi = lane >> 5;
+  if constexpr (EPI == EPI_SWIGLU) {
+    const int64_t F = p.N / 2;
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ / 2; ++j) {
+        const int64_t c = col[j] + l32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t row = row0 + i * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+          if (row < re && c < F) {
+            const float gt = acc[i][j][r], up = acc[i][j + NJ / 2][r];
+            E::store1(p.C, row * F + c, gt / (1.f + __expf(-gt)) * up);
+            if (p.epi_save) {
+              E::store1(p.epi_save, row * p.N + c, gt);
+              E::store1(p.epi_save, row * p.N + F + c, up);
+            }
+          }
+        }
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int64_t c = col[j] + l32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t row = row0 + i * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+          if (row < re && c < p.N) {
+            const float v = acc[i][j][r];
+            if (EPI == EPI_NONE) {
+              E::store1(p.C, row * p.N + c, v);
+            } else {  // SwiGLU backward: v = dH; saved pre-activations [G | U] of width 2N
+              const float gt = E::load1(p.epi_in, row * 2 * p.N + c);
+              const float up = E::load1(p.epi_in, row * 2 * p.N + p.N + c);
+              const float sg = 1.f / (1.f + __expf(-gt));
+              E::store1(p.C, row * 2 * p.N + c, v * up * sg * (1.f + gt * (1.f - sg)));
+              E::store1(p.C, row * 2 * p.N + p.N + c, v * gt * sg);
+            }
+          }
+        }
+      }
+  }
+}
+
+// Block -> (group, first row, column tile) from the group offsets in device
+// memory; false when this workgroup has no tile.  Uniform over the workgroup.
+template <int NTHR>
+__device__ __forceinline__ bool find_tile(const GemmParams& p, int& g_out, int64_t& m0_out, int64_t& re_out,
+                                          int& nt_out) {
+  constexpr int NW = NTHR / 64;
+  __shared__ int s_wtot[NW];
+  __shared__ int s_res[2];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-
-  // ---- row tiles per group and their prefix sum (group counts stay on the device)
-  const int gpt = (p.G + kThreads - 1) / kThreads;
+  // row tiles per group and their prefix sum
+  const int gpt = (p.G + NTHR - 1) / NTHR;
   const int g0 = tid * gpt;
   int local = 0;
   for (int g = g0; g < g0 + gpt && g < p.G; ++g) {
@@ -287,14 +602,14 @@ void grouped_gemm_kernel(GemmParams p) {
   __syncthreads();
   int total_mt = 0;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
+  for (int w = 0; w < NW; ++w) {
     const int v = s_wtot[w];
     if (w < wave) incl += v;
     total_mt += v;
   }
   const int excl = incl - local;
   const int64_t total = (int64_t)total_mt * p.NT;
-  if ((int64_t)blockIdx.x >= total) return;  // uniform over the workgroup
+  if ((int64_t)blockIdx.x >= total) return false;
 
   const int64_t L = xcd_remap(blockIdx.x, total);
   const int64_t per = (int64_t)kGroupM * p.NT;
@@ -303,7 +618,7 @@ void grouped_gemm_kernel(GemmParams p) {
   const int gm = min(total_mt - first, kGroupM);
   const int rem = (int)(L - grp * per);
   const int mt = first + rem % gm;
-  const int nt = rem / gm;
+  nt_out = rem / gm;
   if (excl <= mt && mt < incl) {
     int run = excl;
     for (int g = g0; g < g0 + gpt && g < p.G; ++g) {
@@ -322,97 +637,128 @@ void grouped_gemm_kernel(GemmParams p) {
   const int g = min(max(s_res[0], 0), p.G - 1);
   int64_t rs, re;
   group_rows(p.offs, g, p.M, rs, re);
-  const int64_t m0 = rs + (int64_t)s_res[1] * kTile;
+  g_out = g;
+  m0_out = rs + (int64_t)s_res[1] * kTile;
+  re_out = re;
+  return true;
+}
 
-  // ---- operand loaders
+template <typename T, int BL, int EPI, bool DMA>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void grouped_gemm_kernel(GemmParams p) {
+  __shared__ uint4 smem[4 * kTileChunks];
+  using E = Elem<T>;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  int g, nt;
+  int64_t m0, re;
+  if (!find_tile<kThreads>(p, g, m0, re, nt)) return;
+
+  // ---- operands
   const int64_t esz = E::kBytes;
-  RowLoader la;
-  la.c = tid & 7;
-  la.kbytes = p.Kd * esz;
-  {
-    const char* A = (const char*)p.A;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      int64_t row = m0 + (tid >> 3) + 32 * i;
-      row = row < p.M ? row : p.M - 1;
-      la.ptr[i] = A + row * p.Kd * esz;
-    }
-  }
   f32x16 acc[4][4];
-  const int nk = (int)((p.Kd * esz + kRowBytes - 1) / kRowBytes);
-  if constexpr (BL == LAYOUT_NK) {
-    RowLoader lb;
-    lb.c = tid & 7;
-    lb.kbytes = p.Kd * esz;
-    const char* Bg = (const char*)p.B + (int64_t)g * p.N * p.Kd * esz;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = (tid >> 3) + 32 * i;
-      int64_t n;
-      if (EPI == EPI_SWIGLU) {
-        const int64_t F = p.N / 2;
-        const int64_t c = (int64_t)nt * 128 + (r & 127);
-        n = (r < 128 ? 0 : F) + (c < F ? c : F - 1);
-      } else {
-        n = (int64_t)nt * kTile + r;
-        n = n < p.N ? n : p.N - 1;
-      }
-      lb.ptr[i] = Bg + n * p.Kd * esz;
+  const char* A = (const char*)p.A;
+  // global row of B (weights of group g) that LDS row r of the tile holds
+  auto b_row = [&](int r) -> int64_t {
+    if (EPI == EPI_SWIGLU) {
+      const int64_t F = p.N / 2;
+      const int64_t c = (int64_t)nt * 128 + (r & 127);
+      return (r < 128 ? 0 : F) + (c < F ? c : F - 1);
     }
-    mainloop<T, EPI>(la, lb, nk, smem, acc);
+    const int64_t n = (int64_t)nt * kTile + r;
+    return n < p.N ? n : p.N - 1;
+  };
+  auto a_row = [&](int r) -> int64_t {
+    const int64_t row = m0 + r;
+    return row < p.M ? row : p.M - 1;
+  };
+  if constexpr (DMA) {
+    const char* Bg = (const char*)p.B + (int64_t)g * p.N * p.Kd * esz;
+    const char* asrc[4];
+    const char* bsrc[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = (wave * 4 + q) * 16 + (lane >> 2);
+      const int c = (lane & 3) ^ dswz_x(r);
+      asrc[q] = A + a_row(r) * p.Kd * esz + c * 16;
+      bsrc[q] = Bg + b_row(r) * p.Kd * esz + c * 16;
+    }
+    mainloop_dma<T, EPI>(asrc, bsrc, (int)(p.Kd * esz / kDmaRowBytes), smem, acc);
   } else {
-    ColLoader<T> lb;
-    lb.init((const char*)p.B + (int64_t)g * p.Kd * p.N * esz, p.N, (int64_t)nt * kTile, p.N, 0, p.Kd);
-    mainloop<T, EPI>(la, lb, nk, smem, acc);
+    RowLoader la;
+    la.c = tid & 7;
+    la.kbytes = p.Kd * esz;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) la.ptr[i] = A + a_row((tid >> 3) + 32 * i) * p.Kd * esz;
+    const int nk = (int)((p.Kd * esz + kRowBytes - 1) / kRowBytes);
+    if constexpr (BL == LAYOUT_NK) {
+      RowLoader lb;
+      lb.c = tid & 7;
+      lb.kbytes = p.Kd * esz;
+      const char* Bg = (const char*)p.B + (int64_t)g * p.N * p.Kd * esz;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) lb.ptr[i] = Bg + b_row((tid >> 3) + 32 * i) * p.Kd * esz;
+      mainloop<T, EPI>(la, lb, nk, smem, acc);
+    } else {
+      ColLoader<T> lb;
+      lb.init((const char*)p.B + (int64_t)g * p.Kd * p.N * esz, p.N, (int64_t)nt * kTile, p.N, 0, p.Kd);
+      mainloop<T, EPI>(la, lb, nk, smem, acc);
+    }
   }
 
-  // ---- epilogue: lane holds column (lane & 31) and rows 8*(r/4) + 4*(lane/32) + r%4 of each 32x32 tile
+  // ---- epilogue
   const int wm = wave >> 1, wn = wave & 1;
-  const int l32 = lane & 31, hi = lane >> 5;
-  if constexpr (EPI == EPI_SWIGLU) {
-    const int64_t F = p.N / 2;
+  int64_t col[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+  for (int j = 0; j < 4; ++j)
+    col[j] = EPI == EPI_SWIGLU ? (int64_t)nt * 128 + wn * 64 + (j & 1) * 32 : (int64_t)nt * kTile + wn * 128 + j * 32;
+  store_tile<T, EPI, 4, 4>(p, acc, m0 + wm * 128, re, col);
+}
+
+// Eight-wave grouped GEMM for the N-by-K weight layout with whole 64-byte K stages.
+template <typename T, int EPI>
+__global__ __launch_bounds__(kThreads8) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void grouped_gemm8_kernel(GemmParams p) {
+  __shared__ uint4 smem[kDmaStages * kDmaStageUnits];
+  using E = Elem<T>;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  int g, nt;
+  int64_t m0, re;
+  if (!find_tile<kThreads8>(p, g, m0, re, nt)) return;
+  const int64_t esz = E::kBytes;
+  const char* A = (const char*)p.A;
+  const char* Bg = (const char*)p.B + (int64_t)g * p.N * p.Kd * esz;
+  const char* asrc[2];
+  const char* bsrc[2];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int64_t col = (int64_t)nt * 128 + wn * 64 + j * 32 + l32;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t row = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-          if (row < re && col < F) {
-            const float gt = acc[i][j][r], up = acc[i][j + 2][r];
-            E::store1(p.C, row * F + col, gt / (1.f + __expf(-gt)) * up);
-            if (p.epi_save) {
-              E::store1(p.epi_save, row * p.N + col, gt);
-              E::store1(p.epi_save, row * p.N + F + col, up);
-            }
-          }
-        }
-      }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t col = (int64_t)nt * kTile + wn * 128 + j * 32 + l32;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t row = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-          if (row < re && col < p.N) {
-            const float v = acc[i][j][r];
-            if (EPI == EPI_NONE) {
-              E::store1(p.C, row * p.N + col, v);
-            } else {  // DSWIGLU: v = dH; saved pre-activations [G | U] of width 2N
-              const float gt = E::load1(p.epi_in, row * 2 * p.N + col);
-              const float up = E::load1(p.epi_in, row * 2 * p.N + p.N + col);
-              const float sg = 1.f / (1.f + __expf(-gt));
-              E::store1(p.C, row * 2 * p.N + col, v * up * sg * (1.f + gt * (1.f - sg)));
-              E::store1(p.C, row * 2 * p.N + p.N + col, v * gt * sg);
-            }
-          }
-        }
-      }
+  for (int q = 0; q < 2; ++q) {
+    const int r = (wave * 2 + q) * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ dswz_x(r);
+    int64_t ar = m0 + r;
+    ar = ar < p.M ? ar : p.M - 1;
+    int64_t br;
+    if (EPI == EPI_SWIGLU) {
+      const int64_t F = p.N / 2;
+      const int64_t cc = (int64_t)nt * 128 + (r & 127);
+      br = (r < 128 ? 0 : F) + (cc < F ? cc : F - 1);
+    } else {
+      br = (int64_t)nt * kTile + r;
+      br = br < p.N ? br : p.N - 1;
+    }
+    asrc[q] = A + ar * p.Kd * esz + c * 16;
+    bsrc[q] = Bg + br * p.Kd * esz + c * 16;
   }
+  f32x16 acc[4][2];
+  mainloop8_dma<T, EPI>(asrc, bsrc, (int)(p.Kd * esz / kDmaRowBytes), smem, acc);
+  const int wm = wave >> 2, wn = wave & 3;
+  int64_t col[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    col[j] = EPI == EPI_SWIGLU ? (int64_t)nt * 128 + wn * 32 : (int64_t)nt * kTile + wn * 64 + j * 32;
+  store_tile<T, EPI, 4, 2>(p, acc, m0 + wm * 128, re, col);
 }
 
 // ---------------------------------------------------------------------------
@@ -478,15 +824,24 @@ void grouped_wgrad_kernel(WgradParams p) {
 }
 
 template <typename T>
-hipError_t gemm_dispatch(const GemmParams& prm, int b_layout, int epi, dim3 grid, hipStream_t s) {
-#define MOE_GG(BL, EP) hipLaunchKernelGGL((grouped_gemm_kernel<T, BL, EP>), grid, dim3(kThreads), 0, s, prm)
+hipError_t gemm_dispatch(const GemmParams& prm, int b_layout, int epi, bool dma, dim3 grid, hipStream_t s) {
+#define MOE_GG(BL, EP, DM) \
+  hipLaunchKernelGGL((grouped_gemm_kernel<T, BL, EP, DM>), grid, dim3(kThreads), 0, s, prm)
   if (b_layout == LAYOUT_NK) {
-    if (epi == EPI_NONE) MOE_GG(LAYOUT_NK, EPI_NONE);
-    else if (epi == EPI_SWIGLU) MOE_GG(LAYOUT_NK, EPI_SWIGLU);
-    else MOE_GG(LAYOUT_NK, EPI_DSWIGLU);
+    if (dma) {
+#define MOE_GG8(EP) hipLaunchKernelGGL((grouped_gemm8_kernel<T, EP>), grid, dim3(kThreads8), 0, s, prm)
+      if (epi == EPI_NONE) MOE_GG8(EPI_NONE);
+      else if (epi == EPI_SWIGLU) MOE_GG8(EPI_SWIGLU);
+      else MOE_GG8(EPI_DSWIGLU);
+#undef MOE_GG8
+    } else {
+      if (epi == EPI_NONE) MOE_GG(LAYOUT_NK, EPI_NONE, false);
+      else if (epi == EPI_SWIGLU) MOE_GG(LAYOUT_NK, EPI_SWIGLU, false);
+      else MOE_GG(LAYOUT_NK, EPI_DSWIGLU, false);
+    }
   } else {
-    if (epi == EPI_NONE) MOE_GG(LAYOUT_KN, EPI_NONE);
-    else if (epi == EPI_DSWIGLU) MOE_GG(LAYOUT_KN, EPI_DSWIGLU);
+    if (epi == EPI_NONE) MOE_GG(LAYOUT_KN, EPI_NONE, false);
+    else if (epi == EPI_DSWIGLU) MOE_GG(LAYOUT_KN, EPI_DSWIGLU, false);
     else return hipErrorInvalidValue;
   }
 #undef MOE_GG
@@ -503,8 +858,11 @@ hipError_t launch_grouped_gemm(const void* A, const void* B, int b_layout, const
   prm.NT = (epilogue == EPI_SWIGLU) ? (int)((N / 2 + 127) / 128) : (int)((N + kTile - 1) / kTile);
   const int64_t max_mt = (M + kTile - 1) / kTile + G;
   const dim3 grid((unsigned)(max_mt * prm.NT));
-  if (dtype == 1) return gemm_dispatch<bf16_t>(prm, b_layout, epilogue, grid, s);
-  return gemm_dispatch<float>(prm, b_layout, epilogue, grid, s);
+  // the LDS-DMA pipeline needs whole 64-byte K stages
+  const int64_t kbytes = Kd * (dtype == 1 ? 2 : 4);
+  const bool dma = b_layout == LAYOUT_NK && kbytes % kDmaRowBytes == 0;
+  if (dtype == 1) return gemm_dispatch<bf16_t>(prm, b_layout, epilogue, dma, grid, s);
+  return gemm_dispatch<float>(prm, b_layout, epilogue, dma, grid, s);
 }
 
 hipError_t launch_grouped_wgrad(const void* X, const void* dY, const int32_t* offs, int64_t M,
