@@ -37,11 +37,27 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mixtral",
                     choices=["mixtral", "fine_grained", "dsv3_share", "tiny_fp32"])
-    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target duration of the CPU-oracle sample (0 disables it)")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="per-launch HBM bytes measured with rocprofv3 counters, if present")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain device copy of 512 MiB (3 launches) to calibrate "
+                         "rocprofv3 FETCH_SIZE / WRITE_SIZE")
     return ap.parse_args()
+
+
+KERNEL_SOURCES = ["grouped_gemm.hip", "common.h"]
+
+
+def kernel_source_hash() -> str:
+    """sha256 of the grouped GEMM sources: traffic figures are valid only for this hash."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "dropless_mixture_experts_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def to_dev(a, torch):
@@ -69,12 +85,13 @@ def cpu_baseline(cfg, inp, target_s: float) -> dict | None:
                     cfg.renorm)
         return time.perf_counter() - t0
 
+    # widening the weights to fp64 is a fixed cost per call, so grow the sample until the
+    # run itself lasts about target_s
     S = min(64, cfg.T)
     dt = run(S)
-    # widening the weights to fp64 is a fixed cost per call; scale the token count for the rest
-    S2 = int(min(cfg.T, max(S, S * target_s / max(dt, 1e-3))))
-    if S2 > S:
-        S, dt = S2, run(S2)
+    while dt < 0.6 * target_s and S < cfg.T:
+        S = int(min(cfg.T, max(2 * S, S * 0.9 * target_s / max(dt, 1e-3))))
+        dt = run(S)
     return {"value": S / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
             "sample": f"first {S} of {cfg.T} tokens of the {cfg.name} workload, full forward "
                       f"(router, top-K, permute, per-expert fp64 GEMMs, combine) in {dt:.1f} s"}
@@ -158,9 +175,9 @@ def main():
     try:
         with open(args.traffic) as f:
             tr = json.load(f)
-        key = f"{cfg.name}/gemm_gate_up"
-        if key in tr:
-            traffic = tr[key]["bytes_per_launch"]
+        rec = tr.get(f"{cfg.name}/gemm_gate_up")
+        if rec and rec.get("source_sha256") == kernel_source_hash():
+            traffic = rec["bytes_per_launch"]
     except (OSError, ValueError, KeyError):
         traffic = None
 
@@ -197,6 +214,12 @@ def main():
         "input_generation_s": gen_s,
     }
     print(json.dumps(out), flush=True)
+    if args.calib_copy:
+        src = torch.ones(256 << 20, dtype=torch.bfloat16, device="cuda")   # 512 MiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
 
 
 if __name__ == "__main__":
