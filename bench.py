@@ -41,6 +41,9 @@ def parse():
                     help="target duration of the CPU-oracle sample (0 disables it)")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="per-launch HBM bytes measured with rocprofv3 counters, if present")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward of the adversarial-skew Mixtral-shaped workload instead "
+                         "(reported as an extra line, not the headline)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain device copy of 512 MiB (3 launches) to calibrate "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE")
@@ -109,6 +112,8 @@ def main():
     import dropless_mixture_experts_amd as moe
     import moe_inputs as mi
 
+    if args.backward:
+        return bench_backward(args, torch, moe, mi)
     cfg = mi.CONFIGS[args.workload]
     torch.cuda.set_device(0)
     t_gen = time.perf_counter()
@@ -220,6 +225,75 @@ def main():
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
+
+
+def bench_backward(args, torch, moe, mi):
+    """Backward of the Mixtral-shaped layer with one expert taking half of the slots and two none:
+    combine backward, SwiGLU-backward dgrad, down wgrad, gate/up dgrad, gate/up wgrad,
+    permute backward (routing held fixed)."""
+    import oracle as orc
+    cfg = mi.CONFIGS["mixtral_bwd_skew"]
+    torch.cuda.set_device(0)
+    inp = mi.make(cfg)
+    hot, dead = mi.skew_choice(cfg)
+    logits = mi.skew_logits(orc.router_logits(inp["x"], inp["w_router"]), hot, dead)
+    dev = {k: to_dev(v, torch) for k, v in inp.items()}
+    dy = to_dev(mi.upstream_grad(cfg), torch)
+    bufs = moe.MoEBuffers(cfg.T, cfg.d, cfg.E, cfg.K, cfg.F, torch.bfloat16, backward=True)
+    moe.layer_forward(dev["x"], dev["w_router"], None, dev["w13"], dev["w2"], cfg.K, cfg.score, cfg.renorm,
+                      bufs, logits=to_dev(logits, torch))
+    stream = torch.cuda.current_stream()
+    b = bufs
+    names = ["combine_bwd", "dgrad_down_dswiglu", "wgrad_down", "dgrad_gate_up", "wgrad_gate_up", "permute_bwd"]
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record(stream)
+        mark(0)
+        moe.moe_permute(dy, cfg.K, b.row_src, b.dy_perm, row_scale=b.gates, y_perm_dot=b.y_perm,
+                        dgate_out=b.d_gates)
+        mark(1)
+        moe.moe_grouped_gemm(b.dy_perm, dev["w2"], moe.MOE_LAYOUT_KN, b.offsets, b.d_pre, moe.MOE_EPI_DSWIGLU,
+                             epi_in=b.pre)
+        mark(2)
+        moe.moe_grouped_gemm_wgrad(b.h, b.dy_perm, b.offsets, b.dw2)
+        mark(3)
+        moe.moe_grouped_gemm(b.d_pre, dev["w13"], moe.MOE_LAYOUT_KN, b.offsets, b.dx_perm, moe.MOE_EPI_NONE)
+        mark(4)
+        moe.moe_grouped_gemm_wgrad(b.x_perm, b.d_pre, b.offsets, b.dw13)
+        mark(5)
+        moe.moe_unpermute_combine(b.dx_perm, b.slot_pos, None, cfg.T, cfg.K, b.dx)
+        mark(6)
+
+    for _ in range(args.warmup):
+        step()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / max(args.steps, 1)
+    per = np.zeros(6)
+    for ev in evs:
+        per += np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(6)])
+    per /= max(args.steps, 1)
+    kms = dict(zip(names, per.tolist()))
+    M = cfg.T * cfg.K
+    fl = {"dgrad_down_dswiglu": 2.0 * M * cfg.d * cfg.F, "wgrad_down": 2.0 * M * cfg.d * cfg.F,
+          "dgrad_gate_up": 2.0 * M * 2 * cfg.F * cfg.d, "wgrad_gate_up": 2.0 * M * 2 * cfg.F * cfg.d}
+    tf = {k: fl[k] / (kms[k] * 1e-3) / 1e12 for k in fl}
+    total_fl = sum(fl.values())
+    out = {"metric": "MoE layer backward tokens/s (routing held fixed)", "value": cfg.T / (ms * 1e-3),
+           "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+           "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": cfg.name, "tokens": cfg.T, "d_model": cfg.d, "experts": cfg.E, "top_k": cfg.K,
+                      "ffn": cfg.F, "hot_expert_slots": int(bufs.counts.max().item()),
+                      "empty_experts": int((bufs.counts == 0).sum().item())},
+           "gemm_tflops": tf, "gemm_total_tflops": total_fl / (sum(kms[k] for k in fl) * 1e-3) / 1e12,
+           "kernels_ms": kms}
+    print(json.dumps(out), flush=True)
 
 
 if __name__ == "__main__":
