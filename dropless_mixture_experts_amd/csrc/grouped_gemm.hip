@@ -26,6 +26,9 @@
 //     so concurrently running tiles share operands in that XCD's L2.
 //   * Epilogues: plain store; SwiGLU (gate and up columns of one output column
 //     live in the same lane); SwiGLU backward using the saved pre-activations.
+#include <cstdint>
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 
@@ -40,6 +43,7 @@ constexpr int kCPR = kRowBytes / 16;       // 16-byte chunks per LDS row
 constexpr int kTileChunks = kTile * kCPR;  // chunks per operand stage (32 KB)
 constexpr int kXcd = 8;                    // MI355X: 8 XCDs, workgroups dealt round-robin
 constexpr int kGroupM = 8;                 // row tiles that share a column tile
+constexpr int kWindow = 256;               // blocks per XCD-remap window (one per CU)
 
 enum { EPI_NONE = 0, EPI_SWIGLU = 1, EPI_DSWIGLU = 2 };
 enum { LAYOUT_NK = 0, LAYOUT_KN = 1 };
@@ -279,17 +283,13 @@ __device__ __forceinline__ void mainloop(LA& la, LB& lb, int nk, uint4* smem, f3
 }
 
 // ---------------------------------------------------------------------------
-// LDS-DMA main loop for operands whose rows are K-contiguous (the forward
-// N-by-K weight layout).  global_load_lds_dwordx4 moves 16 bytes per lane from
+// LDS-DMA pipeline.  global_load_lds_dwordx4 moves 16 bytes per lane from
 // global memory straight into LDS (lane L lands at M0 + 16 L), so no VGPRs or
 // LDS write instructions are spent on staging and several stages can be in
-// flight: 4 LDS stages of 64 K-bytes per row, each stage's loads issued three
-// stages before it is consumed.  Rows are 4 chunks of 16 bytes, the chunk
-// index XORed with (row >> 2) & 3, which keeps the 16 lanes of one LDS cycle
-// (16 consecutive rows, one chunk) on distinct bank groups.  The DMA is issued
-// through inline assembly so that the compiler does not serialise every LDS
-// read behind it; completion is tracked with explicit vmcnt waits and one
-// workgroup barrier per stage.
+// flight: 4 LDS stages, each stage's loads issued three stages before it is
+// consumed.  The DMA is issued through inline assembly so that the compiler
+// does not serialise every LDS read behind it; completion is tracked with
+// explicit vmcnt waits and one workgroup barrier per stage.
 constexpr int kDmaStages = 4;
 constexpr int kDmaRowBytes = 64;
 constexpr int kDmaCPR = kDmaRowBytes / 16;          // 4 chunks per row
@@ -303,110 +303,106 @@ __device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_byte) {
                :: "s"(lds_byte), "v"(gptr) : "memory", "m0");
 }
 __device__ __forceinline__ void wait_vmcnt_8() { asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); }
-__device__ __forceinline__ void wait_vmcnt_16() { asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); }
+__device__ __forceinline__ void wait_vmcnt_4() { asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); }
 __device__ __forceinline__ void wait_vmcnt_0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// asrc[q] / bsrc[q]: global address, at K offset 0, of the 16 bytes this lane moves
-// with DMA instruction q of operand A / B (LDS rows (wave*4 + q)*16 + lane/4).
-template <typename T, int EPI>
-__device__ __forceinline__ void mainloop_dma(const char* const (&asrc)[4], const char* const (&bsrc)[4],
-                                             int nk, uint4* smem, f32x16 (&acc)[4][4]) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int l32 = lane & 31, hi = lane >> 5;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-  if (nk <= 0) return;
-
-  const uint32_t wbase = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)smem + wave * 4 * 1024);
-  auto issue = [&](int st) {
-    const uint32_t lb = wbase + (uint32_t)(st & (kDmaStages - 1)) * (kDmaStageUnits * 16);
-    const int64_t koff = (int64_t)st * kDmaRowBytes;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) lds_dma16(asrc[q] + koff, lb + q * 1024);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) lds_dma16(bsrc[q] + koff, lb + kDmaOpUnits * 16 + q * 1024);
-  };
-
-  const int x = dswz_x(l32);
-  const int a_row4 = (wm * 128 + l32) * kDmaCPR;
-  int b_row4[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    b_row4[j] = kDmaOpUnits +
-                ((EPI == EPI_SWIGLU ? ((j >> 1) * 128 + wn * 64 + (j & 1) * 32) : (wn * 128 + j * 32)) + l32) * kDmaCPR;
-  auto read = [&](int st, int kk, uint4 (&a)[4], uint4 (&b)[4]) {
-    const uint4* S = smem + (st & (kDmaStages - 1)) * kDmaStageUnits;
-    const int cc = (2 * kk + hi) ^ x;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = S[a_row4 + i * 32 * kDmaCPR + cc];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = S[b_row4[j] + cc];
-  };
-  auto mma16 = [&](const uint4 (&a)[4], const uint4 (&b)[4]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) Mma<T>::run(a[i], b[j], acc[i][j]);
-  };
-
-  issue(0);
-  if (nk > 1) issue(1);
-  if (nk > 2) issue(2);
-  if (nk > 2) wait_vmcnt_16();
-  else if (nk > 1) wait_vmcnt_8();
-  else wait_vmcnt_0();
-  __syncthreads();
-  uint4 fa0[4], fb0[4], fa1[4], fb1[4];
-  read(0, 0, fa0, fb0);
-  int s = 0;
-  // steady state, straight-line so that LDS read counts stay exact: stage s+1 has
-  // landed for this thread after vmcnt(8); after the barrier it has for every thread,
-  // and every wave has finished reading stage s-1, whose buffer stage s+3 reuses
-  for (; s + 3 < nk; ++s) {
-    read(s, 1, fa1, fb1);
-    mma16(fa0, fb0);
-    wait_vmcnt_8();
-    __syncthreads();
-    issue(s + 3);
-    read(s + 1, 0, fa0, fb0);
-    mma16(fa1, fb1);
-  }
-  // drain the last (up to three) stages
-  for (; s < nk; ++s) {
-    read(s, 1, fa1, fb1);
-    mma16(fa0, fb0);
-    if (s + 1 < nk) {
-      if (s + 2 < nk) wait_vmcnt_8();
-      else wait_vmcnt_0();
-      __syncthreads();
-      read(s + 1, 0, fa0, fb0);
-    }
-    mma16(fa1, fb1);
-  }
-}
-
-// Eight-wave variant of the LDS-DMA main loop: two waves per SIMD, each owning a
-// 128 x 64 block of the 256 x 256 tile (4 x 2 MFMA tiles, 128 accumulators).  A
-// single wave per SIMD cannot pull LDS operands fast enough to keep its MFMA
-// pipe busy; two waves per SIMD double the LDS read rate, and each wave's MFMAs
-// cover the other's LDS, barrier and memory waits.  Stage and DMA layout are
-// those of mainloop_dma; each thread issues 2 + 2 DMA per stage.
+// ---------------------------------------------------------------------------
+// Eight-wave LDS-DMA main loop.  Two waves per SIMD, each owning a 128 x 64
+// block of the 256 x 256 tile (4 x 2 MFMA tiles, 128 accumulators): a single
+// wave per SIMD cannot pull LDS operands fast enough to keep its MFMA pipe busy;
+// two waves per SIMD double the LDS read rate, and each wave's MFMAs cover the
+// other's LDS, barrier and memory waits.  A stage is 32 K values of both
+// operands (16 KB each); each thread issues 2 + 2 DMA per stage.
+//
+// Operand modes (the same 16 KB per stage either way):
+//   OpRow: the tile's rows are K-contiguous global rows (the forward operands and
+//          the data-gradient A).  LDS row = 64 K-bytes = 4 chunks of 16 bytes, the
+//          chunk index XORed with (row >> 2) & 3 so that the 16 lanes of one LDS
+//          cycle (16 consecutive rows, one chunk) hit distinct bank groups.  One
+//          ds_read_b128 gives a lane its 8 K values.
+//   OpCol: the global row index is K and the tile's rows are columns (the K-by-N
+//          weights of the data gradient; both operands of the weight gradient).
+//          LDS row = one K value x 256 columns (512 bytes, whole cache lines from
+//          global memory), 32-byte segments XORed with (k & 3) << 1.  Operands are
+//          read with ds_read_b64_tr_b16: within each group of 16 lanes, lane i
+//          receives halfword (i & 3) of the 8 bytes addressed by lane 4e + (i >> 2)
+//          as its element e; lanes 4e + q point at K row k0 + e, columns 4q..4q+3,
+//          so lane i gets column i at K rows k0..k0+3, and two reads give the 8
+//          consecutive K values of an MFMA operand.  K rows past the valid range
+//          are read from a zero block, so ragged reductions need no LDS clearing.
 constexpr int kThreads8 = 512;
-__device__ __forceinline__ void wait_vmcnt_4() { asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); }
+constexpr int kColRows = 32;                        // K rows per OpCol stage
+constexpr int kColRowBytes = kTile * 2;             // 512 bytes (bf16)
 
-template <typename T, int EPI>
-__device__ __forceinline__ void mainloop8_dma(const char* const (&asrc)[2], const char* const (&bsrc)[2],
-                                              int nk, uint4* smem, f32x16 (&acc)[4][2]) {
+__device__ const uint4 kZero16 = {0u, 0u, 0u, 0u};  // DMA source of rows outside the reduction
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+struct OpRow {
+  const char* src[2];  // per DMA instruction q: global address at K offset 0
+  __device__ __forceinline__ const char* at(int q, int st) const { return src[q] + (int64_t)st * kDmaRowBytes; }
+  // operand of the 32 x 16 MFMA tile whose rows start at LDS row rb
+  __device__ __forceinline__ static uint4 frag(const uint4* S, int rb, int kk) {
+    const int lane = threadIdx.x & 63;
+    const int l32 = lane & 31, hi = lane >> 5;
+    return S[(rb + l32) * kDmaCPR + ((2 * kk + hi) ^ dswz_x(l32))];
+  }
+};
+
+struct OpCol {
+  const char* base[2];  // per DMA instruction q: global address of K row 0 at this lane's columns
+  const char* zero;     // this lane's bytes when its K row or columns are out of range
+  int64_t ld;           // row pitch in bytes
+  int64_t k0, kend;     // first and end K row of the reduction
+  int kr[2];            // per DMA instruction q: K row within the stage
+  __device__ __forceinline__ const char* at(int q, int st) const {
+    const int64_t k = k0 + (int64_t)st * kColRows + kr[q];
+    return k < kend ? base[q] + k * ld : zero;
+  }
+  __device__ __forceinline__ static uint4 frag(const uint4* S, int cb, int kk) {
+    const int lane = threadIdx.x & 63;
+    const int hi = lane >> 5, g = (lane >> 4) & 1, e = (lane >> 2) & 3, q = lane & 3;
+    const char* Sb = (const char*)S;
+    const int seg = ((cb >> 4) + g) ^ (e << 1);
+    uint32_t w[4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int row = 16 * kk + 8 * hi + 4 * t + e;
+      const char* addr = Sb + row * kColRowBytes + seg * 32 + q * 8;
+      const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)addr);
+      w[2 * t] = (uint16_t)v[0] | ((uint32_t)(uint16_t)v[1] << 16);
+      w[2 * t + 1] = (uint16_t)v[2] | ((uint32_t)(uint16_t)v[3] << 16);
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+  }
+  // set up DMA sources for an operand stored [K rows][ncols] (ld elements per row) whose tile
+  // covers columns [c0, c0 + 256); lanes of DMA instruction q fill LDS K row (wave*2+q)*2 + lane/32
+  __device__ __forceinline__ void init(const void* g, int64_t ld_elems, int64_t c0, int64_t ncols, int64_t kbeg,
+                                       int64_t kfin) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    ld = ld_elems * 2;
+    k0 = kbeg;
+    kend = kfin;
+    zero = (const char*)&kZero16;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      kr[q] = (wave * 2 + q) * 2 + (lane >> 5);
+      const int u = lane & 31;                                      // physical 16-byte unit in the LDS row
+      const int lu = (((u >> 1) ^ ((kr[q] & 3) << 1)) << 1) | (u & 1);  // logical unit (8 columns)
+      int64_t col = c0 + (int64_t)lu * 8;
+      col = col < ncols ? col : ncols - 8;                         // clamped: only unstored outputs use it
+      base[q] = (const char*)g + col * 2;
+    }
+  }
+};
+
+template <typename T, int EPI, typename OA, typename OB>
+__device__ __forceinline__ void mainloop8(const OA& oa, const OB& ob, int nk, uint4* smem, f32x16 (&acc)[4][2]) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wm = wave >> 2, wn = wave & 3;
-  const int l32 = lane & 31, hi = lane >> 5;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -418,26 +414,20 @@ __device__ __forceinline__ void mainloop8_dma(const char* const (&asrc)[2], cons
   const uint32_t wbase = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)smem + wave * 2 * 1024);
   auto issue = [&](int st) {
     const uint32_t lb = wbase + (uint32_t)(st & (kDmaStages - 1)) * (kDmaStageUnits * 16);
-    const int64_t koff = (int64_t)st * kDmaRowBytes;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) lds_dma16(asrc[q] + koff, lb + q * 1024);
+    for (int q = 0; q < 2; ++q) lds_dma16(oa.at(q, st), lb + q * 1024);
 #pragma unroll
-    for (int q = 0; q < 2; ++q) lds_dma16(bsrc[q] + koff, lb + kDmaOpUnits * 16 + q * 1024);
+    for (int q = 0; q < 2; ++q) lds_dma16(ob.at(q, st), lb + kDmaOpUnits * 16 + q * 1024);
   };
-
-  const int x = dswz_x(l32);
-  const int a_row4 = (wm * 128 + l32) * kDmaCPR;
-  int b_row4[2];
+  int b_rb[2];
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
-    b_row4[j] = kDmaOpUnits + ((EPI == EPI_SWIGLU ? (j * 128 + wn * 32) : (wn * 64 + j * 32)) + l32) * kDmaCPR;
+  for (int j = 0; j < 2; ++j) b_rb[j] = EPI == EPI_SWIGLU ? (j * 128 + wn * 32) : (wn * 64 + j * 32);
   auto read = [&](int st, int kk, uint4 (&a)[4], uint4 (&b)[2]) {
     const uint4* S = smem + (st & (kDmaStages - 1)) * kDmaStageUnits;
-    const int cc = (2 * kk + hi) ^ x;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = S[a_row4 + i * 32 * kDmaCPR + cc];
+    for (int i = 0; i < 4; ++i) a[i] = OA::frag(S, wm * 128 + i * 32, kk);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) b[j] = S[b_row4[j] + cc];
+    for (int j = 0; j < 2; ++j) b[j] = OB::frag(S + kDmaOpUnits, b_rb[j], kk);
   };
   auto mma8 = [&](const uint4 (&a)[4], const uint4 (&b)[2]) {
 #pragma unroll
@@ -445,6 +435,9 @@ __device__ __forceinline__ void mainloop8_dma(const char* const (&asrc)[2], cons
 #pragma unroll
       for (int j = 0; j < 2; ++j) Mma<T>::run(a[i], b[j], acc[i][j]);
   };
+  // LDS read instructions per sub-step (a transposed fragment takes two)
+  constexpr int kReads = 4 * (std::is_same<OA, OpCol>::value ? 2 : 1) + 2 * (std::is_same<OB, OpCol>::value ? 2 : 1);
+  constexpr int kMfmaPer8 = 8 * (Elem<T>::kVec == 8 ? 1 : 4);
 
   issue(0);
   if (nk > 1) issue(1);
@@ -456,12 +449,14 @@ __device__ __forceinline__ void mainloop8_dma(const char* const (&asrc)[2], cons
   uint4 fa0[4], fb0[2], fa1[4], fb1[2];
   read(0, 0, fa0, fb0);
   int s = 0;
-  constexpr int kMfmaPer8 = 8 * (Elem<T>::kVec == 8 ? 1 : 4);
+  // steady state, straight-line so that LDS read counts stay exact: stage s+1 has landed
+  // for this thread after vmcnt(4); after the barrier for every thread, and every wave has
+  // finished reading stage s-1, whose buffer stage s+3 reuses
   for (; s + 3 < nk; ++s) {
     // region 1: operand reads of sub-step 1, then the MFMAs of sub-step 0
     read(s, 1, fa1, fb1);
     mma8(fa0, fb0);
-    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 6, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, kReads, 0);
     __builtin_amdgcn_sched_group_barrier(SG_MFMA, kMfmaPer8, 0);
     __builtin_amdgcn_sched_barrier(0);  // keep those MFMAs ahead of the workgroup barrier
     wait_vmcnt_4();
@@ -470,9 +465,10 @@ __device__ __forceinline__ void mainloop8_dma(const char* const (&asrc)[2], cons
     issue(s + 3);
     read(s + 1, 0, fa0, fb0);
     mma8(fa1, fb1);
-    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 6, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, kReads, 0);
     __builtin_amdgcn_sched_group_barrier(SG_MFMA, kMfmaPer8, 0);
   }
+  // drain the last (up to three) stages
   for (; s < nk; ++s) {
     read(s, 1, fa1, fb1);
     mma8(fa0, fb0);
@@ -542,7 +538,7 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const f32x16 (&a
           }
         }
       }
-  } else {
+  } else if constexpr (EPI == EPI_NONE) {
 #pragma unroll
     for (int i = 0; i < NI; ++i)
 #pragma unroll
@@ -551,17 +547,34 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const f32x16 (&a
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int64_t row = row0 + i * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+          if (row < re && c < p.N) E::store1(p.C, row * p.N + c, acc[i][j][r]);
+        }
+      }
+  } else {  // SwiGLU backward: acc = dH; saved pre-activations [G | U] of width 2N
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int64_t c = col[j] + l32;
+        const int64_t cc = c < p.N ? c : p.N - 1;
+        // every load of the fragment first, at indices clamped into range, so that
+        // they are all in flight together; the stores are masked
+        float gt[16], up[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          int64_t row = row0 + i * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+          row = row < re ? row : re - 1;
+          gt[r] = E::load1(p.epi_in, row * 2 * p.N + cc);
+          up[r] = E::load1(p.epi_in, row * 2 * p.N + p.N + cc);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t row = row0 + i * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
           if (row < re && c < p.N) {
             const float v = acc[i][j][r];
-            if (EPI == EPI_NONE) {
-              E::store1(p.C, row * p.N + c, v);
-            } else {  // SwiGLU backward: v = dH; saved pre-activations [G | U] of width 2N
-              const float gt = E::load1(p.epi_in, row * 2 * p.N + c);
-              const float up = E::load1(p.epi_in, row * 2 * p.N + p.N + c);
-              const float sg = 1.f / (1.f + __expf(-gt));
-              E::store1(p.C, row * 2 * p.N + c, v * up * sg * (1.f + gt * (1.f - sg)));
-              E::store1(p.C, row * 2 * p.N + p.N + c, v * gt * sg);
-            }
+            const float sg = 1.f / (1.f + __expf(-gt[r]));
+            E::store1(p.C, row * 2 * p.N + c, v * up[r] * sg * (1.f + gt[r] * (1.f - sg)));
+            E::store1(p.C, row * 2 * p.N + p.N + c, v * gt[r] * sg);
           }
         }
       }
@@ -643,13 +656,12 @@ __device__ __forceinline__ bool find_tile(const GemmParams& p, int& g_out, int64
   return true;
 }
 
-template <typename T, int BL, int EPI, bool DMA>
+template <typename T, int BL, int EPI>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void grouped_gemm_kernel(GemmParams p) {
   __shared__ uint4 smem[4 * kTileChunks];
   using E = Elem<T>;
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
   const int wave = tid >> 6;
   int g, nt;
   int64_t m0, re;
@@ -673,38 +685,24 @@ void grouped_gemm_kernel(GemmParams p) {
     const int64_t row = m0 + r;
     return row < p.M ? row : p.M - 1;
   };
-  if constexpr (DMA) {
+  RowLoader la;
+  la.c = tid & 7;
+  la.kbytes = p.Kd * esz;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) la.ptr[i] = A + a_row((tid >> 3) + 32 * i) * p.Kd * esz;
+  const int nk = (int)((p.Kd * esz + kRowBytes - 1) / kRowBytes);
+  if constexpr (BL == LAYOUT_NK) {
+    RowLoader lb;
+    lb.c = tid & 7;
+    lb.kbytes = p.Kd * esz;
     const char* Bg = (const char*)p.B + (int64_t)g * p.N * p.Kd * esz;
-    const char* asrc[4];
-    const char* bsrc[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int r = (wave * 4 + q) * 16 + (lane >> 2);
-      const int c = (lane & 3) ^ dswz_x(r);
-      asrc[q] = A + a_row(r) * p.Kd * esz + c * 16;
-      bsrc[q] = Bg + b_row(r) * p.Kd * esz + c * 16;
-    }
-    mainloop_dma<T, EPI>(asrc, bsrc, (int)(p.Kd * esz / kDmaRowBytes), smem, acc);
+    for (int i = 0; i < 8; ++i) lb.ptr[i] = Bg + b_row((tid >> 3) + 32 * i) * p.Kd * esz;
+    mainloop<T, EPI>(la, lb, nk, smem, acc);
   } else {
-    RowLoader la;
-    la.c = tid & 7;
-    la.kbytes = p.Kd * esz;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) la.ptr[i] = A + a_row((tid >> 3) + 32 * i) * p.Kd * esz;
-    const int nk = (int)((p.Kd * esz + kRowBytes - 1) / kRowBytes);
-    if constexpr (BL == LAYOUT_NK) {
-      RowLoader lb;
-      lb.c = tid & 7;
-      lb.kbytes = p.Kd * esz;
-      const char* Bg = (const char*)p.B + (int64_t)g * p.N * p.Kd * esz;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) lb.ptr[i] = Bg + b_row((tid >> 3) + 32 * i) * p.Kd * esz;
-      mainloop<T, EPI>(la, lb, nk, smem, acc);
-    } else {
-      ColLoader<T> lb;
-      lb.init((const char*)p.B + (int64_t)g * p.Kd * p.N * esz, p.N, (int64_t)nt * kTile, p.N, 0, p.Kd);
-      mainloop<T, EPI>(la, lb, nk, smem, acc);
-    }
+    ColLoader<T> lb;
+    lb.init((const char*)p.B + (int64_t)g * p.Kd * p.N * esz, p.N, (int64_t)nt * kTile, p.N, 0, p.Kd);
+    mainloop<T, EPI>(la, lb, nk, smem, acc);
   }
 
   // ---- epilogue
@@ -716,8 +714,10 @@ void grouped_gemm_kernel(GemmParams p) {
   store_tile<T, EPI, 4, 4>(p, acc, m0 + wm * 128, re, col);
 }
 
-// Eight-wave grouped GEMM for the N-by-K weight layout with whole 64-byte K stages.
-template <typename T, int EPI>
+// Eight-wave grouped GEMM with whole 32-element K stages.  A (activations) is
+// always K-contiguous; B is the N-by-K weight layout (OpRow) or the K-by-N one
+// (OpCol, bf16 only).
+template <typename T, int EPI, int BL>
 __global__ __launch_bounds__(kThreads8) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void grouped_gemm8_kernel(GemmParams p) {
   __shared__ uint4 smem[kDmaStages * kDmaStageUnits];
@@ -731,28 +731,40 @@ void grouped_gemm8_kernel(GemmParams p) {
   const int64_t esz = E::kBytes;
   const char* A = (const char*)p.A;
   const char* Bg = (const char*)p.B + (int64_t)g * p.N * p.Kd * esz;
-  const char* asrc[2];
-  const char* bsrc[2];
+  OpRow oa;
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int r = (wave * 2 + q) * 16 + (lane >> 2);
     const int c = (lane & 3) ^ dswz_x(r);
     int64_t ar = m0 + r;
     ar = ar < p.M ? ar : p.M - 1;
-    int64_t br;
-    if (EPI == EPI_SWIGLU) {
-      const int64_t F = p.N / 2;
-      const int64_t cc = (int64_t)nt * 128 + (r & 127);
-      br = (r < 128 ? 0 : F) + (cc < F ? cc : F - 1);
-    } else {
-      br = (int64_t)nt * kTile + r;
-      br = br < p.N ? br : p.N - 1;
-    }
-    asrc[q] = A + ar * p.Kd * esz + c * 16;
-    bsrc[q] = Bg + br * p.Kd * esz + c * 16;
+    oa.src[q] = A + ar * p.Kd * esz + c * 16;
   }
+  const int nk = (int)(p.Kd * esz / kDmaRowBytes);
   f32x16 acc[4][2];
-  mainloop8_dma<T, EPI>(asrc, bsrc, (int)(p.Kd * esz / kDmaRowBytes), smem, acc);
+  if constexpr (BL == LAYOUT_NK) {
+    OpRow ob;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int r = (wave * 2 + q) * 16 + (lane >> 2);
+      const int c = (lane & 3) ^ dswz_x(r);
+      int64_t br;
+      if (EPI == EPI_SWIGLU) {
+        const int64_t F = p.N / 2;
+        const int64_t cc = (int64_t)nt * 128 + (r & 127);
+        br = (r < 128 ? 0 : F) + (cc < F ? cc : F - 1);
+      } else {
+        br = (int64_t)nt * kTile + r;
+        br = br < p.N ? br : p.N - 1;
+      }
+      ob.src[q] = Bg + br * p.Kd * esz + c * 16;
+    }
+    mainloop8<T, EPI>(oa, ob, nk, smem, acc);
+  } else {
+    OpCol ob;
+    ob.init(Bg, p.N, (int64_t)nt * kTile, p.N, 0, p.Kd);
+    mainloop8<T, EPI>(oa, ob, nk, smem, acc);
+  }
   const int wm = wave >> 2, wn = wave & 3;
   int64_t col[2];
 #pragma unroll
@@ -823,28 +835,121 @@ void grouped_wgrad_kernel(WgradParams p) {
     }
 }
 
+// Eight-wave weight gradient (bf16): both operands are read along the group's
+// rows (OpCol); rows past the group end come from the zero block.
+//
+// Every group has the same number of output tiles but a tile's cost grows with
+// the group's row count, so tiles are handed out longest group first (groups
+// ranked by row count, ties by index): the short tiles of small groups then
+// fill the machine at the end instead of a few long ones trailing.  The XCD
+// remap is applied per window of 256 blocks, which keeps that order in time
+// while each XCD still runs contiguous tiles of a window.
+__global__ __launch_bounds__(kThreads8) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void grouped_wgrad8_kernel(WgradParams p) {
+  __shared__ uint4 smem[kDmaStages * kDmaStageUnits];
+  __shared__ int s_rows[kThreads8];
+  __shared__ int s_group;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int64_t tpg = (int64_t)p.TN * p.TK;
+  const int64_t total = tpg * p.G;
+  const int64_t win = (int64_t)blockIdx.x / kWindow * kWindow;
+  const int64_t L = win + xcd_remap((int64_t)blockIdx.x - win, min((int64_t)kWindow, total - win));
+  const int rank = (int)(L / tpg);
+  int g = rank;
+  if (p.G <= kThreads8) {
+    int64_t rs, re;
+    int rows = 0;
+    if (tid < p.G) {
+      group_rows(p.offs, tid, p.M, rs, re);
+      rows = (int)(re - rs);
+      s_rows[tid] = rows;
+    }
+    if (tid == 0) s_group = 0;
+    __syncthreads();
+    if (tid < p.G) {
+      int r = 0;
+      for (int h = 0; h < p.G; ++h) {
+        const int o = s_rows[h];
+        r += (o > rows) | ((o == rows) & (h < tid));
+      }
+      if (r == rank) s_group = tid;
+    }
+    __syncthreads();
+    g = s_group;
+  }
+  const int rem = (int)(L - (int64_t)rank * tpg);
+  const int tk = rem / p.TN;  // neighbouring tiles share the same X columns
+  const int tn = rem % p.TN;
+  int64_t rs, re;
+  group_rows(p.offs, g, p.M, rs, re);
+  const int64_t n0 = (int64_t)tn * kTile, k0 = (int64_t)tk * kTile;
+  const int nk = (int)((re - rs + kColRows - 1) / kColRows);
+  OpCol oa, ob;
+  oa.init(p.dY, p.N, n0, p.N, rs, re);
+  ob.init(p.X, p.Kd, k0, p.Kd, rs, re);
+  f32x16 acc[4][2];
+  mainloop8<bf16_t, EPI_NONE>(oa, ob, nk, smem, acc);  // zeros when the group is empty
+
+  float* out = p.dW + (int64_t)g * p.N * p.Kd;
+  const int wm = wave >> 2, wn = wave & 3;
+  const int l32 = lane & 31, hi = lane >> 5;
+  if (p.accumulate && nk == 0) return;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int64_t col = k0 + wn * 64 + j * 32 + l32;
+      const int64_t cc = col < p.Kd ? col : p.Kd - 1;
+      float prev[16];
+      if (p.accumulate) {  // all loads first (clamped in range), then the stores
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          int64_t row = n0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+          row = row < p.N ? row : p.N - 1;
+          prev[r] = out[row * p.Kd + cc];
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) prev[r] = 0.f;
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = n0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+        if (row < p.N && col < p.Kd) out[row * p.Kd + col] = prev[r] + acc[i][j][r];
+      }
+    }
+}
+
 template <typename T>
 hipError_t gemm_dispatch(const GemmParams& prm, int b_layout, int epi, bool dma, dim3 grid, hipStream_t s) {
-#define MOE_GG(BL, EP, DM) \
-  hipLaunchKernelGGL((grouped_gemm_kernel<T, BL, EP, DM>), grid, dim3(kThreads), 0, s, prm)
+#define MOE_GG(BL, EP) hipLaunchKernelGGL((grouped_gemm_kernel<T, BL, EP>), grid, dim3(kThreads), 0, s, prm)
+#define MOE_GG8(EP, BL) hipLaunchKernelGGL((grouped_gemm8_kernel<T, EP, BL>), grid, dim3(kThreads8), 0, s, prm)
   if (b_layout == LAYOUT_NK) {
     if (dma) {
-#define MOE_GG8(EP) hipLaunchKernelGGL((grouped_gemm8_kernel<T, EP>), grid, dim3(kThreads8), 0, s, prm)
-      if (epi == EPI_NONE) MOE_GG8(EPI_NONE);
-      else if (epi == EPI_SWIGLU) MOE_GG8(EPI_SWIGLU);
-      else MOE_GG8(EPI_DSWIGLU);
-#undef MOE_GG8
+      if (epi == EPI_NONE) MOE_GG8(EPI_NONE, LAYOUT_NK);
+      else if (epi == EPI_SWIGLU) MOE_GG8(EPI_SWIGLU, LAYOUT_NK);
+      else MOE_GG8(EPI_DSWIGLU, LAYOUT_NK);
     } else {
-      if (epi == EPI_NONE) MOE_GG(LAYOUT_NK, EPI_NONE, false);
-      else if (epi == EPI_SWIGLU) MOE_GG(LAYOUT_NK, EPI_SWIGLU, false);
-      else MOE_GG(LAYOUT_NK, EPI_DSWIGLU, false);
+      if (epi == EPI_NONE) MOE_GG(LAYOUT_NK, EPI_NONE);
+      else if (epi == EPI_SWIGLU) MOE_GG(LAYOUT_NK, EPI_SWIGLU);
+      else MOE_GG(LAYOUT_NK, EPI_DSWIGLU);
     }
   } else {
-    if (epi == EPI_NONE) MOE_GG(LAYOUT_KN, EPI_NONE, false);
-    else if (epi == EPI_DSWIGLU) MOE_GG(LAYOUT_KN, EPI_DSWIGLU, false);
-    else return hipErrorInvalidValue;
+    if (epi == EPI_SWIGLU) return hipErrorInvalidValue;
+    if constexpr (std::is_same<T, bf16_t>::value) {
+      if (dma) {
+        if (epi == EPI_NONE) MOE_GG8(EPI_NONE, LAYOUT_KN);
+        else MOE_GG8(EPI_DSWIGLU, LAYOUT_KN);
+        return hipGetLastError();
+      }
+    }
+    if (epi == EPI_NONE) MOE_GG(LAYOUT_KN, EPI_NONE);
+    else MOE_GG(LAYOUT_KN, EPI_DSWIGLU);
   }
 #undef MOE_GG
+#undef MOE_GG8
   return hipGetLastError();
 }
 
@@ -858,9 +963,11 @@ hipError_t launch_grouped_gemm(const void* A, const void* B, int b_layout, const
   prm.NT = (epilogue == EPI_SWIGLU) ? (int)((N / 2 + 127) / 128) : (int)((N + kTile - 1) / kTile);
   const int64_t max_mt = (M + kTile - 1) / kTile + G;
   const dim3 grid((unsigned)(max_mt * prm.NT));
-  // the LDS-DMA pipeline needs whole 64-byte K stages
+  // the LDS-DMA pipeline needs whole 64-byte K stages of A, 16-byte aligned rows of
+  // B in the K-by-N layout, and 16-byte aligned operands
   const int64_t kbytes = Kd * (dtype == 1 ? 2 : 4);
-  const bool dma = b_layout == LAYOUT_NK && kbytes % kDmaRowBytes == 0;
+  const bool aligned = ((uintptr_t)A | (uintptr_t)B) % 16 == 0;
+  const bool dma = aligned && kbytes % kDmaRowBytes == 0 && (b_layout == LAYOUT_NK || N % 8 == 0);
   if (dtype == 1) return gemm_dispatch<bf16_t>(prm, b_layout, epilogue, dma, grid, s);
   return gemm_dispatch<float>(prm, b_layout, epilogue, dma, grid, s);
 }
@@ -872,7 +979,11 @@ hipError_t launch_grouped_wgrad(const void* X, const void* dY, const int32_t* of
   prm.TN = (int)((N + kTile - 1) / kTile);
   prm.TK = (int)((Kd + kTile - 1) / kTile);
   const dim3 grid((unsigned)((int64_t)prm.TN * prm.TK * G));
-  if (dtype == 1)
+  // the LDS-DMA pipeline moves 16-byte pieces of rows: bf16 widths that are multiples of 8
+  const bool dma = dtype == 1 && N % 8 == 0 && Kd % 8 == 0 && ((uintptr_t)X | (uintptr_t)dY) % 16 == 0;
+  if (dma)
+    hipLaunchKernelGGL(grouped_wgrad8_kernel, grid, dim3(kThreads8), 0, s, prm);
+  else if (dtype == 1)
     hipLaunchKernelGGL((grouped_wgrad_kernel<bf16_t>), grid, dim3(kThreads), 0, s, prm);
   else
     hipLaunchKernelGGL((grouped_wgrad_kernel<float>), grid, dim3(kThreads), 0, s, prm);

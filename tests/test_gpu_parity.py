@@ -238,10 +238,13 @@ def _check_untouched(C, off, M):
     assert not np.any(np.isnan(c[off[0]:off[-1]]))
 
 
+# K = 200 or 104 (400 / 208 bytes per bf16 row) takes the register-staged kernel; K = 192 or
+# 96 takes the LDS-DMA pipeline (whole 32-element K stages), in both weight layouts
 @pytest.mark.parametrize("bf16", [True, False])
 @pytest.mark.parametrize("layout", [0, 1])
-def test_grouped_gemm_plain(bf16, layout):
-    N, Kd = 264, 200
+@pytest.mark.parametrize("Kd", [200, 192])
+def test_grouped_gemm_plain(bf16, layout, Kd):
+    N = 264
     A, W, off, M = _gemm_case(bf16, N, Kd, seed=1 + layout)
     Wl = W if layout == 0 else np.ascontiguousarray(W.transpose(0, 2, 1))
     Ad = dev(A)
@@ -274,8 +277,9 @@ def test_grouped_gemm_swiglu(bf16, save):
 
 @pytest.mark.parametrize("bf16", [True, False])
 @pytest.mark.parametrize("layout", [0, 1])
-def test_grouped_gemm_dswiglu(bf16, layout):
-    F, Kd = 136, 104
+@pytest.mark.parametrize("Kd", [104, 96])
+def test_grouped_gemm_dswiglu(bf16, layout, Kd):
+    F = 136
     A, W, off, M = _gemm_case(bf16, F, Kd, seed=4)
     Wl = W if layout == 0 else np.ascontiguousarray(W.transpose(0, 2, 1))
     rng = np.random.default_rng(9)
