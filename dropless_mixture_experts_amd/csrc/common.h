@@ -39,6 +39,15 @@ template <> struct Elem<float> {
   }
   __device__ static float load1(const void* p, int64_t i) { return ((const float*)p)[i]; }
   __device__ static void store1(void* p, int64_t i, float v) { ((float*)p)[i] = v; }
+  // elements i..i+3 (i a multiple of 4: one 16-byte access)
+  __device__ static void load4(const void* p, int64_t i, float (&f)[4]) {
+    const f32x4 v = *(const f32x4*)((const float*)p + i);
+    f[0] = v.x; f[1] = v.y; f[2] = v.z; f[3] = v.w;
+  }
+  __device__ static void store4(void* p, int64_t i, const float (&f)[4]) {
+    const f32x4 v = {f[0], f[1], f[2], f[3]};
+    *(f32x4*)((float*)p + i) = v;
+  }
 };
 struct bf16_t {};
 template <> struct Elem<bf16_t> {
@@ -58,6 +67,15 @@ template <> struct Elem<bf16_t> {
     return bf16_bits_to_f32(((const uint16_t*)p)[i]);
   }
   __device__ static void store1(void* p, int64_t i, float v) { ((uint16_t*)p)[i] = f32_to_bf16_bits(v); }
+  // elements i..i+3 (i a multiple of 4: one 8-byte access)
+  __device__ static void load4(const void* p, int64_t i, float (&f)[4]) {
+    const uint2 v = *(const uint2*)((const uint16_t*)p + i);
+    f[0] = __uint_as_float(v.x << 16); f[1] = __uint_as_float(v.x & 0xffff0000u);
+    f[2] = __uint_as_float(v.y << 16); f[3] = __uint_as_float(v.y & 0xffff0000u);
+  }
+  __device__ static void store4(void* p, int64_t i, const float (&f)[4]) {
+    *(uint2*)((uint16_t*)p + i) = make_uint2(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]));
+  }
 };
 
 // streaming (non-temporal) 16-byte global accesses

@@ -71,6 +71,15 @@ template <> struct Mma<float> {
   }
 };
 
+// acc += (A B^T)^T for a 32 x 32 tile: the MFMA is fed B as its first operand, so
+// a lane ends up holding row (lane & 31) of the output at the 16 columns
+// 8 (r / 4) + 4 (lane / 32) + r % 4: runs of 4 consecutive columns, which the
+// epilogues store as one 8-byte (bf16) or 16-byte (fp32) access each.
+template <typename T>
+__device__ __forceinline__ void mma_rows(const uint4& a, const uint4& b, f32x16& acc) {
+  Mma<T>::run(b, a, acc);
+}
+
 // ---------------------------------------------------------------------------
 // Loader of an operand whose rows are K-contiguous: LDS row r <- global row ptr_r.
 // Thread tid moves chunk (tid & 7) of rows (tid >> 3) + 32 i, i < 8.
@@ -251,7 +260,7 @@ __device__ __forceinline__ void mainloop(LA& la, LB& lb, int nk, uint4* smem, f3
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) Mma<T>::run(a[i], b[j], acc[i][j]);
+      for (int j = 0; j < 4; ++j) mma_rows<T>(a[i], b[j], acc[i][j]);
   };
 
   la.load(0);
@@ -433,7 +442,7 @@ __device__ __forceinline__ void mainloop8(const OA& oa, const OB& ob, int nk, ui
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) Mma<T>::run(a[i], b[j], acc[i][j]);
+      for (int j = 0; j < 2; ++j) mma_rows<T>(a[i], b[j], acc[i][j]);
   };
   // LDS read instructions per sub-step (a transposed fragment takes two)
   constexpr int kReads = 4 * (std::is_same<OA, OpCol>::value ? 2 : 1) + 2 * (std::is_same<OB, OpCol>::value ? 2 : 1);
@@ -510,7 +519,9 @@ struct GemmParams {
 };
 
 // Epilogue of one wave: acc[i][j] is the 32 x 32 tile at rows row0 + 32 i and
-// columns col[j]; a lane holds column (lane & 31) and rows 8 (r/4) + 4 (lane/32) + r%4.
+// columns col[j]; a lane holds row (lane & 31) at columns 8 q + 4 (lane / 32) + 0..3
+// in acc[i][j][4 q .. 4 q + 3].  Widths are multiples of 8 elements, so a run of 4
+// columns is either wholly inside the output or wholly past its end.
 // SwiGLU: fragments j < NJ/2 are gate columns and j + NJ/2 the matching up columns.
 template <typename T, int EPI, int NI, int NJ>
 __device__ __forceinline__ void store_tile(const GemmParams& p, const f32x16 (&acc)[NI][NJ], int64_t row0,
@@ -518,66 +529,82 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const f32x16 (&a
   using E = Elem<T>;
   const int lane = threadIdx.x & 63;
   const int l32 = lane & 31, hi = lane >> 5;
-  if constexpr (EPI == EPI_SWIGLU) {
-    const int64_t F = p.N / 2;
 #pragma unroll
-    for (int i = 0; i < NI; ++i)
+  for (int i = 0; i < NI; ++i) {
+    const int64_t row = row0 + i * 32 + l32;
+    if (EPI == EPI_DSWIGLU) {
+      // SwiGLU backward: acc = dH; saved pre-activations [G | U] of width 2N.  The loads
+      // of JB fragments go first (clamped into range) so that they are in flight together.
+      constexpr int JB = NJ < 2 ? NJ : 2;
+      const int64_t rc = row < re ? row : re - 1;
 #pragma unroll
-      for (int j = 0; j < NJ / 2; ++j) {
-        const int64_t c = col[j] + l32;
+      for (int j0 = 0; j0 < NJ; j0 += JB) {
+        float gt[JB][4][4], up[JB][4][4];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t row = row0 + i * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-          if (row < re && c < F) {
-            const float gt = acc[i][j][r], up = acc[i][j + NJ / 2][r];
-            E::store1(p.C, row * F + c, gt / (1.f + __expf(-gt)) * up);
-            if (p.epi_save) {
-              E::store1(p.epi_save, row * p.N + c, gt);
-              E::store1(p.epi_save, row * p.N + F + c, up);
+        for (int jj = 0; jj < JB; ++jj)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            int64_t c = col[j0 + jj] + 8 * q + 4 * hi;
+            c = c < p.N ? c : p.N - 4;
+            E::load4(p.epi_in, rc * 2 * p.N + c, gt[jj][q]);
+            E::load4(p.epi_in, rc * 2 * p.N + p.N + c, up[jj][q]);
+          }
+        if (row >= re) continue;
+#pragma unroll
+        for (int jj = 0; jj < JB; ++jj)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int64_t c = col[j0 + jj] + 8 * q + 4 * hi;
+            if (c >= p.N) continue;
+            float da[4], du[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float v = acc[i][j0 + jj][4 * q + e], g = gt[jj][q][e], u = up[jj][q][e];
+              const float sg = 1.f / (1.f + __expf(-g));
+              da[e] = v * u * sg * (1.f + g * (1.f - sg));
+              du[e] = v * g * sg;
             }
+            E::store4(p.C, row * 2 * p.N + c, da);
+            E::store4(p.C, row * 2 * p.N + p.N + c, du);
+          }
+      }
+      continue;
+    }
+    if (row >= re) continue;
+    if constexpr (EPI == EPI_SWIGLU) {
+      const int64_t F = p.N / 2;
+#pragma unroll
+      for (int j = 0; j < NJ / 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t c = col[j] + 8 * q + 4 * hi;
+          if (c >= F) continue;
+          float h[4], g[4], u[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            g[e] = acc[i][j][4 * q + e];
+            u[e] = acc[i][j + NJ / 2][4 * q + e];
+            h[e] = g[e] / (1.f + __expf(-g[e])) * u[e];
+          }
+          E::store4(p.C, row * F + c, h);
+          if (p.epi_save) {
+            E::store4(p.epi_save, row * p.N + c, g);
+            E::store4(p.epi_save, row * p.N + F + c, u);
           }
         }
-      }
-  } else if constexpr (EPI == EPI_NONE) {
+    } else {
 #pragma unroll
-    for (int i = 0; i < NI; ++i)
+      for (int j = 0; j < NJ; ++j)
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const int64_t c = col[j] + l32;
+        for (int q = 0; q < 4; ++q) {
+          const int64_t c = col[j] + 8 * q + 4 * hi;
+          if (c >= p.N) continue;
+          float v[4];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t row = row0 + i * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-          if (row < re && c < p.N) E::store1(p.C, row * p.N + c, acc[i][j][r]);
+          for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e];
+          E::store4(p.C, row * p.N + c, v);
         }
-      }
-  } else {  // SwiGLU backward: acc = dH; saved pre-activations [G | U] of width 2N
-#pragma unroll
-    for (int i = 0; i < NI; ++i)
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const int64_t c = col[j] + l32;
-        const int64_t cc = c < p.N ? c : p.N - 1;
-        // every load of the fragment first, at indices clamped into range, so that
-        // they are all in flight together; the stores are masked
-        float gt[16], up[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          int64_t row = row0 + i * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-          row = row < re ? row : re - 1;
-          gt[r] = E::load1(p.epi_in, row * 2 * p.N + cc);
-          up[r] = E::load1(p.epi_in, row * 2 * p.N + p.N + cc);
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t row = row0 + i * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-          if (row < re && c < p.N) {
-            const float v = acc[i][j][r];
-            const float sg = 1.f / (1.f + __expf(-gt[r]));
-            E::store1(p.C, row * 2 * p.N + c, v * up[r] * sg * (1.f + gt[r] * (1.f - sg)));
-            E::store1(p.C, row * 2 * p.N + p.N + c, v * gt[r] * sg);
-          }
-        }
-      }
+    }
   }
 }
 
@@ -786,6 +813,47 @@ struct WgradParams {
   int accumulate;
 };
 
+// dW epilogue of one wave: acc[i][j] covers rows row0 + 32 i and columns col0 + 32 j of
+// one group's [N, Kd] fp32 gradient (lane layout as in store_tile).  Accumulate mode
+// loads the previous values of a row first, all together, then adds and stores.
+template <int NI, int NJ>
+__device__ __forceinline__ void store_wgrad(float* out, const f32x16 (&acc)[NI][NJ], int64_t row0, int64_t col0,
+                                            int64_t N, int64_t Kd, int accumulate) {
+  using E = Elem<float>;
+  const int lane = threadIdx.x & 63;
+  const int l32 = lane & 31, hi = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int64_t row = row0 + i * 32 + l32;
+    if (row >= N) continue;
+    float prev[NJ][4][4];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (accumulate) {
+          int64_t c = col0 + j * 32 + 8 * q + 4 * hi;
+          c = c < Kd ? c : Kd - 4;
+          E::load4(out, row * Kd + c, prev[j][q]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) prev[j][q][e] = 0.f;
+        }
+      }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t c = col0 + j * 32 + 8 * q + 4 * hi;
+        if (c >= Kd) continue;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = prev[j][q][e] + acc[i][j][4 * q + e];
+        E::store4(out, row * Kd + c, v);
+      }
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void grouped_wgrad_kernel(WgradParams p) {
@@ -803,9 +871,7 @@ void grouped_wgrad_kernel(WgradParams p) {
   int64_t rs, re;
   group_rows(p.offs, g, p.M, rs, re);
   const int64_t n0 = (int64_t)tn * kTile, k0 = (int64_t)tk * kTile;
-  float* out = p.dW + (int64_t)g * p.N * p.Kd;
   const int wm = wave >> 1, wn = wave & 1;
-  const int l32 = lane & 31, hi = lane >> 5;
 
   f32x16 acc[4][4];
   constexpr int BK = kRowBytes / Elem<T>::kBytes;
@@ -814,25 +880,8 @@ void grouped_wgrad_kernel(WgradParams p) {
   la.init(p.dY, p.N, n0, p.N, rs, re);
   lb.init(p.X, p.Kd, k0, p.Kd, rs, re);
   mainloop<T, EPI_NONE>(la, lb, nk, smem, acc);  // zeros when the group is empty
-
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t col = k0 + wn * 128 + j * 32 + l32;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t row = n0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-        if (row < p.N && col < p.Kd) {
-          float* q = out + row * p.Kd + col;
-          if (p.accumulate) {
-            if (nk > 0) *q += acc[i][j][r];
-          } else {
-            *q = acc[i][j][r];
-          }
-        }
-      }
-    }
+  if (p.accumulate && nk == 0) return;  // accumulate mode leaves an empty group's dW as it is
+  store_wgrad<4, 4>(p.dW + (int64_t)g * p.N * p.Kd, acc, n0 + wm * 128, k0 + wn * 128, p.N, p.Kd, p.accumulate);
 }
 
 // Eight-wave weight gradient (bf16): both operands are read along the group's
@@ -892,34 +941,9 @@ void grouped_wgrad8_kernel(WgradParams p) {
   f32x16 acc[4][2];
   mainloop8<bf16_t, EPI_NONE>(oa, ob, nk, smem, acc);  // zeros when the group is empty
 
-  float* out = p.dW + (int64_t)g * p.N * p.Kd;
   const int wm = wave >> 2, wn = wave & 3;
-  const int l32 = lane & 31, hi = lane >> 5;
-  if (p.accumulate && nk == 0) return;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t col = k0 + wn * 64 + j * 32 + l32;
-      const int64_t cc = col < p.Kd ? col : p.Kd - 1;
-      float prev[16];
-      if (p.accumulate) {  // all loads first (clamped in range), then the stores
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          int64_t row = n0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-          row = row < p.N ? row : p.N - 1;
-          prev[r] = out[row * p.Kd + cc];
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) prev[r] = 0.f;
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t row = n0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-        if (row < p.N && col < p.Kd) out[row * p.Kd + col] = prev[r] + acc[i][j][r];
-      }
-    }
+  if (p.accumulate && nk == 0) return;  // accumulate mode leaves an empty group's dW as it is
+  store_wgrad<4, 2>(p.dW + (int64_t)g * p.N * p.Kd, acc, n0 + wm * 128, k0 + wn * 64, p.N, p.Kd, p.accumulate);
 }
 
 template <typename T>
