@@ -312,6 +312,7 @@ __device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_byte) {
                :: "s"(lds_byte), "v"(gptr) : "memory", "m0");
 }
 __device__ __forceinline__ void wait_vmcnt_8() { asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); }
+__device__ __forceinline__ void wait_vmcnt_6() { asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); }
 __device__ __forceinline__ void wait_vmcnt_4() { asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); }
 __device__ __forceinline__ void wait_vmcnt_0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
@@ -407,6 +408,12 @@ struct OpCol {
   }
 };
 
+// Workgroup barrier without the LDS-drain wait that __syncthreads() implies: the
+// only LDS writes here are DMA, completed by the explicit vmcnt waits, and every
+// LDS read of a buffer about to be refilled has been consumed by an issued MFMA.
+// The memory clobber keeps the compiler from moving LDS reads across it.
+__device__ __forceinline__ void dma_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
 template <typename T, int EPI, typename OA, typename OB>
 __device__ __forceinline__ void mainloop8(const OA& oa, const OB& ob, int nk, uint4* smem, f32x16 (&acc)[4][2]) {
   const int lane = threadIdx.x & 63;
@@ -421,13 +428,9 @@ __device__ __forceinline__ void mainloop8(const OA& oa, const OB& ob, int nk, ui
   if (nk <= 0) return;
 
   const uint32_t wbase = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)smem + wave * 2 * 1024);
-  auto issue = [&](int st) {
-    const uint32_t lb = wbase + (uint32_t)(st & (kDmaStages - 1)) * (kDmaStageUnits * 16);
-#pragma unroll
-    for (int q = 0; q < 2; ++q) lds_dma16(oa.at(q, st), lb + q * 1024);
-#pragma unroll
-    for (int q = 0; q < 2; ++q) lds_dma16(ob.at(q, st), lb + kDmaOpUnits * 16 + q * 1024);
-  };
+  auto lbase = [&](int st) { return wbase + (uint32_t)(st & (kDmaStages - 1)) * (kDmaStageUnits * 16); };
+  auto issue_a = [&](int st, int q) { lds_dma16(oa.at(q, st), lbase(st) + q * 1024); };
+  auto issue_b = [&](int st, int q) { lds_dma16(ob.at(q, st), lbase(st) + kDmaOpUnits * 16 + q * 1024); };
   int b_rb[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) b_rb[j] = EPI == EPI_SWIGLU ? (j * 128 + wn * 32) : (wn * 64 + j * 32);
@@ -438,56 +441,76 @@ __device__ __forceinline__ void mainloop8(const OA& oa, const OB& ob, int nk, ui
 #pragma unroll
     for (int j = 0; j < 2; ++j) b[j] = OB::frag(S + kDmaOpUnits, b_rb[j], kk);
   };
-  auto mma8 = [&](const uint4 (&a)[4], const uint4 (&b)[2]) {
+  // MFMAs t0 .. t1-1 of a sub-step (t = 2 i + j)
+  auto mma = [&](const uint4 (&a)[4], const uint4 (&b)[2], int t0, int t1) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) mma_rows<T>(a[i], b[j], acc[i][j]);
+    for (int t = 0; t < 8; ++t)
+      if (t >= t0 && t < t1) mma_rows<T>(a[t >> 1], b[t & 1], acc[t >> 1][t & 1]);
   };
   // LDS read instructions per sub-step (a transposed fragment takes two)
   constexpr int kReads = 4 * (std::is_same<OA, OpCol>::value ? 2 : 1) + 2 * (std::is_same<OB, OpCol>::value ? 2 : 1);
-  constexpr int kMfmaPer8 = 8 * (Elem<T>::kVec == 8 ? 1 : 4);
+  constexpr int kMfmaPer = Elem<T>::kVec == 8 ? 1 : 4;  // MFMA instructions per 32 x 32 x 16 step
 
-  issue(0);
-  if (nk > 1) issue(1);
-  if (nk > 2) issue(2);
-  if (nk > 2) wait_vmcnt_8();
+  // Stage st is issued in two halves: its A rows one iteration before its B rows.  In
+  // every state below, the DMAs issued after the last one of stage st+1 are exactly the
+  // 4 of stage st+2, so vmcnt(4) (vmcnt(0) at the end) means stage st+1 has landed.
+  issue_a(0, 0); issue_a(0, 1); issue_b(0, 0); issue_b(0, 1);
+  if (nk > 1) { issue_a(1, 0); issue_a(1, 1); issue_b(1, 0); issue_b(1, 1); }
+  if (nk > 2) { issue_a(2, 0); issue_a(2, 1); }
+  if (nk > 2) wait_vmcnt_6();
   else if (nk > 1) wait_vmcnt_4();
   else wait_vmcnt_0();
-  __syncthreads();
+  dma_barrier();
   uint4 fa0[4], fb0[2], fa1[4], fb1[2];
   read(0, 0, fa0, fb0);
   int s = 0;
-  // steady state, straight-line so that LDS read counts stay exact: stage s+1 has landed
-  // for this thread after vmcnt(4); after the barrier for every thread, and every wave has
-  // finished reading stage s-1, whose buffer stage s+3 reuses
+  // steady state, straight-line so that LDS read counts stay exact.  The DMAs are spread
+  // between MFMAs so that the 8 waves do not hand the address unit a burst of 32 at once.
+  // The B half of stage s+2 reuses the buffer of stage s-2 and the A half of stage s+3
+  // that of stage s-1: every wave finished reading those before the previous barrier.
   for (; s + 3 < nk; ++s) {
-    // region 1: operand reads of sub-step 1, then the MFMAs of sub-step 0
+    // region 1: operand reads of sub-step 1, the MFMAs of sub-step 0, B half of stage s+2
     read(s, 1, fa1, fb1);
-    mma8(fa0, fb0);
+    mma(fa0, fb0, 0, 4);
     __builtin_amdgcn_sched_group_barrier(SG_DS_READ, kReads, 0);
-    __builtin_amdgcn_sched_group_barrier(SG_MFMA, kMfmaPer8, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 4 * kMfmaPer, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_b(s + 2, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(fa0, fb0, 4, 6);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_b(s + 2, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(fa0, fb0, 6, 8);
     __builtin_amdgcn_sched_barrier(0);  // keep those MFMAs ahead of the workgroup barrier
     wait_vmcnt_4();
-    __syncthreads();
-    // region 2: next stage's DMA and its sub-step-0 reads, then the MFMAs of sub-step 1
-    issue(s + 3);
+    dma_barrier();
+    // region 2: sub-step-0 reads of stage s+1, the MFMAs of sub-step 1, A half of stage s+3
     read(s + 1, 0, fa0, fb0);
-    mma8(fa1, fb1);
+    mma(fa1, fb1, 0, 2);
     __builtin_amdgcn_sched_group_barrier(SG_DS_READ, kReads, 0);
-    __builtin_amdgcn_sched_group_barrier(SG_MFMA, kMfmaPer8, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 2 * kMfmaPer, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_a(s + 3, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(fa1, fb1, 2, 5);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_a(s + 3, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(fa1, fb1, 5, 8);
   }
   // drain the last (up to three) stages
   for (; s < nk; ++s) {
     read(s, 1, fa1, fb1);
-    mma8(fa0, fb0);
+    if (s + 2 < nk) { issue_b(s + 2, 0); issue_b(s + 2, 1); }
+    mma(fa0, fb0, 0, 8);
     if (s + 1 < nk) {
       if (s + 2 < nk) wait_vmcnt_4();
       else wait_vmcnt_0();
-      __syncthreads();
+      dma_barrier();
       read(s + 1, 0, fa0, fb0);
     }
-    mma8(fa1, fb1);
+    mma(fa1, fb1, 0, 8);
   }
 }
 
