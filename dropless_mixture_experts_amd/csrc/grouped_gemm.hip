@@ -299,13 +299,7 @@ __device__ __forceinline__ void mainloop(LA& la, LB& lb, int nk, uint4* smem, f3
 // consumed.  The DMA is issued through inline assembly so that the compiler
 // does not serialise every LDS read behind it; completion is tracked with
 // explicit vmcnt waits and one workgroup barrier per stage.
-constexpr int kDmaStages = 4;
-constexpr int kDmaRowBytes = 64;
-constexpr int kDmaCPR = kDmaRowBytes / 16;          // 4 chunks per row
-constexpr int kDmaOpUnits = kTile * kDmaCPR;        // 1024 chunks = 16 KB per operand per stage
-constexpr int kDmaStageUnits = 2 * kDmaOpUnits;     // A then B
-
-__device__ __forceinline__ int dswz_x(int row) { return (row >> 2) & 3; }
+constexpr int kDmaUnits = 8192;                   // LDS of the pipelines: 128 KB in 16-byte units
 
 __device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_byte) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
@@ -315,21 +309,28 @@ __device__ __forceinline__ void wait_vmcnt_8() { asm volatile("s_waitcnt vmcnt(8
 __device__ __forceinline__ void wait_vmcnt_6() { asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); }
 __device__ __forceinline__ void wait_vmcnt_4() { asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); }
 __device__ __forceinline__ void wait_vmcnt_0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void wait_all_0() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory"); }
 
 // ---------------------------------------------------------------------------
-// Eight-wave LDS-DMA main loop.  Two waves per SIMD, each owning a 128 x 64
+// Eight-wave LDS-DMA main loops.  Two waves per SIMD, each owning a 128 x 64
 // block of the 256 x 256 tile (4 x 2 MFMA tiles, 128 accumulators): a single
 // wave per SIMD cannot pull LDS operands fast enough to keep its MFMA pipe busy;
 // two waves per SIMD double the LDS read rate, and each wave's MFMAs cover the
-// other's LDS, barrier and memory waits.  A stage is 32 K values of both
-// operands (16 KB each); each thread issues 2 + 2 DMA per stage.
+// other's LDS, barrier and memory waits.
 //
-// Operand modes (the same 16 KB per stage either way):
+// A stage holds 16 NQ K values of both operands (8 NQ KB each); each wave issues
+// NQ DMA instructions of 1 KB per operand per stage.  NQ = 4 (64-element stages
+// for bf16, two 64 KB buffers) makes every row request a whole 128-byte cache
+// line, which halves the requests the address unit and L1 must process compared
+// with NQ = 2 (32-element stages, four 32 KB buffers, 64-byte half lines); NQ = 2
+// serves K that is a multiple of 64 bytes but not of 128.
+//
+// Operand modes:
 //   OpRow: the tile's rows are K-contiguous global rows (the forward operands and
-//          the data-gradient A).  LDS row = 64 K-bytes = 4 chunks of 16 bytes, the
-//          chunk index XORed with (row >> 2) & 3 so that the 16 lanes of one LDS
-//          cycle (16 consecutive rows, one chunk) hit distinct bank groups.  One
-//          ds_read_b128 gives a lane its 8 K values.
+//          the data-gradient A).  An LDS row holds 32 NQ K-bytes = 2 NQ chunks of
+//          16 bytes, the chunk index XORed with a function of the row chosen so
+//          that the 16 lanes of one LDS cycle (16 consecutive rows, one chunk) hit
+//          distinct bank groups.  One ds_read_b128 gives a lane its 8 K values.
 //   OpCol: the global row index is K and the tile's rows are columns (the K-by-N
 //          weights of the data gradient; both operands of the weight gradient).
 //          LDS row = one K value x 256 columns (512 bytes, whole cache lines from
@@ -341,7 +342,6 @@ __device__ __forceinline__ void wait_vmcnt_0() { asm volatile("s_waitcnt vmcnt(0
 //          consecutive K values of an MFMA operand.  K rows past the valid range
 //          are read from a zero block, so ragged reductions need no LDS clearing.
 constexpr int kThreads8 = 512;
-constexpr int kColRows = 32;                        // K rows per OpCol stage
 constexpr int kColRowBytes = kTile * 2;             // 512 bytes (bf16)
 
 __device__ const uint4 kZero16 = {0u, 0u, 0u, 0u};  // DMA source of rows outside the reduction
@@ -349,37 +349,59 @@ __device__ const uint4 kZero16 = {0u, 0u, 0u, 0u};  // DMA source of rows outsid
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
+template <int NQ>
+struct Stage {
+  static constexpr int kRowBytes = 32 * NQ;           // OpRow K bytes per row
+  static constexpr int kCPR = kRowBytes / 16;         // 16-byte chunks per OpRow row
+  static constexpr int kColRows = 16 * NQ;            // OpCol K rows
+  static constexpr int kOpUnits = kTile * kCPR;       // per operand (8 NQ KB)
+  static constexpr int kUnits = 2 * kOpUnits;         // A then B
+  static constexpr int kBuffers = kDmaUnits / kUnits; // 4 (NQ = 2) or 2 (NQ = 4)
+};
+
+template <int NQ>
 struct OpRow {
-  const char* src[2];  // per DMA instruction q: global address at K offset 0
-  __device__ __forceinline__ const char* at(int q, int st) const { return src[q] + (int64_t)st * kDmaRowBytes; }
-  // operand of the 32 x 16 MFMA tile whose rows start at LDS row rb
-  __device__ __forceinline__ static uint4 frag(const uint4* S, int rb, int kk) {
+  using S = Stage<NQ>;
+  const char* src[NQ];  // per DMA instruction q: global address at K offset 0
+  __device__ __forceinline__ static int swz(int row) { return (row >> (NQ == 2 ? 2 : 1)) & (S::kCPR - 1); }
+  // LDS row filled by this lane in DMA instruction q, and the logical chunk it fetches
+  __device__ __forceinline__ static int dma_row(int q) {
+    return ((threadIdx.x >> 6) * NQ + q) * (64 / S::kCPR) + (threadIdx.x & 63) / S::kCPR;
+  }
+  __device__ __forceinline__ static int dma_chunk(int row) { return ((threadIdx.x & 63) % S::kCPR) ^ swz(row); }
+  __device__ __forceinline__ const char* at(int q, int st) const { return src[q] + (int64_t)st * S::kRowBytes; }
+  // operand of the 32 x 16 MFMA tile whose rows start at LDS row rb (a multiple of 32)
+  __device__ __forceinline__ static uint4 frag(const uint4* L, int rb, int kk) {
     const int lane = threadIdx.x & 63;
     const int l32 = lane & 31, hi = lane >> 5;
-    return S[(rb + l32) * kDmaCPR + ((2 * kk + hi) ^ dswz_x(l32))];
+    return L[(rb + l32) * S::kCPR + ((2 * kk + hi) ^ swz(l32))];
   }
 };
 
+template <int NQ>
 struct OpCol {
-  const char* base[2];  // per DMA instruction q: global address of K row 0 at this lane's columns
-  const char* zero;     // this lane's bytes when its K row or columns are out of range
-  int64_t ld;           // row pitch in bytes
-  int64_t k0, kend;     // first and end K row of the reduction
-  int kr[2];            // per DMA instruction q: K row within the stage
+  using S = Stage<NQ>;
+  // global address of K row 0 at this lane's columns for DMA instruction q: the column
+  // swizzle depends on kr[q] & 3 = (2 q + lane / 32) & 3, so base[q & 1] serves every q
+  const char* base[2];
+  const char* zero;      // this lane's bytes when its K row is out of range
+  int64_t ld;            // row pitch in bytes
+  int64_t k0, kend;      // first and end K row of the reduction
+  int kr[NQ];            // per DMA instruction q: K row within the stage
   __device__ __forceinline__ const char* at(int q, int st) const {
-    const int64_t k = k0 + (int64_t)st * kColRows + kr[q];
-    return k < kend ? base[q] + k * ld : zero;
+    const int64_t k = k0 + (int64_t)st * S::kColRows + kr[q];
+    return k < kend ? base[q & 1] + k * ld : zero;
   }
-  __device__ __forceinline__ static uint4 frag(const uint4* S, int cb, int kk) {
+  __device__ __forceinline__ static uint4 frag(const uint4* L, int cb, int kk) {
     const int lane = threadIdx.x & 63;
     const int hi = lane >> 5, g = (lane >> 4) & 1, e = (lane >> 2) & 3, q = lane & 3;
-    const char* Sb = (const char*)S;
+    const char* Lb = (const char*)L;
     const int seg = ((cb >> 4) + g) ^ (e << 1);
     uint32_t w[4];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int row = 16 * kk + 8 * hi + 4 * t + e;
-      const char* addr = Sb + row * kColRowBytes + seg * 32 + q * 8;
+      const char* addr = Lb + row * kColRowBytes + seg * 32 + q * 8;
       const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)addr);
       w[2 * t] = (uint16_t)v[0] | ((uint32_t)(uint16_t)v[1] << 16);
       w[2 * t + 1] = (uint16_t)v[2] | ((uint32_t)(uint16_t)v[3] << 16);
@@ -387,7 +409,7 @@ struct OpCol {
     return make_uint4(w[0], w[1], w[2], w[3]);
   }
   // set up DMA sources for an operand stored [K rows][ncols] (ld elements per row) whose tile
-  // covers columns [c0, c0 + 256); lanes of DMA instruction q fill LDS K row (wave*2+q)*2 + lane/32
+  // covers columns [c0, c0 + 256); lanes of DMA instruction q fill LDS K row (wave*NQ+q)*2 + lane/32
   __device__ __forceinline__ void init(const void* g, int64_t ld_elems, int64_t c0, int64_t ncols, int64_t kbeg,
                                        int64_t kfin) {
     const int lane = threadIdx.x & 63;
@@ -397,120 +419,202 @@ struct OpCol {
     kend = kfin;
     zero = (const char*)&kZero16;
 #pragma unroll
+    for (int q = 0; q < NQ; ++q) kr[q] = (wave * NQ + q) * 2 + (lane >> 5);
+#pragma unroll
     for (int q = 0; q < 2; ++q) {
-      kr[q] = (wave * 2 + q) * 2 + (lane >> 5);
-      const int u = lane & 31;                                      // physical 16-byte unit in the LDS row
+      const int u = lane & 31;                                          // physical 16-byte unit in the LDS row
       const int lu = (((u >> 1) ^ ((kr[q] & 3) << 1)) << 1) | (u & 1);  // logical unit (8 columns)
       int64_t col = c0 + (int64_t)lu * 8;
-      col = col < ncols ? col : ncols - 8;                         // clamped: only unstored outputs use it
+      col = col < ncols ? col : ncols - 8;                             // clamped: only unstored outputs use it
       base[q] = (const char*)g + col * 2;
     }
   }
 };
 
+template <typename O> struct OpTraits;
+template <int NQ> struct OpTraits<OpRow<NQ>> { static constexpr int kReads = 1; static constexpr int kNQ = NQ; };
+template <int NQ> struct OpTraits<OpCol<NQ>> { static constexpr int kReads = 2; static constexpr int kNQ = NQ; };
+
 // Workgroup barrier without the LDS-drain wait that __syncthreads() implies: the
-// only LDS writes here are DMA, completed by the explicit vmcnt waits, and every
-// LDS read of a buffer about to be refilled has been consumed by an issued MFMA.
+// only LDS writes here are DMA, completed by the explicit vmcnt waits, and the
+// callers wait for their own LDS reads where a buffer is refilled right after.
 // The memory clobber keeps the compiler from moving LDS reads across it.
 __device__ __forceinline__ void dma_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
+// Shared pieces of both main loops: DMA issue, fragment reads and MFMA ranges.
 template <typename T, int EPI, typename OA, typename OB>
-__device__ __forceinline__ void mainloop8(const OA& oa, const OB& ob, int nk, uint4* smem, f32x16 (&acc)[4][2]) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int wm = wave >> 2, wn = wave & 3;
+struct Pipe8 {
+  static constexpr int NQ = OpTraits<OA>::kNQ;
+  using S = Stage<NQ>;
+  // LDS read instructions per sub-step (a transposed fragment takes two)
+  static constexpr int kReads = 4 * OpTraits<OA>::kReads + 2 * OpTraits<OB>::kReads;
+  static constexpr int kMfmaPer = Elem<T>::kVec == 8 ? 1 : 4;  // MFMA instructions per 32 x 32 x 16 step
+  const OA& oa;
+  const OB& ob;
+  uint4* smem;
+  f32x16 (&acc)[4][2];
+  uint32_t wbase;
+  int arow, b_rb[2];
+  __device__ __forceinline__ Pipe8(const OA& a, const OB& b, uint4* sm, f32x16 (&c)[4][2]) : oa(a), ob(b), smem(sm), acc(c) {
+    const int wave = threadIdx.x >> 6;
+    const int wm = wave >> 2, wn = wave & 3;
+    wbase = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)smem + wave * NQ * 1024);
+    arow = wm * 128;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < 2; ++j) b_rb[j] = EPI == EPI_SWIGLU ? (j * 128 + wn * 32) : (wn * 64 + j * 32);
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-  if (nk <= 0) return;
-
-  const uint32_t wbase = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)smem + wave * 2 * 1024);
-  auto lbase = [&](int st) { return wbase + (uint32_t)(st & (kDmaStages - 1)) * (kDmaStageUnits * 16); };
-  auto issue_a = [&](int st, int q) { lds_dma16(oa.at(q, st), lbase(st) + q * 1024); };
-  auto issue_b = [&](int st, int q) { lds_dma16(ob.at(q, st), lbase(st) + kDmaOpUnits * 16 + q * 1024); };
-  int b_rb[2];
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-  for (int j = 0; j < 2; ++j) b_rb[j] = EPI == EPI_SWIGLU ? (j * 128 + wn * 32) : (wn * 64 + j * 32);
-  auto read = [&](int st, int kk, uint4 (&a)[4], uint4 (&b)[2]) {
-    const uint4* S = smem + (st & (kDmaStages - 1)) * kDmaStageUnits;
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  }
+  __device__ __forceinline__ uint32_t lbase(int st) const {
+    return wbase + (uint32_t)(st % S::kBuffers) * (S::kUnits * 16);
+  }
+  __device__ __forceinline__ void issue_a(int st, int q) const { lds_dma16(oa.at(q, st), lbase(st) + q * 1024); }
+  __device__ __forceinline__ void issue_b(int st, int q) const {
+    lds_dma16(ob.at(q, st), lbase(st) + S::kOpUnits * 16 + q * 1024);
+  }
+  __device__ __forceinline__ void read(int st, int kk, uint4 (&a)[4], uint4 (&b)[2]) const {
+    const uint4* L = smem + (st % S::kBuffers) * S::kUnits;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = OA::frag(S, wm * 128 + i * 32, kk);
+    for (int i = 0; i < 4; ++i) a[i] = OA::frag(L, arow + i * 32, kk);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) b[j] = OB::frag(S + kDmaOpUnits, b_rb[j], kk);
-  };
+    for (int j = 0; j < 2; ++j) b[j] = OB::frag(L + S::kOpUnits, b_rb[j], kk);
+  }
   // MFMAs t0 .. t1-1 of a sub-step (t = 2 i + j)
-  auto mma = [&](const uint4 (&a)[4], const uint4 (&b)[2], int t0, int t1) {
+  __device__ __forceinline__ void mma(const uint4 (&a)[4], const uint4 (&b)[2], int t0, int t1) const {
 #pragma unroll
     for (int t = 0; t < 8; ++t)
       if (t >= t0 && t < t1) mma_rows<T>(a[t >> 1], b[t & 1], acc[t >> 1][t & 1]);
-  };
-  // LDS read instructions per sub-step (a transposed fragment takes two)
-  constexpr int kReads = 4 * (std::is_same<OA, OpCol>::value ? 2 : 1) + 2 * (std::is_same<OB, OpCol>::value ? 2 : 1);
-  constexpr int kMfmaPer = Elem<T>::kVec == 8 ? 1 : 4;  // MFMA instructions per 32 x 32 x 16 step
+  }
+  // a sub-step's reads (issued first), then its MFMAs with DMA instructions between them
+  template <typename F>
+  __device__ __forceinline__ void step_with_dma(const uint4 (&a)[4], const uint4 (&b)[2], F&& dma) const {
+    mma(a, b, 0, 1);
+    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, kReads, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, kMfmaPer, 0);
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      __builtin_amdgcn_sched_barrier(0);
+      dma(q);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(a, b, 1 + q * 7 / NQ, 1 + (q + 1) * 7 / NQ);
+    }
+  }
+  __device__ __forceinline__ void step(const uint4 (&a)[4], const uint4 (&b)[2]) const {
+    mma(a, b, 0, 8);
+    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, kReads, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 8 * kMfmaPer, 0);
+  }
+};
 
-  // Stage st is issued in two halves: its A rows one iteration before its B rows.  In
-  // every state below, the DMAs issued after the last one of stage st+1 are exactly the
-  // 4 of stage st+2, so vmcnt(4) (vmcnt(0) at the end) means stage st+1 has landed.
-  issue_a(0, 0); issue_a(0, 1); issue_b(0, 0); issue_b(0, 1);
-  if (nk > 1) { issue_a(1, 0); issue_a(1, 1); issue_b(1, 0); issue_b(1, 1); }
-  if (nk > 2) { issue_a(2, 0); issue_a(2, 1); }
+// 32-element stages (NQ = 2), four buffers.  Stage st is issued in two halves: its A
+// rows one iteration before its B rows.  In every state below, the DMAs issued after
+// the last one of stage st+1 are exactly the 4 of stage st+2, so vmcnt(4) (vmcnt(0)
+// at the end) means stage st+1 has landed.
+template <typename T, int EPI, typename OA, typename OB>
+__device__ __forceinline__ void mainloop8(const OA& oa, const OB& ob, int nk, uint4* smem, f32x16 (&acc)[4][2]) {
+  Pipe8<T, EPI, OA, OB> P(oa, ob, smem, acc);
+  static_assert(Pipe8<T, EPI, OA, OB>::NQ == 2, "four-buffer loop takes 32-element stages");
+  if (nk <= 0) return;
+  P.issue_a(0, 0); P.issue_a(0, 1); P.issue_b(0, 0); P.issue_b(0, 1);
+  if (nk > 1) { P.issue_a(1, 0); P.issue_a(1, 1); P.issue_b(1, 0); P.issue_b(1, 1); }
+  if (nk > 2) { P.issue_a(2, 0); P.issue_a(2, 1); }
   if (nk > 2) wait_vmcnt_6();
   else if (nk > 1) wait_vmcnt_4();
   else wait_vmcnt_0();
   dma_barrier();
   uint4 fa0[4], fb0[2], fa1[4], fb1[2];
-  read(0, 0, fa0, fb0);
+  P.read(0, 0, fa0, fb0);
   int s = 0;
   // steady state, straight-line so that LDS read counts stay exact.  The DMAs are spread
-  // between MFMAs so that the 8 waves do not hand the address unit a burst of 32 at once.
+  // between MFMAs so that the 8 waves do not hand the address unit a burst at once.
   // The B half of stage s+2 reuses the buffer of stage s-2 and the A half of stage s+3
-  // that of stage s-1: every wave finished reading those before the previous barrier.
+  // that of stage s-1: every wave consumed its reads of those before the previous barrier.
   for (; s + 3 < nk; ++s) {
     // region 1: operand reads of sub-step 1, the MFMAs of sub-step 0, B half of stage s+2
-    read(s, 1, fa1, fb1);
-    mma(fa0, fb0, 0, 4);
-    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, kReads, 0);
-    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 4 * kMfmaPer, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    issue_b(s + 2, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(fa0, fb0, 4, 6);
-    __builtin_amdgcn_sched_barrier(0);
-    issue_b(s + 2, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(fa0, fb0, 6, 8);
+    P.read(s, 1, fa1, fb1);
+    P.step_with_dma(fa0, fb0, [&](int q) { P.issue_b(s + 2, q); });
     __builtin_amdgcn_sched_barrier(0);  // keep those MFMAs ahead of the workgroup barrier
     wait_vmcnt_4();
     dma_barrier();
     // region 2: sub-step-0 reads of stage s+1, the MFMAs of sub-step 1, A half of stage s+3
-    read(s + 1, 0, fa0, fb0);
-    mma(fa1, fb1, 0, 2);
-    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, kReads, 0);
-    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 2 * kMfmaPer, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    issue_a(s + 3, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(fa1, fb1, 2, 5);
-    __builtin_amdgcn_sched_barrier(0);
-    issue_a(s + 3, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(fa1, fb1, 5, 8);
+    P.read(s + 1, 0, fa0, fb0);
+    P.step_with_dma(fa1, fb1, [&](int q) { P.issue_a(s + 3, q); });
   }
   // drain the last (up to three) stages
   for (; s < nk; ++s) {
-    read(s, 1, fa1, fb1);
-    if (s + 2 < nk) { issue_b(s + 2, 0); issue_b(s + 2, 1); }
-    mma(fa0, fb0, 0, 8);
+    P.read(s, 1, fa1, fb1);
+    if (s + 2 < nk) { P.issue_b(s + 2, 0); P.issue_b(s + 2, 1); }
+    P.mma(fa0, fb0, 0, 8);
     if (s + 1 < nk) {
       if (s + 2 < nk) wait_vmcnt_4();
       else wait_vmcnt_0();
       dma_barrier();
-      read(s + 1, 0, fa0, fb0);
+      P.read(s + 1, 0, fa0, fb0);
     }
-    mma(fa1, fb1, 0, 8);
+    P.mma(fa1, fb1, 0, 8);
+  }
+}
+
+// 64-element stages (NQ = 4), two buffers, four MFMA sub-steps per stage.  Stage s+1's
+// A half is issued after the barrier of stage s-1 and its B half during the first
+// sub-step of stage s; the barrier of stage s sits before its last sub-step and
+// certifies that stage s+1 has landed (vmcnt(0): nothing is issued after it by then)
+// and that every wave's reads of stage s are complete (lgkmcnt(0)), so stage s+2 may
+// refill that buffer right after it.
+template <typename T, int EPI, typename OA, typename OB>
+__device__ __forceinline__ void mainloop8w(const OA& oa, const OB& ob, int nk, uint4* smem, f32x16 (&acc)[4][2]) {
+  Pipe8<T, EPI, OA, OB> P(oa, ob, smem, acc);
+  static_assert(Pipe8<T, EPI, OA, OB>::NQ == 4, "two-buffer loop takes 64-element stages");
+  if (nk <= 0) return;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) P.issue_a(0, q);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) P.issue_b(0, q);
+  if (nk > 1) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) P.issue_a(1, q);
+    wait_vmcnt_4();
+  } else {
+    wait_vmcnt_0();
+  }
+  dma_barrier();
+  uint4 fa0[4], fb0[2], fa1[4], fb1[2];
+  P.read(0, 0, fa0, fb0);
+  int s = 0;
+  for (; s + 2 < nk; ++s) {
+    P.read(s, 1, fa1, fb1);
+    P.step_with_dma(fa0, fb0, [&](int q) { P.issue_b(s + 1, q); });
+    P.read(s, 2, fa0, fb0);
+    P.step(fa1, fb1);
+    P.read(s, 3, fa1, fb1);
+    P.step(fa0, fb0);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_all_0();
+    dma_barrier();
+    P.read(s + 1, 0, fa0, fb0);
+    P.step_with_dma(fa1, fb1, [&](int q) { P.issue_a(s + 2, q); });
+  }
+  for (; s < nk; ++s) {
+    P.read(s, 1, fa1, fb1);
+    if (s + 1 < nk) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) P.issue_b(s + 1, q);
+    }
+    P.mma(fa0, fb0, 0, 8);
+    P.read(s, 2, fa0, fb0);
+    P.mma(fa1, fb1, 0, 8);
+    P.read(s, 3, fa1, fb1);
+    P.mma(fa0, fb0, 0, 8);
+    if (s + 1 < nk) {
+      wait_all_0();
+      dma_barrier();
+      P.read(s + 1, 0, fa0, fb0);
+    }
+    P.mma(fa1, fb1, 0, 8);
   }
 }
 
@@ -764,40 +868,41 @@ void grouped_gemm_kernel(GemmParams p) {
   store_tile<T, EPI, 4, 4>(p, acc, m0 + wm * 128, re, col);
 }
 
-// Eight-wave grouped GEMM with whole 32-element K stages.  A (activations) is
-// always K-contiguous; B is the N-by-K weight layout (OpRow) or the K-by-N one
-// (OpCol, bf16 only).
-template <typename T, int EPI, int BL>
+// Eight-wave grouped GEMM with whole K stages of 16 NQ elements (bf16; 8 NQ for
+// fp32).  A (activations) is always K-contiguous; B is the N-by-K weight layout
+// (OpRow) or the K-by-N one (OpCol, bf16 only).
+template <int NQ, typename T, int EPI, typename OA, typename OB>
+__device__ __forceinline__ void run_mainloop(const OA& oa, const OB& ob, int nk, uint4* smem, f32x16 (&acc)[4][2]) {
+  if constexpr (NQ == 4) mainloop8w<T, EPI>(oa, ob, nk, smem, acc);
+  else mainloop8<T, EPI>(oa, ob, nk, smem, acc);
+}
+
+template <typename T, int EPI, int BL, int NQ>
 __global__ __launch_bounds__(kThreads8) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void grouped_gemm8_kernel(GemmParams p) {
-  __shared__ uint4 smem[kDmaStages * kDmaStageUnits];
+  __shared__ uint4 smem[kDmaUnits];
   using E = Elem<T>;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
   int g, nt;
   int64_t m0, re;
   if (!find_tile<kThreads8>(p, g, m0, re, nt)) return;
   const int64_t esz = E::kBytes;
   const char* A = (const char*)p.A;
   const char* Bg = (const char*)p.B + (int64_t)g * p.N * p.Kd * esz;
-  OpRow oa;
+  OpRow<NQ> oa;
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int r = (wave * 2 + q) * 16 + (lane >> 2);
-    const int c = (lane & 3) ^ dswz_x(r);
+  for (int q = 0; q < NQ; ++q) {
+    const int r = OpRow<NQ>::dma_row(q);
     int64_t ar = m0 + r;
     ar = ar < p.M ? ar : p.M - 1;
-    oa.src[q] = A + ar * p.Kd * esz + c * 16;
+    oa.src[q] = A + ar * p.Kd * esz + OpRow<NQ>::dma_chunk(r) * 16;
   }
-  const int nk = (int)(p.Kd * esz / kDmaRowBytes);
+  const int nk = (int)(p.Kd * esz / Stage<NQ>::kRowBytes);
   f32x16 acc[4][2];
   if constexpr (BL == LAYOUT_NK) {
-    OpRow ob;
+    OpRow<NQ> ob;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int r = (wave * 2 + q) * 16 + (lane >> 2);
-      const int c = (lane & 3) ^ dswz_x(r);
+    for (int q = 0; q < NQ; ++q) {
+      const int r = OpRow<NQ>::dma_row(q);
       int64_t br;
       if (EPI == EPI_SWIGLU) {
         const int64_t F = p.N / 2;
@@ -807,14 +912,15 @@ void grouped_gemm8_kernel(GemmParams p) {
         br = (int64_t)nt * kTile + r;
         br = br < p.N ? br : p.N - 1;
       }
-      ob.src[q] = Bg + br * p.Kd * esz + c * 16;
+      ob.src[q] = Bg + br * p.Kd * esz + OpRow<NQ>::dma_chunk(r) * 16;
     }
-    mainloop8<T, EPI>(oa, ob, nk, smem, acc);
+    run_mainloop<NQ, T, EPI>(oa, ob, nk, smem, acc);
   } else {
-    OpCol ob;
+    OpCol<NQ> ob;
     ob.init(Bg, p.N, (int64_t)nt * kTile, p.N, 0, p.Kd);
-    mainloop8<T, EPI>(oa, ob, nk, smem, acc);
+    run_mainloop<NQ, T, EPI>(oa, ob, nk, smem, acc);
   }
+  const int wave = threadIdx.x >> 6;
   const int wm = wave >> 2, wn = wave & 3;
   int64_t col[2];
 #pragma unroll
@@ -916,9 +1022,10 @@ void grouped_wgrad_kernel(WgradParams p) {
 // fill the machine at the end instead of a few long ones trailing.  The XCD
 // remap is applied per window of 256 blocks, which keeps that order in time
 // while each XCD still runs contiguous tiles of a window.
+template <int NQ>
 __global__ __launch_bounds__(kThreads8) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void grouped_wgrad8_kernel(WgradParams p) {
-  __shared__ uint4 smem[kDmaStages * kDmaStageUnits];
+  __shared__ uint4 smem[kDmaUnits];
   __shared__ int s_rows[kThreads8];
   __shared__ int s_group;
   const int tid = threadIdx.x;
@@ -957,24 +1064,30 @@ void grouped_wgrad8_kernel(WgradParams p) {
   int64_t rs, re;
   group_rows(p.offs, g, p.M, rs, re);
   const int64_t n0 = (int64_t)tn * kTile, k0 = (int64_t)tk * kTile;
-  const int nk = (int)((re - rs + kColRows - 1) / kColRows);
-  OpCol oa, ob;
+  const int nk = (int)((re - rs + Stage<NQ>::kColRows - 1) / Stage<NQ>::kColRows);
+  OpCol<NQ> oa, ob;
   oa.init(p.dY, p.N, n0, p.N, rs, re);
   ob.init(p.X, p.Kd, k0, p.Kd, rs, re);
   f32x16 acc[4][2];
-  mainloop8<bf16_t, EPI_NONE>(oa, ob, nk, smem, acc);  // zeros when the group is empty
+  run_mainloop<NQ, bf16_t, EPI_NONE>(oa, ob, nk, smem, acc);  // zeros when the group is empty
 
   const int wm = wave >> 2, wn = wave & 3;
   if (p.accumulate && nk == 0) return;  // accumulate mode leaves an empty group's dW as it is
   store_wgrad<4, 2>(p.dW + (int64_t)g * p.N * p.Kd, acc, n0 + wm * 128, k0 + wn * 64, p.N, p.Kd, p.accumulate);
 }
 
+// nq: DMA instructions per wave per operand per stage (4: 64-element stages, 2: 32-element
+// stages), 0 for the register-staged kernel
 template <typename T>
-hipError_t gemm_dispatch(const GemmParams& prm, int b_layout, int epi, bool dma, dim3 grid, hipStream_t s) {
+hipError_t gemm_dispatch(const GemmParams& prm, int b_layout, int epi, int nq, dim3 grid, hipStream_t s) {
 #define MOE_GG(BL, EP) hipLaunchKernelGGL((grouped_gemm_kernel<T, BL, EP>), grid, dim3(kThreads), 0, s, prm)
-#define MOE_GG8(EP, BL) hipLaunchKernelGGL((grouped_gemm8_kernel<T, EP, BL>), grid, dim3(kThreads8), 0, s, prm)
+#define MOE_GG8(EP, BL)                                                                                   \
+  do {                                                                                                    \
+    if (nq == 4) hipLaunchKernelGGL((grouped_gemm8_kernel<T, EP, BL, 4>), grid, dim3(kThreads8), 0, s, prm); \
+    else hipLaunchKernelGGL((grouped_gemm8_kernel<T, EP, BL, 2>), grid, dim3(kThreads8), 0, s, prm);        \
+  } while (0)
   if (b_layout == LAYOUT_NK) {
-    if (dma) {
+    if (nq) {
       if (epi == EPI_NONE) MOE_GG8(EPI_NONE, LAYOUT_NK);
       else if (epi == EPI_SWIGLU) MOE_GG8(EPI_SWIGLU, LAYOUT_NK);
       else MOE_GG8(EPI_DSWIGLU, LAYOUT_NK);
@@ -986,7 +1099,7 @@ hipError_t gemm_dispatch(const GemmParams& prm, int b_layout, int epi, bool dma,
   } else {
     if (epi == EPI_SWIGLU) return hipErrorInvalidValue;
     if constexpr (std::is_same<T, bf16_t>::value) {
-      if (dma) {
+      if (nq) {
         if (epi == EPI_NONE) MOE_GG8(EPI_NONE, LAYOUT_KN);
         else MOE_GG8(EPI_DSWIGLU, LAYOUT_KN);
         return hipGetLastError();
@@ -1010,13 +1123,13 @@ hipError_t launch_grouped_gemm(const void* A, const void* B, int b_layout, const
   prm.NT = (epilogue == EPI_SWIGLU) ? (int)((N / 2 + 127) / 128) : (int)((N + kTile - 1) / kTile);
   const int64_t max_mt = (M + kTile - 1) / kTile + G;
   const dim3 grid((unsigned)(max_mt * prm.NT));
-  // the LDS-DMA pipeline needs whole 64-byte K stages of A, 16-byte aligned rows of
-  // B in the K-by-N layout, and 16-byte aligned operands
+  // the LDS-DMA pipelines need whole K stages of A (128 or 64 bytes per row), 16-byte
+  // aligned rows of B in the K-by-N layout, and 16-byte aligned operands
   const int64_t kbytes = Kd * (dtype == 1 ? 2 : 4);
-  const bool aligned = ((uintptr_t)A | (uintptr_t)B) % 16 == 0;
-  const bool dma = aligned && kbytes % kDmaRowBytes == 0 && (b_layout == LAYOUT_NK || N % 8 == 0);
-  if (dtype == 1) return gemm_dispatch<bf16_t>(prm, b_layout, epilogue, dma, grid, s);
-  return gemm_dispatch<float>(prm, b_layout, epilogue, dma, grid, s);
+  const bool aligned = ((uintptr_t)A | (uintptr_t)B) % 16 == 0 && (b_layout == LAYOUT_NK || N % 8 == 0);
+  const int nq = !aligned ? 0 : kbytes % Stage<4>::kRowBytes == 0 ? 4 : kbytes % Stage<2>::kRowBytes == 0 ? 2 : 0;
+  if (dtype == 1) return gemm_dispatch<bf16_t>(prm, b_layout, epilogue, nq, grid, s);
+  return gemm_dispatch<float>(prm, b_layout, epilogue, nq, grid, s);
 }
 
 hipError_t launch_grouped_wgrad(const void* X, const void* dY, const int32_t* offs, int64_t M,
@@ -1029,7 +1142,7 @@ hipError_t launch_grouped_wgrad(const void* X, const void* dY, const int32_t* of
   // the LDS-DMA pipeline moves 16-byte pieces of rows: bf16 widths that are multiples of 8
   const bool dma = dtype == 1 && N % 8 == 0 && Kd % 8 == 0 && ((uintptr_t)X | (uintptr_t)dY) % 16 == 0;
   if (dma)
-    hipLaunchKernelGGL(grouped_wgrad8_kernel, grid, dim3(kThreads8), 0, s, prm);
+    hipLaunchKernelGGL(grouped_wgrad8_kernel<4>, grid, dim3(kThreads8), 0, s, prm);
   else if (dtype == 1)
     hipLaunchKernelGGL((grouped_wgrad_kernel<bf16_t>), grid, dim3(kThreads), 0, s, prm);
   else
