@@ -739,10 +739,10 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const f32x16 (&a
 // memory; false when this workgroup has no tile.  Uniform over the workgroup.
 template <int NTHR>
 __device__ __forceinline__ bool find_tile(const GemmParams& p, int& g_out, int64_t& m0_out, int64_t& re_out,
-                                          int& nt_out) {
+                                          int& nt_out, int* scratch) {
   constexpr int NW = NTHR / 64;
-  __shared__ int s_wtot[NW];
-  __shared__ int s_res[2];
+  int* s_wtot = scratch;       // NW ints
+  int* s_res = scratch + NW;   // 2 ints
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -819,7 +819,8 @@ void grouped_gemm_kernel(GemmParams p) {
   const int wave = tid >> 6;
   int g, nt;
   int64_t m0, re;
-  if (!find_tile<kThreads>(p, g, m0, re, nt)) return;
+  __shared__ int s_find[kThreads / 64 + 2];
+  if (!find_tile<kThreads>(p, g, m0, re, nt, s_find)) return;
 
   // ---- operands
   const int64_t esz = E::kBytes;
@@ -884,7 +885,8 @@ void grouped_gemm8_kernel(GemmParams p) {
   using E = Elem<T>;
   int g, nt;
   int64_t m0, re;
-  if (!find_tile<kThreads8>(p, g, m0, re, nt)) return;
+  __shared__ int s_find[kThreads8 / 64 + 2];
+  if (!find_tile<kThreads8>(p, g, m0, re, nt, s_find)) return;
   const int64_t esz = E::kBytes;
   const char* A = (const char*)p.A;
   const char* Bg = (const char*)p.B + (int64_t)g * p.N * p.Kd * esz;
@@ -927,6 +929,259 @@ void grouped_gemm8_kernel(GemmParams p) {
   for (int j = 0; j < 2; ++j)
     col[j] = EPI == EPI_SWIGLU ? (int64_t)nt * 128 + wn * 32 : (int64_t)nt * kTile + wn * 64 + j * 32;
   store_tile<T, EPI, 4, 2>(p, acc, m0 + wm * 128, re, col);
+}
+
+// ---------------------------------------------------------------------------
+// Four-wave grouped GEMM on a five-slot LDS ring (bf16, N-by-K weights).
+//
+// One wave per SIMD owns a 128 x 128 block of the 256 x 256 tile (4 x 4 MFMA
+// tiles, 256 accumulators): per 16-element K step a wave reads 8 operand
+// fragments for 16 MFMAs, a third fewer LDS reads per flop than two waves of
+// 128 x 64 per SIMD.  Stages are 64 K elements, so every DMA row request is a
+// whole 128-byte line.  LDS is a ring of five 32 KB slots, each holding one
+// operand of one stage (half-stage h: A of stage h/2 when h is even, B when odd,
+// in slot h mod 5).  The two slots of stage s are released together by the
+// barrier that follows the last operand reads of stage s; the ring then holds
+// stage s+1 (landed), the A half of stage s+2 (in flight) and two free slots, so
+// the loads run up to a stage and a half ahead of the MFMAs instead of one.
+//
+// Per stage s the wave issues: the A half of stage s+2 spread over the MFMAs of
+// sub-steps 0..2, then, right after the barrier, the B half of stage s+2 within
+// sub-step 3.  The barrier waits for stage s+1 only (vmcnt(8): the 8 DMAs of the
+// A half of stage s+2 may still be in flight).
+namespace ring4 {
+
+constexpr int kThreads = 256;
+constexpr int kSlotUnits = 256 * 8;       // one operand of one stage: 256 rows x 8 chunks of 16 B
+constexpr int kSlotBytes = kSlotUnits * 16;
+constexpr int kSlots = 5;                 // 160 KB: all of a CU's LDS
+constexpr int kQ = 8;                     // DMA instructions per wave per half-stage (8 rows x 128 B each)
+constexpr int kStageBytes = 128;          // K bytes per row per stage
+
+// 16-byte chunk XOR of an LDS row (8 chunks): the 16 lanes served by one LDS cycle
+// (16 consecutive rows, one logical chunk) hit 16 distinct 16-byte bank groups
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+
+// global_load_lds_dwordx4 with a uniform 64-bit base and a 32-bit per-lane offset;
+// lane L lands at M0 + 16 L
+__device__ __forceinline__ void dma(const char* sbase, uint32_t voff, uint32_t lds_byte) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 offset:0"
+               :: "v"(voff), "s"(sbase), "s"(lds_byte) : "memory", "m0");
+}
+
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ const char* uniform_ptr(const char* p) { return (const char*)uniform64((int64_t)p); }
+
+template <int EPI>
+struct Pipe {
+  const char* a_base;   // uniform: A at (first tile row, K = 0)
+  const char* b_base;   // uniform: B at (first tile row, K = 0)
+  uint32_t va[kQ], vb[kQ];
+  uint32_t lds_w;       // uniform: LDS byte address of slot 0 + this wave's DMA block
+  uint32_t a_off, b_off[4];  // per lane: byte offset of fragment row l32 within a slot
+  uint32_t ch[4];            // per lane: byte offset of the 16-byte chunk of sub-step kk
+  const char* L;
+  f32x16 (&acc)[4][4];
+
+  __device__ __forceinline__ Pipe(f32x16 (&c)[4][4], uint4* smem) : acc(c) {
+    L = (const char*)smem;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int l32 = lane & 31, hi = lane >> 5;
+    lds_w = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)smem + wave * kQ * 1024);
+    a_off = (wm * 128 + l32) * 128;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      b_off[j] = ((EPI == EPI_SWIGLU ? ((j >> 1) * 128 + wn * 64 + (j & 1) * 32) : (wn * 128 + j * 32)) + l32) * 128;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) ch[kk] = ((2 * kk + hi) ^ swz(l32)) * 16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  }
+  // DMA q of operand OP (0: A, 1: B) of stage st, i.e. of half-stage 2 st + OP
+  template <int OP>
+  __device__ __forceinline__ void issue(int st, int q) const {
+    const uint32_t lb = lds_w + (uint32_t)((2 * st + OP) % kSlots) * kSlotBytes + q * 1024;
+    const int64_t ko = (int64_t)st * kStageBytes;
+    if (OP) dma(b_base + ko, vb[q], lb);
+    else dma(a_base + ko, va[q], lb);
+  }
+  __device__ __forceinline__ void read(int s, int kk, uint4 (&a)[4], uint4 (&b)[4]) const {
+    const uint32_t sa = (uint32_t)((2 * s) % kSlots) * kSlotBytes;
+    const uint32_t sb = (uint32_t)((2 * s + 1) % kSlots) * kSlotBytes;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = *(const uint4*)(L + sa + a_off + i * 4096 + ch[kk]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = *(const uint4*)(L + sb + b_off[j] + ch[kk]);
+  }
+  // fragment r of sub-step kk of stage s: r < 4 the A fragment of rows 32 r, else B fragment r - 4
+  __device__ __forceinline__ void read1(int s, int kk, int r, uint4 (&a)[4], uint4 (&b)[4]) const {
+    if (r < 4) a[r] = *(const uint4*)(L + (uint32_t)((2 * s) % kSlots) * kSlotBytes + a_off + r * 4096 + ch[kk]);
+    else b[r - 4] = *(const uint4*)(L + (uint32_t)((2 * s + 1) % kSlots) * kSlotBytes + b_off[r - 4] + ch[kk]);
+  }
+  __device__ __forceinline__ void mma(const uint4 (&a)[4], const uint4 (&b)[4], int t0, int t1) const {
+#pragma unroll
+    for (int t = 0; t < 16; ++t)
+      if (t >= t0 && t < t1) mma_rows<bf16_t>(a[t >> 2], b[t & 3], acc[t >> 2][t & 3]);
+  }
+  // one sub-step's 16 MFMAs with DMAs Q0 .. Q1-1 of operand OP of stage st spread between them
+  template <int OP, int Q0, int Q1>
+  __device__ __forceinline__ void step_dma(const uint4 (&a)[4], const uint4 (&b)[4], int st) const {
+    constexpr int n = Q1 - Q0;
+#pragma unroll
+    for (int q = 0; q < n; ++q) {
+      mma(a, b, q * 16 / n, (q + 1) * 16 / n);
+      __builtin_amdgcn_sched_barrier(0);
+      issue<OP>(st, Q0 + q);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  __device__ __forceinline__ void step(const uint4 (&a)[4], const uint4 (&b)[4]) const { mma(a, b, 0, 16); }
+};
+
+__device__ __forceinline__ void wait_vm8_lgkm0() { asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void wait_vm18() { asm volatile("s_waitcnt vmcnt(18)" ::: "memory"); }
+__device__ __forceinline__ void wait_vm16() { asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); }
+
+// Operand fragments of the four sub-steps of a stage: set u holds sub-step u.
+struct Frags {
+  uint4 a[4][4], b[4][4];
+};
+
+// One sub-step: the 16 MFMAs of set CUR, one LDS read after each of them when RD (the
+// fragments of sub-steps R0 and R0 + 1 of stage rs, into their sets), and DMAs Q0 .. Q1-1
+// of operand OP of stage st spread between them.
+template <int EPI, int CUR, bool RD, int R0, int OP, int Q0, int Q1>
+__device__ __forceinline__ void substep(const Pipe<EPI>& P, Frags& f, int rs, int st) {
+  constexpr int n = Q1 - Q0;
+#pragma unroll
+  for (int t = 0; t < 16; ++t) {
+    P.mma(f.a[CUR], f.b[CUR], t, t + 1);
+    if (RD) {
+      if (t < 8) P.read1(rs, R0, t, f.a[R0], f.b[R0]);
+      else P.read1(rs, R0 + 1, t - 8, f.a[R0 + 1], f.b[R0 + 1]);
+    }
+#pragma unroll
+    for (int q = 0; q < n; ++q)
+      if (t == (2 * q + 1) * 16 / (2 * n)) P.template issue<OP>(st, Q0 + q);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// One stage.  Sub-step 0 reads the fragments of sub-steps 2 and 3, sub-step 2 those of
+// sub-steps 0 and 1 of the next stage, so every read has at least a sub-step of MFMAs
+// to land; the barrier sits between sub-steps 1 and 2, after the last reads of the
+// stage.  Loads: the A half of stage s+2 (DMAs 2..7) in sub-steps 0 and 1, the B half of
+// stage s+2 in sub-step 2 and DMAs 0..1 of the A half of stage s+3 in sub-step 3.
+// LOADS = 2: all of those; 1: no A half of stage s+3; 0: none.  VMC: the vmcnt the
+// barrier waits for (the DMAs issued after the B half of stage s+1).
+template <int EPI, int LOADS, bool NEXT, int VMC>
+__device__ __forceinline__ void stage(const Pipe<EPI>& P, int s, Frags& f) {
+  constexpr int L1 = LOADS ? 1 : 0, L2 = LOADS == 2 ? 1 : 0;
+  substep<EPI, 0, true, 2, 0, 2, 2 + 3 * L1>(P, f, s, s + 2);
+  substep<EPI, 1, false, 0, 0, 5, 5 + 3 * L1>(P, f, s, s + 2);
+  if (NEXT) {
+    if (VMC == 8) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    dma_barrier();  // stage s+1 landed and visible; every read of stage s done
+  }
+  substep<EPI, 2, NEXT, 0, 1, 0, 8 * L1>(P, f, s + 1, s + 2);
+  substep<EPI, 3, false, 0, 0, 0, 2 * L2>(P, f, s + 1, s + 3);
+}
+
+template <int EPI>
+__device__ __forceinline__ void mainloop(Pipe<EPI>& P, int nk) {
+  if (nk <= 0) return;
+  // prologue: stages 0 and 1, and DMAs 0..1 of the A half of stage 2
+#pragma unroll
+  for (int q = 0; q < kQ; ++q) P.template issue<0>(0, q);
+#pragma unroll
+  for (int q = 0; q < kQ; ++q) P.template issue<1>(0, q);
+  if (nk > 1) {
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) P.template issue<0>(1, q);
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) P.template issue<1>(1, q);
+  }
+  if (nk > 2) {
+    P.template issue<0>(2, 0);
+    P.template issue<0>(2, 1);
+    wait_vm18();
+  } else if (nk > 1) {
+    wait_vm16();
+  } else {
+    wait_all_0();
+  }
+  dma_barrier();
+  Frags f;
+  P.read(0, 0, f.a[0], f.b[0]);
+  P.read(0, 1, f.a[1], f.b[1]);
+  __builtin_amdgcn_sched_barrier(0);
+  int s = 0;
+  for (; s + 3 < nk; ++s) stage<EPI, 2, true, 8>(P, s, f);
+  if (s + 2 < nk) stage<EPI, 1, true, 8>(P, s++, f);
+  if (s + 1 < nk) stage<EPI, 0, true, 0>(P, s++, f);
+  stage<EPI, 0, false, 0>(P, s, f);
+}
+
+}  // namespace ring4
+
+template <int EPI>
+__global__ __launch_bounds__(ring4::kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void grouped_gemm_ring4_kernel(GemmParams p) {
+  using namespace ring4;
+  __shared__ uint4 smem[kSlots * kSlotUnits];
+  int g, nt;
+  int64_t m0, re;
+  if (!find_tile<ring4::kThreads>(p, g, m0, re, nt, (int*)smem)) return;
+  __syncthreads();  // every thread has read the tile from the scratch that the loads overwrite
+  g = __builtin_amdgcn_readfirstlane(g);
+  nt = __builtin_amdgcn_readfirstlane(nt);
+  m0 = uniform64(m0);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t ldb = p.Kd * 2;
+
+  f32x16 acc[4][4];
+  Pipe<EPI> P(acc, smem);
+  P.a_base = uniform_ptr((const char*)p.A + m0 * ldb);
+  const int64_t b0row = EPI == EPI_SWIGLU ? (int64_t)nt * 128 : (int64_t)nt * 256;
+  P.b_base = uniform_ptr((const char*)p.B + ((int64_t)g * p.N + b0row) * ldb);
+#pragma unroll
+  for (int q = 0; q < kQ; ++q) {
+    const int r = (wave * kQ + q) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ swz(r);
+    int64_t ar = m0 + r;
+    ar = ar < p.M ? ar : p.M - 1;
+    P.va[q] = (uint32_t)((ar - m0) * ldb + c * 16);
+    int64_t br;
+    if (EPI == EPI_SWIGLU) {
+      const int64_t F = p.N / 2;
+      int64_t cc = (int64_t)nt * 128 + (r & 127);
+      cc = cc < F ? cc : F - 1;
+      br = (r < 128 ? 0 : F) + cc;
+    } else {
+      br = (int64_t)nt * 256 + r;
+      br = br < p.N ? br : p.N - 1;
+    }
+    P.vb[q] = (uint32_t)((br - b0row) * ldb + c * 16);
+  }
+  const int nk = (int)(ldb / kStageBytes);
+  mainloop<EPI>(P, nk);
+
+  const int wm = wave >> 1, wn = wave & 1;
+  int64_t col[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    col[j] = EPI == EPI_SWIGLU ? (int64_t)nt * 128 + wn * 64 + (j & 1) * 32 : (int64_t)nt * 256 + wn * 128 + j * 32;
+  store_tile<bf16_t, EPI, 4, 4>(p, acc, m0 + wm * 128, re, col);
 }
 
 // ---------------------------------------------------------------------------
@@ -1128,6 +1383,15 @@ hipError_t launch_grouped_gemm(const void* A, const void* B, int b_layout, const
   const int64_t kbytes = Kd * (dtype == 1 ? 2 : 4);
   const bool aligned = ((uintptr_t)A | (uintptr_t)B) % 16 == 0 && (b_layout == LAYOUT_NK || N % 8 == 0);
   const int nq = !aligned ? 0 : kbytes % Stage<4>::kRowBytes == 0 ? 4 : kbytes % Stage<2>::kRowBytes == 0 ? 2 : 0;
+  // the ring kernel: bf16, N-by-K weights, whole 128-byte K stages, per-lane DMA offsets within 32 bits
+  if (dtype == 1 && nq == 4 && b_layout == LAYOUT_NK && epilogue != EPI_DSWIGLU &&
+      (N + 256) * kbytes < ((int64_t)1 << 32)) {
+    if (epilogue == EPI_SWIGLU)
+      hipLaunchKernelGGL(grouped_gemm_ring4_kernel<EPI_SWIGLU>, grid, dim3(ring4::kThreads), 0, s, prm);
+    else
+      hipLaunchKernelGGL(grouped_gemm_ring4_kernel<EPI_NONE>, grid, dim3(ring4::kThreads), 0, s, prm);
+    return hipGetLastError();
+  }
   if (dtype == 1) return gemm_dispatch<bf16_t>(prm, b_layout, epilogue, nq, grid, s);
   return gemm_dispatch<float>(prm, b_layout, epilogue, nq, grid, s);
 }
