@@ -26,6 +26,7 @@
 //     so concurrently running tiles share operands in that XCD's L2.
 //   * Epilogues: plain store; SwiGLU (gate and up columns of one output column
 //     live in the same lane); SwiGLU backward using the saved pre-activations.
+#include <algorithm>
 #include <cstdint>
 #include <type_traits>
 
@@ -645,6 +646,11 @@ struct GemmParams {
   int NT;  // column tiles
 };
 
+// Logistic sigmoid for the SwiGLU epilogues: the hardware exponential and reciprocal
+// (about 1 ulp each) instead of an IEEE division, far below the bf16 rounding of the
+// outputs and within the fp32 tolerance.
+__device__ __forceinline__ float sigmoid_fast(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
+
 // Epilogue of one wave: acc[i][j] is the 32 x 32 tile at rows row0 + 32 i and
 // columns col[j]; a lane holds row (lane & 31) at columns 8 q + 4 (lane / 32) + 0..3
 // in acc[i][j][4 q .. 4 q + 3].  Widths are multiples of 8 elements, so a run of 4
@@ -687,7 +693,7 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const f32x16 (&a
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const float v = acc[i][j0 + jj][4 * q + e], g = gt[jj][q][e], u = up[jj][q][e];
-              const float sg = 1.f / (1.f + __expf(-g));
+              const float sg = sigmoid_fast(g);
               da[e] = v * u * sg * (1.f + g * (1.f - sg));
               du[e] = v * g * sg;
             }
@@ -700,6 +706,8 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const f32x16 (&a
     if (row >= re) continue;
     if constexpr (EPI == EPI_SWIGLU) {
       const int64_t F = p.N / 2;
+      char* hrow = (char*)p.C + row * F * E::kBytes;
+      char* srow = p.epi_save ? (char*)p.epi_save + row * p.N * E::kBytes : nullptr;
 #pragma unroll
       for (int j = 0; j < NJ / 2; ++j)
 #pragma unroll
@@ -711,15 +719,16 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const f32x16 (&a
           for (int e = 0; e < 4; ++e) {
             g[e] = acc[i][j][4 * q + e];
             u[e] = acc[i][j + NJ / 2][4 * q + e];
-            h[e] = g[e] / (1.f + __expf(-g[e])) * u[e];
+            h[e] = g[e] * sigmoid_fast(g[e]) * u[e];
           }
-          E::store4(p.C, row * F + c, h);
-          if (p.epi_save) {
-            E::store4(p.epi_save, row * p.N + c, g);
-            E::store4(p.epi_save, row * p.N + F + c, u);
+          E::store4(hrow, c, h);
+          if (srow) {
+            E::store4(srow, c, g);
+            E::store4(srow, F + c, u);
           }
         }
     } else {
+      char* crow = (char*)p.C + row * p.N * E::kBytes;
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
 #pragma unroll
@@ -729,7 +738,7 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const f32x16 (&a
           float v[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e];
-          E::store4(p.C, row * p.N + c, v);
+          E::store4(crow, c, v);
         }
     }
   }
@@ -957,6 +966,7 @@ constexpr int kSlotBytes = kSlotUnits * 16;
 constexpr int kSlots = 5;                 // 160 KB: all of a CU's LDS
 constexpr int kQ = 8;                     // DMA instructions per wave per half-stage (8 rows x 128 B each)
 constexpr int kStageBytes = 128;          // K bytes per row per stage
+constexpr int kMaxGroups = 256;           // groups held by the register table (4 per lane)
 
 // 16-byte chunk XOR of an LDS row (8 chunks): the 16 lanes served by one LDS cycle
 // (16 consecutive rows, one logical chunk) hit 16 distinct 16-byte bank groups
@@ -976,12 +986,82 @@ __device__ __forceinline__ int64_t uniform64(int64_t v) {
 }
 __device__ __forceinline__ const char* uniform_ptr(const char* p) { return (const char*)uniform64((int64_t)p); }
 
+// Row tiles of every group, held in registers by each wave: lane l keeps groups l + 64 i
+// (i < 4): first row, end row and the inclusive prefix sum of 256-row tiles.
+struct GroupTable {
+  int lo[4], hi[4], incl[4];
+  int total_mt;  // uniform: row tiles over all groups
+};
+
+__device__ __forceinline__ void build_table(const GemmParams& p, GroupTable& t) {
+  const int lane = threadIdx.x & 63;
+  int carry = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int g = lane + 64 * i;
+    int64_t rs = 0, re = 0;
+    if (g < p.G) group_rows(p.offs, g, p.M, rs, re);
+    int x = (int)((re - rs + 255) / 256);
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(x, o, 64);
+      if (lane >= o) x += u;
+    }
+    t.incl[i] = x + carry;
+    t.lo[i] = (int)rs;
+    t.hi[i] = (int)re;
+    carry += __shfl(x, 63, 64);
+  }
+  t.total_mt = __builtin_amdgcn_readfirstlane(carry);
+}
+
+__device__ __forceinline__ int pick(const int (&v)[4], int i) {
+  return i == 0 ? v[0] : i == 1 ? v[1] : i == 2 ? v[2] : v[3];
+}
+
+// Tile L of the workgroup order -> (group, first row, end row, column tile), uniform.
+// The order is the XCD-aware one of the other kernels: each XCD takes a contiguous run
+// of tiles, 8 row tiles sharing each column tile.  Tile counts fit in 31 bits (checked
+// on the host).
+struct TileInfo {
+  int g, nt, m0, re;
+};
+__device__ __forceinline__ TileInfo lookup(const GroupTable& t, int L, int total, int NT) {
+  const int xcd = L % kXcd, local = L / kXcd;
+  const int q = total / kXcd, r = total % kXcd;
+  const int Lr = xcd * q + (xcd < r ? xcd : r) + local;
+  const int per = kGroupM * NT;
+  const int grp = Lr / per;
+  const int first = grp * kGroupM;
+  const int gm = min(t.total_mt - first, kGroupM);
+  const int rem = Lr - grp * per;
+  const int mt = first + rem % gm;
+  TileInfo ti;
+  ti.nt = rem / gm;
+  // the group is the number of groups whose row tiles end at or before mt
+  int cnt = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) cnt += __popcll(__ballot(t.incl[i] <= mt));
+  ti.g = cnt;
+  const int sl = cnt >> 6, ln = cnt & 63;
+  const int incl = __builtin_amdgcn_readlane(pick(t.incl, sl), ln);
+  const int lo = __builtin_amdgcn_readlane(pick(t.lo, sl), ln);
+  const int hi = __builtin_amdgcn_readlane(pick(t.hi, sl), ln);
+  const int rt = (hi - lo + 255) / 256;
+  ti.m0 = lo + (mt - (incl - rt)) * 256;
+  ti.re = hi;
+  return ti;
+}
+
 template <int EPI>
 struct Pipe {
-  const char* a_base;   // uniform: A at (first tile row, K = 0)
-  const char* b_base;   // uniform: B at (first tile row, K = 0)
+  // loads (the producer runs two stages ahead of the MFMAs, across tile boundaries)
+  const char* a_base;   // uniform: A at (first row of the producer's tile, K = 0)
+  const char* b_base;   // uniform: B at (first row of the producer's tile, K = 0)
+  int p_begin;          // uniform: workgroup stage of the producer tile's first stage
   uint32_t va[kQ], vb[kQ];
   uint32_t lds_w;       // uniform: LDS byte address of slot 0 + this wave's DMA block
+  // operand reads
   uint32_t a_off, b_off[4];  // per lane: byte offset of fragment row l32 within a slot
   uint32_t ch[4];            // per lane: byte offset of the 16-byte chunk of sub-step kk
   const char* L;
@@ -999,6 +1079,9 @@ struct Pipe {
       b_off[j] = ((EPI == EPI_SWIGLU ? ((j >> 1) * 128 + wn * 64 + (j & 1) * 32) : (wn * 128 + j * 32)) + l32) * 128;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) ch[kk] = ((2 * kk + hi) ^ swz(l32)) * 16;
+    zero();
+  }
+  __device__ __forceinline__ void zero() {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -1006,13 +1089,36 @@ struct Pipe {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
   }
-  // DMA q of operand OP (0: A, 1: B) of stage st, i.e. of half-stage 2 st + OP
+  // point the loads at tile (g, m0, nt), whose first stage is workgroup stage begin.  Row
+  // offsets are 32-bit (the host checks (N + 256) rows of B fit): rows past the end of A,
+  // or of the gate or up half of B, are clamped to the last row (their outputs are not stored).
+  __device__ __forceinline__ void retarget(const GemmParams& p, int g, int m0, int nt, int begin) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint32_t ldb = (uint32_t)p.Kd * 2;
+    p_begin = begin;
+    a_base = uniform_ptr((const char*)p.A + (int64_t)m0 * ldb);
+    const int b0row = EPI == EPI_SWIGLU ? nt * 128 : nt * 256;
+    b_base = uniform_ptr((const char*)p.B + ((int64_t)g * p.N + b0row) * ldb);
+    const int amax = (int)p.M - 1 - m0;  // last valid row of A, relative to m0
+    const int F = (int)(EPI == EPI_SWIGLU ? p.N / 2 : p.N);
+    const int bmax = F - 1 - b0row;       // last valid gate (or plain) row, relative to b0row
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) {
+      const int r = (wave * kQ + q) * 8 + (lane >> 3);
+      const uint32_t c16 = (uint32_t)(((lane & 7) ^ swz(r)) * 16);
+      va[q] = (uint32_t)min(r, amax) * ldb + c16;
+      // up rows: F + min(b0row + r - 128, F - 1), relative to b0row
+      const int rb = EPI == EPI_SWIGLU ? (r < 128 ? min(r, bmax) : F + min(r - 128, bmax)) : min(r, bmax);
+      vb[q] = (uint32_t)rb * ldb + c16;
+    }
+  }
+  // DMA q of operand OP (0: A, 1: B) of workgroup stage gs, i.e. of half-stage 2 gs + OP
   template <int OP>
-  __device__ __forceinline__ void issue(int st, int q) const {
-    const uint32_t lb = lds_w + (uint32_t)((2 * st + OP) % kSlots) * kSlotBytes + q * 1024;
-    const int64_t ko = (int64_t)st * kStageBytes;
-    if (OP) dma(b_base + ko, vb[q], lb);
-    else dma(a_base + ko, va[q], lb);
+  __device__ __forceinline__ void issue(int gs, int q) const {
+    const uint32_t lb = lds_w + (uint32_t)((2 * gs + OP) % kSlots) * kSlotBytes + q * 1024;
+    const int64_t ko = (int64_t)(gs - p_begin) * kStageBytes;
+    if (OP) dma(uniform_ptr(b_base + ko), vb[q], __builtin_amdgcn_readfirstlane(lb));
+    else dma(uniform_ptr(a_base + ko), va[q], __builtin_amdgcn_readfirstlane(lb));
   }
   __device__ __forceinline__ void read(int s, int kk, uint4 (&a)[4], uint4 (&b)[4]) const {
     const uint32_t sa = (uint32_t)((2 * s) % kSlots) * kSlotBytes;
@@ -1032,24 +1138,7 @@ struct Pipe {
     for (int t = 0; t < 16; ++t)
       if (t >= t0 && t < t1) mma_rows<bf16_t>(a[t >> 2], b[t & 3], acc[t >> 2][t & 3]);
   }
-  // one sub-step's 16 MFMAs with DMAs Q0 .. Q1-1 of operand OP of stage st spread between them
-  template <int OP, int Q0, int Q1>
-  __device__ __forceinline__ void step_dma(const uint4 (&a)[4], const uint4 (&b)[4], int st) const {
-    constexpr int n = Q1 - Q0;
-#pragma unroll
-    for (int q = 0; q < n; ++q) {
-      mma(a, b, q * 16 / n, (q + 1) * 16 / n);
-      __builtin_amdgcn_sched_barrier(0);
-      issue<OP>(st, Q0 + q);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-  __device__ __forceinline__ void step(const uint4 (&a)[4], const uint4 (&b)[4]) const { mma(a, b, 0, 16); }
 };
-
-__device__ __forceinline__ void wait_vm8_lgkm0() { asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory"); }
-__device__ __forceinline__ void wait_vm18() { asm volatile("s_waitcnt vmcnt(18)" ::: "memory"); }
-__device__ __forceinline__ void wait_vm16() { asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); }
 
 // Operand fragments of the four sub-steps of a stage: set u holds sub-step u.
 struct Frags {
@@ -1076,112 +1165,94 @@ __device__ __forceinline__ void substep(const Pipe<EPI>& P, Frags& f, int rs, in
   }
 }
 
-// One stage.  Sub-step 0 reads the fragments of sub-steps 2 and 3, sub-step 2 those of
-// sub-steps 0 and 1 of the next stage, so every read has at least a sub-step of MFMAs
-// to land; the barrier sits between sub-steps 1 and 2, after the last reads of the
-// stage.  Loads: the A half of stage s+2 (DMAs 2..7) in sub-steps 0 and 1, the B half of
-// stage s+2 in sub-step 2 and DMAs 0..1 of the A half of stage s+3 in sub-step 3.
-// LOADS = 2: all of those; 1: no A half of stage s+3; 0: none.  VMC: the vmcnt the
-// barrier waits for (the DMAs issued after the B half of stage s+1).
-template <int EPI, int LOADS, bool NEXT, int VMC>
+// One stage s of the workgroup's stream.  Sub-step 0 reads the fragments of sub-steps 2
+// and 3, sub-step 2 those of sub-steps 0 and 1 of stage s+1, so every read has at least a
+// sub-step of MFMAs to land; the barrier sits between sub-steps 1 and 2, after the last
+// reads of stage s.  Every load issued here belongs to stage s+2: its A half in sub-steps
+// 0 and 1 (into the slot of the B half of stage s-1, released by the previous barrier),
+// its B half in sub-step 2 (into the slot of the A half of stage s, released by this
+// stage's barrier).  The barrier waits for stage s+1 only: vmcnt(8) leaves the A half of
+// stage s+2 in flight.  LOADS: stage s+2 exists; NEXT: stage s+1 exists; RD: sub-step 2
+// reads the first fragments of stage s+1 (a tile's last stage leaves them to after its
+// epilogue, so that no operand registers are live across it).
+template <int EPI, bool LOADS, bool NEXT, bool RD = NEXT>
 __device__ __forceinline__ void stage(const Pipe<EPI>& P, int s, Frags& f) {
-  constexpr int L1 = LOADS ? 1 : 0, L2 = LOADS == 2 ? 1 : 0;
-  substep<EPI, 0, true, 2, 0, 2, 2 + 3 * L1>(P, f, s, s + 2);
-  substep<EPI, 1, false, 0, 0, 5, 5 + 3 * L1>(P, f, s, s + 2);
+  constexpr int L = LOADS ? 1 : 0;
+  substep<EPI, 0, true, 2, 0, 0, 4 * L>(P, f, s, s + 2);
+  substep<EPI, 1, false, 0, 0, 4, 4 + 4 * L>(P, f, s, s + 2);
   if (NEXT) {
-    if (VMC == 8) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");
+    if (LOADS) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");
     else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     dma_barrier();  // stage s+1 landed and visible; every read of stage s done
   }
-  substep<EPI, 2, NEXT, 0, 1, 0, 8 * L1>(P, f, s + 1, s + 2);
-  substep<EPI, 3, false, 0, 0, 0, 2 * L2>(P, f, s + 1, s + 3);
-}
-
-template <int EPI>
-__device__ __forceinline__ void mainloop(Pipe<EPI>& P, int nk) {
-  if (nk <= 0) return;
-  // prologue: stages 0 and 1, and DMAs 0..1 of the A half of stage 2
-#pragma unroll
-  for (int q = 0; q < kQ; ++q) P.template issue<0>(0, q);
-#pragma unroll
-  for (int q = 0; q < kQ; ++q) P.template issue<1>(0, q);
-  if (nk > 1) {
-#pragma unroll
-    for (int q = 0; q < kQ; ++q) P.template issue<0>(1, q);
-#pragma unroll
-    for (int q = 0; q < kQ; ++q) P.template issue<1>(1, q);
-  }
-  if (nk > 2) {
-    P.template issue<0>(2, 0);
-    P.template issue<0>(2, 1);
-    wait_vm18();
-  } else if (nk > 1) {
-    wait_vm16();
-  } else {
-    wait_all_0();
-  }
-  dma_barrier();
-  Frags f;
-  P.read(0, 0, f.a[0], f.b[0]);
-  P.read(0, 1, f.a[1], f.b[1]);
-  __builtin_amdgcn_sched_barrier(0);
-  int s = 0;
-  for (; s + 3 < nk; ++s) stage<EPI, 2, true, 8>(P, s, f);
-  if (s + 2 < nk) stage<EPI, 1, true, 8>(P, s++, f);
-  if (s + 1 < nk) stage<EPI, 0, true, 0>(P, s++, f);
-  stage<EPI, 0, false, 0>(P, s, f);
+  substep<EPI, 2, RD, 0, 1, 0, 8 * L>(P, f, s + 1, s + 2);
+  substep<EPI, 3, false, 0, 0, 0, 0>(P, f, s + 1, s + 2);
 }
 
 }  // namespace ring4
 
+// Persistent four-wave grouped GEMM: one workgroup per CU walks the tiles w, w + P, ...
+// of the XCD-aware order as one stream of 64-element K stages (at least two per tile).
+// The LDS ring and the loads run straight across tile boundaries: the last two stages of
+// a tile load the first two of the next, so the next tile's operands are in flight while
+// the previous tile's results are stored, and no workgroup is launched, and no group
+// offset re-read, per tile.
 template <int EPI>
 __global__ __launch_bounds__(ring4::kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void grouped_gemm_ring4_kernel(GemmParams p) {
+void grouped_gemm_persist_kernel(GemmParams p) {
   using namespace ring4;
   __shared__ uint4 smem[kSlots * kSlotUnits];
-  int g, nt;
-  int64_t m0, re;
-  if (!find_tile<ring4::kThreads>(p, g, m0, re, nt, (int*)smem)) return;
-  __syncthreads();  // every thread has read the tile from the scratch that the loads overwrite
-  g = __builtin_amdgcn_readfirstlane(g);
-  nt = __builtin_amdgcn_readfirstlane(nt);
-  m0 = uniform64(m0);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t ldb = p.Kd * 2;
+  GroupTable tab;
+  build_table(p, tab);
+  const int total = tab.total_mt * p.NT;
+  const int P = gridDim.x, w = blockIdx.x;
+  if (w >= total) return;
+  const int my_tiles = (total - 1 - w) / P + 1;
+  const int nk = (int)(p.Kd * 2 / kStageBytes);
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
 
   f32x16 acc[4][4];
-  Pipe<EPI> P(acc, smem);
-  P.a_base = uniform_ptr((const char*)p.A + m0 * ldb);
-  const int64_t b0row = EPI == EPI_SWIGLU ? (int64_t)nt * 128 : (int64_t)nt * 256;
-  P.b_base = uniform_ptr((const char*)p.B + ((int64_t)g * p.N + b0row) * ldb);
+  Pipe<EPI> Pp(acc, smem);
+  TileInfo cur = lookup(tab, w, total, p.NT);
+  Pp.retarget(p, cur.g, cur.m0, cur.nt, 0);
+  // prologue: stages 0 and 1 of the first tile
 #pragma unroll
-  for (int q = 0; q < kQ; ++q) {
-    const int r = (wave * kQ + q) * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ swz(r);
-    int64_t ar = m0 + r;
-    ar = ar < p.M ? ar : p.M - 1;
-    P.va[q] = (uint32_t)((ar - m0) * ldb + c * 16);
-    int64_t br;
-    if (EPI == EPI_SWIGLU) {
-      const int64_t F = p.N / 2;
-      int64_t cc = (int64_t)nt * 128 + (r & 127);
-      cc = cc < F ? cc : F - 1;
-      br = (r < 128 ? 0 : F) + cc;
-    } else {
-      br = (int64_t)nt * 256 + r;
-      br = br < p.N ? br : p.N - 1;
-    }
-    P.vb[q] = (uint32_t)((br - b0row) * ldb + c * 16);
-  }
-  const int nk = (int)(ldb / kStageBytes);
-  mainloop<EPI>(P, nk);
+  for (int q = 0; q < kQ; ++q) Pp.template issue<0>(0, q);
+#pragma unroll
+  for (int q = 0; q < kQ; ++q) Pp.template issue<1>(0, q);
+#pragma unroll
+  for (int q = 0; q < kQ; ++q) Pp.template issue<0>(1, q);
+#pragma unroll
+  for (int q = 0; q < kQ; ++q) Pp.template issue<1>(1, q);
+  asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  dma_barrier();
+  Frags f;
+  Pp.read(0, 0, f.a[0], f.b[0]);
+  Pp.read(0, 1, f.a[1], f.b[1]);
+  __builtin_amdgcn_sched_barrier(0);
 
-  const int wm = wave >> 1, wn = wave & 1;
-  int64_t col[4];
+  int gs = 0;  // workgroup stage of the current tile's first stage
+  for (int k = 0; k < my_tiles; ++k, gs += nk) {
+    for (int s = gs; s < gs + nk - 2; ++s) stage<EPI, true, true>(Pp, s, f);
+    // the last two stages load the first two of the next tile (the last tile loads its own
+    // first two again: one code path, and the loads land before the workgroup ends)
+    const TileInfo nxt = k + 1 < my_tiles ? lookup(tab, w + (k + 1) * P, total, p.NT) : cur;
+    Pp.retarget(p, nxt.g, nxt.m0, nxt.nt, gs + nk);
+    stage<EPI, true, true>(Pp, gs + nk - 2, f);
+    stage<EPI, true, true, false>(Pp, gs + nk - 1, f);
+    int64_t col[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    col[j] = EPI == EPI_SWIGLU ? (int64_t)nt * 128 + wn * 64 + (j & 1) * 32 : (int64_t)nt * 256 + wn * 128 + j * 32;
-  store_tile<bf16_t, EPI, 4, 4>(p, acc, m0 + wm * 128, re, col);
+    for (int j = 0; j < 4; ++j)
+      col[j] = EPI == EPI_SWIGLU ? (int64_t)cur.nt * 128 + wn * 64 + (j & 1) * 32 : (int64_t)cur.nt * 256 + wn * 128 + j * 32;
+    store_tile<bf16_t, EPI, 4, 4>(p, acc, (int64_t)cur.m0 + wm * 128, cur.re, col);
+    Pp.zero();
+    cur = nxt;
+    Pp.read(gs + nk, 0, f.a[0], f.b[0]);
+    Pp.read(gs + nk, 1, f.a[1], f.b[1]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  wait_all_0();  // no load may still target this workgroup's LDS when it ends
 }
 
 // ---------------------------------------------------------------------------
@@ -1384,12 +1455,17 @@ hipError_t launch_grouped_gemm(const void* A, const void* B, int b_layout, const
   const bool aligned = ((uintptr_t)A | (uintptr_t)B) % 16 == 0 && (b_layout == LAYOUT_NK || N % 8 == 0);
   const int nq = !aligned ? 0 : kbytes % Stage<4>::kRowBytes == 0 ? 4 : kbytes % Stage<2>::kRowBytes == 0 ? 2 : 0;
   // the ring kernel: bf16, N-by-K weights, whole 128-byte K stages, per-lane DMA offsets within 32 bits
-  if (dtype == 1 && nq == 4 && b_layout == LAYOUT_NK && epilogue != EPI_DSWIGLU &&
-      (N + 256) * kbytes < ((int64_t)1 << 32)) {
+  if (dtype == 1 && nq == 4 && b_layout == LAYOUT_NK && epilogue != EPI_DSWIGLU && G <= ring4::kMaxGroups &&
+      kbytes >= 2 * ring4::kStageBytes && (N + 256) * kbytes < ((int64_t)1 << 32) && max_mt * prm.NT < ((int64_t)1 << 31)) {
+    // persistent: one workgroup per CU, never more than the tiles can use
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return hipGetLastError();
+    const dim3 pgrid((unsigned)std::min<int64_t>(cus, (int64_t)grid.x));
     if (epilogue == EPI_SWIGLU)
-      hipLaunchKernelGGL(grouped_gemm_ring4_kernel<EPI_SWIGLU>, grid, dim3(ring4::kThreads), 0, s, prm);
+      hipLaunchKernelGGL(grouped_gemm_persist_kernel<EPI_SWIGLU>, pgrid, dim3(ring4::kThreads), 0, s, prm);
     else
-      hipLaunchKernelGGL(grouped_gemm_ring4_kernel<EPI_NONE>, grid, dim3(ring4::kThreads), 0, s, prm);
+      hipLaunchKernelGGL(grouped_gemm_persist_kernel<EPI_NONE>, pgrid, dim3(ring4::kThreads), 0, s, prm);
     return hipGetLastError();
   }
   if (dtype == 1) return gemm_dispatch<bf16_t>(prm, b_layout, epilogue, nq, grid, s);
