@@ -139,9 +139,11 @@ def main():
         mark(2)
         moe.moe_permute(x, cfg.K, bufs.row_src, bufs.x_perm)
         mark(3)
-        moe.moe_grouped_gemm(bufs.x_perm, w13, moe.MOE_LAYOUT_NK, bufs.offsets, bufs.h, moe.MOE_EPI_SWIGLU)
+        moe.moe_grouped_gemm(bufs.x_perm, w13, moe.MOE_LAYOUT_NK, bufs.offsets, bufs.h, moe.MOE_EPI_SWIGLU,
+                             workspace=bufs.gemm_ws)
         mark(4)
-        moe.moe_grouped_gemm(bufs.h, w2, moe.MOE_LAYOUT_NK, bufs.offsets, bufs.y_perm, moe.MOE_EPI_NONE)
+        moe.moe_grouped_gemm(bufs.h, w2, moe.MOE_LAYOUT_NK, bufs.offsets, bufs.y_perm, moe.MOE_EPI_NONE,
+                             workspace=bufs.gemm_ws)
         mark(5)
         moe.moe_unpermute_combine(bufs.y_perm, bufs.slot_pos, bufs.gates, cfg.T, cfg.K, bufs.y)
         mark(6)
@@ -259,7 +261,8 @@ def bench_backward(args, torch, moe, mi):
         mark(2)
         moe.moe_grouped_gemm_wgrad(b.h, b.dy_perm, b.offsets, b.dw2)
         mark(3)
-        moe.moe_grouped_gemm(b.d_pre, dev["w13"], moe.MOE_LAYOUT_KN, b.offsets, b.dx_perm, moe.MOE_EPI_NONE)
+        moe.moe_grouped_gemm(b.d_pre, dev["w13"], moe.MOE_LAYOUT_KN, b.offsets, b.dx_perm, moe.MOE_EPI_NONE,
+                             workspace=b.gemm_ws)
         mark(4)
         moe.moe_grouped_gemm_wgrad(b.x_perm, b.d_pre, b.offsets, b.dw13)
         mark(5)

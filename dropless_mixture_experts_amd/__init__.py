@@ -32,7 +32,8 @@ SIGNATURES = {
     "moe_router_logits": (_I32, [_P, _P, _I64, _I64, _I32, _I32, _P, _P]),
     "moe_route": (_I32, [_P, _P, _I64, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_permute": (_I32, [_P, _I64, _I64, _I32, _I32, _P, _P, _P, _P, _P, _P]),
-    "moe_grouped_gemm": (_I32, [_P, _P, _I32, _P, _I64, _I64, _I64, _I32, _I32, _I32, _P, _P, _P, _P]),
+    "moe_grouped_gemm": (_I32, [_P, _P, _I32, _P, _I64, _I64, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _SZ, _P]),
+    "moe_grouped_gemm_workspace_size": (_I32, [_c.POINTER(_SZ)]),
     "moe_unpermute_combine": (_I32, [_P, _P, _P, _I64, _I64, _I32, _I32, _P, _P]),
     "moe_grouped_gemm_wgrad": (_I32, [_P, _P, _P, _I64, _I64, _I64, _I32, _I32, _I32, _P, _P]),
 }
@@ -132,14 +133,23 @@ def moe_permute(x, K: int, row_src, x_perm, row_scale=None, y_perm_dot=None, dga
           _ptr(dgate_out), _ptr(x_perm), _stream(stream))
 
 
+def moe_grouped_gemm_workspace_size() -> int:
+    n = ctypes.c_size_t(0)
+    _call("moe_grouped_gemm_workspace_size", ctypes.byref(n))
+    return int(n.value)
+
+
 def moe_grouped_gemm(A, B, b_layout: int, group_offsets, C, epilogue: int = MOE_EPI_NONE, epi_in=None,
-                     epi_save=None, stream=None) -> None:
-    """One launch over all groups: C_g = epilogue(A_g . B_g^T (NK) or A_g . B_g (KN))."""
+                     epi_save=None, workspace=None, stream=None) -> None:
+    """One launch over all groups: C_g = epilogue(A_g . B_g^T (NK) or A_g . B_g (KN)).
+
+    ``workspace``: None or a zero-initialised device buffer of moe_grouped_gemm_workspace_size() bytes."""
     M, Kd = A.shape
     G = B.shape[0]
     N = B.shape[1] if b_layout == MOE_LAYOUT_NK else B.shape[2]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _call("moe_grouped_gemm", _ptr(A), _ptr(B), b_layout, _ptr(group_offsets), M, N, Kd, G, dtype_code(A),
-          epilogue, _ptr(epi_in), _ptr(epi_save), _ptr(C), _stream(stream))
+          epilogue, _ptr(epi_in), _ptr(epi_save), _ptr(C), _ptr(workspace), ws_bytes, _stream(stream))
 
 
 def moe_unpermute_combine(y_perm, slot_pos, gates, T: int, K: int, y, stream=None) -> None:

@@ -644,7 +644,14 @@ struct GemmParams {
   int64_t M, N, Kd;
   int G;
   int NT;  // column tiles
+  // split tail of the persistent kernel: per-(tail tile, wave) counters, then fp32 partial
+  // tiles (kSplitSlotFloats each); ws_slots == 0 disables the split
+  int* ws_count;
+  float* ws_part;
+  int ws_slots;
 };
+constexpr int kSplitCountBytes = 4096;             // counters: up to 1024 (tile, wave) pairs
+constexpr int kSplitSlotFloats = 256 * 256;        // one fp32 256 x 256 partial tile
 
 // Logistic sigmoid for the SwiGLU epilogues: the hardware exponential and reciprocal
 // (about 1 ulp each) instead of an IEEE division, far below the bf16 rounding of the
@@ -1191,12 +1198,62 @@ __device__ __forceinline__ void stage(const Pipe<EPI>& P, int s, Frags& f) {
 
 }  // namespace ring4
 
+// Split tail: the last R tiles (R = total mod P) would run alone on R CUs, so each is
+// cut along K into f pieces (f <= P / R, at least two stages each) that run at once.
+// Every piece stores its fp32 partial tile, then counts itself in per-(tile, wave)
+// counter; the piece that counts last sums all f partials in piece order (so the result
+// does not depend on which piece finished last), writes the epilogue and resets the
+// counter.  No workgroup waits for another.
+namespace ring4 {
+
+struct Item {
+  int L;    // tile in the workgroup order
+  int k0;   // first stage of the item within the tile
+  int len;  // stages
+  int part; // piece index within a split tail tile, -1 for a whole tile
+};
+
+// wave's 128 x 128 block of a partial tile: 64 float4 per lane, coalesced per register group
+__device__ __forceinline__ float4* part_ptr(const GemmParams& p, int slot) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  return (float4*)(p.ws_part + (size_t)slot * kSplitSlotFloats) + wave * 4096 + lane;
+}
+
+__device__ __forceinline__ void store_partial(const GemmParams& p, int slot, const f32x16 (&acc)[4][4]) {
+  float4* dst = part_ptr(p, slot);
+#pragma unroll
+  for (int t = 0; t < 16; ++t)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const f32x16& a = acc[t >> 2][t & 3];
+      dst[(t * 4 + e) * 64] = make_float4(a[4 * e], a[4 * e + 1], a[4 * e + 2], a[4 * e + 3]);
+    }
+}
+
+__device__ __forceinline__ void load_partial(const GemmParams& p, int slot, f32x16 (&acc)[4][4], bool add) {
+  const float4* src = part_ptr(p, slot);
+#pragma unroll
+  for (int t = 0; t < 16; ++t)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float4 v = src[(t * 4 + e) * 64];
+      f32x16& a = acc[t >> 2][t & 3];
+      if (add) {
+        a[4 * e] += v.x; a[4 * e + 1] += v.y; a[4 * e + 2] += v.z; a[4 * e + 3] += v.w;
+      } else {
+        a[4 * e] = v.x; a[4 * e + 1] = v.y; a[4 * e + 2] = v.z; a[4 * e + 3] = v.w;
+      }
+    }
+}
+
+}  // namespace ring4
+
 // Persistent four-wave grouped GEMM: one workgroup per CU walks the tiles w, w + P, ...
-// of the XCD-aware order as one stream of 64-element K stages (at least two per tile).
-// The LDS ring and the loads run straight across tile boundaries: the last two stages of
-// a tile load the first two of the next, so the next tile's operands are in flight while
-// the previous tile's results are stored, and no workgroup is launched, and no group
-// offset re-read, per tile.
+// of the XCD-aware order as one stream of 64-element K stages (at least two per item),
+// then, with a workspace, one K piece of a split tail tile.  The LDS ring and the loads
+// run straight across item boundaries: the last two stages of an item load the first two
+// of the next, so the next item's operands are in flight while the previous results are
+// stored, and no workgroup is launched, and no group offset re-read, per tile.
 template <int EPI>
 __global__ __launch_bounds__(ring4::kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void grouped_gemm_persist_kernel(GemmParams p) {
@@ -1206,17 +1263,34 @@ void grouped_gemm_persist_kernel(GemmParams p) {
   build_table(p, tab);
   const int total = tab.total_mt * p.NT;
   const int P = gridDim.x, w = blockIdx.x;
-  if (w >= total) return;
-  const int my_tiles = (total - 1 - w) / P + 1;
   const int nk = (int)(p.Kd * 2 / kStageBytes);
-  const int wave = threadIdx.x >> 6;
+  // whole tiles of this workgroup, and the split of the tail
+  const int D = total / P, R = total - D * P;
+  int f = 1;
+  if (R > 0 && 4 * R <= kSplitCountBytes / 4 && p.ws_slots > 0) f = min(min(P / R, nk / 2), p.ws_slots / R);
+  const int n_full = f > 1 ? D : (w < total ? (total - 1 - w) / P + 1 : 0);
+  const bool piece = f > 1 && w < R * f;
+  const int n_items = n_full + (piece ? 1 : 0);
+  if (n_items == 0) return;
+  auto item = [&](int i) {
+    Item it;
+    if (i < n_full) {
+      it.L = w + i * P; it.k0 = 0; it.len = nk; it.part = -1;
+    } else {
+      const int r = w % R, j = w / R;
+      it.L = D * P + r; it.k0 = j * nk / f; it.len = (j + 1) * nk / f - it.k0; it.part = j;
+    }
+    return it;
+  };
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int wm = wave >> 1, wn = wave & 1;
 
   f32x16 acc[4][4];
   Pipe<EPI> Pp(acc, smem);
-  TileInfo cur = lookup(tab, w, total, p.NT);
-  Pp.retarget(p, cur.g, cur.m0, cur.nt, 0);
-  // prologue: stages 0 and 1 of the first tile
+  Item ci = item(0);
+  TileInfo cur = lookup(tab, ci.L, total, p.NT);
+  Pp.retarget(p, cur.g, cur.m0, cur.nt, -ci.k0);
+  // prologue: the first two stages of the first item
 #pragma unroll
   for (int q = 0; q < kQ; ++q) Pp.template issue<0>(0, q);
 #pragma unroll
@@ -1227,30 +1301,57 @@ void grouped_gemm_persist_kernel(GemmParams p) {
   for (int q = 0; q < kQ; ++q) Pp.template issue<1>(1, q);
   asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
   dma_barrier();
-  Frags f;
-  Pp.read(0, 0, f.a[0], f.b[0]);
-  Pp.read(0, 1, f.a[1], f.b[1]);
+  Frags f4;
+  Pp.read(0, 0, f4.a[0], f4.b[0]);
+  Pp.read(0, 1, f4.a[1], f4.b[1]);
   __builtin_amdgcn_sched_barrier(0);
 
-  int gs = 0;  // workgroup stage of the current tile's first stage
-  for (int k = 0; k < my_tiles; ++k, gs += nk) {
-    for (int s = gs; s < gs + nk - 2; ++s) stage<EPI, true, true>(Pp, s, f);
-    // the last two stages load the first two of the next tile (the last tile loads its own
-    // first two again: one code path, and the loads land before the workgroup ends)
-    const TileInfo nxt = k + 1 < my_tiles ? lookup(tab, w + (k + 1) * P, total, p.NT) : cur;
-    Pp.retarget(p, nxt.g, nxt.m0, nxt.nt, gs + nk);
-    stage<EPI, true, true>(Pp, gs + nk - 2, f);
-    stage<EPI, true, true, false>(Pp, gs + nk - 1, f);
+  int gs = 0;  // workgroup stage of the current item's first stage
+  auto epilogue = [&](const TileInfo& t) {
     int64_t col[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      col[j] = EPI == EPI_SWIGLU ? (int64_t)cur.nt * 128 + wn * 64 + (j & 1) * 32 : (int64_t)cur.nt * 256 + wn * 128 + j * 32;
-    store_tile<bf16_t, EPI, 4, 4>(p, acc, (int64_t)cur.m0 + wm * 128, cur.re, col);
+      col[j] = EPI == EPI_SWIGLU ? (int64_t)t.nt * 128 + wn * 64 + (j & 1) * 32 : (int64_t)t.nt * 256 + wn * 128 + j * 32;
+    store_tile<bf16_t, EPI, 4, 4>(p, acc, (int64_t)t.m0 + wm * 128, t.re, col);
+  };
+  // whole tiles
+  for (int i = 0; i < n_full; ++i) {
+    for (int s = gs; s < gs + nk - 2; ++s) stage<EPI, true, true>(Pp, s, f4);
+    // the last two stages load the first two of the next item (the last item loads its
+    // own first two again: one code path, and the loads land before the workgroup ends)
+    const Item ni = i + 1 < n_items ? item(i + 1) : ci;
+    const TileInfo nxt = i + 1 < n_items ? lookup(tab, ni.L, total, p.NT) : cur;
+    Pp.retarget(p, nxt.g, nxt.m0, nxt.nt, gs + nk - ni.k0);
+    stage<EPI, true, true>(Pp, gs + nk - 2, f4);
+    stage<EPI, true, true, false>(Pp, gs + nk - 1, f4);
+    epilogue(cur);
     Pp.zero();
     cur = nxt;
-    Pp.read(gs + nk, 0, f.a[0], f.b[0]);
-    Pp.read(gs + nk, 1, f.a[1], f.b[1]);
+    ci = ni;
+    gs += nk;
+    Pp.read(gs, 0, f4.a[0], f4.b[0]);
+    Pp.read(gs, 1, f4.a[1], f4.b[1]);
     __builtin_amdgcn_sched_barrier(0);
+  }
+  // a K piece of a split tail tile: publish the partial; the last piece reduces
+  if (piece) {
+    for (int s = gs; s < gs + ci.len - 2; ++s) stage<EPI, true, true>(Pp, s, f4);
+    Pp.retarget(p, cur.g, cur.m0, cur.nt, gs + ci.len - ci.k0);
+    stage<EPI, true, true>(Pp, gs + ci.len - 2, f4);
+    stage<EPI, true, true, false>(Pp, gs + ci.len - 1, f4);
+    const int r = ci.L - D * P;
+    store_partial(p, w, acc);
+    __threadfence();
+    int old = 0;
+    if (lane == 0) old = atomicAdd(p.ws_count + r * 4 + wave, 1);
+    old = __builtin_amdgcn_readfirstlane(old);
+    if (old == f - 1) {
+      __threadfence();
+      load_partial(p, r, acc, false);
+      for (int j = 1; j < f; ++j) load_partial(p, j * R + r, acc, true);
+      if (lane == 0) p.ws_count[r * 4 + wave] = 0;
+      epilogue(cur);
+    }
   }
   wait_all_0();  // no load may still target this workgroup's LDS when it ends
 }
@@ -1441,11 +1542,24 @@ hipError_t gemm_dispatch(const GemmParams& prm, int b_layout, int epi, int nq, d
 
 }  // namespace
 
+size_t grouped_gemm_workspace_bytes() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  return kSplitCountBytes + (size_t)cus * kSplitSlotFloats * sizeof(float);
+}
+
 hipError_t launch_grouped_gemm(const void* A, const void* B, int b_layout, const int32_t* offs,
                                int64_t M, int64_t N, int64_t Kd, int G, int dtype, int epilogue,
-                               const void* epi_in, void* epi_save, void* C, hipStream_t s) {
+                               const void* epi_in, void* epi_save, void* C, void* ws, size_t ws_bytes,
+                               hipStream_t s) {
   if (M == 0) return hipSuccess;
-  GemmParams prm{A, B, offs, epi_in, epi_save, C, M, N, Kd, G, 0};
+  GemmParams prm{A, B, offs, epi_in, epi_save, C, M, N, Kd, G, 0, nullptr, nullptr, 0};
+  if (ws && ws_bytes >= kSplitCountBytes + kSplitSlotFloats * sizeof(float)) {
+    prm.ws_count = (int*)ws;
+    prm.ws_part = (float*)((char*)ws + kSplitCountBytes);
+    prm.ws_slots = (int)std::min<size_t>((ws_bytes - kSplitCountBytes) / (kSplitSlotFloats * sizeof(float)), 1 << 20);
+  }
   prm.NT = (epilogue == EPI_SWIGLU) ? (int)((N / 2 + 127) / 128) : (int)((N + kTile - 1) / kTile);
   const int64_t max_mt = (M + kTile - 1) / kTile + G;
   const dim3 grid((unsigned)(max_mt * prm.NT));

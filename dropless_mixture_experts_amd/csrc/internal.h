@@ -26,9 +26,13 @@ hipError_t launch_permute(const void* x, int64_t T, int64_t d, int K, int dtype,
 hipError_t launch_combine(const void* y_perm, const int32_t* slot_pos, const float* gates, int64_t T,
                           int64_t d, int K, int dtype, void* y, hipStream_t s);
 
+// bytes of the grouped GEMM workspace on the current device (0 if the device cannot be queried)
+size_t grouped_gemm_workspace_bytes();
+
 hipError_t launch_grouped_gemm(const void* A, const void* B, int b_layout, const int32_t* offs,
                                int64_t M, int64_t N, int64_t Kd, int G, int dtype, int epilogue,
-                               const void* epi_in, void* epi_save, void* C, hipStream_t s);
+                               const void* epi_in, void* epi_save, void* C, void* ws, size_t ws_bytes,
+                               hipStream_t s);
 
 hipError_t launch_grouped_wgrad(const void* X, const void* dY, const int32_t* offs, int64_t M,
                                 int64_t N, int64_t Kd, int G, int dtype, int accumulate, float* dW,

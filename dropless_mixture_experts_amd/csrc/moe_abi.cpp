@@ -78,10 +78,16 @@ int32_t moe_permute(const void* x, int64_t T, int64_t d, int32_t K, int32_t dtyp
                                       x_perm, (hipStream_t)stream));
 }
 
+int32_t moe_grouped_gemm_workspace_size(size_t* bytes) {
+  if (!bytes) return MOE_INVALID_ARG;
+  *bytes = moe::grouped_gemm_workspace_bytes();
+  return *bytes ? MOE_OK : MOE_HIP_ERROR;
+}
+
 int32_t moe_grouped_gemm(const void* A, const void* B, int32_t b_layout,
                          const int32_t* group_offsets, int64_t M, int64_t N, int64_t Kd, int32_t G,
                          int32_t dtype, int32_t epilogue, const void* epi_in, void* epi_save,
-                         void* C, moe_stream_t stream) {
+                         void* C, void* workspace, size_t workspace_bytes, moe_stream_t stream) {
   if (M < 0 || M >= ((int64_t)1 << 31) || N < 8 || N % 8 != 0 || Kd < 8 || Kd % 8 != 0) return MOE_INVALID_ARG;
   if (G < 1 || G > kMaxGroups) return MOE_INVALID_ARG;
   if (!dtype_ok(dtype)) return MOE_UNSUPPORTED;
@@ -96,9 +102,10 @@ int32_t moe_grouped_gemm(const void* A, const void* B, int32_t b_layout,
   if (!aligned16(A) || !aligned16(B) || !aligned4(group_offsets)) return MOE_INVALID_ARG;
   if ((epi_in && !aligned16(epi_in)) || (epi_save && !aligned16(epi_save)) || !aligned16(C))
     return MOE_INVALID_ARG;
+  if (workspace && !aligned16(workspace)) return MOE_INVALID_ARG;
   return from_hip(moe::launch_grouped_gemm(A, B, b_layout, group_offsets, M, N, Kd, G, dtype, epilogue,
                                            epi_in, epilogue == MOE_EPI_SWIGLU ? epi_save : nullptr, C,
-                                           (hipStream_t)stream));
+                                           workspace, workspace ? workspace_bytes : 0, (hipStream_t)stream));
 }
 
 int32_t moe_unpermute_combine(const void* y_perm, const int32_t* slot_pos, const float* gates,

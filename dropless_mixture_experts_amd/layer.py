@@ -20,8 +20,8 @@ from __future__ import annotations
 import torch
 
 from . import (MOE_EPI_DSWIGLU, MOE_EPI_NONE, MOE_EPI_SWIGLU, MOE_LAYOUT_KN, MOE_LAYOUT_NK,
-               moe_grouped_gemm, moe_grouped_gemm_wgrad, moe_permute, moe_route,
-               moe_route_workspace_size, moe_router_logits, moe_unpermute_combine)
+               moe_grouped_gemm, moe_grouped_gemm_wgrad, moe_grouped_gemm_workspace_size, moe_permute,
+               moe_route, moe_route_workspace_size, moe_router_logits, moe_unpermute_combine)
 
 
 class MoEBuffers:
@@ -44,6 +44,8 @@ class MoEBuffers:
         self.row_src = torch.empty((M,), **i32)
         ws = moe_route_workspace_size(T, E)
         self.ws = torch.empty((max(ws, 256),), dtype=torch.uint8, device=dev)
+        # grouped GEMM workspace: zeroed once, every call leaves its counters at zero
+        self.gemm_ws = torch.zeros((moe_grouped_gemm_workspace_size(),), dtype=torch.uint8, device=dev)
         self.x_perm = torch.empty((M, d), **act)
         self.h = torch.empty((M, F), **act)
         self.pre = torch.empty((M, 2 * F), **act) if (save_pre or backward) else None
@@ -72,8 +74,9 @@ def layer_forward(x, w_router, bias, w13, w2, K: int, score: int, renorm: bool, 
               b.row_src, b.ws, stream=stream)
     moe_permute(x, K, b.row_src, b.x_perm, stream=stream)
     moe_grouped_gemm(b.x_perm, w13, MOE_LAYOUT_NK, b.offsets, b.h, MOE_EPI_SWIGLU, epi_save=b.pre,
+                     workspace=b.gemm_ws, stream=stream)
+    moe_grouped_gemm(b.h, w2, MOE_LAYOUT_NK, b.offsets, b.y_perm, MOE_EPI_NONE, workspace=b.gemm_ws,
                      stream=stream)
-    moe_grouped_gemm(b.h, w2, MOE_LAYOUT_NK, b.offsets, b.y_perm, MOE_EPI_NONE, stream=stream)
     moe_unpermute_combine(b.y_perm, b.slot_pos, b.gates, b.T, K, b.y, stream=stream)
     return b.y
 
@@ -86,9 +89,10 @@ def layer_backward(dy, w13, w2, K: int, bufs: MoEBuffers, stream=None):
     moe_permute(dy, K, b.row_src, b.dy_perm, row_scale=b.gates, y_perm_dot=b.y_perm, dgate_out=b.d_gates,
                 stream=stream)
     moe_grouped_gemm(b.dy_perm, w2, MOE_LAYOUT_KN, b.offsets, b.d_pre, MOE_EPI_DSWIGLU, epi_in=b.pre,
-                     stream=stream)
+                     workspace=b.gemm_ws, stream=stream)
     moe_grouped_gemm_wgrad(b.h, b.dy_perm, b.offsets, b.dw2, stream=stream)
-    moe_grouped_gemm(b.d_pre, w13, MOE_LAYOUT_KN, b.offsets, b.dx_perm, MOE_EPI_NONE, stream=stream)
+    moe_grouped_gemm(b.d_pre, w13, MOE_LAYOUT_KN, b.offsets, b.dx_perm, MOE_EPI_NONE, workspace=b.gemm_ws,
+                     stream=stream)
     moe_grouped_gemm_wgrad(b.x_perm, b.d_pre, b.offsets, b.dw13, stream=stream)
     moe_unpermute_combine(b.dx_perm, b.slot_pos, None, b.T, K, b.dx, stream=stream)
     return b.dx, b.dw13, b.dw2, b.d_gates

@@ -55,7 +55,7 @@ enum moe_score { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 };
 enum moe_layout { MOE_LAYOUT_NK = 0, MOE_LAYOUT_KN = 1 };
 enum moe_epilogue { MOE_EPI_NONE = 0, MOE_EPI_SWIGLU = 1, MOE_EPI_DSWIGLU = 2 };
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 #define MOE_MAX_EXPERTS 256
 #define MOE_MAX_TOPK 32
 #define MOE_MAX_GROUPS 1024
@@ -140,6 +140,13 @@ int32_t moe_permute(const void* x, int64_t T, int64_t d, int32_t K, int32_t dtyp
  *   epilogue DSWIGLU: P = dH [M, N] with N = F; epi_in = saved pre-activations
  *                     [M, 2F] (G | U);  C [M, 2F] = [dH*U*silu'(G) | dH*silu(G)]
  *   A DEVICE [M, Kd] dtype;  group_offsets DEVICE [G+1] int32 (read on the device only)
+ *   workspace DEVICE, NULL or workspace_bytes (moe_grouped_gemm_workspace_size) bytes,
+ *     16-byte aligned, caller-owned: lets the last, partly filled round of output tiles be
+ *     split along Kd across otherwise idle CUs (fp32 partial tiles summed in a fixed order,
+ *     so results are deterministic).  Its first 4096 bytes must be zero before the first
+ *     call; every call leaves them zero.  Calls that overlap in time need separate
+ *     workspaces.  With NULL no tile is split (results differ only in the fp32 summation
+ *     order of those tiles).
  * Requires 0 <= M < 2^31, N >= 8, N % 8 == 0 (SWIGLU: N % 16 == 0 and layout NK),
  * Kd >= 8, Kd % 8 == 0, 1 <= G <= MOE_MAX_GROUPS; epi_in is required for DSWIGLU.
  * Rows of C outside every group are not written.
@@ -147,7 +154,14 @@ int32_t moe_permute(const void* x, int64_t T, int64_t d, int32_t K, int32_t dtyp
 int32_t moe_grouped_gemm(const void* A, const void* B, int32_t b_layout,
                          const int32_t* group_offsets, int64_t M, int64_t N, int64_t Kd, int32_t G,
                          int32_t dtype, int32_t epilogue, const void* epi_in, void* epi_save,
-                         void* C, moe_stream_t stream);
+                         void* C, void* workspace, size_t workspace_bytes, moe_stream_t stream);
+
+/*
+ * Bytes of the moe_grouped_gemm workspace for the current device (a 4096-byte counter
+ * block, then one fp32 256 x 256 partial tile per compute unit).  Returns
+ * MOE_HIP_ERROR when the device cannot be queried.
+ */
+int32_t moe_grouped_gemm_workspace_size(size_t* bytes);
 
 /*
  * Unpermute + gate-weighted combine back to token order (S7; TE-MoE Figure 3

@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert moe.moe_abi_version() == 1
+    assert moe.moe_abi_version() == 2
     assert moe.status_str(0) == "ok"
     assert "invalid" in moe.status_str(1)
     assert moe.status_str(99) == "unknown status"
@@ -84,8 +84,9 @@ def test_route_rejects_bad_arguments(lib):
 
 
 def test_gemm_rejects_bad_arguments(lib):
-    def call(A=P, B=P, lay=0, offs=P, M=512, N=256, Kd=128, G=4, dt=1, epi=0, ein=None, esave=None, C=P):
-        return lib.moe_grouped_gemm(A, B, lay, offs, M, N, Kd, G, dt, epi, ein, esave, C, None)
+    def call(A=P, B=P, lay=0, offs=P, M=512, N=256, Kd=128, G=4, dt=1, epi=0, ein=None, esave=None, C=P,
+             ws=None, wsb=0):
+        return lib.moe_grouped_gemm(A, B, lay, offs, M, N, Kd, G, dt, epi, ein, esave, C, ws, wsb, None)
     assert call(N=12) == 1
     assert call(Kd=4) == 1
     assert call(G=0) == 1
@@ -98,6 +99,7 @@ def test_gemm_rejects_bad_arguments(lib):
     assert call(epi=2, ein=None) == 1     # SwiGLU backward needs the saved pre-activations
     assert call(A=P + 4) == 1             # misaligned
     assert call(C=None) == 1
+    assert call(ws=P + 8, wsb=1 << 20) == 1  # misaligned workspace
     assert call(M=-1) == 1
     assert call(M=0) == 0                 # nothing to do: returns before any launch
 

@@ -318,6 +318,36 @@ def test_grouped_gemm_single_group_is_plain_matmul():
     assert rel_err(C, orc.to_f64(A) @ orc.to_f64(W[0]).T) < TOL_BF16 / 4
 
 
+@pytest.mark.parametrize("swiglu", [False, True])
+def test_grouped_gemm_split_tail(swiglu):
+    """With a workspace, the output tiles of the last, partly filled round are split along Kd
+    across the otherwise idle CUs.  Ragged groups of cus + 2 row tiles leave 2 tiles for that
+    round (4 pieces each at Kd = 512).  Results match the oracle row by row, repeat bit for bit,
+    the workspace counters return to zero, and without a workspace the result also matches."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    counts = [300, 256 * (cus - 3), 700]   # 2 + (cus - 3) + 3 row tiles, one column tile
+    N, Kd = 256, 512
+    A, W, off, M = _gemm_case(True, N, Kd, lead=0, tail=0, seed=21, counts=counts)
+    ws = torch.zeros((moe.moe_grouped_gemm_workspace_size(),), dtype=torch.uint8, device="cuda")
+    epi = moe.MOE_EPI_SWIGLU if swiglu else moe.MOE_EPI_NONE
+    width = N // 2 if swiglu else N
+    outs = []
+    for w in (ws, ws, None):
+        C = empty_like_poisoned((M, width), torch.bfloat16)
+        moe.moe_grouped_gemm(dev(A), dev(W), 0, dev(off), C, epi, workspace=w)
+        torch.cuda.synchronize()
+        outs.append(C)
+    assert torch.count_nonzero(ws[:4096]).item() == 0
+    assert torch.equal(outs[0], outs[1])
+    pre = orc.grouped_gemm(A, W, off, "nk")
+    ref = orc.swiglu(pre) if swiglu else pre
+    for C in (outs[0], outs[2]):
+        got = f64(C)
+        assert rel_err(got, ref) < TOL_BF16 / 4
+        row = np.linalg.norm(got - ref, axis=1) / np.maximum(np.linalg.norm(ref, axis=1), 1e-30)
+        assert row.max() < TOL_BF16
+
+
 # ----------------------------------------------------------------- weight gradient
 
 @pytest.mark.parametrize("bf16", [True, False])
