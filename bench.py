@@ -137,7 +137,7 @@ def main():
         moe.moe_route(bufs.logits, b, cfg.K, cfg.score, cfg.renorm, bufs.topk_idx, bufs.gates, bufs.counts,
                       bufs.offsets, bufs.slot_pos, bufs.row_src, bufs.ws)
         mark(2)
-        moe.moe_permute(x, cfg.K, bufs.row_src, bufs.x_perm)
+        moe.moe_permute(x, cfg.K, bufs.slot_pos, bufs.x_perm)
         mark(3)
         moe.moe_grouped_gemm(bufs.x_perm, w13, moe.MOE_LAYOUT_NK, bufs.offsets, bufs.h, moe.MOE_EPI_SWIGLU,
                              workspace=bufs.gemm_ws)
@@ -253,7 +253,7 @@ def bench_backward(args, torch, moe, mi):
             if ev is not None:
                 ev[i].record(stream)
         mark(0)
-        moe.moe_permute(dy, cfg.K, b.row_src, b.dy_perm, row_scale=b.gates, y_perm_dot=b.y_perm,
+        moe.moe_permute(dy, cfg.K, b.slot_pos, b.dy_perm, row_scale=b.gates, y_perm_dot=b.y_perm,
                         dgate_out=b.d_gates)
         mark(1)
         moe.moe_grouped_gemm(b.dy_perm, dev["w2"], moe.MOE_LAYOUT_KN, b.offsets, b.d_pre, moe.MOE_EPI_DSWIGLU,

@@ -125,11 +125,11 @@ def moe_route(logits, bias, K: int, score: int, renorm: bool, topk_idx, topk_gat
           _stream(stream))
 
 
-def moe_permute(x, K: int, row_src, x_perm, row_scale=None, y_perm_dot=None, dgate_out=None,
+def moe_permute(x, K: int, slot_pos, x_perm, row_scale=None, y_perm_dot=None, dgate_out=None,
                 stream=None) -> None:
-    """x_perm[r] = (row_scale[s] *) x[s // K] for s = row_src[r]; optional dgate_out[s] = <x[t], y_perm_dot[r]>."""
+    """x_perm[slot_pos[s]] = (row_scale[s] *) x[s // K]; optional dgate_out[s] = <x[s // K], y_perm_dot[slot_pos[s]]>."""
     T, d = x.shape
-    _call("moe_permute", _ptr(x), T, d, K, dtype_code(x), _ptr(row_src), _ptr(row_scale), _ptr(y_perm_dot),
+    _call("moe_permute", _ptr(x), T, d, K, dtype_code(x), _ptr(slot_pos), _ptr(row_scale), _ptr(y_perm_dot),
           _ptr(dgate_out), _ptr(x_perm), _stream(stream))
 
 

@@ -19,7 +19,7 @@ hipError_t launch_route(const float* logits, const float* bias, int64_t T, int E
                         int32_t* offsets, int32_t* slot_pos, int32_t* row_src, void* ws,
                         hipStream_t s);
 
-hipError_t launch_permute(const void* x, int64_t T, int64_t d, int K, int dtype, const int32_t* row_src,
+hipError_t launch_permute(const void* x, int64_t T, int64_t d, int K, int dtype, const int32_t* slot_pos,
                           const float* row_scale, const void* y_perm_dot, float* dgate_out,
                           void* x_perm, hipStream_t s);
 

@@ -65,16 +65,16 @@ int32_t moe_route(const float* logits, const float* bias, int64_t T, int32_t E, 
 }
 
 int32_t moe_permute(const void* x, int64_t T, int64_t d, int32_t K, int32_t dtype,
-                    const int32_t* row_src, const float* row_scale, const void* y_perm_dot,
+                    const int32_t* slot_pos, const float* row_scale, const void* y_perm_dot,
                     float* dgate_out, void* x_perm, moe_stream_t stream) {
   if (T < 0 || d < 8 || d % 8 != 0 || K < 1 || K > MOE_MAX_TOPK) return MOE_INVALID_ARG;
   if (!dtype_ok(dtype)) return MOE_UNSUPPORTED;
   if ((y_perm_dot == nullptr) != (dgate_out == nullptr)) return MOE_INVALID_ARG;
   if (T * (int64_t)K >= ((int64_t)1 << 31)) return MOE_INVALID_ARG;
   if (T == 0) return MOE_OK;
-  if (!x || !row_src || !x_perm) return MOE_INVALID_ARG;
+  if (!x || !slot_pos || !x_perm) return MOE_INVALID_ARG;
   if (!aligned16(x) || !aligned16(x_perm) || (y_perm_dot && !aligned16(y_perm_dot))) return MOE_INVALID_ARG;
-  return from_hip(moe::launch_permute(x, T, d, K, dtype, row_src, row_scale, y_perm_dot, dgate_out,
+  return from_hip(moe::launch_permute(x, T, d, K, dtype, slot_pos, row_scale, y_perm_dot, dgate_out,
                                       x_perm, (hipStream_t)stream));
 }
 

@@ -4,8 +4,8 @@
 // back to their original order afterwards (page "Accelerating dropless MoE
 // training in JAX with NVIDIA Transformer Engine", Figure 3 paragraph of
 // "What specialised optimisations does dropless MoE need?").  Both are pure
-// HBM streams: one wave moves one row with 16-byte lanes, so every row read
-// and written is a run of full 64-byte segments.
+// HBM streams over token rows: one wave per token moves whole rows with 16-byte
+// lanes, so every row is read once and written once as full 64-byte segments.
 #include "common.h"
 #include "internal.h"
 
@@ -14,64 +14,101 @@ namespace moe {
 namespace {
 
 constexpr int kRowsPerBlock = 4;  // one wave per row
-constexpr int kUnroll = 4;        // 16-byte vectors in flight per lane
+constexpr int kUnroll = 8;   // 16-byte vectors in flight per lane (permute: a whole 4096-wide bf16 row)
+constexpr int kCUnroll = 4;  // 16-byte vectors per lane per gathered row (combine)
 
-// x_perm[r] = (scale_s *) x[s / K] for s = row_src[r]; optional dgate_s = <x[s/K], ydot[r]>.
+// x_perm[slot_pos[s]] = (scale_s *) x[t] for the K slots s = t K + k of token t; optional
+// dgate_s = <x[t], ydot[slot_pos[s]]>.  One wave per token, so each token row is read from
+// HBM once and written to its K rows.  Without the dot, every loaded piece of the row goes
+// straight to all K rows; with it, the slots are taken one by one (the row comes back from
+// the cache) so that each slot's dot product is a single wave reduction.
 template <typename T, bool SCALE, bool DOT>
 __global__ __launch_bounds__(256) void permute_kernel(const uint4* __restrict__ x, int64_t nvec, int K,
-                                                      const int32_t* __restrict__ row_src,
+                                                      const int32_t* __restrict__ slot_pos,
                                                       const float* __restrict__ row_scale,
                                                       const uint4* __restrict__ ydot,
                                                       float* __restrict__ dgate,
-                                                      uint4* __restrict__ xp, int64_t M) {
+                                                      uint4* __restrict__ xp, int64_t ntok) {
   using E = Elem<T>;
   const int lane = threadIdx.x & 63;
-  const int64_t r = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
-  if (r >= M) return;
-  int64_t s = row_src[r];
-  s = s < 0 ? 0 : (s >= M ? M - 1 : s);  // never leave the buffers, whatever row_src holds
-  const uint4* src = x + (s / K) * nvec;
-  uint4* dst = xp + r * nvec;
-  const uint4* yd = DOT ? ydot + r * nvec : nullptr;
-  const float sc = SCALE ? row_scale[s] : 1.f;
-  float dot = 0.f;
-  for (int64_t i0 = 0; i0 < nvec; i0 += 64 * kUnroll) {
-    uint4 v[kUnroll], w[kUnroll];
+  const int64_t t = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (t >= ntok) return;
+  const int64_t M = ntok * K;
+  // lane k holds slot k's destination row and scale (K <= 32)
+  int pos = 0;
+  float sk = 1.f;
+  if (lane < K) {
+    pos = slot_pos[t * K + lane];
+    pos = pos < 0 ? 0 : (pos >= M ? (int)(M - 1) : pos);  // never leave the buffers
+    if (SCALE) sk = row_scale[t * K + lane];
+  }
+  const uint4* src = x + t * nvec;
+  if constexpr (!DOT) {
+    for (int64_t i0 = 0; i0 < nvec; i0 += 64 * kUnroll) {
+      uint4 v[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int64_t i = i0 + u * 64 + lane;
-      if (i < nvec) {
-        v[u] = src[i];  // a token row is read K times: keep it cacheable
-        if (DOT) w[u] = ld_nt(yd + i);
+      for (int u = 0; u < kUnroll; ++u) {
+        const int64_t i = i0 + u * 64 + lane;
+        if (i < nvec) v[u] = ld_nt(src + i);
+      }
+      for (int k = 0; k < K; ++k) {
+        const int64_t p = __shfl(pos, k, 64);
+        const float sc = __shfl(sk, k, 64);
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+          const int64_t i = i0 + u * 64 + lane;
+          if (i < nvec) {
+            uint4 o = v[u];
+            if (SCALE) {
+              float f[E::kVec];
+              E::to_f32(v[u], f);
+#pragma unroll
+              for (int q = 0; q < E::kVec; ++q) f[q] *= sc;
+              o = E::from_f32(f);
+            }
+            st_nt(xp + p * nvec + i, o);
+          }
+        }
       }
     }
+  } else {
+    for (int k = 0; k < K; ++k) {
+      const int64_t p = __shfl(pos, k, 64);
+      const float sc = __shfl(sk, k, 64);
+      const uint4* yd = ydot + p * nvec;
+      float dot = 0.f;
+      for (int64_t i0 = 0; i0 < nvec; i0 += 64 * kUnroll) {
+        uint4 v[kUnroll], w[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int64_t i = i0 + u * 64 + lane;
-      if (i < nvec) {
-        uint4 o = v[u];
-        if (SCALE || DOT) {
-          float f[E::kVec];
-          E::to_f32(v[u], f);
-          if (DOT) {
-            float g[E::kVec];
+        for (int u = 0; u < kUnroll; ++u) {
+          const int64_t i = i0 + u * 64 + lane;
+          if (i < nvec) {
+            v[u] = src[i];  // read once from HBM, again from the cache for the other slots
+            w[u] = ld_nt(yd + i);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+          const int64_t i = i0 + u * 64 + lane;
+          if (i < nvec) {
+            float f[E::kVec], g[E::kVec];
+            E::to_f32(v[u], f);
             E::to_f32(w[u], g);
 #pragma unroll
             for (int q = 0; q < E::kVec; ++q) dot += f[q] * g[q];
-          }
-          if (SCALE) {
+            uint4 o = v[u];
+            if (SCALE) {
 #pragma unroll
-            for (int q = 0; q < E::kVec; ++q) f[q] *= sc;
-            o = E::from_f32(f);
+              for (int q = 0; q < E::kVec; ++q) f[q] *= sc;
+              o = E::from_f32(f);
+            }
+            st_nt(xp + p * nvec + i, o);
           }
         }
-        st_nt(dst + i, o);
       }
+      dot = wave_sum(dot);
+      if (lane == 0) dgate[t * K + k] = dot;
     }
-  }
-  if (DOT) {
-    dot = wave_sum(dot);
-    if (lane == 0) dgate[s] = dot;
   }
 }
 
@@ -94,28 +131,44 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
     pos = pos < 0 ? 0 : (pos >= M ? (int)(M - 1) : pos);
     if (GATES) gk = gates[t * K + lane];
   }
-  for (int64_t i0 = 0; i0 < nvec; i0 += 64 * 2) {
-    float acc[2][E::kVec];
+  for (int64_t i0 = 0; i0 < nvec; i0 += 64 * kCUnroll) {
+    float acc[kCUnroll][E::kVec];
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int u = 0; u < kCUnroll; ++u)
 #pragma unroll
       for (int q = 0; q < E::kVec; ++q) acc[u][q] = 0.f;
-    for (int k = 0; k < K; ++k) {
-      const int64_t p = __shfl(pos, k, 64);
-      const float g = __shfl(gk, k, 64);
+    // two gathered rows per step: their loads are in flight together
+    for (int k = 0; k < K; k += 2) {
+      const bool two = k + 1 < K;
+      const int64_t p0 = __shfl(pos, k, 64), p1 = __shfl(pos, two ? k + 1 : k, 64);
+      const float g0 = __shfl(gk, k, 64), g1 = __shfl(gk, two ? k + 1 : k, 64);
+      uint4 v0[kCUnroll], v1[kCUnroll];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+      for (int u = 0; u < kCUnroll; ++u) {
+        const int64_t i = i0 + u * 64 + lane;
+        if (i < nvec) {
+          v0[u] = ld_nt(yp + p0 * nvec + i);
+          if (two) v1[u] = ld_nt(yp + p1 * nvec + i);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kCUnroll; ++u) {
         const int64_t i = i0 + u * 64 + lane;
         if (i < nvec) {
           float f[E::kVec];
-          E::to_f32(ld_nt(yp + p * nvec + i), f);
+          E::to_f32(v0[u], f);
 #pragma unroll
-          for (int q = 0; q < E::kVec; ++q) acc[u][q] = fmaf(g, f[q], acc[u][q]);
+          for (int q = 0; q < E::kVec; ++q) acc[u][q] = fmaf(g0, f[q], acc[u][q]);
+          if (two) {
+            E::to_f32(v1[u], f);
+#pragma unroll
+            for (int q = 0; q < E::kVec; ++q) acc[u][q] = fmaf(g1, f[q], acc[u][q]);
+          }
         }
       }
     }
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < kCUnroll; ++u) {
       const int64_t i = i0 + u * 64 + lane;
       if (i < nvec) st_nt(y + t * nvec + i, E::from_f32(acc[u]));
     }
@@ -123,28 +176,27 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
 }
 
 template <typename T>
-hipError_t permute_t(const void* x, int64_t T_, int64_t d, int K, const int32_t* row_src,
+hipError_t permute_t(const void* x, int64_t T_, int64_t d, int K, const int32_t* slot_pos,
                      const float* row_scale, const void* ydot, float* dgate, void* xp, hipStream_t s) {
-  const int64_t M = T_ * K;
-  if (M == 0) return hipSuccess;
+  if (T_ == 0) return hipSuccess;
   const int64_t nvec = d / Elem<T>::kVec;
-  const dim3 grid((unsigned)((M + kRowsPerBlock - 1) / kRowsPerBlock));
+  const dim3 grid((unsigned)((T_ + kRowsPerBlock - 1) / kRowsPerBlock));
   const uint4* xv = (const uint4*)x;
   const uint4* yv = (const uint4*)ydot;
   uint4* o = (uint4*)xp;
   const bool dot = ydot != nullptr && dgate != nullptr;
   if (row_scale && dot)
-    hipLaunchKernelGGL((permute_kernel<T, true, true>), grid, dim3(256), 0, s, xv, nvec, K, row_src,
-                       row_scale, yv, dgate, o, M);
+    hipLaunchKernelGGL((permute_kernel<T, true, true>), grid, dim3(256), 0, s, xv, nvec, K, slot_pos,
+                       row_scale, yv, dgate, o, T_);
   else if (row_scale)
-    hipLaunchKernelGGL((permute_kernel<T, true, false>), grid, dim3(256), 0, s, xv, nvec, K, row_src,
-                       row_scale, yv, dgate, o, M);
+    hipLaunchKernelGGL((permute_kernel<T, true, false>), grid, dim3(256), 0, s, xv, nvec, K, slot_pos,
+                       row_scale, yv, dgate, o, T_);
   else if (dot)
-    hipLaunchKernelGGL((permute_kernel<T, false, true>), grid, dim3(256), 0, s, xv, nvec, K, row_src,
-                       row_scale, yv, dgate, o, M);
+    hipLaunchKernelGGL((permute_kernel<T, false, true>), grid, dim3(256), 0, s, xv, nvec, K, slot_pos,
+                       row_scale, yv, dgate, o, T_);
   else
-    hipLaunchKernelGGL((permute_kernel<T, false, false>), grid, dim3(256), 0, s, xv, nvec, K, row_src,
-                       row_scale, yv, dgate, o, M);
+    hipLaunchKernelGGL((permute_kernel<T, false, false>), grid, dim3(256), 0, s, xv, nvec, K, slot_pos,
+                       row_scale, yv, dgate, o, T_);
   return hipGetLastError();
 }
 
@@ -165,12 +217,12 @@ hipError_t combine_t(const void* yp, const int32_t* slot_pos, const float* gates
 
 }  // namespace
 
-hipError_t launch_permute(const void* x, int64_t T, int64_t d, int K, int dtype, const int32_t* row_src,
+hipError_t launch_permute(const void* x, int64_t T, int64_t d, int K, int dtype, const int32_t* slot_pos,
                           const float* row_scale, const void* y_perm_dot, float* dgate_out,
                           void* x_perm, hipStream_t s) {
   if (dtype == 1)
-    return permute_t<bf16_t>(x, T, d, K, row_src, row_scale, y_perm_dot, dgate_out, x_perm, s);
-  return permute_t<float>(x, T, d, K, row_src, row_scale, y_perm_dot, dgate_out, x_perm, s);
+    return permute_t<bf16_t>(x, T, d, K, slot_pos, row_scale, y_perm_dot, dgate_out, x_perm, s);
+  return permute_t<float>(x, T, d, K, slot_pos, row_scale, y_perm_dot, dgate_out, x_perm, s);
 }
 
 hipError_t launch_combine(const void* y_perm, const int32_t* slot_pos, const float* gates, int64_t T,

@@ -72,7 +72,7 @@ def layer_forward(x, w_router, bias, w13, w2, K: int, score: int, renorm: bool, 
         logits = b.logits
     moe_route(logits, bias, K, score, renorm, b.topk_idx, b.gates, b.counts, b.offsets, b.slot_pos,
               b.row_src, b.ws, stream=stream)
-    moe_permute(x, K, b.row_src, b.x_perm, stream=stream)
+    moe_permute(x, K, b.slot_pos, b.x_perm, stream=stream)
     moe_grouped_gemm(b.x_perm, w13, MOE_LAYOUT_NK, b.offsets, b.h, MOE_EPI_SWIGLU, epi_save=b.pre,
                      workspace=b.gemm_ws, stream=stream)
     moe_grouped_gemm(b.h, w2, MOE_LAYOUT_NK, b.offsets, b.y_perm, MOE_EPI_NONE, workspace=b.gemm_ws,
@@ -86,7 +86,7 @@ def layer_backward(dy, w13, w2, K: int, bufs: MoEBuffers, stream=None):
 
     Returns (dx, dw13, dw2, d_gates) in bufs."""
     b = bufs
-    moe_permute(dy, K, b.row_src, b.dy_perm, row_scale=b.gates, y_perm_dot=b.y_perm, dgate_out=b.d_gates,
+    moe_permute(dy, K, b.slot_pos, b.dy_perm, row_scale=b.gates, y_perm_dot=b.y_perm, dgate_out=b.d_gates,
                 stream=stream)
     moe_grouped_gemm(b.dy_perm, w2, MOE_LAYOUT_KN, b.offsets, b.d_pre, MOE_EPI_DSWIGLU, epi_in=b.pre,
                      workspace=b.gemm_ws, stream=stream)

@@ -113,18 +113,19 @@ int32_t moe_route(const float* logits, const float* bias, int64_t T, int32_t E, 
 /*
  * Permute / dispatch into expert-contiguous order (S4; TE-MoE Figure 3
  * paragraph), and the combine backward (B1) when the optional arguments are
- * given.  For every permuted row r with s = row_src[r], t = s / K:
+ * given.  For every slot s = t*K + k of token t, with r = slot_pos[s]:
  *   x_perm[r] = x[t]                                (row_scale == NULL: a bit copy)
  *   x_perm[r] = round(row_scale[s] * x[t])          (row_scale != NULL)
  *   dgate_out[s] = sum_j x[t, j] * y_perm_dot[r, j]  (when y_perm_dot and dgate_out are given)
- *   x          DEVICE [T, d] dtype;   row_src DEVICE [T*K] int32 (a permutation of [0, T*K))
+ * Each token row is read once and written to its K rows.
+ *   x          DEVICE [T, d] dtype;   slot_pos DEVICE [T*K] int32 (a permutation of [0, T*K))
  *   row_scale  DEVICE [T*K] fp32 or NULL
  *   y_perm_dot DEVICE [T*K, d] dtype or NULL;  dgate_out DEVICE [T*K] fp32 or NULL (both or neither)
  *   x_perm     DEVICE [T*K, d] dtype (written)
  * Requires d % 8 == 0, 1 <= K <= MOE_MAX_TOPK.
  */
 int32_t moe_permute(const void* x, int64_t T, int64_t d, int32_t K, int32_t dtype,
-                    const int32_t* row_src, const float* row_scale, const void* y_perm_dot,
+                    const int32_t* slot_pos, const float* row_scale, const void* y_perm_dot,
                     float* dgate_out, void* x_perm, moe_stream_t stream);
 
 /*

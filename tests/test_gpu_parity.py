@@ -157,7 +157,7 @@ def test_permute_bit_exact(bf16):
         x = mi.f32_to_bf16_bits(x)
     xd = dev(x)
     out = empty_like_poisoned((T * K, d), xd.dtype)
-    moe.moe_permute(xd, K, dev(r.row_src), out)
+    moe.moe_permute(xd, K, dev(r.slot_pos), out)
     torch.cuda.synchronize()
     assert np.array_equal(host(out), orc.permute(x, r.row_src, K))
 
@@ -172,7 +172,7 @@ def test_permute_gate_scale_and_dgate():
     gates = r.gates.astype(np.float32)
     out = torch.empty((T * K, d), dtype=torch.bfloat16, device="cuda")
     dg = torch.empty((T * K,), dtype=torch.float32, device="cuda")
-    moe.moe_permute(dev(dy), K, dev(r.row_src), out, row_scale=dev(gates.ravel()), y_perm_dot=dev(yp),
+    moe.moe_permute(dev(dy), K, dev(r.slot_pos), out, row_scale=dev(gates.ravel()), y_perm_dot=dev(yp),
                     dgate_out=dg)
     torch.cuda.synchronize()
     ref_dyp, ref_dg = orc.combine_backward(dy, yp, r.slot_pos, gates, T, K)
@@ -210,7 +210,7 @@ def test_identity_experts_return_x_bit_exact():
     xd = dev(x)
     xp = torch.empty((T * K, d), dtype=torch.bfloat16, device="cuda")
     y = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
-    moe.moe_permute(xd, K, dev(r.row_src), xp)
+    moe.moe_permute(xd, K, dev(r.slot_pos), xp)
     moe.moe_unpermute_combine(xp, dev(r.slot_pos), dev(r.gates.astype(np.float32)), T, K, y)
     torch.cuda.synchronize()
     assert np.array_equal(host(y), x)
