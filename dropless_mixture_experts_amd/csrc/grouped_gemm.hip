@@ -644,11 +644,13 @@ struct GemmParams {
   int64_t M, N, Kd;
   int G;
   int NT;  // column tiles
-  // split tail of the persistent kernel: per-(tail tile, wave) counters, then fp32 partial
+  // split tail of the ring kernel: per-(split tile, wave) counters, then fp32 partial
   // tiles (kSplitSlotFloats each); ws_slots == 0 disables the split
   int* ws_count;
   float* ws_part;
   int ws_slots;
+  int P;   // CUs the split tail spreads over
+  int nk;  // K stages of a tile (ring kernel)
 };
 constexpr int kSplitCountBytes = 4096;             // counters: up to 1024 (tile, wave) pairs
 constexpr int kSplitSlotFloats = 256 * 256;        // one fp32 256 x 256 partial tile
@@ -753,9 +755,23 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const f32x16 (&a
 
 // Block -> (group, first row, column tile) from the group offsets in device
 // memory; false when this workgroup has no tile.  Uniform over the workgroup.
+// Split tail of the ring kernel.  With dynamic dispatch the last R tiles (R = total mod P)
+// would run alone on R CUs, so, given a workspace, the grid ends in R f piece blocks
+// instead: each of those tiles is cut along K into f pieces (f <= P / R, at least two
+// stages each) that run at once.  Every piece stores its fp32 partial tile, then counts
+// itself in a per-(tile, wave) counter; the piece that counts last sums all f partials in
+// piece order (so the result does not depend on which piece finished last), writes the
+// epilogue and resets the counter.  No workgroup waits for another.
+struct Piece {
+  int part = -1;  // piece of a split tile, -1 for a whole tile
+  int f = 1;      // pieces per split tile
+  int R = 0;      // split tiles
+  int slot = 0;   // partial-tile slot of this piece (part R + tile)
+};
+
 template <int NTHR>
 __device__ __forceinline__ bool find_tile(const GemmParams& p, int& g_out, int64_t& m0_out, int64_t& re_out,
-                                          int& nt_out, int* scratch) {
+                                          int& nt_out, int* scratch, Piece* piece = nullptr) {
   constexpr int NW = NTHR / 64;
   int* s_wtot = scratch;       // NW ints
   int* s_res = scratch + NW;   // 2 ints
@@ -792,9 +808,28 @@ __device__ __forceinline__ bool find_tile(const GemmParams& p, int& g_out, int64
   }
   const int excl = incl - local;
   const int64_t total = (int64_t)total_mt * p.NT;
-  if ((int64_t)blockIdx.x >= total) return false;
-
-  const int64_t L = xcd_remap(blockIdx.x, total);
+  int64_t full = total, L;
+  const int64_t b = blockIdx.x;
+  if (piece && p.ws_slots > 0 && p.P > 0) {
+    const int R = (int)(total % p.P);
+    int f = 1;
+    if (R > 0 && 4 * R <= kSplitCountBytes / 4) f = min(min(p.P / R, p.nk / 2), p.ws_slots / R);
+    if (f > 1) {
+      full = total - R;
+      piece->f = f;
+      piece->R = R;
+    }
+  }
+  if (b < full) {
+    L = xcd_remap(b, full);
+  } else if (piece && piece->f > 1 && b < full + (int64_t)piece->R * piece->f) {
+    const int pi = (int)(b - full);
+    L = full + pi % piece->R;
+    piece->part = pi / piece->R;
+    piece->slot = pi;
+  } else {
+    return false;
+  }
   const int64_t per = (int64_t)kGroupM * p.NT;
   const int64_t grp = L / per;
   const int first = (int)(grp * kGroupM);
@@ -973,7 +1008,6 @@ constexpr int kSlotBytes = kSlotUnits * 16;
 constexpr int kSlots = 5;                 // 160 KB: all of a CU's LDS
 constexpr int kQ = 8;                     // DMA instructions per wave per half-stage (8 rows x 128 B each)
 constexpr int kStageBytes = 128;          // K bytes per row per stage
-constexpr int kMaxGroups = 256;           // groups held by the register table (4 per lane)
 
 // 16-byte chunk XOR of an LDS row (8 chunks): the 16 lanes served by one LDS cycle
 // (16 consecutive rows, one logical chunk) hit 16 distinct 16-byte bank groups
@@ -993,82 +1027,12 @@ __device__ __forceinline__ int64_t uniform64(int64_t v) {
 }
 __device__ __forceinline__ const char* uniform_ptr(const char* p) { return (const char*)uniform64((int64_t)p); }
 
-// Row tiles of every group, held in registers by each wave: lane l keeps groups l + 64 i
-// (i < 4): first row, end row and the inclusive prefix sum of 256-row tiles.
-struct GroupTable {
-  int lo[4], hi[4], incl[4];
-  int total_mt;  // uniform: row tiles over all groups
-};
-
-__device__ __forceinline__ void build_table(const GemmParams& p, GroupTable& t) {
-  const int lane = threadIdx.x & 63;
-  int carry = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int g = lane + 64 * i;
-    int64_t rs = 0, re = 0;
-    if (g < p.G) group_rows(p.offs, g, p.M, rs, re);
-    int x = (int)((re - rs + 255) / 256);
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int u = __shfl_up(x, o, 64);
-      if (lane >= o) x += u;
-    }
-    t.incl[i] = x + carry;
-    t.lo[i] = (int)rs;
-    t.hi[i] = (int)re;
-    carry += __shfl(x, 63, 64);
-  }
-  t.total_mt = __builtin_amdgcn_readfirstlane(carry);
-}
-
-__device__ __forceinline__ int pick(const int (&v)[4], int i) {
-  return i == 0 ? v[0] : i == 1 ? v[1] : i == 2 ? v[2] : v[3];
-}
-
-// Tile L of the workgroup order -> (group, first row, end row, column tile), uniform.
-// The order is the XCD-aware one of the other kernels: each XCD takes a contiguous run
-// of tiles, 8 row tiles sharing each column tile.  Tile counts fit in 31 bits (checked
-// on the host).
-struct TileInfo {
-  int g, nt, m0, re;
-};
-__device__ __forceinline__ TileInfo lookup(const GroupTable& t, int L, int total, int NT) {
-  const int xcd = L % kXcd, local = L / kXcd;
-  const int q = total / kXcd, r = total % kXcd;
-  const int Lr = xcd * q + (xcd < r ? xcd : r) + local;
-  const int per = kGroupM * NT;
-  const int grp = Lr / per;
-  const int first = grp * kGroupM;
-  const int gm = min(t.total_mt - first, kGroupM);
-  const int rem = Lr - grp * per;
-  const int mt = first + rem % gm;
-  TileInfo ti;
-  ti.nt = rem / gm;
-  // the group is the number of groups whose row tiles end at or before mt
-  int cnt = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) cnt += __popcll(__ballot(t.incl[i] <= mt));
-  ti.g = cnt;
-  const int sl = cnt >> 6, ln = cnt & 63;
-  const int incl = __builtin_amdgcn_readlane(pick(t.incl, sl), ln);
-  const int lo = __builtin_amdgcn_readlane(pick(t.lo, sl), ln);
-  const int hi = __builtin_amdgcn_readlane(pick(t.hi, sl), ln);
-  const int rt = (hi - lo + 255) / 256;
-  ti.m0 = lo + (mt - (incl - rt)) * 256;
-  ti.re = hi;
-  return ti;
-}
-
 template <int EPI>
 struct Pipe {
-  // loads (the producer runs two stages ahead of the MFMAs, across tile boundaries)
-  const char* a_base;   // uniform: A at (first row of the producer's tile, K = 0)
-  const char* b_base;   // uniform: B at (first row of the producer's tile, K = 0)
-  int p_begin;          // uniform: workgroup stage of the producer tile's first stage
+  const char* a_base;   // uniform: A at (first tile row, K = 0)
+  const char* b_base;   // uniform: B at (first tile row, K = 0)
   uint32_t va[kQ], vb[kQ];
   uint32_t lds_w;       // uniform: LDS byte address of slot 0 + this wave's DMA block
-  // operand reads
   uint32_t a_off, b_off[4];  // per lane: byte offset of fragment row l32 within a slot
   uint32_t ch[4];            // per lane: byte offset of the 16-byte chunk of sub-step kk
   const char* L;
@@ -1086,9 +1050,6 @@ struct Pipe {
       b_off[j] = ((EPI == EPI_SWIGLU ? ((j >> 1) * 128 + wn * 64 + (j & 1) * 32) : (wn * 128 + j * 32)) + l32) * 128;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) ch[kk] = ((2 * kk + hi) ^ swz(l32)) * 16;
-    zero();
-  }
-  __device__ __forceinline__ void zero() {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -1096,36 +1057,13 @@ struct Pipe {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
   }
-  // point the loads at tile (g, m0, nt), whose first stage is workgroup stage begin.  Row
-  // offsets are 32-bit (the host checks (N + 256) rows of B fit): rows past the end of A,
-  // or of the gate or up half of B, are clamped to the last row (their outputs are not stored).
-  __device__ __forceinline__ void retarget(const GemmParams& p, int g, int m0, int nt, int begin) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const uint32_t ldb = (uint32_t)p.Kd * 2;
-    p_begin = begin;
-    a_base = uniform_ptr((const char*)p.A + (int64_t)m0 * ldb);
-    const int b0row = EPI == EPI_SWIGLU ? nt * 128 : nt * 256;
-    b_base = uniform_ptr((const char*)p.B + ((int64_t)g * p.N + b0row) * ldb);
-    const int amax = (int)p.M - 1 - m0;  // last valid row of A, relative to m0
-    const int F = (int)(EPI == EPI_SWIGLU ? p.N / 2 : p.N);
-    const int bmax = F - 1 - b0row;       // last valid gate (or plain) row, relative to b0row
-#pragma unroll
-    for (int q = 0; q < kQ; ++q) {
-      const int r = (wave * kQ + q) * 8 + (lane >> 3);
-      const uint32_t c16 = (uint32_t)(((lane & 7) ^ swz(r)) * 16);
-      va[q] = (uint32_t)min(r, amax) * ldb + c16;
-      // up rows: F + min(b0row + r - 128, F - 1), relative to b0row
-      const int rb = EPI == EPI_SWIGLU ? (r < 128 ? min(r, bmax) : F + min(r - 128, bmax)) : min(r, bmax);
-      vb[q] = (uint32_t)rb * ldb + c16;
-    }
-  }
-  // DMA q of operand OP (0: A, 1: B) of workgroup stage gs, i.e. of half-stage 2 gs + OP
+  // DMA q of operand OP (0: A, 1: B) of stage st, i.e. of half-stage 2 st + OP
   template <int OP>
-  __device__ __forceinline__ void issue(int gs, int q) const {
-    const uint32_t lb = lds_w + (uint32_t)((2 * gs + OP) % kSlots) * kSlotBytes + q * 1024;
-    const int64_t ko = (int64_t)(gs - p_begin) * kStageBytes;
-    if (OP) dma(uniform_ptr(b_base + ko), vb[q], __builtin_amdgcn_readfirstlane(lb));
-    else dma(uniform_ptr(a_base + ko), va[q], __builtin_amdgcn_readfirstlane(lb));
+  __device__ __forceinline__ void issue(int st, int q) const {
+    const uint32_t lb = lds_w + (uint32_t)((2 * st + OP) % kSlots) * kSlotBytes + q * 1024;
+    const int64_t ko = (int64_t)st * kStageBytes;
+    if (OP) dma(b_base + ko, vb[q], lb);
+    else dma(a_base + ko, va[q], lb);
   }
   __device__ __forceinline__ void read(int s, int kk, uint4 (&a)[4], uint4 (&b)[4]) const {
     const uint32_t sa = (uint32_t)((2 * s) % kSlots) * kSlotBytes;
@@ -1145,7 +1083,24 @@ struct Pipe {
     for (int t = 0; t < 16; ++t)
       if (t >= t0 && t < t1) mma_rows<bf16_t>(a[t >> 2], b[t & 3], acc[t >> 2][t & 3]);
   }
+  // one sub-step's 16 MFMAs with DMAs Q0 .. Q1-1 of operand OP of stage st spread between them
+  template <int OP, int Q0, int Q1>
+  __device__ __forceinline__ void step_dma(const uint4 (&a)[4], const uint4 (&b)[4], int st) const {
+    constexpr int n = Q1 - Q0;
+#pragma unroll
+    for (int q = 0; q < n; ++q) {
+      mma(a, b, q * 16 / n, (q + 1) * 16 / n);
+      __builtin_amdgcn_sched_barrier(0);
+      issue<OP>(st, Q0 + q);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  __device__ __forceinline__ void step(const uint4 (&a)[4], const uint4 (&b)[4]) const { mma(a, b, 0, 16); }
 };
+
+__device__ __forceinline__ void wait_vm8_lgkm0() { asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void wait_vm18() { asm volatile("s_waitcnt vmcnt(18)" ::: "memory"); }
+__device__ __forceinline__ void wait_vm16() { asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); }
 
 // Operand fragments of the four sub-steps of a stage: set u holds sub-step u.
 struct Frags {
@@ -1167,53 +1122,74 @@ __device__ __forceinline__ void substep(const Pipe<EPI>& P, Frags& f, int rs, in
     }
 #pragma unroll
     for (int q = 0; q < n; ++q)
-      if (t == (2 * q + 1) * 16 / (2 * n)) P.template issue<OP>(st, Q0 + q);
+      if (t == (2 * q + 1) * 16 / (2 * (n > 0 ? n : 1))) P.template issue<OP>(st, Q0 + q);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// One stage s of the workgroup's stream.  Sub-step 0 reads the fragments of sub-steps 2
-// and 3, sub-step 2 those of sub-steps 0 and 1 of stage s+1, so every read has at least a
-// sub-step of MFMAs to land; the barrier sits between sub-steps 1 and 2, after the last
-// reads of stage s.  Every load issued here belongs to stage s+2: its A half in sub-steps
-// 0 and 1 (into the slot of the B half of stage s-1, released by the previous barrier),
-// its B half in sub-step 2 (into the slot of the A half of stage s, released by this
-// stage's barrier).  The barrier waits for stage s+1 only: vmcnt(8) leaves the A half of
-// stage s+2 in flight.  LOADS: stage s+2 exists; NEXT: stage s+1 exists; RD: sub-step 2
-// reads the first fragments of stage s+1 (a tile's last stage leaves them to after its
-// epilogue, so that no operand registers are live across it).
-template <int EPI, bool LOADS, bool NEXT, bool RD = NEXT>
+// One stage.  Sub-step 0 reads the fragments of sub-steps 2 and 3, sub-step 2 those of
+// sub-steps 0 and 1 of the next stage, so every read has at least a sub-step of MFMAs
+// to land; the barrier sits between sub-steps 1 and 2, after the last reads of the
+// stage.  Loads: the A half of stage s+2 (DMAs 2..7) in sub-steps 0 and 1, the B half of
+// stage s+2 in sub-step 2 and DMAs 0..1 of the A half of stage s+3 in sub-step 3.
+// LOADS = 2: all of those; 1: no A half of stage s+3; 0: none.  VMC: the vmcnt the
+// barrier waits for (the DMAs issued after the B half of stage s+1).
+template <int EPI, int LOADS, bool NEXT, int VMC>
 __device__ __forceinline__ void stage(const Pipe<EPI>& P, int s, Frags& f) {
-  constexpr int L = LOADS ? 1 : 0;
-  substep<EPI, 0, true, 2, 0, 0, 4 * L>(P, f, s, s + 2);
-  substep<EPI, 1, false, 0, 0, 4, 4 + 4 * L>(P, f, s, s + 2);
+  constexpr int L1 = LOADS ? 1 : 0, L2 = LOADS == 2 ? 1 : 0;
+  substep<EPI, 0, true, 2, 0, 2, 2 + 3 * L1>(P, f, s, s + 2);
+  substep<EPI, 1, false, 0, 0, 5, 5 + 3 * L1>(P, f, s, s + 2);
   if (NEXT) {
-    if (LOADS) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");
+    if (VMC == 8) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");
     else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     dma_barrier();  // stage s+1 landed and visible; every read of stage s done
   }
-  substep<EPI, 2, RD, 0, 1, 0, 8 * L>(P, f, s + 1, s + 2);
-  substep<EPI, 3, false, 0, 0, 0, 0>(P, f, s + 1, s + 2);
+  substep<EPI, 2, NEXT, 0, 1, 0, 8 * L1>(P, f, s + 1, s + 2);
+  substep<EPI, 3, false, 0, 0, 0, 2 * L2>(P, f, s + 1, s + 3);
+}
+
+template <int EPI>
+__device__ __forceinline__ void mainloop(Pipe<EPI>& P, int nk) {
+  if (nk <= 0) return;
+  // prologue: stages 0 and 1, and DMAs 0..1 of the A half of stage 2
+#pragma unroll
+  for (int q = 0; q < kQ; ++q) P.template issue<0>(0, q);
+#pragma unroll
+  for (int q = 0; q < kQ; ++q) P.template issue<1>(0, q);
+  if (nk > 1) {
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) P.template issue<0>(1, q);
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) P.template issue<1>(1, q);
+  }
+  if (nk > 2) {
+    P.template issue<0>(2, 0);
+    P.template issue<0>(2, 1);
+    wait_vm18();
+  } else if (nk > 1) {
+    wait_vm16();
+  } else {
+    wait_all_0();
+  }
+  dma_barrier();
+  Frags f;
+  P.read(0, 0, f.a[0], f.b[0]);
+  P.read(0, 1, f.a[1], f.b[1]);
+  __builtin_amdgcn_sched_barrier(0);
+  int s = 0;
+  for (; s + 3 < nk; ++s) stage<EPI, 2, true, 8>(P, s, f);
+  if (s + 2 < nk) stage<EPI, 1, true, 8>(P, s++, f);
+  if (s + 1 < nk) stage<EPI, 0, true, 0>(P, s++, f);
+  stage<EPI, 0, false, 0>(P, s, f);
 }
 
 }  // namespace ring4
 
-// Split tail: the last R tiles (R = total mod P) would run alone on R CUs, so each is
-// cut along K into f pieces (f <= P / R, at least two stages each) that run at once.
-// Every piece stores its fp32 partial tile, then counts itself in per-(tile, wave)
-// counter; the piece that counts last sums all f partials in piece order (so the result
-// does not depend on which piece finished last), writes the epilogue and resets the
-// counter.  No workgroup waits for another.
+
+// Partial tiles of the split tail: a wave's 128 x 128 block is 64 float4 per lane,
+// coalesced per register group.
 namespace ring4 {
 
-struct Item {
-  int L;    // tile in the workgroup order
-  int k0;   // first stage of the item within the tile
-  int len;  // stages
-  int part; // piece index within a split tail tile, -1 for a whole tile
-};
-
-// wave's 128 x 128 block of a partial tile: 64 float4 per lane, coalesced per register group
 __device__ __forceinline__ float4* part_ptr(const GemmParams& p, int slot) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   return (float4*)(p.ws_part + (size_t)slot * kSplitSlotFloats) + wave * 4096 + lane;
@@ -1248,112 +1224,72 @@ __device__ __forceinline__ void load_partial(const GemmParams& p, int slot, f32x
 
 }  // namespace ring4
 
-// Persistent four-wave grouped GEMM: one workgroup per CU walks the tiles w, w + P, ...
-// of the XCD-aware order as one stream of 64-element K stages (at least two per item),
-// then, with a workspace, one K piece of a split tail tile.  The LDS ring and the loads
-// run straight across item boundaries: the last two stages of an item load the first two
-// of the next, so the next item's operands are in flight while the previous results are
-// stored, and no workgroup is launched, and no group offset re-read, per tile.
 template <int EPI>
 __global__ __launch_bounds__(ring4::kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void grouped_gemm_persist_kernel(GemmParams p) {
+void grouped_gemm_ring4_kernel(GemmParams p) {
   using namespace ring4;
   __shared__ uint4 smem[kSlots * kSlotUnits];
-  GroupTable tab;
-  build_table(p, tab);
-  const int total = tab.total_mt * p.NT;
-  const int P = gridDim.x, w = blockIdx.x;
-  const int nk = (int)(p.Kd * 2 / kStageBytes);
-  // whole tiles of this workgroup, and the split of the tail
-  const int D = total / P, R = total - D * P;
-  int f = 1;
-  if (R > 0 && 4 * R <= kSplitCountBytes / 4 && p.ws_slots > 0) f = min(min(P / R, nk / 2), p.ws_slots / R);
-  const int n_full = f > 1 ? D : (w < total ? (total - 1 - w) / P + 1 : 0);
-  const bool piece = f > 1 && w < R * f;
-  const int n_items = n_full + (piece ? 1 : 0);
-  if (n_items == 0) return;
-  auto item = [&](int i) {
-    Item it;
-    if (i < n_full) {
-      it.L = w + i * P; it.k0 = 0; it.len = nk; it.part = -1;
-    } else {
-      const int r = w % R, j = w / R;
-      it.L = D * P + r; it.k0 = j * nk / f; it.len = (j + 1) * nk / f - it.k0; it.part = j;
-    }
-    return it;
-  };
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wm = wave >> 1, wn = wave & 1;
+  int g, nt;
+  int64_t m0, re;
+  Piece pc;
+  if (!find_tile<ring4::kThreads>(p, g, m0, re, nt, (int*)smem, &pc)) return;
+  __syncthreads();  // every thread has read the tile from the scratch that the loads overwrite
+  g = __builtin_amdgcn_readfirstlane(g);
+  nt = __builtin_amdgcn_readfirstlane(nt);
+  m0 = uniform64(m0);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t ldb = p.Kd * 2;
+  // stages of this block: the whole K extent, or one piece of it
+  const int nk = (int)(ldb / kStageBytes);
+  const int k0 = pc.part >= 0 ? pc.part * nk / pc.f : 0;
+  const int len = pc.part >= 0 ? (pc.part + 1) * nk / pc.f - k0 : nk;
 
   f32x16 acc[4][4];
-  Pipe<EPI> Pp(acc, smem);
-  Item ci = item(0);
-  TileInfo cur = lookup(tab, ci.L, total, p.NT);
-  Pp.retarget(p, cur.g, cur.m0, cur.nt, -ci.k0);
-  // prologue: the first two stages of the first item
+  Pipe<EPI> P(acc, smem);
+  P.a_base = uniform_ptr((const char*)p.A + m0 * ldb + (int64_t)k0 * kStageBytes);
+  const int64_t b0row = EPI == EPI_SWIGLU ? (int64_t)nt * 128 : (int64_t)nt * 256;
+  P.b_base = uniform_ptr((const char*)p.B + ((int64_t)g * p.N + b0row) * ldb + (int64_t)k0 * kStageBytes);
 #pragma unroll
-  for (int q = 0; q < kQ; ++q) Pp.template issue<0>(0, q);
-#pragma unroll
-  for (int q = 0; q < kQ; ++q) Pp.template issue<1>(0, q);
-#pragma unroll
-  for (int q = 0; q < kQ; ++q) Pp.template issue<0>(1, q);
-#pragma unroll
-  for (int q = 0; q < kQ; ++q) Pp.template issue<1>(1, q);
-  asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-  dma_barrier();
-  Frags f4;
-  Pp.read(0, 0, f4.a[0], f4.b[0]);
-  Pp.read(0, 1, f4.a[1], f4.b[1]);
-  __builtin_amdgcn_sched_barrier(0);
-
-  int gs = 0;  // workgroup stage of the current item's first stage
-  auto epilogue = [&](const TileInfo& t) {
-    int64_t col[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      col[j] = EPI == EPI_SWIGLU ? (int64_t)t.nt * 128 + wn * 64 + (j & 1) * 32 : (int64_t)t.nt * 256 + wn * 128 + j * 32;
-    store_tile<bf16_t, EPI, 4, 4>(p, acc, (int64_t)t.m0 + wm * 128, t.re, col);
-  };
-  // whole tiles
-  for (int i = 0; i < n_full; ++i) {
-    for (int s = gs; s < gs + nk - 2; ++s) stage<EPI, true, true>(Pp, s, f4);
-    // the last two stages load the first two of the next item (the last item loads its
-    // own first two again: one code path, and the loads land before the workgroup ends)
-    const Item ni = i + 1 < n_items ? item(i + 1) : ci;
-    const TileInfo nxt = i + 1 < n_items ? lookup(tab, ni.L, total, p.NT) : cur;
-    Pp.retarget(p, nxt.g, nxt.m0, nxt.nt, gs + nk - ni.k0);
-    stage<EPI, true, true>(Pp, gs + nk - 2, f4);
-    stage<EPI, true, true, false>(Pp, gs + nk - 1, f4);
-    epilogue(cur);
-    Pp.zero();
-    cur = nxt;
-    ci = ni;
-    gs += nk;
-    Pp.read(gs, 0, f4.a[0], f4.b[0]);
-    Pp.read(gs, 1, f4.a[1], f4.b[1]);
-    __builtin_amdgcn_sched_barrier(0);
+  for (int q = 0; q < kQ; ++q) {
+    const int r = (wave * kQ + q) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ swz(r);
+    int64_t ar = m0 + r;
+    ar = ar < p.M ? ar : p.M - 1;
+    P.va[q] = (uint32_t)((ar - m0) * ldb + c * 16);
+    int64_t br;
+    if (EPI == EPI_SWIGLU) {
+      const int64_t F = p.N / 2;
+      int64_t cc = (int64_t)nt * 128 + (r & 127);
+      cc = cc < F ? cc : F - 1;
+      br = (r < 128 ? 0 : F) + cc;
+    } else {
+      br = (int64_t)nt * 256 + r;
+      br = br < p.N ? br : p.N - 1;
+    }
+    P.vb[q] = (uint32_t)((br - b0row) * ldb + c * 16);
   }
-  // a K piece of a split tail tile: publish the partial; the last piece reduces
-  if (piece) {
-    for (int s = gs; s < gs + ci.len - 2; ++s) stage<EPI, true, true>(Pp, s, f4);
-    Pp.retarget(p, cur.g, cur.m0, cur.nt, gs + ci.len - ci.k0);
-    stage<EPI, true, true>(Pp, gs + ci.len - 2, f4);
-    stage<EPI, true, true, false>(Pp, gs + ci.len - 1, f4);
-    const int r = ci.L - D * P;
-    store_partial(p, w, acc);
+  mainloop<EPI>(P, len);
+
+  const int wm = wave >> 1, wn = wave & 1;
+  int64_t col[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    col[j] = EPI == EPI_SWIGLU ? (int64_t)nt * 128 + wn * 64 + (j & 1) * 32 : (int64_t)nt * 256 + wn * 128 + j * 32;
+  if (pc.part >= 0) {
+    // a piece of a split tile: publish the partial; the last piece of the tile reduces
+    const int r = pc.slot % pc.R;
+    store_partial(p, pc.slot, acc);
     __threadfence();
     int old = 0;
     if (lane == 0) old = atomicAdd(p.ws_count + r * 4 + wave, 1);
     old = __builtin_amdgcn_readfirstlane(old);
-    if (old == f - 1) {
-      __threadfence();
-      load_partial(p, r, acc, false);
-      for (int j = 1; j < f; ++j) load_partial(p, j * R + r, acc, true);
-      if (lane == 0) p.ws_count[r * 4 + wave] = 0;
-      epilogue(cur);
-    }
+    if (old != pc.f - 1) return;
+    __threadfence();
+    load_partial(p, r, acc, false);
+    for (int j = 1; j < pc.f; ++j) load_partial(p, j * pc.R + r, acc, true);
+    if (lane == 0) p.ws_count[r * 4 + wave] = 0;
   }
-  wait_all_0();  // no load may still target this workgroup's LDS when it ends
+  store_tile<bf16_t, EPI, 4, 4>(p, acc, m0 + wm * 128, re, col);
 }
 
 // ---------------------------------------------------------------------------
@@ -1554,7 +1490,7 @@ hipError_t launch_grouped_gemm(const void* A, const void* B, int b_layout, const
                                const void* epi_in, void* epi_save, void* C, void* ws, size_t ws_bytes,
                                hipStream_t s) {
   if (M == 0) return hipSuccess;
-  GemmParams prm{A, B, offs, epi_in, epi_save, C, M, N, Kd, G, 0, nullptr, nullptr, 0};
+  GemmParams prm{A, B, offs, epi_in, epi_save, C, M, N, Kd, G, 0, nullptr, nullptr, 0, 0, 0};
   if (ws && ws_bytes >= kSplitCountBytes + kSplitSlotFloats * sizeof(float)) {
     prm.ws_count = (int*)ws;
     prm.ws_part = (float*)((char*)ws + kSplitCountBytes);
@@ -1569,17 +1505,22 @@ hipError_t launch_grouped_gemm(const void* A, const void* B, int b_layout, const
   const bool aligned = ((uintptr_t)A | (uintptr_t)B) % 16 == 0 && (b_layout == LAYOUT_NK || N % 8 == 0);
   const int nq = !aligned ? 0 : kbytes % Stage<4>::kRowBytes == 0 ? 4 : kbytes % Stage<2>::kRowBytes == 0 ? 2 : 0;
   // the ring kernel: bf16, N-by-K weights, whole 128-byte K stages, per-lane DMA offsets within 32 bits
-  if (dtype == 1 && nq == 4 && b_layout == LAYOUT_NK && epilogue != EPI_DSWIGLU && G <= ring4::kMaxGroups &&
-      kbytes >= 2 * ring4::kStageBytes && (N + 256) * kbytes < ((int64_t)1 << 32) && max_mt * prm.NT < ((int64_t)1 << 31)) {
-    // persistent: one workgroup per CU, never more than the tiles can use
+  if (dtype == 1 && nq == 4 && b_layout == LAYOUT_NK && epilogue != EPI_DSWIGLU &&
+      (N + 256) * kbytes < ((int64_t)1 << 32)) {
+    // with a workspace the grid ends in up to P piece blocks of a split tail
     int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      return hipGetLastError();
-    const dim3 pgrid((unsigned)std::min<int64_t>(cus, (int64_t)grid.x));
+    if (prm.ws_slots > 0) {
+      if (hipGetDevice(&dev) != hipSuccess ||
+          hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return hipGetLastError();
+    }
+    prm.P = cus;
+    prm.nk = (int)(kbytes / ring4::kStageBytes);
+    const dim3 rgrid((unsigned)(grid.x + cus));
     if (epilogue == EPI_SWIGLU)
-      hipLaunchKernelGGL(grouped_gemm_persist_kernel<EPI_SWIGLU>, pgrid, dim3(ring4::kThreads), 0, s, prm);
+      hipLaunchKernelGGL(grouped_gemm_ring4_kernel<EPI_SWIGLU>, rgrid, dim3(ring4::kThreads), 0, s, prm);
     else
-      hipLaunchKernelGGL(grouped_gemm_persist_kernel<EPI_NONE>, pgrid, dim3(ring4::kThreads), 0, s, prm);
+      hipLaunchKernelGGL(grouped_gemm_ring4_kernel<EPI_NONE>, rgrid, dim3(ring4::kThreads), 0, s, prm);
     return hipGetLastError();
   }
   if (dtype == 1) return gemm_dispatch<bf16_t>(prm, b_layout, epilogue, nq, grid, s);
