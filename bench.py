@@ -45,8 +45,8 @@ def parse():
                     help="time the backward of the adversarial-skew Mixtral-shaped workload instead "
                          "(reported as an extra line, not the headline)")
     ap.add_argument("--calib-copy", action="store_true",
-                    help="also run a plain device copy of 512 MiB (3 launches) to calibrate "
-                         "rocprofv3 FETCH_SIZE / WRITE_SIZE")
+                    help="also run a plain elementwise pass over 512 MiB (3 launches of torch's neg "
+                         "kernel: 512 MiB read, 512 MiB written) to calibrate rocprofv3 FETCH_SIZE / WRITE_SIZE")
     return ap.parse_args()
 
 
@@ -222,10 +222,12 @@ def main():
     }
     print(json.dumps(out), flush=True)
     if args.calib_copy:
-        src = torch.ones(256 << 20, dtype=torch.bfloat16, device="cuda")   # 512 MiB
+        # one kernel per launch that reads and writes exactly 512 MiB (a device-to-device copy may
+        # be split into several dispatches)
+        src = torch.ones(256 << 20, dtype=torch.bfloat16, device="cuda")
         dst = torch.empty_like(src)
         for _ in range(3):
-            dst.copy_(src)
+            torch.neg(src, out=dst)
         torch.cuda.synchronize()
 
 
