@@ -16,6 +16,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import re
 import sys
 import time
 
@@ -53,13 +54,21 @@ def parse():
 KERNEL_SOURCES = ["grouped_gemm.hip", "common.h"]
 
 
+def code_text(src: str) -> str:
+    """C++ source without comments and with whitespace runs collapsed: edits to comments leave
+    the code, and so the counters taken on it, unchanged."""
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
 def kernel_source_hash() -> str:
-    """sha256 of the grouped GEMM sources: traffic figures are valid only for this hash."""
+    """sha256 of the grouped GEMM code (comments stripped): traffic figures are valid only for it."""
     import hashlib
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "dropless_mixture_experts_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "dropless_mixture_experts_amd", "csrc", name)) as f:
+            h.update(code_text(f.read()).encode())
     return h.hexdigest()
 
 

@@ -6,19 +6,24 @@
 // that hold valid tokens; the group sizes are never copied to the host, so
 // the launch shape is fixed and the call can be captured in a graph.
 //
-// gfx950 design
-//   * 256x256 output tile per workgroup of 4 waves (2x2), 128x128 per wave,
-//     accumulated in 16 v_mfma_f32_32x32x16_bf16 tiles (v_mfma_f32_32x32x2_f32
-//     for fp32 inputs).
-//   * K is staged through LDS 128 bytes per row at a time, two stages
-//     (2 x 64 KB); rows are 8 chunks of 16 bytes with the chunk index XORed by
-//     a function of the row, so both the 16-byte LDS writes and the MFMA
-//     operand reads hit distinct banks.  The next stage's global loads are in flight while the
-//     current stage is multiplied.
-//   * Operands stored K-contiguous are copied chunk for chunk; operands stored
-//     with K as the row index (the K-by-N weight layout of the data-gradient
-//     GEMMs, and both operands of the weight gradient) are read as 8x8 (bf16)
-//     or 4x4 (fp32) blocks and transposed in registers before the LDS write.
+// gfx950 design: three engines share the tile lookup and the epilogues.
+//   * Ring kernel (bf16, weights N-by-K, K a multiple of 64: the forward GEMMs).
+//     256x256 output tile per workgroup of 4 waves (one per SIMD), 128x128 per
+//     wave in 16 v_mfma_f32_32x32x16_bf16 tiles.  K advances 64 elements at a
+//     time; each 32 KB half-stage (A or B) is copied global->LDS by DMA into a
+//     five-slot ring that fills the 160 KB LDS, two stages ahead of the MFMAs.
+//     Operand fragments are read from LDS two sub-steps ahead, one read between
+//     consecutive MFMAs.  An optional workspace splits the last, partly filled
+//     round of tiles along K (see the split-tail notes at the kernel).
+//   * Eight-wave DMA kernel (bf16 data gradient with K-by-N weights, the weight
+//     gradient, and the N-by-K cases the ring does not take).  Two waves per
+//     SIMD, 128x64 per wave; K-contiguous operands are copied chunk for chunk,
+//     K-row operands are read with transposing LDS reads.
+//   * Register-staged kernel (fp32, and K not a multiple of 32 elements).  Operands
+//     with K as the row index are read as 8x8 (bf16) or 4x4 (fp32) blocks and
+//     transposed in registers before the LDS write.
+//   * LDS rows are 16-byte chunks with the chunk index XORed by a function of the
+//     row, so DMA writes and MFMA operand reads hit distinct banks.
 //   * Each workgroup finds its (group, row tile, column tile) from the group
 //     offsets in device memory.  The grid is an upper bound computed on the
 //     host; surplus workgroups exit.  Consecutive tiles go to one XCD in
