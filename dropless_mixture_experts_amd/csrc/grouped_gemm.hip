@@ -1211,6 +1211,100 @@ __device__ __forceinline__ void store_partial(const GemmParams& p, int slot, con
     }
 }
 
+// Epilogue through LDS.  A wave's results leave the MFMAs with 4 consecutive columns per
+// lane (row lane & 31 of fragment i, columns 8 q + 4 (lane >> 5) + 0..3), so direct stores
+// would write 16 bytes to each of 32 rows per instruction.  Instead the wave converts its
+// 128-row block to bf16 in its own 32 KB of LDS (16-byte chunks XORed with the row, as in
+// the ring) and reads it back a row segment at a time: each store then writes whole rows
+// of CW columns (CW = 128: 4 rows of 256 bytes, CW = 64: 8 rows of 128 bytes).
+template <int CW>
+struct Out {
+  static constexpr int kCPR = CW / 8;         // 16-byte chunks per row
+  static constexpr int kRowBytes = CW * 2;
+  static constexpr int kRPI = 64 / kCPR;      // rows per store instruction
+  // columns 8 q + 4 hi + 0..3 of fragment jc at local row r
+  __device__ static void put(char* wl, int r, int jc, int q, int hi, const float (&v)[4]) {
+    const int chunk = (jc * 4 + q) ^ (r % kCPR);
+    *(uint2*)(wl + r * kRowBytes + chunk * 16 + hi * 8) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+  }
+  // rows row0 .. row0 + 127 (those below re) of columns col0 .. col0 + CW - 1 (those below
+  // ncols, a multiple of 8) to base + row * ld + col * 2
+  __device__ static void flush(const char* wl, char* base, int64_t ld, int64_t row0, int64_t re, int64_t col0,
+                               int64_t ncols) {
+    const int lane = threadIdx.x & 63;
+    const int c = lane % kCPR, rr = lane / kCPR;
+    const int64_t col = col0 + c * 8;
+    const bool cok = col < ncols;
+#pragma unroll
+    for (int it = 0; it < 128 / kRPI; ++it) {
+      const int r = it * kRPI + rr;
+      const uint4 v = *(const uint4*)(wl + r * kRowBytes + ((c ^ (r % kCPR)) * 16));
+      const int64_t row = row0 + r;
+      if (cok && row < re) *(uint4*)(base + row * ld + col * 2) = v;
+    }
+  }
+};
+
+// The ring kernel's epilogue (bf16 outputs; EPI_NONE or EPI_SWIGLU) for the wave's 128-row
+// block at row0; wl = this wave's 32 KB of LDS, free of every other wave's accesses.
+template <int EPI>
+__device__ __forceinline__ void store_tile_lds(const GemmParams& p, const f32x16 (&acc)[4][4], char* wl,
+                                               int64_t row0, int64_t re, int64_t col0) {
+  const int lane = threadIdx.x & 63;
+  const int l32 = lane & 31, hi = lane >> 5;
+  if constexpr (EPI == EPI_SWIGLU) {
+    // h (and, when saved, the gate half) in phase 1, the up half in phase 2
+    const int64_t F = p.N / 2;
+    char* wl2 = wl + 16384;
+    const bool save = p.epi_save != nullptr;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float h[4], g[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            g[e] = acc[i][j][4 * q + e];
+            h[e] = g[e] * sigmoid_fast(g[e]) * acc[i][j + 2][4 * q + e];
+          }
+          Out<64>::put(wl, i * 32 + l32, j, q, hi, h);
+          if (save) Out<64>::put(wl2, i * 32 + l32, j, q, hi, g);
+        }
+    Out<64>::flush(wl, (char*)p.C, F * 2, row0, re, col0, F);
+    if (save) {
+      Out<64>::flush(wl2, (char*)p.epi_save, p.N * 2, row0, re, col0, F);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            float u[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) u[e] = acc[i][j + 2][4 * q + e];
+            Out<64>::put(wl, i * 32 + l32, j, q, hi, u);
+          }
+      // the up half sits F columns to the right of the gate half of the saved row
+      Out<64>::flush(wl, (char*)p.epi_save + F * 2, p.N * 2, row0, re, col0, F);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e];
+          Out<128>::put(wl, i * 32 + l32, j, q, hi, v);
+        }
+    Out<128>::flush(wl, (char*)p.C, p.N * 2, row0, re, col0, p.N);
+  }
+}
+
 __device__ __forceinline__ void load_partial(const GemmParams& p, int slot, f32x16 (&acc)[4][4], bool add) {
   const float4* src = part_ptr(p, slot);
 #pragma unroll
@@ -1274,12 +1368,9 @@ void grouped_gemm_ring4_kernel(GemmParams p) {
     P.vb[q] = (uint32_t)((br - b0row) * ldb + c * 16);
   }
   mainloop<EPI>(P, len);
+  __syncthreads();  // every wave is done with the ring: its LDS now holds the epilogue staging
 
   const int wm = wave >> 1, wn = wave & 1;
-  int64_t col[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    col[j] = EPI == EPI_SWIGLU ? (int64_t)nt * 128 + wn * 64 + (j & 1) * 32 : (int64_t)nt * 256 + wn * 128 + j * 32;
   if (pc.part >= 0) {
     // a piece of a split tile: publish the partial; the last piece of the tile reduces
     const int r = pc.slot % pc.R;
@@ -1294,7 +1385,8 @@ void grouped_gemm_ring4_kernel(GemmParams p) {
     for (int j = 1; j < pc.f; ++j) load_partial(p, j * pc.R + r, acc, true);
     if (lane == 0) p.ws_count[r * 4 + wave] = 0;
   }
-  store_tile<bf16_t, EPI, 4, 4>(p, acc, m0 + wm * 128, re, col);
+  const int64_t col0 = EPI == EPI_SWIGLU ? (int64_t)nt * 128 + wn * 64 : (int64_t)nt * 256 + wn * 128;
+  store_tile_lds<EPI>(p, acc, (char*)smem + wave * 32768, m0 + wm * 128, re, col0);
 }
 
 // ---------------------------------------------------------------------------
