@@ -779,7 +779,7 @@ __device__ __forceinline__ bool find_tile(const GemmParams& p, int& g_out, int64
                                           int& nt_out, int* scratch, Piece* piece = nullptr) {
   constexpr int NW = NTHR / 64;
   int* s_wtot = scratch;       // NW ints
-  int* s_res = scratch + NW;   // 2 ints
+  int* s_res = scratch + NW;   // 4 ints: group, row tile in the group, its first and end row
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -787,9 +787,14 @@ __device__ __forceinline__ bool find_tile(const GemmParams& p, int& g_out, int64
   const int gpt = (p.G + NTHR - 1) / NTHR;
   const int g0 = tid * gpt;
   int local = 0;
+  int64_t rs0 = 0, re0 = 0;  // rows of group g0 (the only group of a thread when G <= NTHR)
   for (int g = g0; g < g0 + gpt && g < p.G; ++g) {
     int64_t rs, re;
     group_rows(p.offs, g, p.M, rs, re);
+    if (g == g0) {
+      rs0 = rs;
+      re0 = re;
+    }
     local += (int)((re - rs + kTile - 1) / kTile);
   }
   int incl = local;
@@ -802,6 +807,8 @@ __device__ __forceinline__ bool find_tile(const GemmParams& p, int& g_out, int64
   if (tid == 0) {
     s_res[0] = 0;
     s_res[1] = 0;
+    s_res[2] = 0;
+    s_res[3] = 0;
   }
   __syncthreads();
   int total_mt = 0;
@@ -845,24 +852,24 @@ __device__ __forceinline__ bool find_tile(const GemmParams& p, int& g_out, int64
   if (excl <= mt && mt < incl) {
     int run = excl;
     for (int g = g0; g < g0 + gpt && g < p.G; ++g) {
-      int64_t rs, re;
-      group_rows(p.offs, g, p.M, rs, re);
+      int64_t rs = rs0, re = re0;
+      if (g != g0) group_rows(p.offs, g, p.M, rs, re);
       const int c = (int)((re - rs + kTile - 1) / kTile);
       if (mt < run + c) {
+        // the owner passes the group's rows on, so no thread reads the offsets again (M < 2^31)
         s_res[0] = g;
         s_res[1] = mt - run;
+        s_res[2] = (int)rs;
+        s_res[3] = (int)re;
         break;
       }
       run += c;
     }
   }
   __syncthreads();
-  const int g = min(max(s_res[0], 0), p.G - 1);
-  int64_t rs, re;
-  group_rows(p.offs, g, p.M, rs, re);
-  g_out = g;
-  m0_out = rs + (int64_t)s_res[1] * kTile;
-  re_out = re;
+  g_out = min(max(s_res[0], 0), p.G - 1);
+  m0_out = (int64_t)s_res[2] + (int64_t)s_res[1] * kTile;
+  re_out = s_res[3];
   return true;
 }
 
@@ -875,7 +882,7 @@ void grouped_gemm_kernel(GemmParams p) {
   const int wave = tid >> 6;
   int g, nt;
   int64_t m0, re;
-  __shared__ int s_find[kThreads / 64 + 2];
+  __shared__ int s_find[kThreads / 64 + 4];
   if (!find_tile<kThreads>(p, g, m0, re, nt, s_find)) return;
 
   // ---- operands
@@ -941,7 +948,7 @@ void grouped_gemm8_kernel(GemmParams p) {
   using E = Elem<T>;
   int g, nt;
   int64_t m0, re;
-  __shared__ int s_find[kThreads8 / 64 + 2];
+  __shared__ int s_find[kThreads8 / 64 + 4];
   if (!find_tile<kThreads8>(p, g, m0, re, nt, s_find)) return;
   const int64_t esz = E::kBytes;
   const char* A = (const char*)p.A;
