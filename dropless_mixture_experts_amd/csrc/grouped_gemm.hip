@@ -1039,16 +1039,27 @@ __device__ __forceinline__ int64_t uniform64(int64_t v) {
 }
 __device__ __forceinline__ const char* uniform_ptr(const char* p) { return (const char*)uniform64((int64_t)p); }
 
-template <int EPI>
+// BL = LAYOUT_NK: B rows are K-contiguous like A (a B half-stage is 256 rows of 128 bytes).
+// BL = LAYOUT_KN (the data gradient's weights, [K rows][N]): a B half-stage is 64 K rows of the
+// tile's 256 columns (512 bytes each); 32-byte segments of an LDS row are XORed with
+// (k & 3) << 1 and fragments are read with ds_read_b64_tr_b16, two reads per fragment: within
+// each 16 lanes, lane i gets halfword (i & 3) of the 8 bytes at lane 4 e + (i >> 2) as element
+// e, so lanes pointed at K rows k0 + e, columns 4 q .. 4 q + 3, leave lane i with column i at
+// K rows k0 .. k0 + 3.
+template <int EPI, int BL = LAYOUT_NK>
 struct Pipe {
   const char* a_base;   // uniform: A at (first tile row, K = 0)
-  const char* b_base;   // uniform: B at (first tile row, K = 0)
+  const char* b_base;   // uniform: B at (first tile row, K = 0); KN: at (K row 0, column 0)
   uint32_t va[kQ], vb[kQ];
   uint32_t lds_w;       // uniform: LDS byte address of slot 0 + this wave's DMA block
   uint32_t a_off, b_off[4];  // per lane: byte offset of fragment row l32 within a slot
+                             // (KN: b_off[j] = 32-byte segment and 8-byte part of fragment j)
   uint32_t ch[4];            // per lane: byte offset of the 16-byte chunk of sub-step kk
+  uint32_t b_row = 0;        // KN, per lane: byte offset of K row 8 hi + e within a slot
+  int64_t b_stage = kStageBytes;  // uniform: global bytes of B per stage
   const char* L;
   f32x16 (&acc)[4][4];
+  static constexpr int kBL = BL;
 
   __device__ __forceinline__ Pipe(f32x16 (&c)[4][4], uint4* smem) : acc(c) {
     L = (const char*)smem;
@@ -1057,9 +1068,16 @@ struct Pipe {
     const int l32 = lane & 31, hi = lane >> 5;
     lds_w = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)smem + wave * kQ * 1024);
     a_off = (wm * 128 + l32) * 128;
+    if constexpr (BL == LAYOUT_KN) {
+      const int g = (lane >> 4) & 1, e = (lane >> 2) & 3, q = lane & 3;
+      b_row = (8 * hi + e) * 512;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      b_off[j] = ((EPI == EPI_SWIGLU ? ((j >> 1) * 128 + wn * 64 + (j & 1) * 32) : (wn * 128 + j * 32)) + l32) * 128;
+      for (int j = 0; j < 4; ++j) b_off[j] = (((wn * 8 + 2 * j + g) ^ (e << 1)) * 32) + q * 8;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        b_off[j] = ((EPI == EPI_SWIGLU ? ((j >> 1) * 128 + wn * 64 + (j & 1) * 32) : (wn * 128 + j * 32)) + l32) * 128;
+    }
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) ch[kk] = ((2 * kk + hi) ^ swz(l32)) * 16;
 #pragma unroll
@@ -1073,22 +1091,49 @@ struct Pipe {
   template <int OP>
   __device__ __forceinline__ void issue(int st, int q) const {
     const uint32_t lb = lds_w + (uint32_t)((2 * st + OP) % kSlots) * kSlotBytes + q * 1024;
-    const int64_t ko = (int64_t)st * kStageBytes;
-    if (OP) dma(b_base + ko, vb[q], lb);
-    else dma(a_base + ko, va[q], lb);
+    if (OP) dma(b_base + (int64_t)st * (BL == LAYOUT_KN ? b_stage : (int64_t)kStageBytes), vb[q], lb);
+    else dma(a_base + (int64_t)st * kStageBytes, va[q], lb);
+  }
+  // KN: half t (K rows 4 t .. 4 t + 3 of each lane's 8) of B fragment j of sub-step kk
+  __device__ __forceinline__ void read_tr(uint32_t sb, int kk, int j, int t, uint4& b) const {
+    const char* addr = L + sb + (16 * kk + 4 * t) * 512 + b_row + b_off[j];
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)addr);
+    const uint32_t w0 = (uint16_t)v[0] | ((uint32_t)(uint16_t)v[1] << 16);
+    const uint32_t w1 = (uint16_t)v[2] | ((uint32_t)(uint16_t)v[3] << 16);
+    if (t == 0) {
+      b.x = w0;
+      b.y = w1;
+    } else {
+      b.z = w0;
+      b.w = w1;
+    }
   }
   __device__ __forceinline__ void read(int s, int kk, uint4 (&a)[4], uint4 (&b)[4]) const {
     const uint32_t sa = (uint32_t)((2 * s) % kSlots) * kSlotBytes;
     const uint32_t sb = (uint32_t)((2 * s + 1) % kSlots) * kSlotBytes;
 #pragma unroll
     for (int i = 0; i < 4; ++i) a[i] = *(const uint4*)(L + sa + a_off + i * 4096 + ch[kk]);
+    if constexpr (BL == LAYOUT_KN) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = *(const uint4*)(L + sb + b_off[j] + ch[kk]);
+      for (int j = 0; j < 4; ++j) {
+        read_tr(sb, kk, j, 0, b[j]);
+        read_tr(sb, kk, j, 1, b[j]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = *(const uint4*)(L + sb + b_off[j] + ch[kk]);
+    }
   }
   // fragment r of sub-step kk of stage s: r < 4 the A fragment of rows 32 r, else B fragment r - 4
+  // (KN: r < 4 as above, else half (r - 4) & 1 of B fragment (r - 4) >> 1; 12 reads a set)
   __device__ __forceinline__ void read1(int s, int kk, int r, uint4 (&a)[4], uint4 (&b)[4]) const {
-    if (r < 4) a[r] = *(const uint4*)(L + (uint32_t)((2 * s) % kSlots) * kSlotBytes + a_off + r * 4096 + ch[kk]);
-    else b[r - 4] = *(const uint4*)(L + (uint32_t)((2 * s + 1) % kSlots) * kSlotBytes + b_off[r - 4] + ch[kk]);
+    if (r < 4) {
+      a[r] = *(const uint4*)(L + (uint32_t)((2 * s) % kSlots) * kSlotBytes + a_off + r * 4096 + ch[kk]);
+    } else if constexpr (BL == LAYOUT_KN) {
+      read_tr((uint32_t)((2 * s + 1) % kSlots) * kSlotBytes, kk, (r - 4) >> 1, (r - 4) & 1, b[(r - 4) >> 1]);
+    } else {
+      b[r - 4] = *(const uint4*)(L + (uint32_t)((2 * s + 1) % kSlots) * kSlotBytes + b_off[r - 4] + ch[kk]);
+    }
   }
   __device__ __forceinline__ void mma(const uint4 (&a)[4], const uint4 (&b)[4], int t0, int t1) const {
 #pragma unroll
@@ -1122,8 +1167,8 @@ struct Frags {
 // One sub-step: the 16 MFMAs of set CUR, one LDS read after each of them when RD (the
 // fragments of sub-steps R0 and R0 + 1 of stage rs, into their sets), and DMAs Q0 .. Q1-1
 // of operand OP of stage st spread between them.
-template <int EPI, int CUR, bool RD, int R0, int OP, int Q0, int Q1>
-__device__ __forceinline__ void substep(const Pipe<EPI>& P, Frags& f, int rs, int st) {
+template <typename PP, int CUR, bool RD, int R0, int OP, int Q0, int Q1>
+__device__ __forceinline__ void substep(const PP& P, Frags& f, int rs, int st) {
   constexpr int n = Q1 - Q0;
 #pragma unroll
   for (int t = 0; t < 16; ++t) {
@@ -1139,6 +1184,22 @@ __device__ __forceinline__ void substep(const Pipe<EPI>& P, Frags& f, int rs, in
   }
 }
 
+// KN form of a sub-step: the 12 reads of one fragment set (set R0 of stage rs), one after
+// each of the first 12 MFMAs.
+template <typename PP, int CUR, bool RD, int R0, int OP, int Q0, int Q1>
+__device__ __forceinline__ void substep_kn(const PP& P, Frags& f, int rs, int st) {
+  constexpr int n = Q1 - Q0;
+#pragma unroll
+  for (int t = 0; t < 16; ++t) {
+    P.mma(f.a[CUR], f.b[CUR], t, t + 1);
+    if (RD && t < 12) P.read1(rs, R0, t, f.a[R0], f.b[R0]);
+#pragma unroll
+    for (int q = 0; q < n; ++q)
+      if (t == (2 * q + 1) * 16 / (2 * (n > 0 ? n : 1))) P.template issue<OP>(st, Q0 + q);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // One stage.  Sub-step 0 reads the fragments of sub-steps 2 and 3, sub-step 2 those of
 // sub-steps 0 and 1 of the next stage, so every read has at least a sub-step of MFMAs
 // to land; the barrier sits between sub-steps 1 and 2, after the last reads of the
@@ -1146,22 +1207,36 @@ __device__ __forceinline__ void substep(const Pipe<EPI>& P, Frags& f, int rs, in
 // stage s+2 in sub-step 2 and DMAs 0..1 of the A half of stage s+3 in sub-step 3.
 // LOADS = 2: all of those; 1: no A half of stage s+3; 0: none.  VMC: the vmcnt the
 // barrier waits for (the DMAs issued after the B half of stage s+1).
-template <int EPI, int LOADS, bool NEXT, int VMC>
-__device__ __forceinline__ void stage(const Pipe<EPI>& P, int s, Frags& f) {
+// The KN form reads one set per sub-step instead (sets 2 and 3 of stage s in sub-steps 0 and
+// 1, sets 0 and 1 of stage s+1 in sub-steps 2 and 3): the same slots are read before the same
+// barrier, and every read still has a sub-step of MFMAs to land.
+template <typename PP, int LOADS, bool NEXT, int VMC>
+__device__ __forceinline__ void stage(const PP& P, int s, Frags& f) {
   constexpr int L1 = LOADS ? 1 : 0, L2 = LOADS == 2 ? 1 : 0;
-  substep<EPI, 0, true, 2, 0, 2, 2 + 3 * L1>(P, f, s, s + 2);
-  substep<EPI, 1, false, 0, 0, 5, 5 + 3 * L1>(P, f, s, s + 2);
+  constexpr bool KN = PP::kBL == LAYOUT_KN;
+  if constexpr (KN) {
+    substep_kn<PP, 0, true, 2, 0, 2, 2 + 3 * L1>(P, f, s, s + 2);
+    substep_kn<PP, 1, true, 3, 0, 5, 5 + 3 * L1>(P, f, s, s + 2);
+  } else {
+    substep<PP, 0, true, 2, 0, 2, 2 + 3 * L1>(P, f, s, s + 2);
+    substep<PP, 1, false, 0, 0, 5, 5 + 3 * L1>(P, f, s, s + 2);
+  }
   if (NEXT) {
     if (VMC == 8) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");
     else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     dma_barrier();  // stage s+1 landed and visible; every read of stage s done
   }
-  substep<EPI, 2, NEXT, 0, 1, 0, 8 * L1>(P, f, s + 1, s + 2);
-  substep<EPI, 3, false, 0, 0, 0, 2 * L2>(P, f, s + 1, s + 3);
+  if constexpr (KN) {
+    substep_kn<PP, 2, NEXT, 0, 1, 0, 8 * L1>(P, f, s + 1, s + 2);
+    substep_kn<PP, 3, NEXT, 1, 0, 0, 2 * L2>(P, f, s + 1, s + 3);
+  } else {
+    substep<PP, 2, NEXT, 0, 1, 0, 8 * L1>(P, f, s + 1, s + 2);
+    substep<PP, 3, false, 0, 0, 0, 2 * L2>(P, f, s + 1, s + 3);
+  }
 }
 
-template <int EPI>
-__device__ __forceinline__ void mainloop(Pipe<EPI>& P, int nk) {
+template <typename PP>
+__device__ __forceinline__ void mainloop(PP& P, int nk) {
   if (nk <= 0) return;
   // prologue: stages 0 and 1, and DMAs 0..1 of the A half of stage 2
 #pragma unroll
@@ -1189,10 +1264,10 @@ __device__ __forceinline__ void mainloop(Pipe<EPI>& P, int nk) {
   P.read(0, 1, f.a[1], f.b[1]);
   __builtin_amdgcn_sched_barrier(0);
   int s = 0;
-  for (; s + 3 < nk; ++s) stage<EPI, 2, true, 8>(P, s, f);
-  if (s + 2 < nk) stage<EPI, 1, true, 8>(P, s++, f);
-  if (s + 1 < nk) stage<EPI, 0, true, 0>(P, s++, f);
-  stage<EPI, 0, false, 0>(P, s, f);
+  for (; s + 3 < nk; ++s) stage<PP, 2, true, 8>(P, s, f);
+  if (s + 2 < nk) stage<PP, 1, true, 8>(P, s++, f);
+  if (s + 1 < nk) stage<PP, 0, true, 0>(P, s++, f);
+  stage<PP, 0, false, 0>(P, s, f);
 }
 
 }  // namespace ring4
@@ -1330,7 +1405,7 @@ __device__ __forceinline__ void load_partial(const GemmParams& p, int slot, f32x
 
 }  // namespace ring4
 
-template <int EPI>
+template <int EPI, int BL>
 __global__ __launch_bounds__(ring4::kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void grouped_gemm_ring4_kernel(GemmParams p) {
   using namespace ring4;
@@ -1351,10 +1426,19 @@ void grouped_gemm_ring4_kernel(GemmParams p) {
   const int len = pc.part >= 0 ? (pc.part + 1) * nk / pc.f - k0 : nk;
 
   f32x16 acc[4][4];
-  Pipe<EPI> P(acc, smem);
+  Pipe<EPI, BL> P(acc, smem);
   P.a_base = uniform_ptr((const char*)p.A + m0 * ldb + (int64_t)k0 * kStageBytes);
   const int64_t b0row = EPI == EPI_SWIGLU ? (int64_t)nt * 128 : (int64_t)nt * 256;
-  P.b_base = uniform_ptr((const char*)p.B + ((int64_t)g * p.N + b0row) * ldb + (int64_t)k0 * kStageBytes);
+  if constexpr (BL == LAYOUT_KN) {
+    // B = [Kd rows][N] per group; a stage is 64 K rows; lanes of DMA q fill K row
+    // 2 (wave * 8 + q) + lane / 32, 16 bytes each of the tile's 256 columns (clamped past N:
+    // those columns are never stored)
+    const int64_t ldn = p.N * 2;
+    P.b_stage = 64 * ldn;
+    P.b_base = uniform_ptr((const char*)p.B + (int64_t)g * p.Kd * ldn + (int64_t)k0 * 64 * ldn);
+  } else {
+    P.b_base = uniform_ptr((const char*)p.B + ((int64_t)g * p.N + b0row) * ldb + (int64_t)k0 * kStageBytes);
+  }
 #pragma unroll
   for (int q = 0; q < kQ; ++q) {
     const int r = (wave * kQ + q) * 8 + (lane >> 3);
@@ -1363,7 +1447,15 @@ void grouped_gemm_ring4_kernel(GemmParams p) {
     ar = ar < p.M ? ar : p.M - 1;
     P.va[q] = (uint32_t)((ar - m0) * ldb + c * 16);
     int64_t br;
-    if (EPI == EPI_SWIGLU) {
+    if constexpr (BL == LAYOUT_KN) {
+      const int kr = (wave * kQ + q) * 2 + (lane >> 5);
+      const int u = lane & 31;                                      // 16-byte unit of the LDS row
+      const int lu = (((u >> 1) ^ ((kr & 3) << 1)) << 1) | (u & 1);  // the 8 columns it holds
+      int64_t col = (int64_t)nt * 256 + lu * 8;
+      col = col < p.N ? col : p.N - 8;
+      P.vb[q] = (uint32_t)(kr * p.N * 2 + col * 2);
+      continue;
+    } else if (EPI == EPI_SWIGLU) {
       const int64_t F = p.N / 2;
       int64_t cc = (int64_t)nt * 128 + (r & 127);
       cc = cc < F ? cc : F - 1;
@@ -1374,7 +1466,7 @@ void grouped_gemm_ring4_kernel(GemmParams p) {
     }
     P.vb[q] = (uint32_t)((br - b0row) * ldb + c * 16);
   }
-  mainloop<EPI>(P, len);
+  mainloop(P, len);
   __syncthreads();  // every wave is done with the ring: its LDS now holds the epilogue staging
 
   const int wm = wave >> 1, wn = wave & 1;
@@ -1392,8 +1484,16 @@ void grouped_gemm_ring4_kernel(GemmParams p) {
     for (int j = 1; j < pc.f; ++j) load_partial(p, j * pc.R + r, acc, true);
     if (lane == 0) p.ws_count[r * 4 + wave] = 0;
   }
-  const int64_t col0 = EPI == EPI_SWIGLU ? (int64_t)nt * 128 + wn * 64 : (int64_t)nt * 256 + wn * 128;
-  store_tile_lds<EPI>(p, acc, (char*)smem + wave * 32768, m0 + wm * 128, re, col0);
+  if constexpr (EPI == EPI_DSWIGLU) {
+    // SwiGLU backward reads the saved pre-activations beside each output: direct loads and stores
+    int64_t col[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) col[j] = (int64_t)nt * 256 + wn * 128 + j * 32;
+    store_tile<bf16_t, EPI, 4, 4>(p, acc, m0 + wm * 128, re, col);
+  } else {
+    const int64_t col0 = EPI == EPI_SWIGLU ? (int64_t)nt * 128 + wn * 64 : (int64_t)nt * 256 + wn * 128;
+    store_tile_lds<EPI>(p, acc, (char*)smem + wave * 32768, m0 + wm * 128, re, col0);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1608,9 +1708,12 @@ hipError_t launch_grouped_gemm(const void* A, const void* B, int b_layout, const
   const int64_t kbytes = Kd * (dtype == 1 ? 2 : 4);
   const bool aligned = ((uintptr_t)A | (uintptr_t)B) % 16 == 0 && (b_layout == LAYOUT_NK || N % 8 == 0);
   const int nq = !aligned ? 0 : kbytes % Stage<4>::kRowBytes == 0 ? 4 : kbytes % Stage<2>::kRowBytes == 0 ? 2 : 0;
-  // the ring kernel: bf16, N-by-K weights, whole 128-byte K stages, per-lane DMA offsets within 32 bits
-  if (dtype == 1 && nq == 4 && b_layout == LAYOUT_NK && epilogue != EPI_DSWIGLU &&
-      (N + 256) * kbytes < ((int64_t)1 << 32)) {
+  // the ring kernel: bf16, whole 128-byte K stages, per-lane DMA offsets within 32 bits; N-by-K
+  // weights with the plain or SwiGLU epilogue, K-by-N weights with the plain or SwiGLU-backward one
+  const bool ring_nk = b_layout == LAYOUT_NK && epilogue != EPI_DSWIGLU && (N + 256) * kbytes < ((int64_t)1 << 32);
+  const bool ring_kn = b_layout == LAYOUT_KN && epilogue != EPI_SWIGLU && 64 * N * 2 < ((int64_t)1 << 32) &&
+                       (int64_t)256 * kbytes < ((int64_t)1 << 32);
+  if (dtype == 1 && nq == 4 && (ring_nk || ring_kn)) {
     // with a workspace the grid ends in up to P piece blocks of a split tail
     int dev = 0, cus = 0;
     if (prm.ws_slots > 0) {
@@ -1621,10 +1724,16 @@ hipError_t launch_grouped_gemm(const void* A, const void* B, int b_layout, const
     prm.P = cus;
     prm.nk = (int)(kbytes / ring4::kStageBytes);
     const dim3 rgrid((unsigned)(grid.x + cus));
-    if (epilogue == EPI_SWIGLU)
-      hipLaunchKernelGGL(grouped_gemm_ring4_kernel<EPI_SWIGLU>, rgrid, dim3(ring4::kThreads), 0, s, prm);
-    else
-      hipLaunchKernelGGL(grouped_gemm_ring4_kernel<EPI_NONE>, rgrid, dim3(ring4::kThreads), 0, s, prm);
+    if (ring_kn) {
+      if (epilogue == EPI_DSWIGLU)
+        hipLaunchKernelGGL((grouped_gemm_ring4_kernel<EPI_DSWIGLU, LAYOUT_KN>), rgrid, dim3(ring4::kThreads), 0, s, prm);
+      else
+        hipLaunchKernelGGL((grouped_gemm_ring4_kernel<EPI_NONE, LAYOUT_KN>), rgrid, dim3(ring4::kThreads), 0, s, prm);
+    } else if (epilogue == EPI_SWIGLU) {
+      hipLaunchKernelGGL((grouped_gemm_ring4_kernel<EPI_SWIGLU, LAYOUT_NK>), rgrid, dim3(ring4::kThreads), 0, s, prm);
+    } else {
+      hipLaunchKernelGGL((grouped_gemm_ring4_kernel<EPI_NONE, LAYOUT_NK>), rgrid, dim3(ring4::kThreads), 0, s, prm);
+    }
     return hipGetLastError();
   }
   if (dtype == 1) return gemm_dispatch<bf16_t>(prm, b_layout, epilogue, nq, grid, s);

@@ -348,6 +348,45 @@ def test_grouped_gemm_split_tail(swiglu):
         assert row.max() < TOL_BF16
 
 
+@pytest.mark.parametrize("dswiglu", [False, True])
+def test_grouped_gemm_kn_ring(dswiglu):
+    """The data-gradient form (K-by-N weights, bf16, K a multiple of 64) on ragged groups, with
+    several column tiles and a partial last one, with and without a workspace (the workspace
+    splits the last, partly filled round of tiles along K).  Results match the oracle row by
+    row, repeat bit for bit, and the workspace counters return to zero."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    N = 1000 if not dswiglu else 488                   # 4 or 2 column tiles, the last partial
+    Kd = 768                                           # 12 K stages
+    nt = (N + 255) // 256
+    rows = max(cus // nt, 1) + 1                       # a bit more than one round of tiles
+    counts = [256 * (rows - 2) + 100, 0, 300]
+    A, W, off, M = _gemm_case(True, N, Kd, lead=3, tail=4, seed=41, counts=counts)
+    Wkn = np.ascontiguousarray(W.transpose(0, 2, 1))   # [G, Kd, N]
+    pre = None
+    if dswiglu:
+        pre = mi.f32_to_bf16_bits(np.random.default_rng(42).standard_normal((M, 2 * N)).astype(np.float32))
+    ws = torch.zeros((moe.moe_grouped_gemm_workspace_size(),), dtype=torch.uint8, device="cuda")
+    epi = moe.MOE_EPI_DSWIGLU if dswiglu else moe.MOE_EPI_NONE
+    width = 2 * N if dswiglu else N
+    outs = []
+    for w in (ws, ws, None):
+        C = empty_like_poisoned((M, width), torch.bfloat16)
+        moe.moe_grouped_gemm(dev(A), dev(Wkn), 1, dev(off), C, epi, epi_in=dev(pre) if dswiglu else None, workspace=w)
+        torch.cuda.synchronize()
+        outs.append(C)
+    assert torch.count_nonzero(ws[:4096]).item() == 0
+    lo, hi = int(off[0]), int(off[-1])
+    assert torch.equal(outs[0][lo:hi], outs[1][lo:hi])
+    dh = orc.grouped_gemm(A[lo:hi], Wkn, off - lo, "kn")
+    ref = orc.swiglu_backward(dh, pre[lo:hi]) if dswiglu else dh
+    for C in (outs[0], outs[2]):
+        _check_untouched(C, off, M)
+        got = f64(C)[lo:hi]
+        assert rel_err(got, ref) < TOL_BF16 / 4
+        row = np.linalg.norm(got - ref, axis=1) / np.maximum(np.linalg.norm(ref, axis=1), 1e-30)
+        assert row.max() < TOL_BF16
+
+
 # ----------------------------------------------------------------- weight gradient
 
 @pytest.mark.parametrize("bf16", [True, False])
