@@ -1309,8 +1309,9 @@ struct Out {
     const int chunk = (jc * 4 + q) ^ (r % kCPR);
     *(uint2*)(wl + r * kRowBytes + chunk * 16 + hi * 8) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
   }
-  // rows row0 .. row0 + 127 (those below re) of columns col0 .. col0 + CW - 1 (those below
-  // ncols, a multiple of 8) to base + row * ld + col * 2
+  // local rows 0 .. NR-1 = rows row0 .. row0 + NR - 1 (those below re) of columns col0 ..
+  // col0 + CW - 1 (those below ncols, a multiple of 8) to base + row * ld + col * 2
+  template <int NR = 128>
   __device__ static void flush(const char* wl, char* base, int64_t ld, int64_t row0, int64_t re, int64_t col0,
                                int64_t ncols) {
     const int lane = threadIdx.x & 63;
@@ -1318,7 +1319,7 @@ struct Out {
     const int64_t col = col0 + c * 8;
     const bool cok = col < ncols;
 #pragma unroll
-    for (int it = 0; it < 128 / kRPI; ++it) {
+    for (int it = 0; it < NR / kRPI; ++it) {
       const int r = it * kRPI + rr;
       const uint4 v = *(const uint4*)(wl + r * kRowBytes + ((c ^ (r % kCPR)) * 16));
       const int64_t row = row0 + r;
@@ -1384,6 +1385,70 @@ __device__ __forceinline__ void store_tile_lds(const GemmParams& p, const f32x16
           Out<128>::put(wl, i * 32 + l32, j, q, hi, v);
         }
     Out<128>::flush(wl, (char*)p.C, p.N * 2, row0, re, col0, p.N);
+  }
+}
+
+// SwiGLU backward through LDS: acc = dH for the wave's 128 rows x 128 columns at (row0, col0);
+// epi_in = saved [G | U] of width 2F (F = N); C [M, 2F] = [dH U silu'(G) | dH silu(G)].  In
+// rounds of 32 rows: the rows of G and U are loaded whole (16 bytes a lane, 4 rows an
+// instruction) into 16 KB of the wave's LDS, each lane takes back the values beside its
+// accumulators, writes both results over them, and the two halves leave as whole row segments.
+__device__ __forceinline__ void store_tile_dswiglu_lds(const GemmParams& p, const f32x16 (&acc)[4][4], char* wl,
+                                                       int64_t row0, int64_t re, int64_t col0) {
+  using O = Out<128>;
+  const int64_t F = p.N;
+  const int64_t ld = 4 * F;  // bytes per row of epi_in and of C
+  const char* pre = (const char*)p.epi_in;
+  const int lane = threadIdx.x & 63;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int c = lane % O::kCPR, rr = lane / O::kCPR;
+  const int64_t col = col0 + c * 8;
+  const bool cok = col < F;
+  char* wg = wl;
+  char* wu = wl + 32 * O::kRowBytes;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint4 g[8], u[8];
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int r = it * O::kRPI + rr;
+      const int64_t row = row0 + i * 32 + r;
+      g[it] = make_uint4(0u, 0u, 0u, 0u);
+      u[it] = g[it];
+      if (cok && row < re) {
+        g[it] = *(const uint4*)(pre + row * ld + col * 2);
+        u[it] = *(const uint4*)(pre + row * ld + (F + col) * 2);
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int r = it * O::kRPI + rr;
+      const int off = r * O::kRowBytes + ((c ^ (r % O::kCPR)) * 16);
+      *(uint4*)(wg + off) = g[it];
+      *(uint4*)(wu + off) = u[it];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int off = l32 * O::kRowBytes + (((j * 4 + q) ^ (l32 % O::kCPR)) * 16) + hi * 8;
+        const uint2 gv = *(const uint2*)(wg + off), uv = *(const uint2*)(wu + off);
+        const float gs[4] = {__uint_as_float(gv.x << 16), __uint_as_float(gv.x & 0xffff0000u),
+                             __uint_as_float(gv.y << 16), __uint_as_float(gv.y & 0xffff0000u)};
+        const float us[4] = {__uint_as_float(uv.x << 16), __uint_as_float(uv.x & 0xffff0000u),
+                             __uint_as_float(uv.y << 16), __uint_as_float(uv.y & 0xffff0000u)};
+        float da[4], du[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float v = acc[i][j][4 * q + e], gg = gs[e], sg = sigmoid_fast(gg);
+          da[e] = v * us[e] * sg * (1.f + gg * (1.f - sg));
+          du[e] = v * gg * sg;
+        }
+        *(uint2*)(wg + off) = make_uint2(pack_bf16x2(da[0], da[1]), pack_bf16x2(da[2], da[3]));
+        *(uint2*)(wu + off) = make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
+      }
+    O::template flush<32>(wg, (char*)p.C, ld, row0 + i * 32, re, col0, F);
+    O::template flush<32>(wu, (char*)p.C + F * 2, ld, row0 + i * 32, re, col0, F);
   }
 }
 
@@ -1485,11 +1550,7 @@ void grouped_gemm_ring4_kernel(GemmParams p) {
     if (lane == 0) p.ws_count[r * 4 + wave] = 0;
   }
   if constexpr (EPI == EPI_DSWIGLU) {
-    // SwiGLU backward reads the saved pre-activations beside each output: direct loads and stores
-    int64_t col[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) col[j] = (int64_t)nt * 256 + wn * 128 + j * 32;
-    store_tile<bf16_t, EPI, 4, 4>(p, acc, m0 + wm * 128, re, col);
+    store_tile_dswiglu_lds(p, acc, (char*)smem + wave * 32768, m0 + wm * 128, re, (int64_t)nt * 256 + wn * 128);
   } else {
     const int64_t col0 = EPI == EPI_SWIGLU ? (int64_t)nt * 128 + wn * 64 : (int64_t)nt * 256 + wn * 128;
     store_tile_lds<EPI>(p, acc, (char*)smem + wave * 32768, m0 + wm * 128, re, col0);
