@@ -6,6 +6,9 @@
 // "What specialised optimisations does dropless MoE need?").  Both are pure
 // HBM streams over token rows: one wave per token moves whole rows with 16-byte
 // lanes, so every row is read once and written once as full 64-byte segments.
+// Measured with the caches cold (as they are between the grouped GEMMs):
+// permute is fastest with ordinary loads and stores (the GEMM reads x_perm next),
+// combine with non-temporal gathers and stores.
 #include "common.h"
 #include "internal.h"
 
@@ -15,7 +18,7 @@ namespace {
 
 constexpr int kRowsPerBlock = 4;  // one wave per row
 constexpr int kUnroll = 8;   // 16-byte vectors in flight per lane (permute: a whole 4096-wide bf16 row)
-constexpr int kCUnroll = 4;  // 16-byte vectors per lane per gathered row (combine)
+constexpr int kCUnroll = 8;  // 16-byte vectors per lane per gathered row (combine)
 
 // x_perm[slot_pos[s]] = (scale_s *) x[t] for the K slots s = t K + k of token t; optional
 // dgate_s = <x[t], ydot[slot_pos[s]]>.  One wave per token, so each token row is read from
@@ -49,7 +52,7 @@ __global__ __launch_bounds__(256) void permute_kernel(const uint4* __restrict__ 
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         const int64_t i = i0 + u * 64 + lane;
-        if (i < nvec) v[u] = ld_nt(src + i);
+        if (i < nvec) v[u] = src[i];
       }
       for (int k = 0; k < K; ++k) {
         const int64_t p = __shfl(pos, k, 64);
@@ -66,7 +69,7 @@ __global__ __launch_bounds__(256) void permute_kernel(const uint4* __restrict__ 
               for (int q = 0; q < E::kVec; ++q) f[q] *= sc;
               o = E::from_f32(f);
             }
-            st_nt(xp + p * nvec + i, o);
+            xp[p * nvec + i] = o;  // plain stores: the grouped GEMM reads these rows next
           }
         }
       }
@@ -84,7 +87,7 @@ __global__ __launch_bounds__(256) void permute_kernel(const uint4* __restrict__ 
           const int64_t i = i0 + u * 64 + lane;
           if (i < nvec) {
             v[u] = src[i];  // read once from HBM, again from the cache for the other slots
-            w[u] = ld_nt(yd + i);
+            w[u] = yd[i];
           }
         }
 #pragma unroll
@@ -102,7 +105,7 @@ __global__ __launch_bounds__(256) void permute_kernel(const uint4* __restrict__ 
               for (int q = 0; q < E::kVec; ++q) f[q] *= sc;
               o = E::from_f32(f);
             }
-            st_nt(xp + p * nvec + i, o);
+            xp[p * nvec + i] = o;
           }
         }
       }
