@@ -53,6 +53,7 @@ constexpr int kWindow = 256;               // blocks per XCD-remap window (one p
 
 enum { EPI_NONE = 0, EPI_SWIGLU = 1, EPI_DSWIGLU = 2 };
 enum { LAYOUT_NK = 0, LAYOUT_KN = 1 };
+constexpr int LAYOUT_WG = 2;  // ring pipeline of the weight gradient: both operands K-row
 
 // LDS chunk index of (row, 16-byte chunk c).  The XOR pattern g(row) = (row & 7) ^ ((row >> 3) & 1)
 // makes the 16 lanes that one LDS cycle serves (16 consecutive rows, one logical chunk:
@@ -1046,6 +1047,8 @@ __device__ __forceinline__ const char* uniform_ptr(const char* p) { return (cons
 // each 16 lanes, lane i gets halfword (i & 3) of the 8 bytes at lane 4 e + (i >> 2) as element
 // e, so lanes pointed at K rows k0 + e, columns 4 q .. 4 q + 3, leave lane i with column i at
 // K rows k0 .. k0 + 3.
+// BL = LAYOUT_WG (the weight gradient, dW = dY^T X over a group's rows): both operands are
+// K-row like the KN B operand, and both are read with ds_read_b64_tr_b16.
 template <int EPI, int BL = LAYOUT_NK>
 struct Pipe {
   const char* a_base;   // uniform: A at (first tile row, K = 0)
@@ -1056,7 +1059,10 @@ struct Pipe {
                              // (KN: b_off[j] = 32-byte segment and 8-byte part of fragment j)
   uint32_t ch[4];            // per lane: byte offset of the 16-byte chunk of sub-step kk
   uint32_t b_row = 0;        // KN, per lane: byte offset of K row 8 hi + e within a slot
+  uint32_t a_seg[4];         // WG, per lane: segment and 8-byte part of A fragment i
   int64_t b_stage = kStageBytes;  // uniform: global bytes of B per stage
+  int64_t a_stage = kStageBytes;  // uniform: global bytes of A per stage (WG)
+  int kvalid = 1 << 30;      // WG: rows of the reduction; DMAs of rows past them write zeros
   const char* L;
   f32x16 (&acc)[4][4];
   static constexpr int kBL = BL;
@@ -1068,11 +1074,13 @@ struct Pipe {
     const int l32 = lane & 31, hi = lane >> 5;
     lds_w = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)smem + wave * kQ * 1024);
     a_off = (wm * 128 + l32) * 128;
-    if constexpr (BL == LAYOUT_KN) {
+    if constexpr (BL == LAYOUT_KN || BL == LAYOUT_WG) {
       const int g = (lane >> 4) & 1, e = (lane >> 2) & 3, q = lane & 3;
       b_row = (8 * hi + e) * 512;
 #pragma unroll
       for (int j = 0; j < 4; ++j) b_off[j] = (((wn * 8 + 2 * j + g) ^ (e << 1)) * 32) + q * 8;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a_seg[i] = (((wm * 8 + 2 * i + g) ^ (e << 1)) * 32) + q * 8;
     } else {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
@@ -1091,12 +1099,31 @@ struct Pipe {
   template <int OP>
   __device__ __forceinline__ void issue(int st, int q) const {
     const uint32_t lb = lds_w + (uint32_t)((2 * st + OP) % kSlots) * kSlotBytes + q * 1024;
-    if (OP) dma(b_base + (int64_t)st * (BL == LAYOUT_KN ? b_stage : (int64_t)kStageBytes), vb[q], lb);
-    else dma(a_base + (int64_t)st * kStageBytes, va[q], lb);
+    const char* src = OP ? b_base + (int64_t)st * (BL != LAYOUT_NK ? b_stage : (int64_t)kStageBytes)
+                         : a_base + (int64_t)st * (BL == LAYOUT_WG ? a_stage : (int64_t)kStageBytes);
+    const uint32_t vo = OP ? vb[q] : va[q];
+    if constexpr (BL == LAYOUT_WG) {
+      if (st * 64 + 64 > kvalid) {
+        // the reduction's last stage: lanes whose row lies past its end write zeros instead
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        const int kr = (wave * kQ + q) * 2 + (lane >> 5);
+        if (st * 64 + kr < kvalid) {
+          dma(src, vo, lb);
+        } else {
+          const uint32_t slot = (uint32_t)((2 * st + OP) % kSlots);
+          *(uint4*)(L + slot * kSlotBytes + (wave * kQ + q) * 1024 + lane * 16) = make_uint4(0u, 0u, 0u, 0u);
+        }
+        return;
+      }
+    }
+    dma(src, vo, lb);
   }
   // KN: half t (K rows 4 t .. 4 t + 3 of each lane's 8) of B fragment j of sub-step kk
   __device__ __forceinline__ void read_tr(uint32_t sb, int kk, int j, int t, uint4& b) const {
-    const char* addr = L + sb + (16 * kk + 4 * t) * 512 + b_row + b_off[j];
+    read_tr_at(sb, kk, b_off[j], t, b);
+  }
+  __device__ __forceinline__ void read_tr_at(uint32_t sb, int kk, uint32_t seg, int t, uint4& b) const {
+    const char* addr = L + sb + (16 * kk + 4 * t) * 512 + b_row + seg;
     const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)addr);
     const uint32_t w0 = (uint16_t)v[0] | ((uint32_t)(uint16_t)v[1] << 16);
     const uint32_t w1 = (uint16_t)v[2] | ((uint32_t)(uint16_t)v[3] << 16);
@@ -1111,9 +1138,17 @@ struct Pipe {
   __device__ __forceinline__ void read(int s, int kk, uint4 (&a)[4], uint4 (&b)[4]) const {
     const uint32_t sa = (uint32_t)((2 * s) % kSlots) * kSlotBytes;
     const uint32_t sb = (uint32_t)((2 * s + 1) % kSlots) * kSlotBytes;
+    if constexpr (BL == LAYOUT_WG) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = *(const uint4*)(L + sa + a_off + i * 4096 + ch[kk]);
-    if constexpr (BL == LAYOUT_KN) {
+      for (int i = 0; i < 4; ++i) {
+        read_tr_at(sa, kk, a_seg[i], 0, a[i]);
+        read_tr_at(sa, kk, a_seg[i], 1, a[i]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = *(const uint4*)(L + sa + a_off + i * 4096 + ch[kk]);
+    }
+    if constexpr (BL == LAYOUT_KN || BL == LAYOUT_WG) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         read_tr(sb, kk, j, 0, b[j]);
@@ -1126,7 +1161,13 @@ struct Pipe {
   }
   // fragment r of sub-step kk of stage s: r < 4 the A fragment of rows 32 r, else B fragment r - 4
   // (KN: r < 4 as above, else half (r - 4) & 1 of B fragment (r - 4) >> 1; 12 reads a set)
+  // (WG: r < 8 half r & 1 of A fragment r >> 1, else half of B fragment (r - 8) >> 1; 16 reads)
   __device__ __forceinline__ void read1(int s, int kk, int r, uint4 (&a)[4], uint4 (&b)[4]) const {
+    if constexpr (BL == LAYOUT_WG) {
+      if (r < 8) read_tr_at((uint32_t)((2 * s) % kSlots) * kSlotBytes, kk, a_seg[r >> 1], r & 1, a[r >> 1]);
+      else read_tr((uint32_t)((2 * s + 1) % kSlots) * kSlotBytes, kk, (r - 8) >> 1, (r - 8) & 1, b[(r - 8) >> 1]);
+      return;
+    }
     if (r < 4) {
       a[r] = *(const uint4*)(L + (uint32_t)((2 * s) % kSlots) * kSlotBytes + a_off + r * 4096 + ch[kk]);
     } else if constexpr (BL == LAYOUT_KN) {
@@ -1184,15 +1225,16 @@ __device__ __forceinline__ void substep(const PP& P, Frags& f, int rs, int st) {
   }
 }
 
-// KN form of a sub-step: the 12 reads of one fragment set (set R0 of stage rs), one after
-// each of the first 12 MFMAs.
+// KN form of a sub-step: the reads of one fragment set (set R0 of stage rs: 12 for KN, 16 for
+// WG), one after each of the first MFMAs.
 template <typename PP, int CUR, bool RD, int R0, int OP, int Q0, int Q1>
 __device__ __forceinline__ void substep_kn(const PP& P, Frags& f, int rs, int st) {
   constexpr int n = Q1 - Q0;
+  constexpr int NR = PP::kBL == LAYOUT_WG ? 16 : 12;
 #pragma unroll
   for (int t = 0; t < 16; ++t) {
     P.mma(f.a[CUR], f.b[CUR], t, t + 1);
-    if (RD && t < 12) P.read1(rs, R0, t, f.a[R0], f.b[R0]);
+    if (RD && t < NR) P.read1(rs, R0, t, f.a[R0], f.b[R0]);
 #pragma unroll
     for (int q = 0; q < n; ++q)
       if (t == (2 * q + 1) * 16 / (2 * (n > 0 ? n : 1))) P.template issue<OP>(st, Q0 + q);
@@ -1213,7 +1255,7 @@ __device__ __forceinline__ void substep_kn(const PP& P, Frags& f, int rs, int st
 template <typename PP, int LOADS, bool NEXT, int VMC>
 __device__ __forceinline__ void stage(const PP& P, int s, Frags& f) {
   constexpr int L1 = LOADS ? 1 : 0, L2 = LOADS == 2 ? 1 : 0;
-  constexpr bool KN = PP::kBL == LAYOUT_KN;
+  constexpr bool KN = PP::kBL == LAYOUT_KN || PP::kBL == LAYOUT_WG;
   if constexpr (KN) {
     substep_kn<PP, 0, true, 2, 0, 2, 2 + 3 * L1>(P, f, s, s + 2);
     substep_kn<PP, 1, true, 3, 0, 5, 5 + 3 * L1>(P, f, s, s + 2);
@@ -1559,6 +1601,8 @@ void grouped_gemm_ring4_kernel(GemmParams p) {
 
 // ---------------------------------------------------------------------------
 // dW[g] = dY_g^T X_g: output tile (n, kd) of group g, reduction over the group's rows.
+constexpr int kMaxGroupsWg = 1024;  // group sizes the ring weight-gradient kernel sorts in LDS
+
 struct WgradParams {
   const void* X;
   const void* dY;
@@ -1704,6 +1748,121 @@ void grouped_wgrad8_kernel(WgradParams p) {
   store_wgrad<4, 2>(p.dW + (int64_t)g * p.N * p.Kd, acc, n0 + wm * 128, k0 + wn * 64, p.N, p.Kd, p.accumulate);
 }
 
+// Weight-gradient epilogue of a ring wave: acc[i][j] = rows row0 + 32 i (N index) and columns
+// col0 + 32 j (Kd index) of one group's [N, Kd] fp32 dW, a lane holding 4 consecutive columns.
+// Through the wave's 32 KB of LDS in two rounds of 64 rows (16-byte chunks XORed with the
+// row), so each store (or accumulate) covers two whole rows of 512 bytes.
+__device__ __forceinline__ void store_wgrad_lds(float* out, const f32x16 (&acc)[4][4], char* wl, int64_t row0,
+                                                int64_t col0, int64_t N, int64_t Kd, int accumulate) {
+  const int lane = threadIdx.x & 63;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int c = lane & 31, rr = lane >> 5;
+  const int64_t col = col0 + c * 4;
+  const bool cok = col < Kd;  // Kd is a multiple of 8: a chunk of 4 columns is all in or all out
+#pragma unroll
+  for (int i0 = 0; i0 < 4; i0 += 2) {
+#pragma unroll
+    for (int di = 0; di < 2; ++di)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int r = di * 32 + l32;
+          const int chunk = (j * 8 + 2 * q + hi) ^ (r & 31);
+          const f32x16& a = acc[i0 + di][j];
+          *(float4*)(wl + r * 512 + chunk * 16) = make_float4(a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]);
+        }
+#pragma unroll
+    for (int it = 0; it < 32; ++it) {
+      const int r = it * 2 + rr;
+      float4 v = *(const float4*)(wl + r * 512 + ((c ^ (r & 31)) * 16));
+      const int64_t row = row0 + i0 * 32 + r;
+      if (cok && row < N) {
+        float4* dst = (float4*)(out + row * Kd + col);
+        if (accumulate) {
+          const float4 o = *dst;
+          v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
+        }
+        *dst = v;
+      }
+    }
+  }
+}
+
+// Weight gradient on the ring pipeline: dW_g[n0:n0+256, k0:k0+256] = dY_g^T X_g over the
+// group's rows, 64 rows a stage (the last one zero-filled past the group's end).  Tiles are
+// ordered as in the eight-wave kernel: groups by decreasing size, column tiles of X adjacent.
+__global__ __launch_bounds__(ring4::kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void grouped_wgrad_ring_kernel(WgradParams p) {
+  using namespace ring4;
+  __shared__ uint4 smem[kSlots * kSlotUnits];
+  int* s_rows = (int*)smem;  // group sizes, before any load targets the LDS
+  int* s_group = s_rows + kMaxGroupsWg;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int64_t tpg = (int64_t)p.TN * p.TK;
+  const int64_t total = tpg * p.G;
+  const int64_t win = (int64_t)blockIdx.x / kWindow * kWindow;
+  const int64_t L = win + xcd_remap((int64_t)blockIdx.x - win, min((int64_t)kWindow, total - win));
+  const int rank = (int)(L / tpg);
+  for (int h = tid; h < p.G; h += ring4::kThreads) {
+    int64_t a, b;
+    group_rows(p.offs, h, p.M, a, b);
+    s_rows[h] = (int)(b - a);
+  }
+  if (tid == 0) s_group[0] = 0;
+  __syncthreads();
+  for (int h = tid; h < p.G; h += ring4::kThreads) {
+    const int rows = s_rows[h];
+    int r = 0;
+    for (int u = 0; u < p.G; ++u) {
+      const int o = s_rows[u];
+      r += (o > rows) | ((o == rows) & (u < h));
+    }
+    if (r == rank) s_group[0] = h;
+  }
+  __syncthreads();
+  const int g = __builtin_amdgcn_readfirstlane(s_group[0]);
+  __syncthreads();  // every thread has read the scratch before the loads overwrite it
+  const int rem = (int)(L - (int64_t)rank * tpg);
+  const int tk = rem / p.TN;  // neighbouring tiles share the same X columns
+  const int tn = rem % p.TN;
+  int64_t rs, re;
+  group_rows(p.offs, g, p.M, rs, re);
+  rs = uniform64(rs);
+  const int rows = (int)(re - rs);
+  const int64_t n0 = (int64_t)tn * kTile, k0 = (int64_t)tk * kTile;
+  const int nk = (rows + 63) / 64;
+
+  f32x16 acc[4][4];
+  Pipe<EPI_NONE, LAYOUT_WG> P(acc, smem);
+  const int64_t lda = p.N * 2, ldb = p.Kd * 2;
+  P.a_stage = 64 * lda;
+  P.b_stage = 64 * ldb;
+  P.kvalid = rows;
+  P.a_base = uniform_ptr((const char*)p.dY + rs * lda);
+  P.b_base = uniform_ptr((const char*)p.X + rs * ldb);
+#pragma unroll
+  for (int q = 0; q < kQ; ++q) {
+    // lanes of DMA q fill row 2 (wave * 8 + q) + lane / 32 of the stage, 16 bytes each of the
+    // tile's 256 columns (clamped past the width: those outputs are never stored)
+    const int kr = (wave * kQ + q) * 2 + (lane >> 5);
+    const int u = lane & 31;
+    const int lu = (((u >> 1) ^ ((kr & 3) << 1)) << 1) | (u & 1);
+    int64_t ca = n0 + lu * 8, cb = k0 + lu * 8;
+    ca = ca < p.N ? ca : p.N - 8;
+    cb = cb < p.Kd ? cb : p.Kd - 8;
+    P.va[q] = (uint32_t)(kr * lda + ca * 2);
+    P.vb[q] = (uint32_t)(kr * ldb + cb * 2);
+  }
+  mainloop(P, nk);  // zeros when the group is empty
+  __syncthreads();  // every wave is done with the ring: its LDS now holds the epilogue staging
+  if (p.accumulate && nk == 0) return;  // accumulate mode leaves an empty group's dW as it is
+  const int wm = wave >> 1, wn = wave & 1;
+  store_wgrad_lds(p.dW + (int64_t)g * p.N * p.Kd, acc, (char*)smem + wave * 32768, n0 + wm * 128, k0 + wn * 128,
+                  p.N, p.Kd, p.accumulate);
+}
+
 // nq: DMA instructions per wave per operand per stage (4: 64-element stages, 2: 32-element
 // stages), 0 for the register-staged kernel
 template <typename T>
@@ -1810,7 +1969,11 @@ hipError_t launch_grouped_wgrad(const void* X, const void* dY, const int32_t* of
   const dim3 grid((unsigned)((int64_t)prm.TN * prm.TK * G));
   // the LDS-DMA pipeline moves 16-byte pieces of rows: bf16 widths that are multiples of 8
   const bool dma = dtype == 1 && N % 8 == 0 && Kd % 8 == 0 && ((uintptr_t)X | (uintptr_t)dY) % 16 == 0;
-  if (dma)
+  // the ring form: per-lane DMA offsets of 64 rows within 32 bits
+  const bool ring = dma && G <= kMaxGroupsWg && 64 * std::max(N, Kd) * 2 < ((int64_t)1 << 32);
+  if (ring)
+    hipLaunchKernelGGL(grouped_wgrad_ring_kernel, grid, dim3(ring4::kThreads), 0, s, prm);
+  else if (dma)
     hipLaunchKernelGGL(grouped_wgrad8_kernel<4>, grid, dim3(kThreads8), 0, s, prm);
   else if (dtype == 1)
     hipLaunchKernelGGL((grouped_wgrad_kernel<bf16_t>), grid, dim3(kThreads), 0, s, prm);

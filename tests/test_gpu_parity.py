@@ -413,6 +413,37 @@ def test_wgrad_parity(bf16, accumulate):
             assert rel_err(got[g], ref[g]) < tol, g
 
 
+@pytest.mark.parametrize("accumulate", [False, True])
+def test_wgrad_multi_tile(accumulate):
+    """bf16 weight gradient over several 256 x 256 output tiles per group (the last partial in
+    both directions), a dozen groups with ragged row counts (reductions ending inside a
+    64-row stage) and empty ones: every group matches the oracle, empty groups are exactly zero
+    (or untouched when accumulating), and two calls agree bit for bit."""
+    rng = np.random.default_rng(23)
+    counts = rng.integers(1, 700, size=12)
+    counts[[2, 7]] = 0
+    counts[5] = 64
+    off = np.concatenate([[0], np.cumsum(counts)])
+    M, N, Kd = int(off[-1]), 520, 776
+    X = mi.f32_to_bf16_bits(rng.standard_normal((M, Kd)).astype(np.float32))
+    dY = mi.f32_to_bf16_bits(rng.standard_normal((M, N)).astype(np.float32))
+    init = rng.standard_normal((len(counts), N, Kd)).astype(np.float32)
+    outs = []
+    for _ in range(2):
+        dW = dev(init) if accumulate else empty_like_poisoned((len(counts), N, Kd), torch.float32)
+        moe.moe_grouped_gemm_wgrad(dev(X), dev(dY), dev(off), dW, accumulate=accumulate)
+        torch.cuda.synchronize()
+        outs.append(dW)
+    assert torch.equal(outs[0], outs[1])
+    got = f64(outs[0])
+    ref = orc.grouped_wgrad(X, dY, off) + (init.astype(np.float64) if accumulate else 0.0)
+    for g in range(len(counts)):
+        if counts[g] == 0:
+            assert np.array_equal(got[g], ref[g]), "empty group must be exactly zero / untouched"
+        else:
+            assert rel_err(got[g], ref[g]) < TOL_BF16 / 4, g
+
+
 # ----------------------------------------------------------------- whole layer
 
 SMALL_BF16 = mi.MoEConfig("small_bf16", seed=31, T=600, d=256, E=8, K=2, F=384, bf16=True, wr_std=0.05)
