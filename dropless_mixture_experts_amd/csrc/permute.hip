@@ -6,9 +6,10 @@
 // "What specialised optimisations does dropless MoE need?").  Both are pure
 // HBM streams over token rows: one wave per token moves whole rows with 16-byte
 // lanes, so every row is read once and written once as full 64-byte segments.
-// Measured with the caches cold (as they are between the grouped GEMMs):
-// permute is fastest with ordinary loads and stores (the GEMM reads x_perm next),
-// combine with non-temporal gathers and stores.
+// Measured with the caches cold (as they are between the grouped GEMMs): the
+// forward permute is fastest with ordinary loads and stores (the GEMM reads x_perm
+// next); combine, and the backward permute's streams of Y_perm and dY_perm, with
+// non-temporal accesses.
 #include "common.h"
 #include "internal.h"
 
@@ -87,7 +88,7 @@ __global__ __launch_bounds__(256) void permute_kernel(const uint4* __restrict__ 
           const int64_t i = i0 + u * 64 + lane;
           if (i < nvec) {
             v[u] = src[i];  // read once from HBM, again from the cache for the other slots
-            w[u] = yd[i];
+            w[u] = ld_nt(yd + i);
           }
         }
 #pragma unroll
@@ -105,7 +106,7 @@ __global__ __launch_bounds__(256) void permute_kernel(const uint4* __restrict__ 
               for (int q = 0; q < E::kVec; ++q) f[q] *= sc;
               o = E::from_f32(f);
             }
-            xp[p * nvec + i] = o;
+            st_nt(xp + p * nvec + i, o);
           }
         }
       }
