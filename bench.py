@@ -106,7 +106,51 @@ def cpu_baseline(cfg, inp, target_s: float) -> dict | None:
         dt = run(S)
     return {"value": S / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
             "sample": f"first {S} of {cfg.T} tokens of the {cfg.name} workload, full forward "
-                      f"(router, top-K, permute, per-expert fp64 GEMMs, combine) in {dt:.1f} s"}
+                      f"(router, top-K, permute, per-expert fp64 GEMMs, combine) in {dt:.1f} s",
+            "host": host_description(cores)}
+
+
+def host_description(threads: int) -> str:
+    """CPU model, logical CPUs and the BLAS the oracle's NumPy uses."""
+    model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = "unknown BLAS"
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if libs:
+            blas = f"{libs[0].get('internal_api', 'blas')} {libs[0].get('version', '')}".strip()
+    except Exception:  # pragma: no cover
+        pass
+    return f"{model}, {os.cpu_count()} logical CPUs visible, {blas} with {threads} threads"
+
+
+def copy_bandwidth(torch) -> float:
+    """On-box HBM reference: GB/s (bytes read + written) of a 1 GiB device copy, median of five
+    launches, each after a 1 GiB elementwise pass that evicts the caches."""
+    src = torch.empty(512 << 20, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    flush_a = torch.empty(256 << 20, dtype=torch.float32, device="cuda").fill_(2.0)
+    flush_b = torch.empty_like(flush_a)
+    ts = []
+    for _ in range(6):
+        torch.neg(flush_a, out=flush_b)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    ms = sorted(ts[1:])[2]
+    del src, dst, flush_a, flush_b
+    return 2 * (1 << 30) / (ms * 1e-3) / 1e9
 
 
 def main():
@@ -199,7 +243,11 @@ def main():
 
     tokens_per_s = cfg.T / (ms_per_step * 1e-3)
     counts = bufs.counts.cpu().numpy()
+    copy_gbs = copy_bandwidth(torch)  # after the timed region
     cpu = cpu_baseline(cfg, inp, args.cpu_seconds)
+    hbm = {"permute": perm_bytes / (kms["permute"] * 1e-3) / 1e9,
+           "combine": comb_bytes / (kms["combine"] * 1e-3) / 1e9,
+           "router": router_bytes / (kms["router"] * 1e-3) / 1e9}
 
     out = {
         "metric": "MoE layer forward tokens/s (grouped-GEMM TFLOP/s and % of bf16 MFMA peak alongside)",
@@ -220,9 +268,10 @@ def main():
         "grouped_gemm": {"tflops": tf_gg, "frac_of_peak": tf_gg / peak, "gate_up_tflops": tf_up,
                          "down_tflops": tf_down, "flops_per_step": flops_up + flops_down},
         "kernels_ms": kms,
-        "hbm_gbs": {"permute": perm_bytes / (kms["permute"] * 1e-3) / 1e9,
-                    "combine": comb_bytes / (kms["combine"] * 1e-3) / 1e9,
-                    "router": router_bytes / (kms["router"] * 1e-3) / 1e9},
+        "hbm_gbs": hbm,
+        # each HBM rate as a fraction of the spec peak (8 TB/s) and of an on-box 1 GiB copy
+        "hbm_frac": {k: {"of_spec": v / 8000.0, "of_onbox_copy": v / copy_gbs} for k, v in hbm.items()},
+        "onbox_copy_gbs": copy_gbs,
         "load": {"min": int(counts.min()), "max": int(counts.max()), "empty": int((counts == 0).sum())},
         "roofline": {"kernel": "grouped GEMM gate/up + SwiGLU", "bound": "mfma", "achieved": tf_up,
                      "peak": peak, "unit": "TFLOP/s", "frac": tf_up / peak, "traffic": traffic},
