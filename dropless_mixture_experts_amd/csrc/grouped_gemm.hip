@@ -1096,13 +1096,14 @@ struct Pipe {
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
   }
   // DMA q of operand OP (0: A, 1: B) of stage st, i.e. of half-stage 2 st + OP
-  template <int OP>
+  // CHK (WG only): the stage may be the reduction's last, partly filled one
+  template <int OP, bool CHK = true>
   __device__ __forceinline__ void issue(int st, int q) const {
     const uint32_t lb = lds_w + (uint32_t)((2 * st + OP) % kSlots) * kSlotBytes + q * 1024;
     const char* src = OP ? b_base + (int64_t)st * (BL != LAYOUT_NK ? b_stage : (int64_t)kStageBytes)
                          : a_base + (int64_t)st * (BL == LAYOUT_WG ? a_stage : (int64_t)kStageBytes);
     const uint32_t vo = OP ? vb[q] : va[q];
-    if constexpr (BL == LAYOUT_WG) {
+    if constexpr (BL == LAYOUT_WG && CHK) {
       if (st * 64 + 64 > kvalid) {
         // the reduction's last stage: lanes whose row lies past its end write zeros instead
         const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -1208,7 +1209,7 @@ struct Frags {
 // One sub-step: the 16 MFMAs of set CUR, one LDS read after each of them when RD (the
 // fragments of sub-steps R0 and R0 + 1 of stage rs, into their sets), and DMAs Q0 .. Q1-1
 // of operand OP of stage st spread between them.
-template <typename PP, int CUR, bool RD, int R0, int OP, int Q0, int Q1>
+template <typename PP, int CUR, bool RD, int R0, int OP, int Q0, int Q1, bool CHK = true>
 __device__ __forceinline__ void substep(const PP& P, Frags& f, int rs, int st) {
   constexpr int n = Q1 - Q0;
 #pragma unroll
@@ -1220,14 +1221,14 @@ __device__ __forceinline__ void substep(const PP& P, Frags& f, int rs, int st) {
     }
 #pragma unroll
     for (int q = 0; q < n; ++q)
-      if (t == (2 * q + 1) * 16 / (2 * (n > 0 ? n : 1))) P.template issue<OP>(st, Q0 + q);
+      if (t == (2 * q + 1) * 16 / (2 * (n > 0 ? n : 1))) P.template issue<OP, CHK>(st, Q0 + q);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
 // KN form of a sub-step: the reads of one fragment set (set R0 of stage rs: 12 for KN, 16 for
 // WG), one after each of the first MFMAs.
-template <typename PP, int CUR, bool RD, int R0, int OP, int Q0, int Q1>
+template <typename PP, int CUR, bool RD, int R0, int OP, int Q0, int Q1, bool CHK = true>
 __device__ __forceinline__ void substep_kn(const PP& P, Frags& f, int rs, int st) {
   constexpr int n = Q1 - Q0;
   constexpr int NR = PP::kBL == LAYOUT_WG ? 16 : 12;
@@ -1237,7 +1238,7 @@ __device__ __forceinline__ void substep_kn(const PP& P, Frags& f, int rs, int st
     if (RD && t < NR) P.read1(rs, R0, t, f.a[R0], f.b[R0]);
 #pragma unroll
     for (int q = 0; q < n; ++q)
-      if (t == (2 * q + 1) * 16 / (2 * (n > 0 ? n : 1))) P.template issue<OP>(st, Q0 + q);
+      if (t == (2 * q + 1) * 16 / (2 * (n > 0 ? n : 1))) P.template issue<OP, CHK>(st, Q0 + q);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -1252,13 +1253,13 @@ __device__ __forceinline__ void substep_kn(const PP& P, Frags& f, int rs, int st
 // The KN form reads one set per sub-step instead (sets 2 and 3 of stage s in sub-steps 0 and
 // 1, sets 0 and 1 of stage s+1 in sub-steps 2 and 3): the same slots are read before the same
 // barrier, and every read still has a sub-step of MFMAs to land.
-template <typename PP, int LOADS, bool NEXT, int VMC>
+template <typename PP, int LOADS, bool NEXT, int VMC, bool CHK = true>
 __device__ __forceinline__ void stage(const PP& P, int s, Frags& f) {
   constexpr int L1 = LOADS ? 1 : 0, L2 = LOADS == 2 ? 1 : 0;
   constexpr bool KN = PP::kBL == LAYOUT_KN || PP::kBL == LAYOUT_WG;
   if constexpr (KN) {
-    substep_kn<PP, 0, true, 2, 0, 2, 2 + 3 * L1>(P, f, s, s + 2);
-    substep_kn<PP, 1, true, 3, 0, 5, 5 + 3 * L1>(P, f, s, s + 2);
+    substep_kn<PP, 0, true, 2, 0, 2, 2 + 3 * L1, CHK>(P, f, s, s + 2);
+    substep_kn<PP, 1, true, 3, 0, 5, 5 + 3 * L1, CHK>(P, f, s, s + 2);
   } else {
     substep<PP, 0, true, 2, 0, 2, 2 + 3 * L1>(P, f, s, s + 2);
     substep<PP, 1, false, 0, 0, 5, 5 + 3 * L1>(P, f, s, s + 2);
@@ -1269,8 +1270,8 @@ __device__ __forceinline__ void stage(const PP& P, int s, Frags& f) {
     dma_barrier();  // stage s+1 landed and visible; every read of stage s done
   }
   if constexpr (KN) {
-    substep_kn<PP, 2, NEXT, 0, 1, 0, 8 * L1>(P, f, s + 1, s + 2);
-    substep_kn<PP, 3, NEXT, 1, 0, 0, 2 * L2>(P, f, s + 1, s + 3);
+    substep_kn<PP, 2, NEXT, 0, 1, 0, 8 * L1, CHK>(P, f, s + 1, s + 2);
+    substep_kn<PP, 3, NEXT, 1, 0, 0, 2 * L2, CHK>(P, f, s + 1, s + 3);
   } else {
     substep<PP, 2, NEXT, 0, 1, 0, 8 * L1>(P, f, s + 1, s + 2);
     substep<PP, 3, false, 0, 0, 0, 2 * L2>(P, f, s + 1, s + 3);
@@ -1306,6 +1307,10 @@ __device__ __forceinline__ void mainloop(PP& P, int nk) {
   P.read(0, 1, f.a[1], f.b[1]);
   __builtin_amdgcn_sched_barrier(0);
   int s = 0;
+  if constexpr (PP::kBL == LAYOUT_WG) {
+    // stages up to nk - 5 load nothing of the last stage: no zero-fill checks there
+    for (; s + 4 < nk; ++s) stage<PP, 2, true, 8, false>(P, s, f);
+  }
   for (; s + 3 < nk; ++s) stage<PP, 2, true, 8>(P, s, f);
   if (s + 2 < nk) stage<PP, 1, true, 8>(P, s++, f);
   if (s + 1 < nk) stage<PP, 0, true, 0>(P, s++, f);
