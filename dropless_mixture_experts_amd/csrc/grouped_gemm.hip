@@ -780,7 +780,7 @@ __device__ __forceinline__ bool find_tile(const GemmParams& p, int& g_out, int64
                                           int& nt_out, int* scratch, Piece* piece = nullptr) {
   constexpr int NW = NTHR / 64;
   int* s_wtot = scratch;       // NW ints
-  int* s_res = scratch + NW;   // 4 ints: group, row tile in the group, its first and end row
+  int* s_res = scratch + NW;   // 5 ints: group, row tile in the group, first and end row, column tile
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -805,12 +805,7 @@ __device__ __forceinline__ bool find_tile(const GemmParams& p, int& g_out, int64
     if (lane >= o) incl += u;
   }
   if (lane == 63) s_wtot[wave] = incl;
-  if (tid == 0) {
-    s_res[0] = 0;
-    s_res[1] = 0;
-    s_res[2] = 0;
-    s_res[3] = 0;
-  }
+  if (tid < 5) s_res[tid] = 0;
   __syncthreads();
   int total_mt = 0;
 #pragma unroll
@@ -843,34 +838,40 @@ __device__ __forceinline__ bool find_tile(const GemmParams& p, int& g_out, int64
   } else {
     return false;
   }
-  const int64_t per = (int64_t)kGroupM * p.NT;
-  const int64_t grp = L / per;
-  const int first = (int)(grp * kGroupM);
-  const int gm = min(total_mt - first, kGroupM);
-  const int rem = (int)(L - grp * per);
-  const int mt = first + rem % gm;
-  nt_out = rem / gm;
-  if (excl <= mt && mt < incl) {
+  // Tile order: group by group (a group's r row tiles give r NT consecutive tiles, so group g
+  // starts at tile excl_g NT); a group's row tiles are cut into ceil(r / kGroupM) balanced
+  // chunks, and a chunk's tiles run column by column, its row tiles innermost.  Neighbouring
+  // tiles then share one group's weight rows, and no chunk mixes two groups.
+  const int u = (int)(L / p.NT);  // a row-tile index inside the group that holds tile L
+  if (excl <= u && u < incl) {
     int run = excl;
     for (int g = g0; g < g0 + gpt && g < p.G; ++g) {
       int64_t rs = rs0, re = re0;
       if (g != g0) group_rows(p.offs, g, p.M, rs, re);
-      const int c = (int)((re - rs + kTile - 1) / kTile);
-      if (mt < run + c) {
+      const int r = (int)((re - rs + kTile - 1) / kTile);
+      if (u < run + r) {
+        const int64_t local = L - (int64_t)run * p.NT;
+        const int c = (r + kGroupM - 1) / kGroupM, sz = r / c, extra = r % c;
+        const int ul = u - run;  // row tile of the chunk's first column
+        const int k = ul < extra * (sz + 1) ? ul / (sz + 1) : extra + (ul - extra * (sz + 1)) / sz;
+        const int start = k * sz + min(k, extra), size = sz + (k < extra ? 1 : 0);
+        const int64_t in_chunk = local - (int64_t)start * p.NT;
         // the owner passes the group's rows on, so no thread reads the offsets again (M < 2^31)
         s_res[0] = g;
-        s_res[1] = mt - run;
+        s_res[1] = start + (int)(in_chunk % size);
         s_res[2] = (int)rs;
         s_res[3] = (int)re;
+        s_res[4] = (int)(in_chunk / size);
         break;
       }
-      run += c;
+      run += r;
     }
   }
   __syncthreads();
   g_out = min(max(s_res[0], 0), p.G - 1);
   m0_out = (int64_t)s_res[2] + (int64_t)s_res[1] * kTile;
   re_out = s_res[3];
+  nt_out = s_res[4];
   return true;
 }
 
@@ -883,7 +884,7 @@ void grouped_gemm_kernel(GemmParams p) {
   const int wave = tid >> 6;
   int g, nt;
   int64_t m0, re;
-  __shared__ int s_find[kThreads / 64 + 4];
+  __shared__ int s_find[kThreads / 64 + 5];
   if (!find_tile<kThreads>(p, g, m0, re, nt, s_find)) return;
 
   // ---- operands
@@ -949,7 +950,7 @@ void grouped_gemm8_kernel(GemmParams p) {
   using E = Elem<T>;
   int g, nt;
   int64_t m0, re;
-  __shared__ int s_find[kThreads8 / 64 + 4];
+  __shared__ int s_find[kThreads8 / 64 + 5];
   if (!find_tile<kThreads8>(p, g, m0, re, nt, s_find)) return;
   const int64_t esz = E::kBytes;
   const char* A = (const char*)p.A;
