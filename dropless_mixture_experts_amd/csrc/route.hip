@@ -8,12 +8,14 @@
 //
 // Three launches, all with shapes fixed on the host:
 //   R1 route_topk_kernel     one workgroup per chunk of 128 tokens.  A group of
-//                            G lanes (G = next power of two >= E, at most 64)
-//                            selects the K largest keys of one token with
-//                            butterfly max-reductions; scores and gates follow.
-//                            The chunk's slots are then ranked stably per
-//                            expert with wave ballots, giving a per-chunk
-//                            histogram and each slot's rank inside its chunk.
+//                            G lanes shares one token, each lane holding up to
+//                            16 of its keys in registers (G = ceil(E/16) rounded
+//                            to a power of two); every one of the K rounds takes
+//                            the lane-local maximum, then a butterfly maximum
+//                            over the group.  Scores and gates follow.  The
+//                            chunk's slots are then ranked stably per expert
+//                            with wave ballots, giving a per-chunk histogram
+//                            and each slot's rank inside its chunk.
 //   R2 route_scan_kernel     one workgroup: per expert, an exclusive scan of
 //                            the chunk histograms; counts and offsets.
 //   R3 route_finalize_kernel slot_pos = offsets[e] + chunk base + rank; row_src.
@@ -24,9 +26,11 @@ namespace moe {
 
 namespace {
 
-constexpr int kTopkThreads = 256;
+constexpr int kTopkThreads = 512;
+constexpr int kTopkWaves = kTopkThreads / 64;
 constexpr int kMaxTopK = 32;
 constexpr int kMaxExperts = 256;
+constexpr int kKeysPerLane = 16;
 
 // rank in the total order of fp32 bit patterns: -inf < ... < -0 < +0 < ... < +inf
 __device__ __forceinline__ uint32_t f32_order(float f) {
@@ -52,36 +56,66 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
-// G lanes per token; each lane holds up to KPL keys (expert e = lane + j*G).
-template <int G>
+// G lanes per token; lane l of a group holds experts l*KPL .. l*KPL + KPL - 1.
+// A key packs the fp32 order of logit(+bias) above the complemented expert
+// index, so one unsigned maximum picks the largest key and, among equal keys,
+// the smallest expert.  A cleared or absent key is 0, below every real key.
+// vec4: the rows may be read as float4 (E % 4 == 0, 16-byte aligned base).
+template <int G, int KPL>
 __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
     const float* __restrict__ logits, const float* __restrict__ bias, int T, int E, int K,
-    int score, int renorm, int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate,
-    int32_t* __restrict__ local_rank, int32_t* __restrict__ hist) {
-  constexpr int KPL = (G == 64) ? (kMaxExperts / 64) : 1;
+    int score, int renorm, int vec4, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_gate, int32_t* __restrict__ local_rank, int32_t* __restrict__ hist) {
   constexpr int TPP = kTopkThreads / G;  // tokens per pass
   __shared__ uint8_t s_sel[kRouteChunk * kMaxTopK];
   __shared__ uint16_t s_rank[kRouteChunk * kMaxTopK];
-  __shared__ int s_cnt[4][kMaxExperts];
+  __shared__ float s_score[kRouteChunk * kMaxTopK];
+  __shared__ float s_bias[kMaxExperts];
+  __shared__ int s_cnt[kTopkWaves][kMaxExperts];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int lig = tid & (G - 1);
+  const int e_lo = lig * KPL;
   const int64_t t0 = (int64_t)blockIdx.x * kRouteChunk;
   const int ntok = (int)min((int64_t)kRouteChunk, (int64_t)T - t0);
+
+  if (bias)
+    for (int e = tid; e < E; e += kTopkThreads) s_bias[e] = bias[e];
+  __syncthreads();
 
   for (int tl = tid / G; tl < ntok; tl += TPP) {
     const int64_t t = t0 + tl;
     const float* row = logits + t * E;
     float kf[KPL];
+    if constexpr (KPL % 4 == 0) {
+      if (vec4) {
+#pragma unroll
+        for (int q = 0; q < KPL / 4; ++q) {
+          const int e = e_lo + 4 * q;
+          float4 v = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+          if (e < E) v = *reinterpret_cast<const float4*>(row + e);
+          kf[4 * q] = v.x;
+          kf[4 * q + 1] = v.y;
+          kf[4 * q + 2] = v.z;
+          kf[4 * q + 3] = v.w;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < KPL; ++j) kf[j] = (e_lo + j < E) ? row[e_lo + j] : -INFINITY;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < KPL; ++j) kf[j] = (e_lo + j < E) ? row[e_lo + j] : -INFINITY;
+    }
     uint64_t comp[KPL];
 #pragma unroll
     for (int j = 0; j < KPL; ++j) {
-      const int e = lig + j * G;
+      const int e = e_lo + j;
       if (e < E) {
-        float v = row[e];
-        if (bias) v = v + bias[e];
+        float v = kf[j];
+        if (bias) v = v + s_bias[e];
         kf[j] = v;
         comp[j] = ((uint64_t)f32_order(v) << 32) | (uint32_t)(0xffffffffu - (uint32_t)e);
       } else {
@@ -89,8 +123,7 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
         comp[j] = 0;
       }
     }
-    float top_key = 0.f, my_key = 0.f;
-    int my_e = 0;
+    float top_key = 0.f, denom = 0.f;
     for (int k = 0; k < K; ++k) {
       uint64_t best = comp[0];
 #pragma unroll
@@ -103,31 +136,30 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
       const int e = (int)(0xffffffffu - (uint32_t)best);
 #pragma unroll
       for (int j = 0; j < KPL; ++j)
-        if (lig + j * G == e) comp[j] = 0;
+        if (e_lo + j == e) comp[j] = 0;
       const float key = order_to_f32((uint32_t)(best >> 32));
       if (k == 0) top_key = key;
-      if (lig == k) {
-        my_e = e;
-        my_key = key;
+      const float s = (score == 1) ? 1.f / (1.f + expf(-key)) : expf(key - top_key);
+      denom += s;
+      // round k is kept by lane k mod G of the group, which also writes it out
+      if (lig == (k & (G - 1))) {
+        s_sel[tl * K + k] = (uint8_t)e;
+        s_score[tl * K + k] = s;
       }
     }
-    float s = 0.f;
-    if (lig < K) s = (score == 1) ? 1.f / (1.f + expf(-my_key)) : expf(my_key - top_key);
-    float denom;
-    if (renorm) {
-      denom = group_sum<G>(s);
-    } else if (score == 0) {
-      float z = 0.f;
+    if (!renorm) {
+      if (score == 0) {
+        float z = 0.f;
 #pragma unroll
-      for (int j = 0; j < KPL; ++j) z += expf(kf[j] - top_key);
-      denom = group_sum<G>(z);
-    } else {
-      denom = 1.f;
+        for (int j = 0; j < KPL; ++j) z += expf(kf[j] - top_key);
+        denom = group_sum<G>(z);
+      } else {
+        denom = 1.f;
+      }
     }
-    if (lig < K) {
-      topk_idx[t * K + lig] = my_e;
-      topk_gate[t * K + lig] = s / denom;
-      s_sel[tl * K + lig] = (uint8_t)my_e;
+    for (int k = lig; k < K; k += G) {
+      topk_idx[t * K + k] = s_sel[tl * K + k];
+      topk_gate[t * K + k] = s_score[tl * K + k] / denom;
     }
   }
 
@@ -135,7 +167,8 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
   for (int e = lane; e < E; e += 64) s_cnt[wave][e] = 0;
   __syncthreads();
   const int n = ntok * K;
-  const int seg = ((n + 255) / 256) * 64;  // slots per wave, a multiple of 64
+  // slots per wave, a multiple of 64
+  const int seg = ((n + 64 * kTopkWaves - 1) / (64 * kTopkWaves)) * 64;
   const int beg = wave * seg;
   const int end = min(n, beg + seg);
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -161,7 +194,7 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
   for (int e = tid; e < E; e += kTopkThreads) {
     int run = 0;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < kTopkWaves; ++w) {
       const int v = s_cnt[w][e];
       s_cnt[w][e] = run;
       run += v;
@@ -175,39 +208,85 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
   }
 }
 
-// One workgroup of 16 waves.  hist[c][e] (chunk counts) becomes the exclusive
-// prefix of expert e's counts over chunks 0..c-1.
-__global__ __launch_bounds__(1024) void route_scan_kernel(int32_t* __restrict__ hist, int nch, int E,
-                                                          int32_t* __restrict__ counts,
-                                                          int32_t* __restrict__ offsets) {
+constexpr int kScanThreads = 1024;
+constexpr int kScanParts = 64;  // at most this many threads share one expert's column
+constexpr int kScanRun = 16;    // chunk counts a thread holds in registers
+
+// One workgroup.  hist[c][e] (chunk counts) becomes the exclusive prefix of
+// expert e's counts over chunks 0..c-1.  Thread (part p, expert e) owns a run
+// of consecutive chunks of column e: it loads them all at once, adds the run
+// totals of parts 0..p-1 from LDS and writes its prefixes back.
+__global__ __launch_bounds__(kScanThreads) void route_scan_kernel(int32_t* __restrict__ hist,
+                                                                  int nch, int E,
+                                                                  int32_t* __restrict__ counts,
+                                                                  int32_t* __restrict__ offsets) {
+  __shared__ int s_part[kScanThreads];
   __shared__ int s_tot[kMaxExperts];
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  for (int e = wave; e < E; e += 16) {
-    int run = 0;
-    for (int c0 = 0; c0 < nch; c0 += 64) {
-      const int c = c0 + lane;
-      const int v = (c < nch) ? hist[(int64_t)c * E + e] : 0;
-      int inc = v;
+  const int tid = threadIdx.x;
+  const int nparts = min(kScanParts, kScanThreads / E);
+  const int e = tid % E;
+  const int part = tid / E;
+  const bool active = part < nparts;
+  const int per = (nch + nparts - 1) / nparts;
+  const int c_beg = active ? part * per : 0;
+  const int c_end = active ? min(nch, c_beg + per) : 0;
+
+  int v[kScanRun];
+  int sum = 0;
 #pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int u = __shfl_up(inc, o, 64);
-        if (lane >= o) inc += u;
-      }
-      if (c < nch) hist[(int64_t)c * E + e] = run + inc - v;
-      run += __shfl(inc, 63, 64);
+  for (int u = 0; u < kScanRun; ++u) {
+    const int c = c_beg + u;
+    v[u] = (c < c_end) ? hist[(int64_t)c * E + e] : 0;
+    sum += v[u];
+  }
+  for (int c0 = c_beg + kScanRun; c0 < c_end; c0 += kScanRun) {
+#pragma unroll
+    for (int u = 0; u < kScanRun; ++u) {
+      const int c = c0 + u;
+      if (c < c_end) sum += hist[(int64_t)c * E + e];
     }
-    if (lane == 0) s_tot[e] = run;
+  }
+  if (active) s_part[part * E + e] = sum;
+  __syncthreads();
+  int run = 0;
+  if (active) {
+    for (int q = 0; q < part; ++q) run += s_part[q * E + e];
+    if (part == nparts - 1) s_tot[e] = run + sum;
+  }
+#pragma unroll
+  for (int u = 0; u < kScanRun; ++u) {
+    const int c = c_beg + u;
+    if (c < c_end) {
+      hist[(int64_t)c * E + e] = run;
+      run += v[u];
+    }
+  }
+  for (int c0 = c_beg + kScanRun; c0 < c_end; c0 += kScanRun) {
+    int w[kScanRun];
+#pragma unroll
+    for (int u = 0; u < kScanRun; ++u) {
+      const int c = c0 + u;
+      w[u] = (c < c_end) ? hist[(int64_t)c * E + e] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < kScanRun; ++u) {
+      const int c = c0 + u;
+      if (c < c_end) {
+        hist[(int64_t)c * E + e] = run;
+        run += w[u];
+      }
+    }
   }
   __syncthreads();
-  if (wave == 0) {
-    int v[4];
+  if (tid < 64) {
+    const int lane = tid;
+    int v4[4];
     int loc = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int e = lane * 4 + j;
-      v[j] = (e < E) ? s_tot[e] : 0;
-      loc += v[j];
+      const int x = lane * 4 + j;
+      v4[j] = (x < E) ? s_tot[x] : 0;
+      loc += v4[j];
     }
     int inc = loc;
 #pragma unroll
@@ -215,15 +294,15 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int32_t* __restrict__ 
       const int u = __shfl_up(inc, o, 64);
       if (lane >= o) inc += u;
     }
-    int run = inc - loc;
+    int r = inc - loc;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int e = lane * 4 + j;
-      if (e < E) {
-        counts[e] = v[j];
-        offsets[e] = run;
+      const int x = lane * 4 + j;
+      if (x < E) {
+        counts[x] = v4[j];
+        offsets[x] = r;
       }
-      run += v[j];
+      r += v4[j];
     }
     if (lane == 63) offsets[E] = inc;
   }
@@ -258,27 +337,31 @@ hipError_t launch_route(const float* logits, const float* bias, int64_t T, int E
   const int nch = (int)((T + kRouteChunk - 1) / kRouteChunk);
   int32_t* hist = (int32_t*)ws;
   if (nch > 0) {
-    int G = 1;
-    while (G < E && G < 64) G <<= 1;
-#define MOE_TOPK_CASE(g)                                                                       \
-  case g:                                                                                      \
-    hipLaunchKernelGGL(route_topk_kernel<g>, dim3(nch), dim3(kTopkThreads), 0, s, logits, bias, \
-                       (int)T, E, K, score, renorm, topk_idx, topk_gate, slot_pos, hist);      \
+    int P = 1;
+    while (P < E) P <<= 1;
+    const int vec4 = (E % 4 == 0) && ((reinterpret_cast<uintptr_t>(logits) & 15) == 0);
+#define MOE_TOPK_CASE(p, g, kpl)                                                                 \
+  case p:                                                                                        \
+    hipLaunchKernelGGL((route_topk_kernel<g, kpl>), dim3(nch), dim3(kTopkThreads), 0, s, logits, \
+                       bias, (int)T, E, K, score, renorm, vec4, topk_idx, topk_gate, slot_pos,   \
+                       hist);                                                                    \
     break;
-    switch (G) {
-      MOE_TOPK_CASE(1)
-      MOE_TOPK_CASE(2)
-      MOE_TOPK_CASE(4)
-      MOE_TOPK_CASE(8)
-      MOE_TOPK_CASE(16)
-      MOE_TOPK_CASE(32)
-      MOE_TOPK_CASE(64)
+    switch (P) {
+      MOE_TOPK_CASE(1, 1, 1)
+      MOE_TOPK_CASE(2, 1, 2)
+      MOE_TOPK_CASE(4, 1, 4)
+      MOE_TOPK_CASE(8, 1, 8)
+      MOE_TOPK_CASE(16, 1, 16)
+      MOE_TOPK_CASE(32, 2, 16)
+      MOE_TOPK_CASE(64, 4, 16)
+      MOE_TOPK_CASE(128, 8, 16)
+      MOE_TOPK_CASE(256, 16, 16)
       default:
         return hipErrorInvalidValue;
     }
 #undef MOE_TOPK_CASE
   }
-  hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, s, hist, nch, E, counts, offsets);
+  hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, hist, nch, E, counts, offsets);
   const int64_t M = T * K;
   if (M > 0) {
     hipLaunchKernelGGL(route_finalize_kernel, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, s,
