@@ -1358,7 +1358,8 @@ struct Out {
     *(uint2*)(wl + r * kRowBytes + chunk * 16 + hi * 8) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
   }
   // local rows 0 .. NR-1 = rows row0 .. row0 + NR - 1 (those below re) of columns col0 ..
-  // col0 + CW - 1 (those below ncols, a multiple of 8) to base + row * ld + col * 2
+  // col0 + CW - 1 (those below ncols, a multiple of 8) to base + row * ld + col * 2; the stores
+  // are non-temporal: the kernel never reads its output back
   template <int NR = 128>
   __device__ static void flush(const char* wl, char* base, int64_t ld, int64_t row0, int64_t re, int64_t col0,
                                int64_t ncols) {
@@ -1371,7 +1372,7 @@ struct Out {
       const int r = it * kRPI + rr;
       const uint4 v = *(const uint4*)(wl + r * kRowBytes + ((c ^ (r % kCPR)) * 16));
       const int64_t row = row0 + r;
-      if (cok && row < re) *(uint4*)(base + row * ld + col * 2) = v;
+      if (cok && row < re) st_nt((uint4*)(base + row * ld + col * 2), v);
     }
   }
 };
