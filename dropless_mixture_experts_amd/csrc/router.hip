@@ -3,10 +3,21 @@
 // The learned router scores every expert for every token (page "Accelerating
 // dropless MoE training in JAX with NVIDIA Transformer Engine", introduction).
 // With E <= 256 this product is a skinny GEMM whose cost is reading x once, so
-// it is shaped for HBM bandwidth: a workgroup owns 32 tokens, its 4 waves split
+// it is shaped for HBM bandwidth.
+//
+// bf16 (router_ring_kernel): a workgroup owns 64 tokens and all experts.  Stages
+// of 64 d-elements of its x rows and of every W row go straight from global
+// memory into an LDS ring with global_load_lds_dwordx4 (whole 128-byte row
+// pieces, no registers spent), as many stages deep as LDS holds, so that enough
+// of x is in flight to cover HBM latency; W (at most 0.5 MB) is re-read from L2
+// once per 64 tokens.  The 4 waves split the experts when there are 128 or more
+// and otherwise also the d axis of each stage, summing their partial tiles
+// through LDS at the end.  32x32x16 MFMA tiles; d past the last whole stage is
+// read as zeros.
+//
+// fp32 (router_logits_kernel): a workgroup owns 32 tokens, its 4 waves split
 // the d axis, and each wave runs 32x32 MFMA tiles (one per 32 experts) fed
-// straight from global memory with several 16-byte loads per lane in flight.
-// The 4 partial tiles are summed through LDS.
+// straight from global memory; the 4 partial tiles are summed through LDS.
 #include "common.h"
 #include "internal.h"
 
@@ -102,6 +113,223 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const char* __restri
   }
 }
 
+namespace rring {
+
+constexpr int kThreads = 256;
+constexpr int kRowBytes = 128;    // bytes of one row in one stage (64 bf16)
+constexpr int kLdsBytes = 160 * 1024;
+
+// 16-byte chunk XOR of a 128-byte LDS row: 16 consecutive rows at one logical
+// chunk land in 16 distinct 16-byte bank groups
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+
+// 16 bytes per lane from a per-lane global address into LDS at M0 + 16 * lane
+__device__ __forceinline__ void dma(const void* gptr, uint32_t lds_byte) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(lds_byte), "v"(gptr) : "memory", "m0");
+}
+
+// wait until at most N of this wave's vector memory operations are outstanding,
+// and for every LDS access
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" :: "n"(N) : "memory");
+}
+template <int NQ, int A>
+__device__ __forceinline__ void wait_ahead(int ahead) {
+  if constexpr (A <= 0) {
+    wait_vm_lgkm0<0>();
+  } else {
+    if (ahead >= A) {
+      wait_vm_lgkm0<A * NQ>();
+      return;
+    }
+    wait_ahead<NQ, A - 1>(ahead);
+  }
+}
+
+__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+__device__ const uint4 kZeroChunk = {0u, 0u, 0u, 0u};  // source of the d tail past the row end
+
+// TT = token tiles of 32 (the workgroup's tokens), NF = expert tiles of 32
+// (E <= 32 NF), D = ring stages.  Waves: NE groups over the expert tiles (NFW
+// each) x NKS over the four 16-element k steps of a stage.
+template <int TT, int NF, int D>
+__global__ __launch_bounds__(kThreads) void router_ring_kernel(const bf16_t* __restrict__ x,
+                                                               const bf16_t* __restrict__ w,
+                                                               int64_t T_, int64_t d, int E,
+                                                               float* __restrict__ logits) {
+  constexpr int EP = NF * 32;
+  constexpr int NE = NF < 4 ? NF : 4;
+  constexpr int NKS = 4 / NE;
+  constexpr int NFW = NF / NE;
+  constexpr int kBT = 32 * TT;
+  constexpr int NQ = TT + NF;  // DMA instructions of a wave per stage: TT of x, NF of W
+  constexpr int kSlotBytes = (kBT + EP) * kRowBytes;
+  static_assert(NE * NKS == 4 && NE * NFW == NF, "wave split");
+  static_assert(D >= 2 && D * kSlotBytes <= kLdsBytes, "ring size");
+  __shared__ uint4 smem[D * kSlotBytes / 16];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int eg = wave % NE, ks = wave / NE;
+  const int64_t t0 = (int64_t)blockIdx.x * kBT;
+  const int64_t dbytes = d * 2;
+  const int nk = (int)((dbytes + kRowBytes - 1) / kRowBytes);
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)smem);
+
+  // this wave's DMA instructions: x rows 8 (TT wave + q) .. +7, W rows 8 (NF wave + q) .. +7;
+  // lane L fills row L / 8, physical chunk L % 8, which holds logical chunk c
+  const char* src[NQ];
+  uint32_t cbyte[NQ];
+  uint32_t ldsoff[NQ];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const bool isx = q < TT;
+    const int row = (isx ? (TT * wave + q) : (NF * wave + (q - TT))) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ swz(row);
+    int64_t grow;
+    if (isx) {
+      grow = t0 + row;
+      grow = grow < T_ ? grow : T_ - 1;
+      src[q] = (const char*)x + grow * dbytes + c * 16;
+    } else {
+      grow = row < E ? row : E - 1;
+      src[q] = (const char*)w + grow * dbytes + c * 16;
+    }
+    cbyte[q] = (uint32_t)(c * 16);
+    ldsoff[q] = (uint32_t)((isx ? 0 : kBT * kRowBytes) + (row & ~7) * kRowBytes);
+  }
+  auto issue = [&](int s) {
+    const uint32_t slot = lds0 + (uint32_t)((s % D) * kSlotBytes);
+    const int64_t kb = (int64_t)s * kRowBytes;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const void* g = (kb + cbyte[q] < dbytes) ? (const void*)(src[q] + kb) : (const void*)&kZeroChunk;
+      dma(g, __builtin_amdgcn_readfirstlane(slot + ldsoff[q]));
+    }
+  };
+
+  // fragment offsets inside a slot: x rows tt * 32 + l32, W rows (eg NFW + f) * 32 + l32
+  uint32_t aoff[TT], boff[NFW];
+  int aswz[TT], bswz[NFW];
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt) {
+    const int r = tt * 32 + l32;
+    aoff[tt] = (uint32_t)(r * kRowBytes);
+    aswz[tt] = swz(r);
+  }
+#pragma unroll
+  for (int f = 0; f < NFW; ++f) {
+    const int r = (eg * NFW + f) * 32 + l32;
+    boff[f] = (uint32_t)(kBT * kRowBytes + r * kRowBytes);
+    bswz[f] = swz(r);
+  }
+
+  f32x16 acc[TT][NFW];
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+    for (int f = 0; f < NFW; ++f)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[tt][f][r] = 0.f;
+
+#pragma unroll
+  for (int s = 0; s < D - 1; ++s)
+    if (s < nk) issue(s);
+  const char* lbase = (const char*)smem;
+  for (int s = 0; s < nk; ++s) {
+    wait_ahead<NQ, D - 2>(min(nk - 1 - s, D - 2));
+    barrier();  // stage s has landed for every wave; slot (s - 1) % D is read by none
+    if (s + D - 1 < nk) issue(s + D - 1);
+    const char* slot = lbase + (s % D) * kSlotBytes;
+#pragma unroll
+    for (int j = 0; j < 4 / NKS; ++j) {
+      const int c = 2 * (ks + j * NKS) + hi;  // logical chunk of this lane's 8 k values
+      uint4 a[TT], b[NFW];
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) a[tt] = *(const uint4*)(slot + aoff[tt] + ((c ^ aswz[tt]) << 4));
+#pragma unroll
+      for (int f = 0; f < NFW; ++f) b[f] = *(const uint4*)(slot + boff[f] + ((c ^ bswz[f]) << 4));
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+        for (int f = 0; f < NFW; ++f)
+          acc[tt][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[tt]),
+                                                              __builtin_bit_cast(bf16x8, b[f]),
+                                                              acc[tt][f], 0, 0, 0);
+    }
+  }
+
+  if constexpr (NKS > 1) {
+    // partial tiles of k groups 1 .. NKS-1 through the (now idle) ring
+    __syncthreads();
+    float* red = (float*)smem;
+    if (ks > 0) {
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+        for (int f = 0; f < NFW; ++f)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            red[((((ks - 1) * NE + eg) * TT + tt) * NFW + f) * 1024 + r * 64 + lane] = acc[tt][f][r];
+    }
+    __syncthreads();
+    if (ks > 0) return;
+#pragma unroll
+    for (int k2 = 1; k2 < NKS; ++k2)
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+        for (int f = 0; f < NFW; ++f)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            acc[tt][f][r] += red[((((k2 - 1) * NE + eg) * TT + tt) * NFW + f) * 1024 + r * 64 + lane];
+  }
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+    for (int f = 0; f < NFW; ++f) {
+      const int e = (eg * NFW + f) * 32 + l32;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t t = t0 + tt * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+        if (t < T_ && e < E) logits[t * E + e] = acc[tt][f][r];
+      }
+    }
+}
+
+}  // namespace rring
+
+// 32-token workgroups when few experts leave fewer than about 1.5 workgroups of
+// 64 tokens per CU, so that every CU streams x; deeper rings where stages are small.
+hipError_t router_ring(const void* x, const void* w, int64_t T_, int64_t d, int E, float* logits,
+                       hipStream_t s) {
+  using namespace rring;
+  const bf16_t* xb = (const bf16_t*)x;
+  const bf16_t* wb = (const bf16_t*)w;
+  const int nf = (E + 31) / 32;
+  const bool small_t = (T_ + 63) / 64 < 384;
+#define MOE_ROUTER_RING(tt, nfe, depth)                                                         \
+  hipLaunchKernelGGL((router_ring_kernel<tt, nfe, depth>), dim3((unsigned)((T_ + 32 * tt - 1) / (32 * tt))), \
+                     dim3(kThreads), 0, s, xb, wb, T_, d, E, logits)
+  if (nf <= 1) {
+    if (small_t) MOE_ROUTER_RING(1, 1, 16);
+    else MOE_ROUTER_RING(2, 1, 8);
+  } else if (nf <= 2) {
+    if (small_t) MOE_ROUTER_RING(1, 2, 13);
+    else MOE_ROUTER_RING(2, 2, 10);
+  } else if (nf <= 4) {
+    MOE_ROUTER_RING(2, 4, 6);
+  } else {
+    MOE_ROUTER_RING(2, 8, 4);
+  }
+#undef MOE_ROUTER_RING
+  return hipGetLastError();
+}
+
 template <typename T>
 hipError_t router_t(const void* x, const void* w, int64_t T_, int64_t d, int E, float* logits,
                     hipStream_t s) {
@@ -125,7 +353,7 @@ hipError_t router_t(const void* x, const void* w, int64_t T_, int64_t d, int E, 
 hipError_t launch_router_logits(const void* x, const void* w, int64_t T, int64_t d, int E, int dtype,
                                 float* logits, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  if (dtype == 1) return router_t<bf16_t>(x, w, T, d, E, logits, s);
+  if (dtype == 1) return router_ring(x, w, T, d, E, logits, s);
   return router_t<float>(x, w, T, d, E, logits, s);
 }
 

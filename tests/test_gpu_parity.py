@@ -138,6 +138,29 @@ def test_router_logits_parity(name, rows):
     assert np.all(err <= 1e-5 * scale + 1e-30), float((err / scale).max())
 
 
+@pytest.mark.parametrize("T,d,E", [
+    (1, 64, 1),         # one token, one expert, one stage
+    (70, 200, 8),       # d not a multiple of the 64-element stage: the tail reads as zeros
+    (3000, 512, 64),    # two expert tiles, 32-token workgroups
+    (30000, 136, 64),   # two expert tiles, 64-token workgroups, d tail
+    (25000, 256, 20),   # one expert tile, 64-token workgroups
+    (130, 2048, 100),   # E not a multiple of 32, four expert tiles
+    (333, 1032, 256),   # eight expert tiles, the largest expert count
+    (97, 8, 3),         # d of one 16-byte chunk
+])
+def test_router_logits_shapes(T, d, E):
+    rng = np.random.default_rng(T + 7 * d + 31 * E)
+    x = mi.f32_to_bf16_bits(rng.standard_normal((T, d)).astype(np.float32))
+    w = mi.f32_to_bf16_bits((rng.standard_normal((E, d)) / np.sqrt(d)).astype(np.float32))
+    out = torch.full((T, E), float("nan"), dtype=torch.float32, device="cuda")
+    moe.moe_router_logits(dev(x), dev(w), out)
+    torch.cuda.synchronize()
+    ref = orc.to_f64(x) @ orc.to_f64(w).T
+    scale = np.abs(orc.to_f64(x)) @ np.abs(orc.to_f64(w)).T
+    err = np.abs(host(out).astype(np.float64) - ref)
+    assert np.all(err <= 1e-5 * scale + 1e-30), float(np.nanmax(err / scale))
+
+
 # ----------------------------------------------------------------- permute / combine
 
 def _routing(T, E, K, seed):
