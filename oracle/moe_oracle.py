@@ -31,7 +31,9 @@ silent this oracle takes the plainest reading the rest supports:
   the first grouped GEMM is gate and up together (W13 = [Wg; Wu], [2F, d]),
   the second is the down projection (W2 [d, F]);
 * the gates are applied in combine: y_t = sum_k g_tk * Y_perm[pos(t, k)];
-* backward holds the routing fixed and yields dX, dW13, dW2 and d_gates.
+* backward holds the routing fixed and yields dX, dW13, dW2 and d_gates;
+  the router backward holds the top-K choice fixed and takes d_gates back
+  through the scores to d_logits, then to dWr and the router's share of dx.
 
 Arithmetic is fp64 from the exact input values with no intermediate rounding;
 the only fp32 step is the key add, because it decides the integer routing and
@@ -87,6 +89,22 @@ class Routing:
     row_src: np.ndarray   # [T*K]  int64 slot held by permuted row r (inverse of slot_pos)
 
 
+def scores(k64: np.ndarray, score: int) -> np.ndarray:
+    """S1b: scores of one token's keys in fp64: a softmax over all E keys, or a sigmoid per key."""
+    if score == SCORE_SOFTMAX:
+        z = np.exp(k64 - k64.max())
+        return z / z.sum()
+    if score == SCORE_SIGMOID:
+        return 1.0 / (1.0 + np.exp(-k64))
+    raise ValueError("score must be softmax (0) or sigmoid (1)")
+
+
+def gates_from_keys(k64: np.ndarray, chosen, score: int, renorm: bool) -> np.ndarray:
+    """S1b-S1c: the chosen experts' scores, divided by their sum when renormalising."""
+    sel = scores(k64, score)[list(chosen)]
+    return sel / sel.sum() if renorm else sel
+
+
 def route(logits: np.ndarray, bias: np.ndarray | None, K: int, score: int = SCORE_SOFTMAX,
           renorm: bool = True) -> Routing:
     logits = np.asarray(logits, dtype=np.float32)
@@ -105,20 +123,8 @@ def route(logits: np.ndarray, bias: np.ndarray | None, K: int, score: int = SCOR
         # S1a: order experts by (key descending, expert ascending); keep the first K
         order = sorted(range(E), key=lambda e: (-_fp32_order(row[e]), e))
         chosen = order[:K]
-        # S1b: scores in fp64 over all experts
-        k64 = row.astype(np.float64)
-        if score == SCORE_SOFTMAX:
-            z = np.exp(k64 - k64.max())
-            s = z / z.sum()
-        elif score == SCORE_SIGMOID:
-            s = 1.0 / (1.0 + np.exp(-k64))
-        else:
-            raise ValueError("score must be softmax (0) or sigmoid (1)")
-        # S1c: renormalise over the chosen experts
-        sel = s[chosen]
-        g = sel / sel.sum() if renorm else sel
         idx[t] = chosen
-        gates[t] = g
+        gates[t] = gates_from_keys(row.astype(np.float64), chosen, score, renorm)
 
     # S2: per-expert histogram and its exclusive prefix sum
     M = T * K
@@ -282,6 +288,53 @@ def backward(dy, fwd: dict, w13, w2, K) -> dict:
     dx = combine(dx_perm, r.slot_pos, None, T, K)
     return {"dy_perm": dy_perm, "d_gates": d_gates, "dh": dh, "d_pre": d_pre, "dw2": dw2,
             "dx_perm": dx_perm, "dw13": dw13, "dx": dx}
+
+
+# ----------------------------------------------------------------------------
+# Router backward.  The router is learned (TE-MoE introduction), so training
+# needs the gradient of the loss with respect to its weights and inputs.  The
+# top-K choice is a discrete decision and is held fixed; the gradient flows
+# through the scores and their renormalisation (S1b-S1c), then through the
+# router product (S0).  A bias is a constant offset of the keys: d key = d logit.
+
+def route_backward(keys: np.ndarray, idx: np.ndarray, d_gates: np.ndarray, score: int = SCORE_SOFTMAX,
+                   renorm: bool = True) -> np.ndarray:
+    """d_logits[t, e] = sum_k d_gates[t, k] * d gate[t, k] / d key[t, e], fp64 [T, E].
+
+    The chain rule step by step for each token: first back through the
+    renormalisation g_k = s_k / S (S = sum of the chosen scores), giving d s for
+    the chosen experts (0 for the rest), then back through the score function:
+    the softmax Jacobian ds/dkey = diag(s) - s s^T, or s (1 - s) for a sigmoid."""
+    keys = np.asarray(keys, np.float64)
+    T, E = keys.shape
+    K = idx.shape[1]
+    d_gates = np.asarray(d_gates, np.float64).reshape(T, K)
+    out = np.zeros((T, E), np.float64)
+    for t in range(T):
+        chosen = [int(e) for e in idx[t]]
+        s = scores(keys[t], score)
+        dg = d_gates[t]
+        ds = np.zeros(E, np.float64)
+        if renorm:
+            S = s[chosen].sum()
+            g = s[chosen] / S
+            # d g_k / d s_j = (delta_kj - g_k) / S over the chosen j
+            for j in range(K):
+                ds[chosen[j]] += sum(dg[k] * ((1.0 if k == j else 0.0) - g[k]) / S for k in range(K))
+        else:
+            for k in range(K):
+                ds[chosen[k]] += dg[k]
+        if score == SCORE_SOFTMAX:
+            out[t] = s * ds - s * np.dot(s, ds)
+        else:
+            out[t] = ds * s * (1.0 - s)
+    return out
+
+
+def router_backward(d_logits: np.ndarray, x: np.ndarray, w_router: np.ndarray):
+    """Backward of logits = x . Wr^T: dWr = d_logits^T . x  [E, d], dx = d_logits . Wr  [T, d]; fp64."""
+    dl = np.asarray(d_logits, np.float64)
+    return dl.T @ to_f64(x), dl @ to_f64(w_router)
 
 
 # ----------------------------------------------------------------------------

@@ -343,6 +343,127 @@ def test_backward_matches_central_differences():
     np.testing.assert_allclose(bwd["d_gates"], dg, rtol=1e-6, atol=1e-8)
 
 
+def _top_k(keys_row, K):
+    return [int(e) for e in sorted(range(len(keys_row)), key=lambda e: (-keys_row[e], e))[:K]]
+
+
+@pytest.mark.parametrize("score", [orc.SCORE_SOFTMAX, orc.SCORE_SIGMOID])
+@pytest.mark.parametrize("renorm", [True, False])
+def test_route_backward_matches_central_differences(score, renorm):
+    """d_logits against central differences of the forward's own gate function, the choice held fixed."""
+    T, E, K = 5, 7, 3
+    rng = np.random.default_rng(40 + 2 * score + renorm)
+    keys = rng.standard_normal((T, E)) * 1.5
+    idx = np.array([_top_k(keys[t], K) for t in range(T)], np.int32)
+    dg = rng.standard_normal((T, K))
+    got = orc.route_backward(keys, idx, dg, score, renorm)
+    eps = 1e-6
+    fd = np.zeros((T, E))
+    for t in range(T):
+        for e in range(E):
+            kp, km = keys[t].copy(), keys[t].copy()
+            kp[e] += eps
+            km[e] -= eps
+            lp = np.dot(dg[t], orc.gates_from_keys(kp, idx[t], score, renorm))
+            lm = np.dot(dg[t], orc.gates_from_keys(km, idx[t], score, renorm))
+            fd[t, e] = (lp - lm) / (2 * eps)
+    np.testing.assert_allclose(got, fd, rtol=1e-6, atol=1e-9)
+
+
+def test_route_backward_closed_forms_and_invariants():
+    T, E, K = 9, 6, 2
+    rng = np.random.default_rng(44)
+    keys = rng.standard_normal((T, E))
+    idx = np.array([_top_k(keys[t], K) for t in range(T)], np.int32)
+    dg = rng.standard_normal((T, K))
+    unchosen = np.ones((T, E), bool)
+    for t in range(T):
+        unchosen[t, idx[t]] = False
+    # softmax, renormalised: the gates are a softmax over the chosen keys, so
+    # d key_k = g_k (dg_k - sum_j g_j dg_j) on the chosen experts and 0 elsewhere
+    d = orc.route_backward(keys, idx, dg, orc.SCORE_SOFTMAX, True)
+    for t in range(T):
+        g = softmax(keys[t, idx[t]])
+        np.testing.assert_allclose(d[t, idx[t]], g * (dg[t] - np.dot(g, dg[t])), rtol=1e-12, atol=1e-14)
+    assert np.all(np.abs(d[unchosen]) < 1e-15)   # s_e * (0 - sum_j s_j ds_j), a sum that is 0 exactly
+    # any softmax: adding one constant to every key changes no gate, so each row sums to 0
+    for renorm in (True, False):
+        d = orc.route_backward(keys, idx, dg, orc.SCORE_SOFTMAX, renorm)
+        np.testing.assert_allclose(d.sum(axis=1), 0, atol=1e-13)
+    # softmax without renormalisation: every expert gets a gradient
+    d = orc.route_backward(keys, idx, dg, orc.SCORE_SOFTMAX, False)
+    assert np.all(d[unchosen] != 0)
+    # sigmoid without renormalisation: d key = dg sigma (1 - sigma) on the chosen experts
+    d = orc.route_backward(keys, idx, dg, orc.SCORE_SIGMOID, False)
+    for t in range(T):
+        sg = expit(keys[t, idx[t]])
+        np.testing.assert_allclose(d[t, idx[t]], dg[t] * sg * (1 - sg), rtol=1e-12)
+    assert np.all(d[unchosen] == 0)
+    # sigmoid, renormalised: scaling every chosen score by one factor leaves the gates alone,
+    # so sum_k d key_k / (1 - sigma_k) = 0; unchosen experts get 0
+    d = orc.route_backward(keys, idx, dg, orc.SCORE_SIGMOID, True)
+    for t in range(T):
+        sg = expit(keys[t, idx[t]])
+        assert abs(np.sum(d[t, idx[t]] / (1 - sg))) < 1e-12
+    assert np.all(d[unchosen] == 0)
+    # K = 1 with renormalisation: the gate is exactly 1, so nothing flows back
+    idx1 = np.array([_top_k(keys[t], 1) for t in range(T)], np.int32)
+    for score in (orc.SCORE_SOFTMAX, orc.SCORE_SIGMOID):
+        assert np.all(orc.route_backward(keys, idx1, dg[:, :1], score, True) == 0)
+
+
+def test_router_backward_adjoint_identity_and_basis_rows():
+    """<d_logits, x Wr^T> = <dWr, Wr> = <dx, x>: the backward is the adjoint of the product."""
+    T, d, E = 11, 9, 4
+    rng = np.random.default_rng(46)
+    x = rng.standard_normal((T, d))
+    w = rng.standard_normal((E, d))
+    dl = rng.standard_normal((T, E))
+    dw, dx = orc.router_backward(dl, x, w)
+    assert dw.shape == (E, d) and dx.shape == (T, d)
+    ref = np.sum(dl * (x @ w.T))
+    np.testing.assert_allclose(np.sum(dw * w), ref, rtol=1e-12)
+    np.testing.assert_allclose(np.sum(dx * x), ref, rtol=1e-12)
+    # x = unit row j: dWr[:, j] is that token's d_logits; Wr = unit row: dx gets d_logits column e
+    xb = np.zeros((1, d))
+    xb[0, 3] = 1.0
+    dw1, _ = orc.router_backward(dl[:1], xb, w)
+    np.testing.assert_array_equal(dw1[:, 3], dl[0])
+    assert np.all(np.delete(dw1, 3, axis=1) == 0)
+    wb = np.zeros((E, d))
+    wb[2, 5] = 1.0
+    _, dx1 = orc.router_backward(dl, x, wb)
+    np.testing.assert_array_equal(dx1[:, 5], dl[:, 2])
+
+
+def test_router_chain_matches_central_differences():
+    """d gates -> d logits -> (dWr, dx) against differences of the fp64 router and gates."""
+    T, d, E, K = 4, 6, 5, 2
+    rng = np.random.default_rng(48)
+    x = rng.standard_normal((T, d))
+    w = rng.standard_normal((E, d)) / math.sqrt(d)
+    idx = np.array([_top_k(x[t] @ w.T, K) for t in range(T)], np.int32)
+    dg = rng.standard_normal((T, K))
+    for score, renorm in ((orc.SCORE_SOFTMAX, True), (orc.SCORE_SIGMOID, False)):
+        def loss():
+            keys = x @ w.T
+            return sum(np.dot(dg[t], orc.gates_from_keys(keys[t], idx[t], score, renorm)) for t in range(T))
+        dl = orc.route_backward(x @ w.T, idx, dg, score, renorm)
+        dw, dx = orc.router_backward(dl, x, w)
+        eps = 1e-6
+        for arr, got in ((w, dw), (x, dx)):
+            fd = np.zeros_like(arr)
+            for i in np.ndindex(arr.shape):
+                old = arr[i]
+                arr[i] = old + eps
+                lp = loss()
+                arr[i] = old - eps
+                lm = loss()
+                arr[i] = old
+                fd[i] = (lp - lm) / (2 * eps)
+            np.testing.assert_allclose(got, fd, rtol=1e-6, atol=1e-9)
+
+
 def test_backward_empty_expert_gets_zero_weight_gradient():
     T, d, E, K, F = 12, 4, 4, 2, 3
     rng = np.random.default_rng(22)
