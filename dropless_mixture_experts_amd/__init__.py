@@ -36,6 +36,9 @@ SIGNATURES = {
     "moe_grouped_gemm_workspace_size": (_I32, [_c.POINTER(_SZ)]),
     "moe_unpermute_combine": (_I32, [_P, _P, _P, _I64, _I64, _I32, _I32, _P, _P]),
     "moe_grouped_gemm_wgrad": (_I32, [_P, _P, _P, _I64, _I64, _I64, _I32, _I32, _I32, _P, _P]),
+    "moe_route_backward": (_I32, [_P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _P, _P]),
+    "moe_router_backward_workspace_size": (_I32, [_I64, _I64, _I32, _I32, _c.POINTER(_SZ)]),
+    "moe_router_logits_backward": (_I32, [_P, _P, _P, _I64, _I64, _I32, _I32, _P, _P, _I32, _P, _SZ, _P]),
 }
 
 _lib = None
@@ -169,3 +172,27 @@ def moe_grouped_gemm_wgrad(X, dY, group_offsets, dW, accumulate: bool = False, s
 
 
 from .layer import MoEBuffers, layer_backward, layer_forward  # noqa: E402,F401
+
+
+def moe_route_backward(logits, bias, topk_idx, d_gates, score: int, renorm: bool, d_logits, stream=None) -> None:
+    """d_logits[T, E] (fp32) = d_gates back through the gates of moe_route, top-K choice held fixed."""
+    T, E = logits.shape
+    K = topk_idx.shape[1]
+    _call("moe_route_backward", _ptr(logits), _ptr(bias), _ptr(topk_idx), _ptr(d_gates), T, E, K, score,
+          int(bool(renorm)), _ptr(d_logits), _stream(stream))
+
+
+def moe_router_backward_workspace_size(T: int, d: int, E: int, dtype: int) -> int:
+    n = ctypes.c_size_t(0)
+    _call("moe_router_backward_workspace_size", T, d, E, dtype, ctypes.byref(n))
+    return int(n.value)
+
+
+def moe_router_logits_backward(d_logits, x, w_router, d_w_router, dx, ws, accumulate: bool = False,
+                               stream=None) -> None:
+    """d_w_router[E, d] (fp32) = d_logits^T x and/or dx[T, d] (+)= d_logits w_router."""
+    T, d = x.shape
+    E = w_router.shape[0]
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _call("moe_router_logits_backward", _ptr(d_logits), _ptr(x), _ptr(w_router), T, d, E, dtype_code(x),
+          _ptr(d_w_router), _ptr(dx), int(bool(accumulate)), _ptr(ws), ws_bytes, _stream(stream))

@@ -38,4 +38,15 @@ hipError_t launch_grouped_wgrad(const void* X, const void* dY, const int32_t* of
                                 int64_t N, int64_t Kd, int G, int dtype, int accumulate, float* dW,
                                 hipStream_t s);
 
+hipError_t launch_route_backward(const float* logits, const float* bias, const int32_t* idx,
+                                 const float* d_gates, int64_t T, int E, int K, int score, int renorm,
+                                 float* d_logits, hipStream_t s);
+
+// bytes of the moe_router_logits_backward workspace (0 for fp32 inputs)
+size_t router_backward_workspace_bytes(int64_t T, int64_t d, int E, int dtype);
+
+hipError_t launch_router_logits_backward(const float* d_logits, const void* x, const void* w, int64_t T,
+                                         int64_t d, int E, int dtype, float* d_w, void* dx, int accumulate,
+                                         void* ws, hipStream_t s);
+
 }  // namespace moe

@@ -134,4 +134,45 @@ int32_t moe_grouped_gemm_wgrad(const void* X, const void* dY, const int32_t* gro
                                             (hipStream_t)stream));
 }
 
+int32_t moe_route_backward(const float* logits, const float* bias, const int32_t* topk_idx,
+                           const float* d_gates, int64_t T, int32_t E, int32_t K, int32_t score,
+                           int32_t renorm, float* d_logits, moe_stream_t stream) {
+  if (T < 0 || E < 1 || E > MOE_MAX_EXPERTS || K < 1 || K > E || K > MOE_MAX_TOPK) return MOE_INVALID_ARG;
+  if (score != MOE_SCORE_SOFTMAX && score != MOE_SCORE_SIGMOID) return MOE_UNSUPPORTED;
+  if (T * (int64_t)K >= ((int64_t)1 << 31)) return MOE_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!logits || !topk_idx || !d_gates || !d_logits) return MOE_INVALID_ARG;
+  if (!aligned4(logits) || !aligned4(topk_idx) || !aligned4(d_gates) || !aligned4(d_logits) ||
+      (bias && !aligned4(bias)))
+    return MOE_INVALID_ARG;
+  return from_hip(moe::launch_route_backward(logits, bias, topk_idx, d_gates, T, E, K, score, renorm != 0,
+                                             d_logits, (hipStream_t)stream));
+}
+
+int32_t moe_router_backward_workspace_size(int64_t T, int64_t d, int32_t E, int32_t dtype, size_t* bytes) {
+  if (!bytes || T < 0 || T >= ((int64_t)1 << 31) || d < 8 || d % 8 != 0 || E < 1 || E > MOE_MAX_EXPERTS)
+    return MOE_INVALID_ARG;
+  if (!dtype_ok(dtype)) return MOE_UNSUPPORTED;
+  *bytes = moe::router_backward_workspace_bytes(T, d, E, dtype);
+  return MOE_OK;
+}
+
+int32_t moe_router_logits_backward(const float* d_logits, const void* x, const void* w_router, int64_t T,
+                                   int64_t d, int32_t E, int32_t dtype, float* d_w_router, void* dx,
+                                   int32_t accumulate, void* workspace, size_t workspace_bytes,
+                                   moe_stream_t stream) {
+  if (T < 0 || T >= ((int64_t)1 << 31) || d < 8 || d % 8 != 0 || E < 1 || E > MOE_MAX_EXPERTS)
+    return MOE_INVALID_ARG;
+  if (!dtype_ok(dtype)) return MOE_UNSUPPORTED;
+  if (!d_w_router && !dx) return MOE_OK;
+  if (d_w_router && (!aligned16(d_w_router) || (T > 0 && (!d_logits || !x)))) return MOE_INVALID_ARG;
+  if (dx && T > 0 && (!d_logits || !w_router || !aligned16(dx))) return MOE_INVALID_ARG;
+  if ((x && !aligned16(x)) || (w_router && !aligned16(w_router)) || (d_logits && !aligned4(d_logits)))
+    return MOE_INVALID_ARG;
+  const size_t need = moe::router_backward_workspace_bytes(T, d, E, dtype);
+  if (workspace_bytes < need || (need > 0 && (!workspace || !aligned16(workspace)))) return MOE_INVALID_ARG;
+  return from_hip(moe::launch_router_logits_backward(d_logits, x, w_router, T, d, E, dtype, d_w_router, dx,
+                                                     accumulate != 0, workspace, (hipStream_t)stream));
+}
+
 }  // extern "C"

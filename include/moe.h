@@ -55,7 +55,7 @@ enum moe_score { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 };
 enum moe_layout { MOE_LAYOUT_NK = 0, MOE_LAYOUT_KN = 1 };
 enum moe_epilogue { MOE_EPI_NONE = 0, MOE_EPI_SWIGLU = 1, MOE_EPI_DSWIGLU = 2 };
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 #define MOE_MAX_EXPERTS 256
 #define MOE_MAX_TOPK 32
 #define MOE_MAX_GROUPS 1024
@@ -192,6 +192,52 @@ int32_t moe_unpermute_combine(const void* y_perm, const int32_t* slot_pos, const
 int32_t moe_grouped_gemm_wgrad(const void* X, const void* dY, const int32_t* group_offsets,
                                int64_t M, int64_t N, int64_t Kd, int32_t G, int32_t dtype,
                                int32_t accumulate, float* dW, moe_stream_t stream);
+
+/*
+ * Router backward through the routing scores (the router is learned: TE-MoE
+ * introduction).  The top-K choice is held fixed; with key = logit (+ bias),
+ *   d_logits[t, e] = sum_k d_gates[t, k] * d topk_gate[t, k] / d key[t, e]
+ * for the gates of moe_route (same score and renorm): back through
+ * g_k = s_k / S (S = sum of the chosen scores) when renorm != 0, then through
+ * the softmax over all E keys (every expert gets a gradient when renorm == 0)
+ * or the sigmoid (only the chosen experts do).  Scores are recomputed from the
+ * logits in fp32.  The bias is a constant: d bias is not formed (it would be
+ * the column sum of d_logits).
+ *   logits   DEVICE [T, E] fp32;  bias DEVICE [E] fp32 or NULL
+ *   topk_idx DEVICE [T, K] int32 (as written by moe_route);  d_gates DEVICE [T, K] fp32
+ *   d_logits DEVICE [T, E] fp32 (written, every element)
+ * Requires 1 <= K <= E <= MOE_MAX_EXPERTS, K <= MOE_MAX_TOPK, T*K < 2^31.
+ */
+int32_t moe_route_backward(const float* logits, const float* bias, const int32_t* topk_idx,
+                           const float* d_gates, int64_t T, int32_t E, int32_t K, int32_t score,
+                           int32_t renorm, float* d_logits, moe_stream_t stream);
+
+/*
+ * Bytes of the moe_router_logits_backward workspace for these sizes (0 for fp32).
+ * MOE_INVALID_ARG / MOE_UNSUPPORTED as moe_router_logits_backward would return.
+ */
+int32_t moe_router_backward_workspace_size(int64_t T, int64_t d, int32_t E, int32_t dtype, size_t* bytes);
+
+/*
+ * Backward of the router product logits = x . w_router^T (S0):
+ *   d_w_router[e, :] = sum_t d_logits[t, e] * x[t, :]          (when d_w_router != NULL)
+ *   dx[t, :] = sum_e d_logits[t, e] * w_router[e, :]            (dx != NULL, accumulate == 0)
+ *   dx[t, :] = dx[t, :] + sum_e d_logits[t, e] * w_router[e, :] (accumulate != 0: adds the
+ *              router's share to the expert path's dX, rounding once)
+ * bf16: d_logits enters the MFMA products as two bf16 parts (high + low, about
+ * 16 significant bits); accumulation is fp32.  d_w_router is summed over runs
+ * of tokens in a fixed order: deterministic.
+ *   d_logits   DEVICE [T, E] fp32;  x DEVICE [T, d] dtype;  w_router DEVICE [E, d] dtype
+ *   d_w_router DEVICE [E, d] fp32 or NULL (T == 0 writes zeros);  dx DEVICE [T, d] dtype or NULL
+ *   workspace  DEVICE, moe_router_backward_workspace_size bytes, 16-byte aligned, caller-owned;
+ *              calls that overlap in time need separate workspaces
+ * Requires 0 <= T < 2^31, d >= 8, d % 8 == 0, 1 <= E <= MOE_MAX_EXPERTS.  fp32 inputs
+ * take plain per-element kernels meant for small shapes.
+ */
+int32_t moe_router_logits_backward(const float* d_logits, const void* x, const void* w_router, int64_t T,
+                                   int64_t d, int32_t E, int32_t dtype, float* d_w_router, void* dx,
+                                   int32_t accumulate, void* workspace, size_t workspace_bytes,
+                                   moe_stream_t stream);
 
 #ifdef __cplusplus
 }

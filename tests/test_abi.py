@@ -28,6 +28,7 @@ def test_header_declares_the_boundary():
     names = _declared()
     for n in ["moe_route", "moe_permute", "moe_grouped_gemm", "moe_unpermute_combine",
               "moe_grouped_gemm_wgrad", "moe_router_logits", "moe_route_workspace_size",
+              "moe_route_backward", "moe_router_logits_backward", "moe_router_backward_workspace_size",
               "moe_status_str", "moe_abi_version"]:
         assert n in names
 
@@ -42,7 +43,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert moe.moe_abi_version() == 2
+    assert moe.moe_abi_version() == 3
     assert moe.status_str(0) == "ok"
     assert "invalid" in moe.status_str(1)
     assert moe.status_str(99) == "unknown status"
@@ -119,3 +120,28 @@ def test_wgrad_permute_combine_reject_bad_arguments(lib):
     assert lib.moe_router_logits(P, P, 10, 20, 8, 1, P, None) == 1
     assert lib.moe_router_logits(P, P, 10, 16, 8, 3, P, None) == 2
     assert lib.moe_router_logits(None, None, 0, 16, 8, 1, None, None) == 0
+
+
+def test_router_backward_rejects_bad_arguments(lib):
+    # moe_route_backward(logits, bias, idx, d_gates, T, E, K, score, renorm, d_logits, stream)
+    assert lib.moe_route_backward(P, None, P, P, 10, 8, 9, 0, 1, P, None) == 1      # K > E
+    assert lib.moe_route_backward(P, None, P, P, 10, 257, 2, 0, 1, P, None) == 1    # E limit
+    assert lib.moe_route_backward(P, None, P, P, 10, 8, 2, 2, 1, P, None) == 2      # unknown score
+    assert lib.moe_route_backward(P, None, None, P, 10, 8, 2, 0, 1, P, None) == 1   # no top-K indices
+    assert lib.moe_route_backward(P + 2, None, P, P, 10, 8, 2, 0, 1, P, None) == 1  # misaligned
+    assert lib.moe_route_backward(None, None, None, None, 0, 8, 2, 0, 1, None, None) == 0  # empty
+    n = ctypes.c_size_t(0)
+    assert lib.moe_router_backward_workspace_size(100, 20, 8, 1, ctypes.byref(n)) == 1   # d % 8
+    assert lib.moe_router_backward_workspace_size(100, 64, 8, 4, ctypes.byref(n)) == 2
+    assert lib.moe_router_backward_workspace_size(100, 64, 8, 0, ctypes.byref(n)) == 0 and n.value == 0
+    assert lib.moe_router_backward_workspace_size(0, 64, 8, 1, ctypes.byref(n)) == 0   # no tokens
+    assert lib.moe_router_backward_workspace_size(1, 8, 1, 1, ctypes.byref(n)) == 0 and n.value > 0
+    assert lib.moe_router_backward_workspace_size(100, 64, 8, 1, ctypes.byref(n)) == 0 and n.value > 0
+    need = n.value
+    # moe_router_logits_backward(dl, x, w, T, d, E, dtype, dw, dx, acc, ws, ws_bytes, stream)
+    assert lib.moe_router_logits_backward(P, P, P, 100, 64, 8, 1, P, P, 0, P, need - 1, None) == 1  # small ws
+    assert lib.moe_router_logits_backward(P, P, P, 100, 64, 8, 1, P, P, 0, P + 8, need, None) == 1  # misaligned
+    assert lib.moe_router_logits_backward(P, None, P, 100, 64, 8, 1, P, None, 0, P, need, None) == 1  # dWr needs x
+    assert lib.moe_router_logits_backward(P, P, None, 100, 64, 8, 1, None, P, 0, P, need, None) == 1  # dx needs Wr
+    assert lib.moe_router_logits_backward(P, P, P, 100, 64, 8, 3, P, P, 0, P, need, None) == 2
+    assert lib.moe_router_logits_backward(P, P, P, 100, 64, 8, 1, None, None, 0, None, 0, None) == 0  # no output

@@ -161,6 +161,157 @@ def test_router_logits_shapes(T, d, E):
     assert np.all(err <= 1e-5 * scale + 1e-30), float(np.nanmax(err / scale))
 
 
+# ----------------------------------------------------------------- router backward
+
+def _route_bwd_case(T, E, K, score, renorm, seed, bias=None):
+    rng = np.random.default_rng(seed)
+    logits = (1.5 * rng.standard_normal((T, E))).astype(np.float32)
+    r = orc.route(logits, bias, K, score, renorm)
+    dg = rng.standard_normal((T, K)).astype(np.float32)
+    out = torch.full((T, E), float("nan"), dtype=torch.float32, device="cuda")
+    moe.moe_route_backward(dev(logits), dev(bias) if bias is not None else None,
+                           dev(r.idx.astype(np.int32)), dev(dg), score, renorm, out)
+    torch.cuda.synchronize()
+    ref = orc.route_backward(r.keys, r.idx, dg, score, renorm)
+    got = host(out).astype(np.float64)
+    # fp32 scores against fp64: a few ulp of the largest term of each row
+    tol = 2e-6 * np.maximum(1.0, np.abs(dg).max(axis=1, keepdims=True)) + 1e-5 * np.abs(ref)
+    assert np.all(np.abs(got - ref) <= tol), float(np.abs(got - ref).max())
+    return r, got
+
+
+@pytest.mark.parametrize("T,E,K,score,renorm", [
+    (300, 8, 2, 0, True),      # Mixtral-shaped routing
+    (257, 128, 8, 0, True),    # fine-grained
+    (200, 32, 8, 1, True),     # sigmoid scores, renormalised (DeepSeek-V3 style)
+    (200, 32, 8, 1, False),    # sigmoid, not renormalised
+    (257, 8, 2, 0, False),     # softmax without renormalisation: every expert gets a gradient
+    (100, 256, 32, 0, True),   # largest E and K
+    (129, 100, 7, 0, False),   # E not a power of two, above 64
+    (130, 5, 5, 0, True),      # K = E
+    (64, 1, 1, 0, True),       # one expert: the gate is 1, no gradient
+])
+def test_route_backward_parity(T, E, K, score, renorm):
+    r, got = _route_bwd_case(T, E, K, score, renorm, seed=T + 3 * E + K)
+    if renorm:  # unchosen experts get exactly nothing
+        mask = np.ones((T, E), bool)
+        for t in range(T):
+            mask[t, r.idx[t]] = False
+        assert np.all(got[mask] == 0)
+
+
+def test_route_backward_with_bias_and_masked_expert():
+    E = 16
+    bias = np.linspace(-0.5, 0.5, E).astype(np.float32)
+    bias[3] = -np.inf
+    for score in (0, 1):
+        _route_bwd_case(333, E, 4, score, True, seed=77 + score, bias=bias)
+        _route_bwd_case(333, E, 4, score, False, seed=79 + score, bias=bias)
+
+
+def _router_bwd_gpu(dl, x, w, accumulate=False, dx0=None, want_dw=True, want_dx=True):
+    T, d = x.shape
+    E = w.shape[0]
+    xd, wd = dev(x), dev(w)
+    dw = torch.full((E, d), float("nan"), dtype=torch.float32, device="cuda") if want_dw else None
+    dx = None
+    if want_dx:
+        dx = dev(dx0) if dx0 is not None else torch.full((T, d), float("nan"), dtype=xd.dtype, device="cuda")
+    nb = moe.moe_router_backward_workspace_size(T, d, E, moe.dtype_code(xd))
+    ws = torch.empty((max(nb, 1),), dtype=torch.uint8, device="cuda")
+    moe.moe_router_logits_backward(dev(dl), xd, wd, dw, dx, ws, accumulate)
+    torch.cuda.synchronize()
+    return (host(dw) if want_dw else None), (dx if want_dx else None)
+
+
+def _check_router_bwd(T, d, E, seed, accumulate=False, fp32=False):
+    rng = np.random.default_rng(seed)
+    xf = rng.standard_normal((T, d)).astype(np.float32)
+    wf = (rng.standard_normal((E, d)) / np.sqrt(d)).astype(np.float32)
+    x = xf if fp32 else mi.f32_to_bf16_bits(xf)
+    w = wf if fp32 else mi.f32_to_bf16_bits(wf)
+    dl = (rng.standard_normal((T, E)) * 0.3).astype(np.float32)
+    dx0 = None
+    if accumulate:
+        dx0f = rng.standard_normal((T, d)).astype(np.float32)
+        dx0 = dx0f if fp32 else mi.f32_to_bf16_bits(dx0f)
+    dw, dx = _router_bwd_gpu(dl, x, w, accumulate, dx0)
+    ref_dw, ref_dx = orc.router_backward(dl, x, w)
+    # dWr: fp32 sums of products of the (high + low) bf16 parts, about 2^-16 relative each
+    scale = np.abs(dl).T.astype(np.float64) @ np.abs(orc.to_f64(x))
+    err = np.abs(dw.astype(np.float64) - ref_dw)
+    assert np.all(err <= 5e-5 * scale + 1e-30), float((err / np.maximum(scale, 1e-30)).max())
+    # dx: same products, then (old +) one rounding to the output type
+    if accumulate:
+        ref_dx = ref_dx + orc.to_f64(dx0)
+    got = orc.to_f64(host(dx))
+    sx = np.abs(dl).astype(np.float64) @ np.abs(orc.to_f64(w))
+    out_ulp = 2.0 ** -24 if fp32 else 2.0 ** -8
+    err = np.abs(got - ref_dx)
+    assert np.all(err <= out_ulp * np.abs(ref_dx) + 5e-5 * sx + 1e-30), float(err.max())
+
+
+@pytest.mark.parametrize("T,d,E", [
+    (1, 64, 1),          # one token, one expert
+    (70, 200, 8),        # column block past d, two runs of tokens with a ragged last stage
+    (3000, 512, 64),     # two expert tiles, eleven runs of tokens
+    (257, 2048, 128),    # four expert tiles (the fine-grained router)
+    (333, 1032, 256),    # eight expert tiles
+    (97, 8, 3),          # d of one 16-byte chunk, E not a multiple of 8
+    (20000, 512, 32),    # 157 runs of tokens summed in order
+    (150, 256, 80),      # 80 experts: launched as four tiles of 32
+])
+def test_router_logits_backward_parity(T, d, E):
+    _check_router_bwd(T, d, E, seed=T + d + E)
+
+
+def test_router_logits_backward_accumulates_into_dx():
+    _check_router_bwd(515, 1024, 20, seed=9, accumulate=True)
+
+
+def test_router_logits_backward_fp32():
+    _check_router_bwd(256, 128, 8, seed=10, fp32=False)
+    _check_router_bwd(256, 128, 8, seed=11, fp32=True)
+    _check_router_bwd(100, 64, 5, seed=12, fp32=True, accumulate=True)
+
+
+def test_router_logits_backward_no_tokens_zeroes_dw():
+    E, d = 8, 64
+    dw = torch.full((E, d), float("nan"), dtype=torch.float32, device="cuda")
+    x = torch.empty((0, d), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((E, d), dtype=torch.bfloat16, device="cuda")
+    nb = moe.moe_router_backward_workspace_size(0, d, E, moe.MOE_BF16)
+    ws = torch.empty((max(nb, 1),), dtype=torch.uint8, device="cuda")
+    moe.moe_router_logits_backward(torch.empty((0, E), device="cuda"), x, w, dw, None, ws)
+    torch.cuda.synchronize()
+    assert torch.all(dw == 0)
+
+
+def test_router_backward_chain_mixtral_full_size():
+    """d_gates -> d_logits -> (dWr, dx) at the Mixtral-shaped sizes (T = 8192, d = 4096, E = 8)."""
+    cfg = mi.CONFIGS["mixtral"]
+    inp = mi.make(cfg, weights=False)
+    x, w = inp["x"], inp["w_router"]
+    logits = orc.router_logits(x, w)
+    r = orc.route(logits, None, cfg.K, cfg.score, cfg.renorm)
+    rng = np.random.default_rng(123)
+    dg = rng.standard_normal((cfg.T, cfg.K)).astype(np.float32)
+    dl_dev = torch.empty((cfg.T, cfg.E), dtype=torch.float32, device="cuda")
+    moe.moe_route_backward(dev(logits), None, dev(r.idx.astype(np.int32)), dev(dg), cfg.score, cfg.renorm, dl_dev)
+    torch.cuda.synchronize()
+    ref_dl = orc.route_backward(r.keys, r.idx, dg, cfg.score, cfg.renorm)
+    dl = host(dl_dev)
+    assert np.all(np.abs(dl - ref_dl) <= 2e-6 * np.maximum(1, np.abs(dg).max(axis=1, keepdims=True)) + 1e-5 * np.abs(ref_dl))
+    dw, dx = _router_bwd_gpu(dl, x, w)
+    ref_dw, ref_dx = orc.router_backward(dl, x, w)
+    scale = np.abs(dl).T.astype(np.float64) @ np.abs(orc.to_f64(x))
+    assert np.all(np.abs(dw - ref_dw) <= 5e-5 * scale + 1e-30)
+    rows = rng.choice(cfg.T, 64, replace=False)
+    got = orc.to_f64(host(dx[torch.as_tensor(rows, device="cuda")]))
+    sx = np.abs(dl[rows]).astype(np.float64) @ np.abs(orc.to_f64(w))
+    assert np.all(np.abs(got - ref_dx[rows]) <= 2.0 ** -8 * np.abs(ref_dx[rows]) + 5e-5 * sx)
+
+
 # ----------------------------------------------------------------- permute / combine
 
 def _routing(T, E, K, seed):
