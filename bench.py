@@ -317,7 +317,8 @@ def main():
 def bench_backward(args, torch, moe, mi):
     """Backward of the Mixtral-shaped layer with one expert taking half of the slots and two none:
     combine backward, SwiGLU-backward dgrad, down wgrad, gate/up dgrad, gate/up wgrad,
-    permute backward (routing held fixed)."""
+    permute backward, then the router's backward (d_gates -> d_logits -> dWr, and its share of
+    dX); routing held fixed."""
     import oracle as orc
     cfg = mi.CONFIGS["mixtral_bwd_skew"]
     torch.cuda.set_device(0)
@@ -331,7 +332,10 @@ def bench_backward(args, torch, moe, mi):
                       bufs, logits=to_dev(logits, torch))
     stream = torch.cuda.current_stream()
     b = bufs
-    names = ["combine_bwd", "dgrad_down_dswiglu", "wgrad_down", "dgrad_gate_up", "wgrad_gate_up", "permute_bwd"]
+    names = ["combine_bwd", "dgrad_down_dswiglu", "wgrad_down", "dgrad_gate_up", "wgrad_gate_up", "permute_bwd",
+             "route_bwd", "router_bwd"]
+    nk = len(names)
+    logits_dev = to_dev(logits, torch)
 
     def step(ev=None):
         def mark(i):
@@ -353,19 +357,24 @@ def bench_backward(args, torch, moe, mi):
         mark(5)
         moe.moe_unpermute_combine(b.dx_perm, b.slot_pos, None, cfg.T, cfg.K, b.dx)
         mark(6)
+        moe.moe_route_backward(logits_dev, None, b.topk_idx, b.d_gates, cfg.score, cfg.renorm, b.d_logits)
+        mark(7)
+        moe.moe_router_logits_backward(b.d_logits, dev["x"], dev["w_router"], b.dw_router, b.dx, b.rb_ws,
+                                       accumulate=True)
+        mark(8)
 
     for _ in range(args.warmup):
         step()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(evs[i])
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / max(args.steps, 1)
-    per = np.zeros(6)
+    per = np.zeros(nk)
     for ev in evs:
-        per += np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(6)])
+        per += np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(nk)])
     per /= max(args.steps, 1)
     kms = dict(zip(names, per.tolist()))
     M = cfg.T * cfg.K
@@ -380,7 +389,11 @@ def bench_backward(args, torch, moe, mi):
                       "ffn": cfg.F, "hot_expert_slots": int(bufs.counts.max().item()),
                       "empty_experts": int((bufs.counts == 0).sum().item())},
            "gemm_tflops": tf, "gemm_total_tflops": total_fl / (sum(kms[k] for k in fl) * 1e-3) / 1e12,
-           "kernels_ms": kms}
+           "kernels_ms": kms,
+           # router backward bytes: the d_logits pass (logits read, d_logits written: 8 T E) and the
+           # product's x read for dWr plus dX read and written for its share (3 T d b)
+           "router_bwd_gbs": {"route_bwd": 8.0 * cfg.T * cfg.E / (kms["route_bwd"] * 1e-3) / 1e9,
+                              "router_bwd": 3.0 * cfg.T * cfg.d * 2 / (kms["router_bwd"] * 1e-3) / 1e9}}
     print(json.dumps(out), flush=True)
 
 

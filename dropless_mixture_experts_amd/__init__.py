@@ -171,7 +171,6 @@ def moe_grouped_gemm_wgrad(X, dY, group_offsets, dW, accumulate: bool = False, s
           int(bool(accumulate)), _ptr(dW), _stream(stream))
 
 
-from .layer import MoEBuffers, layer_backward, layer_forward  # noqa: E402,F401
 
 
 def moe_route_backward(logits, bias, topk_idx, d_gates, score: int, renorm: bool, d_logits, stream=None) -> None:
@@ -196,3 +195,6 @@ def moe_router_logits_backward(d_logits, x, w_router, d_w_router, dx, ws, accumu
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _call("moe_router_logits_backward", _ptr(d_logits), _ptr(x), _ptr(w_router), T, d, E, dtype_code(x),
           _ptr(d_w_router), _ptr(dx), int(bool(accumulate)), _ptr(ws), ws_bytes, _stream(stream))
+
+
+from .layer import MoEBuffers, layer_backward, layer_forward  # noqa: E402,F401

@@ -10,6 +10,7 @@ Backward (routing held fixed):
     moe_permute (gate-scaled dY + d_gates) -> moe_grouped_gemm (KN, SwiGLU backward)
       -> moe_grouped_gemm_wgrad (dW2) -> moe_grouped_gemm (KN, dX_perm)
       -> moe_grouped_gemm_wgrad (dW13) -> moe_unpermute_combine (unit weights, dX)
+      [-> moe_route_backward (d_logits) -> moe_router_logits_backward (dWr, dX += router share)]
 
 torch provides device memory and the stream; every arithmetic step runs in
 libmoe.so.  Buffers are allocated once per shape and reused, so a forward can
@@ -20,8 +21,10 @@ from __future__ import annotations
 import torch
 
 from . import (MOE_EPI_DSWIGLU, MOE_EPI_NONE, MOE_EPI_SWIGLU, MOE_LAYOUT_KN, MOE_LAYOUT_NK,
-               moe_grouped_gemm, moe_grouped_gemm_wgrad, moe_grouped_gemm_workspace_size, moe_permute,
-               moe_route, moe_route_workspace_size, moe_router_logits, moe_unpermute_combine)
+               dtype_code, moe_grouped_gemm, moe_grouped_gemm_wgrad, moe_grouped_gemm_workspace_size,
+               moe_permute, moe_route, moe_route_backward, moe_route_workspace_size,
+               moe_router_backward_workspace_size, moe_router_logits, moe_router_logits_backward,
+               moe_unpermute_combine)
 
 
 class MoEBuffers:
@@ -59,6 +62,11 @@ class MoEBuffers:
             self.dx = torch.empty((T, d), **act)
             self.dw13 = torch.empty((E, 2 * F, d), **f32)
             self.dw2 = torch.empty((E, d, F), **f32)
+            self.d_logits = torch.empty((T, E), **f32)
+            self.dw_router = torch.empty((E, d), **f32)
+            code = dtype_code(torch.empty(0, dtype=dtype))
+            self.rb_ws = torch.empty((max(moe_router_backward_workspace_size(T, d, E, code), 256),),
+                                     dtype=torch.uint8, device=dev)
 
 
 def layer_forward(x, w_router, bias, w13, w2, K: int, score: int, renorm: bool, bufs: MoEBuffers,
@@ -81,10 +89,12 @@ def layer_forward(x, w_router, bias, w13, w2, K: int, score: int, renorm: bool, 
     return b.y
 
 
-def layer_backward(dy, w13, w2, K: int, bufs: MoEBuffers, stream=None):
+def layer_backward(dy, w13, w2, K: int, bufs: MoEBuffers, stream=None, router=None):
     """Gradients of <dY, Y> with the routing of the last forward held fixed.
 
-    Returns (dx, dw13, dw2, d_gates) in bufs."""
+    Returns (dx, dw13, dw2, d_gates) in bufs.  With ``router`` = dict(logits, x, w_router,
+    bias, score, renorm) of that forward, also takes d_gates back through the gates (top-K
+    held fixed) to bufs.d_logits and bufs.dw_router, and adds the router's share to dx."""
     b = bufs
     moe_permute(dy, K, b.slot_pos, b.dy_perm, row_scale=b.gates, y_perm_dot=b.y_perm, dgate_out=b.d_gates,
                 stream=stream)
@@ -95,4 +105,9 @@ def layer_backward(dy, w13, w2, K: int, bufs: MoEBuffers, stream=None):
                      stream=stream)
     moe_grouped_gemm_wgrad(b.x_perm, b.d_pre, b.offsets, b.dw13, stream=stream)
     moe_unpermute_combine(b.dx_perm, b.slot_pos, None, b.T, K, b.dx, stream=stream)
+    if router is not None:
+        moe_route_backward(router["logits"], router.get("bias"), b.topk_idx, b.d_gates, router["score"],
+                           router["renorm"], b.d_logits, stream=stream)
+        moe_router_logits_backward(b.d_logits, router["x"], router["w_router"], b.dw_router, b.dx, b.rb_ws,
+                                   accumulate=True, stream=stream)
     return b.dx, b.dw13, b.dw2, b.d_gates
