@@ -396,7 +396,15 @@ __global__ __launch_bounds__(256) void router_dwr_reduce_kernel(const float* __r
   if (i >= n4) return;
   const f32x4* p4 = (const f32x4*)part;
   f32x4 s = p4[i];
-  for (int p = 1; p < P; ++p) s += p4[(int64_t)p * n4 + i];
+  int p = 1;
+  for (; p + 8 <= P; p += 8) {  // eight loads in flight, added in order
+    f32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = p4[(int64_t)(p + u) * n4 + i];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += v[u];
+  }
+  for (; p < P; ++p) s += p4[(int64_t)p * n4 + i];
   ((f32x4*)dw)[i] = s;
 }
 
@@ -412,7 +420,7 @@ __global__ __launch_bounds__(256) void router_dx_kernel(const uint16_t* __restri
                                                         const uint16_t* __restrict__ dl_lo,
                                                         const uint16_t* __restrict__ wt, int64_t T, int64_t d,
                                                         int E16, int accumulate, uint16_t* __restrict__ dx) {
-  __shared__ uint4 smem[4 * 32 * 512 / 16];  // 4 waves x [32][128] fp32
+  __shared__ uint4 smem[4 * 32 * 256 / 16];  // 4 waves x [32][64] fp32
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
@@ -422,55 +430,74 @@ __global__ __launch_bounds__(256) void router_dx_kernel(const uint16_t* __restri
   const int64_t c0 = ((int64_t)blockIdx.x % ncb) * 256 + wj * 128;
   int64_t tr = t0 + l32;
   tr = tr < T ? tr : T - 1;
+  const uint16_t* ah_p = dl_hi + tr * E16 + hi * 8;
+  const uint16_t* al_p = dl_lo + tr * E16 + hi * 8;
+  const uint16_t* b_p[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    int64_t col = c0 + j * 32 + l32;
+    col = col < d ? col : d - 1;
+    b_p[j] = wt + col * E16 + hi * 8;
+  }
   f32x16 acc[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
+#pragma unroll 2
   for (int k0 = 0; k0 < E16; k0 += 16) {
-    const uint4 bh = *(const uint4*)(dl_hi + tr * E16 + k0 + hi * 8);
-    const uint4 bl = *(const uint4*)(dl_lo + tr * E16 + k0 + hi * 8);
+    const uint4 bh = *(const uint4*)(ah_p + k0);
+    const uint4 bl = *(const uint4*)(al_p + k0);
+    uint4 a[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) a[j] = *(const uint4*)(b_p[j] + k0);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      int64_t col = c0 + j * 32 + l32;
-      col = col < d ? col : d - 1;
-      const uint4 a = *(const uint4*)(wt + col * E16 + k0 + hi * 8);
-      acc[j] = mfma_bf16(a, bh, acc[j]);
-      acc[j] = mfma_bf16(a, bl, acc[j]);
+      acc[j] = mfma_bf16(a[j], bh, acc[j]);
+      acc[j] = mfma_bf16(a[j], bl, acc[j]);
     }
   }
-  // lane: token l32, columns j 32 + 8 (r >> 2) + 4 hi + 0..3 in register group r >> 2; they go
-  // to the wave's region as fp32 [32 tokens][128 columns], 16-byte chunks XORed with the token
-  char* wl = (char*)smem + wave * (32 * 512);
+  // two rounds of 64 columns: lane (token l32) writes 4 consecutive fp32 columns per register
+  // group to the wave's [32][64] region (16-byte chunks XORed with the token), then 32 rows x
+  // 8 groups of 8 columns leave as bf16, the old values added first when accumulating
+  char* wl = (char*)smem + wave * (32 * 256);
+  const int c = lane & 7;
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+  for (int half = 0; half < 2; ++half) {
+    const int64_t col = c0 + half * 64 + c * 8;
+    uint4 old[4];
+    if (accumulate) {
 #pragma unroll
-    for (int rg = 0; rg < 4; ++rg) {
-      const int ch = (j * 8 + 2 * rg + hi) ^ l32;
-      *(f32x4*)(wl + l32 * 512 + ch * 16) =
-          f32x4{acc[j][4 * rg], acc[j][4 * rg + 1], acc[j][4 * rg + 2], acc[j][4 * rg + 3]};
+      for (int it = 0; it < 4; ++it) {
+        const int64_t t = t0 + it * 8 + (lane >> 3);
+        old[it] = (t < T && col < d) ? *(const uint4*)(dx + t * d + col) : make_uint4(0u, 0u, 0u, 0u);
+      }
     }
-  __builtin_amdgcn_wave_barrier();  // the wave's staging is written before it is read back
-  // 32 rows x 16 groups of 8 columns; lane: group lane & 15, rows 4 it + lane / 16.  One
-  // rounding to bf16, after the old value is added when accumulating.
+    if (half) __builtin_amdgcn_wave_barrier();  // the first round's reads are done
 #pragma unroll
-  for (int it = 0; it < 8; ++it) {
-    const int r = it * 4 + (lane >> 4);
-    const int c = lane & 15;
-    const int64_t t = t0 + r;
-    const int64_t col = c0 + c * 8;
-    const f32x4 v0 = *(const f32x4*)(wl + r * 512 + (((2 * c) ^ r) * 16));
-    const f32x4 v1 = *(const f32x4*)(wl + r * 512 + (((2 * c + 1) ^ r) * 16));
-    float a[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-    if (t < T && col < d) {
-      uint4* dst = (uint4*)(dx + t * d + col);
+    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int j = half * 2 + jj;
+        const int ch = (jj * 8 + 2 * rg + hi) ^ (l32 & 15);
+        *(f32x4*)(wl + l32 * 256 + ch * 16) =
+            f32x4{acc[j][4 * rg], acc[j][4 * rg + 1], acc[j][4 * rg + 2], acc[j][4 * rg + 3]};
+      }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int r = it * 8 + (lane >> 3);
+      const int64_t t = t0 + r;
+      const f32x4 v0 = *(const f32x4*)(wl + r * 256 + (((2 * c) ^ (r & 15)) * 16));
+      const f32x4 v1 = *(const f32x4*)(wl + r * 256 + (((2 * c + 1) ^ (r & 15)) * 16));
+      float a[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
       if (accumulate) {
         float b[8];
-        Elem<bf16_t>::to_f32(*dst, b);
+        Elem<bf16_t>::to_f32(old[it], b);
 #pragma unroll
         for (int u = 0; u < 8; ++u) a[u] += b[u];
       }
-      *dst = Elem<bf16_t>::from_f32(a);
+      if (t < T && col < d) *(uint4*)(dx + t * d + col) = Elem<bf16_t>::from_f32(a);
     }
   }
 }
