@@ -36,6 +36,9 @@ SIGNATURES = {
     "moe_grouped_gemm_workspace_size": (_I32, [_c.POINTER(_SZ)]),
     "moe_unpermute_combine": (_I32, [_P, _P, _P, _I64, _I64, _I32, _I32, _P, _P]),
     "moe_grouped_gemm_wgrad": (_I32, [_P, _P, _P, _I64, _I64, _I64, _I32, _I32, _I32, _P, _P]),
+    "moe_router_route_workspace_size": (_I32, [_I64, _I32, _c.POINTER(_SZ)]),
+    "moe_router_route": (_I32, [_P, _P, _P, _I64, _I64, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P,
+                                _P, _SZ, _P]),
     "moe_route_backward": (_I32, [_P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _P, _P]),
     "moe_router_backward_workspace_size": (_I32, [_I64, _I64, _I32, _I32, _c.POINTER(_SZ)]),
     "moe_router_logits_backward": (_I32, [_P, _P, _P, _I64, _I64, _I32, _I32, _P, _P, _I32, _P, _SZ, _P]),
@@ -195,6 +198,23 @@ def moe_router_logits_backward(d_logits, x, w_router, d_w_router, dx, ws, accumu
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _call("moe_router_logits_backward", _ptr(d_logits), _ptr(x), _ptr(w_router), T, d, E, dtype_code(x),
           _ptr(d_w_router), _ptr(dx), int(bool(accumulate)), _ptr(ws), ws_bytes, _stream(stream))
+
+
+def moe_router_route_workspace_size(T: int, E: int) -> int:
+    n = ctypes.c_size_t(0)
+    _call("moe_router_route_workspace_size", T, E, ctypes.byref(n))
+    return int(n.value)
+
+
+def moe_router_route(x, w_router, bias, K: int, score: int, renorm: bool, logits, topk_idx, topk_gate, counts,
+                     offsets, slot_pos, row_src, ws, stream=None) -> None:
+    """Fused router product + routing (bf16): the results of moe_router_logits then moe_route."""
+    T, d = x.shape
+    E = w_router.shape[0]
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _call("moe_router_route", _ptr(x), _ptr(w_router), _ptr(bias), T, d, E, K, dtype_code(x), score,
+          int(bool(renorm)), _ptr(logits), _ptr(topk_idx), _ptr(topk_gate), _ptr(counts), _ptr(offsets),
+          _ptr(slot_pos), _ptr(row_src), _ptr(ws), ws_bytes, _stream(stream))
 
 
 from .layer import MoEBuffers, layer_backward, layer_forward  # noqa: E402,F401

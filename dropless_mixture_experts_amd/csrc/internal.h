@@ -14,10 +14,23 @@ size_t route_workspace_bytes(int64_t T, int E);
 hipError_t launch_router_logits(const void* x, const void* w, int64_t T, int64_t d, int E, int dtype,
                                 float* logits, hipStream_t s);
 
+// fused S0-S3 (bf16): the router product with top-K routing, histogram and positions
+size_t router_route_workspace_bytes(int64_t T, int E);
+hipError_t launch_router_route(const void* x, const void* w, const float* bias, int64_t T, int64_t d, int E, int K,
+                               int score, int renorm, float* logits, int32_t* topk_idx, float* topk_gate,
+                               int32_t* counts, int32_t* offsets, int32_t* slot_pos, int32_t* row_src, void* ws,
+                               hipStream_t s);
+
 hipError_t launch_route(const float* logits, const float* bias, int64_t T, int E, int K, int score,
                         int renorm, int32_t* topk_idx, float* topk_gate, int32_t* counts,
                         int32_t* offsets, int32_t* slot_pos, int32_t* row_src, void* ws,
                         hipStream_t s);
+
+// the histogram scan and slot positions of routing, over nch chunks of `chunk` tokens whose
+// per-chunk expert counts are in hist [nch][E] and in-chunk ranks in slot_pos
+hipError_t launch_route_scan_finalize(int32_t* hist, int nch, int chunk, int64_t T, int E, int K,
+                                      const int32_t* topk_idx, int32_t* counts, int32_t* offsets,
+                                      int32_t* slot_pos, int32_t* row_src, hipStream_t s);
 
 hipError_t launch_permute(const void* x, int64_t T, int64_t d, int K, int dtype, const int32_t* slot_pos,
                           const float* row_scale, const void* y_perm_dot, float* dgate_out,

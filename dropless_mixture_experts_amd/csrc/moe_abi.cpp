@@ -175,4 +175,30 @@ int32_t moe_router_logits_backward(const float* d_logits, const void* x, const v
                                                      accumulate != 0, workspace, (hipStream_t)stream));
 }
 
+int32_t moe_router_route_workspace_size(int64_t T, int32_t E, size_t* bytes) {
+  if (!bytes || T < 0 || E < 1 || E > MOE_MAX_EXPERTS) return MOE_INVALID_ARG;
+  *bytes = moe::router_route_workspace_bytes(T, E);
+  return MOE_OK;
+}
+
+int32_t moe_router_route(const void* x, const void* w_router, const float* bias, int64_t T, int64_t d, int32_t E,
+                         int32_t K, int32_t dtype, int32_t score, int32_t renorm, float* logits, int32_t* topk_idx,
+                         float* topk_gate, int32_t* counts, int32_t* offsets, int32_t* slot_pos, int32_t* row_src,
+                         void* ws, size_t ws_bytes, moe_stream_t stream) {
+  if (T < 0 || d < 8 || d % 8 != 0 || E < 1 || E > MOE_MAX_EXPERTS || K < 1 || K > E || K > MOE_MAX_TOPK)
+    return MOE_INVALID_ARG;
+  if (dtype != MOE_BF16) return MOE_UNSUPPORTED;
+  if (score != MOE_SCORE_SOFTMAX && score != MOE_SCORE_SIGMOID) return MOE_UNSUPPORTED;
+  if (T * (int64_t)K >= ((int64_t)1 << 31)) return MOE_INVALID_ARG;
+  if (!counts || !offsets) return MOE_INVALID_ARG;
+  if (T > 0 && (!x || !w_router || !topk_idx || !topk_gate || !slot_pos || !row_src)) return MOE_INVALID_ARG;
+  if ((x && !aligned16(x)) || (w_router && !aligned16(w_router)) || (logits && !aligned4(logits)) ||
+      (bias && !aligned4(bias)))
+    return MOE_INVALID_ARG;
+  const size_t need = moe::router_route_workspace_bytes(T, E);
+  if (ws_bytes < need || (need > 0 && !ws)) return MOE_INVALID_ARG;
+  return from_hip(moe::launch_router_route(x, w_router, bias, T, d, E, K, score, renorm != 0, logits, topk_idx,
+                                           topk_gate, counts, offsets, slot_pos, row_src, ws, (hipStream_t)stream));
+}
+
 }  // extern "C"

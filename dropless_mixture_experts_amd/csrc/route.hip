@@ -21,45 +21,18 @@
 //   R3 route_finalize_kernel slot_pos = offsets[e] + chunk base + rank; row_src.
 #include "common.h"
 #include "internal.h"
+#include "route_device.h"
 
 namespace moe {
 
 namespace {
 
+using namespace rdev;
+
 constexpr int kTopkThreads = 512;
 constexpr int kTopkWaves = kTopkThreads / 64;
-constexpr int kMaxTopK = 32;
-constexpr int kMaxExperts = 256;
-constexpr int kKeysPerLane = 16;
-
-// rank in the total order of fp32 bit patterns: -inf < ... < -0 < +0 < ... < +inf
-__device__ __forceinline__ uint32_t f32_order(float f) {
-  uint32_t u = __float_as_uint(f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-__device__ __forceinline__ float order_to_f32(uint32_t o) {
-  uint32_t u = (o & 0x80000000u) ? (o & 0x7fffffffu) : ~o;
-  return __uint_as_float(u);
-}
-
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
-  uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
-  lo = __shfl_xor(lo, m, 64);
-  hi = __shfl_xor(hi, m, 64);
-  return ((uint64_t)hi << 32) | lo;
-}
-
-template <int G>
-__device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-  for (int o = 1; o < G; o <<= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
 
 // G lanes per token; lane l of a group holds experts l*KPL .. l*KPL + KPL - 1.
-// A key packs the fp32 order of logit(+bias) above the complemented expert
-// index, so one unsigned maximum picks the largest key and, among equal keys,
-// the smallest expert.  A cleared or absent key is 0, below every real key.
 // vec4: the rows may be read as float4 (E % 4 == 0, 16-byte aligned base).
 template <int G, int KPL>
 __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
@@ -74,8 +47,6 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
   __shared__ int s_cnt[kTopkWaves][kMaxExperts];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
   const int lig = tid & (G - 1);
   const int e_lo = lig * KPL;
   const int64_t t0 = (int64_t)blockIdx.x * kRouteChunk;
@@ -109,103 +80,15 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
 #pragma unroll
       for (int j = 0; j < KPL; ++j) kf[j] = (e_lo + j < E) ? row[e_lo + j] : -INFINITY;
     }
-    uint64_t comp[KPL];
-#pragma unroll
-    for (int j = 0; j < KPL; ++j) {
-      const int e = e_lo + j;
-      if (e < E) {
-        float v = kf[j];
-        if (bias) v = v + s_bias[e];
-        kf[j] = v;
-        comp[j] = ((uint64_t)f32_order(v) << 32) | (uint32_t)(0xffffffffu - (uint32_t)e);
-      } else {
-        kf[j] = -INFINITY;
-        comp[j] = 0;
-      }
-    }
-    float top_key = 0.f, denom = 0.f;
-    for (int k = 0; k < K; ++k) {
-      uint64_t best = comp[0];
-#pragma unroll
-      for (int j = 1; j < KPL; ++j) best = comp[j] > best ? comp[j] : best;
-#pragma unroll
-      for (int o = 1; o < G; o <<= 1) {
-        const uint64_t other = shfl_xor_u64(best, o);
-        best = other > best ? other : best;
-      }
-      const int e = (int)(0xffffffffu - (uint32_t)best);
+    if (bias) {
 #pragma unroll
       for (int j = 0; j < KPL; ++j)
-        if (e_lo + j == e) comp[j] = 0;
-      const float key = order_to_f32((uint32_t)(best >> 32));
-      if (k == 0) top_key = key;
-      const float s = (score == 1) ? 1.f / (1.f + expf(-key)) : expf(key - top_key);
-      denom += s;
-      // round k is kept by lane k mod G of the group, which also writes it out
-      if (lig == (k & (G - 1))) {
-        s_sel[tl * K + k] = (uint8_t)e;
-        s_score[tl * K + k] = s;
-      }
+        if (e_lo + j < E) kf[j] = kf[j] + s_bias[e_lo + j];
     }
-    if (!renorm) {
-      if (score == 0) {
-        float z = 0.f;
-#pragma unroll
-        for (int j = 0; j < KPL; ++j) z += expf(kf[j] - top_key);
-        denom = group_sum<G>(z);
-      } else {
-        denom = 1.f;
-      }
-    }
-    for (int k = lig; k < K; k += G) {
-      topk_idx[t * K + k] = s_sel[tl * K + k];
-      topk_gate[t * K + k] = s_score[tl * K + k] / denom;
-    }
-  }
-
-  // ---- stable per-expert ranks of the chunk's slots (slot order = t*K + k)
-  for (int e = lane; e < E; e += 64) s_cnt[wave][e] = 0;
-  __syncthreads();
-  const int n = ntok * K;
-  // slots per wave, a multiple of 64
-  const int seg = ((n + 64 * kTopkWaves - 1) / (64 * kTopkWaves)) * 64;
-  const int beg = wave * seg;
-  const int end = min(n, beg + seg);
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int b = beg; b < end; b += 64) {
-    const int s = b + lane;
-    const bool valid = s < end;
-    const int e = valid ? (int)s_sel[s] : 0;
-    uint64_t eq = __ballot(valid);
-#pragma unroll
-    for (int bit = 0; bit < 8; ++bit) {
-      const uint64_t m = __ballot(valid && ((e >> bit) & 1));
-      eq &= ((e >> bit) & 1) ? m : ~m;
-    }
-    int c = 0;
-    if (valid) {
-      c = s_cnt[wave][e];
-      s_rank[s] = (uint16_t)(c + __popcll(eq & lt_mask));
-    }
-    // the highest lane of each equal-expert set advances that expert's counter
-    if (valid && (eq >> lane) == 1ull) s_cnt[wave][e] = c + __popcll(eq);
+    select_token<G, KPL>(kf, e_lo, E, K, score, renorm, lig, t, tl, s_sel, s_score, topk_idx, topk_gate);
   }
   __syncthreads();
-  for (int e = tid; e < E; e += kTopkThreads) {
-    int run = 0;
-#pragma unroll
-    for (int w = 0; w < kTopkWaves; ++w) {
-      const int v = s_cnt[w][e];
-      s_cnt[w][e] = run;
-      run += v;
-    }
-    hist[(int64_t)blockIdx.x * E + e] = run;
-  }
-  __syncthreads();
-  for (int s = tid; s < n; s += kTopkThreads) {
-    const int w = s / seg;
-    local_rank[t0 * K + s] = s_cnt[w][s_sel[s]] + s_rank[s];
-  }
+  rank_chunk<kTopkWaves>(ntok * K, E, s_sel, s_rank, s_cnt, hist + (int64_t)blockIdx.x * E, local_rank + t0 * K);
 }
 
 constexpr int kScanThreads = 1024;
@@ -308,15 +191,16 @@ __global__ __launch_bounds__(kScanThreads) void route_scan_kernel(int32_t* __res
   }
 }
 
+// chunk = tokens per histogram chunk
 __global__ __launch_bounds__(256) void route_finalize_kernel(const int32_t* __restrict__ topk_idx,
                                                              const int32_t* __restrict__ hist,
                                                              const int32_t* __restrict__ offsets,
-                                                             int64_t M, int K, int E,
+                                                             int64_t M, int K, int E, int chunk,
                                                              int32_t* __restrict__ slot_pos,
                                                              int32_t* __restrict__ row_src) {
   const int64_t s = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (s >= M) return;
-  const int64_t c = (s / K) / kRouteChunk;
+  const int64_t c = (s / K) / chunk;
   const int e = topk_idx[s];
   const int pos = offsets[e] + hist[c * E + e] + slot_pos[s];
   slot_pos[s] = pos;
@@ -361,11 +245,18 @@ hipError_t launch_route(const float* logits, const float* bias, int64_t T, int E
     }
 #undef MOE_TOPK_CASE
   }
+  return launch_route_scan_finalize(hist, nch, kRouteChunk, T, E, K, topk_idx, counts, offsets, slot_pos, row_src,
+                                    s);
+}
+
+hipError_t launch_route_scan_finalize(int32_t* hist, int nch, int chunk, int64_t T, int E, int K,
+                                      const int32_t* topk_idx, int32_t* counts, int32_t* offsets,
+                                      int32_t* slot_pos, int32_t* row_src, hipStream_t s) {
   hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, hist, nch, E, counts, offsets);
   const int64_t M = T * K;
   if (M > 0) {
     hipLaunchKernelGGL(route_finalize_kernel, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, s,
-                       topk_idx, hist, offsets, M, K, E, slot_pos, row_src);
+                       topk_idx, hist, offsets, M, K, E, chunk, slot_pos, row_src);
   }
   return hipGetLastError();
 }

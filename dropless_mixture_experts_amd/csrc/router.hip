@@ -20,6 +20,7 @@
 // straight from global memory; the 4 partial tiles are summed through LDS.
 #include "common.h"
 #include "internal.h"
+#include "route_device.h"
 
 namespace moe {
 
@@ -155,11 +156,21 @@ __device__ const uint4 kZeroChunk = {0u, 0u, 0u, 0u};  // source of the d tail p
 // TT = token tiles of 32 (the workgroup's tokens), NF = expert tiles of 32
 // (E <= 32 NF), D = ring stages.  Waves: NE groups over the expert tiles (NFW
 // each) x NKS over the four 16-element k steps of a stage.
-template <int TT, int NF, int D>
+// FUSE: after the product, the tile's logits stay in LDS and the same workgroup routes its
+// tokens there (top-K, scores, gates, the tile's expert histogram and in-tile ranks; G lanes
+// of KPL keys per token), so that the logits need not return from HBM (they are still written
+// when `logits` is given).
+template <int TT, int NF, int D, bool FUSE = false, int G = 1, int KPL = 1>
 __global__ __launch_bounds__(kThreads) void router_ring_kernel(const bf16_t* __restrict__ x,
                                                                const bf16_t* __restrict__ w,
                                                                int64_t T_, int64_t d, int E,
-                                                               float* __restrict__ logits) {
+                                                               float* __restrict__ logits,
+                                                               const float* __restrict__ bias = nullptr,
+                                                               int K = 0, int score = 0, int renorm = 0,
+                                                               int32_t* __restrict__ topk_idx = nullptr,
+                                                               float* __restrict__ topk_gate = nullptr,
+                                                               int32_t* __restrict__ local_rank = nullptr,
+                                                               int32_t* __restrict__ hist = nullptr) {
   constexpr int EP = NF * 32;
   constexpr int NE = NF < 4 ? NF : 4;
   constexpr int NKS = 4 / NE;
@@ -277,7 +288,9 @@ __global__ __launch_bounds__(kThreads) void router_ring_kernel(const bf16_t* __r
             red[((((ks - 1) * NE + eg) * TT + tt) * NFW + f) * 1024 + r * 64 + lane] = acc[tt][f][r];
     }
     __syncthreads();
-    if (ks > 0) return;
+    if constexpr (!FUSE) {
+      if (ks > 0) return;
+    }
 #pragma unroll
     for (int k2 = 1; k2 < NKS; ++k2)
 #pragma unroll
@@ -288,17 +301,77 @@ __global__ __launch_bounds__(kThreads) void router_ring_kernel(const bf16_t* __r
           for (int r = 0; r < 16; ++r)
             acc[tt][f][r] += red[((((k2 - 1) * NE + eg) * TT + tt) * NFW + f) * 1024 + r * 64 + lane];
   }
+  if constexpr (!FUSE) {
 #pragma unroll
-  for (int tt = 0; tt < TT; ++tt)
+    for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-    for (int f = 0; f < NFW; ++f) {
-      const int e = (eg * NFW + f) * 32 + l32;
+      for (int f = 0; f < NFW; ++f) {
+        const int e = (eg * NFW + f) * 32 + l32;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t t = t0 + tt * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-        if (t < T_ && e < E) logits[t * E + e] = acc[tt][f][r];
+        for (int r = 0; r < 16; ++r) {
+          const int64_t t = t0 + tt * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+          if (t < T_ && e < E) logits[t * E + e] = acc[tt][f][r];
+        }
       }
+  } else {
+    using namespace rdev;
+    // LDS of the idle ring: logits [kBT][EP] fp32, then the routing scratch
+    constexpr int kLogBytes = kBT * EP * 4;
+    constexpr int kSelOff = kLogBytes;
+    constexpr int kRankOff = kSelOff + kBT * kMaxTopK;
+    constexpr int kScoreOff = kRankOff + kBT * kMaxTopK * 2;
+    constexpr int kBiasOff = kScoreOff + kBT * kMaxTopK * 4;
+    constexpr int kCntOff = kBiasOff + kMaxExperts * 4;
+    static_assert(kCntOff + 4 * kMaxExperts * 4 <= D * kSlotBytes, "routing scratch fits the ring");
+    static_assert(G * KPL >= EP || G * KPL >= 8, "a token's lanes hold its keys");
+    char* lds = (char*)smem;
+    float* s_log = (float*)lds;
+    uint8_t* s_sel = (uint8_t*)(lds + kSelOff);
+    uint16_t* s_rank = (uint16_t*)(lds + kRankOff);
+    float* s_score = (float*)(lds + kScoreOff);
+    float* s_bias = (float*)(lds + kBiasOff);
+    int(*s_cnt)[kMaxExperts] = (int(*)[kMaxExperts])(lds + kCntOff);
+    __syncthreads();  // every wave is done with the ring and with the partial tiles
+    if (ks == 0) {
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+        for (int f = 0; f < NFW; ++f) {
+          const int e = (eg * NFW + f) * 32 + l32;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int tl = tt * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+            s_log[tl * EP + e] = acc[tt][f][r];
+            const int64_t t = t0 + tl;
+            if (logits && t < T_ && e < E) logits[t * E + e] = acc[tt][f][r];
+          }
+        }
     }
+    if (bias)
+      for (int e = threadIdx.x; e < E; e += kThreads) s_bias[e] = bias[e];
+    __syncthreads();
+    const int tid = threadIdx.x;
+    const int lig = tid & (G - 1);
+    const int e_lo = lig * KPL;
+    const int ntok = (int)min((int64_t)kBT, T_ - t0);
+    for (int tl = tid / G; tl < ntok; tl += kThreads / G) {
+      float kf[KPL];
+#pragma unroll
+      for (int j = 0; j < KPL; ++j) {
+        const int e = e_lo + j;
+        float v = -INFINITY;
+        if (e < E) {
+          v = s_log[tl * EP + e];
+          if (bias) v = v + s_bias[e];
+        }
+        kf[j] = v;
+      }
+      select_token<G, KPL>(kf, e_lo, E, K, score, renorm, lig, t0 + tl, tl, s_sel, s_score, topk_idx, topk_gate);
+    }
+    __syncthreads();
+    rank_chunk<kThreads / 64>(ntok * K, E, s_sel, s_rank, s_cnt, hist + (int64_t)blockIdx.x * E,
+                              local_rank + t0 * K);
+  }
 }
 
 }  // namespace rring
@@ -330,6 +403,53 @@ hipError_t router_ring(const void* x, const void* w, int64_t T_, int64_t d, int 
   return hipGetLastError();
 }
 
+// Tokens per workgroup of the fused router: the same choice as the router product's.
+int router_route_chunk(int64_t T_, int E) {
+  const int nf = (E + 31) / 32;
+  return (nf <= 2 && (T_ + 63) / 64 < 384) ? 32 : 64;
+}
+
+hipError_t router_route(const void* x, const void* w, const float* bias, int64_t T_, int64_t d, int E, int K,
+                        int score, int renorm, float* logits, int32_t* topk_idx, float* topk_gate,
+                        int32_t* counts, int32_t* offsets, int32_t* slot_pos, int32_t* row_src, void* ws,
+                        hipStream_t s) {
+  using namespace rring;
+  const bf16_t* xb = (const bf16_t*)x;
+  const bf16_t* wb = (const bf16_t*)w;
+  const int nf = (E + 31) / 32;
+  const int chunk = router_route_chunk(T_, E);
+  const int nch = (int)((T_ + chunk - 1) / chunk);
+  int32_t* hist = (int32_t*)ws;
+  if (nch > 0) {
+    const dim3 grid((unsigned)nch);
+#define MOE_ROUTER_FUSED(tt, nfe, depth, g, kpl)                                                        \
+  hipLaunchKernelGGL((router_ring_kernel<tt, nfe, depth, true, g, kpl>), grid, dim3(kThreads), 0, s, xb, wb, \
+                     T_, d, E, logits, bias, K, score, renorm, topk_idx, topk_gate, slot_pos, hist)
+    if (nf <= 1) {
+      if (chunk == 32) {
+        if (E <= 8) MOE_ROUTER_FUSED(1, 1, 16, 1, 8);
+        else if (E <= 16) MOE_ROUTER_FUSED(1, 1, 16, 1, 16);
+        else MOE_ROUTER_FUSED(1, 1, 16, 2, 16);
+      } else {
+        if (E <= 8) MOE_ROUTER_FUSED(2, 1, 8, 1, 8);
+        else if (E <= 16) MOE_ROUTER_FUSED(2, 1, 8, 1, 16);
+        else MOE_ROUTER_FUSED(2, 1, 8, 2, 16);
+      }
+    } else if (nf <= 2) {
+      if (chunk == 32) MOE_ROUTER_FUSED(1, 2, 13, 4, 16);
+      else MOE_ROUTER_FUSED(2, 2, 10, 4, 16);
+    } else if (nf <= 4) {
+      MOE_ROUTER_FUSED(2, 4, 6, 8, 16);
+    } else {
+      MOE_ROUTER_FUSED(2, 8, 4, 16, 16);
+    }
+#undef MOE_ROUTER_FUSED
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return launch_route_scan_finalize(hist, nch, chunk, T_, E, K, topk_idx, counts, offsets, slot_pos, row_src, s);
+}
+
 template <typename T>
 hipError_t router_t(const void* x, const void* w, int64_t T_, int64_t d, int E, float* logits,
                     hipStream_t s) {
@@ -349,6 +469,19 @@ hipError_t router_t(const void* x, const void* w, int64_t T_, int64_t d, int E, 
 }
 
 }  // namespace
+
+size_t router_route_workspace_bytes(int64_t T, int E) {
+  const int64_t nch = (T + 31) / 32;  // the smallest chunk the fused router uses
+  return (size_t)(((nch * E * 4) + 255) / 256 * 256);
+}
+
+hipError_t launch_router_route(const void* x, const void* w, const float* bias, int64_t T, int64_t d, int E, int K,
+                               int score, int renorm, float* logits, int32_t* topk_idx, float* topk_gate,
+                               int32_t* counts, int32_t* offsets, int32_t* slot_pos, int32_t* row_src, void* ws,
+                               hipStream_t s) {
+  return router_route(x, w, bias, T, d, E, K, score, renorm, logits, topk_idx, topk_gate, counts, offsets, slot_pos,
+                      row_src, ws, s);
+}
 
 hipError_t launch_router_logits(const void* x, const void* w, int64_t T, int64_t d, int E, int dtype,
                                 float* logits, hipStream_t s) {

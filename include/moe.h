@@ -55,7 +55,7 @@ enum moe_score { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 };
 enum moe_layout { MOE_LAYOUT_NK = 0, MOE_LAYOUT_KN = 1 };
 enum moe_epilogue { MOE_EPI_NONE = 0, MOE_EPI_SWIGLU = 1, MOE_EPI_DSWIGLU = 2 };
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 #define MOE_MAX_EXPERTS 256
 #define MOE_MAX_TOPK 32
 #define MOE_MAX_GROUPS 1024
@@ -109,6 +109,32 @@ int32_t moe_route(const float* logits, const float* bias, int64_t T, int32_t E, 
                   int32_t score, int32_t renorm, int32_t* topk_idx, float* topk_gate,
                   int32_t* counts, int32_t* offsets, int32_t* slot_pos, int32_t* row_src,
                   void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/*
+ * Bytes of device workspace moe_router_route needs for T tokens and E experts.
+ * MOE_INVALID_ARG if bytes is NULL, T < 0 or E is outside [1, MOE_MAX_EXPERTS].
+ */
+int32_t moe_router_route_workspace_size(int64_t T, int32_t E, size_t* bytes);
+
+/*
+ * Fused router (S0-S3 in three launches; TE-MoE "Optimisation 2": fused router
+ * kernels assign tokens to experts): the router product of moe_router_logits,
+ * then the routing of moe_route on those logits, with identical results (the
+ * same products in the same order, the same keys, choices, gates, counts,
+ * offsets and positions).  Each workgroup keeps its tile of logits on chip and
+ * routes its own tokens; the histogram scan and the positions follow.
+ *   x DEVICE [T, d] bf16;  w_router DEVICE [E, d] bf16;  bias DEVICE [E] fp32 or NULL
+ *   logits   DEVICE [T, E] fp32, written when not NULL (the router backward reads them)
+ *   topk_idx, topk_gate, counts, offsets, slot_pos, row_src: as moe_route
+ *   ws       DEVICE scratch of at least moe_router_route_workspace_size(T, E) bytes
+ * Requires dtype == MOE_BF16 (MOE_UNSUPPORTED otherwise: fp32 takes moe_router_logits and
+ * moe_route), d >= 8, d % 8 == 0, 1 <= K <= E <= MOE_MAX_EXPERTS, K <= MOE_MAX_TOPK,
+ * T*K < 2^31.
+ */
+int32_t moe_router_route(const void* x, const void* w_router, const float* bias, int64_t T, int64_t d, int32_t E,
+                         int32_t K, int32_t dtype, int32_t score, int32_t renorm, float* logits, int32_t* topk_idx,
+                         float* topk_gate, int32_t* counts, int32_t* offsets, int32_t* slot_pos, int32_t* row_src,
+                         void* ws, size_t ws_bytes, moe_stream_t stream);
 
 /*
  * Permute / dispatch into expert-contiguous order (S4; TE-MoE Figure 3

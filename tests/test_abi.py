@@ -29,6 +29,7 @@ def test_header_declares_the_boundary():
     for n in ["moe_route", "moe_permute", "moe_grouped_gemm", "moe_unpermute_combine",
               "moe_grouped_gemm_wgrad", "moe_router_logits", "moe_route_workspace_size",
               "moe_route_backward", "moe_router_logits_backward", "moe_router_backward_workspace_size",
+              "moe_router_route", "moe_router_route_workspace_size",
               "moe_status_str", "moe_abi_version"]:
         assert n in names
 
@@ -43,7 +44,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert moe.moe_abi_version() == 3
+    assert moe.moe_abi_version() == 4
     assert moe.status_str(0) == "ok"
     assert "invalid" in moe.status_str(1)
     assert moe.status_str(99) == "unknown status"
@@ -145,3 +146,22 @@ def test_router_backward_rejects_bad_arguments(lib):
     assert lib.moe_router_logits_backward(P, P, None, 100, 64, 8, 1, None, P, 0, P, need, None) == 1  # dx needs Wr
     assert lib.moe_router_logits_backward(P, P, P, 100, 64, 8, 3, P, P, 0, P, need, None) == 2
     assert lib.moe_router_logits_backward(P, P, P, 100, 64, 8, 1, None, None, 0, None, 0, None) == 0  # no output
+
+
+def test_router_route_rejects_bad_arguments(lib):
+    n = ctypes.c_size_t(0)
+    assert lib.moe_router_route_workspace_size(1000, 8, ctypes.byref(n)) == 0 and n.value >= 32 * 8 * 4
+    assert lib.moe_router_route_workspace_size(-1, 8, ctypes.byref(n)) == 1
+    ws = n.value
+
+    def rr(T=100, d=64, E=8, K=2, dt=1, score=0, x=P, bias=None, wsb=None):
+        return lib.moe_router_route(x, P, bias, T, d, E, K, dt, score, 1, None, P, P, P, P, P, P, P,
+                                    ws if wsb is None else wsb, None)
+    assert rr(dt=0) == 2                  # fp32 takes the unfused path
+    assert rr(score=3) == 2
+    assert rr(K=9) == 1                   # K > E
+    assert rr(d=12) == 1                  # d % 8
+    assert rr(x=P + 8) == 1               # misaligned
+    assert rr(bias=P + 2) == 1
+    assert rr(wsb=0) == 1                 # workspace too small
+    assert rr(x=None) == 1

@@ -161,6 +161,83 @@ def test_router_logits_shapes(T, d, E):
     assert np.all(err <= 1e-5 * scale + 1e-30), float(np.nanmax(err / scale))
 
 
+# ----------------------------------------------------------------- fused router
+
+def _fused_vs_unfused(T, d, E, K, score, renorm, bias=None, seed=0, with_logits=True):
+    rng = np.random.default_rng(seed)
+    x = mi.f32_to_bf16_bits(rng.standard_normal((T, d)).astype(np.float32))
+    w = mi.f32_to_bf16_bits((rng.standard_normal((E, d)) * 1.5 / np.sqrt(d)).astype(np.float32))
+    xd, wd = dev(x), dev(w)
+    bd = dev(bias) if bias is not None else None
+    i32 = dict(dtype=torch.int32, device="cuda")
+
+    def outs():
+        return dict(logits=torch.full((T, E), float("nan"), dtype=torch.float32, device="cuda"),
+                    idx=torch.full((T, K), -7, **i32),
+                    gate=torch.full((T, K), float("nan"), dtype=torch.float32, device="cuda"),
+                    counts=torch.full((E,), -7, **i32), offs=torch.full((E + 1,), -7, **i32),
+                    pos=torch.full((T * K,), -7, **i32), src=torch.full((T * K,), -7, **i32))
+    a, b = outs(), outs()
+    ws_a = torch.empty((max(1, moe.moe_router_route_workspace_size(T, E)),), dtype=torch.uint8, device="cuda")
+    ws_b = torch.empty((max(1, moe.moe_route_workspace_size(T, E)),), dtype=torch.uint8, device="cuda")
+    moe.moe_router_route(xd, wd, bd, K, score, renorm, a["logits"] if with_logits else None, a["idx"], a["gate"],
+                         a["counts"], a["offs"], a["pos"], a["src"], ws_a)
+    moe.moe_router_logits(xd, wd, b["logits"])
+    moe.moe_route(b["logits"], bd, K, score, renorm, b["idx"], b["gate"], b["counts"], b["offs"], b["pos"],
+                  b["src"], ws_b)
+    torch.cuda.synchronize()
+    for k in a:
+        if k == "logits" and not with_logits:
+            continue
+        assert torch.equal(a[k], b[k]), k
+    return host(b["logits"])
+
+
+@pytest.mark.parametrize("T,d,E,K,score,renorm", [
+    (1, 64, 1, 1, 0, True),        # one token, one expert
+    (100, 64, 3, 2, 0, True),      # E < 8
+    (1000, 512, 8, 2, 0, True),    # Mixtral-like, 32-token chunks
+    (30000, 256, 8, 2, 0, False),  # 64-token chunks, softmax without renormalisation
+    (700, 512, 16, 4, 1, True),    # sigmoid
+    (333, 256, 20, 6, 1, False),   # E not a power of two, sigmoid without renormalisation
+    (25000, 128, 32, 8, 1, True),  # DeepSeek-V3-like shape class, 64-token chunks
+    (3000, 512, 64, 6, 0, True),   # two expert tiles, 32-token chunks
+    (30000, 136, 64, 8, 0, True),  # two expert tiles, 64-token chunks, d tail
+    (257, 2048, 128, 8, 0, True),  # fine-grained class
+    (130, 256, 100, 7, 0, True),   # E not a multiple of 32
+    (333, 1032, 256, 32, 0, True), # largest E and K
+])
+def test_router_route_matches_unfused(T, d, E, K, score, renorm):
+    logits = _fused_vs_unfused(T, d, E, K, score, renorm, seed=T + d + E + K)
+    # and the routing of those logits is the oracle's
+    _check_route(logits, None, K, score, renorm)
+
+
+def test_router_route_bias_masked_expert_and_no_logits_output():
+    E = 16
+    bias = np.linspace(-0.4, 0.4, E).astype(np.float32)
+    bias[5] = -np.inf
+    bias[0] = -0.0
+    logits = _fused_vs_unfused(900, 256, E, 3, 0, True, bias=bias, seed=5)
+    _check_route(logits, bias, 3)
+    _fused_vs_unfused(900, 256, E, 3, 1, True, bias=bias, seed=6, with_logits=False)
+
+
+def test_router_route_empty_batch():
+    E = 8
+    i32 = dict(dtype=torch.int32, device="cuda")
+    counts = torch.full((E,), -1, **i32)
+    offs = torch.full((E + 1,), -1, **i32)
+    e0 = torch.empty((0,), **i32)
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((E, 64), dtype=torch.bfloat16, device="cuda")
+    moe.moe_router_route(x, w, None, 2, 0, True, None, e0, torch.empty(0, device="cuda"), counts, offs, e0, e0,
+                         None)
+    torch.cuda.synchronize()
+    assert host(counts).tolist() == [0] * E
+    assert host(offs).tolist() == [0] * (E + 1)
+
+
 # ----------------------------------------------------------------- router backward
 
 def _route_bwd_case(T, E, K, score, renorm, seed, bias=None):
