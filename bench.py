@@ -178,28 +178,40 @@ def main():
     bufs = moe.MoEBuffers(cfg.T, cfg.d, cfg.E, cfg.K, cfg.F, dt)
     stream = torch.cuda.current_stream()
 
-    names = ["router", "route", "permute", "gemm_gate_up", "gemm_down", "combine"]
+    # bf16: the fused router (product + routing in one call); fp32: product, then routing
+    fused = cfg.bf16
+    names = (["router_route"] if fused else ["router", "route"]) + ["permute", "gemm_gate_up", "gemm_down", "combine"]
+    nk = len(names)
+    rr_ws = torch.empty((max(moe.moe_router_route_workspace_size(cfg.T, cfg.E), 256),), dtype=torch.uint8,
+                        device="cuda")
 
     def step(ev=None):
         def mark(i):
             if ev is not None:
                 ev[i].record(stream)
-        mark(0)
-        moe.moe_router_logits(x, wr, bufs.logits)
-        mark(1)
-        moe.moe_route(bufs.logits, b, cfg.K, cfg.score, cfg.renorm, bufs.topk_idx, bufs.gates, bufs.counts,
-                      bufs.offsets, bufs.slot_pos, bufs.row_src, bufs.ws)
-        mark(2)
+        i = 0
+        mark(i)
+        if fused:
+            moe.moe_router_route(x, wr, b, cfg.K, cfg.score, cfg.renorm, None, bufs.topk_idx, bufs.gates,
+                                 bufs.counts, bufs.offsets, bufs.slot_pos, bufs.row_src, rr_ws)
+        else:
+            moe.moe_router_logits(x, wr, bufs.logits)
+            i += 1
+            mark(i)
+            moe.moe_route(bufs.logits, b, cfg.K, cfg.score, cfg.renorm, bufs.topk_idx, bufs.gates, bufs.counts,
+                          bufs.offsets, bufs.slot_pos, bufs.row_src, bufs.ws)
+        i += 1
+        mark(i)
         moe.moe_permute(x, cfg.K, bufs.slot_pos, bufs.x_perm)
-        mark(3)
+        mark(i + 1)
         moe.moe_grouped_gemm(bufs.x_perm, w13, moe.MOE_LAYOUT_NK, bufs.offsets, bufs.h, moe.MOE_EPI_SWIGLU,
                              workspace=bufs.gemm_ws)
-        mark(4)
+        mark(i + 2)
         moe.moe_grouped_gemm(bufs.h, w2, moe.MOE_LAYOUT_NK, bufs.offsets, bufs.y_perm, moe.MOE_EPI_NONE,
                              workspace=bufs.gemm_ws)
-        mark(5)
+        mark(i + 3)
         moe.moe_unpermute_combine(bufs.y_perm, bufs.slot_pos, bufs.gates, cfg.T, cfg.K, bufs.y)
-        mark(6)
+        mark(i + 4)
 
     for _ in range(args.warmup):
         step()
@@ -226,7 +238,7 @@ def main():
     ms_per_step = (time.perf_counter() - t0) * 1e3 / max(args.steps, 1)
 
     # per-kernel breakdown: K eager steps with HIP events on the launch stream around every call
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -235,7 +247,7 @@ def main():
     eager_ms_per_step = (time.perf_counter() - t0) * 1e3 / max(args.steps, 1)
     per = np.zeros(len(names))
     for ev in evs:
-        per += np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(6)])
+        per += np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(nk)])
     per /= max(args.steps, 1)
     kms = dict(zip(names, per.tolist()))
 
@@ -250,6 +262,9 @@ def main():
     perm_bytes = (cfg.T + M) * cfg.d * esz + 4 * M
     comb_bytes = (M + cfg.T) * cfg.d * esz + 8 * M
     router_bytes = cfg.T * cfg.d * esz + cfg.E * cfg.d * esz + 4 * cfg.T * cfg.E
+    # fused: x and W once, then per slot the index and gate written, its in-tile rank written
+    # and read back, its position and its inverse written
+    router_route_bytes = cfg.T * cfg.d * esz + cfg.E * cfg.d * esz + 24 * M
 
     traffic = None
     try:
@@ -269,7 +284,8 @@ def main():
     cpu = cpu_baseline(cfg, inp, args.cpu_seconds)
     hbm = {"permute": perm_bytes / (kms["permute"] * 1e-3) / 1e9,
            "combine": comb_bytes / (kms["combine"] * 1e-3) / 1e9,
-           "router": router_bytes / (kms["router"] * 1e-3) / 1e9}
+           **({"router_route": router_route_bytes / (kms["router_route"] * 1e-3) / 1e9} if fused else
+              {"router": router_bytes / (kms["router"] * 1e-3) / 1e9})}
 
     out = {
         "metric": "MoE layer forward tokens/s (grouped-GEMM TFLOP/s and % of bf16 MFMA peak alongside)",

@@ -3,7 +3,7 @@
 Forward (page "Accelerating dropless MoE training in JAX with NVIDIA
 Transformer Engine", Figure 3 paragraph: router -> dispatch -> grouped MLP of
 two grouped GEMMs -> combine):
-    moe_router_logits -> moe_route -> moe_permute
+    moe_router_route (bf16; fp32: moe_router_logits -> moe_route) -> moe_permute
       -> moe_grouped_gemm (gate/up, SwiGLU epilogue) -> moe_grouped_gemm (down)
       -> moe_unpermute_combine
 Backward (routing held fixed):
@@ -24,7 +24,7 @@ from . import (MOE_EPI_DSWIGLU, MOE_EPI_NONE, MOE_EPI_SWIGLU, MOE_LAYOUT_KN, MOE
                dtype_code, moe_grouped_gemm, moe_grouped_gemm_wgrad, moe_grouped_gemm_workspace_size,
                moe_permute, moe_route, moe_route_backward, moe_route_workspace_size,
                moe_router_backward_workspace_size, moe_router_logits, moe_router_logits_backward,
-               moe_unpermute_combine)
+               moe_router_route, moe_router_route_workspace_size, moe_unpermute_combine)
 
 
 class MoEBuffers:
@@ -47,6 +47,10 @@ class MoEBuffers:
         self.row_src = torch.empty((M,), **i32)
         ws = moe_route_workspace_size(T, E)
         self.ws = torch.empty((max(ws, 256),), dtype=torch.uint8, device=dev)
+        self.fused_router = dtype == torch.bfloat16
+        if self.fused_router:
+            self.rr_ws = torch.empty((max(moe_router_route_workspace_size(T, E), 256),), dtype=torch.uint8,
+                                     device=dev)
         # grouped GEMM workspace: zeroed once, every call leaves its counters at zero
         self.gemm_ws = torch.zeros((moe_grouped_gemm_workspace_size(),), dtype=torch.uint8, device=dev)
         self.x_perm = torch.empty((M, d), **act)
@@ -75,11 +79,16 @@ def layer_forward(x, w_router, bias, w13, w2, K: int, score: int, renorm: bool, 
 
     ``logits`` (fp32 [T, E]) skips the router product and routes on the given values."""
     b = bufs
-    if logits is None:
-        moe_router_logits(x, w_router, b.logits, stream=stream)
-        logits = b.logits
-    moe_route(logits, bias, K, score, renorm, b.topk_idx, b.gates, b.counts, b.offsets, b.slot_pos,
-              b.row_src, b.ws, stream=stream)
+    if logits is None and b.fused_router:
+        # product and routing in one call; the logits are still written for the router backward
+        moe_router_route(x, w_router, bias, K, score, renorm, b.logits, b.topk_idx, b.gates, b.counts,
+                         b.offsets, b.slot_pos, b.row_src, b.rr_ws, stream=stream)
+    else:
+        if logits is None:
+            moe_router_logits(x, w_router, b.logits, stream=stream)
+            logits = b.logits
+        moe_route(logits, bias, K, score, renorm, b.topk_idx, b.gates, b.counts, b.offsets, b.slot_pos,
+                  b.row_src, b.ws, stream=stream)
     moe_permute(x, K, b.slot_pos, b.x_perm, stream=stream)
     moe_grouped_gemm(b.x_perm, w13, MOE_LAYOUT_NK, b.offsets, b.h, MOE_EPI_SWIGLU, epi_save=b.pre,
                      workspace=b.gemm_ws, stream=stream)
