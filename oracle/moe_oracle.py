@@ -41,6 +41,7 @@ both sides must take that decision in the same precision.
 """
 from __future__ import annotations
 
+import math
 from dataclasses import dataclass
 
 import numpy as np
@@ -335,6 +336,92 @@ def router_backward(d_logits: np.ndarray, x: np.ndarray, w_router: np.ndarray):
     """Backward of logits = x . Wr^T: dWr = d_logits^T . x  [E, d], dx = d_logits . Wr  [T, d]; fp64."""
     dl = np.asarray(d_logits, np.float64)
     return dl.T @ to_f64(x), dl @ to_f64(w_router)
+
+
+# ----------------------------------------------------------------------------
+# MXFP8 block scaling of the expert matmuls (TE-MoE "Optimisation 1": on newer
+# GPUs the grouped GEMM path takes MXFP8 operands from grouped quantisation).
+# The pages name the format only.  Its definition is the OCP Microscaling (MX)
+# format: every 32 consecutive elements along the reduction axis share one
+# power-of-two scale stored as E8M0 (code c means 2^(c - 127)); the elements
+# are FP8 E4M3 (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; largest
+# finite value 448, smallest subnormal 2^-9, no infinities).  The conversion
+# reads: shared exponent = floor(log2(max |v|)) - 8 (8 is E4M3's largest
+# exponent), clamped to [-127, 127]; a block of zeros takes code 0; each
+# element is v / 2^shared rounded to nearest even and saturated to +-448.
+
+MX_BLOCK = 32
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(code: int) -> float:
+    """Value of an FP8 E4M3 code (0x7F / 0xFF are NaN)."""
+    code = int(code) & 0xFF
+    sign = -1.0 if code & 0x80 else 1.0
+    e, m = (code >> 3) & 0xF, code & 7
+    if e == 0xF and m == 7:
+        return float("nan")
+    if e == 0:
+        return sign * (m / 8.0) * 2.0 ** -6
+    return sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+def e4m3_encode(v: float) -> int:
+    """Nearest E4M3 code (ties to even mantissa), saturating to +-448; v finite."""
+    v = float(v)
+    sign = 0x80 if math.copysign(1.0, v) < 0 else 0
+    a = abs(v)
+    if a >= E4M3_MAX:
+        return sign | 0x7E
+    if a < 2.0 ** -6:                       # subnormal grid of 2^-9
+        q = round(a * 2.0 ** 9)             # Python's round: ties to even
+        return sign | q                     # q == 8 is the smallest normal, code 0x08
+    f, e = math.frexp(a)                    # a = f 2^e, f in [0.5, 1)
+    e -= 1                                  # a = (2 f) 2^e, 2 f in [1, 2)
+    m = round((2.0 * f - 1.0) * 8.0)
+    if m == 8:
+        e, m = e + 1, 0
+    return sign | ((e + 7) << 3) | m
+
+
+def mx_quantize(a: np.ndarray):
+    """MXFP8 of a [R, K] array (K a multiple of 32) along its last axis.
+
+    Returns (codes uint8 [R, K], scales uint8 [R, K / 32]) with value = e4m3(code) * 2^(scale - 127)."""
+    v = to_f64(a)
+    R, K = v.shape
+    if K % MX_BLOCK:
+        raise ValueError("K must be a multiple of 32")
+    codes = np.zeros((R, K), np.uint8)
+    scales = np.zeros((R, K // MX_BLOCK), np.uint8)
+    for r in range(R):
+        for b in range(K // MX_BLOCK):
+            blk = v[r, b * MX_BLOCK:(b + 1) * MX_BLOCK]
+            amax = float(np.max(np.abs(blk)))
+            if amax == 0.0:
+                shared = -127
+            else:
+                shared = min(127, max(-127, math.frexp(amax)[1] - 1 - 8))
+            scales[r, b] = shared + 127
+            for i, x in enumerate(blk):
+                codes[r, b * MX_BLOCK + i] = e4m3_encode(math.ldexp(float(x), -shared))
+    return codes, scales
+
+
+def mx_dequantize(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """fp64 values of MXFP8 codes and their block scales."""
+    table = np.array([e4m3_decode(c) for c in range(256)], np.float64)
+    val = table[codes]
+    factor = np.exp2(scales.astype(np.float64) - 127.0)
+    return val * np.repeat(factor, MX_BLOCK, axis=-1)
+
+
+def grouped_gemm_mx(a_codes, a_scales, b_codes, b_scales, offsets: np.ndarray) -> np.ndarray:
+    """The grouped GEMM (N-by-K weights) on the values the MXFP8 operands represent, in fp64."""
+    a = mx_dequantize(a_codes, a_scales)
+    G, N, K = b_codes.shape
+    b = mx_dequantize(b_codes.reshape(G * N, K), b_scales.reshape(G * N, K // MX_BLOCK)).reshape(G, N, K)
+    return grouped_gemm(a, b, offsets, "nk")
 
 
 # ----------------------------------------------------------------------------

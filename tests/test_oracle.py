@@ -507,3 +507,76 @@ def test_input_prefix_rows_are_reproducible():
     a = mi.normal(c.seed, mi.TAG_X, (c.T, c.d), 1.0, True, rows=3000)
     b = mi.normal(c.seed, mi.TAG_X, (c.T, c.d), 1.0, True, rows=100)
     assert np.array_equal(a[:100], b)
+
+
+# ----------------------------------------------------------------------------
+# MXFP8 (OCP MX: 32-element blocks, E8M0 scales, E4M3 elements)
+
+def test_e4m3_code_table_closed_forms():
+    vals = [orc.e4m3_decode(c) for c in range(0x7F)]         # the finite positive codes
+    assert vals[0] == 0.0 and vals[0x01] == 2.0 ** -9 and vals[0x07] == 7 * 2.0 ** -9
+    assert vals[0x08] == 2.0 ** -6 and vals[0x38] == 1.0 and vals[0x7E] == 448.0
+    assert all(b > a for a, b in zip(vals, vals[1:]))          # strictly increasing
+    assert math.isnan(orc.e4m3_decode(0x7F)) and math.isnan(orc.e4m3_decode(0xFF))
+    for c in range(0x7F):
+        assert orc.e4m3_decode(c | 0x80) == -vals[c] or (c == 0 and orc.e4m3_decode(0x80) == 0.0)
+
+
+def test_e4m3_encode_round_trips_ties_to_even_and_saturates():
+    for c in list(range(0x7F)) + list(range(0x80, 0xFF)):
+        assert orc.e4m3_encode(orc.e4m3_decode(c)) == c
+    # every midpoint between neighbouring codes goes to the code with the even mantissa
+    for c in range(0x7E):
+        lo, hi = orc.e4m3_decode(c), orc.e4m3_decode(c + 1)
+        mid = (lo + hi) / 2
+        want = c if (c & 1) == 0 else c + 1
+        assert orc.e4m3_encode(mid) == want, hex(c)
+        assert orc.e4m3_encode(-mid) == 0x80 | want
+        assert orc.e4m3_encode(lo + (hi - lo) / 4) == c and orc.e4m3_encode(hi - (hi - lo) / 4) == c + 1
+    for big in (448.0, 460.0, 464.0, 479.0, 1e6):
+        assert orc.e4m3_encode(big) == 0x7E and orc.e4m3_encode(-big) == 0xFE
+
+
+def test_mx_quantize_scale_rule_and_error_bound():
+    rng = np.random.default_rng(60)
+    a = (rng.standard_normal((6, 128)) * np.exp2(rng.integers(-20, 20, (6, 1)))).astype(np.float32)
+    a[2, 32:64] = 0.0                                           # a block of zeros
+    a[3, 0] = -0.0
+    codes, scales = orc.mx_quantize(a)
+    assert codes.shape == a.shape and scales.shape == (6, 4)
+    assert scales[2, 1] == 0 and np.all(codes[2, 32:64] == 0)
+    back = orc.mx_dequantize(codes, scales)
+    for r in range(6):
+        for b in range(4):
+            blk = a[r, b * 32:(b + 1) * 32].astype(np.float64)
+            amax = np.abs(blk).max()
+            if amax == 0:
+                continue
+            shared = int(scales[r, b]) - 127
+            assert shared == math.floor(math.log2(amax)) - 8      # the largest element lands in [256, 512)
+            x = 2.0 ** shared
+            err = np.abs(back[r, b * 32:(b + 1) * 32] - blk)
+            # half a step of each element's binade (steps of 2^-9 x below 2^-6 x), or the saturation
+            # of values above 448 x
+            step = np.where(np.abs(blk) < 2.0 ** -6 * x, 2.0 ** -9 * x,
+                            np.exp2(np.floor(np.log2(np.maximum(np.abs(blk), 1e-300)))) / 8)
+            ok = (err <= step / 2 * (1 + 1e-12)) | ((np.abs(blk) > 448 * x) & (np.abs(back[r, b * 32:(b + 1) * 32]) == 448 * x))
+            assert np.all(ok), (r, b)
+
+
+def test_mx_grouped_gemm_is_exact_on_representable_values():
+    """Values that E4M3 holds exactly under their block scale quantise losslessly, so the MX
+    grouped GEMM equals the plain grouped GEMM of the inputs."""
+    rng = np.random.default_rng(61)
+    M, N, K, G = 40, 24, 64, 3
+    grid = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, -1.0, -2.5, 0.25])
+    a = rng.choice(grid, (M, K))
+    b = rng.choice(grid, (G, N, K))
+    a[:, ::32] = 3.0                                            # every block's max is 3: scale 2^-7
+    b[:, :, ::32] = -3.0
+    offsets = np.array([0, 10, 10, M])
+    ac, asc = orc.mx_quantize(a)
+    bc, bsc = orc.mx_quantize(b.reshape(G * N, K))
+    np.testing.assert_array_equal(orc.mx_dequantize(ac, asc), a)
+    got = orc.grouped_gemm_mx(ac, asc, bc.reshape(G, N, K), bsc.reshape(G, N, K // 32), offsets)
+    np.testing.assert_array_equal(got, orc.grouped_gemm(a, b, offsets, "nk"))
