@@ -39,6 +39,8 @@ SIGNATURES = {
     "moe_router_route_workspace_size": (_I32, [_I64, _I32, _c.POINTER(_SZ)]),
     "moe_router_route": (_I32, [_P, _P, _P, _I64, _I64, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P,
                                 _P, _SZ, _P]),
+    "moe_mx_quantize": (_I32, [_P, _I64, _I64, _I32, _P, _P, _P]),
+    "moe_grouped_gemm_mx": (_I32, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _P, _P]),
     "moe_route_backward": (_I32, [_P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _P, _P]),
     "moe_router_backward_workspace_size": (_I32, [_I64, _I64, _I32, _I32, _c.POINTER(_SZ)]),
     "moe_router_logits_backward": (_I32, [_P, _P, _P, _I64, _I64, _I32, _I32, _P, _P, _I32, _P, _SZ, _P]),
@@ -215,6 +217,21 @@ def moe_router_route(x, w_router, bias, K: int, score: int, renorm: bool, logits
     _call("moe_router_route", _ptr(x), _ptr(w_router), _ptr(bias), T, d, E, K, dtype_code(x), score,
           int(bool(renorm)), _ptr(logits), _ptr(topk_idx), _ptr(topk_gate), _ptr(counts), _ptr(offsets),
           _ptr(slot_pos), _ptr(row_src), _ptr(ws), ws_bytes, _stream(stream))
+
+
+def moe_mx_quantize(x, codes, scales, stream=None) -> None:
+    """MXFP8 of the rows of x [R, K] (bf16): codes [R, K] uint8, scales [R, K / 32] uint8."""
+    R, K = x.shape
+    _call("moe_mx_quantize", _ptr(x), R, K, dtype_code(x), _ptr(codes), _ptr(scales), _stream(stream))
+
+
+def moe_grouped_gemm_mx(A, A_scales, B, B_scales, group_offsets, C, epilogue: int = MOE_EPI_NONE,
+                        stream=None) -> None:
+    """Grouped GEMM on MXFP8 operands: A [M, Kd] codes, B [G, N, Kd] codes, bf16 C."""
+    M, Kd = A.shape
+    G, N = B.shape[0], B.shape[1]
+    _call("moe_grouped_gemm_mx", _ptr(A), _ptr(A_scales), _ptr(B), _ptr(B_scales), _ptr(group_offsets), M, N, Kd,
+          G, epilogue, _ptr(C), _stream(stream))
 
 
 from .layer import MoEBuffers, layer_backward, layer_forward  # noqa: E402,F401

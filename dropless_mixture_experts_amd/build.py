@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
-SOURCES = ["route.hip", "router.hip", "router_backward.hip", "permute.hip", "grouped_gemm.hip", "moe_abi.cpp"]
+SOURCES = ["route.hip", "router.hip", "router_backward.hip", "mxfp8.hip", "permute.hip", "grouped_gemm.hip", "moe_abi.cpp"]
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 
 

@@ -657,6 +657,9 @@ struct GemmParams {
   int ws_slots;
   int P;   // CUs the split tail spreads over
   int nk;  // K stages of a tile (ring kernel)
+  // MXFP8 operands: E8M0 block scales of A [M][Kd/32] and B [G*N][Kd/32]
+  const uint8_t* sa = nullptr;
+  const uint8_t* sb = nullptr;
 };
 constexpr int kSplitCountBytes = 4096;             // counters: up to 1024 (tile, wave) pairs
 constexpr int kSplitSlotFloats = 256 * 256;        // one fp32 256 x 256 partial tile
@@ -1914,6 +1917,189 @@ size_t grouped_gemm_workspace_bytes() {
   if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
   return kSplitCountBytes + (size_t)cus * kSplitSlotFloats * sizeof(float);
+}
+
+// ---------------------------------------------------------------------------
+// MXFP8 grouped GEMM (N-by-K weights): A [M][Kd] and B [G][N][Kd] are FP8 E4M3 codes with
+// one E8M0 scale per 32 consecutive Kd values of a row; C = A_g . B_g^T in fp32, bf16 out
+// (plain or SwiGLU epilogue).  256 x 256 tiles in the grouped order of find_tile, 4 waves of
+// 128 x 128.  A stage is 128 Kd values (128 bytes a row) of both operands plus their 4 scale
+// bytes a row, moved by LDS DMA into one of two 66 KB slots while the other is read.  The
+// MFMA v_mfma_scale_f32_32x32x64_f8f6f4 takes 32 bytes a lane for 64 Kd values of a row
+// split over two lanes (hi = 0, 1); the hardware applies lane hi's scale byte to bytes
+// 16 hi .. 16 hi + 15 of both lanes.  So lane hi holds Kd values 64 j + 16 hi .. + 15 (block
+// 2 j) then 64 j + 32 + 16 hi .. + 15 (block 2 j + 1) of sub-step j, and the scale of block
+// 2 j + hi.
+namespace mxg {
+constexpr int kMxRow = 128;                     // Kd values of a row per stage
+constexpr int kOpBytes = 256 * kMxRow;          // 32 KB: one operand's rows of a stage
+constexpr int kScaleOff = 2 * kOpBytes;            // then 256 scale words of A, 256 of B
+constexpr int kSlotBytes = 2 * kOpBytes + 2 * 1024;
+constexpr int kQ = 8;                              // row DMAs of one operand per wave per stage
+constexpr int kNQ = 2 * kQ + 2;                    // DMAs per wave per stage (rows, then scales)
+
+__device__ __forceinline__ void dma4(const char* sbase, uint32_t voff, uint32_t lds_byte) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1 offset:0"
+               :: "v"(voff), "s"(sbase), "s"(lds_byte) : "memory", "m0");
+}
+__device__ __forceinline__ void wait_stage() { asm volatile("s_waitcnt vmcnt(18) lgkmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void wait_none() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory"); }
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+}  // namespace mxg
+
+template <int EPI>
+__global__ __launch_bounds__(ring4::kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void grouped_gemm_mx_kernel(GemmParams p) {
+  using namespace mxg;
+  static_assert(kNQ == 18, "the stage wait counts 18 DMAs a wave");
+  __shared__ uint4 smem[2 * kSlotBytes / 16];
+  int g, nt;
+  int64_t m0, re;
+  if (!find_tile<ring4::kThreads>(p, g, m0, re, nt, (int*)smem)) return;
+  __syncthreads();  // every thread has read the tile from the scratch that the loads overwrite
+  g = __builtin_amdgcn_readfirstlane(g);
+  nt = __builtin_amdgcn_readfirstlane(nt);
+  m0 = ring4::uniform64(m0);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int64_t ld = p.Kd;           // bytes per row of codes
+  const int64_t lds_ = p.Kd / 32;    // bytes per row of scales
+  const int nk = (int)(p.Kd / kMxRow);
+  const int64_t b0row = EPI == EPI_SWIGLU ? (int64_t)nt * 128 : (int64_t)nt * 256;
+  const int64_t F = p.N / 2;
+  // the tile's B row of local row r (SwiGLU: gate rows, then the matching up rows)
+  auto brow = [&](int r) -> int64_t {
+    int64_t br;
+    if (EPI == EPI_SWIGLU) {
+      int64_t cc = (int64_t)nt * 128 + (r & 127);
+      cc = cc < F ? cc : F - 1;
+      br = (r < 128 ? 0 : F) + cc;
+    } else {
+      br = (int64_t)nt * 256 + r;
+      br = br < p.N ? br : p.N - 1;
+    }
+    return (int64_t)g * p.N + br;
+  };
+  auto arow = [&](int r) -> int64_t {
+    const int64_t ar = m0 + r;
+    return ar < p.M ? ar : p.M - 1;
+  };
+  // uniform bases at the tile's first rows; per-lane 32-bit offsets of rows relative to them
+  // (within (N + 256) Kd bytes, checked on the host)
+  const int64_t b_first = (int64_t)g * p.N + b0row;
+  const char* a_base = ring4::uniform_ptr((const char*)p.A + m0 * ld);
+  const char* b_base = ring4::uniform_ptr((const char*)p.B + b_first * ld);
+  const char* sa_base = ring4::uniform_ptr((const char*)p.sa + m0 * lds_);
+  const char* sb_base = ring4::uniform_ptr((const char*)p.sb + b_first * lds_);
+  uint32_t va[kQ], vb[kQ];
+#pragma unroll
+  for (int q = 0; q < kQ; ++q) {
+    const int r = (wave * kQ + q) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ ring4::swz(r);
+    va[q] = (uint32_t)((arow(r) - m0) * ld + c * 16);
+    vb[q] = (uint32_t)((brow(r) - b_first) * ld + c * 16);
+  }
+  const int sr = wave * 64 + lane;  // scale DMA: this lane's row
+  const uint32_t vsa = (uint32_t)((arow(sr) - m0) * lds_), vsb = (uint32_t)((brow(sr) - b_first) * lds_);
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)smem);
+  // this wave's LDS destinations, uniform: its 8 KB blocks of the A and B rows, its 256 bytes of each scale
+  const uint32_t lw = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(wave * kQ * 1024));
+  const uint32_t lws = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(kScaleOff + wave * 256));
+  auto issue = [&](int st) {
+    const uint32_t slot = (uint32_t)((st & 1) * kSlotBytes);
+    const char* ab = a_base + (int64_t)st * kMxRow;
+    const char* bb = b_base + (int64_t)st * kMxRow;
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) ring4::dma(ab, va[q], lw + slot + (uint32_t)(q * 1024));
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) ring4::dma(bb, vb[q], lw + slot + (uint32_t)(kOpBytes + q * 1024));
+    dma4(sa_base + st * 4, vsa, lws + slot);
+    dma4(sb_base + st * 4, vsb, lws + slot + 1024u);
+  };
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // LDS row of B fragment jj of this wave: plain, 32-column tiles of its 128 columns; SwiGLU,
+  // gate fragments (jj = 0, 1) and the matching up fragments (jj = 2, 3) of its 64 columns
+  auto bfrag_row = [&](int jj) -> int {
+    return EPI == EPI_SWIGLU ? (jj >> 1) * 128 + wn * 64 + (jj & 1) * 32 + l32 : wn * 128 + jj * 32 + l32;
+  };
+  const char* L = (const char*)smem;
+  issue(0);
+  for (int st = 0; st < nk; ++st) {
+    if (st + 1 < nk) {
+      issue(st + 1);
+      wait_stage();   // stage st has landed for this wave (the 18 DMAs of stage st + 1 may be in flight)
+    } else {
+      wait_none();
+    }
+    dma_barrier();  // ... and for every wave
+    const char* slot = L + (st & 1) * kSlotBytes;
+    uint32_t wsa[4], wsb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      wsa[i] = *(const uint32_t*)(slot + kScaleOff + (wm * 128 + i * 32 + l32) * 4);
+      wsb[i] = *(const uint32_t*)(slot + kScaleOff + 1024 + bfrag_row(i) * 4);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      // this lane's 16-byte chunks: 4 j + hi (Kd 64 j + 16 hi ..) then 4 j + 2 + hi (64 j + 32 + 16 hi ..).
+      // The MFMA forms an MX block from the same 16-byte half of the two lanes of a row, with the
+      // scale of lane 0 for the first halves and of lane 1 for the second.
+      const int c0 = 4 * j + hi, c1 = 4 * j + 2 + hi;
+      i32x8 a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int ra = wm * 128 + i * 32 + l32, rb = bfrag_row(i);
+        const uint4 a0 = *(const uint4*)(slot + ra * kMxRow + ((c0 ^ ring4::swz(ra)) << 4));
+        const uint4 a1 = *(const uint4*)(slot + ra * kMxRow + ((c1 ^ ring4::swz(ra)) << 4));
+        const uint4 b0 = *(const uint4*)(slot + kOpBytes + rb * kMxRow + ((c0 ^ ring4::swz(rb)) << 4));
+        const uint4 b1 = *(const uint4*)(slot + kOpBytes + rb * kMxRow + ((c1 ^ ring4::swz(rb)) << 4));
+        a[i] = i32x8{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+        b[i] = i32x8{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+      }
+      const int sh = 8 * (2 * j + hi);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          // B first, as mma_rows: each lane ends with one A row and 4 consecutive columns a register
+          // group, the layout the epilogues store
+          acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              b[jj], a[i], acc[i][jj], 0, 0, 0, (int)((wsb[jj] >> sh) & 0xffu), 0, (int)((wsa[i] >> sh) & 0xffu));
+    }
+    __syncthreads();  // every wave is done with this slot before stage st + 2 lands in it
+  }
+  // the ring kernel's epilogue: LDS staging (32 KB a wave of the idle slots), bf16 out
+  const int64_t col0 = EPI == EPI_SWIGLU ? (int64_t)nt * 128 + wn * 64 : (int64_t)nt * 256 + wn * 128;
+  ring4::store_tile_lds<EPI>(p, acc, (char*)smem + wave * 32768, m0 + wm * 128, re, col0);
+}
+
+hipError_t launch_grouped_gemm_mx(const uint8_t* A, const uint8_t* SA, const uint8_t* B, const uint8_t* SB,
+                                  const int32_t* offs, int64_t M, int64_t N, int64_t Kd, int G, int epilogue,
+                                  void* C, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  if ((N + 256) * Kd >= ((int64_t)1 << 32)) return hipErrorInvalidValue;  // per-lane DMA offsets
+  GemmParams prm{A, B, offs, nullptr, nullptr, C, M, N, Kd, G, 0, nullptr, nullptr, 0, 0, 0};
+  prm.sa = SA;
+  prm.sb = SB;
+  prm.NT = (epilogue == EPI_SWIGLU) ? (int)((N / 2 + 127) / 128) : (int)((N + kTile - 1) / kTile);
+  prm.nk = (int)(Kd / mxg::kMxRow);
+  const int64_t max_mt = (M + kTile - 1) / kTile + G;
+  const dim3 grid((unsigned)(max_mt * prm.NT));
+  if (epilogue == EPI_SWIGLU)
+    hipLaunchKernelGGL((grouped_gemm_mx_kernel<EPI_SWIGLU>), grid, dim3(ring4::kThreads), 0, s, prm);
+  else
+    hipLaunchKernelGGL((grouped_gemm_mx_kernel<EPI_NONE>), grid, dim3(ring4::kThreads), 0, s, prm);
+  return hipGetLastError();
 }
 
 hipError_t launch_grouped_gemm(const void* A, const void* B, int b_layout, const int32_t* offs,

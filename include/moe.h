@@ -55,7 +55,7 @@ enum moe_score { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 };
 enum moe_layout { MOE_LAYOUT_NK = 0, MOE_LAYOUT_KN = 1 };
 enum moe_epilogue { MOE_EPI_NONE = 0, MOE_EPI_SWIGLU = 1, MOE_EPI_DSWIGLU = 2 };
 
-#define MOE_ABI_VERSION 4
+#define MOE_ABI_VERSION 5
 #define MOE_MAX_EXPERTS 256
 #define MOE_MAX_TOPK 32
 #define MOE_MAX_GROUPS 1024
@@ -264,6 +264,36 @@ int32_t moe_router_logits_backward(const float* d_logits, const void* x, const v
                                    int64_t d, int32_t E, int32_t dtype, float* d_w_router, void* dx,
                                    int32_t accumulate, void* workspace, size_t workspace_bytes,
                                    moe_stream_t stream);
+
+/*
+ * MXFP8 block quantisation (TE-MoE "Optimisation 1": the grouped GEMM path with
+ * MXFP8 block scaling from grouped quantisation).  The format is the OCP
+ * Microscaling one: each 32 consecutive values of a row share an E8M0 scale
+ * (code c = 2^(c - 127)), each value is an FP8 E4M3 code (bias 7, largest
+ * finite 448, subnormals down to 2^-9).  For each block:
+ *   shared = floor(log2(max |v|)) - 8 clamped to [-127, 127] (a block of zeros: -127)
+ *   scales[r, b] = shared + 127;  codes[r, k] = E4M3(v / 2^shared), nearest even, saturated to +-448
+ *   x      DEVICE [R, K] bf16 (rows along the reduction axis: activations or N-by-K weights)
+ *   codes  DEVICE [R, K] uint8 (written);  scales DEVICE [R, K / 32] uint8 (written)
+ * Requires R >= 0, K >= 32, K % 32 == 0, dtype == MOE_BF16.
+ */
+int32_t moe_mx_quantize(const void* x, int64_t R, int64_t K, int32_t dtype, uint8_t* codes, uint8_t* scales,
+                        moe_stream_t stream);
+
+/*
+ * Grouped GEMM on MXFP8 operands (the MX counterpart of moe_grouped_gemm with
+ * N-by-K weights): group g owns rows [group_offsets[g], group_offsets[g+1]);
+ *   P = A_g . B_g^T on the values the codes and scales represent, fp32 accumulation
+ *   epilogue NONE: C [M, N] = P;  SWIGLU: N = 2F, C [M, F] = silu(P[:, :F]) * P[:, F:];  bf16 out
+ *   A DEVICE [M, Kd] codes, A_scales DEVICE [M, Kd / 32];  B DEVICE [G, N, Kd] codes,
+ *   B_scales DEVICE [G, N, Kd / 32] (as written by moe_mx_quantize)
+ * Requires 0 <= M < 2^31, N >= 8, N % 8 == 0 (SWIGLU: N % 16 == 0), Kd % 128 == 0,
+ * (N + 256) * Kd < 2^32, 1 <= G <= MOE_MAX_GROUPS.  Rows of C outside every group are not
+ * written.
+ */
+int32_t moe_grouped_gemm_mx(const uint8_t* A, const uint8_t* A_scales, const uint8_t* B, const uint8_t* B_scales,
+                            const int32_t* group_offsets, int64_t M, int64_t N, int64_t Kd, int32_t G,
+                            int32_t epilogue, void* C, moe_stream_t stream);
 
 #ifdef __cplusplus
 }

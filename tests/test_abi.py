@@ -29,7 +29,7 @@ def test_header_declares_the_boundary():
     for n in ["moe_route", "moe_permute", "moe_grouped_gemm", "moe_unpermute_combine",
               "moe_grouped_gemm_wgrad", "moe_router_logits", "moe_route_workspace_size",
               "moe_route_backward", "moe_router_logits_backward", "moe_router_backward_workspace_size",
-              "moe_router_route", "moe_router_route_workspace_size",
+              "moe_router_route", "moe_router_route_workspace_size", "moe_mx_quantize", "moe_grouped_gemm_mx",
               "moe_status_str", "moe_abi_version"]:
         assert n in names
 
@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert moe.moe_abi_version() == 4
+    assert moe.moe_abi_version() == 5
     assert moe.status_str(0) == "ok"
     assert "invalid" in moe.status_str(1)
     assert moe.status_str(99) == "unknown status"
@@ -165,3 +165,21 @@ def test_router_route_rejects_bad_arguments(lib):
     assert rr(bias=P + 2) == 1
     assert rr(wsb=0) == 1                 # workspace too small
     assert rr(x=None) == 1
+
+
+def test_mx_rejects_bad_arguments(lib):
+    assert lib.moe_mx_quantize(P, 10, 48, 1, P, P, None) == 1          # K % 32
+    assert lib.moe_mx_quantize(P, 10, 64, 0, P, P, None) == 2          # bf16 input only
+    assert lib.moe_mx_quantize(P + 8, 10, 64, 1, P, P, None) == 1      # misaligned
+    assert lib.moe_mx_quantize(None, 0, 64, 1, None, None, None) == 0  # empty: no launch
+
+    def gm(M=64, N=64, Kd=256, G=2, epi=0, A=P, SA=P):
+        return lib.moe_grouped_gemm_mx(A, SA, P, P, P, M, N, Kd, G, epi, P, None)
+    assert gm(Kd=192) == 1                 # Kd % 128
+    assert gm(epi=2) == 2                  # no SwiGLU-backward epilogue
+    assert gm(epi=1, N=24) == 1            # gate|up halves of 8
+    assert gm(G=0) == 1
+    assert gm(A=P + 4) == 1
+    assert gm(SA=P + 2) == 1
+    assert gm(N=1 << 20, Kd=1 << 13) == 1  # per-lane offsets past 32 bits
+    assert gm(M=0) == 0

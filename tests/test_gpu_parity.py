@@ -238,6 +238,116 @@ def test_router_route_empty_batch():
     assert host(offs).tolist() == [0] * (E + 1)
 
 
+# ----------------------------------------------------------------- MXFP8
+
+def _u8(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def test_mx_quantize_bit_exact():
+    rng = np.random.default_rng(70)
+    R, K = 200, 256
+    v = rng.standard_normal((R, K)) * np.exp2(rng.integers(-20, 20, (R, 1)))
+    v[3, 32:64] = 0.0                                  # a block of zeros
+    v[4, 5] = -0.0
+    v[5, :32] = np.linspace(-1.0, 1.0, 32) * 3.7       # the block maximum saturates at 448 x
+    v[6, :] = rng.standard_normal(K) * 1e-40           # bf16 subnormals
+    v[7, :] = rng.standard_normal(K) * 5e37            # up to about 2e38, below the bf16 maximum
+    x = mi.f32_to_bf16_bits(v.astype(np.float32))
+    codes = torch.full((R, K), 0xAA, dtype=torch.uint8, device="cuda")
+    scales = torch.full((R, K // 32), 0xAA, dtype=torch.uint8, device="cuda")
+    moe.moe_mx_quantize(dev(x), codes, scales)
+    torch.cuda.synchronize()
+    rc, rs = orc.mx_quantize(x)
+    np.testing.assert_array_equal(host(scales), rs)
+    np.testing.assert_array_equal(host(codes), rc)
+
+
+def _mx_operands(rng, rows, K):
+    codes = rng.integers(0, 256, (rows, K)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x38                # no NaN codes
+    scales = rng.integers(120, 135, (rows, K // 32)).astype(np.uint8)
+    return codes, scales
+
+
+@pytest.mark.parametrize("counts,N,Kd,epi", [
+    ([300, 0, 257, 40], 256, 256, 0),      # ragged groups, an empty one, one row tile tail
+    ([513], 512, 128, 0),                  # one stage
+    ([100, 200], 264, 512, 0),             # a column tile past N
+    ([130, 0, 70, 256], 512, 384, 1),      # SwiGLU epilogue, three stages
+    ([1, 2, 3], 64, 128, 1),               # tiny groups, N below one tile
+])
+def test_grouped_gemm_mx_parity(counts, N, Kd, epi):
+    rng = np.random.default_rng(sum(counts) + N + Kd + epi)
+    G, M = len(counts), sum(counts)
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    ac, asc = _mx_operands(rng, M, Kd)
+    bc, bsc = _mx_operands(rng, G * N, Kd)
+    Nout = N // 2 if epi == 1 else N
+    C = torch.full((M, Nout), float("nan"), dtype=torch.bfloat16, device="cuda")
+    moe.moe_grouped_gemm_mx(_u8(ac), _u8(asc), _u8(bc.reshape(G, N, Kd)), _u8(bsc.reshape(G, N, Kd // 32)),
+                            dev(offs), C, epilogue=epi)
+    torch.cuda.synchronize()
+    p = orc.grouped_gemm_mx(ac, asc, bc.reshape(G, N, Kd), bsc.reshape(G, N, Kd // 32), offs.astype(np.int64))
+    ad = orc.mx_dequantize(ac, asc)
+    bd = orc.mx_dequantize(bc, bsc).reshape(G, N, Kd)
+    scale = orc.grouped_gemm(np.abs(ad), np.abs(bd), offs.astype(np.int64), "nk")
+    got = orc.to_f64(host(C))
+    # The MX MFMA adds the products of a 64-value step with less than fp32 precision: measured at
+    # up to 1.5e-4 of sum |a b| for Kd of 256 to 4096, not growing with Kd.  Allowed: 3e-4 of it,
+    # then the bf16 rounding of the result (half a unit in the last place, 2^-8 relative).
+    acc_tol = 3e-4
+    if epi == 1:
+        F = N // 2
+        ref = orc.swiglu(p)
+        # h = silu(g) u: |dh| <= 1.1 |u| |dg| + (|g| + 1) |du|
+        tol = 2.0 ** -8 * np.abs(ref) + acc_tol * (1.1 * scale[:, :F] * np.abs(p[:, F:]) + scale[:, F:] * (np.abs(p[:, :F]) + 1))
+    else:
+        ref = p
+        tol = 2.0 ** -8 * np.abs(ref) + acc_tol * scale
+    assert np.all(np.abs(got - ref) <= tol + 1e-30), float(np.nanmax(np.abs(got - ref) - tol))
+
+
+def test_mx_gate_up_mixtral_shape_sampled():
+    """GPU quantisation of X_perm-sized activations and W13-sized weights, then the MX gate/up
+    GEMM with SwiGLU at the Mixtral-shaped sizes; sampled rows against the oracle."""
+    cfg = mi.CONFIGS["mixtral"]
+    M, d, F, E = cfg.T * cfg.K, cfg.d, cfg.F, cfg.E
+    g = torch.Generator(device="cuda").manual_seed(71)
+    x = torch.randn(M, d, device="cuda", generator=g).bfloat16()
+    w = (torch.randn(E, 2 * F, d, device="cuda", generator=g) / 64).bfloat16()
+    counts = np.array([2172, 2091, 2066, 2041, 2030, 2017, 1991, 1976])
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    xc = torch.empty(M, d, dtype=torch.uint8, device="cuda")
+    xs = torch.empty(M, d // 32, dtype=torch.uint8, device="cuda")
+    wc = torch.empty(E, 2 * F, d, dtype=torch.uint8, device="cuda")
+    ws = torch.empty(E, 2 * F, d // 32, dtype=torch.uint8, device="cuda")
+    moe.moe_mx_quantize(x, xc, xs)
+    moe.moe_mx_quantize(w.view(E * 2 * F, d), wc.view(E * 2 * F, d), ws.view(E * 2 * F, d // 32))
+    H = torch.empty(M, F, dtype=torch.bfloat16, device="cuda")
+    moe.moe_grouped_gemm_mx(xc, xs, wc, ws, dev(offs), H, epilogue=moe.MOE_EPI_SWIGLU)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(72)
+    rows = np.sort(rng.choice(M, 24, replace=False))
+    # the quantisation of the sampled rows is the oracle's
+    xr = host(x[torch.as_tensor(rows, device="cuda")])
+    rc, rs = orc.mx_quantize(xr)
+    np.testing.assert_array_equal(host(xc[torch.as_tensor(rows, device="cuda")]), rc)
+    np.testing.assert_array_equal(host(xs[torch.as_tensor(rows, device="cuda")]), rs)
+    # and each sampled row of H against the fp64 product of the MX values of its expert
+    wcd, wsd = host(wc), host(ws)
+    hs = orc.to_f64(host(H[torch.as_tensor(rows, device="cuda")]))
+    a = orc.mx_dequantize(rc, rs)
+    for n, r in enumerate(rows):
+        e = int(np.searchsorted(offs, r, side="right") - 1)
+        b = orc.mx_dequantize(wcd[e], wsd[e])                # [2F, d]
+        pre = b @ a[n]
+        ref = orc.swiglu(pre[None, :])[0]
+        sc = np.abs(b) @ np.abs(a[n])
+        tol = 2.0 ** -8 * np.abs(ref) + 3e-4 * (1.1 * sc[:F] * np.abs(pre[F:]) + sc[F:] * (np.abs(pre[:F]) + 1))
+        assert np.all(np.abs(hs[n] - ref) <= tol), (int(r), float(np.max(np.abs(hs[n] - ref) - tol)))
+
+
 # ----------------------------------------------------------------- router backward
 
 def _route_bwd_case(T, E, K, score, renorm, seed, bias=None):
