@@ -28,6 +28,7 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3       # MI355X fp32 (matrix)
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA (MX formats included)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 
 
@@ -45,6 +46,9 @@ def parse():
     ap.add_argument("--backward", action="store_true",
                     help="time the backward of the adversarial-skew Mixtral-shaped workload instead "
                          "(reported as an extra line, not the headline)")
+    ap.add_argument("--mxfp8", action="store_true",
+                    help="time the layer forward with MXFP8 expert GEMMs instead (weights quantised once "
+                         "before the timed region, activations quantised inside every step)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain elementwise pass over 512 MiB (3 launches of torch's neg "
                          "kernel: 512 MiB read, 512 MiB written) to calibrate rocprofv3 FETCH_SIZE / WRITE_SIZE")
@@ -167,6 +171,8 @@ def main():
 
     if args.backward:
         return bench_backward(args, torch, moe, mi)
+    if args.mxfp8:
+        return bench_mxfp8(args, torch, moe, mi)
     cfg = mi.CONFIGS[args.workload]
     torch.cuda.set_device(0)
     t_gen = time.perf_counter()
@@ -410,6 +416,102 @@ def bench_backward(args, torch, moe, mi):
            # product's x read for dWr plus dX read and written for its share (3 T d b)
            "router_bwd_gbs": {"route_bwd": 8.0 * cfg.T * cfg.E / (kms["route_bwd"] * 1e-3) / 1e9,
                               "router_bwd": 3.0 * cfg.T * cfg.d * 2 / (kms["router_bwd"] * 1e-3) / 1e9}}
+    print(json.dumps(out), flush=True)
+
+
+def bench_mxfp8(args, torch, moe, mi):
+    """The bf16 layer forward with both expert GEMMs on MXFP8 operands: the routed tokens and H
+    are quantised (32-value blocks, E8M0 scales, E4M3 values) inside every step; the weights
+    once, before the timed region, as stored MX weights would be."""
+    cfg = mi.CONFIGS[args.workload]
+    if not cfg.bf16:
+        raise SystemExit("--mxfp8 needs a bf16 workload")
+    torch.cuda.set_device(0)
+    inp = mi.make(cfg)
+    x, wr, b = to_dev(inp["x"], torch), to_dev(inp["w_router"], torch), to_dev(inp["bias"], torch)
+    w13, w2 = to_dev(inp["w13"], torch), to_dev(inp["w2"], torch)
+    E, d, F, K, T = cfg.E, cfg.d, cfg.F, cfg.K, cfg.T
+    M = T * K
+    bufs = moe.MoEBuffers(T, d, E, K, F, torch.bfloat16)
+    u8 = dict(dtype=torch.uint8, device="cuda")
+    w13c, w13s = torch.empty(E, 2 * F, d, **u8), torch.empty(E, 2 * F, d // 32, **u8)
+    w2c, w2s = torch.empty(E, d, F, **u8), torch.empty(E, d, F // 32, **u8)
+    moe.moe_mx_quantize(w13.view(E * 2 * F, d), w13c.view(E * 2 * F, d), w13s.view(E * 2 * F, d // 32))
+    moe.moe_mx_quantize(w2.view(E * d, F), w2c.view(E * d, F), w2s.view(E * d, F // 32))
+    del w13, w2
+    xq, xs = torch.empty(M, d, **u8), torch.empty(M, d // 32, **u8)
+    hq, hs = torch.empty(M, F, **u8), torch.empty(M, F // 32, **u8)
+    rr_ws = torch.empty((max(moe.moe_router_route_workspace_size(T, E), 256),), **u8)
+    stream = torch.cuda.current_stream()
+    names = ["router_route", "permute", "quantize_x", "gemm_gate_up", "quantize_h", "gemm_down", "combine"]
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record(stream)
+        mark(0)
+        moe.moe_router_route(x, wr, b, K, cfg.score, cfg.renorm, None, bufs.topk_idx, bufs.gates, bufs.counts,
+                             bufs.offsets, bufs.slot_pos, bufs.row_src, rr_ws)
+        mark(1)
+        moe.moe_permute(x, K, bufs.slot_pos, bufs.x_perm)
+        mark(2)
+        moe.moe_mx_quantize(bufs.x_perm, xq, xs)
+        mark(3)
+        moe.moe_grouped_gemm_mx(xq, xs, w13c, w13s, bufs.offsets, bufs.h, moe.MOE_EPI_SWIGLU)
+        mark(4)
+        moe.moe_mx_quantize(bufs.h, hq, hs)
+        mark(5)
+        moe.moe_grouped_gemm_mx(hq, hs, w2c, w2s, bufs.offsets, bufs.y_perm, moe.MOE_EPI_NONE)
+        mark(6)
+        moe.moe_unpermute_combine(bufs.y_perm, bufs.slot_pos, bufs.gates, T, K, bufs.y)
+        mark(7)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(max(args.warmup, 1)):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / max(args.steps, 1)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    per = np.zeros(len(names))
+    for ev in evs:
+        per += np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(len(names))])
+    per /= max(args.steps, 1)
+    kms = dict(zip(names, per.tolist()))
+    fl_up, fl_down = 2.0 * M * 2 * F * d, 2.0 * M * F * d
+    tf_up = fl_up / (kms["gemm_gate_up"] * 1e-3) / 1e12
+    tf_down = fl_down / (kms["gemm_down"] * 1e-3) / 1e12
+    out = {"metric": "MoE layer forward tokens/s, MXFP8 expert GEMMs (weights quantised once)",
+           "value": T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "mxfp8",
+           "data": "synthetic (seeded N(0,1) tokens, random-init router and SwiGLU experts)",
+           "config": {"workload": cfg.name, "tokens": T, "d_model": d, "experts": E, "top_k": K, "ffn": F,
+                      "parallelism": "single GPU"},
+           "grouped_gemm": {"gate_up_tflops": tf_up, "down_tflops": tf_down,
+                            "tflops": (fl_up + fl_down) / ((kms["gemm_gate_up"] + kms["gemm_down"]) * 1e-3) / 1e12},
+           "kernels_ms": kms,
+           "quantize_gbs": {"x": (M * d * 3 + M * d // 32) / (kms["quantize_x"] * 1e-3) / 1e9,
+                            "h": (M * F * 3 + M * F // 32) / (kms["quantize_h"] * 1e-3) / 1e9},
+           "roofline": {"kernel": "MXFP8 grouped GEMM gate/up + SwiGLU", "bound": "mfma", "achieved": tf_up,
+                        "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": tf_up / PEAK_FP8_TFLOPS, "traffic": None},
+           "cpu_baseline": None}
     print(json.dumps(out), flush=True)
 
 
