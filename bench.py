@@ -420,9 +420,9 @@ def bench_backward(args, torch, moe, mi):
 
 
 def bench_mxfp8(args, torch, moe, mi):
-    """The bf16 layer forward with both expert GEMMs on MXFP8 operands: the routed tokens and H
-    are quantised (32-value blocks, E8M0 scales, E4M3 values) inside every step; the weights
-    once, before the timed region, as stored MX weights would be."""
+    """The bf16 layer forward with both expert GEMMs on MXFP8 operands: the tokens (then their
+    codes are permuted) and H are quantised (32-value blocks, E8M0 scales, E4M3 values) inside
+    every step; the weights once, before the timed region, as stored MX weights would be."""
     cfg = mi.CONFIGS[args.workload]
     if not cfg.bf16:
         raise SystemExit("--mxfp8 needs a bf16 workload")
@@ -439,11 +439,12 @@ def bench_mxfp8(args, torch, moe, mi):
     moe.moe_mx_quantize(w13.view(E * 2 * F, d), w13c.view(E * 2 * F, d), w13s.view(E * 2 * F, d // 32))
     moe.moe_mx_quantize(w2.view(E * d, F), w2c.view(E * d, F), w2s.view(E * d, F // 32))
     del w13, w2
+    tq, ts = torch.empty(T, d, **u8), torch.empty(T, d // 32, **u8)
     xq, xs = torch.empty(M, d, **u8), torch.empty(M, d // 32, **u8)
     hq, hs = torch.empty(M, F, **u8), torch.empty(M, F // 32, **u8)
     rr_ws = torch.empty((max(moe.moe_router_route_workspace_size(T, E), 256),), **u8)
     stream = torch.cuda.current_stream()
-    names = ["router_route", "permute", "quantize_x", "gemm_gate_up", "quantize_h", "gemm_down", "combine"]
+    names = ["router_route", "quantize_x", "permute", "gemm_gate_up", "quantize_h", "gemm_down", "combine"]
 
     def step(ev=None):
         def mark(i):
@@ -453,9 +454,9 @@ def bench_mxfp8(args, torch, moe, mi):
         moe.moe_router_route(x, wr, b, K, cfg.score, cfg.renorm, None, bufs.topk_idx, bufs.gates, bufs.counts,
                              bufs.offsets, bufs.slot_pos, bufs.row_src, rr_ws)
         mark(1)
-        moe.moe_permute(x, K, bufs.slot_pos, bufs.x_perm)
+        moe.moe_mx_quantize(x, tq, ts)
         mark(2)
-        moe.moe_mx_quantize(bufs.x_perm, xq, xs)
+        moe.moe_permute_mx(tq, ts, K, bufs.slot_pos, xq, xs)
         mark(3)
         moe.moe_grouped_gemm_mx(xq, xs, w13c, w13s, bufs.offsets, bufs.h, moe.MOE_EPI_SWIGLU)
         mark(4)
@@ -507,7 +508,7 @@ def bench_mxfp8(args, torch, moe, mi):
            "grouped_gemm": {"gate_up_tflops": tf_up, "down_tflops": tf_down,
                             "tflops": (fl_up + fl_down) / ((kms["gemm_gate_up"] + kms["gemm_down"]) * 1e-3) / 1e12},
            "kernels_ms": kms,
-           "quantize_gbs": {"x": (M * d * 3 + M * d // 32) / (kms["quantize_x"] * 1e-3) / 1e9,
+           "quantize_gbs": {"x": (T * d * 3 + T * d // 32) / (kms["quantize_x"] * 1e-3) / 1e9,
                             "h": (M * F * 3 + M * F // 32) / (kms["quantize_h"] * 1e-3) / 1e9},
            "roofline": {"kernel": "MXFP8 grouped GEMM gate/up + SwiGLU", "bound": "mfma", "achieved": tf_up,
                         "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": tf_up / PEAK_FP8_TFLOPS, "traffic": None},

@@ -39,6 +39,7 @@ SIGNATURES = {
     "moe_router_route_workspace_size": (_I32, [_I64, _I32, _c.POINTER(_SZ)]),
     "moe_router_route": (_I32, [_P, _P, _P, _I64, _I64, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P,
                                 _P, _SZ, _P]),
+    "moe_permute_mx": (_I32, [_P, _P, _I64, _I64, _I32, _P, _P, _P, _P]),
     "moe_mx_quantize": (_I32, [_P, _I64, _I64, _I32, _P, _P, _P]),
     "moe_grouped_gemm_mx": (_I32, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _P, _P]),
     "moe_route_backward": (_I32, [_P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _P, _P]),
@@ -232,6 +233,13 @@ def moe_grouped_gemm_mx(A, A_scales, B, B_scales, group_offsets, C, epilogue: in
     G, N = B.shape[0], B.shape[1]
     _call("moe_grouped_gemm_mx", _ptr(A), _ptr(A_scales), _ptr(B), _ptr(B_scales), _ptr(group_offsets), M, N, Kd,
           G, epilogue, _ptr(C), _stream(stream))
+
+
+def moe_permute_mx(codes, scales, K: int, slot_pos, codes_perm, scales_perm, stream=None) -> None:
+    """Row permute of MXFP8 codes [T, d] and scales [T, d / 32] into expert-contiguous order."""
+    T, d = codes.shape
+    _call("moe_permute_mx", _ptr(codes), _ptr(scales), T, d, K, _ptr(slot_pos), _ptr(codes_perm), _ptr(scales_perm),
+          _stream(stream))
 
 
 from .layer import MoEBuffers, layer_backward, layer_forward  # noqa: E402,F401

@@ -62,6 +62,10 @@ hipError_t launch_router_logits_backward(const float* d_logits, const void* x, c
                                          int64_t d, int E, int dtype, float* d_w, void* dx, int accumulate,
                                          void* ws, hipStream_t s);
 
+// row copy of the permute over rows of row_bytes bytes (a multiple of 16): MXFP8 codes and scales
+hipError_t launch_permute_rows(const void* x, int64_t T, int64_t row_bytes, int K, const int32_t* slot_pos,
+                               void* x_perm, hipStream_t s);
+
 // MXFP8: block quantisation (bf16 rows, 32-value blocks) and the grouped GEMM on MX operands
 hipError_t launch_mx_quantize(const void* x, int64_t R, int64_t K, uint8_t* codes, uint8_t* scales, hipStream_t s);
 hipError_t launch_grouped_gemm_mx(const uint8_t* A, const uint8_t* SA, const uint8_t* B, const uint8_t* SB,

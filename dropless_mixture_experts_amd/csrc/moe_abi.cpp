@@ -229,4 +229,17 @@ int32_t moe_grouped_gemm_mx(const uint8_t* A, const uint8_t* A_scales, const uin
                                               (hipStream_t)stream));
 }
 
+int32_t moe_permute_mx(const uint8_t* codes, const uint8_t* scales, int64_t T, int64_t d, int32_t K,
+                       const int32_t* slot_pos, uint8_t* codes_perm, uint8_t* scales_perm, moe_stream_t stream) {
+  if (T < 0 || d < 512 || d % 512 != 0 || K < 1 || K > MOE_MAX_TOPK) return MOE_INVALID_ARG;
+  if (T * (int64_t)K >= ((int64_t)1 << 31)) return MOE_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!codes || !scales || !slot_pos || !codes_perm || !scales_perm) return MOE_INVALID_ARG;
+  if (!aligned16(codes) || !aligned16(scales) || !aligned16(codes_perm) || !aligned16(scales_perm))
+    return MOE_INVALID_ARG;
+  const hipError_t e = moe::launch_permute_rows(codes, T, d, K, slot_pos, codes_perm, (hipStream_t)stream);
+  if (e != hipSuccess) return MOE_HIP_ERROR;
+  return from_hip(moe::launch_permute_rows(scales, T, d / 32, K, slot_pos, scales_perm, (hipStream_t)stream));
+}
+
 }  // extern "C"

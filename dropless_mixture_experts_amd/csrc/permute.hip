@@ -229,6 +229,17 @@ hipError_t launch_permute(const void* x, int64_t T, int64_t d, int K, int dtype,
   return permute_t<float>(x, T, d, K, slot_pos, row_scale, y_perm_dot, dgate_out, x_perm, s);
 }
 
+// Permute of MXFP8 rows: the same row copy as the plain permute, over rows of `row_bytes`
+// bytes (a multiple of 16) of codes, then of scales.
+hipError_t launch_permute_rows(const void* x, int64_t T, int64_t row_bytes, int K, const int32_t* slot_pos,
+                               void* x_perm, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const dim3 grid((unsigned)((T + kRowsPerBlock - 1) / kRowsPerBlock));
+  hipLaunchKernelGGL((permute_kernel<bf16_t, false, false>), grid, dim3(256), 0, s, (const uint4*)x, row_bytes / 16,
+                     K, slot_pos, nullptr, nullptr, nullptr, (uint4*)x_perm, T);
+  return hipGetLastError();
+}
+
 hipError_t launch_combine(const void* y_perm, const int32_t* slot_pos, const float* gates, int64_t T,
                           int64_t d, int K, int dtype, void* y, hipStream_t s) {
   if (dtype == 1) return combine_t<bf16_t>(y_perm, slot_pos, gates, T, d, K, y, s);

@@ -55,7 +55,7 @@ enum moe_score { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 };
 enum moe_layout { MOE_LAYOUT_NK = 0, MOE_LAYOUT_KN = 1 };
 enum moe_epilogue { MOE_EPI_NONE = 0, MOE_EPI_SWIGLU = 1, MOE_EPI_DSWIGLU = 2 };
 
-#define MOE_ABI_VERSION 5
+#define MOE_ABI_VERSION 6
 #define MOE_MAX_EXPERTS 256
 #define MOE_MAX_TOPK 32
 #define MOE_MAX_GROUPS 1024
@@ -294,6 +294,18 @@ int32_t moe_mx_quantize(const void* x, int64_t R, int64_t K, int32_t dtype, uint
 int32_t moe_grouped_gemm_mx(const uint8_t* A, const uint8_t* A_scales, const uint8_t* B, const uint8_t* B_scales,
                             const int32_t* group_offsets, int64_t M, int64_t N, int64_t Kd, int32_t G,
                             int32_t epilogue, void* C, moe_stream_t stream);
+
+/*
+ * Permute of MXFP8 rows (S4 on quantised tokens): codes_perm[slot_pos[s]] = codes[s / K] and
+ * scales_perm[slot_pos[s]] = scales[s / K], bit copies.  Quantising the T tokens once
+ * (moe_mx_quantize) and permuting the codes gives the same bytes as quantising the T*K
+ * routed rows, with an eighth of the quantisation work at K = 8 and half the permute bytes.
+ *   codes DEVICE [T, d] uint8, scales DEVICE [T, d / 32] uint8
+ *   codes_perm DEVICE [T*K, d] uint8, scales_perm DEVICE [T*K, d / 32] uint8 (written)
+ * Requires d % 512 == 0 (whole 16-byte rows of scales), 1 <= K <= MOE_MAX_TOPK, T*K < 2^31.
+ */
+int32_t moe_permute_mx(const uint8_t* codes, const uint8_t* scales, int64_t T, int64_t d, int32_t K,
+                       const int32_t* slot_pos, uint8_t* codes_perm, uint8_t* scales_perm, moe_stream_t stream);
 
 #ifdef __cplusplus
 }

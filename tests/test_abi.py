@@ -30,6 +30,7 @@ def test_header_declares_the_boundary():
               "moe_grouped_gemm_wgrad", "moe_router_logits", "moe_route_workspace_size",
               "moe_route_backward", "moe_router_logits_backward", "moe_router_backward_workspace_size",
               "moe_router_route", "moe_router_route_workspace_size", "moe_mx_quantize", "moe_grouped_gemm_mx",
+              "moe_permute_mx",
               "moe_status_str", "moe_abi_version"]:
         assert n in names
 
@@ -44,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert moe.moe_abi_version() == 5
+    assert moe.moe_abi_version() == 6
     assert moe.status_str(0) == "ok"
     assert "invalid" in moe.status_str(1)
     assert moe.status_str(99) == "unknown status"
@@ -183,3 +184,6 @@ def test_mx_rejects_bad_arguments(lib):
     assert gm(SA=P + 2) == 1
     assert gm(N=1 << 20, Kd=1 << 13) == 1  # per-lane offsets past 32 bits
     assert gm(M=0) == 0
+    assert lib.moe_permute_mx(P, P, 10, 256, 2, P, P, P, None) == 1        # d % 512
+    assert lib.moe_permute_mx(P, P + 4, 10, 512, 2, P, P, P, None) == 1    # misaligned scales
+    assert lib.moe_permute_mx(None, None, 0, 512, 2, None, None, None, None) == 0

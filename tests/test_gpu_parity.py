@@ -263,6 +263,27 @@ def test_mx_quantize_bit_exact():
     np.testing.assert_array_equal(host(codes), rc)
 
 
+def test_permute_mx_equals_quantised_permute():
+    """Quantise then permute the codes == permute then quantise the rows (bit for bit)."""
+    rng = np.random.default_rng(73)
+    T, d, K, E = 333, 1024, 4, 16
+    x = torch.from_numpy(rng.standard_normal((T, d)).astype(np.float32)).cuda().bfloat16()
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    r = orc.route(logits, None, K)
+    pos = dev(r.slot_pos.astype(np.int32))
+    u8 = dict(dtype=torch.uint8, device="cuda")
+    xc, xs = torch.empty(T, d, **u8), torch.empty(T, d // 32, **u8)
+    moe.moe_mx_quantize(x, xc, xs)
+    pc, ps = torch.full((T * K, d), 7, **u8), torch.full((T * K, d // 32), 7, **u8)
+    moe.moe_permute_mx(xc, xs, K, pos, pc, ps)
+    xp = torch.empty(T * K, d, dtype=torch.bfloat16, device="cuda")
+    moe.moe_permute(x, K, pos, xp)
+    qc, qs = torch.empty(T * K, d, **u8), torch.empty(T * K, d // 32, **u8)
+    moe.moe_mx_quantize(xp, qc, qs)
+    torch.cuda.synchronize()
+    assert torch.equal(pc, qc) and torch.equal(ps, qs)
+
+
 def _mx_operands(rng, rows, K):
     codes = rng.integers(0, 256, (rows, K)).astype(np.uint8)
     codes[(codes & 0x7F) == 0x7F] = 0x38                # no NaN codes
