@@ -1612,6 +1612,7 @@ void grouped_gemm_ring4_kernel(GemmParams p) {
 // ---------------------------------------------------------------------------
 // dW[g] = dY_g^T X_g: output tile (n, kd) of group g, reduction over the group's rows.
 constexpr int kMaxGroupsWg = 1024;  // group sizes the ring weight-gradient kernel sorts in LDS
+constexpr int kWgBand = 4;          // column tiles of X in a band of the weight-gradient tile order
 
 struct WgradParams {
   const void* X;
@@ -1800,8 +1801,8 @@ __device__ __forceinline__ void store_wgrad_lds(float* out, const f32x16 (&acc)[
 }
 
 // Weight gradient on the ring pipeline: dW_g[n0:n0+256, k0:k0+256] = dY_g^T X_g over the
-// group's rows, 64 rows a stage (the last one zero-filled past the group's end).  Tiles are
-// ordered as in the eight-wave kernel: groups by decreasing size, column tiles of X adjacent.
+// group's rows, 64 rows a stage (the last one zero-filled past the group's end).  Groups are
+// taken by decreasing size; within a group the tiles go in bands of column tiles of X.
 __global__ __launch_bounds__(ring4::kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void grouped_wgrad_ring_kernel(WgradParams p) {
   using namespace ring4;
@@ -1834,9 +1835,15 @@ void grouped_wgrad_ring_kernel(WgradParams p) {
   __syncthreads();
   const int g = __builtin_amdgcn_readfirstlane(s_group[0]);
   __syncthreads();  // every thread has read the scratch before the loads overwrite it
+  // Bands of kWgBand column tiles of X, the tiles of a band in column-major order: the 32
+  // consecutive tiles one XCD runs together cover 4 column tiles of X by 8 of dY, so its L2
+  // streams 12 operand panels a stage instead of 33 with a row of 32 dY tiles.
   const int rem = (int)(L - (int64_t)rank * tpg);
-  const int tk = rem / p.TN;  // neighbouring tiles share the same X columns
-  const int tn = rem % p.TN;
+  const int band = rem / (kWgBand * p.TN);
+  const int h = min(kWgBand, p.TK - band * kWgBand);
+  const int w = rem - band * kWgBand * p.TN;
+  const int tk = band * kWgBand + w % h;
+  const int tn = w / h;
   int64_t rs, re;
   group_rows(p.offs, g, p.M, rs, re);
   rs = uniform64(rs);
