@@ -1931,7 +1931,8 @@ size_t grouped_gemm_workspace_bytes() {
 // one E8M0 scale per 32 consecutive Kd values of a row; C = A_g . B_g^T in fp32, bf16 out
 // (plain or SwiGLU epilogue).  256 x 256 tiles in the grouped order of find_tile, 4 waves of
 // 128 x 128.  A stage is 128 Kd values (128 bytes a row) of both operands plus their 4 scale
-// bytes a row, moved by LDS DMA into one of two 66 KB slots while the other is read.  The
+// bytes a row, moved by LDS DMA into one of two 66 KB slots while the other is read (one
+// barrier a stage: it publishes the stage and frees the slot the next one loads into).  The
 // MFMA v_mfma_scale_f32_32x32x64_f8f6f4 takes 32 bytes a lane for 64 Kd values of a row
 // split over two lanes (hi = 0, 1); the hardware applies lane hi's scale byte to bytes
 // 16 hi .. 16 hi + 15 of both lanes.  So lane hi holds Kd values 64 j + 16 hi .. + 15 (block
@@ -1943,13 +1944,11 @@ constexpr int kOpBytes = 256 * kMxRow;          // 32 KB: one operand's rows of 
 constexpr int kScaleOff = 2 * kOpBytes;            // then 256 scale words of A, 256 of B
 constexpr int kSlotBytes = 2 * kOpBytes + 2 * 1024;
 constexpr int kQ = 8;                              // row DMAs of one operand per wave per stage
-constexpr int kNQ = 2 * kQ + 2;                    // DMAs per wave per stage (rows, then scales)
 
 __device__ __forceinline__ void dma4(const char* sbase, uint32_t voff, uint32_t lds_byte) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1 offset:0"
                :: "v"(voff), "s"(sbase), "s"(lds_byte) : "memory", "m0");
 }
-__device__ __forceinline__ void wait_stage() { asm volatile("s_waitcnt vmcnt(18) lgkmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void wait_none() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory"); }
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
@@ -1959,7 +1958,6 @@ template <int EPI>
 __global__ __launch_bounds__(ring4::kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void grouped_gemm_mx_kernel(GemmParams p) {
   using namespace mxg;
-  static_assert(kNQ == 18, "the stage wait counts 18 DMAs a wave");
   __shared__ uint4 smem[2 * kSlotBytes / 16];
   int g, nt;
   int64_t m0, re;
@@ -2042,13 +2040,9 @@ void grouped_gemm_mx_kernel(GemmParams p) {
   const char* L = (const char*)smem;
   issue(0);
   for (int st = 0; st < nk; ++st) {
-    if (st + 1 < nk) {
-      issue(st + 1);
-      wait_stage();   // stage st has landed for this wave (the 18 DMAs of stage st + 1 may be in flight)
-    } else {
-      wait_none();
-    }
-    dma_barrier();  // ... and for every wave
+    wait_none();    // stage st has landed for this wave
+    dma_barrier();  // ... and for every wave, which are all done with stage st - 1
+    if (st + 1 < nk) issue(st + 1);  // into the slot stage st - 1 used
     const char* slot = L + (st & 1) * kSlotBytes;
     uint32_t wsa[4], wsb[4];
 #pragma unroll
@@ -2083,8 +2077,8 @@ void grouped_gemm_mx_kernel(GemmParams p) {
           acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
               b[jj], a[i], acc[i][jj], 0, 0, 0, (int)((wsb[jj] >> sh) & 0xffu), 0, (int)((wsa[i] >> sh) & 0xffu));
     }
-    __syncthreads();  // every wave is done with this slot before stage st + 2 lands in it
   }
+  __syncthreads();  // every wave is done with the slots: they hold the epilogue staging now
   // the ring kernel's epilogue: LDS staging (32 KB a wave of the idle slots), bf16 out
   const int64_t col0 = EPI == EPI_SWIGLU ? (int64_t)nt * 128 + wn * 64 : (int64_t)nt * 256 + wn * 128;
   ring4::store_tile_lds<EPI>(p, acc, (char*)smem + wave * 32768, m0 + wm * 128, re, col0);
