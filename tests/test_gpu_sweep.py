@@ -1,0 +1,157 @@
+"""GPU parity over seeded random shapes of the grouped GEMM paths the layer uses: the N-by-K
+ring (plain and SwiGLU), the K-by-N ring (plain and SwiGLU backward), and the weight gradient,
+against the CPU oracle.  Each case draws a group count, ragged group sizes with empty and
+dominant groups, widths and reduction lengths spanning several tiles with ragged tails, rows
+outside the groups, and whether a workspace (the split tail) is passed.  Bars as in the other
+parity tests: relative Frobenius error within 2e-2 / 4 over the groups' rows, 2e-2 row by row,
+rows outside the groups untouched, empty groups' weight gradients exactly zero.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs as mi
+import oracle as orc
+from tests.gpu_util import TOL_BF16, dev, empty_like_poisoned, f64, rel_err
+
+pytestmark = pytest.mark.gpu
+moe = pytest.importorskip("dropless_mixture_experts_amd")
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    moe.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+def _counts(rng, G, mean):
+    """Ragged group sizes: a quarter of the groups empty, one group dominant, the rest spread."""
+    c = rng.integers(0, 2 * mean + 1, size=G)
+    c[rng.random(G) < 0.25] = 0
+    c[rng.integers(G)] += int(rng.integers(mean, 4 * mean + 1))
+    return c
+
+
+def _case(seed, N, Kd, mean, gmax=24):
+    rng = np.random.default_rng(seed)
+    G = int(rng.integers(1, gmax + 1))
+    counts = _counts(rng, G, mean)
+    lead, tail = int(rng.integers(0, 9)), int(rng.integers(0, 9))
+    off = lead + np.concatenate([[0], np.cumsum(counts)])
+    M = int(off[-1]) + tail
+    A = mi.f32_to_bf16_bits(rng.standard_normal((M, Kd)).astype(np.float32))
+    W = mi.f32_to_bf16_bits((rng.standard_normal((G, N, Kd)) / math.sqrt(Kd)).astype(np.float32))
+    use_ws = bool(rng.integers(2))
+    return rng, A, W, off, M, use_ws
+
+
+def _check_rows(C, off, M, ref):
+    c = f64(C)
+    lo, hi = int(off[0]), int(off[-1])
+    assert np.all(np.isnan(c[:lo])) and np.all(np.isnan(c[hi:M])), "rows outside the groups written"
+    got = c[lo:hi]
+    assert not np.any(np.isnan(got))
+    if hi > lo:
+        assert rel_err(got, ref) < TOL_BF16 / 4
+        row = np.linalg.norm(got - ref, axis=1) / np.maximum(np.linalg.norm(ref, axis=1), 1e-30)
+        assert row.max() < TOL_BF16
+
+
+def _workspace(use):
+    if not use:
+        return None
+    return torch.zeros((moe.moe_grouped_gemm_workspace_size(),), dtype=torch.uint8, device="cuda")
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_sweep_nk_plain(seed):
+    rng0 = np.random.default_rng(1000 + 500 + seed)
+    N = 8 * int(rng0.integers(1, 97))          # 8 .. 768
+    Kd = 64 * int(rng0.integers(1, 13))        # 64 .. 768: whole ring stages
+    _, A, W, off, M, use_ws = _case(1000 + seed, N, Kd, mean=200)
+    C = empty_like_poisoned((M, N), torch.bfloat16)
+    ws = _workspace(use_ws)
+    moe.moe_grouped_gemm(dev(A), dev(W), 0, dev(off), C, workspace=ws)
+    torch.cuda.synchronize()
+    if ws is not None:
+        assert torch.count_nonzero(ws[:4096]).item() == 0
+    lo = int(off[0])
+    _check_rows(C, off, M, orc.grouped_gemm(A[lo:int(off[-1])], W, off - lo, "nk"))
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_sweep_nk_swiglu(seed):
+    rng0 = np.random.default_rng(2000 + 500 + seed)
+    F = 8 * int(rng0.integers(1, 65))          # 8 .. 512
+    Kd = 64 * int(rng0.integers(1, 13))
+    _, A, W, off, M, use_ws = _case(2000 + seed, 2 * F, Kd, mean=200)
+    H = empty_like_poisoned((M, F), torch.bfloat16)
+    P = empty_like_poisoned((M, 2 * F), torch.bfloat16)
+    moe.moe_grouped_gemm(dev(A), dev(W), 0, dev(off), H, moe.MOE_EPI_SWIGLU, epi_save=P,
+                         workspace=_workspace(use_ws))
+    torch.cuda.synchronize()
+    lo = int(off[0])
+    pre = orc.grouped_gemm(A[lo:int(off[-1])], W, off - lo, "nk")
+    _check_rows(H, off, M, orc.swiglu(pre))
+    _check_rows(P, off, M, pre)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_sweep_kn_plain(seed):
+    rng0 = np.random.default_rng(3000 + 500 + seed)
+    N = 8 * int(rng0.integers(1, 97))
+    Kd = 64 * int(rng0.integers(1, 13))
+    _, A, W, off, M, use_ws = _case(3000 + seed, N, Kd, mean=200)
+    Wkn = np.ascontiguousarray(W.transpose(0, 2, 1))   # [G, Kd, N]
+    C = empty_like_poisoned((M, N), torch.bfloat16)
+    moe.moe_grouped_gemm(dev(A), dev(Wkn), 1, dev(off), C, workspace=_workspace(use_ws))
+    torch.cuda.synchronize()
+    lo = int(off[0])
+    _check_rows(C, off, M, orc.grouped_gemm(A[lo:int(off[-1])], Wkn, off - lo, "kn"))
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_sweep_kn_dswiglu(seed):
+    rng0 = np.random.default_rng(4000 + 500 + seed)
+    F = 8 * int(rng0.integers(1, 65))
+    Kd = 64 * int(rng0.integers(1, 13))
+    rng, A, W, off, M, use_ws = _case(4000 + seed, F, Kd, mean=200)
+    Wkn = np.ascontiguousarray(W.transpose(0, 2, 1))   # [G, Kd, F]
+    pre = mi.f32_to_bf16_bits(rng.standard_normal((M, 2 * F)).astype(np.float32))
+    C = empty_like_poisoned((M, 2 * F), torch.bfloat16)
+    moe.moe_grouped_gemm(dev(A), dev(Wkn), 1, dev(off), C, moe.MOE_EPI_DSWIGLU, epi_in=dev(pre),
+                         workspace=_workspace(use_ws))
+    torch.cuda.synchronize()
+    lo, hi = int(off[0]), int(off[-1])
+    dh = orc.grouped_gemm(A[lo:hi], Wkn, off - lo, "kn")
+    _check_rows(C, off, M, orc.swiglu_backward(dh, pre[lo:hi]))
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_sweep_wgrad(seed):
+    rng = np.random.default_rng(5000 + seed)
+    G = int(rng.integers(1, 17))
+    counts = _counts(rng, G, 150)
+    off = np.concatenate([[0], np.cumsum(counts)])
+    M = int(off[-1])
+    N = 8 * int(rng.integers(1, 97))
+    Kd = 8 * int(rng.integers(1, 97))
+    accumulate = bool(rng.integers(2))
+    X = mi.f32_to_bf16_bits(rng.standard_normal((M, Kd)).astype(np.float32))
+    dY = mi.f32_to_bf16_bits(rng.standard_normal((M, N)).astype(np.float32))
+    init = rng.standard_normal((G, N, Kd)).astype(np.float32)
+    dW = dev(init) if accumulate else empty_like_poisoned((G, N, Kd), torch.float32)
+    moe.moe_grouped_gemm_wgrad(dev(X), dev(dY), dev(off), dW, accumulate=accumulate)
+    torch.cuda.synchronize()
+    got = f64(dW)
+    ref = orc.grouped_wgrad(X, dY, off) + (init.astype(np.float64) if accumulate else 0.0)
+    for g in range(G):
+        if counts[g] == 0:
+            assert np.array_equal(got[g], ref[g]), "an empty group's gradient must be zero (or untouched)"
+        else:
+            assert rel_err(got[g], ref[g]) < TOL_BF16 / 4, g
