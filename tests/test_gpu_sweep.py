@@ -155,3 +155,42 @@ def test_sweep_wgrad(seed):
             assert np.array_equal(got[g], ref[g]), "an empty group's gradient must be zero (or untouched)"
         else:
             assert rel_err(got[g], ref[g]) < TOL_BF16 / 4, g
+
+
+def _route_case(rng, E, K):
+    """A bias for half the cases, with up to E - K experts masked by -inf (K finite keys remain)."""
+    if not rng.integers(2):
+        return None
+    bias = (0.5 * rng.standard_normal(E)).astype(np.float32)
+    bias[rng.choice(E, int(rng.integers(0, E - K + 1)), replace=False)] = -np.inf
+    return bias
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_sweep_route(seed):
+    """Routing of random logits: indices, counts, offsets, slot positions and the permutation
+    bit-exact against the oracle, gates within 1e-5."""
+    from tests.test_gpu_parity import _check_route
+    rng = np.random.default_rng(6000 + seed)
+    E = int(rng.integers(1, 257))
+    K = int(rng.integers(1, min(E, 32) + 1))
+    T = int(rng.integers(1, 6000))
+    score, renorm = int(rng.integers(2)), bool(rng.integers(2))
+    logits = (rng.standard_normal((T, E)) * rng.uniform(0.1, 3.0)).astype(np.float32)
+    _check_route(logits, _route_case(rng, E, K), K, score, renorm)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_sweep_router_route(seed):
+    """The fused router equals the router product followed by routing (every output bit for
+    bit), and the routing of its logits is the oracle's."""
+    from tests.test_gpu_parity import _check_route, _fused_vs_unfused
+    rng = np.random.default_rng(7000 + seed)
+    E = int(rng.integers(1, 257))
+    K = int(rng.integers(1, min(E, 32) + 1))
+    T = int(rng.integers(1, 20000))
+    d = 8 * int(rng.integers(1, 257))
+    score, renorm = int(rng.integers(2)), bool(rng.integers(2))
+    bias = _route_case(rng, E, K)
+    logits = _fused_vs_unfused(T, d, E, K, score, renorm, bias=bias, seed=7100 + seed)
+    _check_route(logits, bias, K, score, renorm)
