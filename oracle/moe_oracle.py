@@ -184,7 +184,9 @@ def grouped_gemm(a: np.ndarray, b: np.ndarray, offsets: np.ndarray, b_layout: st
 
 
 def silu(v: np.ndarray) -> np.ndarray:
-    return v / (1.0 + np.exp(-v))
+    # below v = -709, exp(-v) overflows to inf and v / inf is the limit, 0: the overflow is expected
+    with np.errstate(over="ignore"):
+        return v / (1.0 + np.exp(-v))
 
 
 def swiglu(pre: np.ndarray) -> np.ndarray:

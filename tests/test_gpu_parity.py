@@ -291,24 +291,8 @@ def _mx_operands(rng, rows, K):
     return codes, scales
 
 
-@pytest.mark.parametrize("counts,N,Kd,epi", [
-    ([300, 0, 257, 40], 256, 256, 0),      # ragged groups, an empty one, one row tile tail
-    ([513], 512, 128, 0),                  # one stage
-    ([100, 200], 264, 512, 0),             # a column tile past N
-    ([130, 0, 70, 256], 512, 384, 1),      # SwiGLU epilogue, three stages
-    ([1, 2, 3], 64, 128, 1),               # tiny groups, N below one tile
-])
-def test_grouped_gemm_mx_parity(counts, N, Kd, epi):
-    rng = np.random.default_rng(sum(counts) + N + Kd + epi)
-    G, M = len(counts), sum(counts)
-    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
-    ac, asc = _mx_operands(rng, M, Kd)
-    bc, bsc = _mx_operands(rng, G * N, Kd)
-    Nout = N // 2 if epi == 1 else N
-    C = torch.full((M, Nout), float("nan"), dtype=torch.bfloat16, device="cuda")
-    moe.moe_grouped_gemm_mx(_u8(ac), _u8(asc), _u8(bc.reshape(G, N, Kd)), _u8(bsc.reshape(G, N, Kd // 32)),
-                            dev(offs), C, epilogue=epi)
-    torch.cuda.synchronize()
+def _check_mx_gemm(ac, asc, bc, bsc, G, N, Kd, offs, C, epi):
+    """The MX grouped GEMM's output against the oracle's fp64 product of the same codes and scales."""
     p = orc.grouped_gemm_mx(ac, asc, bc.reshape(G, N, Kd), bsc.reshape(G, N, Kd // 32), offs.astype(np.int64))
     ad = orc.mx_dequantize(ac, asc)
     bd = orc.mx_dequantize(bc, bsc).reshape(G, N, Kd)
@@ -327,6 +311,27 @@ def test_grouped_gemm_mx_parity(counts, N, Kd, epi):
         ref = p
         tol = 2.0 ** -8 * np.abs(ref) + acc_tol * scale
     assert np.all(np.abs(got - ref) <= tol + 1e-30), float(np.nanmax(np.abs(got - ref) - tol))
+
+
+@pytest.mark.parametrize("counts,N,Kd,epi", [
+    ([300, 0, 257, 40], 256, 256, 0),      # ragged groups, an empty one, one row tile tail
+    ([513], 512, 128, 0),                  # one stage
+    ([100, 200], 264, 512, 0),             # a column tile past N
+    ([130, 0, 70, 256], 512, 384, 1),      # SwiGLU epilogue, three stages
+    ([1, 2, 3], 64, 128, 1),               # tiny groups, N below one tile
+])
+def test_grouped_gemm_mx_parity(counts, N, Kd, epi):
+    rng = np.random.default_rng(sum(counts) + N + Kd + epi)
+    G, M = len(counts), sum(counts)
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    ac, asc = _mx_operands(rng, M, Kd)
+    bc, bsc = _mx_operands(rng, G * N, Kd)
+    Nout = N // 2 if epi == 1 else N
+    C = torch.full((M, Nout), float("nan"), dtype=torch.bfloat16, device="cuda")
+    moe.moe_grouped_gemm_mx(_u8(ac), _u8(asc), _u8(bc.reshape(G, N, Kd)), _u8(bsc.reshape(G, N, Kd // 32)),
+                            dev(offs), C, epilogue=epi)
+    torch.cuda.synchronize()
+    _check_mx_gemm(ac, asc, bc, bsc, G, N, Kd, offs, C, epi)
 
 
 def test_mx_gate_up_mixtral_shape_sampled():

@@ -194,3 +194,44 @@ def test_sweep_router_route(seed):
     bias = _route_case(rng, E, K)
     logits = _fused_vs_unfused(T, d, E, K, score, renorm, bias=bias, seed=7100 + seed)
     _check_route(logits, bias, K, score, renorm)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_sweep_mx_quantize(seed):
+    """MX block quantisation of random rows with per-row magnitudes from 2^-30 to 2^30: codes
+    and scales bit-exact against the oracle."""
+    rng = np.random.default_rng(8000 + seed)
+    R, K = int(rng.integers(1, 3000)), 32 * int(rng.integers(1, 129))
+    v = rng.standard_normal((R, K)) * np.exp2(rng.integers(-30, 31, (R, 1)))
+    v[rng.random((R, K)) < 0.01] = 0.0
+    x = mi.f32_to_bf16_bits(v.astype(np.float32))
+    codes = torch.full((R, K), 0xAA, dtype=torch.uint8, device="cuda")
+    scales = torch.full((R, K // 32), 0xAA, dtype=torch.uint8, device="cuda")
+    moe.moe_mx_quantize(dev(x), codes, scales)
+    torch.cuda.synchronize()
+    rc, rs = orc.mx_quantize(x)
+    np.testing.assert_array_equal(codes.cpu().numpy(), rc)
+    np.testing.assert_array_equal(scales.cpu().numpy(), rs)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_sweep_grouped_gemm_mx(seed):
+    """The MX grouped GEMM on random group loads, widths and reduction lengths, plain or SwiGLU,
+    against the oracle's product of the same codes and scales."""
+    from tests.test_gpu_parity import _check_mx_gemm, _mx_operands
+    rng = np.random.default_rng(9000 + seed)
+    G = int(rng.integers(1, 13))
+    counts = _counts(rng, G, 150)
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    M = int(offs[-1])
+    epi = int(rng.integers(2))
+    N = 16 * int(rng.integers(1, 49))           # 16 .. 768
+    Kd = 128 * int(rng.integers(1, 9))          # 128 .. 1024
+    ac, asc = _mx_operands(rng, M, Kd)
+    bc, bsc = _mx_operands(rng, G * N, Kd)
+    C = torch.full((M, N // 2 if epi == 1 else N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    u8 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    moe.moe_grouped_gemm_mx(u8(ac), u8(asc), u8(bc.reshape(G, N, Kd)), u8(bsc.reshape(G, N, Kd // 32)),
+                            dev(offs), C, epilogue=epi)
+    torch.cuda.synchronize()
+    _check_mx_gemm(ac, asc, bc, bsc, G, N, Kd, offs, C, epi)
