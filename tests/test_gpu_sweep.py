@@ -235,3 +235,49 @@ def test_sweep_grouped_gemm_mx(seed):
                             dev(offs), C, epilogue=epi)
     torch.cuda.synchronize()
     _check_mx_gemm(ac, asc, bc, bsc, G, N, Kd, offs, C, epi)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_sweep_layer_forward_backward(seed):
+    """The whole layer, forward and backward with the router backward, on random small
+    configurations (routing on the oracle's fp32 logits so that it is exact): outputs and every
+    gradient against the oracle; empty experts' weight gradients exactly zero."""
+    from tests.test_gpu_parity import _run_layer
+    rng = np.random.default_rng(10000 + seed)
+    E = int(rng.integers(1, 65))
+    K = int(rng.integers(1, min(E, 8) + 1))
+    cfg = mi.MoEConfig(f"sweep_{seed}", seed=10100 + seed, T=int(rng.integers(16, 1500)),
+                       d=64 * int(rng.integers(1, 9)), E=E, K=K, F=8 * int(rng.integers(8, 65)), bf16=True,
+                       score=int(rng.integers(2)), renorm=bool(rng.integers(2)), wr_std=0.05,
+                       dy_seed=10200 + seed)
+    inp = mi.make(cfg)
+    logits = orc.router_logits(inp["x"], inp["w_router"])
+    dy = mi.upstream_grad(cfg)
+    bufs, dv = _run_layer(cfg, inp, logits=logits, backward=True)
+    router = dict(logits=dev(logits), x=dv["x"], w_router=dv["w_router"], bias=None, score=cfg.score,
+                  renorm=cfg.renorm)
+    moe.layer_backward(dev(dy), dv["w13"], dv["w2"], cfg.K, bufs, router=router)
+    torch.cuda.synchronize()
+    fwd = orc.forward(inp["x"], None, None, inp["w13"], inp["w2"], cfg.K, cfg.score, cfg.renorm, logits=logits)
+    bwd = orc.backward(dy, fwd, inp["w13"], inp["w2"], cfg.K)
+    r = fwd["routing"]
+    np.testing.assert_array_equal(host_i(bufs.topk_idx), r.idx)
+    np.testing.assert_array_equal(host_i(bufs.counts), r.counts)
+    d_logits = orc.route_backward(logits, r.idx, bwd["d_gates"], cfg.score, cfg.renorm)
+    dwr, dx_router = orc.router_backward(d_logits, inp["x"], inp["w_router"])
+    assert rel_err(bufs.y, fwd["y"]) < TOL_BF16
+    assert rel_err(bufs.d_gates, bwd["d_gates"]) < TOL_BF16
+    assert rel_err(bufs.dx, bwd["dx"] + dx_router) < TOL_BF16
+    assert rel_err(bufs.d_logits, d_logits) < TOL_BF16
+    assert rel_err(bufs.dw_router, dwr) < TOL_BF16
+    dw13, dw2 = f64(bufs.dw13), f64(bufs.dw2)
+    for e in range(cfg.E):
+        if r.counts[e] == 0:
+            assert not np.any(dw13[e]) and not np.any(dw2[e]), e
+        else:
+            assert rel_err(dw13[e], bwd["dw13"][e]) < TOL_BF16, e
+            assert rel_err(dw2[e], bwd["dw2"][e]) < TOL_BF16, e
+
+
+def host_i(t):
+    return t.detach().cpu().numpy()
