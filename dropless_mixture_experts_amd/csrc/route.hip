@@ -93,12 +93,13 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
 
 constexpr int kScanThreads = 1024;
 constexpr int kScanParts = 64;  // at most this many threads share one expert's column
-constexpr int kScanRun = 16;    // chunk counts a thread holds in registers
 
 // One workgroup.  hist[c][e] (chunk counts) becomes the exclusive prefix of
 // expert e's counts over chunks 0..c-1.  Thread (part p, expert e) owns a run
 // of consecutive chunks of column e: it loads them all at once, adds the run
 // totals of parts 0..p-1 from LDS and writes its prefixes back.
+// RUN: chunk counts a thread holds in registers (16, or 32 when a thread owns more than 16 chunks)
+template <int RUN>
 __global__ __launch_bounds__(kScanThreads) void route_scan_kernel(int32_t* __restrict__ hist,
                                                                   int nch, int E,
                                                                   int32_t* __restrict__ counts,
@@ -114,17 +115,17 @@ __global__ __launch_bounds__(kScanThreads) void route_scan_kernel(int32_t* __res
   const int c_beg = active ? part * per : 0;
   const int c_end = active ? min(nch, c_beg + per) : 0;
 
-  int v[kScanRun];
+  int v[RUN];
   int sum = 0;
 #pragma unroll
-  for (int u = 0; u < kScanRun; ++u) {
+  for (int u = 0; u < RUN; ++u) {
     const int c = c_beg + u;
     v[u] = (c < c_end) ? hist[(int64_t)c * E + e] : 0;
     sum += v[u];
   }
-  for (int c0 = c_beg + kScanRun; c0 < c_end; c0 += kScanRun) {
+  for (int c0 = c_beg + RUN; c0 < c_end; c0 += RUN) {
 #pragma unroll
-    for (int u = 0; u < kScanRun; ++u) {
+    for (int u = 0; u < RUN; ++u) {
       const int c = c0 + u;
       if (c < c_end) sum += hist[(int64_t)c * E + e];
     }
@@ -137,22 +138,22 @@ __global__ __launch_bounds__(kScanThreads) void route_scan_kernel(int32_t* __res
     if (part == nparts - 1) s_tot[e] = run + sum;
   }
 #pragma unroll
-  for (int u = 0; u < kScanRun; ++u) {
+  for (int u = 0; u < RUN; ++u) {
     const int c = c_beg + u;
     if (c < c_end) {
       hist[(int64_t)c * E + e] = run;
       run += v[u];
     }
   }
-  for (int c0 = c_beg + kScanRun; c0 < c_end; c0 += kScanRun) {
-    int w[kScanRun];
+  for (int c0 = c_beg + RUN; c0 < c_end; c0 += RUN) {
+    int w[RUN];
 #pragma unroll
-    for (int u = 0; u < kScanRun; ++u) {
+    for (int u = 0; u < RUN; ++u) {
       const int c = c0 + u;
       w[u] = (c < c_end) ? hist[(int64_t)c * E + e] : 0;
     }
 #pragma unroll
-    for (int u = 0; u < kScanRun; ++u) {
+    for (int u = 0; u < RUN; ++u) {
       const int c = c0 + u;
       if (c < c_end) {
         hist[(int64_t)c * E + e] = run;
@@ -252,7 +253,12 @@ hipError_t launch_route(const float* logits, const float* bias, int64_t T, int E
 hipError_t launch_route_scan_finalize(int32_t* hist, int nch, int chunk, int64_t T, int E, int K,
                                       const int32_t* topk_idx, int32_t* counts, int32_t* offsets,
                                       int32_t* slot_pos, int32_t* row_src, hipStream_t s) {
-  hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, hist, nch, E, counts, offsets);
+  // chunks a thread scans (as the kernel splits them): more than 16 take the deeper register run
+  const int nparts = std::min(kScanParts, kScanThreads / E);
+  if ((nch + nparts - 1) / nparts > 16)
+    hipLaunchKernelGGL(route_scan_kernel<32>, dim3(1), dim3(kScanThreads), 0, s, hist, nch, E, counts, offsets);
+  else
+    hipLaunchKernelGGL(route_scan_kernel<16>, dim3(1), dim3(kScanThreads), 0, s, hist, nch, E, counts, offsets);
   const int64_t M = T * K;
   if (M > 0) {
     hipLaunchKernelGGL(route_finalize_kernel, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, s,
