@@ -294,6 +294,90 @@ def backward(dy, fwd: dict, w13, w2, K) -> dict:
 
 
 # ----------------------------------------------------------------------------
+# Single rows and single weight-gradient entries of the same layer.  A row of
+# the expert-contiguous order depends only on its own token, its expert and
+# that expert's weights, and an entry dW_e[n, k] only on column n of one factor
+# and column k of the other over the group's rows; these functions evaluate
+# exactly the definitions of forward() and backward() for the rows and entries
+# asked for, so that layers too large to form whole can still be checked.
+
+def group_of_rows(routing: Routing, rows) -> np.ndarray:
+    """Expert owning each expert-contiguous row: offsets[e] <= r < offsets[e + 1]."""
+    rows = np.asarray(rows, np.int64)
+    return np.searchsorted(routing.offsets, rows, side="right") - 1
+
+
+def layer_rows(x, w13, w2, routing: Routing, rows, K: int) -> dict:
+    """x_perm, pre, h and y_perm of the expert-contiguous rows ``rows`` (S4-S6)."""
+    rows = np.asarray(rows, np.int64)
+    x = np.asarray(x)
+    tok = routing.row_src[rows] // K
+    grp = group_of_rows(routing, rows)
+    F = w13.shape[1] // 2
+    out = {"x_perm": x[tok], "pre": np.zeros((len(rows), 2 * F)), "h": np.zeros((len(rows), F)),
+           "y_perm": np.zeros((len(rows), w2.shape[1]))}
+    for e in np.unique(grp):
+        sel = np.nonzero(grp == e)[0]
+        pre = to_f64(x[tok[sel]]) @ to_f64(w13[e]).T
+        h = swiglu(pre)
+        out["pre"][sel] = pre
+        out["h"][sel] = h
+        out["y_perm"][sel] = h @ to_f64(w2[e]).T
+    return out
+
+
+def backward_rows(x, dy, w13, w2, routing: Routing, rows, K: int) -> dict:
+    """dy_perm, d_pre and dx_perm of the expert-contiguous rows ``rows`` (B1, B2, B4)."""
+    rows = np.asarray(rows, np.int64)
+    slot = routing.row_src[rows]
+    tok, kk = slot // K, slot % K
+    grp = group_of_rows(routing, rows)
+    fw = layer_rows(x, w13, w2, routing, rows, K)
+    dy_perm = routing.gates[tok, kk][:, None] * to_f64(np.asarray(dy)[tok])
+    d_pre = np.zeros_like(fw["pre"])
+    dx_perm = np.zeros((len(rows), w13.shape[2]))
+    for e in np.unique(grp):
+        sel = np.nonzero(grp == e)[0]
+        dh = dy_perm[sel] @ to_f64(w2[e])
+        d_pre[sel] = swiglu_backward(dh, fw["pre"][sel])
+        dx_perm[sel] = d_pre[sel] @ to_f64(w13[e])
+    return {"dy_perm": dy_perm, "d_pre": d_pre, "dx_perm": dx_perm}
+
+
+def wgrad_entries(x, dy, w13, w2, routing: Routing, K: int, e: int, which: str, n_idx, k_idx) -> np.ndarray:
+    """Entries [n_idx][:, k_idx] of one expert's weight gradient (B3 / B5):
+    which = "w2":  dW2_e[n, k]  = sum over the group's rows r of dy_perm[r, n] * h[r, k];
+    which = "w13": dW13_e[n, k] = sum over the group's rows r of d_pre[r, n] * x_perm[r, k].
+    Only the columns of h or d_pre that the entries need are formed."""
+    n_idx = np.asarray(n_idx, np.int64)
+    k_idx = np.asarray(k_idx, np.int64)
+    lo, hi = int(routing.offsets[e]), int(routing.offsets[e + 1])
+    F = w13.shape[1] // 2
+    if hi == lo:
+        return np.zeros((len(n_idx), len(k_idx)))
+    slot = routing.row_src[lo:hi]
+    tok, kk = slot // K, slot % K
+    X = to_f64(np.asarray(x)[tok])                                       # x_perm rows of the group
+    dYp = routing.gates[tok, kk][:, None] * to_f64(np.asarray(dy)[tok])  # dy_perm rows of the group
+    W13 = w13[e]
+
+    def pre_cols(j):   # [gate | up] pre-activations of the group at hidden columns j
+        return np.concatenate([X @ to_f64(W13[j]).T, X @ to_f64(W13[F + j]).T], axis=1)
+
+    if which == "w2":
+        h = swiglu(pre_cols(k_idx))                                     # h[:, k_idx]
+        return dYp[:, n_idx].T @ h
+    if which == "w13":
+        j = n_idx % F
+        dh = dYp @ to_f64(w2[e][:, j])                                  # dh[:, j]
+        dpre = swiglu_backward(dh, pre_cols(j))                         # [dG | dU] at columns j
+        m = len(j)
+        cols = np.where(n_idx < F, np.arange(m), m + np.arange(m))
+        return dpre[:, cols].T @ X[:, k_idx]
+    raise ValueError("which must be 'w2' or 'w13'")
+
+
+# ----------------------------------------------------------------------------
 # Router backward.  The router is learned (TE-MoE introduction), so training
 # needs the gradient of the loss with respect to its weights and inputs.  The
 # top-K choice is a discrete decision and is held fixed; the gradient flows

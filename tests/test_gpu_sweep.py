@@ -183,8 +183,8 @@ def test_sweep_route(seed):
 @pytest.mark.parametrize("seed", range(8))
 def test_sweep_router_route(seed):
     """The fused router equals the router product followed by routing (every output bit for
-    bit), and the routing of its logits is the oracle's."""
-    from tests.test_gpu_parity import _check_route, _fused_vs_unfused
+    bit), and routes the tokens with a clear top-K margin as the oracle does."""
+    from tests.test_gpu_parity import _check_route_clear_tokens, _fused_vs_unfused
     rng = np.random.default_rng(7000 + seed)
     E = int(rng.integers(1, 257))
     K = int(rng.integers(1, min(E, 32) + 1))
@@ -192,8 +192,8 @@ def test_sweep_router_route(seed):
     d = 8 * int(rng.integers(1, 257))
     score, renorm = int(rng.integers(2)), bool(rng.integers(2))
     bias = _route_case(rng, E, K)
-    logits = _fused_vs_unfused(T, d, E, K, score, renorm, bias=bias, seed=7100 + seed)
-    _check_route(logits, bias, K, score, renorm)
+    x, w, idx, gate = _fused_vs_unfused(T, d, E, K, score, renorm, bias=bias, seed=7100 + seed)
+    _check_route_clear_tokens(x, w, bias, K, score, renorm, idx, gate)
 
 
 @pytest.mark.parametrize("seed", range(6))

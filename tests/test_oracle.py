@@ -30,6 +30,26 @@ def _tiny(T=48, d=16, E=6, K=2, F=8, seed=11, bias=False):
     return x, wr, w13, w2, b
 
 
+# ---------------------------------------------------------------- value decoding
+
+def test_to_f64_decodes_bf16_bit_patterns():
+    """bf16 is the upper half of an IEEE binary32: sign, 8 exponent bits (bias 127), 7 mantissa bits."""
+    table = {0x3F80: 1.0, 0xBF80: -1.0, 0xC000: -2.0, 0x4049: 3.140625, 0x3E80: 0.25,
+             0x0000: 0.0, 0x7F7F: (2.0 - 2.0 ** -7) * 2.0 ** 127, 0x0080: 2.0 ** -126,
+             0x0001: 2.0 ** -133, 0x807F: -(1.0 - 2.0 ** -7) * 2.0 ** -126,
+             0x7F80: math.inf, 0xFF80: -math.inf}
+    codes = np.array(list(table), dtype=np.uint16)
+    got = orc.to_f64(codes)
+    assert got.dtype == np.float64
+    assert got.tolist() == list(table.values())
+    neg0 = orc.to_f64(np.array([0x8000], np.uint16))[0]
+    assert neg0 == 0.0 and math.copysign(1.0, neg0) == -1.0
+    assert np.isnan(orc.to_f64(np.array([0x7FC0, 0xFFC1], np.uint16))).all()
+    # fp32 and fp64 inputs are widened exactly
+    f = np.array([0.1, -3.5e-40], np.float32)
+    assert orc.to_f64(f).tolist() == [float(v) for v in f]
+
+
 # ---------------------------------------------------------------- worked examples
 
 def _golden():
@@ -270,6 +290,65 @@ def test_layer_matches_dense_on_tiny_fp32_workload():
     ref = orc.dense_layer(inp["x"], orc.dense_gate_matrix(out["routing"], cfg.E), inp["w13"], inp["w2"])
     np.testing.assert_allclose(out["y"], ref, rtol=1e-10, atol=1e-12)
     assert out["routing"].counts.sum() == cfg.T * cfg.K
+
+
+@pytest.mark.parametrize("name", ["mixtral", "fine_grained", "dsv3_share"])
+def test_layer_matches_dense_masked_evaluation_at_workload_widths(name):
+    """The per-expert loop against every expert on every token at the real widths, router
+    recipes and score functions of the three bf16 workloads (64 tokens each): softmax with
+    near-uniform load, softmax with a N(0,1) per-expert bias over 128 experts, sigmoid with
+    Zipf-like rank offsets and four masked experts at d = 7168."""
+    cfg = mi.CONFIGS[name]
+    inp = mi.make(cfg, rows=64)
+    out = orc.forward(inp["x"], inp["w_router"], inp["bias"], inp["w13"], inp["w2"], cfg.K, cfg.score, cfg.renorm)
+    r = out["routing"]
+    assert r.counts.sum() == 64 * cfg.K
+    if name == "dsv3_share":
+        assert np.all(r.counts[~np.isfinite(inp["bias"])] == 0)
+    ref = orc.dense_layer(inp["x"], orc.dense_gate_matrix(r, cfg.E), inp["w13"], inp["w2"])
+    np.testing.assert_allclose(out["y"], ref, rtol=1e-11, atol=1e-12 * np.abs(ref).max())
+
+
+def _rows_case(bf16):
+    if bf16:
+        cfg = mi.MoEConfig("rows_skew", seed=51, T=90, d=64, E=6, K=3, F=40, bf16=True, wr_std=0.3,
+                           bias="normal", dy_seed=52)
+    else:
+        cfg = mi.CONFIGS["tiny_fp32"]
+    inp = mi.make(cfg)
+    dy = mi.upstream_grad(cfg)
+    fwd = orc.forward(inp["x"], inp["w_router"], inp["bias"], inp["w13"], inp["w2"], cfg.K, cfg.score, cfg.renorm)
+    return cfg, inp, dy, fwd
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_single_rows_and_entries_equal_the_whole_layer(bf16):
+    """layer_rows / backward_rows / wgrad_entries (the oracle's per-row and per-entry forms used
+    on full-size layers) reproduce the whole-layer forward and backward, which the dense masked
+    evaluation and central differences pin."""
+    cfg, inp, dy, fwd = _rows_case(bf16)
+    bwd = orc.backward(dy, fwd, inp["w13"], inp["w2"], cfg.K)
+    r = fwd["routing"]
+    M = cfg.T * cfg.K
+    rows = np.random.default_rng(3).permutation(M)
+    fr = orc.layer_rows(inp["x"], inp["w13"], inp["w2"], r, rows, cfg.K)
+    assert np.array_equal(fr["x_perm"], fwd["x_perm"][rows])
+    for k in ("pre", "h", "y_perm"):
+        np.testing.assert_allclose(fr[k], fwd[k][rows], rtol=1e-12, atol=1e-13)
+    br = orc.backward_rows(inp["x"], dy, inp["w13"], inp["w2"], r, rows, cfg.K)
+    for k in ("dy_perm", "d_pre", "dx_perm"):
+        np.testing.assert_allclose(br[k], bwd[k][rows], rtol=1e-12, atol=1e-13)
+    assert np.array_equal(orc.group_of_rows(r, np.arange(M)), np.repeat(np.arange(cfg.E), r.counts))
+    rng = np.random.default_rng(4)
+    for e in range(cfg.E):
+        n2, k2 = rng.choice(cfg.d, 5, replace=False), rng.choice(cfg.F, 7, replace=False)
+        n13, k13 = rng.choice(2 * cfg.F, 9, replace=False), rng.choice(cfg.d, 4, replace=False)
+        got2 = orc.wgrad_entries(inp["x"], dy, inp["w13"], inp["w2"], r, cfg.K, e, "w2", n2, k2)
+        got13 = orc.wgrad_entries(inp["x"], dy, inp["w13"], inp["w2"], r, cfg.K, e, "w13", n13, k13)
+        np.testing.assert_allclose(got2, bwd["dw2"][e][np.ix_(n2, k2)], rtol=1e-11, atol=1e-13)
+        np.testing.assert_allclose(got13, bwd["dw13"][e][np.ix_(n13, k13)], rtol=1e-11, atol=1e-13)
+        if r.counts[e] == 0:
+            assert not np.any(got2) and not np.any(got13)
 
 
 def test_capacity_contrast():
