@@ -44,6 +44,12 @@ def rel_err(got, ref) -> float:
     return float(np.linalg.norm(got - ref) / (den if den > 0 else 1.0))
 
 
+def by_expert(idx, gate):
+    """Each token's chosen experts in ascending order, with their gates alongside."""
+    o = np.argsort(idx, axis=1, kind="stable")
+    return np.take_along_axis(idx, o, axis=1), np.take_along_axis(gate, o, axis=1)
+
+
 def empty_like_poisoned(shape, dtype):
     """A device buffer filled with a NaN pattern, to show which elements a kernel wrote."""
     t = torch.empty(shape, dtype=dtype, device=DEV)

@@ -24,7 +24,7 @@ import torch
 
 import moe_inputs as mi
 import oracle as orc
-from tests.gpu_util import GATE_ATOL, TOL_BF16, dev, f64, host
+from tests.gpu_util import GATE_ATOL, TOL_BF16, by_expert, dev, f64, host
 
 pytestmark = pytest.mark.gpu
 
@@ -217,8 +217,11 @@ def test_full_fused_router(name):
     assert clear.mean() > 0.9
     S = np.nonzero(clear)[0]
     r = orc.route(logits[S], inp["bias"], K, cfg.score, cfg.renorm)
-    np.testing.assert_array_equal(host(a["idx"])[S], r.idx)
-    np.testing.assert_allclose(host(a["gate"])[S], r.gates, atol=1e-4, rtol=0)
+    # two chosen experts closer than the product's rounding may trade places: compare the sets
+    gi, gg = by_expert(host(a["idx"])[S], host(a["gate"])[S])
+    ri, rg = by_expert(r.idx, r.gates)
+    np.testing.assert_array_equal(gi, ri)
+    np.testing.assert_allclose(gg, rg, atol=1e-4, rtol=0)
     scale = np.abs(orc.to_f64(inp["x"][S])) @ np.abs(orc.to_f64(inp["w_router"])).T
     assert np.all(np.abs(host(a["logits"])[S].astype(np.float64) - logits[S]) <= 1e-5 * scale + 1e-30)
 

@@ -13,7 +13,7 @@ import torch
 
 import moe_inputs as mi
 import oracle as orc
-from tests.gpu_util import GATE_ATOL, TOL_BF16, TOL_F32, dev, empty_like_poisoned, f64, host, rel_err
+from tests.gpu_util import GATE_ATOL, TOL_BF16, TOL_F32, by_expert, dev, empty_like_poisoned, f64, host, rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -195,8 +195,9 @@ def _fused_vs_unfused(T, d, E, K, score, renorm, bias=None, seed=0, with_logits=
 
 def _check_route_clear_tokens(x, w, bias, K, score, renorm, idx, gate):
     """Tokens whose K-th and (K+1)-th keys, from the oracle's own logits, are more than 1e-3
-    apart are routed as the oracle routes them (the GPU product differs from the fp64 one in
-    its last bits, which can only swap experts closer than that)."""
+    apart choose the oracle's experts with the oracle's gates (the GPU product differs from the
+    fp64 one in its last bits, which can only exchange experts closer than that: across the
+    K-th place, or in the order of two chosen experts, so the chosen set is compared)."""
     logits = orc.router_logits(x, w)
     keys = logits.astype(np.float64) + (bias.astype(np.float64) if bias is not None else 0.0)
     E = keys.shape[1]
@@ -207,8 +208,10 @@ def _check_route_clear_tokens(x, w, bias, K, score, renorm, idx, gate):
     else:
         clear = np.arange(len(keys))
     r = orc.route(logits[clear], bias, K, score, renorm)
-    np.testing.assert_array_equal(idx[clear], r.idx)
-    np.testing.assert_allclose(gate[clear], r.gates, atol=1e-4, rtol=0)
+    gi, gg = by_expert(idx[clear], gate[clear])
+    ri, rg = by_expert(r.idx, r.gates)
+    np.testing.assert_array_equal(gi, ri)
+    np.testing.assert_allclose(gg, rg, atol=1e-4, rtol=0)
 
 
 @pytest.mark.parametrize("T,d,E,K,score,renorm", [
