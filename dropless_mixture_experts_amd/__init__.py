@@ -15,12 +15,13 @@ import os
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe.so")
 
-MOE_OK, MOE_INVALID_ARG, MOE_UNSUPPORTED, MOE_HIP_ERROR = 0, 1, 2, 3
+MOE_OK, MOE_INVALID_ARG, MOE_UNSUPPORTED, MOE_HIP_ERROR, MOE_SCRATCH_LIMIT = 0, 1, 2, 3, 4
 MOE_F32, MOE_BF16 = 0, 1
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
 MOE_LAYOUT_NK, MOE_LAYOUT_KN = 0, 1
 MOE_EPI_NONE, MOE_EPI_SWIGLU, MOE_EPI_DSWIGLU = 0, 1, 2
 MOE_MAX_EXPERTS, MOE_MAX_TOPK, MOE_MAX_GROUPS = 256, 32, 1024
+MOE_ROUTER_ROUTE_NOALLOC_MAX_BYTES = 4 << 20
 
 # exported symbols and their C signatures (mirrors include/moe.h)
 _c = ctypes
@@ -39,6 +40,8 @@ SIGNATURES = {
     "moe_router_route_workspace_size": (_I32, [_I64, _I32, _c.POINTER(_SZ)]),
     "moe_router_route": (_I32, [_P, _P, _P, _I64, _I64, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P,
                                 _P, _SZ, _P]),
+    "moe_router_route_noalloc": (_I32, [_P, _P, _P, _I64, _I64, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P,
+                                        _P, _P]),
     "moe_permute_mx": (_I32, [_P, _P, _I64, _I64, _I32, _P, _P, _P, _P]),
     "moe_mx_quantize": (_I32, [_P, _I64, _I64, _I32, _P, _P, _P]),
     "moe_grouped_gemm_mx": (_I32, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _P, _P]),
@@ -308,6 +311,25 @@ def moe_router_route(x, w_router, bias, K: int, score: int, renorm: bool, logits
     _call("moe_router_route", _ptr(x), _ptr(w_router), _ptr(bias), T, d, E, K, dtype_code(x), score,
           int(bool(renorm)), _ptr(logits), _ptr(topk_idx), _ptr(topk_gate), _ptr(counts), _ptr(offsets),
           _ptr(slot_pos), _ptr(row_src), _ptr(ws), ws_bytes, _stream(stream))
+
+
+def moe_router_route_noalloc(x, w_router, bias, K: int, score: int, renorm: bool, logits, topk_idx, topk_gate,
+                             counts, offsets, slot_pos, row_src, stream=None) -> None:
+    """moe_router_route with its workspace in the library's static device array: no allocation.
+    Calls that overlap in time on one device race on that array."""
+    T, d = x.shape
+    E = w_router.shape[0]
+    _dense("x", x)
+    _dense("w_router", w_router, x.dtype, (E, d))
+    _dense("bias", bias, _f32(), (E,), optional=True, flat=True)
+    _dense("logits", logits, _f32(), (T, E), optional=True)
+    for n, t, dt, sh in (("topk_idx", topk_idx, _i32(), (T, K)), ("topk_gate", topk_gate, _f32(), (T, K)),
+                         ("counts", counts, _i32(), (E,)), ("offsets", offsets, _i32(), (E + 1,)),
+                         ("slot_pos", slot_pos, _i32(), (T * K,)), ("row_src", row_src, _i32(), (T * K,))):
+        _dense(n, t, dt, sh, flat=True)
+    _call("moe_router_route_noalloc", _ptr(x), _ptr(w_router), _ptr(bias), T, d, E, K, dtype_code(x), score,
+          int(bool(renorm)), _ptr(logits), _ptr(topk_idx), _ptr(topk_gate), _ptr(counts), _ptr(offsets),
+          _ptr(slot_pos), _ptr(row_src), _stream(stream))
 
 
 def moe_mx_quantize(x, codes, scales, stream=None) -> None:

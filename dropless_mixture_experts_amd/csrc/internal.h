@@ -21,6 +21,12 @@ hipError_t launch_router_route(const void* x, const void* w, const float* bias, 
                                int32_t* counts, int32_t* offsets, int32_t* slot_pos, int32_t* row_src, void* ws,
                                hipStream_t s);
 
+// moe_router_route with the histograms in the library's static device array (no workspace)
+hipError_t launch_router_route_noalloc(const void* x, const void* w, const float* bias, int64_t T, int64_t d, int E,
+                                       int K, int score, int renorm, float* logits, int32_t* topk_idx,
+                                       float* topk_gate, int32_t* counts, int32_t* offsets, int32_t* slot_pos,
+                                       int32_t* row_src, hipStream_t s);
+
 hipError_t launch_route(const float* logits, const float* bias, int64_t T, int E, int K, int score,
                         int renorm, int32_t* topk_idx, float* topk_gate, int32_t* counts,
                         int32_t* offsets, int32_t* slot_pos, int32_t* row_src, void* ws,

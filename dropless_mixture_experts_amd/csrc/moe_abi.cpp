@@ -28,6 +28,7 @@ const char* moe_status_str(int32_t status) {
     case MOE_INVALID_ARG: return "invalid argument";
     case MOE_UNSUPPORTED: return "unsupported dtype/layout/epilogue combination";
     case MOE_HIP_ERROR: return "HIP launch error";
+    case MOE_SCRATCH_LIMIT: return "input larger than the static scratch of an allocation-free entry point";
     default: return "unknown status";
   }
 }
@@ -199,6 +200,26 @@ int32_t moe_router_route(const void* x, const void* w_router, const float* bias,
   if (ws_bytes < need || (need > 0 && !ws)) return MOE_INVALID_ARG;
   return from_hip(moe::launch_router_route(x, w_router, bias, T, d, E, K, score, renorm != 0, logits, topk_idx,
                                            topk_gate, counts, offsets, slot_pos, row_src, ws, (hipStream_t)stream));
+}
+
+int32_t moe_router_route_noalloc(const void* x, const void* w_router, const float* bias, int64_t T, int64_t d,
+                                 int32_t E, int32_t K, int32_t dtype, int32_t score, int32_t renorm, float* logits,
+                                 int32_t* topk_idx, float* topk_gate, int32_t* counts, int32_t* offsets,
+                                 int32_t* slot_pos, int32_t* row_src, moe_stream_t stream) {
+  if (T < 0 || d < 8 || d % 8 != 0 || E < 1 || E > MOE_MAX_EXPERTS || K < 1 || K > E || K > MOE_MAX_TOPK)
+    return MOE_INVALID_ARG;
+  if (dtype != MOE_BF16) return MOE_UNSUPPORTED;
+  if (score != MOE_SCORE_SOFTMAX && score != MOE_SCORE_SIGMOID) return MOE_UNSUPPORTED;
+  if (T * (int64_t)K >= ((int64_t)1 << 31)) return MOE_INVALID_ARG;
+  if (!counts || !offsets) return MOE_INVALID_ARG;
+  if (T > 0 && (!x || !w_router || !topk_idx || !topk_gate || !slot_pos || !row_src)) return MOE_INVALID_ARG;
+  if ((x && !aligned16(x)) || (w_router && !aligned16(w_router)) || (logits && !aligned4(logits)) ||
+      (bias && !aligned4(bias)))
+    return MOE_INVALID_ARG;
+  if (moe::router_route_workspace_bytes(T, E) > MOE_ROUTER_ROUTE_NOALLOC_MAX_BYTES) return MOE_SCRATCH_LIMIT;
+  return from_hip(moe::launch_router_route_noalloc(x, w_router, bias, T, d, E, K, score, renorm != 0, logits,
+                                                   topk_idx, topk_gate, counts, offsets, slot_pos, row_src,
+                                                   (hipStream_t)stream));
 }
 
 int32_t moe_mx_quantize(const void* x, int64_t R, int64_t K, int32_t dtype, uint8_t* codes, uint8_t* scales,

@@ -18,6 +18,9 @@
 // fp32 (router_logits_kernel): a workgroup owns 32 tokens, its 4 waves split
 // the d axis, and each wave runs 32x32 MFMA tiles (one per 32 experts) fed
 // straight from global memory; the 4 partial tiles are summed through LDS.
+#include <mutex>
+
+#include "../../include/moe.h"
 #include "common.h"
 #include "internal.h"
 #include "route_device.h"
@@ -481,6 +484,39 @@ hipError_t launch_router_route(const void* x, const void* w, const float* bias, 
                                hipStream_t s) {
   return router_route(x, w, bias, T, d, E, K, score, renorm, logits, topk_idx, topk_gate, counts, offsets, slot_pos,
                       row_src, ws, s);
+}
+
+// The allocation-free fused router's workspace: one static device array per device (each
+// device that loads the library holds its own copy at its own address until the process
+// ends).  In host code `scratch` names a host-side stand-in, not device memory: its device
+// address is looked up once per device with hipGetSymbolAddress, and only that address is
+// ever handed to a kernel.
+static __device__ __align__(256) int32_t scratch[MOE_ROUTER_ROUTE_NOALLOC_MAX_BYTES / sizeof(int32_t)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+}  // namespace
+
+hipError_t launch_router_route_noalloc(const void* x, const void* w, const float* bias, int64_t T, int64_t d, int E,
+                                       int K, int score, int renorm, float* logits, int32_t* topk_idx,
+                                       float* topk_gate, int32_t* counts, int32_t* offsets, int32_t* slot_pos,
+                                       int32_t* row_src, hipStream_t s) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = p;
+  });
+  if (g_scratch_err[dev] != hipSuccess) return g_scratch_err[dev];
+  if (g_scratch_ptr[dev] == nullptr) return hipErrorInvalidSymbol;
+  return router_route(x, w, bias, T, d, E, K, score, renorm, logits, topk_idx, topk_gate, counts, offsets, slot_pos,
+                      row_src, g_scratch_ptr[dev], s);
 }
 
 hipError_t launch_router_logits(const void* x, const void* w, int64_t T, int64_t d, int E, int dtype,

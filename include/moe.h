@@ -26,9 +26,10 @@
  *     frees, synchronises, copies to the host or prints.
  *   - Every call only enqueues kernels on `stream` (a hipStream_t; NULL is
  *     the default stream) and returns; calls are capturable in a hipGraph.
- *   - Return value: MOE_OK, or MOE_INVALID_ARG / MOE_UNSUPPORTED for
- *     arguments rejected on the host before anything is launched, or
- *     MOE_HIP_ERROR when a launch fails.  Values that live on the device
+ *   - Return value: MOE_OK, or MOE_INVALID_ARG / MOE_UNSUPPORTED (and, for the
+ *     allocation-free entry point, MOE_SCRATCH_LIMIT) for arguments rejected
+ *     on the host before anything is launched, or MOE_HIP_ERROR when a launch
+ *     fails.  Values that live on the device
  *     (logits, offsets) are not checked: NaN logits and group offsets that are
  *     not monotone with offsets[G] == M are the caller's error and give
  *     undefined results (never an out-of-bounds access for offsets within
@@ -49,13 +50,13 @@ extern "C" {
 
 typedef void* moe_stream_t; /* a hipStream_t */
 
-enum moe_status { MOE_OK = 0, MOE_INVALID_ARG = 1, MOE_UNSUPPORTED = 2, MOE_HIP_ERROR = 3 };
+enum moe_status { MOE_OK = 0, MOE_INVALID_ARG = 1, MOE_UNSUPPORTED = 2, MOE_HIP_ERROR = 3, MOE_SCRATCH_LIMIT = 4 };
 enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 };
 enum moe_score { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 };
 enum moe_layout { MOE_LAYOUT_NK = 0, MOE_LAYOUT_KN = 1 };
 enum moe_epilogue { MOE_EPI_NONE = 0, MOE_EPI_SWIGLU = 1, MOE_EPI_DSWIGLU = 2 };
 
-#define MOE_ABI_VERSION 6
+#define MOE_ABI_VERSION 7
 #define MOE_MAX_EXPERTS 256
 #define MOE_MAX_TOPK 32
 #define MOE_MAX_GROUPS 1024
@@ -135,6 +136,33 @@ int32_t moe_router_route(const void* x, const void* w_router, const float* bias,
                          int32_t K, int32_t dtype, int32_t score, int32_t renorm, float* logits, int32_t* topk_idx,
                          float* topk_gate, int32_t* counts, int32_t* offsets, int32_t* slot_pos, int32_t* row_src,
                          void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/*
+ * moe_router_route for callers that cannot allocate device memory: code under
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The same
+ * kernels and results as moe_router_route, with its workspace (the per-chunk
+ * expert histograms) taken from a static device array of
+ * MOE_ROUTER_ROUTE_NOALLOC_MAX_BYTES bytes that the library holds on every
+ * device it runs on until the process ends.  The caller passes every input and
+ * output as for moe_router_route (no ws, ws_bytes).
+ *   - The call allocates nothing: no hipMalloc, hipFree or allocating library
+ *     routine.  Its first call on a device looks up that device's copy of the
+ *     array once (hipGetSymbolAddress) with the device current.
+ *   - MOE_SCRATCH_LIMIT (checked on the host, nothing launched) when
+ *     moe_router_route_workspace_size(T, E) exceeds MOE_ROUTER_ROUTE_NOALLOC_MAX_BYTES
+ *     (for example T > 131072 tokens at E = 256, T > 4194304 at E = 8).
+ *   - Every call on a device shares that device's array and leaves its last
+ *     contents there; the kernels overwrite every entry they read, so nothing
+ *     needs clearing.  Calls that overlap in time on one device (two streams,
+ *     two host threads) race on the array and give undefined results: order them
+ *     on one stream, or use moe_router_route with separate workspaces.
+ * Other arguments, requirements and errors as moe_router_route.
+ */
+#define MOE_ROUTER_ROUTE_NOALLOC_MAX_BYTES ((size_t)4 << 20)
+int32_t moe_router_route_noalloc(const void* x, const void* w_router, const float* bias, int64_t T, int64_t d,
+                                 int32_t E, int32_t K, int32_t dtype, int32_t score, int32_t renorm, float* logits,
+                                 int32_t* topk_idx, float* topk_gate, int32_t* counts, int32_t* offsets,
+                                 int32_t* slot_pos, int32_t* row_src, moe_stream_t stream);
 
 /*
  * Permute / dispatch into expert-contiguous order (S4; TE-MoE Figure 3

@@ -30,7 +30,7 @@ def test_header_declares_the_boundary():
               "moe_grouped_gemm_wgrad", "moe_router_logits", "moe_route_workspace_size",
               "moe_route_backward", "moe_router_logits_backward", "moe_router_backward_workspace_size",
               "moe_router_route", "moe_router_route_workspace_size", "moe_mx_quantize", "moe_grouped_gemm_mx",
-              "moe_permute_mx",
+              "moe_permute_mx", "moe_router_route_noalloc",
               "moe_status_str", "moe_abi_version"]:
         assert n in names
 
@@ -45,9 +45,10 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert moe.moe_abi_version() == 6
+    assert moe.moe_abi_version() == 7
     assert moe.status_str(0) == "ok"
     assert "invalid" in moe.status_str(1)
+    assert "static scratch" in moe.status_str(moe.MOE_SCRATCH_LIMIT)
     assert moe.status_str(99) == "unknown status"
 
 
@@ -166,6 +167,24 @@ def test_router_route_rejects_bad_arguments(lib):
     assert rr(bias=P + 2) == 1
     assert rr(wsb=0) == 1                 # workspace too small
     assert rr(x=None) == 1
+
+
+def test_router_route_noalloc_rejects_bad_arguments_and_oversized_inputs(lib):
+    def rr(T=100, d=64, E=8, K=2, dt=1, score=0, x=P, bias=None):
+        return lib.moe_router_route_noalloc(x, P, bias, T, d, E, K, dt, score, 1, None, P, P, P, P, P, P, None)
+    assert rr(dt=0) == 2
+    assert rr(score=3) == 2
+    assert rr(K=9) == 1
+    assert rr(d=12) == 1
+    assert rr(x=P + 8) == 1
+    assert rr(x=None) == 1
+    limit = moe.MOE_ROUTER_ROUTE_NOALLOC_MAX_BYTES
+    assert limit == 4 << 20
+    # the largest inputs whose workspace fits, and the first that do not (ceil(T / 32) E 4 bytes)
+    assert moe.moe_router_route_workspace_size(131072, 256) <= limit
+    assert moe.moe_router_route_workspace_size(131104, 256) > limit
+    assert rr(T=131104, E=256) == moe.MOE_SCRATCH_LIMIT
+    assert rr(T=4194336, E=8) == moe.MOE_SCRATCH_LIMIT
 
 
 def test_mx_rejects_bad_arguments(lib):
