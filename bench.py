@@ -49,6 +49,12 @@ def parse():
     ap.add_argument("--mxfp8", action="store_true",
                     help="time the layer forward with MXFP8 expert GEMMs instead (weights quantised once "
                          "before the timed region, activations quantised inside every step)")
+    ap.add_argument("--gemm-zipf", action="store_true",
+                    help="time the two grouped GEMMs alone on 32768 rows in 32 groups of exact Zipf(1.2) sizes "
+                         "(d = 7168, F = 2048; 4 empty groups) instead (an extra line, not the headline)")
+    ap.add_argument("--cold-reps", type=int, default=100,
+                    help="launches of each kernel timed alone with the caches flushed before each one")
+    ap.add_argument("--no-clock", action="store_true", help="skip sampling the GPU clock with amd-smi")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain elementwise pass over 512 MiB (3 launches of torch's neg "
                          "kernel: 512 MiB read, 512 MiB written) to calibrate rocprofv3 FETCH_SIZE / WRITE_SIZE")
@@ -138,14 +144,14 @@ def host_description(threads: int) -> str:
 
 def copy_bandwidth(torch) -> float:
     """On-box HBM reference: GB/s (bytes read + written) of a 1 GiB device copy, median of five
-    launches, each after a 1 GiB elementwise pass that evicts the caches."""
+    launches, each after a read-only 1 GiB pass that evicts the caches."""
     src = torch.empty(512 << 20, dtype=torch.bfloat16, device="cuda").fill_(1.0)
     dst = torch.empty_like(src)
-    flush_a = torch.empty(256 << 20, dtype=torch.float32, device="cuda").fill_(2.0)
-    flush_b = torch.empty_like(flush_a)
+    flush = torch.ones(256 << 20, dtype=torch.float32, device="cuda")
+    acc = torch.empty((), dtype=torch.float32, device="cuda")
     ts = []
     for _ in range(6):
-        torch.neg(flush_a, out=flush_b)
+        torch.sum(flush, dim=0, out=acc)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         dst.copy_(src)
@@ -153,8 +159,177 @@ def copy_bandwidth(torch) -> float:
         torch.cuda.synchronize()
         ts.append(e0.elapsed_time(e1))
     ms = sorted(ts[1:])[2]
-    del src, dst, flush_a, flush_b
+    del src, dst, flush, acc
     return 2 * (1 << 30) / (ms * 1e-3) / 1e9
+
+
+class ColdTimer:
+    """Times single launches with the caches cold: before each launch a read-only pass over
+    1 GiB (a sum) evicts the 4 MB L2s and the 256 MB Infinity Cache, leaving clean lines, so
+    the timed kernel neither hits on its inputs nor pays for earlier dirty lines.  HIP events
+    on the launch stream bracket the launch alone."""
+
+    def __init__(self, torch, stream):
+        self.torch, self.stream = torch, stream
+        self.buf = torch.ones((256 << 20,), dtype=torch.float32, device="cuda")
+        self.out = torch.empty((), dtype=torch.float32, device="cuda")
+
+    def time(self, fn, reps: int) -> dict:
+        torch = self.torch
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for e0, e1 in evs:
+            torch.sum(self.buf, dim=0, out=self.out)
+            e0.record(self.stream)
+            fn()
+            e1.record(self.stream)
+        torch.cuda.synchronize()
+        ts = np.array([e0.elapsed_time(e1) for e0, e1 in evs])
+        return {"median": float(np.median(ts)), "min": float(ts.min()), "mean": float(ts.mean()), "reps": int(reps)}
+
+
+def _find_gfx_clocks(obj, out, under_gfx=False):
+    """MHz values of the graphics clocks anywhere in amd-smi's JSON."""
+    if isinstance(obj, dict):
+        for k, v in obj.items():
+            key = str(k).lower()
+            gfx = under_gfx or key.startswith("gfx")
+            if gfx and key == "clk":
+                val = v.get("value") if isinstance(v, dict) else v
+                try:
+                    out.append(float(val))
+                except (TypeError, ValueError):
+                    pass
+            else:
+                _find_gfx_clocks(v, out, gfx)
+    elif isinstance(obj, list):
+        for v in obj:
+            _find_gfx_clocks(v, out, under_gfx)
+
+
+def sample_clock(torch, replay, seconds: float = 2.0) -> dict | None:
+    """The graphics clock under sustained load: amd-smi sampled from a thread while the layer
+    graph replays back to back."""
+    import shutil
+    import subprocess
+    import threading
+    exe = shutil.which("amd-smi")
+    if exe is None:
+        return None
+    samples, raw = [], []
+    stop = threading.Event()
+
+    def poll():
+        while not stop.is_set():
+            try:
+                r = subprocess.run([exe, "metric", "-g", "0", "-c", "--json"], capture_output=True, text=True,
+                                   timeout=10)
+                raw.append(r.stdout[:400])
+                vals = []
+                _find_gfx_clocks(json.loads(r.stdout), vals)
+                vals = [v for v in vals if v > 0]
+                if vals:
+                    samples.append(float(np.mean(vals)))
+            except Exception:
+                pass
+            time.sleep(0.1)
+
+    th = threading.Thread(target=poll, daemon=True)
+    th.start()
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(20):
+            replay()
+        n += 20
+        torch.cuda.synchronize()
+    stop.set()
+    th.join(timeout=15)
+    if not samples:
+        return {"sclk_mhz_median": None, "samples": 0, "raw": raw[:1]}
+    return {"sclk_mhz_median": float(np.median(samples)), "sclk_mhz_min": float(min(samples)),
+            "sclk_mhz_max": float(max(samples)), "samples": len(samples), "replays": n,
+            "source": "amd-smi metric -c, sampled while the layer graph replays"}
+
+
+def one_core_oracle(cfg_tiny, cfg, inp) -> dict:
+    """The oracle on one BLAS thread: the tiny fp32 workload (median of 5 runs) and the first
+    tokens of the bf16 workload, with fp64 GFLOP/s of the expert and router products."""
+    import moe_inputs as mi
+    import oracle as orc
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:  # pragma: no cover
+        return None
+
+    def flops(c, T):
+        return T * (2.0 * c.d * c.E + c.K * 6.0 * c.d * c.F)
+
+    out = {}
+    with threadpool_limits(limits=1):
+        ti = mi.make(cfg_tiny)
+        ts = []
+        for _ in range(5):
+            t0 = time.perf_counter()
+            orc.forward(ti["x"], ti["w_router"], ti["bias"], ti["w13"], ti["w2"], cfg_tiny.K, cfg_tiny.score,
+                        cfg_tiny.renorm)
+            ts.append(time.perf_counter() - t0)
+        dt = float(np.median(ts))
+        out[cfg_tiny.name] = {"tokens_per_s": cfg_tiny.T / dt, "seconds": dt,
+                              "gflops_fp64": flops(cfg_tiny, cfg_tiny.T) / dt / 1e9}
+        S = min(128, cfg.T)
+        t0 = time.perf_counter()
+        orc.forward(inp["x"][:S], inp["w_router"], inp["bias"], inp["w13"], inp["w2"], cfg.K, cfg.score, cfg.renorm)
+        dt = time.perf_counter() - t0
+        out[cfg.name] = {"tokens_per_s": S / dt, "seconds": dt, "tokens": S,
+                         "gflops_fp64": flops(cfg, S) / dt / 1e9}
+    out["threads"] = 1
+    return out
+
+
+def capture(torch, fn):
+    """fn captured once as a HIP graph (after one run on a side stream, as capture requires)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fn()
+    return graph
+
+
+def time_replays(torch, graph, warmup: int, steps: int) -> float:
+    for _ in range(max(warmup, 1)):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / max(steps, 1)
+
+
+def time_steps(torch, steps, stream, reps: int) -> tuple[dict, float]:
+    """Average duration of each (name, call) over reps eager passes, from HIP events recorded
+    on the launch stream between the calls; and the eager ms per pass."""
+    n = len(steps)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)] for _ in range(reps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for ev in evs:
+        ev[0].record(stream)
+        for i, (_, call) in enumerate(steps):
+            call()
+            ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    eager = (time.perf_counter() - t0) * 1e3 / max(reps, 1)
+    per = np.zeros(n)
+    for ev in evs:
+        per += np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(n)])
+    per /= max(reps, 1)
+    return dict(zip([nm for nm, _ in steps], per.tolist())), eager
 
 
 def main():
@@ -173,6 +348,8 @@ def main():
         return bench_backward(args, torch, moe, mi)
     if args.mxfp8:
         return bench_mxfp8(args, torch, moe, mi)
+    if args.gemm_zipf:
+        return bench_gemm_zipf(args, torch, moe, mi)
     cfg = mi.CONFIGS[args.workload]
     torch.cuda.set_device(0)
     t_gen = time.perf_counter()
@@ -184,78 +361,31 @@ def main():
     bufs = moe.MoEBuffers(cfg.T, cfg.d, cfg.E, cfg.K, cfg.F, dt)
     stream = torch.cuda.current_stream()
 
-    # bf16: the fused router (product + routing in one call); fp32: product, then routing
-    fused = cfg.bf16
-    names = (["router_route"] if fused else ["router", "route"]) + ["permute", "gemm_gate_up", "gemm_down", "combine"]
-    nk = len(names)
-    rr_ws = torch.empty((max(moe.moe_router_route_workspace_size(cfg.T, cfg.E), 256),), dtype=torch.uint8,
-                        device="cuda")
+    # the product's forward, call for call (bf16: the fused router; fp32: product, then routing)
+    steps = moe.forward_steps(x, wr, b, w13, w2, cfg.K, cfg.score, cfg.renorm, bufs)
+    fused = steps[0][0] == "router_route"
 
-    def step(ev=None):
-        def mark(i):
-            if ev is not None:
-                ev[i].record(stream)
-        i = 0
-        mark(i)
-        if fused:
-            moe.moe_router_route(x, wr, b, cfg.K, cfg.score, cfg.renorm, None, bufs.topk_idx, bufs.gates,
-                                 bufs.counts, bufs.offsets, bufs.slot_pos, bufs.row_src, rr_ws)
-        else:
-            moe.moe_router_logits(x, wr, bufs.logits)
-            i += 1
-            mark(i)
-            moe.moe_route(bufs.logits, b, cfg.K, cfg.score, cfg.renorm, bufs.topk_idx, bufs.gates, bufs.counts,
-                          bufs.offsets, bufs.slot_pos, bufs.row_src, bufs.ws)
-        i += 1
-        mark(i)
-        moe.moe_permute(x, cfg.K, bufs.slot_pos, bufs.x_perm)
-        mark(i + 1)
-        moe.moe_grouped_gemm(bufs.x_perm, w13, moe.MOE_LAYOUT_NK, bufs.offsets, bufs.h, moe.MOE_EPI_SWIGLU,
-                             workspace=bufs.gemm_ws)
-        mark(i + 2)
-        moe.moe_grouped_gemm(bufs.h, w2, moe.MOE_LAYOUT_NK, bufs.offsets, bufs.y_perm, moe.MOE_EPI_NONE,
-                             workspace=bufs.gemm_ws)
-        mark(i + 3)
-        moe.moe_unpermute_combine(bufs.y_perm, bufs.slot_pos, bufs.gates, cfg.T, cfg.K, bufs.y)
-        mark(i + 4)
+    def run_all():
+        for _, call in steps:
+            call()
 
     for _ in range(args.warmup):
-        step()
+        run_all()
     torch.cuda.synchronize()
 
     # the layer captured once as a HIP graph (group sizes stay on the device, so one capture
     # serves every routing); the timed region is K replays, one layer forward each
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        step()
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        step()
-    for _ in range(max(args.warmup, 1)):
-        graph.replay()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        graph.replay()
-    torch.cuda.synchronize()
-    ms_per_step = (time.perf_counter() - t0) * 1e3 / max(args.steps, 1)
+    graph = capture(torch, run_all)
+    ms_per_step = time_replays(torch, graph, args.warmup, args.steps)
 
-    # per-kernel breakdown: K eager steps with HIP events on the launch stream around every call
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    eager_ms_per_step = (time.perf_counter() - t0) * 1e3 / max(args.steps, 1)
-    per = np.zeros(len(names))
-    for ev in evs:
-        per += np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(nk)])
-    per /= max(args.steps, 1)
-    kms = dict(zip(names, per.tolist()))
+    # per-kernel breakdown inside the layer: K eager passes, HIP events on the launch stream
+    kms, eager_ms_per_step = time_steps(torch, steps, stream, args.steps)
+
+    # each kernel alone with the caches flushed before every launch (median and min of the reps)
+    cold = ColdTimer(torch, stream)
+    kcold = {name: cold.time(call, args.cold_reps) for name, call in steps}
+    del cold
+    torch.cuda.empty_cache()
 
     M = cfg.T * cfg.K
     esz = 2 if cfg.bf16 else 4
@@ -265,12 +395,14 @@ def main():
     tf_up = flops_up / (kms["gemm_gate_up"] * 1e-3) / 1e12
     tf_down = flops_down / (kms["gemm_down"] * 1e-3) / 1e12
     tf_gg = (flops_up + flops_down) / ((kms["gemm_gate_up"] + kms["gemm_down"]) * 1e-3) / 1e12
-    perm_bytes = (cfg.T + M) * cfg.d * esz + 4 * M
-    comb_bytes = (M + cfg.T) * cfg.d * esz + 8 * M
-    router_bytes = cfg.T * cfg.d * esz + cfg.E * cfg.d * esz + 4 * cfg.T * cfg.E
-    # fused: x and W once, then per slot the index and gate written, its in-tile rank written
-    # and read back, its position and its inverse written
-    router_route_bytes = cfg.T * cfg.d * esz + cfg.E * cfg.d * esz + 24 * M
+    nbytes = {
+        "permute": (cfg.T + M) * cfg.d * esz + 4 * M,
+        "combine": (M + cfg.T) * cfg.d * esz + 8 * M,
+        # fused: x and W once, then per slot the index and gate written, its in-tile rank written
+        # and read back, its position and its inverse written, and the fp32 logits written
+        "router_route": cfg.T * cfg.d * esz + cfg.E * cfg.d * esz + 24 * M + 4 * cfg.T * cfg.E,
+        "router": cfg.T * cfg.d * esz + cfg.E * cfg.d * esz + 4 * cfg.T * cfg.E,
+    }
 
     traffic = None
     try:
@@ -284,14 +416,18 @@ def main():
 
     tokens_per_s = cfg.T / (ms_per_step * 1e-3)
     counts = bufs.counts.cpu().numpy()
+    clock = None if args.no_clock or args.calib_copy else sample_clock(torch, graph.replay)
     # after the timed region; left out of the counter-calibration runs, whose own 512 MiB pass must
     # be the only elementwise kernel of its kind
     copy_gbs = copy_bandwidth(torch) if not args.calib_copy else float("nan")
     cpu = cpu_baseline(cfg, inp, args.cpu_seconds)
-    hbm = {"permute": perm_bytes / (kms["permute"] * 1e-3) / 1e9,
-           "combine": comb_bytes / (kms["combine"] * 1e-3) / 1e9,
-           **({"router_route": router_route_bytes / (kms["router_route"] * 1e-3) / 1e9} if fused else
-              {"router": router_bytes / (kms["router"] * 1e-3) / 1e9})}
+    if cpu is not None and cfg.name != "tiny_fp32":
+        cpu["one_core"] = one_core_oracle(mi.CONFIGS["tiny_fp32"], cfg, inp)
+    hbm_names = [n for n in ("router_route", "router", "permute", "combine") if n in kms]
+    hbm_cold = {n: nbytes[n] / (kcold[n]["median"] * 1e-3) / 1e9 for n in hbm_names}
+    hbm_best = {n: nbytes[n] / (kcold[n]["min"] * 1e-3) / 1e9 for n in hbm_names}
+    hbm_layer = {n: nbytes[n] / (kms[n] * 1e-3) / 1e9 for n in hbm_names}
+    sclk = clock.get("sclk_mhz_median") if clock else None
 
     out = {
         "metric": "MoE layer forward tokens/s (grouped-GEMM TFLOP/s and % of bf16 MFMA peak alongside)",
@@ -310,18 +446,28 @@ def main():
                    "ffn": cfg.F, "score": "sigmoid" if cfg.score else "softmax", "renorm": cfg.renorm,
                    "parallelism": "single GPU"},
         "grouped_gemm": {"tflops": tf_gg, "frac_of_peak": tf_gg / peak, "gate_up_tflops": tf_up,
-                         "down_tflops": tf_down, "flops_per_step": flops_up + flops_down},
+                         "down_tflops": tf_down, "flops_per_step": flops_up + flops_down,
+                         "cold_median_tflops": {"gate_up": flops_up / (kcold["gemm_gate_up"]["median"] * 1e-3) / 1e12,
+                                                "down": flops_down / (kcold["gemm_down"]["median"] * 1e-3) / 1e12}},
         "kernels_ms": kms,
+        "kernels_cold_ms": kcold,
         "timing": {"value": "one HIP-graph replay of the layer per step",
+                   "kernels_ms": "average of K eager passes of the layer, HIP events between the calls",
+                   "kernels_cold_ms": f"each kernel alone, {args.cold_reps} launches, a read-only 1 GiB pass "
+                                      "before each (L2 and Infinity Cache cold)",
                    "eager_ms_per_step": eager_ms_per_step,
                    "eager_tokens_per_s": cfg.T / (eager_ms_per_step * 1e-3)},
-        "hbm_gbs": hbm,
-        # each HBM rate as a fraction of the spec peak (8 TB/s) and of an on-box 1 GiB copy
-        "hbm_frac": {k: {"of_spec": v / 8000.0, "of_onbox_copy": v / copy_gbs} for k, v in hbm.items()},
+        # HBM rates from the cold launches' median (min in hbm_gbs_best); in-layer rates may hit cache
+        "hbm_gbs": hbm_cold,
+        "hbm_gbs_best": hbm_best,
+        "hbm_gbs_in_layer": hbm_layer,
+        "hbm_frac": {k: {"of_spec": v / PEAK_HBM_GBS, "of_onbox_copy": v / copy_gbs} for k, v in hbm_cold.items()},
         "onbox_copy_gbs": copy_gbs,
+        "clock": clock,
         "load": {"min": int(counts.min()), "max": int(counts.max()), "empty": int((counts == 0).sum())},
         "roofline": {"kernel": "grouped GEMM gate/up + SwiGLU", "bound": "mfma", "achieved": tf_up,
-                     "peak": peak, "unit": "TFLOP/s", "frac": tf_up / peak, "traffic": traffic},
+                     "peak": peak, "unit": "TFLOP/s", "frac": tf_up / peak, "traffic": traffic,
+                     **({"frac_of_peak_at_sustained_clock": tf_up / (peak * sclk / 2400.0)} if sclk else {})},
         "cpu_baseline": cpu,
         "input_generation_s": gen_s,
     }
@@ -337,10 +483,11 @@ def main():
 
 
 def bench_backward(args, torch, moe, mi):
-    """Backward of the Mixtral-shaped layer with one expert taking half of the slots and two none:
-    combine backward, SwiGLU-backward dgrad, down wgrad, gate/up dgrad, gate/up wgrad,
-    permute backward, then the router's backward (d_gates -> d_logits -> dWr, and its share of
-    dX); routing held fixed."""
+    """Backward of the Mixtral-shaped layer with one expert taking half of the slots and two none,
+    the product's call sequence (layer_backward with the router): combine backward, SwiGLU-backward
+    dgrad, down wgrad, gate/up dgrad, gate/up wgrad, permute backward, then the router's backward
+    (d_gates -> d_logits -> dWr, and its share of dX); routing held fixed.  Timed as HIP-graph
+    replays of the whole backward."""
     import oracle as orc
     cfg = mi.CONFIGS["mixtral_bwd_skew"]
     torch.cuda.set_device(0)
@@ -350,72 +497,99 @@ def bench_backward(args, torch, moe, mi):
     dev = {k: to_dev(v, torch) for k, v in inp.items()}
     dy = to_dev(mi.upstream_grad(cfg), torch)
     bufs = moe.MoEBuffers(cfg.T, cfg.d, cfg.E, cfg.K, cfg.F, torch.bfloat16, backward=True)
-    moe.layer_forward(dev["x"], dev["w_router"], None, dev["w13"], dev["w2"], cfg.K, cfg.score, cfg.renorm,
-                      bufs, logits=to_dev(logits, torch))
-    stream = torch.cuda.current_stream()
-    b = bufs
-    names = ["combine_bwd", "dgrad_down_dswiglu", "wgrad_down", "dgrad_gate_up", "wgrad_gate_up", "permute_bwd",
-             "route_bwd", "router_bwd"]
-    nk = len(names)
     logits_dev = to_dev(logits, torch)
+    moe.layer_forward(dev["x"], dev["w_router"], None, dev["w13"], dev["w2"], cfg.K, cfg.score, cfg.renorm,
+                      bufs, logits=logits_dev)
+    stream = torch.cuda.current_stream()
+    router = dict(logits=logits_dev, x=dev["x"], w_router=dev["w_router"], bias=None, score=cfg.score,
+                  renorm=cfg.renorm)
+    steps = moe.backward_steps(dy, dev["w13"], dev["w2"], cfg.K, bufs, router=router)
 
-    def step(ev=None):
-        def mark(i):
-            if ev is not None:
-                ev[i].record(stream)
-        mark(0)
-        moe.moe_permute(dy, cfg.K, b.slot_pos, b.dy_perm, row_scale=b.gates, y_perm_dot=b.y_perm,
-                        dgate_out=b.d_gates)
-        mark(1)
-        moe.moe_grouped_gemm(b.dy_perm, dev["w2"], moe.MOE_LAYOUT_KN, b.offsets, b.d_pre, moe.MOE_EPI_DSWIGLU,
-                             epi_in=b.pre)
-        mark(2)
-        moe.moe_grouped_gemm_wgrad(b.h, b.dy_perm, b.offsets, b.dw2)
-        mark(3)
-        moe.moe_grouped_gemm(b.d_pre, dev["w13"], moe.MOE_LAYOUT_KN, b.offsets, b.dx_perm, moe.MOE_EPI_NONE,
-                             workspace=b.gemm_ws)
-        mark(4)
-        moe.moe_grouped_gemm_wgrad(b.x_perm, b.d_pre, b.offsets, b.dw13)
-        mark(5)
-        moe.moe_unpermute_combine(b.dx_perm, b.slot_pos, None, cfg.T, cfg.K, b.dx)
-        mark(6)
-        moe.moe_route_backward(logits_dev, None, b.topk_idx, b.d_gates, cfg.score, cfg.renorm, b.d_logits)
-        mark(7)
-        moe.moe_router_logits_backward(b.d_logits, dev["x"], dev["w_router"], b.dw_router, b.dx, b.rb_ws,
-                                       accumulate=True)
-        mark(8)
+    def run_all():
+        for _, call in steps:
+            call()
 
     for _ in range(args.warmup):
-        step()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(args.steps)]
+        run_all()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / max(args.steps, 1)
-    per = np.zeros(nk)
-    for ev in evs:
-        per += np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(nk)])
-    per /= max(args.steps, 1)
-    kms = dict(zip(names, per.tolist()))
+    graph = capture(torch, run_all)
+    ms = time_replays(torch, graph, args.warmup, args.steps)
+    kms, eager_ms = time_steps(torch, steps, stream, args.steps)
+    cold = ColdTimer(torch, stream)
+    by_name = dict(steps)
+    kcold = {n: cold.time(by_name[n], args.cold_reps) for n in ("combine_bwd", "permute_bwd", "route_bwd",
+                                                                "router_bwd")}
     M = cfg.T * cfg.K
     fl = {"dgrad_down_dswiglu": 2.0 * M * cfg.d * cfg.F, "wgrad_down": 2.0 * M * cfg.d * cfg.F,
           "dgrad_gate_up": 2.0 * M * 2 * cfg.F * cfg.d, "wgrad_gate_up": 2.0 * M * 2 * cfg.F * cfg.d}
     tf = {k: fl[k] / (kms[k] * 1e-3) / 1e12 for k in fl}
     total_fl = sum(fl.values())
+    # combine backward: dY read, dY_perm written, Y_perm read for the gate dot, gates and positions
+    # read, d_gates written; permute backward: dX_perm read, dX written, positions read
+    nb = {"combine_bwd": (cfg.T + 2 * M) * cfg.d * 2 + 12 * M, "permute_bwd": (M + cfg.T) * cfg.d * 2 + 4 * M,
+          # d_logits pass: logits read, d_logits written, indices and d_gates read
+          "route_bwd": 8.0 * cfg.T * cfg.E + 8 * M,
+          # the router products: x read for dWr, dX read and written for its share
+          "router_bwd": 3.0 * cfg.T * cfg.d * 2}
     out = {"metric": "MoE layer backward tokens/s (routing held fixed)", "value": cfg.T / (ms * 1e-3),
            "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
            "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
            "config": {"workload": cfg.name, "tokens": cfg.T, "d_model": cfg.d, "experts": cfg.E, "top_k": cfg.K,
                       "ffn": cfg.F, "hot_expert_slots": int(bufs.counts.max().item()),
                       "empty_experts": int((bufs.counts == 0).sum().item())},
-           "gemm_tflops": tf, "gemm_total_tflops": total_fl / (sum(kms[k] for k in fl) * 1e-3) / 1e12,
-           "kernels_ms": kms,
-           # router backward bytes: the d_logits pass (logits read, d_logits written: 8 T E) and the
-           # product's x read for dWr plus dX read and written for its share (3 T d b)
-           "router_bwd_gbs": {"route_bwd": 8.0 * cfg.T * cfg.E / (kms["route_bwd"] * 1e-3) / 1e9,
-                              "router_bwd": 3.0 * cfg.T * cfg.d * 2 / (kms["router_bwd"] * 1e-3) / 1e9}}
+           "timing": {"value": "one HIP-graph replay of layer_backward (router included) per step",
+                      "eager_ms_per_step": eager_ms},
+           "gemm_tflops": tf, "gemm_frac_of_peak": {k: v / PEAK_BF16_TFLOPS for k, v in tf.items()},
+           "gemm_total_tflops": total_fl / (sum(kms[k] for k in fl) * 1e-3) / 1e12,
+           "kernels_ms": kms, "kernels_cold_ms": kcold,
+           "hbm_gbs": {k: nb[k] / (kcold[k]["median"] * 1e-3) / 1e9 for k in kcold},
+           "hbm_gbs_in_layer": {k: nb[k] / (kms[k] * 1e-3) / 1e9 for k in kcold}}
+    print(json.dumps(out), flush=True)
+
+
+def bench_gemm_zipf(args, torch, moe, mi):
+    """The two grouped GEMMs alone on 32768 rows in 32 groups of exact Zipf(1.2) sizes (ranks
+    1..28 get floor(M r^-1.2 / H) rows, 4 groups none) at the DeepSeek-V3-share widths: the
+    reading of "32768 routed tokens" as pre-routed rows with exact Zipf group sizes."""
+    cfg = mi.CONFIGS["dsv3_share"]
+    torch.cuda.set_device(0)
+    M = 32768
+    sizes = mi.zipf_group_sizes(M, cfg.E)
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    a = mi.normal(cfg.seed, mi.TAG_X, (M, cfg.d), 1.0, True)
+    wts = mi.make(cfg, rows=1)
+    A, w13, w2 = to_dev(a, torch), to_dev(wts["w13"], torch), to_dev(wts["w2"], torch)
+    offs = torch.from_numpy(off).cuda()
+    H = torch.empty((M, cfg.F), dtype=torch.bfloat16, device="cuda")
+    Y = torch.empty((M, cfg.d), dtype=torch.bfloat16, device="cuda")
+    ws = torch.zeros((moe.moe_grouped_gemm_workspace_size(),), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    steps = [("gemm_gate_up", lambda: moe.moe_grouped_gemm(A, w13, moe.MOE_LAYOUT_NK, offs, H, moe.MOE_EPI_SWIGLU,
+                                                           workspace=ws)),
+             ("gemm_down", lambda: moe.moe_grouped_gemm(H, w2, moe.MOE_LAYOUT_NK, offs, Y, moe.MOE_EPI_NONE,
+                                                        workspace=ws))]
+
+    def run_all():
+        for _, call in steps:
+            call()
+
+    for _ in range(args.warmup):
+        run_all()
+    graph = capture(torch, run_all)
+    ms = time_replays(torch, graph, args.warmup, max(args.steps, 100))
+    kms, _ = time_steps(torch, steps, stream, max(args.steps, 100))
+    fl_up, fl_down = 2.0 * M * 2 * cfg.F * cfg.d, 2.0 * M * cfg.F * cfg.d
+    tf_up = fl_up / (kms["gemm_gate_up"] * 1e-3) / 1e12
+    tf_down = fl_down / (kms["gemm_down"] * 1e-3) / 1e12
+    out = {"metric": "grouped GEMM TFLOP/s, exact Zipf(1.2) group sizes (GEMMs only)",
+           "value": (fl_up + fl_down) / (ms * 1e-3) / 1e12, "unit": "TFLOP/s", "n_gpus": 1,
+           "steps": max(args.steps, 100), "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+           "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "dsv3_share_zipf_rows", "rows": M, "groups": cfg.E, "d_model": cfg.d,
+                      "ffn": cfg.F, "group_sizes": sorted(sizes.tolist(), reverse=True)},
+           "kernels_ms": kms, "gate_up_tflops": tf_up, "down_tflops": tf_down,
+           "frac_of_peak": {"gate_up": tf_up / PEAK_BF16_TFLOPS, "down": tf_down / PEAK_BF16_TFLOPS,
+                            "both": (fl_up + fl_down) / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}}
     print(json.dumps(out), flush=True)
 
 

@@ -373,4 +373,4 @@ def moe_permute_mx(codes, scales, K: int, slot_pos, codes_perm, scales_perm, str
           _stream(stream))
 
 
-from .layer import MoEBuffers, layer_backward, layer_forward  # noqa: E402,F401
+from .layer import MoEBuffers, backward_steps, forward_steps, layer_backward, layer_forward  # noqa: E402,F401

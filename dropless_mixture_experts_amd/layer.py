@@ -73,29 +73,69 @@ class MoEBuffers:
                                      dtype=torch.uint8, device=dev)
 
 
+def forward_steps(x, w_router, bias, w13, w2, K: int, score: int, renorm: bool, bufs: MoEBuffers, logits=None,
+                  stream=None):
+    """The forward as (name, call) pairs in launch order: one C-ABI call each.
+
+    ``logits`` (fp32 [T, E]) skips the router product and routes on the given values."""
+    b = bufs
+    steps = []
+    if logits is None and b.fused_router:
+        # product and routing in one call; the logits are still written for the router backward
+        steps.append(("router_route", lambda: moe_router_route(
+            x, w_router, bias, K, score, renorm, b.logits, b.topk_idx, b.gates, b.counts, b.offsets, b.slot_pos,
+            b.row_src, b.rr_ws, stream=stream)))
+    else:
+        if logits is None:
+            steps.append(("router", lambda: moe_router_logits(x, w_router, b.logits, stream=stream)))
+            logits = b.logits
+        steps.append(("route", lambda: moe_route(logits, bias, K, score, renorm, b.topk_idx, b.gates, b.counts,
+                                                 b.offsets, b.slot_pos, b.row_src, b.ws, stream=stream)))
+    steps += [
+        ("permute", lambda: moe_permute(x, K, b.slot_pos, b.x_perm, stream=stream)),
+        ("gemm_gate_up", lambda: moe_grouped_gemm(b.x_perm, w13, MOE_LAYOUT_NK, b.offsets, b.h, MOE_EPI_SWIGLU,
+                                                  epi_save=b.pre, workspace=b.gemm_ws, stream=stream)),
+        ("gemm_down", lambda: moe_grouped_gemm(b.h, w2, MOE_LAYOUT_NK, b.offsets, b.y_perm, MOE_EPI_NONE,
+                                               workspace=b.gemm_ws, stream=stream)),
+        ("combine", lambda: moe_unpermute_combine(b.y_perm, b.slot_pos, b.gates, b.T, K, b.y, stream=stream)),
+    ]
+    return steps
+
+
 def layer_forward(x, w_router, bias, w13, w2, K: int, score: int, renorm: bool, bufs: MoEBuffers,
                   logits=None, stream=None):
     """y = combine(down(SwiGLU(gate_up(permute(x))))) with top-K routing; returns bufs.y.
 
     ``logits`` (fp32 [T, E]) skips the router product and routes on the given values."""
+    for _, call in forward_steps(x, w_router, bias, w13, w2, K, score, renorm, bufs, logits, stream):
+        call()
+    return bufs.y
+
+
+def backward_steps(dy, w13, w2, K: int, bufs: MoEBuffers, stream=None, router=None):
+    """The backward as (name, call) pairs in launch order (routing of the last forward held fixed)."""
     b = bufs
-    if logits is None and b.fused_router:
-        # product and routing in one call; the logits are still written for the router backward
-        moe_router_route(x, w_router, bias, K, score, renorm, b.logits, b.topk_idx, b.gates, b.counts,
-                         b.offsets, b.slot_pos, b.row_src, b.rr_ws, stream=stream)
-    else:
-        if logits is None:
-            moe_router_logits(x, w_router, b.logits, stream=stream)
-            logits = b.logits
-        moe_route(logits, bias, K, score, renorm, b.topk_idx, b.gates, b.counts, b.offsets, b.slot_pos,
-                  b.row_src, b.ws, stream=stream)
-    moe_permute(x, K, b.slot_pos, b.x_perm, stream=stream)
-    moe_grouped_gemm(b.x_perm, w13, MOE_LAYOUT_NK, b.offsets, b.h, MOE_EPI_SWIGLU, epi_save=b.pre,
-                     workspace=b.gemm_ws, stream=stream)
-    moe_grouped_gemm(b.h, w2, MOE_LAYOUT_NK, b.offsets, b.y_perm, MOE_EPI_NONE, workspace=b.gemm_ws,
-                     stream=stream)
-    moe_unpermute_combine(b.y_perm, b.slot_pos, b.gates, b.T, K, b.y, stream=stream)
-    return b.y
+    steps = [
+        ("combine_bwd", lambda: moe_permute(dy, K, b.slot_pos, b.dy_perm, row_scale=b.gates, y_perm_dot=b.y_perm,
+                                            dgate_out=b.d_gates, stream=stream)),
+        ("dgrad_down_dswiglu", lambda: moe_grouped_gemm(b.dy_perm, w2, MOE_LAYOUT_KN, b.offsets, b.d_pre,
+                                                        MOE_EPI_DSWIGLU, epi_in=b.pre, workspace=b.gemm_ws,
+                                                        stream=stream)),
+        ("wgrad_down", lambda: moe_grouped_gemm_wgrad(b.h, b.dy_perm, b.offsets, b.dw2, stream=stream)),
+        ("dgrad_gate_up", lambda: moe_grouped_gemm(b.d_pre, w13, MOE_LAYOUT_KN, b.offsets, b.dx_perm, MOE_EPI_NONE,
+                                                   workspace=b.gemm_ws, stream=stream)),
+        ("wgrad_gate_up", lambda: moe_grouped_gemm_wgrad(b.x_perm, b.d_pre, b.offsets, b.dw13, stream=stream)),
+        ("permute_bwd", lambda: moe_unpermute_combine(b.dx_perm, b.slot_pos, None, b.T, K, b.dx, stream=stream)),
+    ]
+    if router is not None:
+        steps += [
+            ("route_bwd", lambda: moe_route_backward(router["logits"], router.get("bias"), b.topk_idx, b.d_gates,
+                                                     router["score"], router["renorm"], b.d_logits, stream=stream)),
+            ("router_bwd", lambda: moe_router_logits_backward(b.d_logits, router["x"], router["w_router"],
+                                                              b.dw_router, b.dx, b.rb_ws, accumulate=True,
+                                                              stream=stream)),
+        ]
+    return steps
 
 
 def layer_backward(dy, w13, w2, K: int, bufs: MoEBuffers, stream=None, router=None):
@@ -104,19 +144,6 @@ def layer_backward(dy, w13, w2, K: int, bufs: MoEBuffers, stream=None, router=No
     Returns (dx, dw13, dw2, d_gates) in bufs.  With ``router`` = dict(logits, x, w_router,
     bias, score, renorm) of that forward, also takes d_gates back through the gates (top-K
     held fixed) to bufs.d_logits and bufs.dw_router, and adds the router's share to dx."""
-    b = bufs
-    moe_permute(dy, K, b.slot_pos, b.dy_perm, row_scale=b.gates, y_perm_dot=b.y_perm, dgate_out=b.d_gates,
-                stream=stream)
-    moe_grouped_gemm(b.dy_perm, w2, MOE_LAYOUT_KN, b.offsets, b.d_pre, MOE_EPI_DSWIGLU, epi_in=b.pre,
-                     workspace=b.gemm_ws, stream=stream)
-    moe_grouped_gemm_wgrad(b.h, b.dy_perm, b.offsets, b.dw2, stream=stream)
-    moe_grouped_gemm(b.d_pre, w13, MOE_LAYOUT_KN, b.offsets, b.dx_perm, MOE_EPI_NONE, workspace=b.gemm_ws,
-                     stream=stream)
-    moe_grouped_gemm_wgrad(b.x_perm, b.d_pre, b.offsets, b.dw13, stream=stream)
-    moe_unpermute_combine(b.dx_perm, b.slot_pos, None, b.T, K, b.dx, stream=stream)
-    if router is not None:
-        moe_route_backward(router["logits"], router.get("bias"), b.topk_idx, b.d_gates, router["score"],
-                           router["renorm"], b.d_logits, stream=stream)
-        moe_router_logits_backward(b.d_logits, router["x"], router["w_router"], b.dw_router, b.dx, b.rb_ws,
-                                   accumulate=True, stream=stream)
-    return b.dx, b.dw13, b.dw2, b.d_gates
+    for _, call in backward_steps(dy, w13, w2, K, bufs, stream, router):
+        call()
+    return bufs.dx, bufs.dw13, bufs.dw2, bufs.d_gates

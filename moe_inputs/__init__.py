@@ -167,6 +167,25 @@ def router_bias(cfg: MoEConfig) -> np.ndarray | None:
     raise ValueError(cfg.bias)
 
 
+def zipf_group_sizes(M: int, E: int, dead: int = 4, s: float = 1.2, seed: int = 4) -> np.ndarray:
+    """Rows per expert group for a GEMM-only workload with an exact Zipf(s) load: the group of
+    rank r (1 .. E - dead) gets floor(M r^-s / H) rows, H = sum of r^-s over those ranks, the
+    remainder goes to rank 1, and the last ``dead`` ranks get none.  Ranks are dealt to
+    experts by the DeepSeek-V3-share permutation stream (tag TAG_RANKS), so the largest
+    group is not always the first."""
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, TAG_RANKS])))
+    ranks = g.permutation(E) + 1
+    live = E - dead
+    w = np.arange(1, live + 1, dtype=np.float64) ** -s
+    by_rank = np.floor(M * w / w.sum()).astype(np.int64)
+    by_rank[0] += M - by_rank.sum()
+    sizes = np.zeros(E, np.int64)
+    for e in range(E):
+        if ranks[e] <= live:
+            sizes[e] = by_rank[ranks[e] - 1]
+    return sizes
+
+
 def make(cfg: MoEConfig, rows: int | None = None, weights: bool = True) -> dict:
     """All layer inputs of ``cfg`` as host arrays.
 
