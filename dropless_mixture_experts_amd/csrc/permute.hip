@@ -6,10 +6,11 @@
 // "What specialised optimisations does dropless MoE need?").  Both are pure
 // HBM streams over token rows: one wave per token moves whole rows with 16-byte
 // lanes, so every row is read once and written once as full 64-byte segments.
-// Measured with the caches cold (as they are between the grouped GEMMs): the
-// forward permute is fastest with ordinary loads and stores (the GEMM reads x_perm
-// next); combine, and the backward permute's streams of Y_perm and dY_perm, with
-// non-temporal accesses.
+// Measured with the caches flushed before each launch, on the three workload shapes:
+// non-temporal stores cost 5-25% everywhere, so every output is written with ordinary
+// stores; combine reads its gathered rows non-temporally (2-4% faster than ordinary
+// loads except on one shape); rows of 512 or more 16-byte vectors move in passes of 4
+// vectors per lane (3% faster on 4096-wide bf16 rows), shorter rows in one pass of 8.
 #include "common.h"
 #include "internal.h"
 
@@ -18,7 +19,6 @@ namespace moe {
 namespace {
 
 constexpr int kRowsPerBlock = 4;  // one wave per row
-constexpr int kUnroll = 8;   // 16-byte vectors in flight per lane (permute: a whole 4096-wide bf16 row)
 constexpr int kCUnroll = 8;  // 16-byte vectors per lane per gathered row (combine)
 
 // x_perm[slot_pos[s]] = (scale_s *) x[t] for the K slots s = t K + k of token t; optional
@@ -26,7 +26,8 @@ constexpr int kCUnroll = 8;  // 16-byte vectors per lane per gathered row (combi
 // HBM once and written to its K rows.  Without the dot, every loaded piece of the row goes
 // straight to all K rows; with it, the slots are taken one by one (the row comes back from
 // the cache) so that each slot's dot product is a single wave reduction.
-template <typename T, bool SCALE, bool DOT>
+// UN: 16-byte vectors in flight per lane per pass over the row.
+template <typename T, bool SCALE, bool DOT, int UN = 8>
 __global__ __launch_bounds__(256) void permute_kernel(const uint4* __restrict__ x, int64_t nvec, int K,
                                                       const int32_t* __restrict__ slot_pos,
                                                       const float* __restrict__ row_scale,
@@ -48,10 +49,10 @@ __global__ __launch_bounds__(256) void permute_kernel(const uint4* __restrict__ 
   }
   const uint4* src = x + t * nvec;
   if constexpr (!DOT) {
-    for (int64_t i0 = 0; i0 < nvec; i0 += 64 * kUnroll) {
-      uint4 v[kUnroll];
+    for (int64_t i0 = 0; i0 < nvec; i0 += 64 * UN) {
+      uint4 v[UN];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
+      for (int u = 0; u < UN; ++u) {
         const int64_t i = i0 + u * 64 + lane;
         if (i < nvec) v[u] = src[i];
       }
@@ -59,7 +60,7 @@ __global__ __launch_bounds__(256) void permute_kernel(const uint4* __restrict__ 
         const int64_t p = __shfl(pos, k, 64);
         const float sc = __shfl(sk, k, 64);
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
+        for (int u = 0; u < UN; ++u) {
           const int64_t i = i0 + u * 64 + lane;
           if (i < nvec) {
             uint4 o = v[u];
@@ -70,7 +71,7 @@ __global__ __launch_bounds__(256) void permute_kernel(const uint4* __restrict__ 
               for (int q = 0; q < E::kVec; ++q) f[q] *= sc;
               o = E::from_f32(f);
             }
-            xp[p * nvec + i] = o;  // plain stores: the grouped GEMM reads these rows next
+            xp[p * nvec + i] = o;
           }
         }
       }
@@ -81,10 +82,10 @@ __global__ __launch_bounds__(256) void permute_kernel(const uint4* __restrict__ 
       const float sc = __shfl(sk, k, 64);
       const uint4* yd = ydot + p * nvec;
       float dot = 0.f;
-      for (int64_t i0 = 0; i0 < nvec; i0 += 64 * kUnroll) {
-        uint4 v[kUnroll], w[kUnroll];
+      for (int64_t i0 = 0; i0 < nvec; i0 += 64 * UN) {
+        uint4 v[UN], w[UN];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
+        for (int u = 0; u < UN; ++u) {
           const int64_t i = i0 + u * 64 + lane;
           if (i < nvec) {
             v[u] = src[i];  // read once from HBM, again from the cache for the other slots
@@ -92,7 +93,7 @@ __global__ __launch_bounds__(256) void permute_kernel(const uint4* __restrict__ 
           }
         }
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
+        for (int u = 0; u < UN; ++u) {
           const int64_t i = i0 + u * 64 + lane;
           if (i < nvec) {
             float f[E::kVec], g[E::kVec];
@@ -106,7 +107,7 @@ __global__ __launch_bounds__(256) void permute_kernel(const uint4* __restrict__ 
               for (int q = 0; q < E::kVec; ++q) f[q] *= sc;
               o = E::from_f32(f);
             }
-            st_nt(xp + p * nvec + i, o);
+            xp[p * nvec + i] = o;
           }
         }
       }
@@ -174,7 +175,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
 #pragma unroll
     for (int u = 0; u < kCUnroll; ++u) {
       const int64_t i = i0 + u * 64 + lane;
-      if (i < nvec) st_nt(y + t * nvec + i, E::from_f32(acc[u]));
+      if (i < nvec) y[t * nvec + i] = E::from_f32(acc[u]);
     }
   }
 }
@@ -197,6 +198,9 @@ hipError_t permute_t(const void* x, int64_t T_, int64_t d, int K, const int32_t*
                        row_scale, yv, dgate, o, T_);
   else if (dot)
     hipLaunchKernelGGL((permute_kernel<T, false, true>), grid, dim3(256), 0, s, xv, nvec, K, slot_pos,
+                       row_scale, yv, dgate, o, T_);
+  else if (nvec >= 512)
+    hipLaunchKernelGGL((permute_kernel<T, false, false, 4>), grid, dim3(256), 0, s, xv, nvec, K, slot_pos,
                        row_scale, yv, dgate, o, T_);
   else
     hipLaunchKernelGGL((permute_kernel<T, false, false>), grid, dim3(256), 0, s, xv, nvec, K, slot_pos,
