@@ -1377,12 +1377,22 @@ struct Out {
     const int c = lane % kCPR, rr = lane / kCPR;
     const int64_t col = col0 + c * 8;
     const bool cok = col < ncols;
+    // in batches of 8 rows: the 8 LDS reads are in flight together before the 8 stores (one
+    // read, wait, store at a time left each store waiting for its own read)
+    constexpr int kIt = NR / kRPI, kB = kIt < 8 ? kIt : 8;
 #pragma unroll
-    for (int it = 0; it < NR / kRPI; ++it) {
-      const int r = it * kRPI + rr;
-      const uint4 v = *(const uint4*)(wl + r * kRowBytes + ((c ^ (r % kCPR)) * 16));
-      const int64_t row = row0 + r;
-      if (cok && row < re) st_nt((uint4*)(base + row * ld + col * 2), v);
+    for (int i0 = 0; i0 < kIt; i0 += kB) {
+      uint4 v[kB];
+#pragma unroll
+      for (int u = 0; u < kB; ++u) {
+        const int r = (i0 + u) * kRPI + rr;
+        v[u] = *(const uint4*)(wl + r * kRowBytes + ((c ^ (r % kCPR)) * 16));
+      }
+#pragma unroll
+      for (int u = 0; u < kB; ++u) {
+        const int64_t row = row0 + (i0 + u) * kRPI + rr;
+        if (cok && row < re) st_nt((uint4*)(base + row * ld + col * 2), v[u]);
+      }
     }
   }
 };
@@ -1511,20 +1521,27 @@ __device__ __forceinline__ void store_tile_dswiglu_lds(const GemmParams& p, cons
   }
 }
 
+// In batches of 16 float4 (four accumulator tiles): the loads of a batch are in flight together
+// (one load, wait, add at a time made the reduction of a split tile latency-bound).
 __device__ __forceinline__ void load_partial(const GemmParams& p, int slot, f32x16 (&acc)[4][4], bool add) {
   const float4* src = part_ptr(p, slot);
 #pragma unroll
-  for (int t = 0; t < 16; ++t)
+  for (int t0 = 0; t0 < 16; t0 += 4) {
+    float4 v[16];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float4 v = src[(t * 4 + e) * 64];
+    for (int u = 0; u < 16; ++u) v[u] = src[(t0 * 4 + u) * 64];
+    __builtin_amdgcn_sched_barrier(0);  // keep the batch's loads ahead of its adds
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int t = t0 + u / 4, e = u % 4;
       f32x16& a = acc[t >> 2][t & 3];
       if (add) {
-        a[4 * e] += v.x; a[4 * e + 1] += v.y; a[4 * e + 2] += v.z; a[4 * e + 3] += v.w;
+        a[4 * e] += v[u].x; a[4 * e + 1] += v[u].y; a[4 * e + 2] += v[u].z; a[4 * e + 3] += v[u].w;
       } else {
-        a[4 * e] = v.x; a[4 * e + 1] = v.y; a[4 * e + 2] = v.z; a[4 * e + 3] = v.w;
+        a[4 * e] = v[u].x; a[4 * e + 1] = v[u].y; a[4 * e + 2] = v[u].z; a[4 * e + 3] = v[u].w;
       }
     }
+  }
 }
 
 }  // namespace ring4
