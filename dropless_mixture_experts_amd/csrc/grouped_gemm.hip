@@ -1807,18 +1807,33 @@ __device__ __forceinline__ void store_wgrad_lds(float* out, const f32x16 (&acc)[
           const f32x16& a = acc[i0 + di][j];
           *(float4*)(wl + r * 512 + chunk * 16) = make_float4(a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]);
         }
+    // in batches of 8 rows: a batch's LDS reads (and, accumulating, its dW loads) are all in
+    // flight before its first store, not one read, wait and store at a time
 #pragma unroll
-    for (int it = 0; it < 32; ++it) {
-      const int r = it * 2 + rr;
-      float4 v = *(const float4*)(wl + r * 512 + ((c ^ (r & 31)) * 16));
-      const int64_t row = row0 + i0 * 32 + r;
-      if (cok && row < N) {
-        float4* dst = (float4*)(out + row * Kd + col);
-        if (accumulate) {
-          const float4 o = *dst;
-          v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
+    for (int i1 = 0; i1 < 32; i1 += 8) {
+      float4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int r = (i1 + u) * 2 + rr;
+        v[u] = *(const float4*)(wl + r * 512 + ((c ^ (r & 31)) * 16));
+      }
+      if (accumulate) {
+        float4 o[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int64_t row = row0 + i0 * 32 + (i1 + u) * 2 + rr;
+          o[u] = cok && row < N ? *(const float4*)(out + row * Kd + col) : make_float4(0.f, 0.f, 0.f, 0.f);
         }
-        *dst = v;
+        __builtin_amdgcn_sched_barrier(0);  // keeps the 8 loads ahead of the first add
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          v[u].x += o[u].x; v[u].y += o[u].y; v[u].z += o[u].z; v[u].w += o[u].w;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t row = row0 + i0 * 32 + (i1 + u) * 2 + rr;
+        if (cok && row < N) *(float4*)(out + row * Kd + col) = v[u];
       }
     }
   }

@@ -157,13 +157,15 @@ __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory
 __device__ const uint4 kZeroChunk = {0u, 0u, 0u, 0u};  // source of the d tail past the row end
 
 // TT = token tiles of 32 (the workgroup's tokens), NF = expert tiles of 32
-// (E <= 32 NF), D = ring stages.  Waves: NE groups over the expert tiles (NFW
-// each) x NKS over the four 16-element k steps of a stage.
+// (E <= 32 NF), D = ring stages, SPB = stages per barrier (D >= 2 SPB).  Waves: NE groups
+// over the expert tiles (NFW each) x NKS over the four 16-element k steps of a stage.
+// A barrier publishes SPB landed stages at once and frees the SPB slots read before it, which
+// are refilled right after it; the ring then holds D - 2 SPB stages in flight beyond them.
 // FUSE: after the product, the tile's logits stay in LDS and the same workgroup routes its
 // tokens there (top-K, scores, gates, the tile's expert histogram and in-tile ranks; G lanes
 // of KPL keys per token), so that the logits need not return from HBM (they are still written
 // when `logits` is given).
-template <int TT, int NF, int D, bool FUSE = false, int G = 1, int KPL = 1>
+template <int TT, int NF, int D, int SPB, bool FUSE = false, int G = 1, int KPL = 1>
 __global__ __launch_bounds__(kThreads) void router_ring_kernel(const bf16_t* __restrict__ x,
                                                                const bf16_t* __restrict__ w,
                                                                int64_t T_, int64_t d, int E,
@@ -183,6 +185,7 @@ __global__ __launch_bounds__(kThreads) void router_ring_kernel(const bf16_t* __r
   constexpr int kSlotBytes = (kBT + EP) * kRowBytes;
   static_assert(NE * NKS == 4 && NE * NFW == NF, "wave split");
   static_assert(D >= 2 && D * kSlotBytes <= kLdsBytes, "ring size");
+  static_assert(SPB >= 1 && D >= 2 * SPB, "a barrier's stages and the ones refilled after it");
   __shared__ uint4 smem[D * kSlotBytes / 16];
 
   const int lane = threadIdx.x & 63;
@@ -251,29 +254,36 @@ __global__ __launch_bounds__(kThreads) void router_ring_kernel(const bf16_t* __r
       for (int r = 0; r < 16; ++r) acc[tt][f][r] = 0.f;
 
 #pragma unroll
-  for (int s = 0; s < D - 1; ++s)
+  for (int s = 0; s < D - SPB; ++s)
     if (s < nk) issue(s);
   const char* lbase = (const char*)smem;
-  for (int s = 0; s < nk; ++s) {
-    wait_ahead<NQ, D - 2>(min(nk - 1 - s, D - 2));
-    barrier();  // stage s has landed for every wave; slot (s - 1) % D is read by none
-    if (s + D - 1 < nk) issue(s + D - 1);
-    const char* slot = lbase + (s % D) * kSlotBytes;
+  for (int s = 0; s < nk; s += SPB) {
+    // stages s .. s + SPB - 1 landed (at most D - 2 SPB later stages still in flight)
+    wait_ahead<NQ, D - 2 * SPB>(max(0, min(nk - s - SPB, D - 2 * SPB)));
+    barrier();  // ... for every wave; the slots of stages s - SPB .. s - 1 are read by none
 #pragma unroll
-    for (int j = 0; j < 4 / NKS; ++j) {
-      const int c = 2 * (ks + j * NKS) + hi;  // logical chunk of this lane's 8 k values
-      uint4 a[TT], b[NFW];
+    for (int u = 0; u < SPB; ++u)
+      if (s + D - SPB + u < nk) issue(s + D - SPB + u);
 #pragma unroll
-      for (int tt = 0; tt < TT; ++tt) a[tt] = *(const uint4*)(slot + aoff[tt] + ((c ^ aswz[tt]) << 4));
+    for (int u = 0; u < SPB; ++u) {
+      if (s + u >= nk) break;
+      const char* slot = lbase + ((s + u) % D) * kSlotBytes;
 #pragma unroll
-      for (int f = 0; f < NFW; ++f) b[f] = *(const uint4*)(slot + boff[f] + ((c ^ bswz[f]) << 4));
+      for (int j = 0; j < 4 / NKS; ++j) {
+        const int c = 2 * (ks + j * NKS) + hi;  // logical chunk of this lane's 8 k values
+        uint4 a[TT], b[NFW];
 #pragma unroll
-      for (int tt = 0; tt < TT; ++tt)
+        for (int tt = 0; tt < TT; ++tt) a[tt] = *(const uint4*)(slot + aoff[tt] + ((c ^ aswz[tt]) << 4));
 #pragma unroll
-        for (int f = 0; f < NFW; ++f)
-          acc[tt][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[tt]),
-                                                              __builtin_bit_cast(bf16x8, b[f]),
-                                                              acc[tt][f], 0, 0, 0);
+        for (int f = 0; f < NFW; ++f) b[f] = *(const uint4*)(slot + boff[f] + ((c ^ bswz[f]) << 4));
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+          for (int f = 0; f < NFW; ++f)
+            acc[tt][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[tt]),
+                                                                __builtin_bit_cast(bf16x8, b[f]),
+                                                                acc[tt][f], 0, 0, 0);
+      }
     }
   }
 
@@ -379,6 +389,17 @@ __global__ __launch_bounds__(kThreads) void router_ring_kernel(const bf16_t* __r
 
 }  // namespace rring
 
+// Stages per barrier of each ring shape (tokens x experts x depth): 1x32x16, 2x32x8, 1x64x13,
+// 2x64x10, 2x128x6, 2x256x4.  Measured with the caches flushed: four stages a barrier make the
+// 32-token, 8-expert ring (the Mixtral shape) 4% faster; two stages left the 64-token rings
+// unchanged (32 experts) or 2% slower (128 experts), so those keep one.
+#define SPB_A 4
+#define SPB_B 1
+#define SPB_C 1
+#define SPB_D 1
+#define SPB_E 1
+#define SPB_F 1
+
 // 32-token workgroups when few experts leave fewer than about 1.5 workgroups of
 // 64 tokens per CU, so that every CU streams x; deeper rings where stages are small.
 hipError_t router_ring(const void* x, const void* w, int64_t T_, int64_t d, int E, float* logits,
@@ -388,19 +409,19 @@ hipError_t router_ring(const void* x, const void* w, int64_t T_, int64_t d, int 
   const bf16_t* wb = (const bf16_t*)w;
   const int nf = (E + 31) / 32;
   const bool small_t = (T_ + 63) / 64 < 384;
-#define MOE_ROUTER_RING(tt, nfe, depth)                                                         \
-  hipLaunchKernelGGL((router_ring_kernel<tt, nfe, depth>), dim3((unsigned)((T_ + 32 * tt - 1) / (32 * tt))), \
+#define MOE_ROUTER_RING(tt, nfe, depth, spb)                                                    \
+  hipLaunchKernelGGL((router_ring_kernel<tt, nfe, depth, spb>), dim3((unsigned)((T_ + 32 * tt - 1) / (32 * tt))), \
                      dim3(kThreads), 0, s, xb, wb, T_, d, E, logits)
   if (nf <= 1) {
-    if (small_t) MOE_ROUTER_RING(1, 1, 16);
-    else MOE_ROUTER_RING(2, 1, 8);
+    if (small_t) MOE_ROUTER_RING(1, 1, 16, SPB_A);
+    else MOE_ROUTER_RING(2, 1, 8, SPB_B);
   } else if (nf <= 2) {
-    if (small_t) MOE_ROUTER_RING(1, 2, 13);
-    else MOE_ROUTER_RING(2, 2, 10);
+    if (small_t) MOE_ROUTER_RING(1, 2, 13, SPB_C);
+    else MOE_ROUTER_RING(2, 2, 10, SPB_D);
   } else if (nf <= 4) {
-    MOE_ROUTER_RING(2, 4, 6);
+    MOE_ROUTER_RING(2, 4, 6, SPB_E);
   } else {
-    MOE_ROUTER_RING(2, 8, 4);
+    MOE_ROUTER_RING(2, 8, 4, SPB_F);
   }
 #undef MOE_ROUTER_RING
   return hipGetLastError();
@@ -425,26 +446,26 @@ hipError_t router_route(const void* x, const void* w, const float* bias, int64_t
   int32_t* hist = (int32_t*)ws;
   if (nch > 0) {
     const dim3 grid((unsigned)nch);
-#define MOE_ROUTER_FUSED(tt, nfe, depth, g, kpl)                                                        \
-  hipLaunchKernelGGL((router_ring_kernel<tt, nfe, depth, true, g, kpl>), grid, dim3(kThreads), 0, s, xb, wb, \
+#define MOE_ROUTER_FUSED(tt, nfe, depth, spb, g, kpl)                                                   \
+  hipLaunchKernelGGL((router_ring_kernel<tt, nfe, depth, spb, true, g, kpl>), grid, dim3(kThreads), 0, s, xb, wb, \
                      T_, d, E, logits, bias, K, score, renorm, topk_idx, topk_gate, slot_pos, hist)
     if (nf <= 1) {
       if (chunk == 32) {
-        if (E <= 8) MOE_ROUTER_FUSED(1, 1, 16, 1, 8);
-        else if (E <= 16) MOE_ROUTER_FUSED(1, 1, 16, 1, 16);
-        else MOE_ROUTER_FUSED(1, 1, 16, 2, 16);
+        if (E <= 8) MOE_ROUTER_FUSED(1, 1, 16, SPB_A, 1, 8);
+        else if (E <= 16) MOE_ROUTER_FUSED(1, 1, 16, SPB_A, 1, 16);
+        else MOE_ROUTER_FUSED(1, 1, 16, SPB_A, 2, 16);
       } else {
-        if (E <= 8) MOE_ROUTER_FUSED(2, 1, 8, 1, 8);
-        else if (E <= 16) MOE_ROUTER_FUSED(2, 1, 8, 1, 16);
-        else MOE_ROUTER_FUSED(2, 1, 8, 2, 16);
+        if (E <= 8) MOE_ROUTER_FUSED(2, 1, 8, SPB_B, 1, 8);
+        else if (E <= 16) MOE_ROUTER_FUSED(2, 1, 8, SPB_B, 1, 16);
+        else MOE_ROUTER_FUSED(2, 1, 8, SPB_B, 2, 16);
       }
     } else if (nf <= 2) {
-      if (chunk == 32) MOE_ROUTER_FUSED(1, 2, 13, 4, 16);
-      else MOE_ROUTER_FUSED(2, 2, 10, 4, 16);
+      if (chunk == 32) MOE_ROUTER_FUSED(1, 2, 13, SPB_C, 4, 16);
+      else MOE_ROUTER_FUSED(2, 2, 10, SPB_D, 4, 16);
     } else if (nf <= 4) {
-      MOE_ROUTER_FUSED(2, 4, 6, 8, 16);
+      MOE_ROUTER_FUSED(2, 4, 6, SPB_E, 8, 16);
     } else {
-      MOE_ROUTER_FUSED(2, 8, 4, 16, 16);
+      MOE_ROUTER_FUSED(2, 8, 4, SPB_F, 16, 16);
     }
 #undef MOE_ROUTER_FUSED
     const hipError_t e = hipGetLastError();
