@@ -1071,6 +1071,7 @@ struct Pipe {
   uint32_t ch[4];            // per lane: byte offset of the 16-byte chunk of sub-step kk
   uint32_t b_row = 0;        // KN, per lane: byte offset of K row 8 hi + e within a slot
   uint32_t a_seg[4];         // WG, per lane: segment and 8-byte part of A fragment i
+                             // (WG: a_seg and b_off also hold the LDS base and b_row)
   int64_t b_stage = kStageBytes;  // uniform: global bytes of B per stage
   int64_t a_stage = kStageBytes;  // uniform: global bytes of A per stage (WG)
   int kvalid = 1 << 30;      // WG: rows of the reduction; DMAs of rows past them write zeros
@@ -1092,6 +1093,14 @@ struct Pipe {
       for (int j = 0; j < 4; ++j) b_off[j] = (((wn * 8 + 2 * j + g) ^ (e << 1)) * 32) + q * 8;
 #pragma unroll
       for (int i = 0; i < 4; ++i) a_seg[i] = (((wm * 8 + 2 * i + g) ^ (e << 1)) * 32) + q * 8;
+      if constexpr (BL == LAYOUT_WG) {
+        // full per-lane LDS byte offsets of each fragment column at K row 0 of slot 0
+        const uint32_t base = (uint32_t)(size_t)L + b_row;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a_seg[i] += base;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) b_off[j] += base;
+      }
     } else {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
@@ -1147,20 +1156,56 @@ struct Pipe {
       b.w = w1;
     }
   }
+  // WG: the LDS byte addresses of the 8 fragment columns of stage s at K row 0 (A: ab, B: bb),
+  // one VALU add each.  The empty asm hands the compiler an opaque register, so each read is
+  // that register plus an immediate offset; left to itself, the compiler re-derived every
+  // read's address with VALU adds in the MFMA stream, two a read.
+  __device__ __forceinline__ void wg_bases(int s, uint32_t (&ab)[4], uint32_t (&bb)[4]) const {
+    const uint32_t sa = __builtin_amdgcn_readfirstlane((uint32_t)((2 * s) % kSlots) * kSlotBytes);
+    const uint32_t sb = __builtin_amdgcn_readfirstlane((uint32_t)((2 * s + 1) % kSlots) * kSlotBytes);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ab[i] = a_seg[i] + sa;
+      asm volatile("" : "+v"(ab[i]));
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      bb[j] = b_off[j] + sb;
+      asm volatile("" : "+v"(bb[j]));
+    }
+  }
+  // WG: read r of sub-step kk: r < 8 half r & 1 of A fragment r >> 1, else half (r - 8) & 1 of
+  // B fragment (r - 8) >> 1 (K rows 16 kk + 4 t .. + 3 of each lane's 8, as in read_tr_at)
+  __device__ __forceinline__ void wg_read(const uint32_t (&ab)[4], const uint32_t (&bb)[4], int kk, int r,
+                                          uint4 (&a)[4], uint4 (&b)[4]) const {
+    const int t = r & 1;
+    const uint32_t base = r < 8 ? ab[r >> 1] : bb[(r - 8) >> 1];
+    uint4& d = r < 8 ? a[r >> 1] : b[(r - 8) >> 1];
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(size_t)(base + (16 * kk + 4 * t) * 512));
+    const uint32_t w0 = (uint16_t)v[0] | ((uint32_t)(uint16_t)v[1] << 16);
+    const uint32_t w1 = (uint16_t)v[2] | ((uint32_t)(uint16_t)v[3] << 16);
+    if (t == 0) {
+      d.x = w0;
+      d.y = w1;
+    } else {
+      d.z = w0;
+      d.w = w1;
+    }
+  }
   __device__ __forceinline__ void read(int s, int kk, uint4 (&a)[4], uint4 (&b)[4]) const {
     const uint32_t sa = (uint32_t)((2 * s) % kSlots) * kSlotBytes;
     const uint32_t sb = (uint32_t)((2 * s + 1) % kSlots) * kSlotBytes;
     if constexpr (BL == LAYOUT_WG) {
+      uint32_t ab[4], bb[4];
+      wg_bases(s, ab, bb);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        read_tr_at(sa, kk, a_seg[i], 0, a[i]);
-        read_tr_at(sa, kk, a_seg[i], 1, a[i]);
-      }
+      for (int r = 0; r < 16; ++r) wg_read(ab, bb, kk, r, a, b);
+      return;
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) a[i] = *(const uint4*)(L + sa + a_off + i * 4096 + ch[kk]);
     }
-    if constexpr (BL == LAYOUT_KN || BL == LAYOUT_WG) {
+    if constexpr (BL == LAYOUT_KN) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         read_tr(sb, kk, j, 0, b[j]);
@@ -1172,14 +1217,9 @@ struct Pipe {
     }
   }
   // fragment r of sub-step kk of stage s: r < 4 the A fragment of rows 32 r, else B fragment r - 4
-  // (KN: r < 4 as above, else half (r - 4) & 1 of B fragment (r - 4) >> 1; 12 reads a set)
-  // (WG: r < 8 half r & 1 of A fragment r >> 1, else half of B fragment (r - 8) >> 1; 16 reads)
+  // (KN: r < 4 as above, else half (r - 4) & 1 of B fragment (r - 4) >> 1; 12 reads a set;
+  // WG reads go through wg_read)
   __device__ __forceinline__ void read1(int s, int kk, int r, uint4 (&a)[4], uint4 (&b)[4]) const {
-    if constexpr (BL == LAYOUT_WG) {
-      if (r < 8) read_tr_at((uint32_t)((2 * s) % kSlots) * kSlotBytes, kk, a_seg[r >> 1], r & 1, a[r >> 1]);
-      else read_tr((uint32_t)((2 * s + 1) % kSlots) * kSlotBytes, kk, (r - 8) >> 1, (r - 8) & 1, b[(r - 8) >> 1]);
-      return;
-    }
     if (r < 4) {
       a[r] = *(const uint4*)(L + (uint32_t)((2 * s) % kSlots) * kSlotBytes + a_off + r * 4096 + ch[kk]);
     } else if constexpr (BL == LAYOUT_KN) {
@@ -1242,11 +1282,19 @@ __device__ __forceinline__ void substep(const PP& P, Frags& f, int rs, int st) {
 template <typename PP, int CUR, bool RD, int R0, int OP, int Q0, int Q1, bool CHK = true>
 __device__ __forceinline__ void substep_kn(const PP& P, Frags& f, int rs, int st) {
   constexpr int n = Q1 - Q0;
-  constexpr int NR = PP::kBL == LAYOUT_WG ? 16 : 12;
+  constexpr bool WG = PP::kBL == LAYOUT_WG;
+  constexpr int NR = WG ? 16 : 12;
+  uint32_t ab[4], bb[4];
+  if constexpr (WG)
+    if (RD) P.wg_bases(rs, ab, bb);
 #pragma unroll
   for (int t = 0; t < 16; ++t) {
     P.mma(f.a[CUR], f.b[CUR], t, t + 1);
-    if (RD && t < NR) P.read1(rs, R0, t, f.a[R0], f.b[R0]);
+    if constexpr (WG) {
+      if (RD) P.wg_read(ab, bb, R0, t, f.a[R0], f.b[R0]);
+    } else if (RD && t < NR) {
+      P.read1(rs, R0, t, f.a[R0], f.b[R0]);
+    }
 #pragma unroll
     for (int q = 0; q < n; ++q)
       if (t == (2 * q + 1) * 16 / (2 * (n > 0 ? n : 1))) P.template issue<OP, CHK>(st, Q0 + q);
