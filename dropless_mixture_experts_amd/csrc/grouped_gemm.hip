@@ -1380,22 +1380,41 @@ __device__ __forceinline__ void mainloop(PP& P, int nk) {
 
 
 // Partial tiles of the split tail: a wave's 128 x 128 block is 64 float4 per lane,
-// coalesced per register group.
+// coalesced per register group.  The pieces of a tile run on any XCD, and each XCD has its
+// own L2, so the partials travel through memory.  They are written with system-scope buffer
+// stores (sc0 sc1: written through L1 and L2), whose vmcnt completes once they are visible
+// there, so a piece only waits for vmcnt(0) before counting itself.  The last piece reads
+// them with ordinary loads after its count returned: a slot is written once and read once
+// per launch, so no L1 or L2 holds an older copy of it (the caches are invalidated at launch).
+// Device-scope fences here wrote back and invalidated the whole L2, full of the GEMM's
+// output, twice a piece: 45-50 us of the tail.  (System-scope loads as well made the
+// compiler spill around the main loop: gate/up 4-8% slower.)  The store descriptor covers
+// the one slot, so a store outside it writes nothing.
 namespace ring4 {
 
-__device__ __forceinline__ float4* part_ptr(const GemmParams& p, int slot) {
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+constexpr int kSysScope = 1 | 16;  // cache-policy bits sc0 | sc1 of a buffer access
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t part_rsrc(const GemmParams& p, int slot) {
+  return __builtin_amdgcn_make_buffer_rsrc(p.ws_part + (size_t)slot * kSplitSlotFloats, (short)0,
+                                           kSplitSlotFloats * (int)sizeof(float), 0x00020000);
+}
+// byte offset in the slot of this lane's float4 r (0..63) of the wave's block
+__device__ __forceinline__ int part_off(int r) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  return (float4*)(p.ws_part + (size_t)slot * kSplitSlotFloats) + wave * 4096 + lane;
+  return (wave * 4096 + lane + r * 64) * 16;
 }
 
 __device__ __forceinline__ void store_partial(const GemmParams& p, int slot, const f32x16 (&acc)[4][4]) {
-  float4* dst = part_ptr(p, slot);
+  const __amdgpu_buffer_rsrc_t rs = part_rsrc(p, slot);
 #pragma unroll
   for (int t = 0; t < 16; ++t)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const f32x16& a = acc[t >> 2][t & 3];
-      dst[(t * 4 + e) * 64] = make_float4(a[4 * e], a[4 * e + 1], a[4 * e + 2], a[4 * e + 3]);
+      const i32x4 w = {__float_as_int(a[4 * e]), __float_as_int(a[4 * e + 1]), __float_as_int(a[4 * e + 2]),
+                       __float_as_int(a[4 * e + 3])};
+      __builtin_amdgcn_raw_buffer_store_b128(w, rs, part_off(t * 4 + e), 0, kSysScope);
     }
 }
 
@@ -1572,7 +1591,8 @@ __device__ __forceinline__ void store_tile_dswiglu_lds(const GemmParams& p, cons
 // In batches of 16 float4 (four accumulator tiles): the loads of a batch are in flight together
 // (one load, wait, add at a time made the reduction of a split tile latency-bound).
 __device__ __forceinline__ void load_partial(const GemmParams& p, int slot, f32x16 (&acc)[4][4], bool add) {
-  const float4* src = part_ptr(p, slot);
+  const float4* src = (const float4*)(p.ws_part + (size_t)slot * kSplitSlotFloats) + (threadIdx.x >> 6) * 4096 +
+                      (threadIdx.x & 63);
 #pragma unroll
   for (int t0 = 0; t0 < 16; t0 += 4) {
     float4 v[16];
@@ -1663,12 +1683,12 @@ void grouped_gemm_ring4_kernel(GemmParams p) {
     // a piece of a split tile: publish the partial; the last piece of the tile reduces
     const int r = pc.slot % pc.R;
     store_partial(p, pc.slot, acc);
-    __threadfence();
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the partial is visible in memory
     int old = 0;
     if (lane == 0) old = atomicAdd(p.ws_count + r * 4 + wave, 1);
     old = __builtin_amdgcn_readfirstlane(old);
     if (old != pc.f - 1) return;
-    __threadfence();
+    asm volatile("" ::: "memory");  // the loads stay after the count that allowed them
     load_partial(p, r, acc, false);
     for (int j = 1; j < pc.f; ++j) load_partial(p, j * pc.R + r, acc, true);
     if (lane == 0) p.ws_count[r * 4 + wave] = 0;
