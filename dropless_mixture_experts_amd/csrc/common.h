@@ -20,8 +20,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
   return __builtin_bit_cast(uint16_t, b);
 }
 
+// two fp32 -> packed bf16 (lo in the low half), one v_cvt_pk_bf16_f32 for the pair; converting
+// them one at a time and shifting the halves together took three VALU ops per pair
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+  const bf16x2v v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // Element traits: a 16-byte vector holds kVec elements.
