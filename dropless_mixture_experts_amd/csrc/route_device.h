@@ -32,6 +32,32 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
   return ((uint64_t)hi << 32) | lo;
 }
 
+// v of the lane that DPP control CTRL names (within a row of 16 lanes; every lane of a group
+// reads a lane of the same group, all of whose lanes are active together)
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const int lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)v, CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
+  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+// Maximum of v over an aligned group of G lanes (G a power of two), in every lane of it: swaps
+// within quads, then the mirror of each half row and of each row (the two halves being equal
+// by then, any pairing across them completes the maximum); shuffles past 16 lanes.
+template <int G>
+__device__ __forceinline__ uint64_t group_max_u64(uint64_t v) {
+  if constexpr (G >= 2) { const uint64_t o = dpp_u64<0xB1>(v); v = o > v ? o : v; }   // quad_perm 1,0,3,2
+  if constexpr (G >= 4) { const uint64_t o = dpp_u64<0x4E>(v); v = o > v ? o : v; }   // quad_perm 2,3,0,1
+  if constexpr (G >= 8) { const uint64_t o = dpp_u64<0x141>(v); v = o > v ? o : v; }  // row_half_mirror
+  if constexpr (G >= 16) { const uint64_t o = dpp_u64<0x140>(v); v = o > v ? o : v; } // row_mirror
+#pragma unroll
+  for (int m = 16; m < G; m <<= 1) {
+    const uint64_t o = shfl_xor_u64(v, m);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
 template <int G>
 __device__ __forceinline__ float group_sum(float v) {
 #pragma unroll
@@ -43,8 +69,8 @@ __device__ __forceinline__ float group_sum(float v) {
 // e_lo .. e_lo + KPL - 1 in kf (-inf past E).  A key packs the fp32 order of the key above
 // the complemented expert index, so one unsigned maximum picks the largest key and, among
 // equal keys, the smallest expert; a cleared or absent key is 0, below every real key.
-// Each of the K rounds takes the lane-local maximum, then a butterfly maximum over the
-// group.  Round k is kept by lane k mod G of the group (s_sel / s_score at slot tl*K + k),
+// Each of the K rounds takes the lane-local maximum (a tree of independent compares), then
+// the maximum over the group.  Round k is kept by lane k mod G of the group (s_sel / s_score at slot tl*K + k),
 // which also writes it out: topk_idx[t*K + k] and topk_gate[t*K + k].
 template <int G, int KPL>
 __device__ __forceinline__ void select_token(float (&kf)[KPL], int e_lo, int E, int K, int score, int renorm,
@@ -63,14 +89,14 @@ __device__ __forceinline__ void select_token(float (&kf)[KPL], int e_lo, int E, 
   }
   float top_key = 0.f, denom = 0.f;
   for (int k = 0; k < K; ++k) {
-    uint64_t best = comp[0];
+    uint64_t m[KPL];
 #pragma unroll
-    for (int j = 1; j < KPL; ++j) best = comp[j] > best ? comp[j] : best;
+    for (int j = 0; j < KPL; ++j) m[j] = comp[j];
 #pragma unroll
-    for (int o = 1; o < G; o <<= 1) {
-      const uint64_t other = shfl_xor_u64(best, o);
-      best = other > best ? other : best;
-    }
+    for (int w = 1; w < KPL; w *= 2)
+#pragma unroll
+      for (int j = 0; j + w < KPL; j += 2 * w) m[j] = m[j + w] > m[j] ? m[j + w] : m[j];
+    const uint64_t best = group_max_u64<G>(m[0]);
     const int e = (int)(0xffffffffu - (uint32_t)best);
 #pragma unroll
     for (int j = 0; j < KPL; ++j)
