@@ -756,6 +756,41 @@ def test_grouped_gemm_split_tail(swiglu):
         assert row.max() < TOL_BF16
 
 
+def test_grouped_gemm_split_tail_repeats():
+    """The split tail's pieces hand their partials over through memory with no fence: each piece
+    writes its fp32 partial through L1 and L2 and waits for the stores before it counts itself,
+    and the last piece reads them.  A stale partial would change the sum, so 16 tiles cut into 16
+    pieces each (every CU busy in the tail) run 30 times, with 64 MB of fresh writes between the
+    calls to fill the L2s with dirty lines, and every output must equal the first bit for bit and
+    the unsplit product within the bf16 bar."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    g = torch.Generator(device="cuda").manual_seed(77)
+    N, Kd = 256, 4096                                  # one column tile, 64 K stages
+    rows = [256 * (cus // 2) + 130, 256 * (cus // 2 - 1), 256 * 16 - 130]  # cus + 16 row tiles
+    M = sum(rows)
+    off = torch.tensor(np.cumsum([0] + rows), dtype=torch.int32, device="cuda")
+    A = (torch.randn((M, Kd), generator=g, device="cuda") * 0.5).to(torch.bfloat16)
+    W = (torch.randn((len(rows), N, Kd), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+    ws = torch.zeros((moe.moe_grouped_gemm_workspace_size(),), dtype=torch.uint8, device="cuda")
+    dirty = torch.empty((16 << 20,), dtype=torch.float32, device="cuda")
+    ref = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    moe.moe_grouped_gemm(A, W, 0, off, ref, moe.MOE_EPI_NONE)     # no workspace: no split
+    first = None
+    for i in range(30):
+        dirty.fill_(float(i))
+        C = empty_like_poisoned((M, N), torch.bfloat16)
+        moe.moe_grouped_gemm(A, W, 0, off, C, moe.MOE_EPI_NONE, workspace=ws)
+        if first is None:
+            first = C
+        else:
+            assert torch.equal(C, first), f"repeat {i} differs from the first"
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(ws[:4096]).item() == 0
+    a, b = f64(first), f64(ref)
+    row = np.linalg.norm(a - b, axis=1) / np.maximum(np.linalg.norm(b, axis=1), 1e-30)
+    assert row.max() < TOL_BF16
+
+
 @pytest.mark.parametrize("dswiglu", [False, True])
 def test_grouped_gemm_kn_ring(dswiglu):
     """The data-gradient form (K-by-N weights, bf16, K a multiple of 64) on ragged groups, with
