@@ -1526,9 +1526,11 @@ __device__ __forceinline__ void store_tile_lds(const GemmParams& p, const f32x16
 
 // SwiGLU backward through LDS: acc = dH for the wave's 128 rows x 128 columns at (row0, col0);
 // epi_in = saved [G | U] of width 2F (F = N); C [M, 2F] = [dH U silu'(G) | dH silu(G)].  In
-// rounds of 32 rows: the rows of G and U are loaded whole (16 bytes a lane, 4 rows an
-// instruction) into 16 KB of the wave's LDS, each lane takes back the values beside its
-// accumulators, writes both results over them, and the two halves leave as whole row segments.
+// rounds of 32 rows, double-buffered in the wave's 32 KB of LDS: round i + 1's rows of G and U
+// go global -> LDS by DMA (in the row swizzle of Out<128>) while round i is computed in place,
+// and round i leaves as whole row segments after a wait that covers round i + 1's loads and
+// round i - 1's stores, both issued before round i's arithmetic.  (Loading each round only after
+// the previous round's stores left a memory round trip a round: 24 of a tile's 115 µs.)
 __device__ __forceinline__ void store_tile_dswiglu_lds(const GemmParams& p, const f32x16 (&acc)[4][4], char* wl,
                                                        int64_t row0, int64_t re, int64_t col0) {
   using O = Out<128>;
@@ -1537,32 +1539,33 @@ __device__ __forceinline__ void store_tile_dswiglu_lds(const GemmParams& p, cons
   const char* pre = (const char*)p.epi_in;
   const int lane = threadIdx.x & 63;
   const int l32 = lane & 31, hi = lane >> 5;
-  const int c = lane % O::kCPR, rr = lane / O::kCPR;
-  const int64_t col = col0 + c * 8;
-  const bool cok = col < F;
-  char* wg = wl;
-  char* wu = wl + 32 * O::kRowBytes;
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)wl);
+  // round i's G and U rows into buffer b: DMA j of 8 fills rows 4 j .. 4 j + 3, lane L landing at
+  // 16-byte position L % 16 of row 4 j + L / 16, which holds logical chunk (L % 16) ^ (row % 16).
+  // Rows are clamped to M - 1 and columns to F - 8 (in bounds; such rows and columns are never
+  // stored).
+  auto issue = [&](int i, int b) {
+    const int64_t rb = min(row0 + i * 32, p.M - 1);
+    const char* base = uniform_ptr(pre + rb * ld);
+    const uint32_t lb = lds0 + b * 16384;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int r = 4 * j + (lane >> 4);
+      const int64_t row = min(row0 + i * 32 + r, p.M - 1);
+      const int c = (lane & 15) ^ (r % O::kCPR);
+      const int64_t col = min(col0 + c * 8, F - 8);
+      const uint32_t off = (uint32_t)((row - rb) * ld + col * 2);
+      dma(base, off, lb + j * 1024);
+      dma(base, off + (uint32_t)(F * 2), lb + 8192 + j * 1024);
+    }
+  };
+  issue(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    uint4 g[8], u[8];
-#pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int r = it * O::kRPI + rr;
-      const int64_t row = row0 + i * 32 + r;
-      g[it] = make_uint4(0u, 0u, 0u, 0u);
-      u[it] = g[it];
-      if (cok && row < re) {
-        g[it] = *(const uint4*)(pre + row * ld + col * 2);
-        u[it] = *(const uint4*)(pre + row * ld + (F + col) * 2);
-      }
-    }
-#pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int r = it * O::kRPI + rr;
-      const int off = r * O::kRowBytes + ((c ^ (r % O::kCPR)) * 16);
-      *(uint4*)(wg + off) = g[it];
-      *(uint4*)(wu + off) = u[it];
-    }
+    char* wg = wl + (i & 1) * 16384;
+    char* wu = wg + 32 * O::kRowBytes;
+    if (i < 3) issue(i + 1, (i + 1) & 1);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -1583,6 +1586,7 @@ __device__ __forceinline__ void store_tile_dswiglu_lds(const GemmParams& p, cons
         *(uint2*)(wg + off) = make_uint2(pack_bf16x2(da[0], da[1]), pack_bf16x2(da[2], da[3]));
         *(uint2*)(wu + off) = make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
       }
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");  // round i + 1 in LDS, round i - 1 out
     O::template flush<32>(wg, (char*)p.C, ld, row0 + i * 32, re, col0, F);
     O::template flush<32>(wu, (char*)p.C + F * 2, ld, row0 + i * 32, re, col0, F);
   }
