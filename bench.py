@@ -2,7 +2,9 @@
 
 One step = the whole forward hot path over one batch of synthetic tokens:
 router logits -> top-K routing (histogram, offsets, stable positions) ->
-permute -> grouped GEMM gate/up + SwiGLU -> grouped GEMM down -> combine.
+permute -> grouped GEMM gate/up + SwiGLU -> grouped GEMM down -> combine,
+with the permute done by the gate/up GEMM's own row loads for bf16 layers
+(the forward of a layer that keeps no backward buffers).
 Inputs and weights are resident in HBM before the timed region.
 
 Prints ONE JSON line.  value = tokens/s of the layer forward; the roofline
@@ -465,6 +467,8 @@ def main():
         "onbox_copy_gbs": copy_gbs,
         "clock": clock,
         "load": {"min": int(counts.min()), "max": int(counts.max()), "empty": int((counts == 0).sum())},
+        # the permute runs inside the gate/up GEMM's row loads (no permuted copy is written)
+        "permute_folded_into_gate_up": bufs.fuse_permute,
         "roofline": {"kernel": "grouped GEMM gate/up + SwiGLU", "bound": "mfma", "achieved": tf_up,
                      "peak": peak, "unit": "TFLOP/s", "frac": tf_up / peak, "traffic": traffic,
                      **({"frac_of_peak_at_sustained_clock": tf_up / (peak * sclk / 2400.0)} if sclk else {})},

@@ -35,6 +35,8 @@ SIGNATURES = {
     "moe_permute": (_I32, [_P, _I64, _I64, _I32, _I32, _P, _P, _P, _P, _P, _P]),
     "moe_grouped_gemm": (_I32, [_P, _P, _I32, _P, _I64, _I64, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _SZ, _P]),
     "moe_grouped_gemm_workspace_size": (_I32, [_c.POINTER(_SZ)]),
+    "moe_grouped_gemm_gather": (_I32, [_P, _P, _I64, _I32, _P, _P, _I64, _I64, _I32, _I32, _I32, _P, _P, _P, _SZ,
+                                       _P]),
     "moe_unpermute_combine": (_I32, [_P, _P, _P, _I64, _I64, _I32, _I32, _P, _P]),
     "moe_grouped_gemm_wgrad": (_I32, [_P, _P, _P, _I64, _I64, _I64, _I32, _I32, _I32, _P, _P]),
     "moe_router_route_workspace_size": (_I32, [_I64, _I32, _c.POINTER(_SZ)]),
@@ -225,6 +227,26 @@ def moe_grouped_gemm(A, B, b_layout: int, group_offsets, C, epilogue: int = MOE_
           epilogue, _ptr(epi_in), _ptr(epi_save), _ptr(C), _ptr(workspace), ws_bytes, _stream(stream))
 
 
+def moe_grouped_gemm_gather(x, row_src, K: int, B, group_offsets, C, epilogue: int = MOE_EPI_NONE,
+                            epi_save=None, workspace=None, stream=None) -> None:
+    """moe_grouped_gemm (layout NK) on A = x[row_src // K] without materialising A: row r of
+    the product reads token row row_src[r] // K of x. Bit-identical to moe_permute followed
+    by moe_grouped_gemm; raises MoEError (MOE_UNSUPPORTED) for shapes the gathered form does
+    not take."""
+    T, Kd = x.shape
+    G, N = B.shape[0], B.shape[1]
+    _dense("x", x)
+    _dense("B", B, x.dtype, (G, N, Kd))
+    _dense("row_src", row_src, _i32(), (T * K,), flat=True)
+    _dense("group_offsets", group_offsets, _i32(), (G + 1,), flat=True)
+    _dense("C", C, x.dtype, (T * K, N // 2 if epilogue == MOE_EPI_SWIGLU else N))
+    _dense("epi_save", epi_save, x.dtype, (T * K, N), optional=True)
+    _dense("workspace", workspace, optional=True)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _call("moe_grouped_gemm_gather", _ptr(x), _ptr(row_src), T, K, _ptr(B), _ptr(group_offsets), N, Kd, G,
+          dtype_code(x), epilogue, _ptr(epi_save), _ptr(C), _ptr(workspace), ws_bytes, _stream(stream))
+
+
 def moe_unpermute_combine(y_perm, slot_pos, gates, T: int, K: int, y, stream=None) -> None:
     """y[t] = sum_k gates[t, k] * y_perm[slot_pos[t*K + k]] (gates None: unit weights)."""
     d = y_perm.shape[1]
@@ -373,4 +395,5 @@ def moe_permute_mx(codes, scales, K: int, slot_pos, codes_perm, scales_perm, str
           _stream(stream))
 
 
-from .layer import MoEBuffers, backward_steps, forward_steps, layer_backward, layer_forward  # noqa: E402,F401
+from .layer import (MoEBuffers, backward_steps, forward_steps, gather_supported, layer_backward,  # noqa: E402,F401
+                    layer_forward)

@@ -661,6 +661,11 @@ struct GemmParams {
   // MXFP8 operands: E8M0 block scales of A [M][Kd/32] and B [G*N][Kd/32]
   const uint8_t* sa = nullptr;
   const uint8_t* sb = nullptr;
+  // gathered A (ring kernel, N-by-K weights): row m of A is row a_rows[m] / a_div of the
+  // matrix at A (the permute fused into the GEMM's loads), clamped to a_last
+  const int32_t* a_rows = nullptr;
+  uint32_t a_div = 1;
+  uint32_t a_last = 0;
 };
 constexpr int kSplitCountBytes = 4096;             // counters: up to 1024 (tile, wave) pairs
 constexpr int kSplitSlotFloats = 256 * 256;        // one fp32 256 x 256 partial tile
@@ -1618,9 +1623,11 @@ __device__ __forceinline__ void load_partial(const GemmParams& p, int slot, f32x
 
 }  // namespace ring4
 
-template <int EPI, int BL>
+// GA: gathered A rows (GemmParams::a_rows), N-by-K weights only
+template <int EPI, int BL, bool GA = false>
 __global__ __launch_bounds__(ring4::kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void grouped_gemm_ring4_kernel(GemmParams p) {
+  static_assert(!GA || BL == LAYOUT_NK, "rows are gathered for N-by-K weights only");
   using namespace ring4;
   __shared__ uint4 smem[kSlots * kSlotUnits];
   int g, nt;
@@ -1640,7 +1647,7 @@ void grouped_gemm_ring4_kernel(GemmParams p) {
 
   f32x16 acc[4][4];
   Pipe<EPI, BL> P(acc, smem);
-  P.a_base = uniform_ptr((const char*)p.A + m0 * ldb + (int64_t)k0 * kStageBytes);
+  P.a_base = uniform_ptr((const char*)p.A + (GA ? 0 : m0 * ldb) + (int64_t)k0 * kStageBytes);
   const int64_t b0row = EPI == EPI_SWIGLU ? (int64_t)nt * 128 : (int64_t)nt * 256;
   if constexpr (BL == LAYOUT_KN) {
     // B = [Kd rows][N] per group; a stage is 64 K rows; lanes of DMA q fill K row
@@ -1658,7 +1665,8 @@ void grouped_gemm_ring4_kernel(GemmParams p) {
     const int c = (lane & 7) ^ swz(r);
     int64_t ar = m0 + r;
     ar = ar < p.M ? ar : p.M - 1;
-    P.va[q] = (uint32_t)((ar - m0) * ldb + c * 16);
+    P.va[q] = GA ? (uint32_t)((int64_t)min((uint32_t)p.a_rows[ar] / p.a_div, p.a_last) * ldb + c * 16)
+                     : (uint32_t)((ar - m0) * ldb + c * 16);
     int64_t br;
     if constexpr (BL == LAYOUT_KN) {
       const int kr = (wave * kQ + q) * 2 + (lane >> 5);
@@ -2214,12 +2222,16 @@ hipError_t launch_grouped_gemm_mx(const uint8_t* A, const uint8_t* SA, const uin
   return hipGetLastError();
 }
 
-hipError_t launch_grouped_gemm(const void* A, const void* B, int b_layout, const int32_t* offs,
-                               int64_t M, int64_t N, int64_t Kd, int G, int dtype, int epilogue,
-                               const void* epi_in, void* epi_save, void* C, void* ws, size_t ws_bytes,
-                               hipStream_t s) {
+namespace {
+hipError_t grouped_gemm_impl(const void* A, const void* B, int b_layout, const int32_t* offs, int64_t M, int64_t N,
+                             int64_t Kd, int G, int dtype, int epilogue, const void* epi_in, void* epi_save, void* C,
+                             void* ws, size_t ws_bytes, const int32_t* a_rows, int a_div, int64_t a_rows_total,
+                             hipStream_t s) {
   if (M == 0) return hipSuccess;
   GemmParams prm{A, B, offs, epi_in, epi_save, C, M, N, Kd, G, 0, nullptr, nullptr, 0, 0, 0};
+  prm.a_rows = a_rows;
+  prm.a_div = (uint32_t)a_div;
+  prm.a_last = a_rows ? (uint32_t)(a_rows_total - 1) : 0;
   if (ws && ws_bytes >= kSplitCountBytes + kSplitSlotFloats * sizeof(float)) {
     prm.ws_count = (int*)ws;
     prm.ws_part = (float*)((char*)ws + kSplitCountBytes);
@@ -2254,6 +2266,13 @@ hipError_t launch_grouped_gemm(const void* A, const void* B, int b_layout, const
         hipLaunchKernelGGL((grouped_gemm_ring4_kernel<EPI_DSWIGLU, LAYOUT_KN>), rgrid, dim3(ring4::kThreads), 0, s, prm);
       else
         hipLaunchKernelGGL((grouped_gemm_ring4_kernel<EPI_NONE, LAYOUT_KN>), rgrid, dim3(ring4::kThreads), 0, s, prm);
+    } else if (a_rows) {
+      if (epilogue == EPI_SWIGLU)
+        hipLaunchKernelGGL((grouped_gemm_ring4_kernel<EPI_SWIGLU, LAYOUT_NK, true>), rgrid, dim3(ring4::kThreads), 0,
+                           s, prm);
+      else
+        hipLaunchKernelGGL((grouped_gemm_ring4_kernel<EPI_NONE, LAYOUT_NK, true>), rgrid, dim3(ring4::kThreads), 0, s,
+                           prm);
     } else if (epilogue == EPI_SWIGLU) {
       hipLaunchKernelGGL((grouped_gemm_ring4_kernel<EPI_SWIGLU, LAYOUT_NK>), rgrid, dim3(ring4::kThreads), 0, s, prm);
     } else {
@@ -2261,8 +2280,28 @@ hipError_t launch_grouped_gemm(const void* A, const void* B, int b_layout, const
     }
     return hipGetLastError();
   }
+  if (a_rows) return hipErrorInvalidValue;  // only the ring kernel gathers A rows
   if (dtype == 1) return gemm_dispatch<bf16_t>(prm, b_layout, epilogue, nq, grid, s);
   return gemm_dispatch<float>(prm, b_layout, epilogue, nq, grid, s);
+}
+}  // namespace
+
+hipError_t launch_grouped_gemm(const void* A, const void* B, int b_layout, const int32_t* offs,
+                               int64_t M, int64_t N, int64_t Kd, int G, int dtype, int epilogue,
+                               const void* epi_in, void* epi_save, void* C, void* ws, size_t ws_bytes,
+                               hipStream_t s) {
+  return grouped_gemm_impl(A, B, b_layout, offs, M, N, Kd, G, dtype, epilogue, epi_in, epi_save, C, ws, ws_bytes,
+                           nullptr, 1, 0, s);
+}
+
+static_assert(ring4::kStageBytes == kGatherStageBytes && EPI_NONE == 0 && EPI_SWIGLU == 1,
+              "the gathered form's shape test assumes the ring kernel's stage and epilogue codes");
+
+hipError_t launch_grouped_gemm_gather(const void* X, int64_t T, const int32_t* a_rows, int a_div, const void* B,
+                                      const int32_t* offs, int64_t M, int64_t N, int64_t Kd, int G, int epilogue,
+                                      void* epi_save, void* C, void* ws, size_t ws_bytes, hipStream_t s) {
+  return grouped_gemm_impl(X, B, LAYOUT_NK, offs, M, N, Kd, G, 1, epilogue, nullptr, epi_save, C, ws, ws_bytes,
+                           a_rows, a_div, T, s);
 }
 
 hipError_t launch_grouped_wgrad(const void* X, const void* dY, const int32_t* offs, int64_t M,

@@ -52,6 +52,19 @@ hipError_t launch_grouped_gemm(const void* A, const void* B, int b_layout, const
                                int64_t M, int64_t N, int64_t Kd, int G, int dtype, int epilogue,
                                const void* epi_in, void* epi_save, void* C, void* ws, size_t ws_bytes,
                                hipStream_t s);
+// The gate/up GEMM with the permute folded into its A loads: row m of A is row
+// a_rows[m] / a_div of X [T, Kd] (bf16, N-by-K weights, plain or SwiGLU epilogue).  It runs
+// on the ring kernel only: whole 128-byte K stages of a row, and the per-lane DMA offsets of
+// token rows and of weight rows within 32 bits.
+constexpr int64_t kGatherStageBytes = 128;
+inline bool grouped_gemm_gather_supported(int64_t T, int64_t N, int64_t Kd, int dtype, int epilogue) {
+  const int64_t kbytes = Kd * 2;
+  return dtype == 1 && (epilogue == 0 || epilogue == 1) && kbytes % kGatherStageBytes == 0 &&
+         (N + 256) * kbytes < ((int64_t)1 << 32) && T * kbytes < ((int64_t)1 << 32);
+}
+hipError_t launch_grouped_gemm_gather(const void* X, int64_t T, const int32_t* a_rows, int a_div, const void* B,
+                                      const int32_t* offs, int64_t M, int64_t N, int64_t Kd, int G, int epilogue,
+                                      void* epi_save, void* C, void* ws, size_t ws_bytes, hipStream_t s);
 
 hipError_t launch_grouped_wgrad(const void* X, const void* dY, const int32_t* offs, int64_t M,
                                 int64_t N, int64_t Kd, int G, int dtype, int accumulate, float* dW,

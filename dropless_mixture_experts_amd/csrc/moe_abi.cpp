@@ -109,6 +109,29 @@ int32_t moe_grouped_gemm(const void* A, const void* B, int32_t b_layout,
                                            workspace, workspace ? workspace_bytes : 0, (hipStream_t)stream));
 }
 
+int32_t moe_grouped_gemm_gather(const void* x, const int32_t* row_src, int64_t T, int32_t K, const void* B,
+                                const int32_t* group_offsets, int64_t N, int64_t Kd, int32_t G, int32_t dtype,
+                                int32_t epilogue, void* epi_save, void* C, void* workspace,
+                                size_t workspace_bytes, moe_stream_t stream) {
+  if (T < 0 || K < 1 || K > MOE_MAX_TOPK || T * (int64_t)K >= ((int64_t)1 << 31)) return MOE_INVALID_ARG;
+  if (N < 8 || N % 8 != 0 || Kd < 8 || Kd % 8 != 0) return MOE_INVALID_ARG;
+  if (G < 1 || G > kMaxGroups) return MOE_INVALID_ARG;
+  if (!dtype_ok(dtype)) return MOE_UNSUPPORTED;
+  if (epilogue != MOE_EPI_NONE && epilogue != MOE_EPI_SWIGLU) return MOE_UNSUPPORTED;
+  if (epilogue == MOE_EPI_SWIGLU && N % 16 != 0) return MOE_UNSUPPORTED;
+  if (!moe::grouped_gemm_gather_supported(T, N, Kd, dtype, epilogue)) return MOE_UNSUPPORTED;
+  if (!B || !group_offsets) return MOE_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!x || !row_src || !C) return MOE_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(B) || !aligned4(row_src) || !aligned4(group_offsets) || !aligned16(C) ||
+      (epi_save && !aligned16(epi_save)) || (workspace && !aligned16(workspace)))
+    return MOE_INVALID_ARG;
+  return from_hip(moe::launch_grouped_gemm_gather(x, T, row_src, K, B, group_offsets, T * (int64_t)K, N, Kd, G,
+                                                  epilogue, epilogue == MOE_EPI_SWIGLU ? epi_save : nullptr, C,
+                                                  workspace, workspace ? workspace_bytes : 0,
+                                                  (hipStream_t)stream));
+}
+
 int32_t moe_unpermute_combine(const void* y_perm, const int32_t* slot_pos, const float* gates,
                               int64_t T, int64_t d, int32_t K, int32_t dtype, void* y,
                               moe_stream_t stream) {

@@ -6,6 +6,9 @@ two grouped GEMMs -> combine):
     moe_router_route (bf16; fp32: moe_router_logits -> moe_route) -> moe_permute
       -> moe_grouped_gemm (gate/up, SwiGLU epilogue) -> moe_grouped_gemm (down)
       -> moe_unpermute_combine
+    A forward-only layer (no backward buffers) folds the permute into the gate/up
+    GEMM's row loads (moe_grouped_gemm_gather) where that form takes the shape, so
+    the permuted token matrix is never written.
 Backward (routing held fixed):
     moe_permute (gate-scaled dY + d_gates) -> moe_grouped_gemm (KN, SwiGLU backward)
       -> moe_grouped_gemm_wgrad (dW2) -> moe_grouped_gemm (KN, dX_perm)
@@ -21,17 +24,29 @@ from __future__ import annotations
 import torch
 
 from . import (MOE_EPI_DSWIGLU, MOE_EPI_NONE, MOE_EPI_SWIGLU, MOE_LAYOUT_KN, MOE_LAYOUT_NK,
-               dtype_code, moe_grouped_gemm, moe_grouped_gemm_wgrad, moe_grouped_gemm_workspace_size,
+               dtype_code, moe_grouped_gemm, moe_grouped_gemm_gather, moe_grouped_gemm_wgrad,
+               moe_grouped_gemm_workspace_size,
                moe_permute, moe_route, moe_route_backward, moe_route_workspace_size,
                moe_router_backward_workspace_size, moe_router_logits, moe_router_logits_backward,
                moe_router_route, moe_router_route_workspace_size, moe_unpermute_combine)
 
 
+def gather_supported(T: int, d: int, F: int, dtype: torch.dtype) -> bool:
+    """Whether moe_grouped_gemm_gather takes the gate/up GEMM of this shape (its header
+    states the same bounds: bf16, d % 64 == 0, 32-bit row offsets of x and of the weights)."""
+    return (dtype == torch.bfloat16 and d % 64 == 0 and (2 * F) % 16 == 0 and (2 * F + 256) * d * 2 < (1 << 32)
+            and T * d * 2 < (1 << 32))
+
+
 class MoEBuffers:
-    """Device buffers of one layer shape."""
+    """Device buffers of one layer shape.
+
+    ``fuse_permute``: run the gate/up GEMM on gathered token rows instead of a permuted copy
+    (None: whenever no backward buffers are asked for and the shape allows it). The backward
+    reads the permuted copy, so ``backward=True`` keeps it."""
 
     def __init__(self, T: int, d: int, E: int, K: int, F: int, dtype: torch.dtype, device="cuda",
-                 save_pre: bool = False, backward: bool = False):
+                 save_pre: bool = False, backward: bool = False, fuse_permute: bool | None = None):
         self.T, self.d, self.E, self.K, self.F = T, d, E, K, F
         M = T * K
         dev = torch.device(device)
@@ -53,7 +68,13 @@ class MoEBuffers:
                                      device=dev)
         # grouped GEMM workspace: zeroed once, every call leaves its counters at zero
         self.gemm_ws = torch.zeros((moe_grouped_gemm_workspace_size(),), dtype=torch.uint8, device=dev)
-        self.x_perm = torch.empty((M, d), **act)
+        if fuse_permute is None:
+            fuse_permute = not backward and gather_supported(T, d, F, dtype)
+        if fuse_permute and (backward or not gather_supported(T, d, F, dtype)):
+            raise ValueError("the permute folds into the gate/up GEMM only for forward-only bf16 layers "
+                             "of a shape moe_grouped_gemm_gather takes")
+        self.fuse_permute = fuse_permute
+        self.x_perm = None if fuse_permute else torch.empty((M, d), **act)
         self.h = torch.empty((M, F), **act)
         self.pre = torch.empty((M, 2 * F), **act) if (save_pre or backward) else None
         self.y_perm = torch.empty((M, d), **act)
@@ -91,10 +112,17 @@ def forward_steps(x, w_router, bias, w13, w2, K: int, score: int, renorm: bool, 
             logits = b.logits
         steps.append(("route", lambda: moe_route(logits, bias, K, score, renorm, b.topk_idx, b.gates, b.counts,
                                                  b.offsets, b.slot_pos, b.row_src, b.ws, stream=stream)))
+    if b.fuse_permute:
+        steps.append(("gemm_gate_up", lambda: moe_grouped_gemm_gather(
+            x, b.row_src, K, w13, b.offsets, b.h, MOE_EPI_SWIGLU, epi_save=b.pre, workspace=b.gemm_ws,
+            stream=stream)))
+    else:
+        steps += [
+            ("permute", lambda: moe_permute(x, K, b.slot_pos, b.x_perm, stream=stream)),
+            ("gemm_gate_up", lambda: moe_grouped_gemm(b.x_perm, w13, MOE_LAYOUT_NK, b.offsets, b.h, MOE_EPI_SWIGLU,
+                                                      epi_save=b.pre, workspace=b.gemm_ws, stream=stream)),
+        ]
     steps += [
-        ("permute", lambda: moe_permute(x, K, b.slot_pos, b.x_perm, stream=stream)),
-        ("gemm_gate_up", lambda: moe_grouped_gemm(b.x_perm, w13, MOE_LAYOUT_NK, b.offsets, b.h, MOE_EPI_SWIGLU,
-                                                  epi_save=b.pre, workspace=b.gemm_ws, stream=stream)),
         ("gemm_down", lambda: moe_grouped_gemm(b.h, w2, MOE_LAYOUT_NK, b.offsets, b.y_perm, MOE_EPI_NONE,
                                                workspace=b.gemm_ws, stream=stream)),
         ("combine", lambda: moe_unpermute_combine(b.y_perm, b.slot_pos, b.gates, b.T, K, b.y, stream=stream)),

@@ -56,7 +56,7 @@ enum moe_score { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 };
 enum moe_layout { MOE_LAYOUT_NK = 0, MOE_LAYOUT_KN = 1 };
 enum moe_epilogue { MOE_EPI_NONE = 0, MOE_EPI_SWIGLU = 1, MOE_EPI_DSWIGLU = 2 };
 
-#define MOE_ABI_VERSION 7
+#define MOE_ABI_VERSION 8
 #define MOE_MAX_EXPERTS 256
 #define MOE_MAX_TOPK 32
 #define MOE_MAX_GROUPS 1024
@@ -217,6 +217,28 @@ int32_t moe_grouped_gemm(const void* A, const void* B, int32_t b_layout,
  * MOE_HIP_ERROR when the device cannot be queried.
  */
 int32_t moe_grouped_gemm_workspace_size(size_t* bytes);
+
+/*
+ * The gate/up grouped GEMM (S5) with the permute (S4) folded into its operand loads:
+ * the same product as moe_permute followed by moe_grouped_gemm with layout NK, without
+ * writing x_perm (TE-MoE "Optimisation 2": dispatch fused into the expert path rather than
+ * run as a separate step whose rows go out to memory and come back; the permutation is a
+ * pure row move, so the GEMM fetches each expert's rows from the token matrix itself).
+ *   row r of A is x[row_src[r] / K], r in [0, T*K);  M = T*K
+ *   x DEVICE [T, Kd] dtype;  row_src DEVICE [T*K] int32 (as moe_route writes it: slot
+ *     s = t*K + k sits at row slot_pos[s], and row_src[slot_pos[s]] = s); an entry
+ *     outside [0, T*K) reads x[T-1]
+ *   B, group_offsets, epilogue, epi_save, C, workspace: as moe_grouped_gemm (layout NK,
+ *     epilogue NONE or SWIGLU)
+ * Results are bit-identical to moe_permute + moe_grouped_gemm on the same workspace.
+ * Requires dtype MOE_BF16, Kd % 64 == 0, (N + 256) * Kd * 2 < 2^32 and T * Kd * 2 < 2^32
+ * (MOE_UNSUPPORTED otherwise: use moe_permute + moe_grouped_gemm), 0 <= T*K < 2^31,
+ * 1 <= K <= MOE_MAX_TOPK, N % 8 == 0 (SWIGLU: N % 16 == 0), 1 <= G <= MOE_MAX_GROUPS.
+ */
+int32_t moe_grouped_gemm_gather(const void* x, const int32_t* row_src, int64_t T, int32_t K, const void* B,
+                                const int32_t* group_offsets, int64_t N, int64_t Kd, int32_t G, int32_t dtype,
+                                int32_t epilogue, void* epi_save, void* C, void* workspace,
+                                size_t workspace_bytes, moe_stream_t stream);
 
 /*
  * Unpermute + gate-weighted combine back to token order (S7; TE-MoE Figure 3

@@ -152,6 +152,31 @@ int main() {
                           nullptr, nullptr, 0, nullptr),
          MOE_OK, false);
 
+  // gate/up GEMM on gathered token rows
+  EXPECT(moe_grouped_gemm_gather(P, PI, 256, 2, P, PI, 256, 128, 4, MOE_BF16, MOE_EPI_SWIGLU, P, P, P, ws, nullptr),
+         MOE_OK, true);
+  EXPECT(moe_grouped_gemm_gather(P, PI, 256, 2, P, PI, 256, 128, 4, MOE_BF16, MOE_EPI_NONE, nullptr, P, nullptr, 0,
+                                 nullptr),
+         MOE_OK, true);
+  EXPECT(moe_grouped_gemm_gather(P, PI, 256, 2, P, PI, 256, 96, 4, MOE_BF16, MOE_EPI_NONE, nullptr, P, nullptr, 0,
+                                 nullptr),
+         MOE_UNSUPPORTED, false);
+  EXPECT(moe_grouped_gemm_gather(P, PI, 256, 2, P, PI, 256, 128, 4, MOE_F32, MOE_EPI_NONE, nullptr, P, nullptr, 0,
+                                 nullptr),
+         MOE_UNSUPPORTED, false);
+  EXPECT(moe_grouped_gemm_gather(P, PI, 256, 2, P, PI, 256, 128, 4, MOE_BF16, MOE_EPI_DSWIGLU, nullptr, P, nullptr,
+                                 0, nullptr),
+         MOE_UNSUPPORTED, false);
+  EXPECT(moe_grouped_gemm_gather(P, nullptr, 256, 2, P, PI, 256, 128, 4, MOE_BF16, MOE_EPI_NONE, nullptr, P,
+                                 nullptr, 0, nullptr),
+         MOE_INVALID_ARG, false);
+  EXPECT(moe_grouped_gemm_gather(P, PI, 256, 0, P, PI, 256, 128, 4, MOE_BF16, MOE_EPI_NONE, nullptr, P, nullptr, 0,
+                                 nullptr),
+         MOE_INVALID_ARG, false);
+  EXPECT(moe_grouped_gemm_gather(nullptr, nullptr, 0, 2, P, PI, 256, 128, 4, MOE_BF16, MOE_EPI_NONE, nullptr,
+                                 nullptr, nullptr, 0, nullptr),
+         MOE_OK, false);
+
   // weight gradient
   EXPECT(moe_grouped_gemm_wgrad(P, P, PI, 64, 16, 16, 2, MOE_BF16, 0, PF, nullptr), MOE_OK, true);
   EXPECT(moe_grouped_gemm_wgrad(P, P, PI, 64, 12, 16, 2, MOE_BF16, 0, PF, nullptr), MOE_INVALID_ARG, false);

@@ -58,6 +58,10 @@ hipError_t launch_grouped_gemm(const void*, const void*, int, const int32_t*, in
                                const void*, void*, void*, void*, size_t, hipStream_t) {
   return hit();
 }
+hipError_t launch_grouped_gemm_gather(const void*, int64_t, const int32_t*, int, const void*, const int32_t*, int64_t,
+                                      int64_t, int64_t, int, int, void*, void*, void*, size_t, hipStream_t) {
+  return hit();
+}
 hipError_t launch_grouped_wgrad(const void*, const void*, const int32_t*, int64_t, int64_t, int64_t, int, int, int,
                                 float*, hipStream_t) {
   return hit();

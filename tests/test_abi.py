@@ -30,7 +30,7 @@ def test_header_declares_the_boundary():
               "moe_grouped_gemm_wgrad", "moe_router_logits", "moe_route_workspace_size",
               "moe_route_backward", "moe_router_logits_backward", "moe_router_backward_workspace_size",
               "moe_router_route", "moe_router_route_workspace_size", "moe_mx_quantize", "moe_grouped_gemm_mx",
-              "moe_permute_mx", "moe_router_route_noalloc",
+              "moe_permute_mx", "moe_router_route_noalloc", "moe_grouped_gemm_gather",
               "moe_status_str", "moe_abi_version"]:
         assert n in names
 
@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert moe.moe_abi_version() == 7
+    assert moe.moe_abi_version() == 8
     assert moe.status_str(0) == "ok"
     assert "invalid" in moe.status_str(1)
     assert "static scratch" in moe.status_str(moe.MOE_SCRATCH_LIMIT)
@@ -106,6 +106,32 @@ def test_gemm_rejects_bad_arguments(lib):
     assert call(ws=P + 8, wsb=1 << 20) == 1  # misaligned workspace
     assert call(M=-1) == 1
     assert call(M=0) == 0                 # nothing to do: returns before any launch
+
+
+def test_gemm_gather_rejects_bad_arguments(lib):
+    def call(x=P, src=P, T=256, K=2, B=P, offs=P, N=256, Kd=128, G=4, dt=1, epi=0, esave=None, C=P,
+             ws=None, wsb=0):
+        return lib.moe_grouped_gemm_gather(x, src, T, K, B, offs, N, Kd, G, dt, epi, esave, C, ws, wsb, None)
+    assert call(K=0) == 1
+    assert call(K=33) == 1                # top-K limit
+    assert call(T=-1) == 1
+    assert call(T=1 << 28, K=8) == 1      # T*K >= 2^31
+    assert call(N=12) == 1
+    assert call(G=0) == 1
+    assert call(dt=0) == 2                # the gathered form is bf16 only
+    assert call(dt=7) == 2
+    assert call(epi=2) == 2               # no SwiGLU-backward epilogue
+    assert call(epi=1, N=24) == 2
+    assert call(Kd=96) == 2               # whole 64-element K stages only
+    assert call(T=1 << 20, Kd=4096) == 2  # token rows beyond 32-bit DMA offsets
+    assert call(N=1 << 20, Kd=4096) == 2  # weight rows beyond 32-bit DMA offsets
+    assert call(src=None) == 1
+    assert call(x=P + 4) == 1             # misaligned
+    assert call(src=P + 2) == 1
+    assert call(esave=P + 8, epi=1) == 1
+    assert call(C=None) == 1
+    assert call(ws=P + 8, wsb=1 << 20) == 1
+    assert call(T=0, x=None, src=None, C=None) == 0  # nothing to do: returns before any launch
 
 
 def test_wgrad_permute_combine_reject_bad_arguments(lib):

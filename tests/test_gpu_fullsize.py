@@ -7,7 +7,11 @@ row or one entry at a time, and the GPU outputs are made complete first:
   afterwards no element of it may still hold the fill, so a row or tile that the
   kernels never wrote fails;
 * the whole routing (indices, counts, offsets, positions, permutation) is
-  compared bit for bit, and the permuted tokens byte for byte;
+  compared bit for bit;
+* the forward runs as the benchmark times it (the permute folded into the
+  gate/up GEMM's row loads), then once more writing the permuted copy, whose
+  rows must be their tokens' rows byte for byte and whose outputs must equal
+  the folded forward's bit for bit;
 * in every expert group, every 256-row tile and every 32-row block inside it
   (the row extent of one matrix-core fragment) contributes one seeded random row,
   so the tiles that only full sizes create (a grid dealt over the XCDs, the
@@ -119,11 +123,13 @@ def _inputs(cfg):
     return inp, {k: dev(v) for k, v in inp.items()}
 
 
-def _forward_full(cfg, inp, dv, logits, backward=False):
-    bufs = moe.MoEBuffers(cfg.T, cfg.d, cfg.E, cfg.K, cfg.F, torch.bfloat16, backward=backward)
+def _forward_full(cfg, inp, dv, logits, backward=False, fuse_permute=None):
+    bufs = moe.MoEBuffers(cfg.T, cfg.d, cfg.E, cfg.K, cfg.F, torch.bfloat16, backward=backward,
+                          fuse_permute=fuse_permute)
     poison(bufs.topk_idx, bufs.gates, bufs.counts, bufs.offsets, bufs.slot_pos, bufs.row_src,
            bufs.x_perm, bufs.h, bufs.pre, bufs.y_perm, bufs.y)
-    print(f"[fullsize] {cfg.name}: T={cfg.T} d={cfg.d} E={cfg.E} K={cfg.K} F={cfg.F}", flush=True)
+    print(f"[fullsize] {cfg.name}: T={cfg.T} d={cfg.d} E={cfg.E} K={cfg.K} F={cfg.F} "
+          f"fused permute={bufs.fuse_permute}", flush=True)
     moe.layer_forward(dv["x"], dv["w_router"], dv["bias"], dv["w13"], dv["w2"], cfg.K, cfg.score, cfg.renorm,
                       bufs, logits=dev(logits))
     torch.cuda.synchronize()
@@ -155,15 +161,13 @@ def test_full_forward(name):
     if name == "dsv3_share":
         assert (r.counts == 0).sum() == 4
 
-    # every permuted row is its token's row, byte for byte
-    src = torch.as_tensor(r.row_src // cfg.K, device="cuda")
-    assert torch.equal(bufs.x_perm.view(torch.int16), dv["x"].view(torch.int16)[src])
+    # the benchmark's forward folds the permute into the gate/up GEMM: no permuted copy
+    assert bufs.fuse_permute and bufs.x_perm is None
 
     # one row in every 32-row block of every tile of every group, against the oracle's rows
     rows = tile_rows(r.offsets, seed=7)
     ref = orc.layer_rows(inp["x"], inp["w13"], inp["w2"], r, rows, cfg.K)
     print(f"[fullsize] {name}: {len(rows)} rows checked", flush=True)
-    assert np.array_equal(host(bufs.x_perm[torch.as_tensor(rows, device="cuda")]), ref["x_perm"])
     check_rows("h", rows_of(bufs.h, rows), ref["h"], rows, r.offsets)
     check_rows("y_perm", rows_of(bufs.y_perm, rows), ref["y_perm"], rows, r.offsets)
 
@@ -172,6 +176,15 @@ def test_full_forward(name):
     fwd = orc.forward(inp["x"][S], None, inp["bias"], inp["w13"], inp["w2"], cfg.K, cfg.score, cfg.renorm,
                       logits=logits[S])
     check_rows("y", f64(bufs.y)[S], fwd["y"], S)
+
+    # the forward that writes the permuted copy: every permuted row is its token's row byte
+    # for byte, and every output equals the folded forward's bit for bit
+    plain = _forward_full(cfg, inp, dv, logits, fuse_permute=False)
+    src = torch.as_tensor(r.row_src // cfg.K, device="cuda")
+    assert torch.equal(plain.x_perm.view(torch.int16), dv["x"].view(torch.int16)[src])
+    assert np.array_equal(host(plain.x_perm[torch.as_tensor(rows, device="cuda")]), ref["x_perm"])
+    for n in ("h", "y_perm", "y"):
+        assert torch.equal(getattr(plain, n), getattr(bufs, n)), n
 
 
 @pytest.mark.parametrize("name", ["mixtral", "fine_grained", "dsv3_share"])

@@ -832,6 +832,116 @@ def test_grouped_gemm_kn_ring(dswiglu):
 
 # ----------------------------------------------------------------- weight gradient
 
+# ----------------------------------------------------------------- gate/up GEMM on gathered rows
+
+def _gather_case(T, d, E, K, N, seed):
+    r = _routing(T, E, K, seed)
+    rng = np.random.default_rng(seed + 1)
+    x = mi.f32_to_bf16_bits(rng.standard_normal((T, d)).astype(np.float32))
+    W = mi.f32_to_bf16_bits((rng.standard_normal((E, N, d)) / math.sqrt(d)).astype(np.float32))
+    return r, x, W
+
+
+def _permute_then_gemm(xd, Wd, r, K, epi, width, save, ws):
+    """The unfused pair: moe_permute, then moe_grouped_gemm on the permuted copy."""
+    M = len(r.row_src)
+    xp = empty_like_poisoned((M, xd.shape[1]), torch.bfloat16)
+    moe.moe_permute(xd, K, dev(r.slot_pos), xp)
+    C = empty_like_poisoned((M, width), torch.bfloat16)
+    P = empty_like_poisoned((M, Wd.shape[1]), torch.bfloat16) if save else None
+    moe.moe_grouped_gemm(xp, Wd, 0, dev(r.offsets), C, epi, epi_save=P, workspace=ws)
+    return C, P
+
+
+@pytest.mark.parametrize("K,epi,save,use_ws", [(3, 0, False, False), (3, 0, False, True), (3, 1, True, True),
+                                               (3, 1, False, False), (1, 1, True, True)])
+def test_grouped_gemm_gather_equals_permute_then_gemm(K, epi, save, use_ws):
+    """The gate/up GEMM reading token rows through row_src equals moe_permute followed by
+    moe_grouped_gemm bit for bit (both in the plain and the SwiGLU epilogue, with the saved
+    pre-activations, with and without the split-tail workspace), and the oracle on the
+    permuted rows within the bf16 bar.  Ragged groups, an empty expert, a partial column tile."""
+    T, d, E = 700, 192, 7
+    N = 272 if epi == 1 else 264
+    width = N // 2 if epi == 1 else N
+    r, x, W = _gather_case(T, d, E, K, N, seed=50 + K)
+    xd, Wd = dev(x), dev(W)
+    ws = torch.zeros((moe.moe_grouped_gemm_workspace_size(),), dtype=torch.uint8, device="cuda") if use_ws else None
+    M = T * K
+    C = empty_like_poisoned((M, width), torch.bfloat16)
+    P = empty_like_poisoned((M, N), torch.bfloat16) if save else None
+    moe.moe_grouped_gemm_gather(xd, dev(r.row_src), K, Wd, dev(r.offsets), C, epi, epi_save=P, workspace=ws)
+    C2, P2 = _permute_then_gemm(xd, Wd, r, K, epi, width, save, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(C, C2)
+    if save:
+        assert torch.equal(P, P2)
+    if use_ws:
+        assert torch.count_nonzero(ws[:4096]).item() == 0
+    pre = orc.grouped_gemm(orc.permute(x, r.row_src, K), W, r.offsets, "nk")
+    assert rel_err(C, orc.swiglu(pre) if epi == 1 else pre) < TOL_BF16 / 4
+    if save:
+        assert rel_err(P, pre) < TOL_BF16 / 4
+
+
+def test_grouped_gemm_gather_many_tiles_split_tail():
+    """More output tiles than CUs (full rounds, then a split tail) on gathered rows, twice in a
+    row on one workspace: bit-identical to the unfused pair, and 64 sampled rows against the
+    oracle."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    T, d, E, K, N = 128 * cus + 700, 512, 8, 2, 512
+    r, x, W = _gather_case(T, d, E, K, N, seed=61)
+    xd, Wd, src, offs = dev(x), dev(W), dev(r.row_src), dev(r.offsets)
+    ws = torch.zeros((moe.moe_grouped_gemm_workspace_size(),), dtype=torch.uint8, device="cuda")
+    M = T * K
+    outs = []
+    for _ in range(2):
+        C = empty_like_poisoned((M, N), torch.bfloat16)
+        moe.moe_grouped_gemm_gather(xd, src, K, Wd, offs, C, workspace=ws)
+        outs.append(C)
+    C2, _ = _permute_then_gemm(xd, Wd, r, K, 0, N, False, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], C2)
+    assert torch.count_nonzero(ws[:4096]).item() == 0
+    rows = np.sort(np.random.default_rng(62).choice(M, size=64, replace=False))
+    grp = np.searchsorted(r.offsets, rows, side="right") - 1
+    sub_off = np.concatenate([[0], np.cumsum(np.bincount(grp, minlength=E))])
+    ref = orc.grouped_gemm(x[r.row_src[rows] // K], W, sub_off, "nk")
+    got = f64(outs[0][torch.as_tensor(rows, device="cuda")])
+    row = np.linalg.norm(got - ref, axis=1) / np.linalg.norm(ref, axis=1)
+    assert row.max() < TOL_BF16
+
+
+def test_grouped_gemm_gather_out_of_range_rows_read_the_last_token():
+    """row_src entries outside [0, T*K) read token T-1 (the loads stay inside x)."""
+    T, d, E, K, N = 300, 128, 4, 2, 256
+    r, x, W = _gather_case(T, d, E, K, N, seed=71)
+    src = r.row_src.copy()
+    bad = np.array([0, 5, 77, 598, 599])
+    src[bad] = np.array([-3, T * K, T * K + 9, -(1 << 30), (1 << 31) - 1])
+    tok = np.where((src < 0) | (src >= T * K), T - 1, src // K)
+    M = T * K
+    C = empty_like_poisoned((M, N), torch.bfloat16)
+    moe.moe_grouped_gemm_gather(dev(x), dev(src), K, dev(W), dev(r.offsets), C)
+    C2 = empty_like_poisoned((M, N), torch.bfloat16)
+    moe.moe_grouped_gemm(dev(x[tok]), dev(W), 0, dev(r.offsets), C2)
+    torch.cuda.synchronize()
+    assert torch.equal(C, C2)
+
+
+def test_grouped_gemm_gather_rejects_unsupported_shapes():
+    x = torch.zeros((64, 96), dtype=torch.bfloat16, device="cuda")      # Kd = 96: not whole 64-element stages
+    W = torch.zeros((2, 64, 96), dtype=torch.bfloat16, device="cuda")
+    src = torch.arange(64, dtype=torch.int32, device="cuda")
+    offs = torch.tensor([0, 32, 64], dtype=torch.int32, device="cuda")
+    C = torch.empty((64, 64), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(moe.MoEError) as e:
+        moe.moe_grouped_gemm_gather(x, src, 1, W, offs, C)
+    assert e.value.status == moe.MOE_UNSUPPORTED
+    assert not moe.gather_supported(64, 96, 32, torch.bfloat16)
+    assert not moe.gather_supported(64, 128, 32, torch.float32)
+    assert moe.gather_supported(64, 128, 32, torch.bfloat16)
+
+
 @pytest.mark.parametrize("bf16", [True, False])
 @pytest.mark.parametrize("accumulate", [False, True])
 def test_wgrad_parity(bf16, accumulate):
@@ -898,10 +1008,11 @@ def _layer_case(cfg, rows=None):
     return inp, logits
 
 
-def _run_layer(cfg, inp, logits=None, save_pre=False, backward=False):
+def _run_layer(cfg, inp, logits=None, save_pre=False, backward=False, fuse_permute=None):
     T = inp["x"].shape[0]
     dt = torch.bfloat16 if cfg.bf16 else torch.float32
-    bufs = moe.MoEBuffers(T, cfg.d, cfg.E, cfg.K, cfg.F, dt, save_pre=save_pre, backward=backward)
+    bufs = moe.MoEBuffers(T, cfg.d, cfg.E, cfg.K, cfg.F, dt, save_pre=save_pre, backward=backward,
+                          fuse_permute=fuse_permute)
     dv = {k: dev(v) for k, v in inp.items()}
     moe.layer_forward(dv["x"], dv["w_router"], dv["bias"], dv["w13"], dv["w2"], cfg.K, cfg.score, cfg.renorm,
                       bufs, logits=dev(logits) if logits is not None else None)
@@ -925,11 +1036,27 @@ def test_layer_forward_parity(name):
     np.testing.assert_array_equal(host(bufs.topk_idx), r.idx)
     np.testing.assert_array_equal(host(bufs.offsets), r.offsets)
     np.testing.assert_array_equal(host(bufs.row_src), r.row_src)
-    assert np.array_equal(host(bufs.x_perm), ref["x_perm"])
+    # bf16 layers of these shapes fold the permute into the gate/up GEMM (no permuted copy)
+    assert (bufs.x_perm is None) == cfg.bf16
+    if bufs.x_perm is not None:
+        assert np.array_equal(host(bufs.x_perm), ref["x_perm"])
     tol = TOL_BF16 if cfg.bf16 else TOL_F32
     assert rel_err(bufs.h, ref["h"]) < tol
     assert rel_err(bufs.y_perm, ref["y_perm"]) < tol
     assert rel_err(bufs.y, ref["y"]) < tol
+
+
+@pytest.mark.parametrize("name", ["small_bf16", "fine_grained_512"])
+def test_layer_forward_fused_permute_is_bit_identical(name):
+    """The forward with the permute folded into the gate/up GEMM gives the same bits as the
+    forward that writes the permuted copy, on every output (h, the saved pre-activations, y_perm, y)."""
+    cfg, rows = (SMALL_BF16, None) if name == "small_bf16" else (mi.CONFIGS["fine_grained"], 512)
+    inp, logits = _layer_case(cfg, rows)
+    fused, _ = _run_layer(cfg, inp, logits=logits, save_pre=True)
+    plain, _ = _run_layer(cfg, inp, logits=logits, save_pre=True, fuse_permute=False)
+    assert fused.fuse_permute and fused.x_perm is None and not plain.fuse_permute
+    for n in ("h", "pre", "y_perm", "y"):
+        assert torch.equal(getattr(fused, n), getattr(plain, n)), n
 
 
 def test_layer_forward_with_gpu_router():
