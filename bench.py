@@ -144,25 +144,35 @@ def host_description(threads: int) -> str:
     return f"{model}, {os.cpu_count()} logical CPUs visible, {blas} with {threads} threads"
 
 
-def copy_bandwidth(torch) -> float:
-    """On-box HBM reference: GB/s (bytes read + written) of a 1 GiB device copy, median of five
-    launches, each after a read-only 1 GiB pass that evicts the caches."""
+def stream_rates(torch) -> dict:
+    """On-box HBM references, GB/s, each the median of five launches after a read-only 1 GiB
+    pass that evicts the caches: a 1 GiB device copy (bytes read + written), a read-mostly pass
+    (the column sums of a [32, 8M] fp32 matrix: 1 GiB read, 32 MiB written) and a write-only
+    pass over 1 GiB (a fill; the 256 MB Infinity Cache may hold part of it when the clock stops)."""
     src = torch.empty(512 << 20, dtype=torch.bfloat16, device="cuda").fill_(1.0)
     dst = torch.empty_like(src)
     flush = torch.ones(256 << 20, dtype=torch.float32, device="cuda")
+    rd = torch.ones((32, 8 << 20), dtype=torch.float32, device="cuda")
+    col = torch.empty((8 << 20,), dtype=torch.float32, device="cuda")
     acc = torch.empty((), dtype=torch.float32, device="cuda")
-    ts = []
-    for _ in range(6):
-        torch.sum(flush, dim=0, out=acc)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        dst.copy_(src)
-        e1.record()
-        torch.cuda.synchronize()
-        ts.append(e0.elapsed_time(e1))
-    ms = sorted(ts[1:])[2]
-    del src, dst, flush, acc
-    return 2 * (1 << 30) / (ms * 1e-3) / 1e9
+
+    def med(fn):
+        ts = []
+        for _ in range(6):
+            torch.sum(flush, dim=0, out=acc)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return sorted(ts[1:])[2]
+    gib = float(1 << 30)
+    out = {"copy": 2 * gib / (med(lambda: dst.copy_(src)) * 1e-3) / 1e9,
+           "read": (gib + (32 << 20)) / (med(lambda: torch.sum(rd, dim=0, out=col)) * 1e-3) / 1e9,
+           "write": gib / (med(lambda: dst.fill_(0.5)) * 1e-3) / 1e9}
+    del src, dst, flush, rd, col, acc
+    return out
 
 
 class ColdTimer:
@@ -386,6 +396,12 @@ def main():
     # each kernel alone with the caches flushed before every launch (median and min of the reps)
     cold = ColdTimer(torch, stream)
     kcold = {name: cold.time(call, args.cold_reps) for name, call in steps}
+    if bufs.x_perm is None:
+        # the layer reads token rows inside the gate/up GEMM; the standalone permute (the call
+        # a training forward and other callers make) is timed on its own, cold, for its HBM rate
+        xp = torch.empty((cfg.T * cfg.K, cfg.d), dtype=dt, device="cuda")
+        kcold["permute"] = cold.time(lambda: moe.moe_permute(x, cfg.K, bufs.slot_pos, xp), args.cold_reps)
+        del xp
     del cold
     torch.cuda.empty_cache()
 
@@ -397,14 +413,16 @@ def main():
     tf_up = flops_up / (kms["gemm_gate_up"] * 1e-3) / 1e12
     tf_down = flops_down / (kms["gemm_down"] * 1e-3) / 1e12
     tf_gg = (flops_up + flops_down) / ((kms["gemm_gate_up"] + kms["gemm_down"]) * 1e-3) / 1e12
-    nbytes = {
-        "permute": (cfg.T + M) * cfg.d * esz + 4 * M,
-        "combine": (M + cfg.T) * cfg.d * esz + 8 * M,
+    # (bytes read, bytes written) of each HBM-bound call
+    nrw = {
+        "permute": (cfg.T * cfg.d * esz + 4 * M, M * cfg.d * esz),
+        "combine": (M * cfg.d * esz + 8 * M, cfg.T * cfg.d * esz),
         # fused: x and W once, then per slot the index and gate written, its in-tile rank written
         # and read back, its position and its inverse written, and the fp32 logits written
-        "router_route": cfg.T * cfg.d * esz + cfg.E * cfg.d * esz + 24 * M + 4 * cfg.T * cfg.E,
-        "router": cfg.T * cfg.d * esz + cfg.E * cfg.d * esz + 4 * cfg.T * cfg.E,
+        "router_route": (cfg.T * cfg.d * esz + cfg.E * cfg.d * esz + 4 * M, 20 * M + 4 * cfg.T * cfg.E),
+        "router": (cfg.T * cfg.d * esz + cfg.E * cfg.d * esz, 4 * cfg.T * cfg.E),
     }
+    nbytes = {k: r + w for k, (r, w) in nrw.items()}
 
     traffic = None
     try:
@@ -421,14 +439,16 @@ def main():
     clock = None if args.no_clock or args.calib_copy else sample_clock(torch, graph.replay)
     # after the timed region; left out of the counter-calibration runs, whose own 512 MiB pass must
     # be the only elementwise kernel of its kind
-    copy_gbs = copy_bandwidth(torch) if not args.calib_copy else float("nan")
+    rates = stream_rates(torch) if not args.calib_copy else {"copy": float("nan"), "read": float("nan"),
+                                                              "write": float("nan")}
+    copy_gbs = rates["copy"]
     cpu = cpu_baseline(cfg, inp, args.cpu_seconds)
     if cpu is not None and cfg.name != "tiny_fp32":
         cpu["one_core"] = one_core_oracle(mi.CONFIGS["tiny_fp32"], cfg, inp)
-    hbm_names = [n for n in ("router_route", "router", "permute", "combine") if n in kms]
+    hbm_names = [n for n in ("router_route", "router", "permute", "combine") if n in kcold]
     hbm_cold = {n: nbytes[n] / (kcold[n]["median"] * 1e-3) / 1e9 for n in hbm_names}
     hbm_best = {n: nbytes[n] / (kcold[n]["min"] * 1e-3) / 1e9 for n in hbm_names}
-    hbm_layer = {n: nbytes[n] / (kms[n] * 1e-3) / 1e9 for n in hbm_names}
+    hbm_layer = {n: nbytes[n] / (kms[n] * 1e-3) / 1e9 for n in hbm_names if n in kms}
     sclk = clock.get("sclk_mhz_median") if clock else None
 
     out = {
@@ -455,7 +475,8 @@ def main():
         "kernels_cold_ms": kcold,
         "timing": {"value": "one HIP-graph replay of the layer per step",
                    "kernels_ms": "average of K eager passes of the layer, HIP events between the calls",
-                   "kernels_cold_ms": f"each kernel alone, {args.cold_reps} launches, a read-only 1 GiB pass "
+                   "kernels_cold_ms": f"each kernel alone (and the standalone permute when the layer folds it "
+                                      f"into the gate/up GEMM), {args.cold_reps} launches, a read-only 1 GiB pass "
                                       "before each (L2 and Infinity Cache cold)",
                    "eager_ms_per_step": eager_ms_per_step,
                    "eager_tokens_per_s": cfg.T / (eager_ms_per_step * 1e-3)},
@@ -464,7 +485,10 @@ def main():
         "hbm_gbs_best": hbm_best,
         "hbm_gbs_in_layer": hbm_layer,
         "hbm_frac": {k: {"of_spec": v / PEAK_HBM_GBS, "of_onbox_copy": v / copy_gbs} for k, v in hbm_cold.items()},
+        "hbm_read_write_bytes": {k: list(nrw[k]) for k in hbm_cold},
         "onbox_copy_gbs": copy_gbs,
+        "onbox_read_gbs": rates["read"],
+        "onbox_write_gbs": rates["write"],
         "clock": clock,
         "load": {"min": int(counts.min()), "max": int(counts.max()), "empty": int((counts == 0).sum())},
         # the permute runs inside the gate/up GEMM's row loads (no permuted copy is written)
