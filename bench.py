@@ -57,6 +57,8 @@ def parse():
     ap.add_argument("--cold-reps", type=int, default=100,
                     help="launches of each kernel timed alone with the caches flushed before each one")
     ap.add_argument("--no-clock", action="store_true", help="skip sampling the GPU clock with amd-smi")
+    ap.add_argument("--no-train-form", action="store_true",
+                    help="skip the training form of the forward (permuted copy written, pre-activations saved)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain elementwise pass over 512 MiB (3 launches of torch's neg "
                          "kernel: 512 MiB read, 512 MiB written) to calibrate rocprofv3 FETCH_SIZE / WRITE_SIZE")
@@ -323,6 +325,22 @@ def time_replays(torch, graph, warmup: int, steps: int) -> float:
     return (time.perf_counter() - t0) * 1e3 / max(steps, 1)
 
 
+def replay_stats(torch, graph, stream, reps: int, flush=None) -> dict:
+    """Each of reps graph replays bracketed by its own HIP events (flush(), when given, runs
+    before each replay, outside the events): median, min and mean ms."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    for e0, e1 in evs:
+        if flush is not None:
+            flush()
+        e0.record(stream)
+        graph.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ts = np.array([e0.elapsed_time(e1) for e0, e1 in evs])
+    return {"median": float(np.median(ts)), "min": float(ts.min()), "mean": float(ts.mean()), "reps": int(reps)}
+
+
 def time_steps(torch, steps, stream, reps: int) -> tuple[dict, float]:
     """Average duration of each (name, call) over reps eager passes, from HIP events recorded
     on the launch stream between the calls; and the eager ms per pass."""
@@ -396,6 +414,10 @@ def main():
     # each kernel alone with the caches flushed before every launch (median and min of the reps)
     cold = ColdTimer(torch, stream)
     kcold = {name: cold.time(call, args.cold_reps) for name, call in steps}
+    # the layer replay by replay: warm (back to back) and cold (caches flushed before each)
+    layer_ms = {"warm": replay_stats(torch, graph, stream, args.cold_reps),
+                "cold": replay_stats(torch, graph, stream, args.cold_reps,
+                                     flush=lambda: torch.sum(cold.buf, dim=0, out=cold.out))}
     if bufs.x_perm is None:
         # the layer reads token rows inside the gate/up GEMM; the standalone permute (the call
         # a training forward and other callers make) is timed on its own, cold, for its HBM rate
@@ -435,6 +457,30 @@ def main():
         traffic = None
 
     tokens_per_s = cfg.T / (ms_per_step * 1e-3)
+
+    # the training form of the forward: the permuted copy written (the weight gradient reads it)
+    # and the SwiGLU pre-activations saved; graph replays as for value
+    train = None
+    if not args.no_train_form and not args.calib_copy and (bufs.fuse_permute or bufs.pre is None):
+        del graph
+        torch.cuda.empty_cache()
+        tb = moe.MoEBuffers(cfg.T, cfg.d, cfg.E, cfg.K, cfg.F, dt, save_pre=True, fuse_permute=False)
+        tsteps = moe.forward_steps(x, wr, b, w13, w2, cfg.K, cfg.score, cfg.renorm, tb)
+
+        def run_train():
+            for _, call in tsteps:
+                call()
+        for _ in range(args.warmup):
+            run_train()
+        tgraph = capture(torch, run_train)
+        tms = time_replays(torch, tgraph, args.warmup, args.steps)
+        tkms, _ = time_steps(torch, tsteps, stream, args.steps)
+        train = {"ms_per_step": tms, "tokens_per_s": cfg.T / (tms * 1e-3),
+                 "gate_up_tflops": flops_up / (tkms["gemm_gate_up"] * 1e-3) / 1e12, "kernels_ms": tkms,
+                 "form": "permute written, SwiGLU pre-activations saved (what a training step's forward does)"}
+        del tgraph, tb, tsteps
+        torch.cuda.empty_cache()
+        graph = capture(torch, run_all)
     counts = bufs.counts.cpu().numpy()
     clock = None if args.no_clock or args.calib_copy else sample_clock(torch, graph.replay)
     # after the timed region; left out of the counter-calibration runs, whose own 512 MiB pass must
@@ -473,8 +519,12 @@ def main():
                                                 "down": flops_down / (kcold["gemm_down"]["median"] * 1e-3) / 1e12}},
         "kernels_ms": kms,
         "kernels_cold_ms": kcold,
+        "layer_replay_ms": layer_ms,
+        "training_forward": train,
         "timing": {"value": "one HIP-graph replay of the layer per step",
                    "kernels_ms": "average of K eager passes of the layer, HIP events between the calls",
+                   "layer_replay_ms": f"{args.cold_reps} graph replays each between its own HIP events, back to "
+                                      "back (warm) and after a read-only 1 GiB pass (cold); median, min, mean",
                    "kernels_cold_ms": f"each kernel alone (and the standalone permute when the layer folds it "
                                       f"into the gate/up GEMM), {args.cold_reps} launches, a read-only 1 GiB pass "
                                       "before each (L2 and Infinity Cache cold)",
