@@ -1356,6 +1356,12 @@ __device__ __forceinline__ void mainloop(PP& P, int nk) {
 #pragma unroll
     for (int q = 0; q < kQ; ++q) P.template issue<1>(1, q);
   }
+  // the accumulators are zeroed here, while the first stages are in flight (left to itself
+  // the compiler zeroed them after the first wait, 256 writes on the tile's critical path)
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) asm volatile("" : "+a"(P.acc[i][j]));
   if (nk > 2) {
     P.template issue<0>(2, 0);
     P.template issue<0>(2, 1);

@@ -1,5 +1,6 @@
 """GPU parity over seeded random shapes of the grouped GEMM paths the layer uses: the N-by-K
-ring (plain and SwiGLU), the K-by-N ring (plain and SwiGLU backward), and the weight gradient,
+ring (plain and SwiGLU, on a permuted copy or on gathered token rows), the K-by-N ring (plain and
+SwiGLU backward), and the weight gradient,
 against the CPU oracle.  Each case draws a group count, ragged group sizes with empty and
 dominant groups, widths and reduction lengths spanning several tiles with ragged tails, rows
 outside the groups, and whether a workspace (the split tail) is passed.  Bars as in the other
@@ -99,6 +100,38 @@ def test_sweep_nk_swiglu(seed):
     pre = orc.grouped_gemm(A[lo:int(off[-1])], W, off - lo, "nk")
     _check_rows(H, off, M, orc.swiglu(pre))
     _check_rows(P, off, M, pre)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_sweep_gather(seed):
+    """The gate/up GEMM on gathered token rows (plain or SwiGLU, with or without the split-tail
+    workspace) over random routings: bit-identical to moe_permute followed by moe_grouped_gemm,
+    and within the bars of the oracle on the permuted rows."""
+    rng = np.random.default_rng(2500 + seed)
+    T, E = int(rng.integers(1, 3000)), int(rng.integers(1, 65))
+    K = int(rng.integers(1, min(E, 8) + 1))
+    Kd = 64 * int(rng.integers(1, 13))
+    swiglu = bool(rng.integers(2))
+    N = 16 * int(rng.integers(1, 49)) if swiglu else 8 * int(rng.integers(1, 97))
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    r = orc.route(logits, None, K)
+    x = mi.f32_to_bf16_bits(rng.standard_normal((T, Kd)).astype(np.float32))
+    W = mi.f32_to_bf16_bits((rng.standard_normal((E, N, Kd)) / math.sqrt(Kd)).astype(np.float32))
+    ws = _workspace(bool(rng.integers(2)))
+    epi = moe.MOE_EPI_SWIGLU if swiglu else moe.MOE_EPI_NONE
+    width = N // 2 if swiglu else N
+    M = T * K
+    xd, Wd, offs = dev(x), dev(W), dev(r.offsets)
+    C = empty_like_poisoned((M, width), torch.bfloat16)
+    moe.moe_grouped_gemm_gather(xd, dev(r.row_src), K, Wd, offs, C, epi, workspace=ws)
+    xp = empty_like_poisoned((M, Kd), torch.bfloat16)
+    moe.moe_permute(xd, K, dev(r.slot_pos), xp)
+    C2 = empty_like_poisoned((M, width), torch.bfloat16)
+    moe.moe_grouped_gemm(xp, Wd, 0, offs, C2, epi, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(C, C2)
+    pre = orc.grouped_gemm(orc.permute(x, r.row_src, K), W, r.offsets, "nk")
+    _check_rows(C, r.offsets, M, orc.swiglu(pre) if swiglu else pre)
 
 
 @pytest.mark.parametrize("seed", range(8))
