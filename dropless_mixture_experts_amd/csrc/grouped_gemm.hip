@@ -1080,6 +1080,11 @@ struct Pipe {
   int64_t b_stage = kStageBytes;  // uniform: global bytes of B per stage
   int64_t a_stage = kStageBytes;  // uniform: global bytes of A per stage (WG)
   int kvalid = 1 << 30;      // WG: rows of the reduction; DMAs of rows past them write zeros
+  // LDS byte offsets of the slots of half-stages 2 s .. 2 s + 4 for the main loop's current
+  // stage s, rotated by two halves from stage to stage.  Every half-stage the loop touches is
+  // 0..6 halves past 2 s, a distance known at compile time (H below), so its offset is one of
+  // these registers (computing (2 st + OP) mod 5 took 6 scalar instructions a slot).
+  uint32_t so0 = 0, so1 = kSlotBytes, so2 = 2 * kSlotBytes, so3 = 3 * kSlotBytes, so4 = 4 * kSlotBytes;
   const char* L;
   f32x16 (&acc)[4][4];
   static constexpr int kBL = BL;
@@ -1120,11 +1125,35 @@ struct Pipe {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
   }
+  template <int H>
+  __device__ __forceinline__ uint32_t sob() const {
+    constexpr int h = H % kSlots;
+    if constexpr (h == 0) return so0;
+    else if constexpr (h == 1) return so1;
+    else if constexpr (h == 2) return so2;
+    else if constexpr (h == 3) return so3;
+    else return so4;
+  }
+  // the slot offset of half-stage h = 2 s + H (H >= 0: from the carried offsets)
+  template <int H>
+  __device__ __forceinline__ uint32_t slot_bytes(int h) const {
+    if constexpr (H >= 0) return sob<H>();
+    else return (uint32_t)(h % kSlots) * kSlotBytes;
+  }
+  __device__ __forceinline__ void rotate() {
+    const uint32_t t0 = so0, t1 = so1;
+    so0 = so2;
+    so1 = so3;
+    so2 = so4;
+    so3 = t0;
+    so4 = t1;
+  }
   // DMA q of operand OP (0: A, 1: B) of stage st, i.e. of half-stage 2 st + OP
   // CHK (WG only): the stage may be the reduction's last, partly filled one
-  template <int OP, bool CHK = true>
+  // H: that half-stage's distance from the current stage's first half (-1: unknown)
+  template <int OP, bool CHK = true, int H = -1>
   __device__ __forceinline__ void issue(int st, int q) const {
-    const uint32_t lb = lds_w + (uint32_t)((2 * st + OP) % kSlots) * kSlotBytes + q * 1024;
+    const uint32_t lb = lds_w + slot_bytes<H>(2 * st + OP) + q * 1024;
     const char* src = OP ? b_base + (int64_t)st * (BL != LAYOUT_NK ? b_stage : (int64_t)kStageBytes)
                          : a_base + (int64_t)st * (BL == LAYOUT_WG ? a_stage : (int64_t)kStageBytes);
     const uint32_t vo = OP ? vb[q] : va[q];
@@ -1136,8 +1165,7 @@ struct Pipe {
         if (st * 64 + kr < kvalid) {
           dma(src, vo, lb);
         } else {
-          const uint32_t slot = (uint32_t)((2 * st + OP) % kSlots);
-          *(uint4*)(L + slot * kSlotBytes + (wave * kQ + q) * 1024 + lane * 16) = make_uint4(0u, 0u, 0u, 0u);
+          *(uint4*)(L + slot_bytes<H>(2 * st + OP) + (wave * kQ + q) * 1024 + lane * 16) = make_uint4(0u, 0u, 0u, 0u);
         }
         return;
       }
@@ -1165,9 +1193,10 @@ struct Pipe {
   // one VALU add each.  The empty asm hands the compiler an opaque register, so each read is
   // that register plus an immediate offset; left to itself, the compiler re-derived every
   // read's address with VALU adds in the MFMA stream, two a read.
+  template <int H = -1>
   __device__ __forceinline__ void wg_bases(int s, uint32_t (&ab)[4], uint32_t (&bb)[4]) const {
-    const uint32_t sa = __builtin_amdgcn_readfirstlane((uint32_t)((2 * s) % kSlots) * kSlotBytes);
-    const uint32_t sb = __builtin_amdgcn_readfirstlane((uint32_t)((2 * s + 1) % kSlots) * kSlotBytes);
+    const uint32_t sa = __builtin_amdgcn_readfirstlane(slot_bytes<H>(2 * s));
+    const uint32_t sb = __builtin_amdgcn_readfirstlane(slot_bytes<H < 0 ? -1 : H + 1>(2 * s + 1));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       ab[i] = a_seg[i] + sa;
@@ -1197,12 +1226,13 @@ struct Pipe {
       d.w = w1;
     }
   }
+  template <int H = -1>
   __device__ __forceinline__ void read(int s, int kk, uint4 (&a)[4], uint4 (&b)[4]) const {
-    const uint32_t sa = (uint32_t)((2 * s) % kSlots) * kSlotBytes;
-    const uint32_t sb = (uint32_t)((2 * s + 1) % kSlots) * kSlotBytes;
+    const uint32_t sa = slot_bytes<H>(2 * s);
+    const uint32_t sb = slot_bytes<H < 0 ? -1 : H + 1>(2 * s + 1);
     if constexpr (BL == LAYOUT_WG) {
       uint32_t ab[4], bb[4];
-      wg_bases(s, ab, bb);
+      wg_bases<H>(s, ab, bb);
 #pragma unroll
       for (int r = 0; r < 16; ++r) wg_read(ab, bb, kk, r, a, b);
       return;
@@ -1224,13 +1254,15 @@ struct Pipe {
   // fragment r of sub-step kk of stage s: r < 4 the A fragment of rows 32 r, else B fragment r - 4
   // (KN: r < 4 as above, else half (r - 4) & 1 of B fragment (r - 4) >> 1; 12 reads a set;
   // WG reads go through wg_read)
+  template <int H = -1>
   __device__ __forceinline__ void read1(int s, int kk, int r, uint4 (&a)[4], uint4 (&b)[4]) const {
+    constexpr int HB = H < 0 ? -1 : H + 1;
     if (r < 4) {
-      a[r] = *(const uint4*)(L + (uint32_t)((2 * s) % kSlots) * kSlotBytes + a_off + r * 4096 + ch[kk]);
+      a[r] = *(const uint4*)(L + slot_bytes<H>(2 * s) + a_off + r * 4096 + ch[kk]);
     } else if constexpr (BL == LAYOUT_KN) {
-      read_tr((uint32_t)((2 * s + 1) % kSlots) * kSlotBytes, kk, (r - 4) >> 1, (r - 4) & 1, b[(r - 4) >> 1]);
+      read_tr(slot_bytes<HB>(2 * s + 1), kk, (r - 4) >> 1, (r - 4) & 1, b[(r - 4) >> 1]);
     } else {
-      b[r - 4] = *(const uint4*)(L + (uint32_t)((2 * s + 1) % kSlots) * kSlotBytes + b_off[r - 4] + ch[kk]);
+      b[r - 4] = *(const uint4*)(L + slot_bytes<HB>(2 * s + 1) + b_off[r - 4] + ch[kk]);
     }
   }
   __device__ __forceinline__ void mma(const uint4 (&a)[4], const uint4 (&b)[4], int t0, int t1) const {
@@ -1264,45 +1296,46 @@ struct Frags {
 
 // One sub-step: the 16 MFMAs of set CUR, one LDS read after each of them when RD (the
 // fragments of sub-steps R0 and R0 + 1 of stage rs, into their sets), and DMAs Q0 .. Q1-1
-// of operand OP of stage st spread between them.
-template <typename PP, int CUR, bool RD, int R0, int OP, int Q0, int Q1, bool CHK = true>
+// of operand OP of stage st spread between them.  HR, HD: the first half-stages of stages rs
+// and st, counted from the current stage's (compile-time slot distances).
+template <typename PP, int CUR, bool RD, int R0, int OP, int Q0, int Q1, bool CHK, int HR, int HD>
 __device__ __forceinline__ void substep(const PP& P, Frags& f, int rs, int st) {
   constexpr int n = Q1 - Q0;
 #pragma unroll
   for (int t = 0; t < 16; ++t) {
     P.mma(f.a[CUR], f.b[CUR], t, t + 1);
     if (RD) {
-      if (t < 8) P.read1(rs, R0, t, f.a[R0], f.b[R0]);
-      else P.read1(rs, R0 + 1, t - 8, f.a[R0 + 1], f.b[R0 + 1]);
+      if (t < 8) P.template read1<HR>(rs, R0, t, f.a[R0], f.b[R0]);
+      else P.template read1<HR>(rs, R0 + 1, t - 8, f.a[R0 + 1], f.b[R0 + 1]);
     }
 #pragma unroll
     for (int q = 0; q < n; ++q)
-      if (t == (2 * q + 1) * 16 / (2 * (n > 0 ? n : 1))) P.template issue<OP, CHK>(st, Q0 + q);
+      if (t == (2 * q + 1) * 16 / (2 * (n > 0 ? n : 1))) P.template issue<OP, CHK, HD + OP>(st, Q0 + q);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
 // KN form of a sub-step: the reads of one fragment set (set R0 of stage rs: 12 for KN, 16 for
 // WG), one after each of the first MFMAs.
-template <typename PP, int CUR, bool RD, int R0, int OP, int Q0, int Q1, bool CHK = true>
+template <typename PP, int CUR, bool RD, int R0, int OP, int Q0, int Q1, bool CHK, int HR, int HD>
 __device__ __forceinline__ void substep_kn(const PP& P, Frags& f, int rs, int st) {
   constexpr int n = Q1 - Q0;
   constexpr bool WG = PP::kBL == LAYOUT_WG;
   constexpr int NR = WG ? 16 : 12;
   uint32_t ab[4], bb[4];
   if constexpr (WG)
-    if (RD) P.wg_bases(rs, ab, bb);
+    if (RD) P.template wg_bases<HR>(rs, ab, bb);
 #pragma unroll
   for (int t = 0; t < 16; ++t) {
     P.mma(f.a[CUR], f.b[CUR], t, t + 1);
     if constexpr (WG) {
       if (RD) P.wg_read(ab, bb, R0, t, f.a[R0], f.b[R0]);
     } else if (RD && t < NR) {
-      P.read1(rs, R0, t, f.a[R0], f.b[R0]);
+      P.template read1<HR>(rs, R0, t, f.a[R0], f.b[R0]);
     }
 #pragma unroll
     for (int q = 0; q < n; ++q)
-      if (t == (2 * q + 1) * 16 / (2 * (n > 0 ? n : 1))) P.template issue<OP, CHK>(st, Q0 + q);
+      if (t == (2 * q + 1) * 16 / (2 * (n > 0 ? n : 1))) P.template issue<OP, CHK, HD + OP>(st, Q0 + q);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -1322,11 +1355,11 @@ __device__ __forceinline__ void stage(const PP& P, int s, Frags& f) {
   constexpr int L1 = LOADS ? 1 : 0, L2 = LOADS == 2 ? 1 : 0;
   constexpr bool KN = PP::kBL == LAYOUT_KN || PP::kBL == LAYOUT_WG;
   if constexpr (KN) {
-    substep_kn<PP, 0, true, 2, 0, 2, 2 + 3 * L1, CHK>(P, f, s, s + 2);
-    substep_kn<PP, 1, true, 3, 0, 5, 5 + 3 * L1, CHK>(P, f, s, s + 2);
+    substep_kn<PP, 0, true, 2, 0, 2, 2 + 3 * L1, CHK, 0, 4>(P, f, s, s + 2);
+    substep_kn<PP, 1, true, 3, 0, 5, 5 + 3 * L1, CHK, 0, 4>(P, f, s, s + 2);
   } else {
-    substep<PP, 0, true, 2, 0, 2, 2 + 3 * L1>(P, f, s, s + 2);
-    substep<PP, 1, false, 0, 0, 5, 5 + 3 * L1>(P, f, s, s + 2);
+    substep<PP, 0, true, 2, 0, 2, 2 + 3 * L1, true, 0, 4>(P, f, s, s + 2);
+    substep<PP, 1, false, 0, 0, 5, 5 + 3 * L1, true, 0, 4>(P, f, s, s + 2);
   }
   if (NEXT) {
     if (VMC == 8) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");
@@ -1334,11 +1367,11 @@ __device__ __forceinline__ void stage(const PP& P, int s, Frags& f) {
     dma_barrier();  // stage s+1 landed and visible; every read of stage s done
   }
   if constexpr (KN) {
-    substep_kn<PP, 2, NEXT, 0, 1, 0, 8 * L1, CHK>(P, f, s + 1, s + 2);
-    substep_kn<PP, 3, NEXT, 1, 0, 0, 2 * L2, CHK>(P, f, s + 1, s + 3);
+    substep_kn<PP, 2, NEXT, 0, 1, 0, 8 * L1, CHK, 2, 4>(P, f, s + 1, s + 2);
+    substep_kn<PP, 3, NEXT, 1, 0, 0, 2 * L2, CHK, 2, 6>(P, f, s + 1, s + 3);
   } else {
-    substep<PP, 2, NEXT, 0, 1, 0, 8 * L1>(P, f, s + 1, s + 2);
-    substep<PP, 3, false, 0, 0, 0, 2 * L2>(P, f, s + 1, s + 3);
+    substep<PP, 2, NEXT, 0, 1, 0, 8 * L1, true, 2, 4>(P, f, s + 1, s + 2);
+    substep<PP, 3, false, 0, 0, 0, 2 * L2, true, 2, 6>(P, f, s + 1, s + 3);
   }
 }
 
@@ -1347,14 +1380,14 @@ __device__ __forceinline__ void mainloop(PP& P, int nk) {
   if (nk <= 0) return;
   // prologue: stages 0 and 1, and DMAs 0..1 of the A half of stage 2
 #pragma unroll
-  for (int q = 0; q < kQ; ++q) P.template issue<0>(0, q);
+  for (int q = 0; q < kQ; ++q) P.template issue<0, true, 0>(0, q);
 #pragma unroll
-  for (int q = 0; q < kQ; ++q) P.template issue<1>(0, q);
+  for (int q = 0; q < kQ; ++q) P.template issue<1, true, 1>(0, q);
   if (nk > 1) {
 #pragma unroll
-    for (int q = 0; q < kQ; ++q) P.template issue<0>(1, q);
+    for (int q = 0; q < kQ; ++q) P.template issue<0, true, 2>(1, q);
 #pragma unroll
-    for (int q = 0; q < kQ; ++q) P.template issue<1>(1, q);
+    for (int q = 0; q < kQ; ++q) P.template issue<1, true, 3>(1, q);
   }
   // the accumulators are zeroed here, while the first stages are in flight (left to itself
   // the compiler zeroed them after the first wait, 256 writes on the tile's critical path)
@@ -1363,8 +1396,8 @@ __device__ __forceinline__ void mainloop(PP& P, int nk) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) asm volatile("" : "+a"(P.acc[i][j]));
   if (nk > 2) {
-    P.template issue<0>(2, 0);
-    P.template issue<0>(2, 1);
+    P.template issue<0, true, 4>(2, 0);
+    P.template issue<0, true, 4>(2, 1);
     wait_vm18();
   } else if (nk > 1) {
     wait_vm16();
@@ -1373,17 +1406,23 @@ __device__ __forceinline__ void mainloop(PP& P, int nk) {
   }
   dma_barrier();
   Frags f;
-  P.read(0, 0, f.a[0], f.b[0]);
-  P.read(0, 1, f.a[1], f.b[1]);
+  P.template read<0>(0, 0, f.a[0], f.b[0]);
+  P.template read<0>(0, 1, f.a[1], f.b[1]);
   __builtin_amdgcn_sched_barrier(0);
   int s = 0;
   if constexpr (PP::kBL == LAYOUT_WG) {
     // stages up to nk - 5 load nothing of the last stage: no zero-fill checks there
-    for (; s + 4 < nk; ++s) stage<PP, 2, true, 8, false>(P, s, f);
+    for (; s + 4 < nk; ++s, P.rotate()) stage<PP, 2, true, 8, false>(P, s, f);
   }
-  for (; s + 3 < nk; ++s) stage<PP, 2, true, 8>(P, s, f);
-  if (s + 2 < nk) stage<PP, 1, true, 8>(P, s++, f);
-  if (s + 1 < nk) stage<PP, 0, true, 0>(P, s++, f);
+  for (; s + 3 < nk; ++s, P.rotate()) stage<PP, 2, true, 8>(P, s, f);
+  if (s + 2 < nk) {
+    stage<PP, 1, true, 8>(P, s++, f);
+    P.rotate();
+  }
+  if (s + 1 < nk) {
+    stage<PP, 0, true, 0>(P, s++, f);
+    P.rotate();
+  }
   stage<PP, 0, false, 0>(P, s, f);
 }
 
