@@ -1190,23 +1190,18 @@ struct Pipe {
     }
   }
   // WG: the LDS byte addresses of the 8 fragment columns of stage s at K row 0 (A: ab, B: bb),
-  // one VALU add each.  The empty asm hands the compiler an opaque register, so each read is
-  // that register plus an immediate offset; left to itself, the compiler re-derived every
-  // read's address with VALU adds in the MFMA stream, two a read.
+  // one VALU add each; every read is then one of them plus an immediate offset.  (With the slot
+  // offset computed as (2 s) mod 5, the compiler re-derived every read's address with VALU adds
+  // in the MFMA stream unless these went through an empty asm, which cost 16 register copies a
+  // stage; with the carried slot offsets neither is needed.)
   template <int H = -1>
   __device__ __forceinline__ void wg_bases(int s, uint32_t (&ab)[4], uint32_t (&bb)[4]) const {
     const uint32_t sa = __builtin_amdgcn_readfirstlane(slot_bytes<H>(2 * s));
     const uint32_t sb = __builtin_amdgcn_readfirstlane(slot_bytes<H < 0 ? -1 : H + 1>(2 * s + 1));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ab[i] = a_seg[i] + sa;
-      asm volatile("" : "+v"(ab[i]));
-    }
+    for (int i = 0; i < 4; ++i) ab[i] = a_seg[i] + sa;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      bb[j] = b_off[j] + sb;
-      asm volatile("" : "+v"(bb[j]));
-    }
+    for (int j = 0; j < 4; ++j) bb[j] = b_off[j] + sb;
   }
   // WG: read r of sub-step kk: r < 8 half r & 1 of A fragment r >> 1, else half (r - 8) & 1 of
   // B fragment (r - 8) >> 1 (K rows 16 kk + 4 t .. + 3 of each lane's 8, as in read_tr_at)
