@@ -4,13 +4,16 @@
 // back to their original order afterwards (page "Accelerating dropless MoE
 // training in JAX with NVIDIA Transformer Engine", Figure 3 paragraph of
 // "What specialised optimisations does dropless MoE need?").  Both are pure
-// HBM streams over token rows: one wave per token moves whole rows with 16-byte
-// lanes, so every row is read once and written once as full 64-byte segments.
+// HBM streams over token rows: one wave per token (combine: two, each with half the row,
+// when rows hold 512 or more 16-byte vectors) moves whole rows with 16-byte lanes, so every
+// row is read once and written once as full 64-byte segments.
 // Measured with the caches flushed before each launch, on the three workload shapes:
 // non-temporal stores cost 5-25% everywhere, so every output is written with ordinary
 // stores; combine reads its gathered rows non-temporally (2-4% faster than ordinary
-// loads except on one shape); rows of 512 or more 16-byte vectors move in passes of 4
-// vectors per lane (3% faster on 4096-wide bf16 rows), shorter rows in one pass of 8.
+// loads except on one shape); permute moves rows of 512 or more 16-byte vectors in passes
+// of 4 vectors per lane (3% faster on 4096-wide bf16 rows), shorter rows in one pass of 8;
+// combine's two waves a wide token were 1-3% faster than one (eleven variants of lanes,
+// waves and rows in flight per token were all within 3% of each other).
 #include "common.h"
 #include "internal.h"
 
@@ -118,15 +121,20 @@ __global__ __launch_bounds__(256) void permute_kernel(const uint4* __restrict__ 
 }
 
 // y[t] = sum_k g_tk * y_perm[slot_pos[t*K + k]], fp32 in ascending k, rounded once.
-template <typename T, bool GATES>
+// SPLIT waves share a token, each taking a contiguous 1/SPLIT of the row; UN: 16-byte vectors
+// in flight per lane per gathered row.
+template <typename T, bool GATES, int SPLIT = 1, int UN = kCUnroll>
 __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ yp,
                                                       const int32_t* __restrict__ slot_pos,
                                                       const float* __restrict__ gates, int64_t ntok,
                                                       int64_t nvec, int K, uint4* __restrict__ y) {
   using E = Elem<T>;
   const int lane = threadIdx.x & 63;
-  const int64_t t = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  const int64_t w = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  const int64_t t = w / SPLIT;
   if (t >= ntok) return;
+  const int64_t seg = (nvec + SPLIT - 1) / SPLIT;
+  const int64_t beg = (w % SPLIT) * seg, end = beg + seg < nvec ? beg + seg : nvec;
   // lane k holds slot k's row and gate (K <= 32)
   int pos = 0;
   float gk = 1.f;
@@ -136,10 +144,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
     pos = pos < 0 ? 0 : (pos >= M ? (int)(M - 1) : pos);
     if (GATES) gk = gates[t * K + lane];
   }
-  for (int64_t i0 = 0; i0 < nvec; i0 += 64 * kCUnroll) {
-    float acc[kCUnroll][E::kVec];
+  for (int64_t i0 = beg; i0 < end; i0 += 64 * UN) {
+    float acc[UN][E::kVec];
 #pragma unroll
-    for (int u = 0; u < kCUnroll; ++u)
+    for (int u = 0; u < UN; ++u)
 #pragma unroll
       for (int q = 0; q < E::kVec; ++q) acc[u][q] = 0.f;
     // two gathered rows per step: their loads are in flight together
@@ -147,19 +155,19 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
       const bool two = k + 1 < K;
       const int64_t p0 = __shfl(pos, k, 64), p1 = __shfl(pos, two ? k + 1 : k, 64);
       const float g0 = __shfl(gk, k, 64), g1 = __shfl(gk, two ? k + 1 : k, 64);
-      uint4 v0[kCUnroll], v1[kCUnroll];
+      uint4 v0[UN], v1[UN];
 #pragma unroll
-      for (int u = 0; u < kCUnroll; ++u) {
+      for (int u = 0; u < UN; ++u) {
         const int64_t i = i0 + u * 64 + lane;
-        if (i < nvec) {
+        if (i < end) {
           v0[u] = ld_nt(yp + p0 * nvec + i);
           if (two) v1[u] = ld_nt(yp + p1 * nvec + i);
         }
       }
 #pragma unroll
-      for (int u = 0; u < kCUnroll; ++u) {
+      for (int u = 0; u < UN; ++u) {
         const int64_t i = i0 + u * 64 + lane;
-        if (i < nvec) {
+        if (i < end) {
           float f[E::kVec];
           E::to_f32(v0[u], f);
 #pragma unroll
@@ -173,9 +181,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
       }
     }
 #pragma unroll
-    for (int u = 0; u < kCUnroll; ++u) {
+    for (int u = 0; u < UN; ++u) {
       const int64_t i = i0 + u * 64 + lane;
-      if (i < nvec) y[t * nvec + i] = E::from_f32(acc[u]);
+      if (i < end) y[t * nvec + i] = E::from_f32(acc[u]);
     }
   }
 }
@@ -213,13 +221,24 @@ hipError_t combine_t(const void* yp, const int32_t* slot_pos, const float* gates
                      int K, void* y, hipStream_t s) {
   if (T_ == 0) return hipSuccess;
   const int64_t nvec = d / Elem<T>::kVec;
-  const dim3 grid((unsigned)((T_ + kRowsPerBlock - 1) / kRowsPerBlock));
-  if (gates)
-    hipLaunchKernelGGL((combine_kernel<T, true>), grid, dim3(256), 0, s, (const uint4*)yp, slot_pos,
-                       gates, T_, nvec, K, (uint4*)y);
-  else
-    hipLaunchKernelGGL((combine_kernel<T, false>), grid, dim3(256), 0, s, (const uint4*)yp, slot_pos,
-                       gates, T_, nvec, K, (uint4*)y);
+  // rows of 512 or more 16-byte vectors: two waves a token (more waves in flight for the same
+  // bytes), each with up to 8 vectors a lane per gathered row
+  const bool wide = nvec >= 512;
+  const int64_t waves = wide ? 2 * T_ : T_;
+  const dim3 grid((unsigned)((waves + kRowsPerBlock - 1) / kRowsPerBlock));
+#define MOE_COMBINE(G_, S_, U_)                                                                             \
+  hipLaunchKernelGGL((combine_kernel<T, G_, S_, U_>), grid, dim3(256), 0, s, (const uint4*)yp, slot_pos, gates, \
+                     T_, nvec, K, (uint4*)y)
+  if (gates) {
+    if (wide && nvec <= 512) MOE_COMBINE(true, 2, 4);
+    else if (wide) MOE_COMBINE(true, 2, 8);
+    else MOE_COMBINE(true, 1, kCUnroll);
+  } else {
+    if (wide && nvec <= 512) MOE_COMBINE(false, 2, 4);
+    else if (wide) MOE_COMBINE(false, 2, 8);
+    else MOE_COMBINE(false, 1, kCUnroll);
+  }
+#undef MOE_COMBINE
   return hipGetLastError();
 }
 
