@@ -4,16 +4,17 @@
 // back to their original order afterwards (page "Accelerating dropless MoE
 // training in JAX with NVIDIA Transformer Engine", Figure 3 paragraph of
 // "What specialised optimisations does dropless MoE need?").  Both are pure
-// HBM streams over token rows: one wave per token (combine: two, each with half the row,
-// when rows hold 512 or more 16-byte vectors) moves whole rows with 16-byte lanes, so every
-// row is read once and written once as full 64-byte segments.
+// HBM streams over token rows: one wave per token (two, each with half the row, when rows
+// hold 512 or more 16-byte vectors and no dot product is formed) moves whole rows with
+// 16-byte lanes, so every row is read once and written once as full 64-byte segments.
 // Measured with the caches flushed before each launch, on the three workload shapes:
 // non-temporal stores cost 5-25% everywhere, so every output is written with ordinary
 // stores; combine reads its gathered rows non-temporally (2-4% faster than ordinary
-// loads except on one shape); permute moves rows of 512 or more 16-byte vectors in passes
-// of 4 vectors per lane (3% faster on 4096-wide bf16 rows), shorter rows in one pass of 8;
-// combine's two waves a wide token were 1-3% faster than one (eleven variants of lanes,
-// waves and rows in flight per token were all within 3% of each other).
+// loads except on one shape); a 4096-wide bf16 row moves in passes of 4 vectors per lane
+// (3% faster than 8), shorter rows in one pass of 8; two waves a wide token were 1-4%
+// faster than one for combine and for the 7168-wide permute, the same for the 4096-wide
+// permute (eleven variants of lanes, waves and rows in flight per token were all within
+// 3% of each other).
 #include "common.h"
 #include "internal.h"
 
@@ -29,18 +30,23 @@ constexpr int kCUnroll = 8;  // 16-byte vectors per lane per gathered row (combi
 // HBM once and written to its K rows.  Without the dot, every loaded piece of the row goes
 // straight to all K rows; with it, the slots are taken one by one (the row comes back from
 // the cache) so that each slot's dot product is a single wave reduction.
-// UN: 16-byte vectors in flight per lane per pass over the row.
-template <typename T, bool SCALE, bool DOT, int UN = 8>
+// UN: 16-byte vectors in flight per lane per pass over the row.  SPLIT (without the dot):
+// waves a token, each moving a contiguous 1/SPLIT of the row.
+template <typename T, bool SCALE, bool DOT, int UN = 8, int SPLIT = 1>
 __global__ __launch_bounds__(256) void permute_kernel(const uint4* __restrict__ x, int64_t nvec, int K,
                                                       const int32_t* __restrict__ slot_pos,
                                                       const float* __restrict__ row_scale,
                                                       const uint4* __restrict__ ydot,
                                                       float* __restrict__ dgate,
                                                       uint4* __restrict__ xp, int64_t ntok) {
+  static_assert(SPLIT == 1 || !DOT, "the dot product needs the whole row in one wave");
   using E = Elem<T>;
   const int lane = threadIdx.x & 63;
-  const int64_t t = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  const int64_t w = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  const int64_t t = w / SPLIT;
   if (t >= ntok) return;
+  const int64_t seg = (nvec + SPLIT - 1) / SPLIT;
+  const int64_t beg = (w % SPLIT) * seg, end = beg + seg < nvec ? beg + seg : nvec;
   const int64_t M = ntok * K;
   // lane k holds slot k's destination row and scale (K <= 32)
   int pos = 0;
@@ -52,12 +58,12 @@ __global__ __launch_bounds__(256) void permute_kernel(const uint4* __restrict__ 
   }
   const uint4* src = x + t * nvec;
   if constexpr (!DOT) {
-    for (int64_t i0 = 0; i0 < nvec; i0 += 64 * UN) {
+    for (int64_t i0 = beg; i0 < end; i0 += 64 * UN) {
       uint4 v[UN];
 #pragma unroll
       for (int u = 0; u < UN; ++u) {
         const int64_t i = i0 + u * 64 + lane;
-        if (i < nvec) v[u] = src[i];
+        if (i < end) v[u] = src[i];
       }
       for (int k = 0; k < K; ++k) {
         const int64_t p = __shfl(pos, k, 64);
@@ -65,7 +71,7 @@ __global__ __launch_bounds__(256) void permute_kernel(const uint4* __restrict__ 
 #pragma unroll
         for (int u = 0; u < UN; ++u) {
           const int64_t i = i0 + u * 64 + lane;
-          if (i < nvec) {
+          if (i < end) {
             uint4 o = v[u];
             if (SCALE) {
               float f[E::kVec];
@@ -207,9 +213,12 @@ hipError_t permute_t(const void* x, int64_t T_, int64_t d, int K, const int32_t*
   else if (dot)
     hipLaunchKernelGGL((permute_kernel<T, false, true>), grid, dim3(256), 0, s, xv, nvec, K, slot_pos,
                        row_scale, yv, dgate, o, T_);
-  else if (nvec >= 512)
-    hipLaunchKernelGGL((permute_kernel<T, false, false, 4>), grid, dim3(256), 0, s, xv, nvec, K, slot_pos,
-                       row_scale, yv, dgate, o, T_);
+  else if (nvec > 512)
+    hipLaunchKernelGGL((permute_kernel<T, false, false, 8, 2>), dim3((unsigned)((2 * T_ + kRowsPerBlock - 1) / kRowsPerBlock)),
+                       dim3(256), 0, s, xv, nvec, K, slot_pos, row_scale, yv, dgate, o, T_);
+  else if (nvec == 512)
+    hipLaunchKernelGGL((permute_kernel<T, false, false, 4, 2>), dim3((unsigned)((2 * T_ + kRowsPerBlock - 1) / kRowsPerBlock)),
+                       dim3(256), 0, s, xv, nvec, K, slot_pos, row_scale, yv, dgate, o, T_);
   else
     hipLaunchKernelGGL((permute_kernel<T, false, false>), grid, dim3(256), 0, s, xv, nvec, K, slot_pos,
                        row_scale, yv, dgate, o, T_);
