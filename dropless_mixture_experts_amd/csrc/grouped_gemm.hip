@@ -1088,6 +1088,11 @@ struct Pipe {
   const char* L;
   f32x16 (&acc)[4][4];
   static constexpr int kBL = BL;
+  // the plain N-by-K form: wave row wm takes the tile's 32-row fragments wm, wm + 2, wm + 4,
+  // wm + 6 (LDS bytes kAStr apart), so that a partly filled tile leaves both wave rows the same
+  // number of live fragments; the other forms take 128 contiguous rows a wave row
+  static constexpr bool kIL = BL == LAYOUT_NK && EPI == EPI_NONE;
+  static constexpr int kAStr = kIL ? 8192 : 4096;
 
   __device__ __forceinline__ Pipe(f32x16 (&c)[4][4], uint4* smem) : acc(c) {
     L = (const char*)smem;
@@ -1095,7 +1100,7 @@ struct Pipe {
     const int wm = wave >> 1, wn = wave & 1;
     const int l32 = lane & 31, hi = lane >> 5;
     lds_w = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)smem + wave * kQ * 1024);
-    a_off = (wm * 128 + l32) * 128;
+    a_off = ((kIL ? wm * 32 : wm * 128) + l32) * 128;
     if constexpr (BL == LAYOUT_KN || BL == LAYOUT_WG) {
       const int g = (lane >> 4) & 1, e = (lane >> 2) & 3, q = lane & 3;
       b_row = (8 * hi + e) * 512;
@@ -1233,7 +1238,7 @@ struct Pipe {
       return;
     } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = *(const uint4*)(L + sa + a_off + i * 4096 + ch[kk]);
+      for (int i = 0; i < 4; ++i) a[i] = *(const uint4*)(L + sa + a_off + i * kAStr + ch[kk]);
     }
     if constexpr (BL == LAYOUT_KN) {
 #pragma unroll
@@ -1253,7 +1258,7 @@ struct Pipe {
   __device__ __forceinline__ void read1(int s, int kk, int r, uint4 (&a)[4], uint4 (&b)[4]) const {
     constexpr int HB = H < 0 ? -1 : H + 1;
     if (r < 4) {
-      a[r] = *(const uint4*)(L + slot_bytes<H>(2 * s) + a_off + r * 4096 + ch[kk]);
+      a[r] = *(const uint4*)(L + slot_bytes<H>(2 * s) + a_off + r * kAStr + ch[kk]);
     } else if constexpr (BL == LAYOUT_KN) {
       read_tr(slot_bytes<HB>(2 * s + 1), kk, (r - 4) >> 1, (r - 4) & 1, b[(r - 4) >> 1]);
     } else {
@@ -1278,6 +1283,33 @@ struct Pipe {
     }
   }
   __device__ __forceinline__ void step(const uint4 (&a)[4], const uint4 (&b)[4]) const { mma(a, b, 0, 16); }
+};
+
+// The main loop of a wave whose last fragments lie past the end of its group (NF < 4 live
+// fragments of the four): their MFMAs are left out, the reads, DMAs and barriers kept, so
+// every wave of the tile still runs the same ring.  NF is a compile-time count, so each such
+// loop is scheduled like the full one, only shorter.
+template <typename PP, int NF>
+struct SkipView {
+  PP& P;
+  f32x16 (&acc)[4][4];
+  static constexpr int kBL = PP::kBL;
+  template <int OP, bool CHK = true, int H = -1>
+  __device__ __forceinline__ void issue(int st, int q) const { P.template issue<OP, CHK, H>(st, q); }
+  template <int H = -1>
+  __device__ __forceinline__ void read1(int s, int kk, int r, uint4 (&a)[4], uint4 (&b)[4]) const {
+    P.template read1<H>(s, kk, r, a, b);
+  }
+  template <int H = -1>
+  __device__ __forceinline__ void read(int s, int kk, uint4 (&a)[4], uint4 (&b)[4]) const {
+    P.template read<H>(s, kk, a, b);
+  }
+  __device__ __forceinline__ void rotate() { P.rotate(); }
+  __device__ __forceinline__ void mma(const uint4 (&a)[4], const uint4 (&b)[4], int t0, int t1) const {
+#pragma unroll
+    for (int t = 0; t < 16; ++t)
+      if (t >= t0 && t < t1 && (t >> 2) < NF) mma_rows<bf16_t>(a[t >> 2], b[t & 3], P.acc[t >> 2][t & 3]);
+  }
 };
 
 __device__ __forceinline__ void wait_vm8_lgkm0() { asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory"); }
@@ -1482,7 +1514,8 @@ struct Out {
   // local rows 0 .. NR-1 = rows row0 .. row0 + NR - 1 (those below re) of columns col0 ..
   // col0 + CW - 1 (those below ncols, a multiple of 8) to base + row * ld + col * 2; the stores
   // are non-temporal: the kernel never reads its output back
-  template <int NR = 128>
+  // IL: local row r is row row0 + 64 (r / 32) + r % 32 (a wave's interleaved fragments)
+  template <int NR = 128, bool IL = false>
   __device__ static void flush(const char* wl, char* base, int64_t ld, int64_t row0, int64_t re, int64_t col0,
                                int64_t ncols) {
     const int lane = threadIdx.x & 63;
@@ -1502,7 +1535,8 @@ struct Out {
       }
 #pragma unroll
       for (int u = 0; u < kB; ++u) {
-        const int64_t row = row0 + (i0 + u) * kRPI + rr;
+        const int r = (i0 + u) * kRPI + rr;
+        const int64_t row = row0 + (IL ? ((r >> 5) << 6) + (r & 31) : r);
         if (cok && row < re) st_nt((uint4*)(base + row * ld + col * 2), v[u]);
       }
     }
@@ -1511,7 +1545,7 @@ struct Out {
 
 // The ring kernel's epilogue (bf16 outputs; EPI_NONE or EPI_SWIGLU) for the wave's 128-row
 // block at row0; wl = this wave's 32 KB of LDS, free of every other wave's accesses.
-template <int EPI>
+template <int EPI, bool IL = false>
 __device__ __forceinline__ void store_tile_lds(const GemmParams& p, const f32x16 (&acc)[4][4], char* wl,
                                                int64_t row0, int64_t re, int64_t col0) {
   const int lane = threadIdx.x & 63;
@@ -1565,7 +1599,7 @@ __device__ __forceinline__ void store_tile_lds(const GemmParams& p, const f32x16
           for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e];
           Out<128>::put(wl, i * 32 + l32, j, q, hi, v);
         }
-    Out<128>::flush(wl, (char*)p.C, p.N * 2, row0, re, col0, p.N);
+    Out<128>::flush<128, IL>(wl, (char*)p.C, p.N * 2, row0, re, col0, p.N);
   }
 }
 
@@ -1727,7 +1761,21 @@ void grouped_gemm_ring4_kernel(GemmParams p) {
     }
     P.vb[q] = (uint32_t)((br - b0row) * ldb + c * 16);
   }
-  mainloop(P, len);
+  if constexpr (decltype(P)::kIL) {
+    // live fragments of this wave: its rows m0 + 32 wm + 64 i below the group's end
+    const int64_t live = re - m0 - 32 * (wave >> 1);
+    const int nf = live <= 0 ? 0 : live >= 256 ? 4 : (int)((live + 63) / 64);
+    using PT = decltype(P);
+    switch (__builtin_amdgcn_readfirstlane(nf)) {
+      case 4: mainloop(P, len); break;
+      case 3: { SkipView<PT, 3> sv{P, P.acc}; mainloop(sv, len); break; }
+      case 2: { SkipView<PT, 2> sv{P, P.acc}; mainloop(sv, len); break; }
+      case 1: { SkipView<PT, 1> sv{P, P.acc}; mainloop(sv, len); break; }
+      default: { SkipView<PT, 0> sv{P, P.acc}; mainloop(sv, len); break; }
+    }
+  } else {
+    mainloop(P, len);
+  }
   __syncthreads();  // every wave is done with the ring: its LDS now holds the epilogue staging
 
   const int wm = wave >> 1, wn = wave & 1;
@@ -1749,7 +1797,8 @@ void grouped_gemm_ring4_kernel(GemmParams p) {
     store_tile_dswiglu_lds(p, acc, (char*)smem + wave * 32768, m0 + wm * 128, re, (int64_t)nt * 256 + wn * 128);
   } else {
     const int64_t col0 = EPI == EPI_SWIGLU ? (int64_t)nt * 128 + wn * 64 : (int64_t)nt * 256 + wn * 128;
-    store_tile_lds<EPI>(p, acc, (char*)smem + wave * 32768, m0 + wm * 128, re, col0);
+    constexpr bool IL = decltype(P)::kIL;
+    store_tile_lds<EPI, IL>(p, acc, (char*)smem + wave * 32768, IL ? m0 + wm * 32 : m0 + wm * 128, re, col0);
   }
 }
 
