@@ -51,6 +51,7 @@ constexpr int kTileChunks = kTile * kCPR;  // chunks per operand stage (32 KB)
 constexpr int kXcd = 8;                    // MI355X: 8 XCDs, workgroups dealt round-robin
 constexpr int kGroupM = 8;                 // row tiles that share a column tile
 constexpr int kWindow = 256;               // blocks per XCD-remap window (one round: one per CU)
+constexpr int kSwigluSkipRows = 1536;      // mean group rows below which SwiGLU skips empty fragments
 
 enum { EPI_NONE = 0, EPI_SWIGLU = 1, EPI_DSWIGLU = 2 };
 enum { LAYOUT_NK = 0, LAYOUT_KN = 1 };
@@ -1065,7 +1066,7 @@ __device__ __forceinline__ const char* uniform_ptr(const char* p) { return (cons
 // K rows k0 .. k0 + 3.
 // BL = LAYOUT_WG (the weight gradient, dW = dY^T X over a group's rows): both operands are
 // K-row like the KN B operand, and both are read with ds_read_b64_tr_b16.
-template <int EPI, int BL = LAYOUT_NK>
+template <int EPI, int BL = LAYOUT_NK, bool SK = false>
 struct Pipe {
   const char* a_base;   // uniform: A at (first tile row, K = 0)
   const char* b_base;   // uniform: B at (first tile row, K = 0); KN: at (K row 0, column 0)
@@ -1088,10 +1089,11 @@ struct Pipe {
   const char* L;
   f32x16 (&acc)[4][4];
   static constexpr int kBL = BL;
-  // the plain N-by-K form: wave row wm takes the tile's 32-row fragments wm, wm + 2, wm + 4,
-  // wm + 6 (LDS bytes kAStr apart), so that a partly filled tile leaves both wave rows the same
-  // number of live fragments; the other forms take 128 contiguous rows a wave row
-  static constexpr bool kIL = BL == LAYOUT_NK && EPI == EPI_NONE;
+  // the plain N-by-K form (and the SwiGLU form with SK): wave row wm takes the tile's 32-row
+  // fragments wm, wm + 2, wm + 4, wm + 6 (LDS bytes kAStr apart), so that a partly filled tile
+  // leaves both wave rows the same number of live fragments; the other forms take 128
+  // contiguous rows a wave row
+  static constexpr bool kIL = BL == LAYOUT_NK && (EPI == EPI_NONE || (EPI == EPI_SWIGLU && SK));
   static constexpr int kAStr = kIL ? 8192 : 4096;
 
   __device__ __forceinline__ Pipe(f32x16 (&c)[4][4], uint4* smem) : acc(c) {
@@ -1570,9 +1572,9 @@ __device__ __forceinline__ void store_tile_lds(const GemmParams& p, const f32x16
           Out<64>::put(wl, i * 32 + l32, j, q, hi, h);
           if (save) Out<64>::put(wl2, i * 32 + l32, j, q, hi, g);
         }
-    Out<64>::flush(wl, (char*)p.C, F * 2, row0, re, col0, F);
+    Out<64>::flush<128, IL>(wl, (char*)p.C, F * 2, row0, re, col0, F);
     if (save) {
-      Out<64>::flush(wl2, (char*)p.epi_save, p.N * 2, row0, re, col0, F);
+      Out<64>::flush<128, IL>(wl2, (char*)p.epi_save, p.N * 2, row0, re, col0, F);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -1585,7 +1587,7 @@ __device__ __forceinline__ void store_tile_lds(const GemmParams& p, const f32x16
             Out<64>::put(wl, i * 32 + l32, j, q, hi, u);
           }
       // the up half sits F columns to the right of the gate half of the saved row
-      Out<64>::flush(wl, (char*)p.epi_save + F * 2, p.N * 2, row0, re, col0, F);
+      Out<64>::flush<128, IL>(wl, (char*)p.epi_save + F * 2, p.N * 2, row0, re, col0, F);
     }
   } else {
 #pragma unroll
@@ -1698,7 +1700,8 @@ __device__ __forceinline__ void load_partial(const GemmParams& p, int slot, f32x
 }  // namespace ring4
 
 // GA: gathered A rows (GemmParams::a_rows), N-by-K weights only
-template <int EPI, int BL, bool GA = false>
+// SK (SwiGLU only): interleaved fragments and the MFMAs of fragments past the group's end left out
+template <int EPI, int BL, bool GA = false, bool SK = false>
 __global__ __launch_bounds__(ring4::kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void grouped_gemm_ring4_kernel(GemmParams p) {
   static_assert(!GA || BL == LAYOUT_NK, "rows are gathered for N-by-K weights only");
@@ -1720,7 +1723,7 @@ void grouped_gemm_ring4_kernel(GemmParams p) {
   const int len = pc.part >= 0 ? (pc.part + 1) * nk / pc.f - k0 : nk;
 
   f32x16 acc[4][4];
-  Pipe<EPI, BL> P(acc, smem);
+  Pipe<EPI, BL, SK> P(acc, smem);
   P.a_base = uniform_ptr((const char*)p.A + (GA ? 0 : m0 * ldb) + (int64_t)k0 * kStageBytes);
   const int64_t b0row = EPI == EPI_SWIGLU ? (int64_t)nt * 128 : (int64_t)nt * 256;
   if constexpr (BL == LAYOUT_KN) {
@@ -2355,15 +2358,25 @@ hipError_t grouped_gemm_impl(const void* A, const void* B, int b_layout, const i
         hipLaunchKernelGGL((grouped_gemm_ring4_kernel<EPI_DSWIGLU, LAYOUT_KN>), rgrid, dim3(ring4::kThreads), 0, s, prm);
       else
         hipLaunchKernelGGL((grouped_gemm_ring4_kernel<EPI_NONE, LAYOUT_KN>), rgrid, dim3(ring4::kThreads), 0, s, prm);
-    } else if (a_rows) {
-      if (epilogue == EPI_SWIGLU)
+    } else if (epilogue == EPI_SWIGLU) {
+      // groups of under 1536 rows on average: each group's partly filled last row tile is a large
+      // share of the work, so the form that leaves out the MFMAs of its empty fragments is taken
+      // (its epilogue spills a little; with larger groups that cost outweighs the skipped MFMAs)
+      const bool skip = M < (int64_t)kSwigluSkipRows * G;
+      if (a_rows && skip)
+        hipLaunchKernelGGL((grouped_gemm_ring4_kernel<EPI_SWIGLU, LAYOUT_NK, true, true>), rgrid,
+                           dim3(ring4::kThreads), 0, s, prm);
+      else if (a_rows)
         hipLaunchKernelGGL((grouped_gemm_ring4_kernel<EPI_SWIGLU, LAYOUT_NK, true>), rgrid, dim3(ring4::kThreads), 0,
                            s, prm);
+      else if (skip)
+        hipLaunchKernelGGL((grouped_gemm_ring4_kernel<EPI_SWIGLU, LAYOUT_NK, false, true>), rgrid,
+                           dim3(ring4::kThreads), 0, s, prm);
       else
-        hipLaunchKernelGGL((grouped_gemm_ring4_kernel<EPI_NONE, LAYOUT_NK, true>), rgrid, dim3(ring4::kThreads), 0, s,
-                           prm);
-    } else if (epilogue == EPI_SWIGLU) {
-      hipLaunchKernelGGL((grouped_gemm_ring4_kernel<EPI_SWIGLU, LAYOUT_NK>), rgrid, dim3(ring4::kThreads), 0, s, prm);
+        hipLaunchKernelGGL((grouped_gemm_ring4_kernel<EPI_SWIGLU, LAYOUT_NK>), rgrid, dim3(ring4::kThreads), 0, s, prm);
+    } else if (a_rows) {
+      hipLaunchKernelGGL((grouped_gemm_ring4_kernel<EPI_NONE, LAYOUT_NK, true>), rgrid, dim3(ring4::kThreads), 0, s,
+                         prm);
     } else {
       hipLaunchKernelGGL((grouped_gemm_ring4_kernel<EPI_NONE, LAYOUT_NK>), rgrid, dim3(ring4::kThreads), 0, s, prm);
     }
