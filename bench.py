@@ -710,11 +710,11 @@ def bench_mxfp8(args, torch, moe, mi):
         mark(2)
         moe.moe_permute_mx(tq, ts, K, bufs.slot_pos, xq, xs)
         mark(3)
-        moe.moe_grouped_gemm_mx(xq, xs, w13c, w13s, bufs.offsets, bufs.h, moe.MOE_EPI_SWIGLU)
+        moe.moe_grouped_gemm_mx(xq, xs, w13c, w13s, bufs.offsets, bufs.h, moe.MOE_EPI_SWIGLU, workspace=bufs.gemm_ws)
         mark(4)
         moe.moe_mx_quantize(bufs.h, hq, hs)
         mark(5)
-        moe.moe_grouped_gemm_mx(hq, hs, w2c, w2s, bufs.offsets, bufs.y_perm, moe.MOE_EPI_NONE)
+        moe.moe_grouped_gemm_mx(hq, hs, w2c, w2s, bufs.offsets, bufs.y_perm, moe.MOE_EPI_NONE, workspace=bufs.gemm_ws)
         mark(6)
         moe.moe_unpermute_combine(bufs.y_perm, bufs.slot_pos, bufs.gates, T, K, bufs.y)
         mark(7)

@@ -2172,7 +2172,8 @@ void grouped_gemm_mx_kernel(GemmParams p) {
   __shared__ uint4 smem[2 * kSlotBytes / 16];
   int g, nt;
   int64_t m0, re;
-  if (!find_tile<ring4::kThreads>(p, g, m0, re, nt, (int*)smem)) return;
+  Piece pc;
+  if (!find_tile<ring4::kThreads>(p, g, m0, re, nt, (int*)smem, &pc)) return;
   __syncthreads();  // every thread has read the tile from the scratch that the loads overwrite
   g = __builtin_amdgcn_readfirstlane(g);
   nt = __builtin_amdgcn_readfirstlane(nt);
@@ -2182,7 +2183,10 @@ void grouped_gemm_mx_kernel(GemmParams p) {
   const int l32 = lane & 31, hi = lane >> 5;
   const int64_t ld = p.Kd;           // bytes per row of codes
   const int64_t lds_ = p.Kd / 32;    // bytes per row of scales
-  const int nk = (int)(p.Kd / kMxRow);
+  // stages of this block: the whole Kd extent, or one piece of it (a split tile of the tail)
+  const int nkt = (int)(p.Kd / kMxRow);
+  const int k0 = pc.part >= 0 ? pc.part * nkt / pc.f : 0;
+  const int nk = pc.part >= 0 ? (pc.part + 1) * nkt / pc.f - k0 : nkt;
   const int64_t b0row = EPI == EPI_SWIGLU ? (int64_t)nt * 128 : (int64_t)nt * 256;
   const int64_t F = p.N / 2;
   // the tile's B row of local row r (SwiGLU: gate rows, then the matching up rows)
@@ -2205,10 +2209,10 @@ void grouped_gemm_mx_kernel(GemmParams p) {
   // uniform bases at the tile's first rows; per-lane 32-bit offsets of rows relative to them
   // (within (N + 256) Kd bytes, checked on the host)
   const int64_t b_first = (int64_t)g * p.N + b0row;
-  const char* a_base = ring4::uniform_ptr((const char*)p.A + m0 * ld);
-  const char* b_base = ring4::uniform_ptr((const char*)p.B + b_first * ld);
-  const char* sa_base = ring4::uniform_ptr((const char*)p.sa + m0 * lds_);
-  const char* sb_base = ring4::uniform_ptr((const char*)p.sb + b_first * lds_);
+  const char* a_base = ring4::uniform_ptr((const char*)p.A + m0 * ld + (int64_t)k0 * kMxRow);
+  const char* b_base = ring4::uniform_ptr((const char*)p.B + b_first * ld + (int64_t)k0 * kMxRow);
+  const char* sa_base = ring4::uniform_ptr((const char*)p.sa + m0 * lds_ + k0 * 4);
+  const char* sb_base = ring4::uniform_ptr((const char*)p.sb + b_first * lds_ + k0 * 4);
   uint32_t va[kQ], vb[kQ];
 #pragma unroll
   for (int q = 0; q < kQ; ++q) {
@@ -2290,6 +2294,21 @@ void grouped_gemm_mx_kernel(GemmParams p) {
     }
   }
   __syncthreads();  // every wave is done with the slots: they hold the epilogue staging now
+  if (pc.part >= 0) {
+    // a piece of a split tile: publish the partial; the last piece of the tile reduces (as the
+    // ring kernel does)
+    const int r = pc.slot % pc.R;
+    ring4::store_partial(p, pc.slot, acc);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the partial is visible in memory
+    int old = 0;
+    if (lane == 0) old = atomicAdd(p.ws_count + r * 4 + wave, 1);
+    old = __builtin_amdgcn_readfirstlane(old);
+    if (old != pc.f - 1) return;
+    asm volatile("" ::: "memory");  // the loads stay after the count that allowed them
+    ring4::load_partial(p, r, acc, false);
+    for (int j = 1; j < pc.f; ++j) ring4::load_partial(p, j * pc.R + r, acc, true);
+    if (lane == 0) p.ws_count[r * 4 + wave] = 0;
+  }
   // the ring kernel's epilogue: LDS staging (32 KB a wave of the idle slots), bf16 out
   const int64_t col0 = EPI == EPI_SWIGLU ? (int64_t)nt * 128 + wn * 64 : (int64_t)nt * 256 + wn * 128;
   ring4::store_tile_lds<EPI>(p, acc, (char*)smem + wave * 32768, m0 + wm * 128, re, col0);
@@ -2297,7 +2316,7 @@ void grouped_gemm_mx_kernel(GemmParams p) {
 
 hipError_t launch_grouped_gemm_mx(const uint8_t* A, const uint8_t* SA, const uint8_t* B, const uint8_t* SB,
                                   const int32_t* offs, int64_t M, int64_t N, int64_t Kd, int G, int epilogue,
-                                  void* C, hipStream_t s) {
+                                  void* C, void* ws, size_t ws_bytes, hipStream_t s) {
   if (M == 0) return hipSuccess;
   if ((N + 256) * Kd >= ((int64_t)1 << 32)) return hipErrorInvalidValue;  // per-lane DMA offsets
   GemmParams prm{A, B, offs, nullptr, nullptr, C, M, N, Kd, G, 0, nullptr, nullptr, 0, 0, 0};
@@ -2305,8 +2324,19 @@ hipError_t launch_grouped_gemm_mx(const uint8_t* A, const uint8_t* SA, const uin
   prm.sb = SB;
   prm.NT = (epilogue == EPI_SWIGLU) ? (int)((N / 2 + 127) / 128) : (int)((N + kTile - 1) / kTile);
   prm.nk = (int)(Kd / mxg::kMxRow);
+  // with a workspace the grid ends in up to P piece blocks of a split tail (as the ring kernel)
+  if (ws && ws_bytes >= kSplitCountBytes + kSplitSlotFloats * sizeof(float)) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return hipGetLastError();
+    prm.ws_count = (int*)ws;
+    prm.ws_part = (float*)((char*)ws + kSplitCountBytes);
+    prm.ws_slots = (int)std::min<size_t>((ws_bytes - kSplitCountBytes) / (kSplitSlotFloats * sizeof(float)), 1 << 20);
+    prm.P = cus;
+  }
   const int64_t max_mt = (M + kTile - 1) / kTile + G;
-  const dim3 grid((unsigned)(max_mt * prm.NT));
+  const dim3 grid((unsigned)(max_mt * prm.NT + prm.P));
   if (epilogue == EPI_SWIGLU)
     hipLaunchKernelGGL((grouped_gemm_mx_kernel<EPI_SWIGLU>), grid, dim3(ring4::kThreads), 0, s, prm);
   else

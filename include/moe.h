@@ -56,7 +56,7 @@ enum moe_score { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 };
 enum moe_layout { MOE_LAYOUT_NK = 0, MOE_LAYOUT_KN = 1 };
 enum moe_epilogue { MOE_EPI_NONE = 0, MOE_EPI_SWIGLU = 1, MOE_EPI_DSWIGLU = 2 };
 
-#define MOE_ABI_VERSION 8
+#define MOE_ABI_VERSION 9
 #define MOE_MAX_EXPERTS 256
 #define MOE_MAX_TOPK 32
 #define MOE_MAX_GROUPS 1024
@@ -337,13 +337,20 @@ int32_t moe_mx_quantize(const void* x, int64_t R, int64_t K, int32_t dtype, uint
  *   epilogue NONE: C [M, N] = P;  SWIGLU: N = 2F, C [M, F] = silu(P[:, :F]) * P[:, F:];  bf16 out
  *   A DEVICE [M, Kd] codes, A_scales DEVICE [M, Kd / 32];  B DEVICE [G, N, Kd] codes,
  *   B_scales DEVICE [G, N, Kd / 32] (as written by moe_mx_quantize)
+ *   workspace DEVICE, NULL or workspace_bytes (moe_grouped_gemm_workspace_size) bytes, 16-byte
+ *     aligned, caller-owned, with the same contract as moe_grouped_gemm's: the last, partly
+ *     filled round of output tiles is split along Kd across otherwise idle CUs (fp32 partials
+ *     summed in a fixed order); its first 4096 bytes must be zero before the first call and
+ *     every call leaves them zero; calls that overlap in time need separate workspaces; with
+ *     NULL no tile is split (results differ only in the fp32 summation order of those tiles).
  * Requires 0 <= M < 2^31, N >= 8, N % 8 == 0 (SWIGLU: N % 16 == 0), Kd % 128 == 0,
  * (N + 256) * Kd < 2^32, 1 <= G <= MOE_MAX_GROUPS.  Rows of C outside every group are not
  * written.
  */
 int32_t moe_grouped_gemm_mx(const uint8_t* A, const uint8_t* A_scales, const uint8_t* B, const uint8_t* B_scales,
                             const int32_t* group_offsets, int64_t M, int64_t N, int64_t Kd, int32_t G,
-                            int32_t epilogue, void* C, moe_stream_t stream);
+                            int32_t epilogue, void* C, void* workspace, size_t workspace_bytes,
+                            moe_stream_t stream);
 
 /*
  * Permute of MXFP8 rows (S4 on quantised tokens): codes_perm[slot_pos[s]] = codes[s / K] and

@@ -341,7 +341,10 @@ def _check_mx_gemm(ac, asc, bc, bsc, G, N, Kd, offs, C, epi):
     ([130, 0, 70, 256], 512, 384, 1),      # SwiGLU epilogue, three stages
     ([1, 2, 3], 64, 128, 1),               # tiny groups, N below one tile
 ])
-def test_grouped_gemm_mx_parity(counts, N, Kd, epi):
+@pytest.mark.parametrize("use_ws", [False, True])
+def test_grouped_gemm_mx_parity(counts, N, Kd, epi, use_ws):
+    """With a workspace, a grid of a few tiles splits them along Kd into pieces (when they have
+    at least two 128-value stages each); the workspace counters return to zero."""
     rng = np.random.default_rng(sum(counts) + N + Kd + epi)
     G, M = len(counts), sum(counts)
     offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
@@ -349,10 +352,46 @@ def test_grouped_gemm_mx_parity(counts, N, Kd, epi):
     bc, bsc = _mx_operands(rng, G * N, Kd)
     Nout = N // 2 if epi == 1 else N
     C = torch.full((M, Nout), float("nan"), dtype=torch.bfloat16, device="cuda")
+    ws = torch.zeros((moe.moe_grouped_gemm_workspace_size(),), dtype=torch.uint8, device="cuda") if use_ws else None
     moe.moe_grouped_gemm_mx(_u8(ac), _u8(asc), _u8(bc.reshape(G, N, Kd)), _u8(bsc.reshape(G, N, Kd // 32)),
-                            dev(offs), C, epilogue=epi)
+                            dev(offs), C, epilogue=epi, workspace=ws)
     torch.cuda.synchronize()
     _check_mx_gemm(ac, asc, bc, bsc, G, N, Kd, offs, C, epi)
+    if use_ws:
+        assert torch.count_nonzero(ws[:4096]).item() == 0
+
+
+def test_grouped_gemm_mx_split_tail():
+    """More output tiles than CUs, so full rounds and then a split tail, twice in a row on one
+    workspace: both calls write the same bits, the counters return to zero, and 48 sampled rows
+    match the oracle's product of the same codes and scales."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    counts = [256 * cus // 4 + 300, 256 * cus // 4 - 90, 700]
+    G, M, N, Kd = len(counts), sum(counts), 1024, 512
+    rng = np.random.default_rng(93)
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    ac, asc = _mx_operands(rng, M, Kd)
+    bc, bsc = _mx_operands(rng, G * N, Kd)
+    args = (_u8(ac), _u8(asc), _u8(bc.reshape(G, N, Kd)), _u8(bsc.reshape(G, N, Kd // 32)), dev(offs))
+    ws = torch.zeros((moe.moe_grouped_gemm_workspace_size(),), dtype=torch.uint8, device="cuda")
+    outs = []
+    for _ in range(2):
+        C = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+        moe.moe_grouped_gemm_mx(*args, C, workspace=ws)
+        outs.append(C)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
+    assert torch.count_nonzero(ws[:4096]).item() == 0
+    assert not torch.isnan(outs[0]).any().item()
+    rows = np.sort(rng.choice(M, 48, replace=False))
+    a = orc.mx_dequantize(ac[rows], asc[rows])
+    b = orc.mx_dequantize(bc, bsc).reshape(G, N, Kd)
+    got = orc.to_f64(host(outs[0][torch.as_tensor(rows, device="cuda")]))
+    for n, r in enumerate(rows):
+        e = int(np.searchsorted(offs, r, side="right") - 1)
+        ref = b[e] @ a[n]
+        tol = 2.0 ** -8 * np.abs(ref) + 3e-4 * (np.abs(b[e]) @ np.abs(a[n]))
+        assert np.all(np.abs(got[n] - ref) <= tol), (int(r), float(np.max(np.abs(got[n] - ref) - tol)))
 
 
 def test_mx_gate_up_mixtral_shape_sampled():

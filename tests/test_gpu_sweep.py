@@ -264,10 +264,13 @@ def test_sweep_grouped_gemm_mx(seed):
     bc, bsc = _mx_operands(rng, G * N, Kd)
     C = torch.full((M, N // 2 if epi == 1 else N), float("nan"), dtype=torch.bfloat16, device="cuda")
     u8 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    ws = _workspace(bool(rng.integers(2)))
     moe.moe_grouped_gemm_mx(u8(ac), u8(asc), u8(bc.reshape(G, N, Kd)), u8(bsc.reshape(G, N, Kd // 32)),
-                            dev(offs), C, epilogue=epi)
+                            dev(offs), C, epilogue=epi, workspace=ws)
     torch.cuda.synchronize()
     _check_mx_gemm(ac, asc, bc, bsc, G, N, Kd, offs, C, epi)
+    if ws is not None:
+        assert torch.count_nonzero(ws[:4096]).item() == 0
 
 
 @pytest.mark.parametrize("seed", range(6))
