@@ -19,7 +19,7 @@ MOE_OK, MOE_INVALID_ARG, MOE_UNSUPPORTED, MOE_HIP_ERROR, MOE_SCRATCH_LIMIT = 0, 
 MOE_F32, MOE_BF16 = 0, 1
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
 MOE_LAYOUT_NK, MOE_LAYOUT_KN = 0, 1
-MOE_EPI_NONE, MOE_EPI_SWIGLU, MOE_EPI_DSWIGLU = 0, 1, 2
+MOE_EPI_NONE, MOE_EPI_SWIGLU, MOE_EPI_DSWIGLU, MOE_EPI_SWIGLU_MX = 0, 1, 2, 3
 MOE_MAX_EXPERTS, MOE_MAX_TOPK, MOE_MAX_GROUPS = 256, 32, 1024
 MOE_ROUTER_ROUTE_NOALLOC_MAX_BYTES = 4 << 20
 
@@ -46,7 +46,7 @@ SIGNATURES = {
                                         _P, _P]),
     "moe_permute_mx": (_I32, [_P, _P, _I64, _I64, _I32, _P, _P, _P, _P]),
     "moe_mx_quantize": (_I32, [_P, _I64, _I64, _I32, _P, _P, _P]),
-    "moe_grouped_gemm_mx": (_I32, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _P, _P, _SZ, _P]),
+    "moe_grouped_gemm_mx": (_I32, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _P, _P, _P, _SZ, _P]),
     "moe_route_backward": (_I32, [_P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _P, _P]),
     "moe_router_backward_workspace_size": (_I32, [_I64, _I64, _I32, _I32, _c.POINTER(_SZ)]),
     "moe_router_logits_backward": (_I32, [_P, _P, _P, _I64, _I64, _I32, _I32, _P, _P, _I32, _P, _SZ, _P]),
@@ -365,8 +365,9 @@ def moe_mx_quantize(x, codes, scales, stream=None) -> None:
 
 
 def moe_grouped_gemm_mx(A, A_scales, B, B_scales, group_offsets, C, epilogue: int = MOE_EPI_NONE,
-                        workspace=None, stream=None) -> None:
-    """Grouped GEMM on MXFP8 operands: A [M, Kd] codes, B [G, N, Kd] codes, bf16 C.
+                        C_scales=None, workspace=None, stream=None) -> None:
+    """Grouped GEMM on MXFP8 operands: A [M, Kd] codes, B [G, N, Kd] codes; bf16 C, or with
+    MOE_EPI_SWIGLU_MX the MXFP8 codes C [M, N/2] and scales C_scales [M, N/64] of H.
     ``workspace``: None or a zero-initialised device buffer of moe_grouped_gemm_workspace_size() bytes."""
     M, Kd = A.shape
     G, N = B.shape[0], B.shape[1]
@@ -377,11 +378,16 @@ def moe_grouped_gemm_mx(A, A_scales, B, B_scales, group_offsets, C, epilogue: in
     _dense("B", B, u8, (G, N, Kd))
     _dense("B_scales", B_scales, u8, (G, N, Kd // 32))
     _dense("group_offsets", group_offsets, _i32(), (G + 1,), flat=True)
-    _dense("C", C, torch.bfloat16, (M, N // 2 if epilogue == MOE_EPI_SWIGLU else N))
+    if epilogue == MOE_EPI_SWIGLU_MX:
+        _dense("C", C, u8, (M, N // 2))
+        _dense("C_scales", C_scales, u8, (M, N // 64))
+    else:
+        _dense("C", C, torch.bfloat16, (M, N // 2 if epilogue == MOE_EPI_SWIGLU else N))
+        C_scales = None
     _dense("workspace", workspace, optional=True)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _call("moe_grouped_gemm_mx", _ptr(A), _ptr(A_scales), _ptr(B), _ptr(B_scales), _ptr(group_offsets), M, N, Kd,
-          G, epilogue, _ptr(C), _ptr(workspace), ws_bytes, _stream(stream))
+          G, epilogue, _ptr(C), _ptr(C_scales), _ptr(workspace), ws_bytes, _stream(stream))
 
 
 def moe_permute_mx(codes, scales, K: int, slot_pos, codes_perm, scales_perm, stream=None) -> None:

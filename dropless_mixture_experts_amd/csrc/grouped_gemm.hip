@@ -38,6 +38,8 @@
 
 #include "common.h"
 #include "internal.h"
+#include "moe.h"
+#include "mx_encode.h"
 
 namespace moe {
 
@@ -53,7 +55,7 @@ constexpr int kGroupM = 8;                 // row tiles that share a column tile
 constexpr int kWindow = 256;               // blocks per XCD-remap window (one round: one per CU)
 constexpr int kSwigluSkipRows = 1536;      // mean group rows below which SwiGLU skips empty fragments
 
-enum { EPI_NONE = 0, EPI_SWIGLU = 1, EPI_DSWIGLU = 2 };
+enum { EPI_NONE = 0, EPI_SWIGLU = 1, EPI_DSWIGLU = 2, EPI_SWIGLU_MX = 3 };  // MX: SwiGLU, MXFP8 out
 enum { LAYOUT_NK = 0, LAYOUT_KN = 1 };
 constexpr int LAYOUT_WG = 2;  // ring pipeline of the weight gradient: both operands K-row
 
@@ -667,6 +669,8 @@ struct GemmParams {
   const int32_t* a_rows = nullptr;
   uint32_t a_div = 1;
   uint32_t a_last = 0;
+  // EPI_SWIGLU_MX: C holds the E4M3 codes of H [M][N/2] and cs its E8M0 scales [M][N/64]
+  uint8_t* cs = nullptr;
 };
 constexpr int kSplitCountBytes = 4096;             // counters: up to 1024 (tile, wave) pairs
 constexpr int kSplitSlotFloats = 256 * 256;        // one fp32 256 x 256 partial tile
@@ -2163,6 +2167,45 @@ __device__ __forceinline__ void dma4(const char* sbase, uint32_t voff, uint32_t 
 __device__ __forceinline__ void wait_none() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory"); }
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// The SwiGLU epilogue with MXFP8 output: h = silu(g) u for the wave's 128 rows x 64 columns at
+// (row0, col0), rounded to bf16 (so the bytes equal quantising the bf16 H afterwards), then
+// quantised in 32-column blocks: fragment j of a row is one block, its 32 values held by lanes
+// l32 (columns 8 q + 0..3) and l32 + 32 (8 q + 4..7).  The block maximum is exchanged between
+// the two lanes; each lane writes its codes as 4-byte words, lane l32 the scale byte.
+// Requires F = N / 2 with F % 32 == 0.
+__device__ __forceinline__ void store_tile_mxq(const GemmParams& p, const f32x16 (&acc)[4][4], int64_t row0,
+                                               int64_t re, int64_t col0) {
+  const int lane = threadIdx.x & 63;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int64_t F = p.N / 2;
+  uint8_t* codes = (uint8_t*)p.C;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t row = row0 + i * 32 + l32;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int64_t col = col0 + 32 * j;  // the block's first column
+      float h[16];
+      float amax = 0.f;
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const float g = acc[i][j][t], u = acc[i][j + 2][t];
+        h[t] = (float)(__bf16)(g * sigmoid_fast(g) * u);
+        amax = fmaxf(amax, fabsf(h[t]));
+      }
+      amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+      const int shared = mx_shared_exponent(amax);
+      if (row >= re || col >= F) continue;
+      uint8_t* dst = codes + row * F + col + 4 * hi;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *(uint32_t*)(dst + 8 * q) = e4m3_pack4(ldexpf(h[4 * q], -shared), ldexpf(h[4 * q + 1], -shared),
+                                               ldexpf(h[4 * q + 2], -shared), ldexpf(h[4 * q + 3], -shared));
+      if (hi == 0) p.cs[row * (F / 32) + col / 32] = (uint8_t)(shared + 127);
+    }
+  }
+}
 }  // namespace mxg
 
 template <int EPI>
@@ -2187,12 +2230,13 @@ void grouped_gemm_mx_kernel(GemmParams p) {
   const int nkt = (int)(p.Kd / kMxRow);
   const int k0 = pc.part >= 0 ? pc.part * nkt / pc.f : 0;
   const int nk = pc.part >= 0 ? (pc.part + 1) * nkt / pc.f - k0 : nkt;
-  const int64_t b0row = EPI == EPI_SWIGLU ? (int64_t)nt * 128 : (int64_t)nt * 256;
+  constexpr bool SW = EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_MX;  // gate|up B rows
+  const int64_t b0row = SW ? (int64_t)nt * 128 : (int64_t)nt * 256;
   const int64_t F = p.N / 2;
   // the tile's B row of local row r (SwiGLU: gate rows, then the matching up rows)
   auto brow = [&](int r) -> int64_t {
     int64_t br;
-    if (EPI == EPI_SWIGLU) {
+    if (SW) {
       int64_t cc = (int64_t)nt * 128 + (r & 127);
       cc = cc < F ? cc : F - 1;
       br = (r < 128 ? 0 : F) + cc;
@@ -2250,7 +2294,7 @@ void grouped_gemm_mx_kernel(GemmParams p) {
   // LDS row of B fragment jj of this wave: plain, 32-column tiles of its 128 columns; SwiGLU,
   // gate fragments (jj = 0, 1) and the matching up fragments (jj = 2, 3) of its 64 columns
   auto bfrag_row = [&](int jj) -> int {
-    return EPI == EPI_SWIGLU ? (jj >> 1) * 128 + wn * 64 + (jj & 1) * 32 + l32 : wn * 128 + jj * 32 + l32;
+    return SW ? (jj >> 1) * 128 + wn * 64 + (jj & 1) * 32 + l32 : wn * 128 + jj * 32 + l32;
   };
   const char* L = (const char*)smem;
   issue(0);
@@ -2310,19 +2354,24 @@ void grouped_gemm_mx_kernel(GemmParams p) {
     if (lane == 0) p.ws_count[r * 4 + wave] = 0;
   }
   // the ring kernel's epilogue: LDS staging (32 KB a wave of the idle slots), bf16 out
-  const int64_t col0 = EPI == EPI_SWIGLU ? (int64_t)nt * 128 + wn * 64 : (int64_t)nt * 256 + wn * 128;
-  ring4::store_tile_lds<EPI>(p, acc, (char*)smem + wave * 32768, m0 + wm * 128, re, col0);
+  const int64_t col0 = SW ? (int64_t)nt * 128 + wn * 64 : (int64_t)nt * 256 + wn * 128;
+  if constexpr (EPI == EPI_SWIGLU_MX)
+    mxg::store_tile_mxq(p, acc, m0 + wm * 128, re, col0);
+  else
+    ring4::store_tile_lds<EPI>(p, acc, (char*)smem + wave * 32768, m0 + wm * 128, re, col0);
 }
 
 hipError_t launch_grouped_gemm_mx(const uint8_t* A, const uint8_t* SA, const uint8_t* B, const uint8_t* SB,
                                   const int32_t* offs, int64_t M, int64_t N, int64_t Kd, int G, int epilogue,
-                                  void* C, void* ws, size_t ws_bytes, hipStream_t s) {
+                                  void* C, uint8_t* CS, void* ws, size_t ws_bytes, hipStream_t s) {
   if (M == 0) return hipSuccess;
   if ((N + 256) * Kd >= ((int64_t)1 << 32)) return hipErrorInvalidValue;  // per-lane DMA offsets
   GemmParams prm{A, B, offs, nullptr, nullptr, C, M, N, Kd, G, 0, nullptr, nullptr, 0, 0, 0};
   prm.sa = SA;
   prm.sb = SB;
-  prm.NT = (epilogue == EPI_SWIGLU) ? (int)((N / 2 + 127) / 128) : (int)((N + kTile - 1) / kTile);
+  prm.cs = CS;
+  const bool sw = epilogue == EPI_SWIGLU || epilogue == EPI_SWIGLU_MX;
+  prm.NT = sw ? (int)((N / 2 + 127) / 128) : (int)((N + kTile - 1) / kTile);
   prm.nk = (int)(Kd / mxg::kMxRow);
   // with a workspace the grid ends in up to P piece blocks of a split tail (as the ring kernel)
   if (ws && ws_bytes >= kSplitCountBytes + kSplitSlotFloats * sizeof(float)) {
@@ -2337,7 +2386,9 @@ hipError_t launch_grouped_gemm_mx(const uint8_t* A, const uint8_t* SA, const uin
   }
   const int64_t max_mt = (M + kTile - 1) / kTile + G;
   const dim3 grid((unsigned)(max_mt * prm.NT + prm.P));
-  if (epilogue == EPI_SWIGLU)
+  if (epilogue == EPI_SWIGLU_MX)
+    hipLaunchKernelGGL((grouped_gemm_mx_kernel<EPI_SWIGLU_MX>), grid, dim3(ring4::kThreads), 0, s, prm);
+  else if (epilogue == EPI_SWIGLU)
     hipLaunchKernelGGL((grouped_gemm_mx_kernel<EPI_SWIGLU>), grid, dim3(ring4::kThreads), 0, s, prm);
   else
     hipLaunchKernelGGL((grouped_gemm_mx_kernel<EPI_NONE>), grid, dim3(ring4::kThreads), 0, s, prm);
@@ -2428,6 +2479,9 @@ hipError_t launch_grouped_gemm(const void* A, const void* B, int b_layout, const
 
 static_assert(ring4::kStageBytes == kGatherStageBytes && EPI_NONE == 0 && EPI_SWIGLU == 1,
               "the gathered form's shape test assumes the ring kernel's stage and epilogue codes");
+static_assert(EPI_NONE == MOE_EPI_NONE && EPI_SWIGLU == MOE_EPI_SWIGLU && EPI_DSWIGLU == MOE_EPI_DSWIGLU &&
+                  EPI_SWIGLU_MX == MOE_EPI_SWIGLU_MX,
+              "the ABI's epilogue codes reach the launchers unchanged");
 
 hipError_t launch_grouped_gemm_gather(const void* X, int64_t T, const int32_t* a_rows, int a_div, const void* B,
                                       const int32_t* offs, int64_t M, int64_t N, int64_t Kd, int G, int epilogue,

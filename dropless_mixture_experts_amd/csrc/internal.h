@@ -89,6 +89,6 @@ hipError_t launch_permute_rows(const void* x, int64_t T, int64_t row_bytes, int 
 hipError_t launch_mx_quantize(const void* x, int64_t R, int64_t K, uint8_t* codes, uint8_t* scales, hipStream_t s);
 hipError_t launch_grouped_gemm_mx(const uint8_t* A, const uint8_t* SA, const uint8_t* B, const uint8_t* SB,
                                   const int32_t* offs, int64_t M, int64_t N, int64_t Kd, int G, int epilogue,
-                                  void* C, void* ws, size_t ws_bytes, hipStream_t s);
+                                  void* C, uint8_t* CS, void* ws, size_t ws_bytes, hipStream_t s);
 
 }  // namespace moe

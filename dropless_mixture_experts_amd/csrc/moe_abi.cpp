@@ -257,21 +257,24 @@ int32_t moe_mx_quantize(const void* x, int64_t R, int64_t K, int32_t dtype, uint
 
 int32_t moe_grouped_gemm_mx(const uint8_t* A, const uint8_t* A_scales, const uint8_t* B, const uint8_t* B_scales,
                             const int32_t* group_offsets, int64_t M, int64_t N, int64_t Kd, int32_t G,
-                            int32_t epilogue, void* C, void* workspace, size_t workspace_bytes,
+                            int32_t epilogue, void* C, uint8_t* C_scales, void* workspace, size_t workspace_bytes,
                             moe_stream_t stream) {
   if (M < 0 || M >= ((int64_t)1 << 31) || N < 8 || N % 8 != 0 || Kd < 128 || Kd % 128 != 0) return MOE_INVALID_ARG;
   if (G < 1 || G > kMaxGroups) return MOE_INVALID_ARG;
-  if (epilogue != MOE_EPI_NONE && epilogue != MOE_EPI_SWIGLU) return MOE_UNSUPPORTED;
+  if (epilogue != MOE_EPI_NONE && epilogue != MOE_EPI_SWIGLU && epilogue != MOE_EPI_SWIGLU_MX) return MOE_UNSUPPORTED;
   if (epilogue == MOE_EPI_SWIGLU && N % 16 != 0) return MOE_INVALID_ARG;
+  if (epilogue == MOE_EPI_SWIGLU_MX && N % 64 != 0) return MOE_INVALID_ARG;  // whole 32-value blocks of H
   if ((N + 256) * Kd >= ((int64_t)1 << 32)) return MOE_INVALID_ARG;
   if (!group_offsets) return MOE_INVALID_ARG;
   if (M == 0) return MOE_OK;
   if (!A || !A_scales || !B || !B_scales || !C) return MOE_INVALID_ARG;
+  if (epilogue == MOE_EPI_SWIGLU_MX && !C_scales) return MOE_INVALID_ARG;
   if (!aligned16(A) || !aligned16(B) || !aligned4(A_scales) || !aligned4(B_scales) || !aligned16(C) ||
       !aligned4(group_offsets) || (workspace && !aligned16(workspace)))
     return MOE_INVALID_ARG;
   return from_hip(moe::launch_grouped_gemm_mx(A, A_scales, B, B_scales, group_offsets, M, N, Kd, G, epilogue, C,
-                                              workspace, workspace ? workspace_bytes : 0, (hipStream_t)stream));
+                                              epilogue == MOE_EPI_SWIGLU_MX ? C_scales : nullptr, workspace,
+                                              workspace ? workspace_bytes : 0, (hipStream_t)stream));
 }
 
 int32_t moe_permute_mx(const uint8_t* codes, const uint8_t* scales, int64_t T, int64_t d, int32_t K,

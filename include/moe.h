@@ -54,9 +54,9 @@ enum moe_status { MOE_OK = 0, MOE_INVALID_ARG = 1, MOE_UNSUPPORTED = 2, MOE_HIP_
 enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 };
 enum moe_score { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 };
 enum moe_layout { MOE_LAYOUT_NK = 0, MOE_LAYOUT_KN = 1 };
-enum moe_epilogue { MOE_EPI_NONE = 0, MOE_EPI_SWIGLU = 1, MOE_EPI_DSWIGLU = 2 };
+enum moe_epilogue { MOE_EPI_NONE = 0, MOE_EPI_SWIGLU = 1, MOE_EPI_DSWIGLU = 2, MOE_EPI_SWIGLU_MX = 3 };
 
-#define MOE_ABI_VERSION 9
+#define MOE_ABI_VERSION 10
 #define MOE_MAX_EXPERTS 256
 #define MOE_MAX_TOPK 32
 #define MOE_MAX_GROUPS 1024
@@ -335,6 +335,10 @@ int32_t moe_mx_quantize(const void* x, int64_t R, int64_t K, int32_t dtype, uint
  * N-by-K weights): group g owns rows [group_offsets[g], group_offsets[g+1]);
  *   P = A_g . B_g^T on the values the codes and scales represent, fp32 accumulation
  *   epilogue NONE: C [M, N] = P;  SWIGLU: N = 2F, C [M, F] = silu(P[:, :F]) * P[:, F:];  bf16 out
+ *   epilogue SWIGLU_MX: H = silu(P[:, :F]) * P[:, F:] rounded to bf16, written as MXFP8 (the
+ *     operand of the down GEMM, TE-MoE "Optimisation 1": grouped quantisation): C [M, F]
+ *     uint8 codes and C_scales [M, F / 32] uint8, byte for byte what moe_mx_quantize writes for
+ *     the bf16 H of the SWIGLU epilogue; needs N % 64 == 0 and C_scales (NULL otherwise: unused)
  *   A DEVICE [M, Kd] codes, A_scales DEVICE [M, Kd / 32];  B DEVICE [G, N, Kd] codes,
  *   B_scales DEVICE [G, N, Kd / 32] (as written by moe_mx_quantize)
  *   workspace DEVICE, NULL or workspace_bytes (moe_grouped_gemm_workspace_size) bytes, 16-byte
@@ -349,8 +353,8 @@ int32_t moe_mx_quantize(const void* x, int64_t R, int64_t K, int32_t dtype, uint
  */
 int32_t moe_grouped_gemm_mx(const uint8_t* A, const uint8_t* A_scales, const uint8_t* B, const uint8_t* B_scales,
                             const int32_t* group_offsets, int64_t M, int64_t N, int64_t Kd, int32_t G,
-                            int32_t epilogue, void* C, void* workspace, size_t workspace_bytes,
-                            moe_stream_t stream);
+                            int32_t epilogue, void* C, uint8_t* C_scales, void* workspace,
+                            size_t workspace_bytes, moe_stream_t stream);
 
 /*
  * Permute of MXFP8 rows (S4 on quantised tokens): codes_perm[slot_pos[s]] = codes[s / K] and

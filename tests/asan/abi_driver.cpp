@@ -200,13 +200,17 @@ int main() {
   EXPECT(moe_mx_quantize(P, 10, 64, MOE_BF16, PU, PU, nullptr), MOE_OK, true);
   EXPECT(moe_mx_quantize(P, 10, 48, MOE_BF16, PU, PU, nullptr), MOE_INVALID_ARG, false);
   EXPECT(moe_mx_quantize(P, 10, 64, MOE_F32, PU, PU, nullptr), MOE_UNSUPPORTED, false);
-  EXPECT(moe_grouped_gemm_mx(PU, PU, PU, PU, PI, 512, 256, 256, 4, MOE_EPI_SWIGLU, P, nullptr, 0, nullptr), MOE_OK,
-         true);
-  EXPECT(moe_grouped_gemm_mx(PU, PU, PU, PU, PI, 512, 256, 256, 4, MOE_EPI_NONE, P, P, 1 << 20, nullptr), MOE_OK,
-         true);
-  EXPECT(moe_grouped_gemm_mx(PU, PU, PU, PU, PI, 512, 256, 192, 4, MOE_EPI_NONE, P, nullptr, 0, nullptr),
+  EXPECT(moe_grouped_gemm_mx(PU, PU, PU, PU, PI, 512, 256, 256, 4, MOE_EPI_SWIGLU, P, nullptr, nullptr, 0, nullptr),
+         MOE_OK, true);
+  EXPECT(moe_grouped_gemm_mx(PU, PU, PU, PU, PI, 512, 256, 256, 4, MOE_EPI_NONE, P, nullptr, P, 1 << 20, nullptr),
+         MOE_OK, true);
+  EXPECT(moe_grouped_gemm_mx(PU, PU, PU, PU, PI, 512, 256, 256, 4, MOE_EPI_SWIGLU_MX, P, PU, nullptr, 0, nullptr),
+         MOE_OK, true);
+  EXPECT(moe_grouped_gemm_mx(PU, PU, PU, PU, PI, 512, 256, 256, 4, MOE_EPI_SWIGLU_MX, P, nullptr, nullptr, 0, nullptr),
          MOE_INVALID_ARG, false);
-  EXPECT(moe_grouped_gemm_mx(PU, PU, PU, PU, PI, 512, 256, 256, 4, MOE_EPI_DSWIGLU, P, nullptr, 0, nullptr),
+  EXPECT(moe_grouped_gemm_mx(PU, PU, PU, PU, PI, 512, 256, 192, 4, MOE_EPI_NONE, P, nullptr, nullptr, 0, nullptr),
+         MOE_INVALID_ARG, false);
+  EXPECT(moe_grouped_gemm_mx(PU, PU, PU, PU, PI, 512, 256, 256, 4, MOE_EPI_DSWIGLU, P, nullptr, nullptr, 0, nullptr),
          MOE_UNSUPPORTED, false);
   EXPECT(moe_permute_mx(PU, PU, 10, 512, 2, PI, PU, PU, nullptr), MOE_OK, true);
   EXPECT(moe_permute_mx(PU, PU, 10, 256, 2, PI, PU, PU, nullptr), MOE_INVALID_ARG, false);

@@ -79,7 +79,7 @@ hipError_t launch_permute_rows(const void*, int64_t, int64_t, int, const int32_t
 }
 hipError_t launch_mx_quantize(const void*, int64_t, int64_t, uint8_t*, uint8_t*, hipStream_t) { return hit(); }
 hipError_t launch_grouped_gemm_mx(const uint8_t*, const uint8_t*, const uint8_t*, const uint8_t*, const int32_t*,
-                                  int64_t, int64_t, int64_t, int, int, void*, void*, size_t, hipStream_t) {
+                                  int64_t, int64_t, int64_t, int, int, void*, uint8_t*, void*, size_t, hipStream_t) {
   return hit();
 }
 }  // namespace moe

@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert moe.moe_abi_version() == 9
+    assert moe.moe_abi_version() == 10
     assert moe.status_str(0) == "ok"
     assert "invalid" in moe.status_str(1)
     assert "static scratch" in moe.status_str(moe.MOE_SCRATCH_LIMIT)
@@ -220,7 +220,7 @@ def test_mx_rejects_bad_arguments(lib):
     assert lib.moe_mx_quantize(None, 0, 64, 1, None, None, None) == 0  # empty: no launch
 
     def gm(M=64, N=64, Kd=256, G=2, epi=0, A=P, SA=P):
-        return lib.moe_grouped_gemm_mx(A, SA, P, P, P, M, N, Kd, G, epi, P, None, 0, None)
+        return lib.moe_grouped_gemm_mx(A, SA, P, P, P, M, N, Kd, G, epi, P, P, None, 0, None)
     assert gm(Kd=192) == 1                 # Kd % 128
     assert gm(epi=2) == 2                  # no SwiGLU-backward epilogue
     assert gm(epi=1, N=24) == 1            # gate|up halves of 8
@@ -228,7 +228,10 @@ def test_mx_rejects_bad_arguments(lib):
     assert gm(A=P + 4) == 1
     assert gm(SA=P + 2) == 1
     assert gm(N=1 << 20, Kd=1 << 13) == 1  # per-lane offsets past 32 bits
-    assert lib.moe_grouped_gemm_mx(P, P, P, P, P, 64, 64, 256, 2, 0, P, P + 8, 1 << 30, None) == 1  # workspace alignment
+    assert lib.moe_grouped_gemm_mx(P, P, P, P, P, 64, 64, 256, 2, 0, P, None, P + 8, 1 << 30, None) == 1  # workspace alignment
+    assert gm(epi=3, N=96) == 1            # MXFP8 H: whole 32-value blocks of F = N / 2
+    assert lib.moe_grouped_gemm_mx(P, P, P, P, P, 64, 128, 256, 2, 3, P, None, None, 0, None) == 1  # no C_scales
+    assert gm(epi=4) == 2
     assert gm(M=0) == 0
     assert lib.moe_permute_mx(P, P, 10, 256, 2, P, P, P, None) == 1        # d % 512
     assert lib.moe_permute_mx(P, P + 4, 10, 512, 2, P, P, P, None) == 1    # misaligned scales

@@ -361,6 +361,36 @@ def test_grouped_gemm_mx_parity(counts, N, Kd, epi, use_ws):
         assert torch.count_nonzero(ws[:4096]).item() == 0
 
 
+@pytest.mark.parametrize("counts,N,Kd,use_ws", [
+    ([130, 0, 70, 256], 512, 384, False),  # ragged groups, an empty one
+    ([300, 41], 320, 256, True),           # F = 160: a partial column tile (one block of it past F)
+    ([1, 2, 3], 64, 128, False),           # tiny groups, one block a row
+])
+def test_grouped_gemm_mx_swiglu_quantised_equals_two_step(counts, N, Kd, use_ws):
+    """The SwiGLU epilogue that writes H as MXFP8 (codes and E8M0 scales) gives the bytes that the
+    bf16 SwiGLU epilogue followed by moe_mx_quantize gives, on the same workspace."""
+    rng = np.random.default_rng(sum(counts) + N + Kd)
+    G, M = len(counts), sum(counts)
+    F = N // 2
+    offs = dev(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32))
+    ac, asc = _mx_operands(rng, M, Kd)
+    bc, bsc = _mx_operands(rng, G * N, Kd)
+    ops = (_u8(ac), _u8(asc), _u8(bc.reshape(G, N, Kd)), _u8(bsc.reshape(G, N, Kd // 32)), offs)
+    ws = torch.zeros((moe.moe_grouped_gemm_workspace_size(),), dtype=torch.uint8, device="cuda") if use_ws else None
+    H = torch.full((M, F), float("nan"), dtype=torch.bfloat16, device="cuda")
+    moe.moe_grouped_gemm_mx(*ops, H, epilogue=moe.MOE_EPI_SWIGLU, workspace=ws)
+    hc = torch.zeros((M, F), dtype=torch.uint8, device="cuda")
+    hs = torch.zeros((M, F // 32), dtype=torch.uint8, device="cuda")
+    moe.moe_mx_quantize(H, hc, hs)
+    qc = torch.full((M, F), 0xFF, dtype=torch.uint8, device="cuda")
+    qs = torch.full((M, F // 32), 0xFF, dtype=torch.uint8, device="cuda")
+    moe.moe_grouped_gemm_mx(*ops, qc, epilogue=moe.MOE_EPI_SWIGLU_MX, C_scales=qs, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(qc, hc) and torch.equal(qs, hs)
+    if use_ws:
+        assert torch.count_nonzero(ws[:4096]).item() == 0
+
+
 def test_grouped_gemm_mx_split_tail():
     """More output tiles than CUs, so full rounds and then a split tail, twice in a row on one
     workspace: both calls write the same bits, the counters return to zero, and 48 sampled rows

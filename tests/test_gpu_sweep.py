@@ -271,6 +271,16 @@ def test_sweep_grouped_gemm_mx(seed):
     _check_mx_gemm(ac, asc, bc, bsc, G, N, Kd, offs, C, epi)
     if ws is not None:
         assert torch.count_nonzero(ws[:4096]).item() == 0
+    if epi == 1 and N % 64 == 0:
+        # H written as MXFP8 by the epilogue: the bytes of quantising the bf16 H above
+        F = N // 2
+        hc, hs = torch.empty((M, F), dtype=torch.uint8, device="cuda"), torch.empty((M, F // 32), dtype=torch.uint8, device="cuda")
+        moe.moe_mx_quantize(C, hc, hs)
+        qc, qs = torch.empty_like(hc), torch.empty_like(hs)
+        moe.moe_grouped_gemm_mx(u8(ac), u8(asc), u8(bc.reshape(G, N, Kd)), u8(bsc.reshape(G, N, Kd // 32)),
+                                dev(offs), qc, epilogue=moe.MOE_EPI_SWIGLU_MX, C_scales=qs, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(qc, hc) and torch.equal(qs, hs)
 
 
 @pytest.mark.parametrize("seed", range(6))
