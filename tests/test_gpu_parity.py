@@ -1223,6 +1223,69 @@ def test_layer_is_deterministic():
     assert np.array_equal(host(b1.row_src), host(b2.row_src))
 
 
+def test_mx_forward_graph_replays_equal_eager():
+    """The MXFP8 forward (fused router, token quantisation, MX permute, the gate/up GEMM writing H
+    as MXFP8, the down GEMM, combine; both GEMMs on one split-tail workspace) captured once as a
+    graph: every replay with new tokens equals the eager run of the same calls bit for bit, with
+    the program's own eager work and synchronisations between the replays, and leaves the
+    workspace counters at zero."""
+    T, d, E, K, F = 600, 512, 8, 2, 384
+    M = T * K
+    rng = np.random.default_rng(77)
+    u8 = dict(dtype=torch.uint8, device="cuda")
+    wr = dev(mi.f32_to_bf16_bits((rng.standard_normal((E, d)) * 0.05).astype(np.float32)))
+    w13 = dev(mi.f32_to_bf16_bits((rng.standard_normal((E, 2 * F, d)) / math.sqrt(d)).astype(np.float32)))
+    w2 = dev(mi.f32_to_bf16_bits((rng.standard_normal((E, d, F)) / math.sqrt(F)).astype(np.float32)))
+    w13c, w13s = torch.empty(E, 2 * F, d, **u8), torch.empty(E, 2 * F, d // 32, **u8)
+    w2c, w2s = torch.empty(E, d, F, **u8), torch.empty(E, d, F // 32, **u8)
+    moe.moe_mx_quantize(w13.view(E * 2 * F, d), w13c.view(E * 2 * F, d), w13s.view(E * 2 * F, d // 32))
+    moe.moe_mx_quantize(w2.view(E * d, F), w2c.view(E * d, F), w2s.view(E * d, F // 32))
+    b = moe.MoEBuffers(T, d, E, K, F, torch.bfloat16)
+    rr = torch.empty((max(moe.moe_router_route_workspace_size(T, E), 256),), **u8)
+    tq, ts = torch.empty(T, d, **u8), torch.empty(T, d // 32, **u8)
+    xq, xs = torch.empty(M, d, **u8), torch.empty(M, d // 32, **u8)
+    hq, hs = torch.empty(M, F, **u8), torch.empty(M, F // 32, **u8)
+    x = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
+
+    def forward():
+        moe.moe_router_route(x, wr, None, K, 0, True, None, b.topk_idx, b.gates, b.counts, b.offsets, b.slot_pos,
+                             b.row_src, rr)
+        moe.moe_mx_quantize(x, tq, ts)
+        moe.moe_permute_mx(tq, ts, K, b.slot_pos, xq, xs)
+        moe.moe_grouped_gemm_mx(xq, xs, w13c, w13s, b.offsets, hq, moe.MOE_EPI_SWIGLU_MX, C_scales=hs,
+                                workspace=b.gemm_ws)
+        moe.moe_grouped_gemm_mx(hq, hs, w2c, w2s, b.offsets, b.y_perm, moe.MOE_EPI_NONE, workspace=b.gemm_ws)
+        moe.moe_unpermute_combine(b.y_perm, b.slot_pos, b.gates, T, K, b.y)
+
+    def new_x(rep):
+        r = np.random.default_rng(200 + rep)
+        return dev(mi.f32_to_bf16_bits((r.standard_normal((T, d)) * (1 + rep)).astype(np.float32)))
+
+    x.copy_(new_x(0))
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        forward()
+    torch.cuda.current_stream().wait_stream(st)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        forward()
+    seen = set()
+    for rep in range(3):
+        x.copy_(new_x(rep + 1))
+        g.replay()
+        torch.cuda.synchronize()
+        y_graph, h_graph = b.y.clone(), hq.clone()
+        seen.add(tuple(host(b.counts).tolist()))
+        forward()                                   # eager, between replays
+        torch.cuda.synchronize()
+        assert torch.equal(b.y, y_graph) and torch.equal(hq, h_graph)
+        assert not torch.isnan(y_graph).any().item()
+        assert torch.count_nonzero(b.gemm_ws[:4096]).item() == 0
+    assert len(seen) == 3, "replays should see different expert loads"
+
+
 def test_graph_capture_replays_with_new_routing():
     """The whole forward is captured once; replays with new inputs (new counts) need no
     re-capture and no host-side counts, and equal the eager result bit for bit."""
