@@ -2173,6 +2173,7 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 // quantised in 32-column blocks: fragment j of a row is one block, its 32 values held by lanes
 // l32 (columns 8 q + 0..3) and l32 + 32 (8 q + 4..7).  The block maximum is exchanged between
 // the two lanes; each lane writes its codes as 4-byte words, lane l32 the scale byte.
+// Rows: fragment i is rows row0 + 64 i .. + 31 (a wave row's interleaved fragments).
 // Requires F = N / 2 with F % 32 == 0.
 __device__ __forceinline__ void store_tile_mxq(const GemmParams& p, const f32x16 (&acc)[4][4], int64_t row0,
                                                int64_t re, int64_t col0) {
@@ -2182,7 +2183,7 @@ __device__ __forceinline__ void store_tile_mxq(const GemmParams& p, const f32x16
   uint8_t* codes = (uint8_t*)p.C;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int64_t row = row0 + i * 32 + l32;
+    const int64_t row = row0 + i * 64 + l32;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int64_t col = col0 + 32 * j;  // the block's first column
@@ -2297,6 +2298,13 @@ void grouped_gemm_mx_kernel(GemmParams p) {
     return SW ? (jj >> 1) * 128 + wn * 64 + (jj & 1) * 32 + l32 : wn * 128 + jj * 32 + l32;
   };
   const char* L = (const char*)smem;
+  // Wave row wm takes the tile's 32-row fragments wm, wm + 2, wm + 4, wm + 6, so a partly filled
+  // tile leaves both wave rows the same number NF of live fragments; each wave runs the loop
+  // compiled for its NF, the reads and MFMAs of dead fragments left out (the DMAs and barriers,
+  // which every wave shares, kept).
+  auto arow_frag = [&](int i) -> int { return wm * 32 + i * 64 + l32; };
+  auto mainloop = [&](auto nfc) {
+  constexpr int NF = decltype(nfc)::value;
   issue(0);
   for (int st = 0; st < nk; ++st) {
     wait_none();    // stage st has landed for this wave
@@ -2306,7 +2314,7 @@ void grouped_gemm_mx_kernel(GemmParams p) {
     uint32_t wsa[4], wsb[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      wsa[i] = *(const uint32_t*)(slot + kScaleOff + (wm * 128 + i * 32 + l32) * 4);
+      if (i < NF) wsa[i] = *(const uint32_t*)(slot + kScaleOff + arow_frag(i) * 4);
       wsb[i] = *(const uint32_t*)(slot + kScaleOff + 1024 + bfrag_row(i) * 4);
     }
 #pragma unroll
@@ -2318,23 +2326,38 @@ void grouped_gemm_mx_kernel(GemmParams p) {
       i32x8 a[4], b[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int ra = wm * 128 + i * 32 + l32, rb = bfrag_row(i);
-        const uint4 a0 = *(const uint4*)(slot + ra * kMxRow + ((c0 ^ ring4::swz(ra)) << 4));
-        const uint4 a1 = *(const uint4*)(slot + ra * kMxRow + ((c1 ^ ring4::swz(ra)) << 4));
+        const int rb = bfrag_row(i);
+        if (i < NF) {
+          const int ra = arow_frag(i);
+          const uint4 a0 = *(const uint4*)(slot + ra * kMxRow + ((c0 ^ ring4::swz(ra)) << 4));
+          const uint4 a1 = *(const uint4*)(slot + ra * kMxRow + ((c1 ^ ring4::swz(ra)) << 4));
+          a[i] = i32x8{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+        }
         const uint4 b0 = *(const uint4*)(slot + kOpBytes + rb * kMxRow + ((c0 ^ ring4::swz(rb)) << 4));
         const uint4 b1 = *(const uint4*)(slot + kOpBytes + rb * kMxRow + ((c1 ^ ring4::swz(rb)) << 4));
-        a[i] = i32x8{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
         b[i] = i32x8{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
       }
       const int sh = 8 * (2 * j + hi);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < NF; ++i)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj)
           // B first, as mma_rows: each lane ends with one A row and 4 consecutive columns a register
           // group, the layout the epilogues store
           acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
               b[jj], a[i], acc[i][jj], 0, 0, 0, (int)((wsb[jj] >> sh) & 0xffu), 0, (int)((wsa[i] >> sh) & 0xffu));
+    }
+  }
+  };
+  {
+    const int64_t live = re - m0 - 32 * wm;
+    const int nf = live <= 0 ? 0 : live >= 256 ? 4 : (int)((live + 63) / 64);
+    switch (__builtin_amdgcn_readfirstlane(nf)) {
+      case 4: mainloop(std::integral_constant<int, 4>{}); break;
+      case 3: mainloop(std::integral_constant<int, 3>{}); break;
+      case 2: mainloop(std::integral_constant<int, 2>{}); break;
+      case 1: mainloop(std::integral_constant<int, 1>{}); break;
+      default: mainloop(std::integral_constant<int, 0>{}); break;
     }
   }
   __syncthreads();  // every wave is done with the slots: they hold the epilogue staging now
@@ -2355,10 +2378,11 @@ void grouped_gemm_mx_kernel(GemmParams p) {
   }
   // the ring kernel's epilogue: LDS staging (32 KB a wave of the idle slots), bf16 out
   const int64_t col0 = SW ? (int64_t)nt * 128 + wn * 64 : (int64_t)nt * 256 + wn * 128;
+  // (fragment i of wave row wm: rows m0 + 32 wm + 64 i ..)
   if constexpr (EPI == EPI_SWIGLU_MX)
-    mxg::store_tile_mxq(p, acc, m0 + wm * 128, re, col0);
+    mxg::store_tile_mxq(p, acc, m0 + wm * 32, re, col0);
   else
-    ring4::store_tile_lds<EPI>(p, acc, (char*)smem + wave * 32768, m0 + wm * 128, re, col0);
+    ring4::store_tile_lds<EPI, true>(p, acc, (char*)smem + wave * 32768, m0 + wm * 32, re, col0);
 }
 
 hipError_t launch_grouped_gemm_mx(const uint8_t* A, const uint8_t* SA, const uint8_t* B, const uint8_t* SB,
