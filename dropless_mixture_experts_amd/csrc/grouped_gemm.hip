@@ -2168,25 +2168,31 @@ __device__ __forceinline__ void wait_none() { asm volatile("s_waitcnt vmcnt(0) l
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
-// The SwiGLU epilogue with MXFP8 output: h = silu(g) u for the wave's 128 rows x 64 columns at
-// (row0, col0), rounded to bf16 (so the bytes equal quantising the bf16 H afterwards), then
-// quantised in 32-column blocks: fragment j of a row is one block, its 32 values held by lanes
-// l32 (columns 8 q + 0..3) and l32 + 32 (8 q + 4..7).  The block maximum is exchanged between
-// the two lanes; each lane writes its codes as 4-byte words, lane l32 the scale byte.
-// Rows: fragment i is rows row0 + 64 i .. + 31 (a wave row's interleaved fragments).
+// The SwiGLU epilogue with MXFP8 output: h = silu(g) u for the wave's 128 rows x 64 columns,
+// fragment i at rows row0 + 64 i .. + 31 (a wave row's interleaved fragments), columns col0 ..,
+// rounded to bf16 (so the bytes equal quantising the bf16 H afterwards), then quantised in
+// 32-column blocks: fragment j of a row is one block, its 32 values held by lanes l32 (columns
+// 8 q + 0..3) and l32 + 32 (8 q + 4..7), which exchange their maxima.  The codes go through the
+// wave's LDS (wl: 64 bytes a row, two rows to a 128-byte line, 16-byte pieces XOR-swizzled by
+// the line) and leave as whole 16-byte pieces; lane l32 writes the row's two scale bytes.
+// A piece holds columns 16 p .. 16 p + 15 as the words (q even, hi 0), (q odd, hi 0), (q even,
+// hi 1), (q odd, hi 1); the flush puts the words back in column order.
 // Requires F = N / 2 with F % 32 == 0.
-__device__ __forceinline__ void store_tile_mxq(const GemmParams& p, const f32x16 (&acc)[4][4], int64_t row0,
-                                               int64_t re, int64_t col0) {
+__device__ __forceinline__ uint32_t mxq_lds_off(int lr, int piece) {
+  return (uint32_t)((lr >> 1) * 128 + ((((lr & 1) << 2) | piece) ^ ((lr >> 1) & 7)) * 16);
+}
+__device__ __forceinline__ void store_tile_mxq(const GemmParams& p, const f32x16 (&acc)[4][4], char* wl,
+                                               int64_t row0, int64_t re, int64_t col0) {
   const int lane = threadIdx.x & 63;
   const int l32 = lane & 31, hi = lane >> 5;
   const int64_t F = p.N / 2;
-  uint8_t* codes = (uint8_t*)p.C;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
+    const int lr = i * 32 + l32;  // local row
     const int64_t row = row0 + i * 64 + l32;
+    uint32_t sc = 0;  // the row's two scale bytes (blocks j = 0, 1)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int64_t col = col0 + 32 * j;  // the block's first column
       float h[16];
       float amax = 0.f;
 #pragma unroll
@@ -2197,14 +2203,28 @@ __device__ __forceinline__ void store_tile_mxq(const GemmParams& p, const f32x16
       }
       amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
       const int shared = mx_shared_exponent(amax);
-      if (row >= re || col >= F) continue;
-      uint8_t* dst = codes + row * F + col + 4 * hi;
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        *(uint32_t*)(dst + 8 * q) = e4m3_pack4(ldexpf(h[4 * q], -shared), ldexpf(h[4 * q + 1], -shared),
-                                               ldexpf(h[4 * q + 2], -shared), ldexpf(h[4 * q + 3], -shared));
-      if (hi == 0) p.cs[row * (F / 32) + col / 32] = (uint8_t)(shared + 127);
+        *(uint32_t*)(wl + mxq_lds_off(lr, 2 * j + (q >> 1)) + 8 * hi + 4 * (q & 1)) =
+            e4m3_pack4(ldexpf(h[4 * q], -shared), ldexpf(h[4 * q + 1], -shared), ldexpf(h[4 * q + 2], -shared),
+                       ldexpf(h[4 * q + 3], -shared));
+      sc |= (uint32_t)(shared + 127) << (8 * j);
     }
+    if (hi == 0 && row < re && col0 < F) {
+      p.cs[row * (F / 32) + col0 / 32] = (uint8_t)sc;
+      if (col0 + 32 < F) p.cs[row * (F / 32) + col0 / 32 + 1] = (uint8_t)(sc >> 8);
+    }
+  }
+  // each lane reads and stores one 16-byte piece: 4 pieces a row, 16 rows an instruction
+  const int c = lane & 3, rr = lane >> 2;
+  const int64_t col = col0 + c * 16;
+  uint8_t* codes = (uint8_t*)p.C;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int lr = k * 16 + rr;
+    const uint4 v = *(const uint4*)(wl + mxq_lds_off(lr, c));
+    const int64_t row = row0 + ((lr >> 5) << 6) + (lr & 31);
+    if (row < re && col < F) st_nt((uint4*)(codes + row * F + col), make_uint4(v.x, v.z, v.y, v.w));
   }
 }
 }  // namespace mxg
@@ -2380,7 +2400,7 @@ void grouped_gemm_mx_kernel(GemmParams p) {
   const int64_t col0 = SW ? (int64_t)nt * 128 + wn * 64 : (int64_t)nt * 256 + wn * 128;
   // (fragment i of wave row wm: rows m0 + 32 wm + 64 i ..)
   if constexpr (EPI == EPI_SWIGLU_MX)
-    mxg::store_tile_mxq(p, acc, m0 + wm * 32, re, col0);
+    mxg::store_tile_mxq(p, acc, (char*)smem + wave * 32768, m0 + wm * 32, re, col0);
   else
     ring4::store_tile_lds<EPI, true>(p, acc, (char*)smem + wave * 32768, m0 + wm * 32, re, col0);
 }
