@@ -1428,11 +1428,16 @@ __device__ __forceinline__ void mainloop(PP& P, int nk) {
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) asm volatile("" : "+a"(P.acc[i][j]));
+  // The weight gradient's last stage may be partly filled: a wave whose DMA of it covers no row
+  // before the reduction's end writes zeros with LDS stores and issues no DMA at all, so a wait
+  // that counts DMAs still outstanding must not count on that stage's.  There it waits for all.
+  constexpr bool WG = PP::kBL == LAYOUT_WG;
   if (nk > 2) {
     P.template issue<0, true, 4>(2, 0);
     P.template issue<0, true, 4>(2, 1);
-    wait_vm18();
-  } else if (nk > 1) {
+    if (WG && nk == 3) wait_all_0();
+    else wait_vm18();
+  } else if (nk > 1 && !WG) {
     wait_vm16();
   } else {
     wait_all_0();
@@ -1449,7 +1454,8 @@ __device__ __forceinline__ void mainloop(PP& P, int nk) {
   }
   for (; s + 3 < nk; ++s, P.rotate()) stage<PP, 2, true, 8>(P, s, f);
   if (s + 2 < nk) {
-    stage<PP, 1, true, 8>(P, s++, f);
+    // its mid-stage wait would count the DMAs of stage s + 2, the last one
+    stage<PP, 1, true, WG ? 0 : 8>(P, s++, f);
     P.rotate();
   }
   if (s + 1 < nk) {

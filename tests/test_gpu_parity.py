@@ -1104,6 +1104,38 @@ def test_wgrad_multi_tile(accumulate):
             assert rel_err(got[g], ref[g]) < TOL_BF16 / 4, g
 
 
+@pytest.mark.parametrize("accumulate", [False, True])
+def test_wgrad_partial_last_stage_repeatable(accumulate):
+    """Regression: reductions whose last 64-row stage is partly filled, at two and three stages
+    (where the ring's first waits and its third-to-last stage's wait cover that stage) and longer.
+    Waves whose DMA of the last stage covers no row write zeros and issue no DMA, so a wait that
+    counted DMAs outstanding could pass before an earlier stage had landed. Eight calls must
+    agree bit for bit and match the oracle."""
+    rng = np.random.default_rng(29)
+    counts = np.array([65, 80, 100, 112, 129, 140, 176, 200, 300, 1, 33, 64, 128, 192, 257, 0])
+    off = np.concatenate([[0], np.cumsum(counts)])
+    M, N, Kd = int(off[-1]), 512, 520
+    X = mi.f32_to_bf16_bits(rng.standard_normal((M, Kd)).astype(np.float32))
+    dY = mi.f32_to_bf16_bits(rng.standard_normal((M, N)).astype(np.float32))
+    init = rng.standard_normal((len(counts), N, Kd)).astype(np.float32)
+    dX, ddY, doff = dev(X), dev(dY), dev(off)
+    outs = []
+    for _ in range(8):
+        dW = dev(init) if accumulate else empty_like_poisoned((len(counts), N, Kd), torch.float32)
+        moe.moe_grouped_gemm_wgrad(dX, ddY, doff, dW, accumulate=accumulate)
+        torch.cuda.synchronize()
+        outs.append(dW)
+    for o in outs[1:]:
+        assert torch.equal(outs[0], o)
+    got = f64(outs[0])
+    ref = orc.grouped_wgrad(X, dY, off) + (init.astype(np.float64) if accumulate else 0.0)
+    for g in range(len(counts)):
+        if counts[g] == 0:
+            assert np.array_equal(got[g], ref[g]), "empty group must be exactly zero / untouched"
+        else:
+            assert rel_err(got[g], ref[g]) < TOL_BF16 / 4, g
+
+
 # ----------------------------------------------------------------- whole layer
 
 SMALL_BF16 = mi.MoEConfig("small_bf16", seed=31, T=600, d=256, E=8, K=2, F=384, bf16=True, wr_std=0.05)
