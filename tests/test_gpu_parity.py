@@ -365,6 +365,7 @@ def test_grouped_gemm_mx_parity(counts, N, Kd, epi, use_ws):
     ([130, 0, 70, 256], 512, 384, False),  # ragged groups, an empty one
     ([300, 41], 320, 256, True),           # F = 160: a partial column tile (one block of it past F)
     ([1, 2, 3], 64, 128, False),           # tiny groups, one block a row
+    ([700, 5, 513], 1344, 256, True),      # several full row and column tiles, F = 672 (21 blocks)
 ])
 def test_grouped_gemm_mx_swiglu_quantised_equals_two_step(counts, N, Kd, use_ws):
     """The SwiGLU epilogue that writes H as MXFP8 (codes and E8M0 scales) gives the bytes that the
