@@ -57,6 +57,9 @@ def parse():
     ap.add_argument("--cold-reps", type=int, default=100,
                     help="launches of each kernel timed alone with the caches flushed before each one")
     ap.add_argument("--no-clock", action="store_true", help="skip sampling the GPU clock with amd-smi")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the shorter backward and MXFP8 runs that the Mixtral-shaped forward line carries "
+                         "under extra_lines")
     ap.add_argument("--no-train-form", action="store_true",
                     help="skip the training form of the forward (permuted copy written, pre-activations saved)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -375,9 +378,11 @@ def main():
     import moe_inputs as mi
 
     if args.backward:
-        return bench_backward(args, torch, moe, mi)
+        print(json.dumps(bench_backward(args, torch, moe, mi)), flush=True)
+        return
     if args.mxfp8:
-        return bench_mxfp8(args, torch, moe, mi)
+        print(json.dumps(bench_mxfp8(args, torch, moe, mi)), flush=True)
+        return
     if args.gemm_zipf:
         return bench_gemm_zipf(args, torch, moe, mi)
     cfg = mi.CONFIGS[args.workload]
@@ -549,6 +554,10 @@ def main():
         "cpu_baseline": cpu,
         "input_generation_s": gen_s,
     }
+    if cfg.name == "mixtral" and not args.no_extras:
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        out["extra_lines"] = extra_lines(args, torch, moe, mi)
     print(json.dumps(out), flush=True)
     if args.calib_copy:
         # one kernel per launch that reads and writes exactly 512 MiB (a device-to-device copy may
@@ -560,19 +569,43 @@ def main():
         torch.cuda.synchronize()
 
 
+def extra_lines(args, torch, moe, mi) -> dict:
+    """Shorter runs of the backward line and the MXFP8 forward line (at most 10 timed steps, 20
+    cold launches per kernel), attached to the Mixtral-shaped forward line so that one default run
+    measures them too. A failure is recorded in place of the line, never raised."""
+    sub = argparse.Namespace(**vars(args))
+    sub.steps, sub.warmup, sub.cold_reps = min(args.steps, 10), min(args.warmup, 3), min(args.cold_reps, 20)
+    keep = ("metric", "value", "unit", "ms_per_step", "steps", "warmup", "dtype", "config", "timing")
+    res = {}
+    for name, fn, more in (("backward", bench_backward, ("gemm_tflops", "gemm_total_tflops", "kernels_ms")),
+                           ("mxfp8", bench_mxfp8, ("grouped_gemm", "kernels_ms", "roofline"))):
+        try:
+            o = fn(sub, torch, moe, mi)
+            res[name] = {k: o[k] for k in keep + more if k in o}
+        except Exception as e:  # noqa: BLE001 - the headline line must still print
+            res[name] = {"error": f"{type(e).__name__}: {e}"}
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    return res
+
+
 def bench_backward(args, torch, moe, mi):
     """Backward of the Mixtral-shaped layer with one expert taking half of the slots and two none,
     the product's call sequence (layer_backward with the router): combine backward, SwiGLU-backward
     dgrad, down wgrad, gate/up dgrad, gate/up wgrad, permute backward, then the router's backward
     (d_gates -> d_logits -> dWr, and its share of dX); routing held fixed.  Timed as HIP-graph
     replays of the whole backward."""
-    import oracle as orc
     cfg = mi.CONFIGS["mixtral_bwd_skew"]
     torch.cuda.set_device(0)
     inp = mi.make(cfg)
     hot, dead = mi.skew_choice(cfg)
-    logits = mi.skew_logits(orc.router_logits(inp["x"], inp["w_router"]), hot, dead)
     dev = {k: to_dev(v, torch) for k, v in inp.items()}
+    # the skewed routing is an input: the router product (the library's) with the dead experts
+    # masked and the hot one lifted above every row's maximum
+    raw = torch.empty((cfg.T, cfg.E), dtype=torch.float32, device="cuda")
+    moe.moe_router_logits(dev["x"], dev["w_router"], raw)
+    torch.cuda.synchronize()
+    logits = mi.skew_logits(raw.cpu().numpy(), hot, dead)
     dy = to_dev(mi.upstream_grad(cfg), torch)
     bufs = moe.MoEBuffers(cfg.T, cfg.d, cfg.E, cfg.K, cfg.F, torch.bfloat16, backward=True)
     logits_dev = to_dev(logits, torch)
@@ -622,7 +655,7 @@ def bench_backward(args, torch, moe, mi):
            "kernels_ms": kms, "kernels_cold_ms": kcold,
            "hbm_gbs": {k: nb[k] / (kcold[k]["median"] * 1e-3) / 1e9 for k in kcold},
            "hbm_gbs_in_layer": {k: nb[k] / (kms[k] * 1e-3) / 1e9 for k in kcold}}
-    print(json.dumps(out), flush=True)
+    return out
 
 
 def bench_gemm_zipf(args, torch, moe, mi):
@@ -765,7 +798,7 @@ def bench_mxfp8(args, torch, moe, mi):
            "roofline": {"kernel": "MXFP8 grouped GEMM gate/up + SwiGLU", "bound": "mfma", "achieved": tf_up,
                         "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": tf_up / PEAK_FP8_TFLOPS, "traffic": None},
            "cpu_baseline": None}
-    print(json.dumps(out), flush=True)
+    return out
 
 
 if __name__ == "__main__":
