@@ -385,6 +385,22 @@ def main():
         return
     if args.gemm_zipf:
         return bench_gemm_zipf(args, torch, moe, mi)
+    out = bench_forward(args, torch, moe, mi)
+    if out["config"]["workload"] == "mixtral" and not args.no_extras:
+        out["extra_lines"] = extra_lines(args, torch, moe, mi)
+    print(json.dumps(out), flush=True)
+    if args.calib_copy:
+        # one kernel per launch that reads and writes exactly 512 MiB (a device-to-device copy may
+        # be split into several dispatches)
+        src = torch.ones(256 << 20, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+
+
+def bench_forward(args, torch, moe, mi) -> dict:
+    """The headline line: the layer forward of one workload (args.workload), as a dict."""
     cfg = mi.CONFIGS[args.workload]
     torch.cuda.set_device(0)
     t_gen = time.perf_counter()
@@ -554,32 +570,27 @@ def main():
         "cpu_baseline": cpu,
         "input_generation_s": gen_s,
     }
-    if cfg.name == "mixtral" and not args.no_extras:
-        torch.cuda.synchronize()
-        torch.cuda.empty_cache()
-        out["extra_lines"] = extra_lines(args, torch, moe, mi)
-    print(json.dumps(out), flush=True)
-    if args.calib_copy:
-        # one kernel per launch that reads and writes exactly 512 MiB (a device-to-device copy may
-        # be split into several dispatches)
-        src = torch.ones(256 << 20, dtype=torch.bfloat16, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            torch.neg(src, out=dst)
-        torch.cuda.synchronize()
+    return out
 
 
 def extra_lines(args, torch, moe, mi) -> dict:
-    """Shorter runs of the backward line and the MXFP8 forward line (at most 10 timed steps, 20
-    cold launches per kernel), attached to the Mixtral-shaped forward line so that one default run
-    measures them too. A failure is recorded in place of the line, never raised."""
+    """Shorter runs of the other lines (at most 10 timed steps, 20 cold launches per kernel): the
+    fine-grained and DeepSeek-V3-share forwards (no CPU sample, clock or training form), the
+    backward and the MXFP8 forward, attached to the Mixtral-shaped forward line so that one default
+    run measures them too. A failure is recorded in place of the line, never raised."""
     sub = argparse.Namespace(**vars(args))
     sub.steps, sub.warmup, sub.cold_reps = min(args.steps, 10), min(args.warmup, 3), min(args.cold_reps, 20)
+    sub.cpu_seconds, sub.no_clock, sub.no_train_form, sub.no_extras = 0.0, True, True, True
+    fwd = ("grouped_gemm", "kernels_ms", "hbm_frac", "roofline")
     keep = ("metric", "value", "unit", "ms_per_step", "steps", "warmup", "dtype", "config", "timing")
     res = {}
-    for name, fn, more in (("backward", bench_backward, ("gemm_tflops", "gemm_total_tflops", "kernels_ms")),
+    for name, fn, more in (("fine_grained", bench_forward, fwd), ("dsv3_share", bench_forward, fwd),
+                           ("backward", bench_backward, ("gemm_tflops", "gemm_total_tflops", "kernels_ms")),
                            ("mxfp8", bench_mxfp8, ("grouped_gemm", "kernels_ms", "roofline"))):
+        sub.workload = name if fn is bench_forward else "mixtral"
         try:
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
             o = fn(sub, torch, moe, mi)
             res[name] = {k: o[k] for k in keep + more if k in o}
         except Exception as e:  # noqa: BLE001 - the headline line must still print
