@@ -89,6 +89,19 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
+def measured_traffic(path: str, key: str):
+    """Calibrated HBM bytes per launch recorded under key in the counter file at path, or None when
+    absent or recorded for other GEMM code (a different kernel_source_hash())."""
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(key)
+        if rec and rec.get("source_sha256") == kernel_source_hash():
+            return rec["bytes_per_launch"]
+    except (OSError, ValueError, KeyError):
+        pass
+    return None
+
+
 def to_dev(a, torch):
     if a is None:
         return None
@@ -379,16 +392,15 @@ def main():
 
     if args.backward:
         print(json.dumps(bench_backward(args, torch, moe, mi)), flush=True)
-        return
-    if args.mxfp8:
+    elif args.mxfp8:
         print(json.dumps(bench_mxfp8(args, torch, moe, mi)), flush=True)
-        return
-    if args.gemm_zipf:
-        return bench_gemm_zipf(args, torch, moe, mi)
-    out = bench_forward(args, torch, moe, mi)
-    if out["config"]["workload"] == "mixtral" and not args.no_extras:
-        out["extra_lines"] = extra_lines(args, torch, moe, mi)
-    print(json.dumps(out), flush=True)
+    elif args.gemm_zipf:
+        bench_gemm_zipf(args, torch, moe, mi)
+    else:
+        out = bench_forward(args, torch, moe, mi)
+        if out["config"]["workload"] == "mixtral" and not args.no_extras:
+            out["extra_lines"] = extra_lines(args, torch, moe, mi)
+        print(json.dumps(out), flush=True)
     if args.calib_copy:
         # one kernel per launch that reads and writes exactly 512 MiB (a device-to-device copy may
         # be split into several dispatches)
@@ -467,15 +479,7 @@ def bench_forward(args, torch, moe, mi) -> dict:
     }
     nbytes = {k: r + w for k, (r, w) in nrw.items()}
 
-    traffic = None
-    try:
-        with open(args.traffic) as f:
-            tr = json.load(f)
-        rec = tr.get(f"{cfg.name}/gemm_gate_up")
-        if rec and rec.get("source_sha256") == kernel_source_hash():
-            traffic = rec["bytes_per_launch"]
-    except (OSError, ValueError, KeyError):
-        traffic = None
+    traffic = measured_traffic(args.traffic, f"{cfg.name}/gemm_gate_up")
 
     tokens_per_s = cfg.T / (ms_per_step * 1e-3)
 
@@ -807,7 +811,8 @@ def bench_mxfp8(args, torch, moe, mi):
            "kernels_ms": kms,
            "quantize_gbs": {"x": (T * d * 3 + T * d // 32) / (kms["quantize_x"] * 1e-3) / 1e9},
            "roofline": {"kernel": "MXFP8 grouped GEMM gate/up + SwiGLU", "bound": "mfma", "achieved": tf_up,
-                        "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": tf_up / PEAK_FP8_TFLOPS, "traffic": None},
+                        "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": tf_up / PEAK_FP8_TFLOPS,
+                        "traffic": measured_traffic(args.traffic, f"{cfg.name}_mx/gemm_gate_up")},
            "cpu_baseline": None}
     return out
 
